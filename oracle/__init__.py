@@ -1,0 +1,2 @@
+"""Float64 CPU oracle (test infrastructure only; see pc_oracle)."""
+from .pc_oracle import forward, backward, em_step, lowrank_effective  # noqa: F401
