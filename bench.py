@@ -1,0 +1,179 @@
+"""Benchmark: one pass of the sum-layer hot path on the HMM workload.
+
+Workload: HMM with 4096 latent states, 32 positions, 512 symbols, batch 512
+(tied 4096 x 4096 transition, softmax(N(0,1)) rows, uniform tokens; seeded
+synthetic data).  A step = forward (input layer, 31 shared-children sum
+layers, products, root) + backward (element flows, parameter flows) + EM
+update, all through the C ABI on one GPU, inputs resident in HBM.
+
+Prints one JSON line.  `value` is the sum layers' algorithmic throughput:
+3 products (forward, element flows, parameter flows) x 2*M*N*B flops per sum
+group, divided by the whole step's wall time.  The roofline object describes
+the dominant kernel: algorithmic flops per launch over its mean launch time
+(HIP events on the library's stream, recorded in a second timed pass over the
+same number of steps), against the bf16 dense MFMA peak of MI355X.
+The CPU baseline times the float64 oracle on a bounded sample of the same
+workload (a subset of the batch) on the host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0
+
+
+def sum_flops(circ, B):
+    """Algorithmic flops of the sum layers per pass (3 products each)."""
+    tot = 0
+    per_kind = 0
+    for layer in circ.layers:
+        if type(layer).__name__ == "Sum":
+            for g in layer.groups:
+                tot += 3 * 2 * g.num_nodes * g.num_children * B
+    return tot
+
+
+def cpu_baseline(cfg, sample_B, budget_s=30.0):
+    """The float64 oracle (as it stands) on the first `sample_B` samples."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count()
+    circ = cfg["circuit"]
+    p = cfg["params"].astype(np.float64)
+    tok = cfg["tokens"][:sample_B]
+    t0 = time.perf_counter()
+    V, ll = oracle.forward(circ, p, sample_B, tokens=tok)
+    oracle.backward(circ, p, V, tokens=tok)
+    dt = time.perf_counter() - t0
+    fl = sum_flops(circ, sample_B)
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"float64 oracle forward+backward on {sample_B} of the {cfg['B']} samples "
+                      f"(all 32 positions), {dt:.2f} s; sum-layer algorithmic flops / time",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--mode", default="auto", choices=["auto", "fp32"])
+    ap.add_argument("--batch", type=int, default=512)
+    ap.add_argument("--H", type=int, default=4096)
+    ap.add_argument("--T", type=int, default=32)
+    ap.add_argument("--cpu-sample", type=int, default=32)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import log_space_sum_amd as L
+    from workloads import make_config
+
+    cfg = make_config("hmm4096", H=args.H, T=args.T, B=args.batch)
+    circ, B = cfg["circuit"], cfg["B"]
+    dev = "cuda:0"
+    h = L.pc_compile_layout(circ, device=0)
+    L.pc_set_precision(h, args.mode)
+    params = torch.tensor(cfg["params"], device=dev)
+    params0 = params.clone()
+    tokens = torch.tensor(cfg["tokens"], device=dev)
+    vals = torch.empty((circ.num_nodes, B), device=dev)
+    flows = torch.empty((circ.num_nodes, B), device=dev)
+    pflows = torch.zeros(circ.num_params, device=dev)
+    ll = torch.empty(B, device=dev)
+    ws = L.workspace(h, B, dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        pflows.zero_()
+        L.pc_forward(h, B, tokens, params, vals, ll, None, ws, stream.cuda_stream)
+        L.pc_backward(h, B, tokens, params, vals, flows, pflows, 0, None, None, ws, stream.cuda_stream)
+        L.pc_em_step(h, params, pflows, 1.0, 0.0, stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms = dt / args.steps * 1e3
+    finite = bool(torch.isfinite(ll).all().item())
+
+    # second timed pass with per-launch HIP events
+    L.pc_set_timing(h, True)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kt = L.pc_kernel_times(h)
+    L.pc_set_timing(h, False)
+
+    flops = sum_flops(circ, B)
+    value = flops / (ms * 1e-3) / 1e12
+    gemm_kinds = ["sum_fwd_gemm", "elem_flow_gemm", "param_flow_gemm"]
+    sum_ms = sum(kt[k][1] for k in gemm_kinds) / args.steps
+    other_sum_ms = sum(kt[k][1] for k in ("weight_split", "column_max", "exp_children", "scaled_flows")) / args.steps
+    per_kind_flops = {"sum_fwd_gemm": flops / 3, "elem_flow_gemm": flops / 3, "param_flow_gemm": flops / 3}
+    dom = max(gemm_kinds, key=lambda k: kt[k][1])
+    n_launch, tot_ms = kt[dom]
+    per_launch_flops = per_kind_flops[dom] * args.steps / max(n_launch, 1)
+    avg_ms = tot_ms / max(n_launch, 1)
+    achieved = per_launch_flops / (avg_ms * 1e-3) / 1e12
+    out = {
+        "metric": "sum-layer fwd+bwd ms & TFLOP/s (frac of MFMA peak), HMM 4096 lat×32 pos, batch 512",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if args.mode == "auto" else "bf16x3-split",
+        "data": "synthetic",
+        "config": {"workload": f"hmm{args.H}x{args.T} symbols 512 batch {B} fwd+bwd+em",
+                   "precision_mode": args.mode, "global_batch": B},
+        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "sum_layer_kernels_ms": round(sum_ms, 4),
+        "sum_layer_kernels_tflops": round(flops / (sum_ms * 1e-3) / 1e12, 3) if sum_ms > 0 else None,
+        "sum_layer_aux_kernels_ms": round(other_sum_ms, 4),
+        "kernel_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in kt.items() if v[0]},
+        "kernel_launches_per_step": {k: v[0] // args.steps for k, v in kt.items() if v[0]},
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 3),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "per_launch_gflop": round(per_launch_flops / 1e9, 4),
+                     "avg_launch_ms": round(avg_ms, 5)},
+        "ll_finite": finite,
+        "context": "pages (RTX PRO 6000, whole circuit, auto): 32.1 ms fwd+bwd at batch 512",
+    }
+    if not args.no_cpu:
+        cpu_cfg = make_config("hmm4096", H=args.H, T=args.T, B=args.batch)
+        out["cpu_baseline"] = cpu_baseline(cpu_cfg, min(args.cpu_sample, B))
+    del params0
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

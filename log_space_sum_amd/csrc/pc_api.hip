@@ -1,0 +1,709 @@
+// pc_api.hip -- the C ABI: handles, workspace plan, and the launch schedule of
+// the forward pass, the backward pass (element flows, then the deferred
+// parameter-flow products of every weight block with all its tied copies as
+// one contraction) and the EM update.  Every launch goes on the caller's
+// stream; nothing here allocates device memory or synchronises, except
+// pc_compile_layout (index tables) and pc_kernel_times (waits on its events).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "pc_elem.h"
+#include "pc_host.h"
+#include "pc_kernels.h"
+
+using namespace pc;
+
+namespace {
+
+thread_local std::string g_err;
+
+int set_error(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+#define HIPCHECK(x)                                                                       \
+  do {                                                                                    \
+    hipError_t e_ = (x);                                                                  \
+    if (e_ != hipSuccess) fail(PC_ERR_HIP, std::string(#x) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+template <typename T>
+T* upload(const std::vector<T>& v) {
+  if (v.empty()) return nullptr;
+  T* d = nullptr;
+  HIPCHECK(hipMalloc((void**)&d, v.size() * sizeof(T)));
+  HIPCHECK(hipMemcpy(d, v.data(), v.size() * sizeof(T), hipMemcpyHostToDevice));
+  return d;
+}
+
+template <typename T>
+void release(T*& p) {
+  if (p) (void)hipFree(p);
+  p = nullptr;
+}
+
+struct DeviceGuard {
+  int prev = -1;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (prev != dev) HIPCHECK(hipSetDevice(dev));
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+enum KernelKind {
+  KK_FWD = 0, KK_ELEM, KK_PARAM, KK_SPLIT, KK_COLMAX, KK_EXP, KK_GPACK, KK_INFWD, KK_INBWD,
+  KK_PRODFWD, KK_PRODBWD, KK_EM, KK_LRFWD, KK_LRBWD, KK_OTHER
+};
+
+// Records a HIP event pair around one launch when the handle times kernels.
+struct Timed {
+  Handle* h;
+  hipStream_t s;
+  size_t slot = 0;
+  Timed(Handle* h_, int kind, hipStream_t s_) : h(h_), s(s_) {
+    if (!h->timing) return;
+    if (h->events_used == h->events.size()) {
+      Handle::Ev ev{kind, nullptr, nullptr};
+      HIPCHECK(hipEventCreate((hipEvent_t*)&ev.start));
+      HIPCHECK(hipEventCreate((hipEvent_t*)&ev.stop));
+      h->events.push_back(ev);
+    }
+    slot = h->events_used++;
+    h->events[slot].kind = kind;
+    HIPCHECK(hipEventRecord((hipEvent_t)h->events[slot].start, s));
+  }
+  ~Timed() {
+    if (h->timing) (void)hipEventRecord((hipEvent_t)h->events[slot].stop, s);
+  }
+};
+
+void check_launch() {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) fail(PC_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
+}
+
+bool planes_ok(int pa, int pb) {
+  return (pa == 1 && pb == 1) || (pa == 2 && pb == 1) || (pa == 1 && pb == 2) || (pa == 2 && pb == 2) ||
+         (pa == 3 && pb == 3);
+}
+
+}  // namespace
+
+namespace pc {
+
+void upload_tables(Handle* h, int device) {
+  HIPCHECK(hipSetDevice(device));
+  h->device = device;
+  for (auto& ip : h->inputs) {
+    ip.d_var = upload(ip.var);
+    ip.d_row = upload(ip.row);
+    ip.d_row_ptr = upload(ip.row_ptr);
+    ip.d_row_nodes = upload(ip.row_nodes);
+  }
+  for (auto& pp : h->prods) {
+    pp.d_ch_ptr = upload(pp.ch_ptr);
+    pp.d_ch_ids = upload(pp.ch_ids);
+    pp.d_uchild = upload(pp.uchild);
+    pp.d_pptr = upload(pp.pptr);
+    pp.d_parents = upload(pp.parents);
+  }
+  for (auto& sp : h->sums) {
+    sp.d_groups = upload(sp.groups);
+    sp.d_blocks = upload(sp.blocks);
+    sp.d_red_child = upload(sp.red_child);
+    sp.d_red_ptr = upload(sp.red_ptr);
+    sp.d_red_src = upload(sp.red_src);
+  }
+  h->d_blocks = upload(h->blocks);
+  h->d_copies = upload(h->copies);
+  h->d_rowsegs = upload(h->rowsegs);
+  h->d_zero = upload(h->zero_ranges);
+  h->d_seed = upload(h->seed_ranges);
+}
+
+void free_tables(Handle* h) {
+  if (h->device < 0) return;
+  int prev = -1;
+  (void)hipGetDevice(&prev);
+  (void)hipSetDevice(h->device);
+  for (auto& ip : h->inputs) {
+    release(ip.d_var);
+    release(ip.d_row);
+    release(ip.d_row_ptr);
+    release(ip.d_row_nodes);
+  }
+  for (auto& pp : h->prods) {
+    release(pp.d_ch_ptr);
+    release(pp.d_ch_ids);
+    release(pp.d_uchild);
+    release(pp.d_pptr);
+    release(pp.d_parents);
+  }
+  for (auto& sp : h->sums) {
+    release(sp.d_groups);
+    release(sp.d_blocks);
+    release(sp.d_red_child);
+    release(sp.d_red_ptr);
+    release(sp.d_red_src);
+  }
+  release(h->d_blocks);
+  release(h->d_copies);
+  release(h->d_rowsegs);
+  release(h->d_zero);
+  release(h->d_seed);
+  for (auto& ev : h->events) {
+    if (ev.start) (void)hipEventDestroy((hipEvent_t)ev.start);
+    if (ev.stop) (void)hipEventDestroy((hipEvent_t)ev.stop);
+  }
+  h->events.clear();
+  if (prev >= 0) (void)hipSetDevice(prev);
+}
+
+WsPlan plan_workspace(const Handle* h, int B) {
+  WsPlan p{};
+  p.B = B;
+  p.B_pad = (int)round_up(B, ROW_PAD);
+  p.B_padK = (int)round_up(B, K_PAD);
+  p.mode = effective_mode(h, B);
+  for (int k = 0; k < 3; ++k)
+    for (int j = 0; j < 2; ++j) p.pl[k][j] = h->planes[p.mode][k][j];
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = (size_t)round_up((int64_t)(off + bytes), 256);
+    return o;
+  };
+  const size_t Bp = p.B_pad, BpK = p.B_padK, Bs = B;
+  p.theta = take((size_t)p.pl[GK_FWD][0] * h->theta_elems * 2);
+  p.thetaT = take((size_t)p.pl[GK_ELEM][0] * h->thetaT_elems * 2);
+  p.ebt = take((size_t)p.pl[GK_FWD][1] * Bp * h->max_ebt_cols * 2);
+  p.gbt = take((size_t)p.pl[GK_ELEM][1] * Bp * h->max_gbt_cols * 2);
+  p.earena = take((size_t)p.pl[GK_PARAM][1] * h->earena_rows * BpK * 2);
+  p.garena = take((size_t)p.pl[GK_PARAM][0] * h->garena_rows * BpK * 2);
+  p.mkeys = take((size_t)h->m_rows * Bs * 4);
+  p.ssum = take((size_t)h->s_rows * Bs * 4);
+  p.scratch = take((size_t)h->max_scratch_rows * Bs * 4);
+  const bool inp = !h->inputs.empty();
+  p.tokT = take(inp ? (size_t)h->num_vars * Bs * 4 : 0);
+  p.bptr = take(inp ? (size_t)h->num_vars * (h->max_cats + 1) * 4 : 0);
+  p.bidx = take(inp ? (size_t)h->num_vars * Bs * 4 : 0);
+  p.lowrank = take(0);
+  p.lowrank_bytes = 0;
+  p.total = off;
+  return p;
+}
+
+WsView make_view(const Handle* h, const WsPlan& p, void* ws) {
+  char* base = (char*)ws;
+  WsView v{};
+  v.theta = (uint16_t*)(base + p.theta);
+  v.thetaT = (uint16_t*)(base + p.thetaT);
+  v.theta_plane = h->theta_elems;
+  v.thetaT_plane = h->thetaT_elems;
+  v.ebt = (uint16_t*)(base + p.ebt);
+  v.gbt = (uint16_t*)(base + p.gbt);
+  v.ebt_plane = (int64_t)p.B_pad * h->max_ebt_cols;
+  v.gbt_plane = (int64_t)p.B_pad * h->max_gbt_cols;
+  v.earena = (uint16_t*)(base + p.earena);
+  v.garena = (uint16_t*)(base + p.garena);
+  v.earena_plane = h->earena_rows * p.B_padK;
+  v.garena_plane = h->garena_rows * p.B_padK;
+  v.mkeys = (uint32_t*)(base + p.mkeys);
+  v.ssum = (float*)(base + p.ssum);
+  v.scratch = (float*)(base + p.scratch);
+  v.tokT = (int32_t*)(base + p.tokT);
+  v.bucket_ptr = (int32_t*)(base + p.bptr);
+  v.bucket_idx = (int32_t*)(base + p.bidx);
+  v.B = p.B;
+  v.B_pad = p.B_pad;
+  v.B_padK = p.B_padK;
+  return v;
+}
+
+}  // namespace pc
+
+// ---------------------------------------------------------------------------
+// schedule helpers
+// ---------------------------------------------------------------------------
+namespace {
+
+Handle* checked(pc_handle hh) {
+  if (!hh) fail(PC_ERR_INVALID_ARG, "null handle");
+  return reinterpret_cast<Handle*>(hh);
+}
+
+struct Call {
+  Handle* h;
+  WsPlan p;
+  WsView v;
+  hipStream_t s;
+};
+
+Call begin_call(pc_handle hh, int B, void* ws, size_t ws_bytes, void* stream) {
+  Handle* h = checked(hh);
+  if (h->device < 0) fail(PC_ERR_NO_DEVICE, "handle was compiled without a device");
+  if (B < 1) fail(PC_ERR_INVALID_ARG, "batch must be >= 1");
+  if (h->lowrank_slots > 0) fail(PC_ERR_UNSUPPORTED, "LowRank layers are not available in this build");
+  if (!h->inputs.empty() && (size_t)(h->max_cats + 1 + B) * 4 > 65536)
+    fail(PC_ERR_UNSUPPORTED, "categories + batch too large for the input-flow bucketing (limit 16383)");
+  Call c{h, plan_workspace(h, B), {}, (hipStream_t)stream};
+  if (c.p.total > 0 && !ws) fail(PC_ERR_INVALID_ARG, "null workspace");
+  if (ws_bytes < c.p.total)
+    fail(PC_ERR_WORKSPACE, "workspace too small: need " + std::to_string(c.p.total) + " bytes, got " +
+                               std::to_string(ws_bytes));
+  c.v = make_view(h, c.p, ws);
+  return c;
+}
+
+GemmArgs gemm_common(const Call& c) {
+  GemmArgs a{};
+  a.B = c.v.B;
+  a.B_pad = c.v.B_pad;
+  a.B_padK = c.v.B_padK;
+  a.ntiles = c.v.B_pad / 128;
+  a.blocks = c.h->d_blocks;
+  a.copies = c.h->d_copies;
+  return a;
+}
+
+SumArgs sum_common(const Call& c, const SumPlan& sp) {
+  SumArgs a{};
+  a.B = c.v.B;
+  a.B_pad = c.v.B_pad;
+  a.B_padK = c.v.B_padK;
+  a.btiles = c.v.B_pad / 64;
+  a.ngroups = (int)sp.groups.size();
+  a.groups = sp.d_groups;
+  a.chblocks = sp.d_blocks;
+  a.mkeys = c.v.mkeys;
+  return a;
+}
+
+InputArgs input_args(const Call& c, const InputPlan& ip, const float* params) {
+  InputArgs a{};
+  a.B = c.v.B;
+  a.node_start = ip.node_start;
+  a.num_nodes = ip.num_nodes;
+  a.K = ip.num_cats;
+  a.num_rows = ip.num_rows;
+  a.Kmax = c.h->max_cats;
+  a.param_offset = ip.param_offset;
+  a.var = ip.d_var;
+  a.row = ip.d_row;
+  a.row_ptr = ip.d_row_ptr;
+  a.row_nodes = ip.d_row_nodes;
+  a.tokT = c.v.tokT;
+  a.bptr = c.v.bucket_ptr;
+  a.bidx = c.v.bucket_idx;
+  a.params = params;
+  return a;
+}
+
+ProdArgs prod_args(const Call& c, const ProductPlan& pp) {
+  ProdArgs a{};
+  a.B = c.v.B;
+  a.node_start = pp.node_start;
+  a.num_nodes = pp.num_nodes;
+  a.nuniq = (int)pp.uchild.size();
+  a.store = pp.store ? 1 : 0;
+  a.ch_ptr = pp.d_ch_ptr;
+  a.ch_ids = pp.d_ch_ids;
+  a.uchild = pp.d_uchild;
+  a.pptr = pp.d_pptr;
+  a.parents = pp.d_parents;
+  return a;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+extern "C" {
+
+const char* pc_last_error(void) { return g_err.c_str(); }
+
+int pc_compile_layout(const pc_circuit_desc* desc, int device, pc_handle* out) {
+  Handle* h = nullptr;
+  try {
+    if (!out) fail(PC_ERR_INVALID_ARG, "null output handle pointer");
+    *out = nullptr;
+    h = compile_layout(desc);
+    if (device >= 0) upload_tables(h, device);
+    *out = reinterpret_cast<pc_handle>(h);
+    return PC_OK;
+  } catch (const Error& e) {
+    if (h) {
+      free_tables(h);
+      delete h;
+    }
+    return set_error(e.code, e.msg);
+  } catch (const std::exception& e) {
+    if (h) {
+      free_tables(h);
+      delete h;
+    }
+    return set_error(PC_ERR_INVALID_ARG, e.what());
+  }
+}
+
+int pc_destroy(pc_handle hh) {
+  if (!hh) return PC_OK;
+  Handle* h = reinterpret_cast<Handle*>(hh);
+  free_tables(h);
+  delete h;
+  return PC_OK;
+}
+
+int pc_set_precision(pc_handle hh, int mode) {
+  try {
+    Handle* h = checked(hh);
+    if (mode == PC_PREC_TF32)
+      fail(PC_ERR_UNSUPPORTED, "precision 'tf32': gfx950 has no TF32 matrix instruction; use PC_PREC_AUTO or PC_PREC_FP32");
+    if (mode != PC_PREC_AUTO && mode != PC_PREC_FP32) fail(PC_ERR_INVALID_ARG, "unknown precision mode " + std::to_string(mode));
+    h->mode = mode;
+    return PC_OK;
+  } catch (const Error& e) {
+    return set_error(e.code, e.msg);
+  }
+}
+
+int pc_get_precision(pc_handle hh, int* mode) {
+  try {
+    Handle* h = checked(hh);
+    if (!mode) fail(PC_ERR_INVALID_ARG, "null mode pointer");
+    *mode = h->mode;
+    return PC_OK;
+  } catch (const Error& e) {
+    return set_error(e.code, e.msg);
+  }
+}
+
+int pc_set_split(pc_handle hh, int mode, int gemm_kind, int planes_a, int planes_b) {
+  try {
+    Handle* h = checked(hh);
+    if (mode != PC_PREC_AUTO && mode != PC_PREC_FP32) fail(PC_ERR_INVALID_ARG, "unknown precision mode");
+    if (gemm_kind < 0 || gemm_kind > 2) fail(PC_ERR_INVALID_ARG, "unknown product kind");
+    if (!planes_ok(planes_a, planes_b)) fail(PC_ERR_INVALID_ARG, "unsupported plane counts");
+    h->planes[mode][gemm_kind][0] = planes_a;
+    h->planes[mode][gemm_kind][1] = planes_b;
+    return PC_OK;
+  } catch (const Error& e) {
+    return set_error(e.code, e.msg);
+  }
+}
+
+int pc_workspace_bytes(pc_handle hh, int batch, size_t* bytes) {
+  try {
+    Handle* h = checked(hh);
+    if (batch < 1) fail(PC_ERR_INVALID_ARG, "batch must be >= 1");
+    if (!bytes) fail(PC_ERR_INVALID_ARG, "null bytes pointer");
+    *bytes = plan_workspace(h, batch).total;
+    return PC_OK;
+  } catch (const Error& e) {
+    return set_error(e.code, e.msg);
+  }
+}
+
+int pc_layout_info(pc_handle hh, pc_layout_summary* info) {
+  try {
+    Handle* h = checked(hh);
+    if (!info) fail(PC_ERR_INVALID_ARG, "null info pointer");
+    info->num_layers = (int32_t)h->layers.size();
+    info->num_sum_layers = (int32_t)h->sums.size();
+    info->num_param_blocks = (int32_t)h->blocks.size();
+    info->num_row_segments = (int32_t)h->rowsegs.size();
+    info->num_params = h->num_params;
+    info->num_outputs = (int32_t)h->outputs.size();
+    info->device = h->device;
+    return PC_OK;
+  } catch (const Error& e) {
+    return set_error(e.code, e.msg);
+  }
+}
+
+int pc_layer_class(pc_handle hh, int layer, int* cls) {
+  try {
+    Handle* h = checked(hh);
+    if (!cls) fail(PC_ERR_INVALID_ARG, "null class pointer");
+    if (layer < 0 || layer >= (int)h->layers.size()) fail(PC_ERR_INVALID_ARG, "layer out of range");
+    const LayerRef& r = h->layers[layer];
+    *cls = (r.kind == PC_LAYER_SUM) ? h->sums[r.idx].cls : -1;
+    return PC_OK;
+  } catch (const Error& e) {
+    return set_error(e.code, e.msg);
+  }
+}
+
+int pc_forward(pc_handle hh, int batch, const int32_t* tokens, const float* params, float* node_vals,
+               float* ll, const pc_lowrank_io* lowrank, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    Call c = begin_call(hh, batch, ws, ws_bytes, stream);
+    Handle* h = c.h;
+    (void)lowrank;
+    if (!params || !node_vals) fail(PC_ERR_INVALID_ARG, "null params or node_vals");
+    if (!h->inputs.empty() && !tokens) fail(PC_ERR_INVALID_ARG, "null tokens");
+    if (ll && h->root < 0) fail(PC_ERR_INVALID_ARG, "ll requested but the circuit has no root");
+    DeviceGuard dg(h->device);
+    const int B = batch;
+    const WsPlan& p = c.p;
+    const WsView& v = c.v;
+    if (h->has_plain_sums) {
+      ThetaArgs ta{};
+      ta.nblocks = (int)h->blocks.size();
+      ta.np_fwd = p.pl[GK_FWD][0];
+      ta.np_elem = p.pl[GK_ELEM][0];
+      ta.blocks = h->d_blocks;
+      ta.params = params;
+      ta.theta = v.theta;
+      ta.theta_plane = v.theta_plane;
+      ta.thetaT = v.thetaT;
+      ta.thetaT_plane = v.thetaT_plane;
+      Timed t(h, KK_SPLIT, c.s);
+      launch_theta_pack(ta, h->pk_block_tiles, c.s);
+    }
+    if (!h->inputs.empty()) {
+      Timed t(h, KK_OTHER, c.s);
+      launch_tokens_t(tokens, v.tokT, B, h->num_vars, c.s);
+    }
+    if (h->m_rows > 0) {
+      Timed t(h, KK_OTHER, c.s);
+      launch_fill_u32(v.mkeys, (int64_t)h->m_rows * B, 0u, c.s);
+    }
+    for (const LayerRef& r : h->layers) {
+      if (r.kind == PC_LAYER_INPUT_CAT) {
+        InputArgs a = input_args(c, h->inputs[r.idx], params);
+        a.vals = node_vals;
+        Timed t(h, KK_INFWD, c.s);
+        launch_input_fwd(a, c.s);
+      } else if (r.kind == PC_LAYER_PRODUCT) {
+        ProdArgs a = prod_args(c, h->prods[r.idx]);
+        a.vals = node_vals;
+        Timed t(h, KK_PRODFWD, c.s);
+        launch_prod_fwd(a, c.s);
+      } else if (r.kind == PC_LAYER_SUM) {
+        const SumPlan& sp = h->sums[r.idx];
+        SumArgs a = sum_common(c, sp);
+        a.vals = node_vals;
+        a.direct = v.earena;
+        a.direct_plane = v.earena_plane;
+        a.np_direct = p.pl[GK_PARAM][1];
+        a.trans = v.ebt;
+        a.trans_plane = v.ebt_plane;
+        a.trans_cols = sp.ebt_cols;
+        a.np_trans = p.pl[GK_FWD][1];
+        {
+          Timed t(h, KK_COLMAX, c.s);
+          launch_colmax(a, sp.pktiles * a.btiles, c.s);
+        }
+        {
+          Timed t(h, KK_EXP, c.s);
+          launch_exp_pack(a, sp.pktiles * a.btiles, c.s);
+        }
+        GemmArgs g = gemm_common(c);
+        g.ngroups = (int)sp.groups.size();
+        g.groups = sp.d_groups;
+        g.chblocks = sp.d_blocks;
+        g.opA = v.theta;
+        g.planeA = v.theta_plane;
+        g.opB = v.ebt;
+        g.planeB = v.ebt_plane;
+        g.ldb = sp.ebt_cols;
+        g.vals = node_vals;
+        g.mkeys = v.mkeys;
+        g.ssum = v.ssum;
+        Timed t(h, KK_FWD, c.s);
+        launch_gemm(EPI_FWD, p.pl[GK_FWD][0], p.pl[GK_FWD][1], sp.mtiles * g.ntiles, g, c.s);
+      }
+    }
+    if (ll) {
+      Timed t(h, KK_OTHER, c.s);
+      launch_copy_row(node_vals + (int64_t)h->root * B, ll, B, c.s);
+    }
+    check_launch();
+    return PC_OK;
+  } catch (const Error& e) {
+    return set_error(e.code, e.msg);
+  }
+}
+
+int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* params, const float* node_vals,
+                float* node_flows, float* param_flows, int flags, const pc_lowrank_io* lowrank, void* ws,
+                size_t ws_bytes, void* stream) {
+  try {
+    Call c = begin_call(hh, batch, ws, ws_bytes, stream);
+    Handle* h = c.h;
+    (void)lowrank;
+    (void)tokens;
+    if (!params || !node_vals || !node_flows || !param_flows) fail(PC_ERR_INVALID_ARG, "null buffer");
+    if (flags & ~PC_BWD_SEEDED) fail(PC_ERR_INVALID_ARG, "unknown flags");
+    const bool seeded = (flags & PC_BWD_SEEDED) != 0;
+    if (!seeded && h->root < 0) fail(PC_ERR_INVALID_ARG, "no root: seed the output flows (PC_BWD_SEEDED)");
+    DeviceGuard dg(h->device);
+    const int B = batch;
+    const WsPlan& p = c.p;
+    const WsView& v = c.v;
+    float* vals = const_cast<float*>(node_vals);
+    {
+      Timed t(h, KK_OTHER, c.s);
+      launch_fill_ranges(node_flows, h->d_zero, (int)h->zero_ranges.size(), h->max_zero_count, B, c.s);
+    }
+    if (!seeded) {
+      Timed t(h, KK_OTHER, c.s);
+      launch_fill_ranges(node_flows, h->d_seed, (int)h->seed_ranges.size(), h->max_seed_count, B, c.s);
+    }
+    if (!h->inputs.empty()) {
+      Timed t(h, KK_OTHER, c.s);
+      launch_bucket(v.tokT, h->num_vars, B, h->max_cats, v.bucket_ptr, v.bucket_idx, c.s);
+    }
+    for (int li = (int)h->layers.size() - 1; li >= 0; --li) {
+      const LayerRef& r = h->layers[li];
+      if (r.kind == PC_LAYER_SUM) {
+        const SumPlan& sp = h->sums[r.idx];
+        SumArgs a = sum_common(c, sp);
+        a.vals = vals;
+        a.flows = node_flows;
+        a.ssum = v.ssum;
+        a.direct = v.garena;
+        a.direct_plane = v.garena_plane;
+        a.np_direct = p.pl[GK_PARAM][0];
+        a.trans = v.gbt;
+        a.trans_plane = v.gbt_plane;
+        a.trans_cols = sp.gbt_cols;
+        a.np_trans = p.pl[GK_ELEM][1];
+        {
+          Timed t(h, KK_GPACK, c.s);
+          launch_g_pack(a, sp.pgtiles * a.btiles, c.s);
+        }
+        GemmArgs g = gemm_common(c);
+        g.ngroups = (int)sp.groups.size();
+        g.groups = sp.d_groups;
+        g.chblocks = sp.d_blocks;
+        g.opA = v.thetaT;
+        g.planeA = v.thetaT_plane;
+        g.opB = v.gbt;
+        g.planeB = v.gbt_plane;
+        g.ldb = sp.gbt_cols;
+        g.vals = vals;
+        g.flows = node_flows;
+        g.scratch = v.scratch;
+        g.mkeys = v.mkeys;
+        g.store = sp.store ? 1 : 0;
+        {
+          Timed t(h, KK_ELEM, c.s);
+          launch_gemm(EPI_ELEM, p.pl[GK_ELEM][0], p.pl[GK_ELEM][1], sp.ctiles * g.ntiles, g, c.s);
+        }
+        if (sp.overlap) {
+          SumArgs ra = sum_common(c, sp);
+          ra.nuniq = (int)sp.red_child.size();
+          ra.store = sp.store ? 1 : 0;
+          ra.red_child = sp.d_red_child;
+          ra.red_ptr = sp.d_red_ptr;
+          ra.red_src = sp.d_red_src;
+          ra.scratch = v.scratch;
+          ra.out_flows = node_flows;
+          Timed t(h, KK_OTHER, c.s);
+          launch_elem_reduce(ra, c.s);
+        }
+      } else if (r.kind == PC_LAYER_PRODUCT) {
+        ProdArgs a = prod_args(c, h->prods[r.idx]);
+        a.flows = node_flows;
+        Timed t(h, KK_PRODBWD, c.s);
+        launch_prod_bwd(a, c.s);
+      } else if (r.kind == PC_LAYER_INPUT_CAT) {
+        InputArgs a = input_args(c, h->inputs[r.idx], params);
+        a.flows = node_flows;
+        a.pflows = param_flows;
+        Timed t(h, KK_INBWD, c.s);
+        launch_input_bwd(a, c.s);
+      }
+    }
+    if (h->has_plain_sums) {
+      GemmArgs g = gemm_common(c);
+      g.ngroups = (int)h->blocks.size();
+      g.opA = v.garena;
+      g.planeA = v.garena_plane;
+      g.opB = v.earena;
+      g.planeB = v.earena_plane;
+      g.params = params;
+      g.pflows = param_flows;
+      Timed t(h, KK_PARAM, c.s);
+      launch_gemm(EPI_PARAM, p.pl[GK_PARAM][0], p.pl[GK_PARAM][1], h->param_tiles, g, c.s);
+    }
+    check_launch();
+    return PC_OK;
+  } catch (const Error& e) {
+    return set_error(e.code, e.msg);
+  }
+}
+
+int pc_em_step(pc_handle hh, float* params, const float* param_flows, float step_size, float pseudocount,
+               void* stream) {
+  try {
+    Handle* h = checked(hh);
+    if (h->device < 0) fail(PC_ERR_NO_DEVICE, "handle was compiled without a device");
+    if (!params || !param_flows) fail(PC_ERR_INVALID_ARG, "null params or param_flows");
+    if (!(step_size >= 0.0f && step_size <= 1.0f)) fail(PC_ERR_INVALID_ARG, "step_size must be in [0, 1]");
+    if (!(pseudocount >= 0.0f)) fail(PC_ERR_INVALID_ARG, "pseudocount must be >= 0");
+    DeviceGuard dg(h->device);
+    EmArgs a{};
+    a.nsegs = (int)h->rowsegs.size();
+    a.segs = h->d_rowsegs;
+    a.params = params;
+    a.pflows = param_flows;
+    a.step = step_size;
+    a.pseudo = pseudocount;
+    hipStream_t s = (hipStream_t)stream;
+    Timed t(h, KK_EM, s);
+    launch_em(a, h->total_rows, s);
+    check_launch();
+    return PC_OK;
+  } catch (const Error& e) {
+    return set_error(e.code, e.msg);
+  }
+}
+
+int pc_set_timing(pc_handle hh, int enable) {
+  try {
+    Handle* h = checked(hh);
+    h->timing = enable != 0;
+    h->events_used = 0;
+    return PC_OK;
+  } catch (const Error& e) {
+    return set_error(e.code, e.msg);
+  }
+}
+
+int pc_kernel_times(pc_handle hh, int64_t* launches, double* ms) {
+  try {
+    Handle* h = checked(hh);
+    if (!launches || !ms) fail(PC_ERR_INVALID_ARG, "null output arrays");
+    for (int k = 0; k < PC_NUM_KERNEL_KINDS; ++k) {
+      launches[k] = 0;
+      ms[k] = 0.0;
+    }
+    for (size_t i = 0; i < h->events_used; ++i) {
+      const Handle::Ev& ev = h->events[i];
+      HIPCHECK(hipEventSynchronize((hipEvent_t)ev.stop));
+      float t = 0.0f;
+      HIPCHECK(hipEventElapsedTime(&t, (hipEvent_t)ev.start, (hipEvent_t)ev.stop));
+      launches[ev.kind] += 1;
+      ms[ev.kind] += t;
+    }
+    h->events_used = 0;
+    return PC_OK;
+  } catch (const Error& e) {
+    return set_error(e.code, e.msg);
+  }
+}
+
+}  // extern "C"

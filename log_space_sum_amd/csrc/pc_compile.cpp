@@ -1,0 +1,453 @@
+// pc_compile.cpp -- host-side layout compiler.
+//
+// Checks a circuit descriptor, classifies every sum layer after the PyJuice
+// pull request #62, Summary item 2 (layers whose blocks share their children
+// are exponentiated once; evenly strided groups run as one batched product;
+// anything else is a general block-sparse layer), finds tied weight blocks,
+// and plans where every operand lives in the workspace and how the backward
+// pass writes element flows (first writer stores, later writers add; several
+// groups sharing a child go through a scratch buffer and a fixed-order
+// reduction, so the flows are deterministic).
+#include <algorithm>
+#include <map>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "pc_host.h"
+
+namespace pc {
+
+[[noreturn]] void fail(int code, const std::string& msg) { throw Error{code, msg}; }
+
+static void need(bool ok, const std::string& msg) {
+  if (!ok) fail(PC_ERR_INVALID_ARG, msg);
+}
+
+static std::string L(int i) { return "layer " + std::to_string(i) + ": "; }
+
+Handle* compile_layout(const pc_circuit_desc* d) {
+  need(d != nullptr, "null descriptor");
+  need(d->num_nodes >= 1, "num_nodes must be >= 1");
+  need(d->num_vars >= 0, "num_vars must be >= 0");
+  need(d->num_params >= 0, "num_params must be >= 0");
+  need(d->num_layers >= 1 && d->layers != nullptr, "need at least one layer");
+  need(d->root >= -1 && d->root < d->num_nodes, "root out of range");
+  if (d->lowrank_rank < 0 || d->lowrank_rank > 64)
+    fail(PC_ERR_UNSUPPORTED, "LowRank rank must be in 1..64 (the fused exp_sum kernels)");
+
+  Handle* h = new Handle();
+  h->num_nodes = d->num_nodes;
+  h->num_vars = d->num_vars;
+  h->num_params = d->num_params;
+  h->root = d->root;
+  h->lowrank_rank = d->lowrank_rank;
+  const int64_t NN = d->num_nodes;
+
+  std::vector<int32_t> defined_at(NN, -1);
+  std::vector<int32_t> last_parent(NN, -1);     // last layer (topological) using the node as a child
+  std::vector<int32_t> stamp(NN, -1);
+  int stamp_id = 0;
+
+  auto define = [&](int li, int64_t s, int64_t n) {
+    need(n >= 0 && s >= 0 && s + n <= NN, L(li) + "node range out of bounds");
+    for (int64_t i = s; i < s + n; ++i) {
+      need(defined_at[i] < 0, L(li) + "node " + std::to_string(i) + " defined twice");
+      defined_at[i] = li;
+    }
+  };
+  auto use = [&](int li, int64_t c) {
+    need(c >= 0 && c < NN, L(li) + "child id out of range");
+    need(defined_at[c] >= 0 && defined_at[c] < li,
+         L(li) + "child " + std::to_string(c) + " not defined by an earlier layer");
+    last_parent[c] = li;
+  };
+  auto param_range = [&](int li, int64_t off, int64_t len) {
+    need(off >= 0 && len >= 0 && off + len <= d->num_params, L(li) + "parameters out of range");
+  };
+
+  // ---- pass 1: check every layer, build per-kind plans ----------------------
+  std::map<int64_t, std::pair<int32_t, int32_t>> block_shape;   // param_offset -> (M, N)
+  std::map<int64_t, int> block_id;
+  std::vector<std::pair<int64_t, int64_t>> param_intervals;      // distinct [off, off+len)
+  std::map<int64_t, std::pair<int32_t, int32_t>> table_shape;   // input tables
+  int lowrank_slots = 0;
+
+  for (int li = 0; li < d->num_layers; ++li) {
+    const pc_layer_desc& ly = d->layers[li];
+    LayerRef ref{ly.kind, -1};
+    if (ly.kind == PC_LAYER_INPUT_CAT) {
+      need(ly.num_nodes >= 1 && ly.num_cats >= 1 && ly.num_rows >= 1, L(li) + "empty input layer");
+      need(ly.var && ly.row, L(li) + "null var/row");
+      need(d->num_vars >= 1, L(li) + "categorical input needs num_vars >= 1");
+      define(li, ly.node_start, ly.num_nodes);
+      param_range(li, ly.param_offset, (int64_t)ly.num_rows * ly.num_cats);
+      InputPlan ip;
+      ip.layer = li;
+      ip.node_start = ly.node_start;
+      ip.num_nodes = ly.num_nodes;
+      ip.num_cats = ly.num_cats;
+      ip.num_rows = ly.num_rows;
+      ip.param_offset = ly.param_offset;
+      ip.var.assign(ly.var, ly.var + ly.num_nodes);
+      ip.row.assign(ly.row, ly.row + ly.num_nodes);
+      for (int32_t i = 0; i < ly.num_nodes; ++i) {
+        need(ip.var[i] >= 0 && ip.var[i] < d->num_vars, L(li) + "var out of range");
+        need(ip.row[i] >= 0 && ip.row[i] < ly.num_rows, L(li) + "row out of range");
+      }
+      // row -> nodes CSR (ascending node order)
+      ip.row_ptr.assign(ly.num_rows + 1, 0);
+      for (int32_t i = 0; i < ly.num_nodes; ++i) ip.row_ptr[ip.row[i] + 1]++;
+      for (int32_t r = 0; r < ly.num_rows; ++r) ip.row_ptr[r + 1] += ip.row_ptr[r];
+      ip.row_nodes.assign(ly.num_nodes, 0);
+      std::vector<int32_t> fillp(ip.row_ptr.begin(), ip.row_ptr.end() - 1);
+      for (int32_t i = 0; i < ly.num_nodes; ++i) ip.row_nodes[fillp[ip.row[i]]++] = ly.node_start + i;
+      auto it = table_shape.find(ly.param_offset);
+      if (it == table_shape.end()) {
+        table_shape[ly.param_offset] = {ly.num_rows, ly.num_cats};
+        param_intervals.push_back({ly.param_offset, ly.param_offset + (int64_t)ly.num_rows * ly.num_cats});
+      } else {
+        need(it->second == std::make_pair(ly.num_rows, ly.num_cats),
+             L(li) + "input tables sharing parameters differ in shape");
+      }
+      h->max_cats = std::max(h->max_cats, ly.num_cats);
+      ref.idx = (int)h->inputs.size();
+      h->inputs.push_back(std::move(ip));
+    } else if (ly.kind == PC_LAYER_INPUT_EXTERNAL) {
+      need(ly.num_nodes >= 1, L(li) + "empty external layer");
+      define(li, ly.node_start, ly.num_nodes);
+    } else if (ly.kind == PC_LAYER_PRODUCT) {
+      need(ly.num_nodes >= 1 && ly.ch_ptr && ly.ch_ids, L(li) + "empty product layer");
+      need(ly.ch_ptr[0] == 0, L(li) + "ch_ptr[0] must be 0");
+      for (int32_t i = 0; i < ly.num_nodes; ++i)
+        need(ly.ch_ptr[i + 1] > ly.ch_ptr[i], L(li) + "product node without children");
+      ProductPlan pp;
+      pp.layer = li;
+      pp.node_start = ly.node_start;
+      pp.num_nodes = ly.num_nodes;
+      pp.ch_ptr.assign(ly.ch_ptr, ly.ch_ptr + ly.num_nodes + 1);
+      pp.ch_ids.assign(ly.ch_ids, ly.ch_ids + ly.ch_ptr[ly.num_nodes]);
+      for (int32_t c : pp.ch_ids) use(li, c);
+      define(li, ly.node_start, ly.num_nodes);
+      // parent CSR over distinct children
+      std::vector<std::pair<int32_t, int32_t>> cp;
+      cp.reserve(pp.ch_ids.size());
+      for (int32_t i = 0; i < ly.num_nodes; ++i)
+        for (int32_t k = pp.ch_ptr[i]; k < pp.ch_ptr[i + 1]; ++k) cp.push_back({pp.ch_ids[k], ly.node_start + i});
+      std::sort(cp.begin(), cp.end());
+      pp.pptr.push_back(0);
+      for (size_t k = 0; k < cp.size(); ++k) {
+        if (k == 0 || cp[k].first != cp[k - 1].first) {
+          if (k) pp.pptr.push_back((int32_t)k);
+          pp.uchild.push_back(cp[k].first);
+        }
+        pp.parents.push_back(cp[k].second);
+      }
+      pp.pptr.push_back((int32_t)cp.size());
+      ref.idx = (int)h->prods.size();
+      h->prods.push_back(std::move(pp));
+    } else if (ly.kind == PC_LAYER_SUM) {
+      need(ly.num_groups >= 1 && ly.groups, L(li) + "empty sum layer");
+      SumPlan sp;
+      sp.layer = li;
+      int n_lr = 0;
+      for (int32_t g = 0; g < ly.num_groups; ++g) {
+        const pc_sum_group& G = ly.groups[g];
+        std::string gs = L(li) + "group " + std::to_string(g) + ": ";
+        need(G.num_nodes >= 1 && G.num_ch_blocks >= 1 && G.ch_block_size >= 1 && G.ch_block_start,
+             gs + "empty group");
+        int64_t N = (int64_t)G.num_ch_blocks * G.ch_block_size;
+        need(N <= (1 << 30) && G.num_nodes <= (1 << 30), gs + "group too large");
+        ++stamp_id;
+        for (int32_t k = 0; k < G.num_ch_blocks; ++k) {
+          int64_t s = G.ch_block_start[k];
+          need(s >= 0 && s + G.ch_block_size <= NN, gs + "child block out of range");
+          for (int64_t c = s; c < s + G.ch_block_size; ++c) {
+            use(li, c);
+            need(stamp[c] != stamp_id, gs + "child " + std::to_string(c) + " listed twice");
+            stamp[c] = stamp_id;
+          }
+        }
+        param_range(li, G.param_offset, (int64_t)G.num_nodes * N);
+        need(G.lowrank_slot >= -1, gs + "bad lowrank slot");
+        if (G.lowrank_slot >= 0) {
+          if (d->lowrank_rank < 1) fail(PC_ERR_UNSUPPORTED, gs + "LowRank group needs lowrank_rank in 1..64");
+          ++n_lr;
+          lowrank_slots = std::max(lowrank_slots, G.lowrank_slot + 1);
+        }
+        auto it = block_shape.find(G.param_offset);
+        if (it == block_shape.end()) {
+          block_shape[G.param_offset] = {G.num_nodes, (int32_t)N};
+          param_intervals.push_back({G.param_offset, G.param_offset + (int64_t)G.num_nodes * N});
+        } else {
+          need(it->second == std::make_pair(G.num_nodes, (int32_t)N), gs + "tied groups differ in shape");
+        }
+        GroupRec r{};
+        r.out_start = G.out_start;
+        r.M = G.num_nodes;
+        r.N = (int32_t)N;
+        r.cbs = G.ch_block_size;
+        r.blk_off = (int32_t)sp.blocks.size();
+        r.nblk = G.num_ch_blocks;
+        r.param_offset = G.param_offset;
+        r.lowrank = G.lowrank_slot;
+        sp.blocks.insert(sp.blocks.end(), G.ch_block_start, G.ch_block_start + G.num_ch_blocks);
+        sp.groups.push_back(r);
+      }
+      need(n_lr == 0 || n_lr == ly.num_groups, L(li) + "a sum layer is either all LowRank or none");
+      sp.lowrank = n_lr > 0;
+      for (auto& r : sp.groups) define(li, r.out_start, r.M);
+      ref.idx = (int)h->sums.size();
+      h->sums.push_back(std::move(sp));
+    } else {
+      fail(PC_ERR_INVALID_ARG, L(li) + "unknown layer kind");
+    }
+    h->layers.push_back(ref);
+  }
+  for (int64_t i = 0; i < NN; ++i) need(defined_at[i] >= 0, "node " + std::to_string(i) + " is not defined");
+  h->lowrank_slots = lowrank_slots;
+
+  // distinct parameter blocks must not overlap
+  std::sort(param_intervals.begin(), param_intervals.end());
+  for (size_t k = 1; k < param_intervals.size(); ++k)
+    need(param_intervals[k].first >= param_intervals[k - 1].second, "parameter blocks overlap");
+
+  // ---- pass 2: sum-layer classification and operand placement -------------
+  int64_t e_rows = 0, g_rows = 0, s_rows = 0;
+  int32_t m_rows = 0;
+  for (auto& sp : h->sums) {
+    const int G = (int)sp.groups.size();
+    auto same_children = [&](const GroupRec& a, const GroupRec& b) {
+      if (a.cbs != b.cbs || a.nblk != b.nblk) return false;
+      for (int k = 0; k < a.nblk; ++k)
+        if (sp.blocks[a.blk_off + k] != sp.blocks[b.blk_off + k]) return false;
+      return true;
+    };
+    bool shared = true;
+    for (int g = 1; g < G; ++g) shared = shared && same_children(sp.groups[0], sp.groups[g]);
+    bool strided = G >= 2;
+    if (strided) {
+      const GroupRec& a = sp.groups[0];
+      const GroupRec& b = sp.groups[1];
+      int64_t d_out = b.out_start - a.out_start;
+      int64_t d_ch = (int64_t)sp.blocks[b.blk_off] - sp.blocks[a.blk_off];
+      int64_t d_par = b.param_offset - a.param_offset;
+      for (int g = 0; g < G && strided; ++g) {
+        const GroupRec& c = sp.groups[g];
+        strided = c.M == a.M && c.N == a.N && c.nblk == 1 &&
+                  c.out_start == a.out_start + g * d_out &&
+                  sp.blocks[c.blk_off] == sp.blocks[a.blk_off] + g * d_ch &&
+                  c.param_offset == a.param_offset + g * d_par;
+      }
+      strided = strided && d_ch != 0;
+    }
+    sp.cls = sp.lowrank ? PC_CLASS_LOWRANK : shared ? PC_CLASS_SHARED : strided ? PC_CLASS_STRIDED : PC_CLASS_GENERAL;
+
+    // overlap: does any child belong to two groups of this layer?
+    ++stamp_id;
+    sp.overlap = false;
+    for (auto& r : sp.groups)
+      for (int k = 0; k < r.nblk && !sp.overlap; ++k)
+        for (int64_t c = sp.blocks[r.blk_off + k]; c < sp.blocks[r.blk_off + k] + r.cbs; ++c) {
+          if (stamp[c] == stamp_id) { sp.overlap = true; break; }
+          stamp[c] = stamp_id;
+        }
+
+    int32_t ekoff = 0, gkoff = 0, mt = 0, ct = 0, pk = 0, pg = 0, srow = 0;
+    for (int g = 0; g < G; ++g) {
+      GroupRec& r = sp.groups[g];
+      r.share_src = (sp.cls == PC_CLASS_SHARED) ? 0 : g;
+      const int64_t Mp = round_up(r.M, ROW_PAD), Np = round_up(r.N, ROW_PAD);
+      const int64_t MpK = round_up(r.M, K_PAD), NpK = round_up(r.N, K_PAD);
+      auto bit = block_id.find(r.param_offset);
+      if (bit == block_id.end()) {
+        int id = (int)h->blocks.size();
+        block_id[r.param_offset] = id;
+        BlockRec b{};
+        b.param_offset = r.param_offset;
+        b.M = r.M;
+        b.N = r.N;
+        h->blocks.push_back(b);
+        r.block = id;
+      } else {
+        r.block = bit->second;
+      }
+      if (r.share_src == g) {
+        r.m_row = m_rows++;
+        r.e_koff = ekoff;
+        ekoff += (int32_t)NpK;
+        r.pk_start = pk;
+        pk += (int32_t)(Np / 64);
+        r.e_row = sp.lowrank ? -1 : e_rows;
+        if (!sp.lowrank) e_rows += Np;
+      } else {
+        const GroupRec& s = sp.groups[r.share_src];
+        r.m_row = s.m_row;
+        r.e_koff = s.e_koff;
+        r.pk_start = pk;          // empty range: packing kernels skip shared copies
+        r.e_row = s.e_row;
+      }
+      r.s_row = sp.lowrank ? -1 : s_rows;
+      if (!sp.lowrank) s_rows += r.M;
+      r.g_koff = gkoff;
+      gkoff += (int32_t)MpK;
+      r.g_row = sp.lowrank ? -1 : g_rows;
+      if (!sp.lowrank) g_rows += Mp;
+      r.mt_start = mt;
+      mt += (int32_t)(Mp / ROW_PAD);
+      r.ct_start = ct;
+      ct += (int32_t)(Np / ROW_PAD);
+      r.pg_start = pg;
+      pg += (int32_t)(Mp / 64);
+      if (sp.overlap) {
+        r.scratch_row = srow;
+        srow += r.N;
+      } else {
+        r.scratch_row = -1;
+      }
+    }
+    sp.ebt_cols = ekoff;
+    sp.gbt_cols = gkoff;
+    sp.mtiles = mt;
+    sp.ctiles = ct;
+    sp.pktiles = pk;
+    sp.pgtiles = pg;
+    sp.scratch_rows = srow;
+    h->max_ebt_cols = std::max(h->max_ebt_cols, ekoff);
+    h->max_gbt_cols = std::max(h->max_gbt_cols, gkoff);
+    h->max_scratch_rows = std::max(h->max_scratch_rows, srow);
+    if (!sp.lowrank) h->has_plain_sums = true;
+
+    if (sp.overlap) {   // reduction CSR: distinct child -> scratch rows (group order)
+      std::vector<std::pair<int32_t, int32_t>> cs;
+      for (auto& r : sp.groups)
+        for (int k = 0; k < r.nblk; ++k)
+          for (int j = 0; j < r.cbs; ++j)
+            cs.push_back({sp.blocks[r.blk_off + k] + j, r.scratch_row + k * r.cbs + j});
+      std::stable_sort(cs.begin(), cs.end(),
+                       [](const std::pair<int32_t, int32_t>& a, const std::pair<int32_t, int32_t>& b) {
+                         return a.first < b.first;
+                       });
+      sp.red_ptr.push_back(0);
+      for (size_t k = 0; k < cs.size(); ++k) {
+        if (k == 0 || cs[k].first != cs[k - 1].first) {
+          if (k) sp.red_ptr.push_back((int32_t)k);
+          sp.red_child.push_back(cs[k].first);
+        }
+        sp.red_src.push_back(cs[k].second);
+      }
+      sp.red_ptr.push_back((int32_t)cs.size());
+    }
+  }
+  h->earena_rows = e_rows;
+  h->s_rows = s_rows;
+  h->garena_rows = g_rows;
+  h->m_rows = m_rows;
+
+  // copies of each block, in layer order
+  {
+    std::vector<std::vector<CopyRec>> per(h->blocks.size());
+    std::vector<bool> plain(h->blocks.size(), false);
+    for (auto& sp : h->sums)
+      for (auto& r : sp.groups) {
+        if (sp.lowrank) continue;
+        per[r.block].push_back(CopyRec{r.e_row, r.g_row});
+        plain[r.block] = true;
+      }
+    int64_t th = 0, tht = 0;
+    int32_t pk = 0, pt = 0;
+    for (size_t b = 0; b < h->blocks.size(); ++b) {
+      BlockRec& B = h->blocks[b];
+      B.copy_off = (int32_t)h->copies.size();
+      B.ncopies = (int32_t)per[b].size();
+      h->copies.insert(h->copies.end(), per[b].begin(), per[b].end());
+      const int64_t Mp = round_up(B.M, ROW_PAD), Np = round_up(B.N, ROW_PAD);
+      const int64_t MpK = round_up(B.M, K_PAD), NpK = round_up(B.N, K_PAD);
+      B.pk_start = pk;
+      B.pt_start = pt;
+      if (plain[b]) {
+        B.th_off = th;
+        th += Mp * NpK;
+        B.tht_off = tht;
+        tht += Np * MpK;
+        pk += (int32_t)((Mp / 64) * (Np / 64));
+        pt += (int32_t)((Mp / ROW_PAD) * (Np / ROW_PAD));
+      } else {
+        B.th_off = B.tht_off = -1;
+      }
+    }
+    h->theta_elems = th;
+    h->thetaT_elems = tht;
+    h->pk_block_tiles = pk;
+    h->param_tiles = pt;
+  }
+
+  // EM row segments: every distinct block and input table
+  {
+    std::map<int64_t, RowSeg> segs;
+    for (auto& B : h->blocks) segs[B.param_offset] = RowSeg{B.param_offset, B.M, B.N, 0, 0};
+    for (auto& kv : table_shape) segs[kv.first] = RowSeg{kv.first, kv.second.first, kv.second.second, 0, 0};
+    int32_t rows = 0;
+    for (auto& kv : segs) {
+      RowSeg s = kv.second;
+      s.row_start = rows;
+      rows += s.nrows;
+      h->rowsegs.push_back(s);
+    }
+    h->total_rows = rows;
+  }
+
+  // ---- pass 3: element-flow write plan --------------------------------------
+  // A layer stores (instead of adding) the flows of its children when it is
+  // the first writer of each of them in reverse order, i.e. the last layer in
+  // topological order that uses them.  Children whose first writer adds are
+  // cleared before the backward starts.
+  std::vector<char> zero(NN, 0);
+  for (auto& pp : h->prods) {
+    bool st = true;
+    for (int32_t c : pp.uchild) st = st && last_parent[c] == pp.layer;
+    pp.store = st;
+    if (!st)
+      for (int32_t c : pp.uchild)
+        if (last_parent[c] == pp.layer) zero[c] = 1;
+  }
+  for (auto& sp : h->sums) {
+    bool st = true;
+    for (auto& r : sp.groups)
+      for (int k = 0; k < r.nblk; ++k)
+        for (int j = 0; j < r.cbs; ++j) st = st && last_parent[sp.blocks[r.blk_off + k] + j] == sp.layer;
+    sp.store = st;
+    if (!st)
+      for (auto& r : sp.groups)
+        for (int k = 0; k < r.nblk; ++k)
+          for (int j = 0; j < r.cbs; ++j) {
+            int32_t c = sp.blocks[r.blk_off + k] + j;
+            if (last_parent[c] == sp.layer) zero[c] = 1;
+          }
+  }
+  for (int64_t i = 0; i < NN; ++i)
+    if (last_parent[i] < 0) h->outputs.push_back((int32_t)i);
+  // runs of cleared nodes
+  for (int64_t i = 0; i < NN;) {
+    if (!zero[i]) { ++i; continue; }
+    int64_t j = i;
+    while (j < NN && zero[j]) ++j;
+    h->zero_ranges.push_back(FillRange{(int32_t)i, (int32_t)(j - i), 0.0f, 0});
+    h->max_zero_count = std::max<int64_t>(h->max_zero_count, j - i);
+    i = j;
+  }
+  // seeds without caller seeds: the root gets 1, every other output 0
+  for (size_t k = 0; k < h->outputs.size();) {
+    size_t q = k;
+    while (q + 1 < h->outputs.size() && h->outputs[q + 1] == h->outputs[q] + 1 &&
+           h->outputs[q + 1] != h->root && h->outputs[k] != h->root)
+      ++q;
+    const int32_t s0 = h->outputs[k], n = (int32_t)(q - k + 1);
+    h->seed_ranges.push_back(FillRange{s0, n, (s0 == h->root) ? 1.0f : 0.0f, 0});
+    h->max_seed_count = std::max<int64_t>(h->max_seed_count, n);
+    k = q + 1;
+  }
+  return h;
+}
+
+}  // namespace pc

@@ -1,0 +1,100 @@
+// pc_device.h -- records and argument blocks shared by the host runtime and
+// the gfx950 kernels.  Every table here is batch-independent: offsets that
+// scale with the batch are stored in rows (or columns) and multiplied by the
+// batch-dependent strides passed as kernel arguments.
+#pragma once
+#include <stdint.h>
+
+namespace pc {
+
+// Padding of every bfloat16 operand kept in the workspace: rows (the M / N
+// dimensions of the products) to ROW_PAD, the contraction dimension to K_PAD.
+// Operands are therefore tile-aligned and the product kernels need no bounds
+// checks in their main loop; pads hold zeros.
+constexpr int ROW_PAD = 128;
+constexpr int K_PAD = 64;
+
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// One sum group (node block) of a sum layer.
+struct GroupRec {
+  int32_t out_start;     // first output node
+  int32_t M;             // number of sum nodes
+  int32_t N;             // number of children
+  int32_t cbs;           // child block size
+  int32_t blk_off;       // first entry of this group's child-block starts in the layer's block array
+  int32_t nblk;          // number of child blocks
+  int64_t param_offset;  // row-major [M, N] weights
+  int32_t block;         // distinct weight block id
+  int32_t m_row;         // row of the per-sample column-max keys
+  int32_t e_koff;        // column offset of the group's slice of the layer's batch-major E
+  int32_t g_koff;        // column offset of the group's slice of the layer's batch-major G
+  int64_t e_row;         // first row of the group's node-major E (kept for parameter flows)
+  int64_t g_row;         // first row of the group's node-major G (kept for parameter flows)
+  int32_t mt_start;      // prefix of output-row tiles over the layer's groups (forward)
+  int32_t ct_start;      // prefix of child-row tiles over the layer's groups (element flows)
+  int32_t pk_start;      // prefix of 64-row child tiles over the layer's groups (column max, exp)
+  int32_t pg_start;      // prefix of 64-row output tiles over the layer's groups (scaled flows)
+  int32_t scratch_row;   // first row in the element-flow scratch (-1: write node flows directly)
+  int32_t lowrank;       // LowRank slot or -1
+  int32_t share_src;     // group whose E slice this group reuses (SHARED layers), or itself
+  int64_t s_row;         // first row of the group's scaled sums S (kept from the forward), -1 if none
+};
+
+// One distinct weight block (tied copies share it).
+struct BlockRec {
+  int64_t param_offset;
+  int32_t M, N;
+  int64_t th_off;        // element offset of the [M_pad, N_padK] split weights (forward operand)
+  int64_t tht_off;       // element offset of the [N_pad, M_padK] transposed split weights (element flows)
+  int32_t ncopies;
+  int32_t copy_off;      // first entry in the copy table
+  int32_t pk_start;      // prefix of 64x64 packing tiles over blocks
+  int32_t pt_start;      // prefix of product tiles over blocks (parameter flows)
+};
+
+// One tied copy of a block: where its kept operands live.
+struct CopyRec {
+  int64_t e_row;
+  int64_t g_row;
+};
+
+// Parameter row run normalised by EM.
+struct RowSeg {
+  int64_t offset;
+  int32_t nrows;
+  int32_t rlen;
+  int32_t row_start;     // prefix of rows over segments
+  int32_t pad_;
+};
+
+// Node range [start, start + count) with one fill value (flow seeding).
+struct FillRange {
+  int32_t start;
+  int32_t count;
+  float value;
+  int32_t pad_;
+};
+
+// Batch-dependent strides and bases of the workspace, filled per call.
+struct WsView {
+  uint16_t* theta;      // split weights arena (planes at theta + p * theta_plane)
+  uint16_t* thetaT;
+  int64_t theta_plane, thetaT_plane;
+  uint16_t* ebt;        // batch-major E of the current layer [B_pad, ebt_cols] per plane
+  uint16_t* gbt;        // batch-major G of the current layer [B_pad, gbt_cols] per plane
+  int64_t ebt_plane, gbt_plane;
+  int32_t ebt_cols, gbt_cols;
+  uint16_t* earena;     // node-major E rows [rows, B_padK] per plane (kept)
+  uint16_t* garena;     // node-major G rows [rows, B_padK] per plane (kept)
+  int64_t earena_plane, garena_plane;
+  uint32_t* mkeys;      // [m_rows, B] order-preserving keys of the column maxima
+  float* ssum;          // [s_rows, B] scaled sums S = sum_j theta e of every plain sum node
+  float* scratch;       // [rows, B] element-flow contributions of overlapping layers
+  int32_t* tokT;        // [num_vars, B] tokens transposed
+  int32_t* bucket_ptr;  // [num_vars, K_max + 1]
+  int32_t* bucket_idx;  // [num_vars, B]
+  int32_t B, B_pad, B_padK;
+};
+
+}  // namespace pc

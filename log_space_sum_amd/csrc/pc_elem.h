@@ -1,0 +1,95 @@
+// pc_elem.h -- argument blocks and launchers of the memory-bound kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "pc_device.h"
+
+namespace pc {
+
+struct InputArgs {
+  int32_t B, node_start, num_nodes, K, num_rows, Kmax;
+  int64_t param_offset;
+  const int32_t* var;
+  const int32_t* row;
+  const int32_t* row_ptr;
+  const int32_t* row_nodes;
+  const int32_t* tokT;
+  const int32_t* bptr;
+  const int32_t* bidx;
+  const float* params;
+  float* vals;
+  const float* flows;
+  float* pflows;
+};
+
+struct ProdArgs {
+  int32_t B, node_start, num_nodes, nuniq, store;
+  const int32_t* ch_ptr;
+  const int32_t* ch_ids;
+  const int32_t* uchild;
+  const int32_t* pptr;
+  const int32_t* parents;
+  float* vals;
+  float* flows;
+};
+
+struct SumArgs {
+  int32_t B, B_pad, B_padK, btiles, ngroups;
+  const GroupRec* groups;
+  const int32_t* chblocks;
+  const float* vals;
+  const float* flows;
+  uint32_t* mkeys;
+  const float* ssum;
+  // packed outputs: node-major ("direct", rows x B_padK) and batch-major ("trans")
+  uint16_t* direct;
+  int64_t direct_plane;
+  int32_t np_direct;
+  uint16_t* trans;
+  int64_t trans_plane;
+  int32_t trans_cols, np_trans;
+  // overlapping-children reduction
+  int32_t nuniq, store;
+  const int32_t* red_child;
+  const int32_t* red_ptr;
+  const int32_t* red_src;
+  const float* scratch;
+  float* out_flows;
+};
+
+struct ThetaArgs {
+  int32_t nblocks, np_fwd, np_elem;
+  const BlockRec* blocks;
+  const float* params;
+  uint16_t* theta;
+  int64_t theta_plane;
+  uint16_t* thetaT;
+  int64_t thetaT_plane;
+};
+
+struct EmArgs {
+  int32_t nsegs;
+  const RowSeg* segs;
+  float* params;
+  const float* pflows;
+  float step, pseudo;
+};
+
+void launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
+void launch_fill_ranges(float* flows, const FillRange* d_ranges, int nranges, int64_t max_count, int B,
+                        hipStream_t s);
+void launch_copy_row(const float* src, float* dst, int B, hipStream_t s);
+void launch_tokens_t(const int32_t* tok, int32_t* tokT, int B, int V, hipStream_t s);
+void launch_input_fwd(const InputArgs& a, hipStream_t s);
+void launch_bucket(const int32_t* tokT, int V, int B, int Kmax, int32_t* bptr, int32_t* bidx, hipStream_t s);
+void launch_input_bwd(const InputArgs& a, hipStream_t s);
+void launch_prod_fwd(const ProdArgs& a, hipStream_t s);
+void launch_prod_bwd(const ProdArgs& a, hipStream_t s);
+void launch_colmax(const SumArgs& a, int tiles, hipStream_t s);
+void launch_exp_pack(const SumArgs& a, int tiles, hipStream_t s);
+void launch_g_pack(const SumArgs& a, int tiles, hipStream_t s);
+void launch_theta_pack(const ThetaArgs& a, int tiles, hipStream_t s);
+void launch_elem_reduce(const SumArgs& a, hipStream_t s);
+void launch_em(const EmArgs& a, int rows, hipStream_t s);
+
+}  // namespace pc

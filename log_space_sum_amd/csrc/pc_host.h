@@ -1,0 +1,140 @@
+// pc_host.h -- the compiled layout held by a pc_handle, and the host-side
+// helpers shared by the layout compiler, the pass scheduler and the kernel
+// launchers.
+#pragma once
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/pc.h"
+#include "pc_device.h"
+
+namespace pc {
+
+// Error raised inside the library; converted to a status code at the C ABI.
+struct Error {
+  int code;
+  std::string msg;
+};
+[[noreturn]] void fail(int code, const std::string& msg);
+
+// Product kinds whose operand split is configurable.
+enum GemmKind { GK_FWD = 0, GK_ELEM = 1, GK_PARAM = 2 };
+
+struct InputPlan {
+  int layer;
+  int32_t node_start, num_nodes, num_cats, num_rows;
+  int64_t param_offset;
+  std::vector<int32_t> var, row;
+  std::vector<int32_t> row_ptr, row_nodes;  // row -> nodes using it (ascending)
+  int32_t* d_var = nullptr;
+  int32_t* d_row = nullptr;
+  int32_t* d_row_ptr = nullptr;
+  int32_t* d_row_nodes = nullptr;
+};
+
+struct ProductPlan {
+  int layer;
+  int32_t node_start, num_nodes;
+  std::vector<int32_t> ch_ptr, ch_ids;
+  std::vector<int32_t> uchild, pptr, parents;  // distinct children, their parents (CSR)
+  bool store = false;                          // flows: first writer of every child
+  int32_t* d_ch_ptr = nullptr;
+  int32_t* d_ch_ids = nullptr;
+  int32_t* d_uchild = nullptr;
+  int32_t* d_pptr = nullptr;
+  int32_t* d_parents = nullptr;
+};
+
+struct SumPlan {
+  int layer;
+  int cls;
+  std::vector<GroupRec> groups;
+  std::vector<int32_t> blocks;                 // concatenated child-block starts
+  bool overlap = false;                        // a child is used by several groups
+  bool store = false;                          // flows: first writer of every child
+  bool lowrank = false;
+  int32_t ebt_cols = 0, gbt_cols = 0;          // widths of the batch-major operands
+  int32_t mtiles = 0, ctiles = 0;              // 128-row tiles over outputs / children
+  int32_t pktiles = 0, pgtiles = 0;            // 64-row tiles over source children / outputs
+  int32_t scratch_rows = 0;
+  std::vector<int32_t> red_child, red_ptr, red_src;   // overlap reduction CSR
+  GroupRec* d_groups = nullptr;
+  int32_t* d_blocks = nullptr;
+  int32_t* d_red_child = nullptr;
+  int32_t* d_red_ptr = nullptr;
+  int32_t* d_red_src = nullptr;
+};
+
+struct LayerRef {
+  int kind;
+  int idx;   // index into inputs / prods / sums (-1 for external)
+};
+
+struct Handle {
+  int device = -1;
+  int mode = PC_PREC_AUTO;
+  // planes[mode][gemm kind][0: first operand, 1: second operand]
+  int planes[2][3][2] = {{{1, 1}, {2, 1}, {2, 1}}, {{3, 3}, {3, 3}, {3, 3}}};
+  int32_t num_nodes = 0, num_vars = 0, root = -1, lowrank_rank = 0;
+  int64_t num_params = 0;
+  std::vector<LayerRef> layers;
+  std::vector<InputPlan> inputs;
+  std::vector<ProductPlan> prods;
+  std::vector<SumPlan> sums;
+  std::vector<BlockRec> blocks;
+  std::vector<CopyRec> copies;
+  int32_t pk_block_tiles = 0;          // 64x64 tiles over all blocks (weight split)
+  int32_t param_tiles = 0;             // 128x128 tiles over all blocks (parameter flows)
+  int64_t theta_elems = 0, thetaT_elems = 0;
+  int64_t earena_rows = 0, garena_rows = 0, s_rows = 0;
+  int32_t m_rows = 0;
+  int32_t max_ebt_cols = 0, max_gbt_cols = 0, max_scratch_rows = 0;
+  int32_t max_cats = 0;
+  int32_t lowrank_slots = 0;
+  std::vector<RowSeg> rowsegs;
+  int32_t total_rows = 0;
+  std::vector<int32_t> outputs;
+  std::vector<FillRange> zero_ranges;   // flows cleared before the backward
+  std::vector<FillRange> seed_ranges;   // output flows without caller seeds: root 1, others 0
+  int64_t max_zero_count = 0, max_seed_count = 0;
+  bool has_plain_sums = false;
+  // device copies of handle-wide tables
+  BlockRec* d_blocks = nullptr;
+  CopyRec* d_copies = nullptr;
+  RowSeg* d_rowsegs = nullptr;
+  FillRange* d_zero = nullptr;
+  FillRange* d_seed = nullptr;
+  // timing
+  bool timing = false;
+  struct Ev {
+    int kind;
+    void* start;
+    void* stop;
+  };
+  std::vector<Ev> events;
+  size_t events_used = 0;
+};
+
+// Layout compiler (host only).
+Handle* compile_layout(const pc_circuit_desc* d);
+// Upload the handle's index tables to `device`.
+void upload_tables(Handle* h, int device);
+void free_tables(Handle* h);
+
+// Effective precision mode for a batch (batches below 16 run fp32-level).
+inline int effective_mode(const Handle* h, int B) { return B < 16 ? PC_PREC_FP32 : h->mode; }
+
+// Workspace plan for a batch: byte offsets of every region.
+struct WsPlan {
+  int B, B_pad, B_padK, mode;
+  int pl[3][2];
+  size_t theta, thetaT, ebt, gbt, earena, garena, mkeys, ssum, scratch, tokT, bptr, bidx, lowrank;
+  size_t lowrank_bytes;
+  size_t total;
+};
+WsPlan plan_workspace(const Handle* h, int B);
+WsView make_view(const Handle* h, const WsPlan& p, void* ws);
+
+}  // namespace pc

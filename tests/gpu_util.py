@@ -1,0 +1,237 @@
+"""Helpers of the GPU parity tests: run a workload through the C ABI (via the
+binding) and through the float64 oracle, and compare them element by element
+with the stated tolerances.
+
+Tolerances (the stated accuracy bar of the two precision modes):
+  node values / log-likelihood:  fp32-level |x - x*| <= 2e-6 |x*|;  auto (bf16) <= 1e-2 absolute
+  element and parameter flows:   fp32-level 1e-5 relative;           auto 5e-3 relative
+A relative comparison uses max(|x*|, 1e-6 * max|x*|) as the scale, so exact
+zeros and underflowed entries are compared against the array's magnitude.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import log_space_sum_amd as L
+import oracle
+
+TOL = {
+    "fp32": dict(val_rel=2e-6, val_abs=0.0, flow_rel=1e-5),
+    "auto": dict(val_rel=0.0, val_abs=1e-2, flow_rel=5e-3),
+}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def torch():
+    import torch as T
+    return T
+
+
+def run_gpu(cfg, mode="auto", splits=None, B=None, em=None, timing=False, device=0, repeat=1):
+    """Forward + backward (+ optional EM) on the GPU.  Returns numpy arrays."""
+    T = torch()
+    circ = cfg["circuit"]
+    B = B or cfg["B"]
+    dev = f"cuda:{device}"
+    h = L.pc_compile_layout(circ, device=device)
+    L.pc_set_precision(h, mode)
+    for (m, k, pa, pb) in (splits or []):
+        L.pc_set_split(h, m, k, pa, pb)
+    params = T.tensor(cfg["params"], device=dev)
+    tokens = T.tensor(cfg["tokens"], device=dev) if cfg.get("tokens") is not None else None
+    vals = T.full((circ.num_nodes, B), float("nan"), device=dev)
+    ext_rows = _external_rows(circ)
+    if cfg.get("external") is not None:
+        vals[T.tensor(ext_rows, device=dev)] = T.tensor(cfg["external"], device=dev)
+    flows = T.full((circ.num_nodes, B), float("nan"), device=dev)
+    flags = 0
+    if cfg.get("seed_flows") is not None:
+        outs = circ.output_nodes()
+        flows[T.tensor(outs, device=dev)] = T.tensor(cfg["seed_flows"], device=dev)
+        flags = L.PC_BWD_SEEDED
+    pflows = T.zeros(circ.num_params, device=dev)
+    ll = T.empty(B, device=dev) if circ.root >= 0 else None
+    ws = L.workspace(h, B, dev)
+    out = []
+    for _ in range(repeat):
+        pflows.zero_()
+        L.pc_forward(h, B, tokens, params, vals, ll, None, ws)
+        L.pc_backward(h, B, tokens, params, vals, flows, pflows, flags, None, None, ws)
+        T.cuda.synchronize()
+        r = dict(vals=vals.cpu().numpy().copy(), flows=flows.cpu().numpy().copy(),
+                 pflows=pflows.cpu().numpy().copy(), ll=None if ll is None else ll.cpu().numpy().copy())
+        out.append(r)
+    if em is not None:
+        newp = params.clone()
+        L.pc_em_step(h, newp, pflows, em[0], em[1])
+        T.cuda.synchronize()
+        out[-1]["em"] = newp.cpu().numpy()
+    return out if repeat > 1 else out[0]
+
+
+def _external_rows(circ):
+    rows = []
+    for l in circ.layers:
+        if type(l).__name__ == "InputExternal":
+            rows.extend(range(l.node_start, l.node_start + l.num_nodes))
+    return np.array(rows, dtype=np.int64)
+
+
+def run_oracle(cfg, B=None, samples=None):
+    circ = cfg["circuit"]
+    p = cfg["params"].astype(np.float64)
+    tok = cfg.get("tokens")
+    ext = cfg.get("external")
+    seeds = cfg.get("seed_flows")
+    if samples is not None:
+        tok = None if tok is None else tok[samples]
+        ext = None if ext is None else ext[:, samples]
+        seeds = None if seeds is None else seeds[:, samples]
+    Bo = (len(samples) if samples is not None else (B or cfg["B"]))
+    V, ll = oracle.forward(circ, p, Bo, tokens=tok, external=ext)
+    r = oracle.backward(circ, p, V, tokens=tok, seed_flows=seeds)
+    return dict(vals=V, ll=ll, flows=r["flows"], pflows=r["param_flows"])
+
+
+def rel_err(got, ref, floor=1e-6):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    scale = np.maximum(np.abs(ref), floor * max(np.abs(ref).max(), 1e-300))
+    both_inf = np.isinf(got) & np.isinf(ref) & (np.sign(got) == np.sign(ref))
+    e = np.where(both_inf, 0.0, np.abs(got - ref) / scale)
+    e[np.isnan(got) | np.isnan(ref)] = np.inf
+    return e
+
+
+def check_values(got, ref, mode, what):
+    t = TOL[mode]
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    both_inf = np.isinf(got) & np.isinf(ref) & (np.sign(got) == np.sign(ref))
+    err = np.where(both_inf, 0.0, np.abs(got - ref))
+    err[np.isnan(got) | np.isnan(ref)] = np.inf
+    bound = t["val_abs"] + t["val_rel"] * np.where(np.isfinite(ref), np.abs(ref), 0.0)
+    bad = err > bound
+    worst = float(np.max(err)) if err.size else 0.0
+    say(f"  {what}: max abs err {worst:.3e} (mode {mode})")
+    assert not bad.any(), f"{what}: {int(bad.sum())} entries out of tolerance, worst {worst:.3e} at {np.argwhere(bad)[0]}"
+    return worst
+
+
+def num_sum_layers(circ):
+    return sum(1 for l in circ.layers if type(l).__name__ == "Sum")
+
+
+def check_flows(got, ref, mode, what, scale=1):
+    e = rel_err(got, ref)
+    worst = float(e.max()) if e.size else 0.0
+    med = float(np.median(e)) if e.size else 0.0
+    say(f"  {what}: max rel err {worst:.3e}, median {med:.3e} (mode {mode}, bound x{scale})")
+    bad = e > TOL[mode]["flow_rel"] * scale
+    assert not bad.any(), f"{what}: {int(bad.sum())}/{e.size} entries out of tolerance, worst {worst:.3e}"
+    return worst
+
+
+def compare(cfg, mode, gpu=None, orc=None, samples=None, what=""):
+    """Full comparison of values, flows and parameter flows."""
+    gpu = gpu or run_gpu(cfg, mode)
+    orc = orc or run_oracle(cfg)
+    circ = cfg["circuit"]
+    if samples is None:
+        check_values(gpu["vals"], orc["vals"], mode, f"{what} node values")
+        check_flows(gpu["flows"], orc["flows"], mode, f"{what} element flows")
+    else:
+        check_values(gpu["vals"][:, samples], orc["vals"], mode, f"{what} node values (sampled)")
+        check_flows(gpu["flows"][:, samples], orc["flows"], mode, f"{what} element flows (sampled)")
+    return gpu, orc
+
+
+# ---------------------------------------------------------------------------
+# Per-layer ("one layer against float64") oracle: every layer's outputs are
+# recomputed by the oracle from the GPU's own inputs to that layer (children
+# values, incoming flows), so the comparison measures that layer's kernels
+# alone, as the precision pull request measures flows on one HMM layer.
+# ---------------------------------------------------------------------------
+
+def _sub_sum_circuit(circ, layer):
+    """The sum layer alone over external copies of its distinct children."""
+    from workloads import circuits as W
+    kids = np.unique(np.concatenate([g.child_ids() for g in layer.groups]))
+    remap = {int(c): i for i, c in enumerate(kids)}
+    n_ext = len(kids)
+    groups = []
+    nxt = n_ext
+    outs = []
+    for g in layer.groups:
+        starts = np.array([remap[int(s)] for s in g.ch_block_start], dtype=np.int32)
+        groups.append(W.SumGroup(nxt, g.num_nodes, starts, g.ch_block_size, g.param_offset, g.lowrank))
+        outs.append(np.arange(g.out_start, g.out_start + g.num_nodes))
+        nxt += g.num_nodes
+    sub = W.Circuit("sub", nxt, 0, circ.num_params, [W.InputExternal(0, n_ext), W.Sum(groups)],
+                    root=-1, lowrank_rank=circ.lowrank_rank)
+    return sub, kids, np.concatenate(outs)
+
+
+def local_oracle(cfg, gpu, samples=None):
+    """Expected values, flows and parameter flows, layer by layer, from the
+    GPU's own inputs to each layer: a sum layer's values and its contributions
+    to its children's flows and to the parameter flows are recomputed by the
+    oracle from the GPU's children values and the GPU's flows at its outputs;
+    products and inputs likewise from theirs."""
+    from workloads import circuits as W
+    circ = cfg["circuit"]
+    p = cfg["params"].astype(np.float64)
+    cols = np.arange(gpu["vals"].shape[1]) if samples is None else np.asarray(samples)
+    GV = gpu["vals"][:, cols].astype(np.float64)
+    GF = gpu["flows"][:, cols].astype(np.float64)
+    Bs = len(cols)
+    vals = GV.copy()
+    flows = np.zeros_like(GF)
+    seeds = cfg.get("seed_flows")
+    if seeds is not None:
+        flows[circ.output_nodes()] = seeds[:, cols]
+    else:
+        flows[circ.root] = 1.0
+    pflows = np.zeros(circ.num_params)
+    tok = cfg.get("tokens")
+    tok = None if tok is None else tok[cols]
+    for layer in circ.layers:
+        if isinstance(layer, W.Sum):
+            sub, kids, outs = _sub_sum_circuit(circ, layer)
+            V, _ = oracle.forward(sub, p, Bs, external=GV[kids])
+            vals[outs] = V[len(kids):]
+            r = oracle.backward(sub, p, V, seed_flows=GF[outs])
+            flows[kids] += r["flows"][:len(kids)]
+            pflows += r["param_flows"]
+        elif isinstance(layer, W.Product):
+            ptr = layer.ch_ptr.astype(np.int64)
+            ids = layer.ch_ids.astype(np.int64)
+            rng_ = slice(layer.node_start, layer.node_start + layer.num_nodes)
+            vals[rng_] = np.add.reduceat(GV[ids], ptr[:-1], axis=0)
+            par = np.repeat(np.arange(layer.node_start, layer.node_start + layer.num_nodes), np.diff(ptr))
+            np.add.at(flows, ids, GF[par])
+        elif isinstance(layer, W.InputCat):
+            sub = W.Circuit("in", circ.num_nodes, circ.num_vars, circ.num_params, [layer], root=-1)
+            V, _ = oracle.forward(sub, p, Bs, tokens=tok)
+            rng_ = slice(layer.node_start, layer.node_start + layer.num_nodes)
+            vals[rng_] = V[rng_]
+            r = oracle.backward(sub, p, V, tokens=tok, seed_flows=GF[rng_])
+            pflows += r["param_flows"]
+    return dict(vals=vals, flows=flows, pflows=pflows)
+
+
+def check_local(cfg, gpu, mode, what, samples=None, pflows=True):
+    """Per-layer parity at the stated tolerances."""
+    loc = local_oracle(cfg, gpu, samples)
+    cols = slice(None) if samples is None else np.asarray(samples)
+    check_values(gpu["vals"][:, cols], loc["vals"], mode, f"{what} per-layer values")
+    check_flows(gpu["flows"][:, cols], loc["flows"], mode, f"{what} per-layer element flows")
+    if pflows:
+        check_flows(gpu["pflows"], loc["pflows"], mode, f"{what} per-layer parameter flows")
+    return loc

@@ -1,0 +1,146 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle,
+element by element, in both precision modes, on the synthetic workloads and
+their edge cases (ragged sizes, -inf columns, batches around the small-batch
+rule, overlapping block-sparse children, tied weights)."""
+import numpy as np
+import pytest
+
+from tests import gpu_util as G
+from workloads import make_config
+
+pytestmark = pytest.mark.gpu
+
+MODES = ["auto", "fp32"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import log_space_sum_amd as L
+    L.lib()          # fails loudly when libpc.so is missing
+
+
+def _full(cfg, mode, what, em=None):
+    """Values and log-likelihood end to end at the stated tolerances; element
+    and parameter flows per layer (each layer's flows recomputed by the
+    oracle from that layer's GPU inputs) at the stated tolerances; flows end
+    to end at the stated tolerance times the number of sum layers."""
+    G.say(f"case {what} mode={mode} B={cfg['B']}")
+    gpu = G.run_gpu(cfg, mode, em=em)
+    orc = G.run_oracle(cfg)
+    G.check_values(gpu["vals"], orc["vals"], mode, f"{what} node values")
+    if orc["ll"] is not None:
+        G.check_values(gpu["ll"], orc["ll"], mode, f"{what} log-likelihood")
+    G.check_local(cfg, gpu, mode, what)
+    depth = G.num_sum_layers(cfg["circuit"])
+    G.check_flows(gpu["flows"], orc["flows"], mode, f"{what} element flows end to end", scale=depth)
+    G.check_flows(gpu["pflows"], orc["pflows"], mode, f"{what} parameter flows end to end", scale=depth)
+    return gpu, orc
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("M,N,groups,B", [(200, 136, 1, 37), (96, 160, 3, 48), (1024, 1024, 1, 128)])
+def test_dense_layer(mode, M, N, groups, B):
+    cfg = make_config("dense_layer", M=M, N=N, groups=groups, B=B)
+    _full(cfg, mode, f"dense {M}x{N} g{groups}")
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_dense_edge_columns(mode):
+    """Per-group column-maximum edge cases: all-(-inf) column, single finite
+    child, far-shifted columns, zero weights."""
+    cfg = make_config("dense_layer", M=70, N=90, groups=2, B=20)
+    ext = cfg["external"]
+    ext[:90, 0] = -np.inf
+    ext[:, 1] = -np.inf
+    ext[7, 1] = -2.0
+    ext[:, 2] -= 1e4
+    ext[:, 3] += 80.0
+    cfg["params"][5:40] = 0.0
+    _full(cfg, mode, "dense edge columns")
+
+
+@pytest.mark.parametrize("B", [1, 15, 16, 17])
+def test_small_batches(B):
+    """Batches below 16 run fp32-level products even in auto mode."""
+    cfg = make_config("dense_layer", M=130, N=70, groups=1, B=B)
+    gpu, orc = _full(cfg, "fp32" if B < 16 else "auto", f"dense small batch B={B}")
+    if B < 16:
+        gpu_auto = G.run_gpu(cfg, "auto")
+        np.testing.assert_array_equal(gpu_auto["vals"], gpu["vals"])
+
+
+@pytest.mark.parametrize("mode", ["fp32"])
+def test_tiny_hmm(mode):
+    cfg = make_config("tiny_hmm")
+    _full(cfg, mode, "tiny hmm", em=(1.0, 0.0))
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_hmm_medium(mode):
+    cfg = make_config("hmm4096", H=320, T=7, V=50, B=70)
+    gpu, orc = _full(cfg, mode, "hmm 320x7")
+    # EM step
+    newp_or = __import__("oracle").em_step(cfg["circuit"], cfg["params"], orc["pflows"])
+    gpu2 = G.run_gpu(cfg, mode, em=(1.0, 0.0))
+    G.check_flows(gpu2["em"], newp_or, mode, "hmm EM parameters")
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_em_pseudocount(mode):
+    cfg = make_config("hmm4096", H=64, T=5, V=20, B=32)
+    gpu = G.run_gpu(cfg, mode, em=(0.7, 0.3))
+    orc = G.run_oracle(cfg)
+    ref = __import__("oracle").em_step(cfg["circuit"], cfg["params"], gpu["pflows"].astype(np.float64),
+                                       step_size=0.7, pseudocount=0.3)
+    G.check_flows(gpu["em"], ref, "fp32", "EM blend + pseudocount")
+    G.check_flows(gpu["pflows"], orc["pflows"], mode, "parameter flows")
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_hclt_small(mode):
+    cfg = make_config("hclt", num_vars=30, H=48, K=12, B=33)
+    _full(cfg, mode, "hclt 30x48")
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("seed", [0, 1])
+def test_block_sparse_layer(mode, seed):
+    cfg = make_config(kind="block_layer", seed=seed, M_blocks=9, node_block=48, ch_blocks=7,
+                      ch_block=40, B=41, spread_hi=20.0)
+    _full(cfg, mode, f"block layer s{seed}")
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_block_sparse_circuit(mode):
+    cfg = make_config(kind="block_sparse", seed=2, num_vars=6, K=5, in_blocks=3, block=24,
+                      sum_blocks=3, depth_sums=2, B=29)
+    _full(cfg, mode, "block-sparse circuit")
+
+
+def test_deterministic():
+    """Two runs give bitwise identical values, flows and parameter flows."""
+    cfg = make_config(kind="block_layer", seed=4, M_blocks=6, node_block=40, ch_blocks=5,
+                      ch_block=32, B=33)
+    r = G.run_gpu(cfg, "auto", repeat=2)
+    for k in ("vals", "flows", "pflows"):
+        np.testing.assert_array_equal(r[0][k], r[1][k])
+
+
+@pytest.mark.parametrize("kind", ["fwd", "elem", "param"])
+def test_fp32_needs_split(kind):
+    """Downgrading any one of the three products of the fp32-level mode to a
+    single bf16 term breaks the fp32-level tolerance."""
+    cfg = make_config("dense_layer", M=256, N=256, groups=1, B=64)
+    gpu = G.run_gpu(cfg, "fp32", splits=[("fp32", kind, 1, 1)])
+    orc = G.run_oracle(cfg)
+    errs = []
+    for (what, fn, a, b) in [("vals", G.check_values, gpu["vals"], orc["vals"]),
+                             ("flows", G.check_flows, gpu["flows"], orc["flows"]),
+                             ("pflows", G.check_flows, gpu["pflows"], orc["pflows"])]:
+        try:
+            fn(a, b, "fp32", f"downgraded {kind}: {what}")
+        except AssertionError as e:
+            errs.append(str(e))
+    assert errs, f"a 1-term {kind} product still met the fp32-level tolerance"
