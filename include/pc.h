@@ -48,8 +48,8 @@ extern "C" {
 /* ---- precision modes (PyJuice pull request #62, Summary item 1) ---------
  * PC_PREC_AUTO: sum-layer products from bfloat16 operands (round to nearest
  *   even) with float32 accumulation -- the counterpart of the page's "auto"
- *   mode, whose forward uses bf16 products; the two flow products split one
- *   operand into hi + lo planes (see pc_set_split).
+ *   mode, whose forward uses bf16 products; each product splits one of its
+ *   operands into hi + lo planes (see pc_set_split).
  * PC_PREC_FP32: fp32-level products: each float32 operand is split into
  *   bfloat16 planes (hi, lo: x ~ hi + lo) and the cross products up to the
  *   second order are accumulated in float32 -- the counterpart of the page's
@@ -187,10 +187,10 @@ int pc_get_precision(pc_handle h, int* mode);
  * operand; the products of planes whose order is below the larger count are
  * accumulated: (1,1) one bf16 product; (2,1) or (1,2) one operand split,
  * two products; (2,2) hi/lo split, three products; (3,3) hi/mid/lo split,
- * six products.  Defaults: auto (1,1) forward, (2,1) element flows (split
- * weights) and (2,1) parameter flows (split scaled flows), so that a flow
- * dominated by one product is within one bf16 rounding (2^-8) of exact;
- * fp32-level (3,3) everywhere.  Errors: PC_ERR_INVALID_ARG for other counts or kinds. */
+ * six products.  Defaults: auto (2,1) for all three (forward and element
+ * flows split the weights, parameter flows split the scaled flows g), so
+ * that every value or flow dominated by one product carries a single bf16
+ * rounding (at most 2^-8 relative); fp32-level (3,3) everywhere.  Errors: PC_ERR_INVALID_ARG for other counts or kinds. */
 int pc_set_split(pc_handle h, int mode, int gemm_kind, int planes_a, int planes_b);
 
 /* Bytes of workspace pc_forward / pc_backward need for `batch` samples in the

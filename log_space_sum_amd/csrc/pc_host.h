@@ -76,7 +76,7 @@ struct Handle {
   int device = -1;
   int mode = PC_PREC_AUTO;
   // planes[mode][gemm kind][0: first operand, 1: second operand]
-  int planes[2][3][2] = {{{1, 1}, {2, 1}, {2, 1}}, {{3, 3}, {3, 3}, {3, 3}}};
+  int planes[2][3][2] = {{{2, 1}, {2, 1}, {2, 1}}, {{3, 3}, {3, 3}, {3, 3}}};
   int32_t num_nodes = 0, num_vars = 0, root = -1, lowrank_rank = 0;
   int64_t num_params = 0;
   std::vector<LayerRef> layers;
