@@ -216,8 +216,9 @@ __global__ void k_exp_pack(SumArgs a) {
     float e = 0.0f;
     if (k < gr.N && b < a.B) e = expf(a.vals[(int64_t)child_of(gr, a.chblocks, k) * a.B + b] - sh);
     tile[r][lane] = e;
-    if (b < a.B_padK)
-      split_store(e, a.np_direct, a.direct + (gr.e_row + k) * (int64_t)a.B_padK + b, a.direct_plane);
+    if (b < a.B_padK)     // node-major copy for every group sharing these children
+      for (int q = g; q >= 0; q = a.groups[q].share_next)
+        split_store(e, a.np_direct, a.direct + (a.groups[q].e_row + k) * (int64_t)a.B_padK + b, a.direct_plane);
   }
   __syncthreads();
   const int NpK = (gr.N + K_PAD - 1) / K_PAD * K_PAD;

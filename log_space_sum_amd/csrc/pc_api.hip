@@ -124,7 +124,6 @@ void upload_tables(Handle* h, int device) {
     sp.d_red_src = upload(sp.red_src);
   }
   h->d_blocks = upload(h->blocks);
-  h->d_copies = upload(h->copies);
   h->d_rowsegs = upload(h->rowsegs);
   h->d_zero = upload(h->zero_ranges);
   h->d_seed = upload(h->seed_ranges);
@@ -156,7 +155,6 @@ void free_tables(Handle* h) {
     release(sp.d_red_src);
   }
   release(h->d_blocks);
-  release(h->d_copies);
   release(h->d_rowsegs);
   release(h->d_zero);
   release(h->d_seed);
@@ -196,6 +194,26 @@ WsPlan plan_workspace(const Handle* h, int B) {
   p.tokT = take(inp ? (size_t)h->num_vars * Bs * 4 : 0);
   p.bptr = take(inp ? (size_t)h->num_vars * (h->max_cats + 1) * 4 : 0);
   p.bidx = take(inp ? (size_t)h->num_vars * Bs * 4 : 0);
+  // split-K partial tiles and arrival counters (forward / element flows)
+  {
+    int64_t pel = 0;
+    int32_t nct = 0;
+    const int ntl = p.B_pad / 128;
+    for (const auto& sp : h->sums) {
+      if (sp.lowrank) continue;
+      for (int e = 0; e < 2; ++e) {
+        const int kt = gemm_kt(p.pl[e][0], p.pl[e][1]);
+        const int tiles = (e == 0 ? sp.mtiles : sp.ctiles) * (ROW_PAD / 128) * ntl;
+        const int S = choose_split(tiles, (e == 0 ? sp.max_npk : sp.max_mpk) / kt);
+        if (S > 1) pel = std::max<int64_t>(pel, (int64_t)tiles * S * 128 * 128);
+        nct = std::max(nct, tiles);
+      }
+    }
+    p.partial_elems = pel;
+    p.ncounters = nct;
+    p.partials = take((size_t)pel * 4);
+    p.counters = take((size_t)nct * 4);
+  }
   p.lowrank = take(0);
   p.lowrank_bytes = 0;
   p.total = off;
@@ -223,6 +241,9 @@ WsView make_view(const Handle* h, const WsPlan& p, void* ws) {
   v.tokT = (int32_t*)(base + p.tokT);
   v.bucket_ptr = (int32_t*)(base + p.bptr);
   v.bucket_idx = (int32_t*)(base + p.bidx);
+  v.partials = (float*)(base + p.partials);
+  v.counters = (uint32_t*)(base + p.counters);
+  v.ncounters = p.ncounters;
   v.B = p.B;
   v.B_pad = p.B_pad;
   v.B_padK = p.B_padK;
@@ -271,7 +292,8 @@ GemmArgs gemm_common(const Call& c) {
   a.B_padK = c.v.B_padK;
   a.ntiles = c.v.B_pad / 128;
   a.blocks = c.h->d_blocks;
-  a.copies = c.h->d_copies;
+  a.partials = c.v.partials;
+  a.counters = c.v.counters;
   return a;
 }
 
@@ -479,6 +501,10 @@ int pc_forward(pc_handle hh, int batch, const int32_t* tokens, const float* para
       Timed t(h, KK_OTHER, c.s);
       launch_fill_u32(v.mkeys, (int64_t)h->m_rows * B, 0u, c.s);
     }
+    if (p.ncounters > 0) {
+      Timed t(h, KK_OTHER, c.s);
+      launch_fill_u32(v.counters, p.ncounters, 0u, c.s);
+    }
     for (const LayerRef& r : h->layers) {
       if (r.kind == PC_LAYER_INPUT_CAT) {
         InputArgs a = input_args(c, h->inputs[r.idx], params);
@@ -521,8 +547,10 @@ int pc_forward(pc_handle hh, int batch, const int32_t* tokens, const float* para
         g.vals = node_vals;
         g.mkeys = v.mkeys;
         g.ssum = v.ssum;
+        const int tiles = sp.mtiles * (ROW_PAD / 128) * g.ntiles;
+        g.splitk = choose_split(tiles, sp.max_npk / gemm_kt(p.pl[GK_FWD][0], p.pl[GK_FWD][1]));
         Timed t(h, KK_FWD, c.s);
-        launch_gemm(EPI_FWD, p.pl[GK_FWD][0], p.pl[GK_FWD][1], sp.mtiles * g.ntiles, g, c.s);
+        launch_gemm(EPI_FWD, p.pl[GK_FWD][0], p.pl[GK_FWD][1], tiles, 0, g, c.s);
       }
     }
     if (ll) {
@@ -560,6 +588,10 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
     if (!seeded) {
       Timed t(h, KK_OTHER, c.s);
       launch_fill_ranges(node_flows, h->d_seed, (int)h->seed_ranges.size(), h->max_seed_count, B, c.s);
+    }
+    if (p.ncounters > 0) {
+      Timed t(h, KK_OTHER, c.s);
+      launch_fill_u32(v.counters, p.ncounters, 0u, c.s);
     }
     if (!h->inputs.empty()) {
       Timed t(h, KK_OTHER, c.s);
@@ -599,8 +631,10 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
         g.mkeys = v.mkeys;
         g.store = sp.store ? 1 : 0;
         {
+          const int tiles = sp.ctiles * (ROW_PAD / 128) * g.ntiles;
+          g.splitk = choose_split(tiles, sp.max_mpk / gemm_kt(p.pl[GK_ELEM][0], p.pl[GK_ELEM][1]));
           Timed t(h, KK_ELEM, c.s);
-          launch_gemm(EPI_ELEM, p.pl[GK_ELEM][0], p.pl[GK_ELEM][1], sp.ctiles * g.ntiles, g, c.s);
+          launch_gemm(EPI_ELEM, p.pl[GK_ELEM][0], p.pl[GK_ELEM][1], tiles, 0, g, c.s);
         }
         if (sp.overlap) {
           SumArgs ra = sum_common(c, sp);
@@ -636,8 +670,11 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
       g.planeB = v.earena_plane;
       g.params = params;
       g.pflows = param_flows;
+      const bool big = h->min_block_dim >= 256 && p.pl[GK_PARAM][0] + p.pl[GK_PARAM][1] <= 3;
+      g.splitk = 1;
       Timed t(h, KK_PARAM, c.s);
-      launch_gemm(EPI_PARAM, p.pl[GK_PARAM][0], p.pl[GK_PARAM][1], h->param_tiles, g, c.s);
+      launch_gemm(EPI_PARAM, p.pl[GK_PARAM][0], p.pl[GK_PARAM][1], big ? h->param_tiles256 : h->param_tiles128,
+                  big ? 1 : 0, g, c.s);
     }
     check_launch();
     return PC_OK;

@@ -213,7 +213,7 @@ Handle* compile_layout(const pc_circuit_desc* d) {
     need(param_intervals[k].first >= param_intervals[k - 1].second, "parameter blocks overlap");
 
   // ---- pass 2: sum-layer classification and operand placement -------------
-  int64_t e_rows = 0, g_rows = 0, s_rows = 0;
+  int64_t s_rows = 0;
   int32_t m_rows = 0;
   for (auto& sp : h->sums) {
     const int G = (int)sp.groups.size();
@@ -272,27 +272,27 @@ Handle* compile_layout(const pc_circuit_desc* d) {
       } else {
         r.block = bit->second;
       }
+      r.share_next = -1;
       if (r.share_src == g) {
         r.m_row = m_rows++;
         r.e_koff = ekoff;
         ekoff += (int32_t)NpK;
         r.pk_start = pk;
         pk += (int32_t)(Np / 64);
-        r.e_row = sp.lowrank ? -1 : e_rows;
-        if (!sp.lowrank) e_rows += Np;
       } else {
-        const GroupRec& s = sp.groups[r.share_src];
+        GroupRec& s = sp.groups[r.share_src];
         r.m_row = s.m_row;
         r.e_koff = s.e_koff;
-        r.pk_start = pk;          // empty range: packing kernels skip shared copies
-        r.e_row = s.e_row;
+        r.pk_start = pk;          // empty range: the source group's tiles write this group's E rows too
+        int q = r.share_src;      // append to the source's chain of sharers
+        while (sp.groups[q].share_next >= 0) q = sp.groups[q].share_next;
+        sp.groups[q].share_next = g;
       }
+      r.e_row = r.g_row = -1;     // placed per weight block below
       r.s_row = sp.lowrank ? -1 : s_rows;
       if (!sp.lowrank) s_rows += r.M;
       r.g_koff = gkoff;
       gkoff += (int32_t)MpK;
-      r.g_row = sp.lowrank ? -1 : g_rows;
-      if (!sp.lowrank) g_rows += Mp;
       r.mt_start = mt;
       mt += (int32_t)(Mp / ROW_PAD);
       r.ct_start = ct;
@@ -305,6 +305,10 @@ Handle* compile_layout(const pc_circuit_desc* d) {
       } else {
         r.scratch_row = -1;
       }
+    }
+    for (auto& r : sp.groups) {
+      sp.max_npk = std::max<int32_t>(sp.max_npk, (int32_t)round_up(r.N, K_PAD));
+      sp.max_mpk = std::max<int32_t>(sp.max_mpk, (int32_t)round_up(r.M, K_PAD));
     }
     sp.ebt_cols = ekoff;
     sp.gbt_cols = gkoff;
@@ -339,39 +343,45 @@ Handle* compile_layout(const pc_circuit_desc* d) {
       sp.red_ptr.push_back((int32_t)cs.size());
     }
   }
-  h->earena_rows = e_rows;
   h->s_rows = s_rows;
-  h->garena_rows = g_rows;
   h->m_rows = m_rows;
 
-  // copies of each block, in layer order
+  // Tied copies of each block, in layer order: copy s keeps its node-major G
+  // rows at g_base + s*M_pad and its E rows at e_base + s*N_pad.
   {
-    std::vector<std::vector<CopyRec>> per(h->blocks.size());
-    std::vector<bool> plain(h->blocks.size(), false);
-    for (auto& sp : h->sums)
-      for (auto& r : sp.groups) {
-        if (sp.lowrank) continue;
-        per[r.block].push_back(CopyRec{r.e_row, r.g_row});
-        plain[r.block] = true;
-      }
-    int64_t th = 0, tht = 0;
-    int32_t pk = 0, pt = 0;
+    std::vector<std::vector<std::pair<int, int>>> per(h->blocks.size());
+    for (int si = 0; si < (int)h->sums.size(); ++si) {
+      if (h->sums[si].lowrank) continue;
+      for (int g = 0; g < (int)h->sums[si].groups.size(); ++g) per[h->sums[si].groups[g].block].push_back({si, g});
+    }
+    int64_t th = 0, tht = 0, erow = 0, grow = 0;
+    int32_t pk = 0, p256 = 0, p128 = 0;
     for (size_t b = 0; b < h->blocks.size(); ++b) {
       BlockRec& B = h->blocks[b];
-      B.copy_off = (int32_t)h->copies.size();
-      B.ncopies = (int32_t)per[b].size();
-      h->copies.insert(h->copies.end(), per[b].begin(), per[b].end());
       const int64_t Mp = round_up(B.M, ROW_PAD), Np = round_up(B.N, ROW_PAD);
       const int64_t MpK = round_up(B.M, K_PAD), NpK = round_up(B.N, K_PAD);
+      B.ncopies = (int32_t)per[b].size();
+      B.g_base = grow;
+      B.e_base = erow;
+      for (int c = 0; c < B.ncopies; ++c) {
+        GroupRec& r = h->sums[per[b][c].first].groups[per[b][c].second];
+        r.g_row = grow + c * Mp;
+        r.e_row = erow + c * Np;
+      }
+      grow += B.ncopies * Mp;
+      erow += B.ncopies * Np;
       B.pk_start = pk;
-      B.pt_start = pt;
-      if (plain[b]) {
+      B.pt256 = p256;
+      B.pt128 = p128;
+      if (B.ncopies > 0) {
         B.th_off = th;
         th += Mp * NpK;
         B.tht_off = tht;
         tht += Np * MpK;
         pk += (int32_t)((Mp / 64) * (Np / 64));
-        pt += (int32_t)((Mp / ROW_PAD) * (Np / ROW_PAD));
+        p256 += (int32_t)((Mp / 256) * (Np / 256));
+        p128 += (int32_t)((Mp / 128) * (Np / 128));
+        h->min_block_dim = std::min<int64_t>(h->min_block_dim, std::min(B.M, B.N));
       } else {
         B.th_off = B.tht_off = -1;
       }
@@ -379,7 +389,11 @@ Handle* compile_layout(const pc_circuit_desc* d) {
     h->theta_elems = th;
     h->thetaT_elems = tht;
     h->pk_block_tiles = pk;
-    h->param_tiles = pt;
+    h->param_tiles256 = p256;
+    h->param_tiles128 = p128;
+    h->earena_rows = erow;
+    h->garena_rows = grow;
+    for (auto& sp : h->sums) h->max_sum_groups = std::max<int32_t>(h->max_sum_groups, (int32_t)sp.groups.size());
   }
 
   // EM row segments: every distinct block and input table

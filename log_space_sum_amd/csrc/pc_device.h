@@ -11,7 +11,7 @@ namespace pc {
 // dimensions of the products) to ROW_PAD, the contraction dimension to K_PAD.
 // Operands are therefore tile-aligned and the product kernels need no bounds
 // checks in their main loop; pads hold zeros.
-constexpr int ROW_PAD = 128;
+constexpr int ROW_PAD = 256;
 constexpr int K_PAD = 64;
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -31,13 +31,14 @@ struct GroupRec {
   int32_t g_koff;        // column offset of the group's slice of the layer's batch-major G
   int64_t e_row;         // first row of the group's node-major E (kept for parameter flows)
   int64_t g_row;         // first row of the group's node-major G (kept for parameter flows)
-  int32_t mt_start;      // prefix of output-row tiles over the layer's groups (forward)
-  int32_t ct_start;      // prefix of child-row tiles over the layer's groups (element flows)
+  int32_t mt_start;      // prefix of 256-row output blocks over the layer's groups (forward)
+  int32_t ct_start;      // prefix of 256-row child blocks over the layer's groups (element flows)
   int32_t pk_start;      // prefix of 64-row child tiles over the layer's groups (column max, exp)
   int32_t pg_start;      // prefix of 64-row output tiles over the layer's groups (scaled flows)
   int32_t scratch_row;   // first row in the element-flow scratch (-1: write node flows directly)
   int32_t lowrank;       // LowRank slot or -1
   int32_t share_src;     // group whose E slice this group reuses (SHARED layers), or itself
+  int32_t share_next;    // next group sharing this group's children (its E rows get a copy), or -1
   int64_t s_row;         // first row of the group's scaled sums S (kept from the forward), -1 if none
 };
 
@@ -47,16 +48,13 @@ struct BlockRec {
   int32_t M, N;
   int64_t th_off;        // element offset of the [M_pad, N_padK] split weights (forward operand)
   int64_t tht_off;       // element offset of the [N_pad, M_padK] transposed split weights (element flows)
-  int32_t ncopies;
-  int32_t copy_off;      // first entry in the copy table
+  int32_t ncopies;       // tied copies; copy s keeps its G rows at g_base + s*M_pad and
+  int64_t g_base;        // its E rows at e_base + s*N_pad, so the parameter-flow product
+  int64_t e_base;        // walks all copies as one contraction with affine addressing
   int32_t pk_start;      // prefix of 64x64 packing tiles over blocks
-  int32_t pt_start;      // prefix of product tiles over blocks (parameter flows)
-};
-
-// One tied copy of a block: where its kept operands live.
-struct CopyRec {
-  int64_t e_row;
-  int64_t g_row;
+  int32_t pt256;         // prefix of 256x256 product tiles over blocks (parameter flows)
+  int32_t pt128;         // prefix of 128x128 product tiles over blocks (parameter flows)
+  int32_t pad_;
 };
 
 // Parameter row run normalised by EM.
@@ -94,6 +92,9 @@ struct WsView {
   int32_t* tokT;        // [num_vars, B] tokens transposed
   int32_t* bucket_ptr;  // [num_vars, K_max + 1]
   int32_t* bucket_idx;  // [num_vars, B]
+  float* partials;      // split-K partial tiles of the current product
+  uint32_t* counters;   // split-K arrival counters
+  int32_t ncounters;
   int32_t B, B_pad, B_padK;
 };
 

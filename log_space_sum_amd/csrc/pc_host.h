@@ -59,6 +59,7 @@ struct SumPlan {
   int32_t mtiles = 0, ctiles = 0;              // 128-row tiles over outputs / children
   int32_t pktiles = 0, pgtiles = 0;            // 64-row tiles over source children / outputs
   int32_t scratch_rows = 0;
+  int32_t max_npk = 0, max_mpk = 0;            // widest contraction of the forward / element flows
   std::vector<int32_t> red_child, red_ptr, red_src;   // overlap reduction CSR
   GroupRec* d_groups = nullptr;
   int32_t* d_blocks = nullptr;
@@ -84,9 +85,10 @@ struct Handle {
   std::vector<ProductPlan> prods;
   std::vector<SumPlan> sums;
   std::vector<BlockRec> blocks;
-  std::vector<CopyRec> copies;
   int32_t pk_block_tiles = 0;          // 64x64 tiles over all blocks (weight split)
-  int32_t param_tiles = 0;             // 128x128 tiles over all blocks (parameter flows)
+  int32_t param_tiles256 = 0, param_tiles128 = 0;   // product tiles over all blocks (parameter flows)
+  int64_t min_block_dim = 1 << 30;     // smallest M or N of a plain block
+  int32_t max_sum_groups = 0;
   int64_t theta_elems = 0, thetaT_elems = 0;
   int64_t earena_rows = 0, garena_rows = 0, s_rows = 0;
   int32_t m_rows = 0;
@@ -102,7 +104,6 @@ struct Handle {
   bool has_plain_sums = false;
   // device copies of handle-wide tables
   BlockRec* d_blocks = nullptr;
-  CopyRec* d_copies = nullptr;
   RowSeg* d_rowsegs = nullptr;
   FillRange* d_zero = nullptr;
   FillRange* d_seed = nullptr;
@@ -131,6 +132,9 @@ struct WsPlan {
   int B, B_pad, B_padK, mode;
   int pl[3][2];
   size_t theta, thetaT, ebt, gbt, earena, garena, mkeys, ssum, scratch, tokT, bptr, bidx, lowrank;
+  size_t partials, counters;
+  int64_t partial_elems;
+  int32_t ncounters;
   size_t lowrank_bytes;
   size_t total;
 };
