@@ -41,6 +41,22 @@ def sum_flops(circ, B):
     return tot
 
 
+def kernel_traffic(kernel_kind):
+    """HBM bytes per launch of `kernel_kind` from the committed counter
+    summary (profiles/traffic_<kind>.json), if it was taken on the current
+    source of the product kernel; else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_kind}.json")
+    src = os.path.join(ROOT, "log_space_sum_amd", "csrc", "k_gemm.hip")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if rec.get("source_sha256") != sha:
+        return None
+    return rec["bytes_per_launch"]
+
+
 def cpu_baseline(cfg, sample_B, budget_s=30.0):
     """The float64 oracle (as it stands) on the first `sample_B` samples."""
     import numpy as np
@@ -75,6 +91,9 @@ def main():
     ap.add_argument("--T", type=int, default=32)
     ap.add_argument("--cpu-sample", type=int, default=32)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0,
+                    help="only run a plain device copy of this many bytes (3 times): the reference "
+                         "dispatch for scaling FETCH_SIZE / WRITE_SIZE counters to bytes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for {args.gpus}).",
@@ -83,6 +102,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration // 4
+        src = torch.ones(n, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n * 4}))
+        return
 
     import log_space_sum_amd as L
     from workloads import make_config
@@ -162,7 +191,7 @@ def main():
         "kernel_launches_per_step": {k: v[0] // args.steps for k, v in kt.items() if v[0]},
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 3),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": kernel_traffic(dom),
                      "per_launch_gflop": round(per_launch_flops / 1e9, 4),
                      "avg_launch_ms": round(avg_ms, 5)},
         "ll_finite": finite,

@@ -20,7 +20,7 @@ SOURCES = ["pc_compile.cpp", "pc_api.hip", "k_gemm.hip", "k_elem.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-I" + os.path.join(ROOT, "include"), "-Wno-unused-command-line-argument"]
+          "-I" + os.path.join(ROOT, "include"), "-Wno-unused-command-line-argument", "-Wno-inline-asm"]
 
 
 def _run(cmd):

@@ -218,14 +218,14 @@ __global__ void k_exp_pack(SumArgs a) {
     tile[r][lane] = e;
     if (b < a.B_padK)     // node-major copy for every group sharing these children
       for (int q = g; q >= 0; q = a.groups[q].share_next)
-        split_store(e, a.np_direct, a.direct + (a.groups[q].e_row + k) * (int64_t)a.B_padK + b, a.direct_plane);
+        split_store(e, a.np_direct, a.direct + panel(a.groups[q].e_row + k, b, a.direct_rows), a.direct_plane);
   }
   __syncthreads();
   const int NpK = (gr.N + K_PAD - 1) / K_PAD * K_PAD;
   for (int r = w; r < 64; r += 4) {          // r = sample within the tile, lane = child
     const int bb = b0 + r, k = k0 + lane;
     if (k < NpK && bb < a.B_pad)
-      split_store(tile[lane][r], a.np_trans, a.trans + (int64_t)bb * a.trans_cols + gr.e_koff + k, a.trans_plane);
+      split_store(tile[lane][r], a.np_trans, a.trans + panel(bb, gr.e_koff + k, a.B_pad), a.trans_plane);
   }
 }
 
@@ -252,14 +252,14 @@ __global__ void k_g_pack(SumArgs a) {
     }
     tile[r][lane] = gv;
     if (b < a.B_padK)
-      split_store(gv, a.np_direct, a.direct + (gr.g_row + i) * (int64_t)a.B_padK + b, a.direct_plane);
+      split_store(gv, a.np_direct, a.direct + panel(gr.g_row + i, b, a.direct_rows), a.direct_plane);
   }
   __syncthreads();
   const int MpK = (gr.M + K_PAD - 1) / K_PAD * K_PAD;
   for (int r = w; r < 64; r += 4) {
     const int bb = b0 + r, i = i0 + lane;
     if (i < MpK && bb < a.B_pad)
-      split_store(tile[lane][r], a.np_trans, a.trans + (int64_t)bb * a.trans_cols + gr.g_koff + i, a.trans_plane);
+      split_store(tile[lane][r], a.np_trans, a.trans + panel(bb, gr.g_koff + i, a.B_pad), a.trans_plane);
   }
 }
 
@@ -275,17 +275,18 @@ __global__ void k_theta_pack(ThetaArgs a) {
   const int i0 = (lt / ntj) * 64, j0 = (lt % ntj) * 64;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int NpK = (bl.N + K_PAD - 1) / K_PAD * K_PAD, MpK = (bl.M + K_PAD - 1) / K_PAD * K_PAD;
+  const int64_t Mp = (bl.M + ROW_PAD - 1) / ROW_PAD * ROW_PAD, Np = (bl.N + ROW_PAD - 1) / ROW_PAD * ROW_PAD;
   const int j = j0 + lane;
   for (int r = w; r < 64; r += 4) {
     const int i = i0 + r;
     const float x = (i < bl.M && j < bl.N) ? a.params[bl.param_offset + (int64_t)i * bl.N + j] : 0.0f;
     tile[r][lane] = x;
-    if (j < NpK) split_store(x, a.np_fwd, a.theta + bl.th_off + (int64_t)i * NpK + j, a.theta_plane);
+    if (j < NpK) split_store(x, a.np_fwd, a.theta + bl.th_off + panel(i, j, Mp), a.theta_plane);
   }
   __syncthreads();
   for (int r = w; r < 64; r += 4) {
     const int jj = j0 + r, i = i0 + lane;
-    if (i < MpK) split_store(tile[lane][r], a.np_elem, a.thetaT + bl.tht_off + (int64_t)jj * MpK + i, a.thetaT_plane);
+    if (i < MpK) split_store(tile[lane][r], a.np_elem, a.thetaT + bl.tht_off + panel(jj, i, Np), a.thetaT_plane);
   }
 }
 

@@ -18,12 +18,9 @@
 // smallest first, into one float32 accumulator.
 //
 // Tiling: MT x NT output tile per workgroup of 4 waves (2 x 2), each wave a
-// (MT/2) x (NT/2) grid of v_mfma_f32_32x32x16_bf16 blocks.  K is staged
-// through LDS in KT-wide slices, double buffered; the global loads of slice
-// k+2 are issued after slice k+1 is stored, so a whole slice of matrix work
-// covers their latency (scheduling fences keep the compiler from hoisting the
-// LDS stores above the matrix instructions).  LDS rows are padded by 16 bytes
-// so the 128-bit fragment reads of 32 consecutive rows hit distinct banks.
+// (MT/2) x (NT/2) grid of v_mfma_f32_32x32x16_bf16 blocks.  K streams through
+// an LDS ring of NS stages filled by direct global->LDS loads (see Ring):
+// while one KT-wide slice is multiplied, the next NS-1 are in flight.
 //
 // Forward and element-flow products at small output sizes split K over
 // `splitk` workgroups; each writes its partial tile, and the last to arrive
@@ -34,13 +31,14 @@
 // rows, meet in one L2.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "pc_kernels.h"
 
 namespace pc {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float key_to_shift(uint32_t k) {
   uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
@@ -65,80 +63,84 @@ __device__ __forceinline__ int find_last_le(const Rec* recs, int n, int x, F fie
   return lo;
 }
 
-// Start of K slice `kt` of an operand: tied copies are consecutive runs of
-// `kst` slices at a fixed stride (parameter flows); otherwise one run.
-template <int EPI, int KT>
-__device__ __forceinline__ const uint16_t* slice_ptr(const uint16_t* base, int64_t stride, int kst, int kt) {
-  if (EPI == EPI_PARAM) {
-    const int s = kt / kst;
-    return base + s * stride + (kt - s * kst) * KT;
-  }
-  return base + kt * KT;
+// LDS ring of NS stages, each holding one K slice (KT wide) of every plane of
+// both operands, rows unpadded and 16-byte chunks XOR-swizzled by row so the
+// 128-bit fragment reads of consecutive rows hit distinct banks.  Slices are
+// fetched with gfx950's direct global->LDS 16-byte loads: one wave
+// instruction fills 1 KB (64 lanes x 16 B) of a stage, so no registers stage
+// the data and NS-1 slices stay in flight while one is multiplied.
+// The load is issued from inline assembly: the ring tracks its completion
+// with explicit vmcnt waits, and a compiler that cannot tell the stages
+// apart would otherwise drain every in-flight load before each LDS read.
+// (M0, the LDS base of the instruction, has no other user in these kernels.)
+__device__ __forceinline__ void lds_load16(const void* g, const void* lds_dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_dst);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
 }
 
-// Global -> register -> LDS staging and the matrix-core loop of one slice.
 template <int PA, int PB, int MT, int NT, int KT>
-struct Tiles {
-  static constexpr int LDK = KT + 8;
-  static constexpr int ATILE = MT * LDK, BTILE = NT * LDK;
-  static constexpr int CPR = KT / 8;
-  static constexpr int CA = MT * CPR / 256, CB = NT * CPR / 256;
+struct Ring {
+  static constexpr int RB = KT * 2;                 // bytes per row of a slice
+  static constexpr int CPR = RB / 16;               // 16-byte chunks per row (8 or 4)
+  static constexpr int RPI = 1024 / RB;             // rows per wave instruction (8 or 16)
+  static constexpr int AROWS = MT * RB / 2, BROWS = NT * RB / 2;   // elements per plane
+  static constexpr int STAGE = PA * AROWS + PB * BROWS;           // elements per stage
+  static constexpr int IA = MT / RPI, IB = NT / RPI;               // instructions per plane
+  static constexpr int PER_WAVE = (PA * IA + PB * IB) / 4;         // instructions per wave per slice
   static constexpr int FM = MT / 64, FN = NT / 64;
   static constexpr int PMAX = PA > PB ? PA : PB;
 
-  static __device__ __forceinline__ void gload(u32x4_t (&ra)[PA][CA], u32x4_t (&rb)[PB][CB], const uint16_t* Ap,
-                                               const uint16_t* Bp, int64_t pA, int64_t pB, int lda, int ldb,
-                                               int tid) {
-#pragma unroll
-    for (int p = 0; p < PA; ++p)
-#pragma unroll
-      for (int i = 0; i < CA; ++i) {
-        const int c = tid + i * 256, row = c / CPR, col = (c % CPR) * 8;
-        ra[p][i] = *(const u32x4_t*)(Ap + p * pA + (int64_t)row * lda + col);
-      }
-#pragma unroll
-    for (int p = 0; p < PB; ++p)
-#pragma unroll
-      for (int i = 0; i < CB; ++i) {
-        const int c = tid + i * 256, row = c / CPR, col = (c % CPR) * 8;
-        rb[p][i] = *(const u32x4_t*)(Bp + p * pB + (int64_t)row * ldb + col);
-      }
+  static __device__ __forceinline__ int slot(int row, int chunk) {
+    return CPR == 8 ? (chunk ^ (row & 7)) : (chunk ^ ((row >> 1) & 3));
   }
 
-  static __device__ __forceinline__ void lstore(uint16_t* s, const u32x4_t (&ra)[PA][CA], const u32x4_t (&rb)[PB][CB],
-                                                int tid) {
+  // Issue the loads of K slice [k0, k0 + KT) of rows [r0, r0 + MT) of the
+  // A panel (R_A rows) and rows [rb0, rb0 + NT) of the B panel into stage
+  // `st` (uniform arguments).  A slice spans KT / 32 K blocks of its panel.
+  static __device__ __forceinline__ void fetch(uint16_t* st, const uint16_t* Ab, int64_t RA, int64_t ra0, int ka0,
+                                               const uint16_t* Bb, int64_t RB, int64_t rb0, int kb0, int64_t pA,
+                                               int64_t pB, int wave, int lane) {
+    const int rin = lane / CPR, sl = lane % CPR;
+    const uint16_t* a0 = Ab + (((int64_t)(ka0 >> 5) * RA + ra0) << 5);
+    const uint16_t* b0 = Bb + (((int64_t)(kb0 >> 5) * RB + rb0) << 5);
 #pragma unroll
-    for (int p = 0; p < PA; ++p)
-#pragma unroll
-      for (int i = 0; i < CA; ++i) {
-        const int c = tid + i * 256, row = c / CPR, col = (c % CPR) * 8;
-        *(u32x4_t*)(s + p * ATILE + row * LDK + col) = ra[p][i];
+    for (int q0 = 0; q0 < PER_WAVE; ++q0) {
+      const int q = q0 * 4 + wave;                  // instruction index within the slice
+      const uint16_t* src;
+      if (q < PA * IA) {
+        const int p = q / IA, qq = q - p * IA, row = qq * RPI + rin;
+        const int chunk = slot(row, sl);            // the swizzle is an involution
+        src = a0 + p * pA + (chunk >> 2) * (RA << 5) + row * 32 + (chunk & 3) * 8;
+      } else {
+        const int q2 = q - PA * IA, p = q2 / IB, qq = q2 - p * IB, row = qq * RPI + rin;
+        const int chunk = slot(row, sl);
+        src = b0 + p * pB + (chunk >> 2) * (RB << 5) + row * 32 + (chunk & 3) * 8;
       }
-#pragma unroll
-    for (int p = 0; p < PB; ++p)
-#pragma unroll
-      for (int i = 0; i < CB; ++i) {
-        const int c = tid + i * 256, row = c / CPR, col = (c % CPR) * 8;
-        *(u32x4_t*)(s + PA * ATILE + p * BTILE + row * LDK + col) = rb[p][i];
-      }
+      lds_load16(src, st + q * 512);
+    }
   }
 
-  static __device__ __forceinline__ void compute(f32x16_t (&acc)[FM][FN], const uint16_t* s, int wm0, int wn0,
+  static __device__ __forceinline__ void compute(f32x16_t (&acc)[FM][FN], const uint16_t* st, int wm0, int wn0,
                                                  int lane) {
 #pragma unroll
     for (int ks = 0; ks < KT / 16; ++ks) {
       bf16x8_t fa[PA][FM], fb[PB][FN];
-      const int kof = ks * 16 + (lane >> 5) * 8;
+      const int c = ks * 2 + (lane >> 5);
 #pragma unroll
       for (int p = 0; p < PA; ++p)
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-          fa[p][i] = *(const bf16x8_t*)(s + p * ATILE + (wm0 + i * 32 + (lane & 31)) * LDK + kof);
+        for (int i = 0; i < FM; ++i) {
+          const int row = wm0 + i * 32 + (lane & 31);
+          fa[p][i] = *(const bf16x8_t*)(st + p * AROWS + row * (RB / 2) + slot(row, c) * 8);
+        }
 #pragma unroll
       for (int p = 0; p < PB; ++p)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          fb[p][j] = *(const bf16x8_t*)(s + PA * ATILE + p * BTILE + (wn0 + j * 32 + (lane & 31)) * LDK + kof);
+        for (int j = 0; j < FN; ++j) {
+          const int row = wn0 + j * 32 + (lane & 31);
+          fb[p][j] = *(const bf16x8_t*)(st + PA * AROWS + p * BROWS + row * (RB / 2) + slot(row, c) * 8);
+        }
       // cross products of planes, highest order (smallest) first
 #pragma unroll
       for (int o = PMAX - 1; o >= 0; --o)
@@ -157,18 +159,36 @@ struct Tiles {
   }
 };
 
-template <int EPI, int PA, int PB, int MT, int NT, int KT>
+// s_waitcnt immediate waiting until at most n vector-memory operations are
+// outstanding (expcnt and lgkmcnt left at their maxima).
+template <int n>
+struct VmWait {
+  static constexpr int imm = (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
+};
+
+// Workgroup barrier without a memory fence (the ring's loads stay in flight);
+// the signal fences keep the compiler from moving memory operations across it.
+__device__ __forceinline__ void ring_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+template <int EPI, int PA, int PB, int MT, int NT, int KT, int NS>
 __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
   constexpr int WTM = MT / 2, WTN = NT / 2;
   constexpr int FM = WTM / 32, FN = WTN / 32;
-  constexpr int LDK = KT + 8;
-  constexpr int ATILE = MT * LDK, BTILE = NT * LDK;
-  constexpr int STAGE = PA * ATILE + PB * BTILE;
-  constexpr int CPR = KT / 8;                  // 16-byte chunks per row of a slice
-  constexpr int CA = MT * CPR / 256, CB = NT * CPR / 256;
-  constexpr int PMAX = PA > PB ? PA : PB;
   constexpr int SUB = ROW_PAD / MT;            // tiles per 256-row block
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
+  using R = Ring<PA, PB, MT, NT, KT>;
+  constexpr int STAGE = R::STAGE;
+  // one array per stage: the compiler then tells the loads filling one stage
+  // apart from the reads of another and inserts no waits of its own
+  __shared__ __attribute__((aligned(1024))) uint16_t st0[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t st1[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t st2[NS > 2 ? STAGE : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t st3[NS > 3 ? STAGE : 8];
   __shared__ int last_flag;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -182,10 +202,12 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
     tile = logical / S;
     split = logical - tile * S;
   }
-  const uint16_t* A0;
-  const uint16_t* B0;
-  int lda, ldb, kst, kbeg, kend, m0, n0;
-  int64_t astride = 0, bstride = 0;            // per tied copy (parameter flows)
+  // operand panels: base, rows, first row of the tile, first K of the range
+  const uint16_t* Ab;
+  const uint16_t* Bb;
+  int64_t RA, RB, ra0, rb0;
+  int ka0, kb0, kst, kbeg, kend, m0, n0;
+  int64_t acopy = 0, bcopy = 0;                // row step per tied copy (parameter flows)
   const GroupRec* gr = nullptr;
   const BlockRec* bl = nullptr;
   if (EPI == EPI_FWD || EPI == EPI_ELEM) {
@@ -199,19 +221,24 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
     gr = a.groups + g;
     bl = a.blocks + gr->block;
     n0 = nt * NT;
+    RB = a.B_pad;
+    rb0 = n0;
     if (EPI == EPI_FWD) {
       m0 = (gt - gr->mt_start * SUB) * MT;
-      lda = (gr->N + K_PAD - 1) / K_PAD * K_PAD;
-      A0 = a.opA + bl->th_off + (int64_t)m0 * lda;
-      B0 = a.opB + (int64_t)n0 * a.ldb + gr->e_koff;
+      kst = (gr->N + K_PAD - 1) / K_PAD * K_PAD / KT;
+      Ab = a.opA + bl->th_off;
+      RA = (bl->M + ROW_PAD - 1) / ROW_PAD * ROW_PAD;
+      kb0 = gr->e_koff;
     } else {
       m0 = (gt - gr->ct_start * SUB) * MT;
-      lda = (gr->M + K_PAD - 1) / K_PAD * K_PAD;
-      A0 = a.opA + bl->tht_off + (int64_t)m0 * lda;
-      B0 = a.opB + (int64_t)n0 * a.ldb + gr->g_koff;
+      kst = (gr->M + K_PAD - 1) / K_PAD * K_PAD / KT;
+      Ab = a.opA + bl->tht_off;
+      RA = (bl->N + ROW_PAD - 1) / ROW_PAD * ROW_PAD;
+      kb0 = gr->g_koff;
     }
-    ldb = a.ldb;
-    kst = lda / KT;
+    ra0 = m0;
+    ka0 = 0;
+    Bb = a.opB;
     kbeg = split * kst / S;
     kend = (split + 1) * kst / S;
   } else {
@@ -225,14 +252,18 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
     const int lt = tile - ((MT == 256) ? bl->pt256 : bl->pt128);
     m0 = (lt / ntn) * MT;
     n0 = (lt % ntn) * NT;
-    lda = ldb = a.B_padK;
     kst = a.B_padK / KT;
     kbeg = 0;
     kend = bl->ncopies * kst;
-    A0 = a.opA + (bl->g_base + m0) * (int64_t)a.B_padK;
-    B0 = a.opB + (bl->e_base + n0) * (int64_t)a.B_padK;
-    astride = (int64_t)Mp * a.B_padK;
-    bstride = (int64_t)Np * a.B_padK;
+    Ab = a.opA;
+    Bb = a.opB;
+    RA = a.rowsA;
+    RB = a.rowsB;
+    ra0 = bl->g_base + m0;
+    rb0 = bl->e_base + n0;
+    acopy = Mp;
+    bcopy = Np;
+    ka0 = kb0 = 0;
   }
 
   f32x16_t acc[FM][FN];
@@ -243,34 +274,50 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  u32x4_t ra[PA][CA], rb[PB][CB];
   const int64_t pA = a.planeA, pB = a.planeB;
   const int n = kend - kbeg;
-  using T = Tiles<PA, PB, MT, NT, KT>;
-  if (n > 0) {
-    // Branch-free pipeline: slice it+2 is fetched while slice it is multiplied
-    // (the fetch index is clamped at the last slice, whose extra copy lands in
-    // the idle buffer and is never read).
-    T::gload(ra, rb, slice_ptr<EPI, KT>(A0, astride, kst, kbeg), slice_ptr<EPI, KT>(B0, bstride, kst, kbeg),
-             pA, pB, lda, ldb, tid);
-    T::lstore(lds, ra, rb, tid);
-    const int k1 = min(kbeg + 1, kend - 1);
-    T::gload(ra, rb, slice_ptr<EPI, KT>(A0, astride, kst, k1), slice_ptr<EPI, KT>(B0, bstride, kst, k1), pA, pB,
-             lda, ldb, tid);
-    __syncthreads();
-    for (int it = 0; it < n; ++it) {
-      T::compute(acc, lds + (it & 1) * STAGE, wm0, wn0, lane);
-      __builtin_amdgcn_sched_barrier(0);
-      T::lstore(lds + ((it + 1) & 1) * STAGE, ra, rb, tid);
-      __builtin_amdgcn_sched_barrier(0);
-      const int k2 = min(kbeg + it + 2, kend - 1);
-      T::gload(ra, rb, slice_ptr<EPI, KT>(A0, astride, kst, k2), slice_ptr<EPI, KT>(B0, bstride, kst, k2), pA,
-               pB, lda, ldb, tid);
-      __syncthreads();
+  auto stage = [&](int j) -> uint16_t* { return j == 0 ? st0 : j == 1 ? st1 : j == 2 ? st2 : st3; };
+  auto fetch = [&](int j, int it) {
+    const int kt = min(kbeg + it, kend - 1);   // clamped: a copy past the end is never read
+    if (EPI == EPI_PARAM) {
+      const int s = kt / kst, kk = (kt - s * kst) * KT;
+      R::fetch(stage(j), Ab, RA, ra0 + s * acopy, kk, Bb, RB, rb0 + s * bcopy, kk, pA, pB, wave, lane);
+    } else {
+      R::fetch(stage(j), Ab, RA, ra0, ka0 + kt * KT, Bb, RB, rb0, kb0 + kt * KT, pA, pB, wave, lane);
     }
+  };
+  // one pipeline step on slice `it`, held in stage J: wait until it has
+  // landed (at most NS-2 newer slices outstanding), barrier (every wave is
+  // also done with the stage read in the previous step), refill that stage
+  // with slice it+NS-1, multiply slice it.
+  auto step = [&](auto J, int it) {
+    constexpr int j = decltype(J)::value;
+    __builtin_amdgcn_s_waitcnt(VmWait<(NS - 2) * R::PER_WAVE>::imm);
+    ring_barrier();
+    fetch((j + NS - 1) % NS, it + NS - 1);
+    R::compute(acc, stage(j), wm0, wn0, lane);
+  };
+  if (n > 0) {
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j) fetch(j, j);
+    for (int it = 0; it < n; it += NS) {
+      step(std::integral_constant<int, 0>(), it);
+      if (it + 1 < n) step(std::integral_constant<int, 1>(), it + 1);
+      if constexpr (NS > 2)
+        if (it + 2 < n) step(std::integral_constant<int, 2 % NS>(), it + 2);
+      if constexpr (NS > 3)
+        if (it + 3 < n) step(std::integral_constant<int, 3 % NS>(), it + 3);
+    }
+    __builtin_amdgcn_s_waitcnt(0);       // no load may still target LDS when the workgroup ends
   }
 
   // ---- split-K: the last workgroup of a tile adds the partials in order -----
+  // Partials are published with device-scope atomic stores (written through
+  // to the device coherence point, so no cache-wide write-back is needed),
+  // completed (vmcnt 0) before the arrival counter moves; the last arrival
+  // reads them back with device-scope atomic loads.  A __threadfence() here
+  // would write back and invalidate the whole L2 of the XCD under every
+  // other workgroup still streaming operands through it.
   if (EPI != EPI_PARAM && S > 1) {
     constexpr int NREG = FM * FN * 16;
     float* mine = a.partials + ((int64_t)tile * S + split) * (NREG * 256);
@@ -279,13 +326,16 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mine[((i * FN + j) * 16 + r) * 256 + tid] = acc[i][j][r];
-    __threadfence();
+        for (int r = 0; r < 16; ++r)
+          __hip_atomic_store(mine + ((i * FN + j) * 16 + r) * 256 + tid, acc[i][j][r], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (tid == 0) last_flag = (atomicAdd(a.counters + tile, 1u) == (unsigned)(S - 1));
+    if (tid == 0)
+      last_flag = (__hip_atomic_fetch_add(a.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                   (unsigned)(S - 1));
     __syncthreads();
     if (!last_flag) return;
-    __threadfence();
     const float* base = a.partials + (int64_t)tile * S * (NREG * 256);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -296,10 +346,13 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
           const int idx = ((i * FN + j) * 16 + r) * 256 + tid;
           const float own = acc[i][j][r];
           float sum = 0.0f;
-          for (int q = 0; q < S; ++q) sum += (q == split) ? own : base[(int64_t)q * (NREG * 256) + idx];
+          for (int q = 0; q < S; ++q)
+            sum += (q == split) ? own
+                                : __hip_atomic_load(base + (int64_t)q * (NREG * 256) + idx, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
           acc[i][j][r] = sum;
         }
-    if (tid == 0) a.counters[tile] = 0u;      // ready for the next launch
+    if (tid == 0) __hip_atomic_store(a.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // ---- epilogue ------------------------------------------------------------
@@ -345,22 +398,34 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
 
 // Tile shapes: forward / element flows 128 x 128 (split over K when the
 // output has few tiles); parameter flows 256 x 256 when every block is at
-// least that large and the planes fit LDS, else 128 x 128.
+// least that large and the planes fit LDS, else 128 x 128.  KT is 64 when a
+// stage of that width is at most 48 KB, else 32; NS stages fill up to 160 KB.
+template <int PA, int PB, int MT, int NT>
+struct Shape {
+  static constexpr int KT = ((PA * MT + PB * NT) * 64 * 2 <= 48 * 1024) ? 64 : 32;
+  static constexpr int STAGE_BYTES = (PA * MT + PB * NT) * KT * 2;
+  static constexpr int NSR = (160 * 1024 - 1024) / STAGE_BYTES;
+  static constexpr int NS = NSR > 4 ? 4 : NSR;
+};
+
+template <int EPI, int PA, int PB, int MT, int NT>
+static void launch_shape(int grid, const GemmArgs& a, hipStream_t s) {
+  using Sh = Shape<PA, PB, MT, NT>;
+  static_assert(Sh::NS >= 2, "LDS ring needs two stages");
+  hipLaunchKernelGGL((k_gemm<EPI, PA, PB, MT, NT, Sh::KT, Sh::NS>), dim3(grid), dim3(256), 0, s, a);
+}
+
 template <int EPI, int PA, int PB>
 static void launch3(int tiles, int big, const GemmArgs& a, hipStream_t s) {
   constexpr bool wide = (PA + PB) <= 3;
   const int grid = tiles * (EPI == EPI_PARAM ? 1 : a.splitk);
-  if constexpr (wide) {
-    if constexpr (EPI == EPI_PARAM) {
-      if (big) {
-        hipLaunchKernelGGL((k_gemm<EPI, PA, PB, 256, 256, 32>), dim3(grid), dim3(256), 0, s, a);
-        return;
-      }
+  if constexpr (EPI == EPI_PARAM && wide) {
+    if (big) {
+      launch_shape<EPI, PA, PB, 256, 256>(grid, a, s);
+      return;
     }
-    hipLaunchKernelGGL((k_gemm<EPI, PA, PB, 128, 128, 64>), dim3(grid), dim3(256), 0, s, a);
-  } else {
-    hipLaunchKernelGGL((k_gemm<EPI, PA, PB, 128, 128, 32>), dim3(grid), dim3(256), 0, s, a);
   }
+  launch_shape<EPI, PA, PB, 128, 128>(grid, a, s);
 }
 
 template <int EPI>

@@ -290,6 +290,8 @@ GemmArgs gemm_common(const Call& c) {
   a.B = c.v.B;
   a.B_pad = c.v.B_pad;
   a.B_padK = c.v.B_padK;
+  a.rowsA = c.h->garena_rows;
+  a.rowsB = c.h->earena_rows;
   a.ntiles = c.v.B_pad / 128;
   a.blocks = c.h->d_blocks;
   a.partials = c.v.partials;
@@ -525,7 +527,7 @@ int pc_forward(pc_handle hh, int batch, const int32_t* tokens, const float* para
         a.np_direct = p.pl[GK_PARAM][1];
         a.trans = v.ebt;
         a.trans_plane = v.ebt_plane;
-        a.trans_cols = sp.ebt_cols;
+        a.direct_rows = h->earena_rows;
         a.np_trans = p.pl[GK_FWD][1];
         {
           Timed t(h, KK_COLMAX, c.s);
@@ -610,7 +612,7 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
         a.np_direct = p.pl[GK_PARAM][0];
         a.trans = v.gbt;
         a.trans_plane = v.gbt_plane;
-        a.trans_cols = sp.gbt_cols;
+        a.direct_rows = h->garena_rows;
         a.np_trans = p.pl[GK_ELEM][1];
         {
           Timed t(h, KK_GPACK, c.s);
@@ -670,7 +672,8 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
       g.planeB = v.earena_plane;
       g.params = params;
       g.pflows = param_flows;
-      const bool big = h->min_block_dim >= 256 && p.pl[GK_PARAM][0] + p.pl[GK_PARAM][1] <= 3;
+      // operand rows are padded to 256, so 256 x 256 tiles fit every block
+      const bool big = p.pl[GK_PARAM][0] + p.pl[GK_PARAM][1] <= 3;
       g.splitk = 1;
       Timed t(h, KK_PARAM, c.s);
       launch_gemm(EPI_PARAM, p.pl[GK_PARAM][0], p.pl[GK_PARAM][1], big ? h->param_tiles256 : h->param_tiles128,

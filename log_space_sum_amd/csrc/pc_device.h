@@ -5,6 +5,13 @@
 #pragma once
 #include <stdint.h>
 
+#ifndef __HIPCC__
+#ifndef __host__
+#define __host__
+#define __device__
+#endif
+#endif
+
 namespace pc {
 
 // Padding of every bfloat16 operand kept in the workspace: rows (the M / N
@@ -13,8 +20,14 @@ namespace pc {
 // checks in their main loop; pads hold zeros.
 constexpr int ROW_PAD = 256;
 constexpr int K_PAD = 64;
+// Operands are stored as K-blocked panels: element (r, k) of an operand with
+// R (padded) rows lives at ((k / KB) * R + r) * KB + k % KB.  The rows of one
+// K block are contiguous, so a tile's K slice is one contiguous run and every
+// 1 KB load instruction of the product kernel reads whole cache lines.
+constexpr int KB = 32;
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+__host__ __device__ inline int64_t panel(int64_t r, int64_t k, int64_t R) { return ((k >> 5) * R + r) * KB + (k & 31); }
 
 // One sum group (node block) of a sum layer.
 struct GroupRec {

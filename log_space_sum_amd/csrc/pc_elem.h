@@ -47,7 +47,8 @@ struct SumArgs {
   int32_t np_direct;
   uint16_t* trans;
   int64_t trans_plane;
-  int32_t trans_cols, np_trans;
+  int64_t direct_rows;      // panel rows of the node-major output
+  int32_t np_trans;
   // overlapping-children reduction
   int32_t nuniq, store;
   const int32_t* red_child;

@@ -11,6 +11,7 @@ enum Epi { EPI_FWD = 0, EPI_ELEM = 1, EPI_PARAM = 2 };
 // Arguments of the MFMA product kernel (see k_gemm.hip).
 struct GemmArgs {
   int32_t B, B_pad, B_padK;
+  int64_t rowsA, rowsB;        // panel rows of the kept operands (parameter flows)
   int32_t ntiles;               // tiles along the batch (forward / element flows)
   int32_t splitk;               // workgroups sharing one tile's K range (forward / element flows)
   int32_t ngroups;              // groups of the layer, or blocks (parameter flows)
