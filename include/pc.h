@@ -193,6 +193,19 @@ int pc_get_precision(pc_handle h, int* mode);
  * rounding (at most 2^-8 relative); fp32-level (3,3) everywhere.  Errors: PC_ERR_INVALID_ARG for other counts or kinds. */
 int pc_set_split(pc_handle h, int mode, int gemm_kind, int planes_a, int planes_b);
 
+/* Product-kernel tuning (advanced; results change only by float32 summation
+ * order).  PC_OPT_LAYER_TILE: output tile of the per-layer forward and
+ * element-flow products, 0 automatic (128 x 128), 1 128 x 128, 2 256 x 128.
+ * PC_OPT_PARAM_TILE: tile of the parameter-flow product, 0 automatic
+ * (256 x 256 when the operand split allows, else 128 x 128), 1 128 x 128.
+ * PC_OPT_SPLIT_MAX: largest K split of a per-layer product (1, 2, 4 or 8;
+ * default 8).  Changing an option can change pc_workspace_bytes.
+ * Errors: PC_ERR_INVALID_ARG (unknown option or value). */
+#define PC_OPT_LAYER_TILE 0
+#define PC_OPT_PARAM_TILE 1
+#define PC_OPT_SPLIT_MAX  2
+int pc_set_option(pc_handle h, int option, int value);
+
 /* Bytes of workspace pc_forward / pc_backward need for `batch` samples in the
  * handle's current precision mode (batch < 16 counts as fp32-level).  The
  * workspace holds the bfloat16 operand planes (weights, exponentiated children

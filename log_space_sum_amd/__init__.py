@@ -67,6 +67,7 @@ EXPORTS = {
     "pc_set_precision": (C.c_int, [C.c_void_p, C.c_int]),
     "pc_get_precision": (C.c_int, [C.c_void_p, C.POINTER(C.c_int)]),
     "pc_set_split": (C.c_int, [C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_int]),
+    "pc_set_option": (C.c_int, [C.c_void_p, C.c_int, C.c_int]),
     "pc_workspace_bytes": (C.c_int, [C.c_void_p, C.c_int, C.POINTER(C.c_size_t)]),
     "pc_forward": (C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                              C.POINTER(pc_lowrank_io), C.c_void_p, C.c_size_t, C.c_void_p]),
@@ -209,6 +210,16 @@ def pc_set_split(h: Handle, mode, gemm_kind, planes_a: int, planes_b: int):
     mode = MODES.get(mode, mode) if isinstance(mode, str) else mode
     gemm_kind = GEMM_KINDS.get(gemm_kind, gemm_kind) if isinstance(gemm_kind, str) else gemm_kind
     _check(lib().pc_set_split(h.ptr, int(mode), int(gemm_kind), int(planes_a), int(planes_b)))
+
+
+OPTIONS = {"layer_tile": 0, "param_tile": 1, "split_max": 2}
+
+
+def pc_set_option(h: Handle, option, value: int):
+    """Product-kernel tuning: layer_tile (0 auto, 1 128x128, 2 256x128),
+    param_tile (0 auto, 1 128x128), split_max (1, 2, 4, 8)."""
+    option = OPTIONS.get(option, option) if isinstance(option, str) else option
+    _check(lib().pc_set_option(h.ptr, int(option), int(value)))
 
 
 def pc_workspace_bytes(h: Handle, batch: int) -> int:

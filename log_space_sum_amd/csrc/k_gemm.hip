@@ -17,21 +17,26 @@
 // is below the larger plane count (3 products for 2x2 planes, 6 for 3x3),
 // smallest first, into one float32 accumulator.
 //
-// Tiling: MT x NT output tile per workgroup of 4 waves (2 x 2), each wave a
-// (MT/2) x (NT/2) grid of v_mfma_f32_32x32x16_bf16 blocks.  K streams through
-// an LDS ring of NS stages filled by direct global->LDS loads (see Ring):
-// while one KT-wide slice is multiplied, the next NS-1 are in flight.
+// Tiling: MT x NT output tile per workgroup of 4 waves laid out WM x (4/WM),
+// each wave a grid of v_mfma_f32_32x32x16_bf16 blocks.  K streams through an
+// LDS ring of NS stages filled by direct global->LDS loads: while one KT-wide
+// slice is multiplied, the next NS-1 are in flight.  Inside a slice the
+// fragments of the next 16-wide K step are read from LDS while the matrix
+// instructions of the current one run, and the loads of the slice NS-1 ahead
+// are issued between them; the ring barrier sits in the middle of a slice's
+// last matrix instructions, so its wait overlaps them.
 //
-// Forward and element-flow products at small output sizes split K over
-// `splitk` workgroups; each writes its partial tile, and the last to arrive
-// (arrival counter per tile) adds the partials in split order and runs the
-// epilogue, so results are deterministic.  Workgroups are renumbered so each
-// XCD (dispatch is round robin over the 8 XCDs) gets a contiguous run of
-// logical tiles: the splits of a tile, and neighbouring tiles sharing weight
-// rows, meet in one L2.
+// Forward and element-flow products of one layer have few output tiles; they
+// split K over `splitk` workgroups.  Every split writes its partial tile, and
+// the last to arrive (arrival counter per tile) adds all partials in split
+// order and runs the epilogue, so results are deterministic.  Workgroups are
+// renumbered so each XCD (dispatch is round robin over the 8 XCDs) gets a
+// contiguous run of logical tiles: the splits of a tile, and neighbouring
+// tiles sharing weight rows, meet in one L2.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "pc_kernels.h"
 
@@ -39,6 +44,16 @@ namespace pc {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+template <int... I, typename F>
+__device__ __forceinline__ void sfor_impl(std::integer_sequence<int, I...>, F&& f) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+// f(integral_constant<0>), ..., f(integral_constant<N-1>), fully unrolled
+template <int N, typename F>
+__device__ __forceinline__ void sfor(F&& f) {
+  sfor_impl(std::make_integer_sequence<int, N>{}, f);
+}
 
 __device__ __forceinline__ float key_to_shift(uint32_t k) {
   uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
@@ -63,107 +78,30 @@ __device__ __forceinline__ int find_last_le(const Rec* recs, int n, int x, F fie
   return lo;
 }
 
-// LDS ring of NS stages, each holding one K slice (KT wide) of every plane of
-// both operands, rows unpadded and 16-byte chunks XOR-swizzled by row so the
-// 128-bit fragment reads of consecutive rows hit distinct banks.  Slices are
-// fetched with gfx950's direct global->LDS 16-byte loads: one wave
-// instruction fills 1 KB (64 lanes x 16 B) of a stage, so no registers stage
-// the data and NS-1 slices stay in flight while one is multiplied.
-// The load is issued from inline assembly: the ring tracks its completion
-// with explicit vmcnt waits, and a compiler that cannot tell the stages
-// apart would otherwise drain every in-flight load before each LDS read.
-// (M0, the LDS base of the instruction, has no other user in these kernels.)
-__device__ __forceinline__ void lds_load16(const void* g, const void* lds_dst) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_dst);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
+// One 16-byte direct global->LDS load per lane: lane L writes LDS bytes
+// [m0 + 16 L, m0 + 16 L + 16) from sbase + voff.  Issued from inline assembly:
+// the ring tracks its completion with explicit vmcnt waits, and a compiler
+// that cannot tell the stages apart would otherwise drain every in-flight
+// load before each LDS read.  (M0, the LDS base of the instruction, has no
+// other user in these kernels.)
+__device__ __forceinline__ void lds_load16(const void* sbase, uint32_t voff, uint32_t lds_byte) {
+  const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_byte);
+  // the base is uniform: pin it to scalar registers (readfirstlane returns a
+  // signed int, so each half goes through uint32_t before widening)
+  const uint64_t b = (uint64_t)(uintptr_t)sbase;
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint64_t sb = (hi << 32) | lo;
+  // one wait state between the SALU write of M0 and the LDS DMA reading it
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sb), "s"(m0)
+               : "memory", "m0");
 }
 
-template <int PA, int PB, int MT, int NT, int KT>
-struct Ring {
-  static constexpr int RB = KT * 2;                 // bytes per row of a slice
-  static constexpr int CPR = RB / 16;               // 16-byte chunks per row (8 or 4)
-  static constexpr int RPI = 1024 / RB;             // rows per wave instruction (8 or 16)
-  static constexpr int AROWS = MT * RB / 2, BROWS = NT * RB / 2;   // elements per plane
-  static constexpr int STAGE = PA * AROWS + PB * BROWS;           // elements per stage
-  static constexpr int IA = MT / RPI, IB = NT / RPI;               // instructions per plane
-  static constexpr int PER_WAVE = (PA * IA + PB * IB) / 4;         // instructions per wave per slice
-  static constexpr int FM = MT / 64, FN = NT / 64;
-  static constexpr int PMAX = PA > PB ? PA : PB;
-
-  static __device__ __forceinline__ int slot(int row, int chunk) {
-    return CPR == 8 ? (chunk ^ (row & 7)) : (chunk ^ ((row >> 1) & 3));
-  }
-
-  // Issue the loads of K slice [k0, k0 + KT) of rows [r0, r0 + MT) of the
-  // A panel (R_A rows) and rows [rb0, rb0 + NT) of the B panel into stage
-  // `st` (uniform arguments).  A slice spans KT / 32 K blocks of its panel.
-  static __device__ __forceinline__ void fetch(uint16_t* st, const uint16_t* Ab, int64_t RA, int64_t ra0, int ka0,
-                                               const uint16_t* Bb, int64_t RB, int64_t rb0, int kb0, int64_t pA,
-                                               int64_t pB, int wave, int lane) {
-    const int rin = lane / CPR, sl = lane % CPR;
-    const uint16_t* a0 = Ab + (((int64_t)(ka0 >> 5) * RA + ra0) << 5);
-    const uint16_t* b0 = Bb + (((int64_t)(kb0 >> 5) * RB + rb0) << 5);
-#pragma unroll
-    for (int q0 = 0; q0 < PER_WAVE; ++q0) {
-      const int q = q0 * 4 + wave;                  // instruction index within the slice
-      const uint16_t* src;
-      if (q < PA * IA) {
-        const int p = q / IA, qq = q - p * IA, row = qq * RPI + rin;
-        const int chunk = slot(row, sl);            // the swizzle is an involution
-        src = a0 + p * pA + (chunk >> 2) * (RA << 5) + row * 32 + (chunk & 3) * 8;
-      } else {
-        const int q2 = q - PA * IA, p = q2 / IB, qq = q2 - p * IB, row = qq * RPI + rin;
-        const int chunk = slot(row, sl);
-        src = b0 + p * pB + (chunk >> 2) * (RB << 5) + row * 32 + (chunk & 3) * 8;
-      }
-      lds_load16(src, st + q * 512);
-    }
-  }
-
-  static __device__ __forceinline__ void compute(f32x16_t (&acc)[FM][FN], const uint16_t* st, int wm0, int wn0,
-                                                 int lane) {
-#pragma unroll
-    for (int ks = 0; ks < KT / 16; ++ks) {
-      bf16x8_t fa[PA][FM], fb[PB][FN];
-      const int c = ks * 2 + (lane >> 5);
-#pragma unroll
-      for (int p = 0; p < PA; ++p)
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const int row = wm0 + i * 32 + (lane & 31);
-          fa[p][i] = *(const bf16x8_t*)(st + p * AROWS + row * (RB / 2) + slot(row, c) * 8);
-        }
-#pragma unroll
-      for (int p = 0; p < PB; ++p)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int row = wn0 + j * 32 + (lane & 31);
-          fb[p][j] = *(const bf16x8_t*)(st + PA * AROWS + p * BROWS + row * (RB / 2) + slot(row, c) * 8);
-        }
-      // cross products of planes, highest order (smallest) first
-#pragma unroll
-      for (int o = PMAX - 1; o >= 0; --o)
-#pragma unroll
-        for (int pa = 0; pa < PA; ++pa) {
-          const int pb = o - pa;
-          if (pb >= 0 && pb < PB) {
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-              for (int j = 0; j < FN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[pa][i], fb[pb][j], acc[i][j], 0, 0, 0);
-          }
-        }
-    }
-  }
-};
-
-// s_waitcnt immediate waiting until at most n vector-memory operations are
-// outstanding (expcnt and lgkmcnt left at their maxima).
-template <int n>
-struct VmWait {
-  static constexpr int imm = (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
+// s_waitcnt immediate: at most `vm` vector-memory operations outstanding, no
+// LDS operation outstanding (expcnt left at its maximum).
+template <int vm>
+struct WaitVmLgkm {
+  static constexpr int imm = (vm & 15) | ((vm >> 4) << 14) | (7 << 4);
 };
 
 // Workgroup barrier without a memory fence (the ring's loads stay in flight);
@@ -176,23 +114,77 @@ __device__ __forceinline__ void ring_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <int EPI, int PA, int PB, int MT, int NT, int KT, int NS>
+// Plane pairs (pa, pb) whose product is accumulated, highest order first.
+template <int PA, int PB>
+struct Pairs {
+  static constexpr int PMAX = PA > PB ? PA : PB;
+  static constexpr int count() {
+    int n = 0;
+    for (int o = PMAX - 1; o >= 0; --o)
+      for (int pa = 0; pa < PA; ++pa)
+        if (o - pa >= 0 && o - pa < PB) ++n;
+    return n;
+  }
+  static constexpr int N = count();
+  static constexpr int at(int t, int which) {
+    int n = 0;
+    for (int o = PMAX - 1; o >= 0; --o)
+      for (int pa = 0; pa < PA; ++pa)
+        if (o - pa >= 0 && o - pa < PB) {
+          if (n == t) return which == 0 ? pa : o - pa;
+          ++n;
+        }
+    return 0;
+  }
+};
+
+// LDS ring geometry.  A stage holds one K slice (KT wide) of every plane of
+// both operands, rows unpadded (KT * 2 bytes), 16-byte chunks XOR-swizzled by
+// row so that the 128-bit fragment reads of 16 consecutive rows touch 16
+// distinct chunk slots of 64 banks (and those of 8 consecutive rows 8 distinct
+// slots of 32 banks).  One wave load instruction fills 1 KB (64 lanes x 16 B)
+// of a stage: RPI rows.
+template <int PA, int PB, int MT, int NT, int KT>
+struct Ring {
+  static constexpr int RB = KT * 2;                 // bytes per row of a slice
+  static constexpr int CPR = RB / 16;               // 16-byte chunks per row (8 or 4)
+  static constexpr int RPI = 1024 / RB;             // rows per load instruction (8 or 16)
+  static constexpr int AEL = MT * KT, BEL = NT * KT;                 // elements per plane
+  static constexpr int STAGE = PA * AEL + PB * BEL;                   // elements per stage
+  static constexpr int IA = MT / RPI, IB = NT / RPI;                 // instructions per plane
+  static constexpr int PER_WAVE = (PA * IA + PB * IB) / 4;           // instructions per wave per slice
+  static constexpr int QA = PA * IA / 4;                              // of which A
+  static_assert(IA % 4 == 0 && IB % 4 == 0, "each wave loads whole instructions of one plane");
+
+  static __device__ __forceinline__ int swz(int row) {
+    return CPR == 8 ? ((row & 7) ^ ((row >> 3) & 1)) : (((row >> 1) ^ (row >> 2)) & 3);
+  }
+};
+
+template <int EPI, int PA, int PB, int MT, int NT, int WM, int KT, int NS>
 __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
-  constexpr int WTM = MT / 2, WTN = NT / 2;
+  constexpr int WN = 4 / WM;
+  constexpr int WTM = MT / WM, WTN = NT / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   constexpr int SUB = ROW_PAD / MT;            // tiles per 256-row block
   using R = Ring<PA, PB, MT, NT, KT>;
-  constexpr int STAGE = R::STAGE;
-  // one array per stage: the compiler then tells the loads filling one stage
-  // apart from the reads of another and inserts no waits of its own
-  __shared__ __attribute__((aligned(1024))) uint16_t st0[STAGE];
-  __shared__ __attribute__((aligned(1024))) uint16_t st1[STAGE];
-  __shared__ __attribute__((aligned(1024))) uint16_t st2[NS > 2 ? STAGE : 8];
-  __shared__ __attribute__((aligned(1024))) uint16_t st3[NS > 3 ? STAGE : 8];
+  using PP = Pairs<PA, PB>;
+  constexpr int KS = KT / 16;                  // matrix K steps per slice
+  constexpr int NMF = PP::N * FM * FN;         // matrix instructions per K step
+  constexpr int NRD = PA * FM + PB * FN;       // fragment reads per K step
+  constexpr int PW = R::PER_WAVE;
+  constexpr int NREG = FM * FN * 16;
+  static_assert(KS % 2 == 0, "fragment buffers alternate per K step");
+  static_assert(WM * WN == 4 && FM >= 1 && FN >= 1, "4 waves");
+  // the ring: NS stages (the loads filling it are issued from inline
+  // assembly, so the compiler tracks no dependence between a stage being
+  // filled and the reads of another)
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[NS * R::STAGE];
   __shared__ int last_flag;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm0 = (wave >> 1) * WTM, wn0 = (wave & 1) * WTN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+  const int wm0 = (wave / WN) * WTM, wn0 = (wave % WN) * WTN;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
 
   // ---- locate the problem, the tile and the K range ------------------------
@@ -202,14 +194,14 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
     tile = logical / S;
     split = logical - tile * S;
   }
-  // operand panels: base, rows, first row of the tile, first K of the range
   const uint16_t* Ab;
   const uint16_t* Bb;
   int64_t RA, RB, ra0, rb0;
-  int ka0, kb0, kst, kbeg, kend, m0, n0;
+  int kst, kbeg, kend, m0, n0;
   int64_t acopy = 0, bcopy = 0;                // row step per tied copy (parameter flows)
-  const GroupRec* gr = nullptr;
-  const BlockRec* bl = nullptr;
+  int ka0 = 0, kb0 = 0;
+  GroupRec gr{};
+  BlockRec bl{};
   if (EPI == EPI_FWD || EPI == EPI_ELEM) {
     const int gt = tile / a.ntiles, nt = tile - gt * a.ntiles;
     const int unit = gt / SUB;
@@ -218,26 +210,25 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
       g = find_last_le(a.groups, a.ngroups, unit, [](const GroupRec& r) { return r.mt_start; });
     else
       g = find_last_le(a.groups, a.ngroups, unit, [](const GroupRec& r) { return r.ct_start; });
-    gr = a.groups + g;
-    bl = a.blocks + gr->block;
+    gr = a.groups[g];
+    bl = a.blocks[gr.block];
     n0 = nt * NT;
     RB = a.B_pad;
     rb0 = n0;
     if (EPI == EPI_FWD) {
-      m0 = (gt - gr->mt_start * SUB) * MT;
-      kst = (gr->N + K_PAD - 1) / K_PAD * K_PAD / KT;
-      Ab = a.opA + bl->th_off;
-      RA = (bl->M + ROW_PAD - 1) / ROW_PAD * ROW_PAD;
-      kb0 = gr->e_koff;
+      m0 = (gt - gr.mt_start * SUB) * MT;
+      kst = (gr.N + K_PAD - 1) / K_PAD * K_PAD / KT;
+      Ab = a.opA + bl.th_off;
+      RA = (bl.M + ROW_PAD - 1) / ROW_PAD * ROW_PAD;
+      kb0 = gr.e_koff;
     } else {
-      m0 = (gt - gr->ct_start * SUB) * MT;
-      kst = (gr->M + K_PAD - 1) / K_PAD * K_PAD / KT;
-      Ab = a.opA + bl->tht_off;
-      RA = (bl->N + ROW_PAD - 1) / ROW_PAD * ROW_PAD;
-      kb0 = gr->g_koff;
+      m0 = (gt - gr.ct_start * SUB) * MT;
+      kst = (gr.M + K_PAD - 1) / K_PAD * K_PAD / KT;
+      Ab = a.opA + bl.tht_off;
+      RA = (bl.N + ROW_PAD - 1) / ROW_PAD * ROW_PAD;
+      kb0 = gr.g_koff;
     }
     ra0 = m0;
-    ka0 = 0;
     Bb = a.opB;
     kbeg = split * kst / S;
     kend = (split + 1) * kst / S;
@@ -245,25 +236,48 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
     const int b = (MT == 256)
         ? find_last_le(a.blocks, a.ngroups, tile, [](const BlockRec& r) { return r.pt256; })
         : find_last_le(a.blocks, a.ngroups, tile, [](const BlockRec& r) { return r.pt128; });
-    bl = a.blocks + b;
-    const int Mp = (bl->M + ROW_PAD - 1) / ROW_PAD * ROW_PAD;
-    const int Np = (bl->N + ROW_PAD - 1) / ROW_PAD * ROW_PAD;
+    bl = a.blocks[b];
+    const int Mp = (bl.M + ROW_PAD - 1) / ROW_PAD * ROW_PAD;
+    const int Np = (bl.N + ROW_PAD - 1) / ROW_PAD * ROW_PAD;
     const int ntn = Np / NT;
-    const int lt = tile - ((MT == 256) ? bl->pt256 : bl->pt128);
+    const int lt = tile - ((MT == 256) ? bl.pt256 : bl.pt128);
     m0 = (lt / ntn) * MT;
     n0 = (lt % ntn) * NT;
     kst = a.B_padK / KT;
     kbeg = 0;
-    kend = bl->ncopies * kst;
+    kend = bl.ncopies * kst;
     Ab = a.opA;
     Bb = a.opB;
     RA = a.rowsA;
     RB = a.rowsB;
-    ra0 = bl->g_base + m0;
-    rb0 = bl->e_base + n0;
+    ra0 = bl.g_base + m0;
+    rb0 = bl.e_base + n0;
     acopy = Mp;
     bcopy = Np;
-    ka0 = kb0 = 0;
+  }
+
+  // ---- per-lane load offsets (bytes within a slice of one plane) -----------
+  uint32_t voff[PW];
+  sfor<PW>([&](auto Q) {
+    constexpr int q0 = decltype(Q)::value;
+    const int qq = q0 * 4 + wave;
+    constexpr bool isA = q0 < R::QA;
+    const int qi = isA ? qq % R::IA : (qq - PA * R::IA) % R::IB;
+    const int row = qi * R::RPI + lane / R::CPR;
+    const int chunk = (lane % R::CPR) ^ R::swz(row);     // the swizzle is an involution
+    const int64_t rows = isA ? RA : RB;
+    voff[q0] = (uint32_t)((((chunk >> 2) * rows + row) * 32 + (chunk & 3) * 8) * 2);
+  });
+  // LDS fragment addresses: rows wm0 + i*32 + lane%32 (A) and wn0 + j*32 +
+  // lane%32 (B) share one swizzle key (it depends on the row modulo 32 only),
+  // so each K step needs one lane offset per operand; fragments i, j and the
+  // stage add constants.
+  const int key = (lane >> 5) ^ R::swz(lane & 31);
+  int a_off[KS], b_off[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    a_off[ks] = (wm0 + (lane & 31)) * R::RB + (((ks * 2) ^ key) << 4);
+    b_off[ks] = (wn0 + (lane & 31)) * R::RB + (((ks * 2) ^ key) << 4);
   }
 
   f32x16_t acc[FM][FN];
@@ -274,52 +288,151 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int64_t pA = a.planeA, pB = a.planeB;
+  const int64_t pAb = a.planeA * 2, pBb = a.planeB * 2;   // plane strides in bytes
   const int n = kend - kbeg;
-  auto stage = [&](int j) -> uint16_t* { return j == 0 ? st0 : j == 1 ? st1 : j == 2 ? st2 : st3; };
-  auto fetch = [&](int j, int it) {
-    const int kt = min(kbeg + it, kend - 1);   // clamped: a copy past the end is never read
-    if (EPI == EPI_PARAM) {
-      const int s = kt / kst, kk = (kt - s * kst) * KT;
-      R::fetch(stage(j), Ab, RA, ra0 + s * acopy, kk, Bb, RB, rb0 + s * bcopy, kk, pA, pB, wave, lane);
-    } else {
-      R::fetch(stage(j), Ab, RA, ra0, ka0 + kt * KT, Bb, RB, rb0, kb0 + kt * KT, pA, pB, wave, lane);
-    }
-  };
-  // one pipeline step on slice `it`, held in stage J: wait until it has
-  // landed (at most NS-2 newer slices outstanding), barrier (every wave is
-  // also done with the stage read in the previous step), refill that stage
-  // with slice it+NS-1, multiply slice it.
-  auto step = [&](auto J, int it) {
-    constexpr int j = decltype(J)::value;
-    __builtin_amdgcn_s_waitcnt(VmWait<(NS - 2) * R::PER_WAVE>::imm);
-    ring_barrier();
-    fetch((j + NS - 1) % NS, it + NS - 1);
-    R::compute(acc, stage(j), wm0, wn0, lane);
-  };
-  if (n > 0) {
-#pragma unroll
-    for (int j = 0; j < NS - 1; ++j) fetch(j, j);
-    for (int it = 0; it < n; it += NS) {
-      step(std::integral_constant<int, 0>(), it);
-      if (it + 1 < n) step(std::integral_constant<int, 1>(), it + 1);
-      if constexpr (NS > 2)
-        if (it + 2 < n) step(std::integral_constant<int, 2 % NS>(), it + 2);
-      if constexpr (NS > 3)
-        if (it + 3 < n) step(std::integral_constant<int, 3 % NS>(), it + 3);
-    }
-    __builtin_amdgcn_s_waitcnt(0);       // no load may still target LDS when the workgroup ends
+  // slice cursor of the loads (advanced once per issued slice)
+  int cur_s = 0, cur_k = 0;                    // parameter flows: copy and K offset within it
+  int next_load = 0;
+  if (EPI == EPI_PARAM) {
+    cur_s = kbeg / kst;
+    cur_k = (kbeg - cur_s * kst) * KT;
   }
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)ring;
+  // uniform byte bases of the next slice to load
+  const char* sa = nullptr;
+  const char* sb = nullptr;
+  // (past the last slice the ring keeps re-loading it: the stages it lands in
+  // are never read, and every wait stays a constant)
+  auto slice_bases = [&]() {
+    if (next_load >= n) return;
+    int64_t ea, eb;
+    if (EPI == EPI_PARAM) {
+      ea = ((int64_t)(cur_k >> 5) * RA + ra0 + (int64_t)cur_s * acopy) * 32;
+      eb = ((int64_t)(cur_k >> 5) * RB + rb0 + (int64_t)cur_s * bcopy) * 32;
+      cur_k += KT;
+      if (cur_k == kst * KT) {
+        cur_k = 0;
+        ++cur_s;
+      }
+    } else {
+      const int k = (kbeg + next_load) * KT;
+      ea = ((int64_t)((ka0 + k) >> 5) * RA + ra0) * 32;
+      eb = ((int64_t)((kb0 + k) >> 5) * RB + rb0) * 32;
+    }
+    ++next_load;
+    sa = (const char*)Ab + ea * 2;
+    sb = (const char*)Bb + eb * 2;
+  };
+  // load instruction q0 of the slice whose bases are (sa, sb) into stage j
+  auto dma = [&](int j, auto Q) {
+    constexpr int q0 = decltype(Q)::value;
+    constexpr bool isA = q0 < R::QA;
+    constexpr int p = isA ? (q0 * 4) / R::IA : (q0 * 4 - PA * R::IA) / R::IB;
+    const char* base = isA ? sa + p * pAb : sb + p * pBb;
+    lds_load16(base, voff[q0], ring_lds + j * (R::STAGE * 2) + (q0 * 4 + wave) * 1024);
+  };
+
+  bf16x8_t fa[2][PA][FM], fb[2][PB][FN];
+  // fragment read u of K step KSI of a stage into buffer BF
+  auto frag = [&](auto BF, int sbyte, auto KSI, auto U) {
+    constexpr int bf = decltype(BF)::value;
+    constexpr int ks = decltype(KSI)::value;
+    constexpr int u = decltype(U)::value;
+    const char* st = (const char*)ring;
+    if constexpr (u < PA * FM) {
+      constexpr int p = u / FM, i = u % FM;
+      fa[bf][p][i] = *(const bf16x8_t*)(st + (sbyte + a_off[ks]) + (p * R::AEL * 2 + i * 32 * R::RB));
+    } else {
+      constexpr int p = (u - PA * FM) / FN, jj = (u - PA * FM) % FN;
+      fb[bf][p][jj] =
+          *(const bf16x8_t*)(st + (sbyte + b_off[ks]) + (PA * R::AEL * 2 + p * R::BEL * 2 + jj * 32 * R::RB));
+    }
+  };
+  auto mfma = [&](auto BF, auto T) {
+    constexpr int bf = decltype(BF)::value;
+    constexpr int t = decltype(T)::value;
+    constexpr int pr = t / (FM * FN), i = (t / FN) % FM, j = t % FN;
+    constexpr int pa = PP::at(pr, 0), pb = PP::at(pr, 1);
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[bf][pa][i], fb[bf][pb][j], acc[i][j], 0, 0, 0);
+  };
+
+  // One pipeline step on slice `it` held in stage j (its first fragments are
+  // already in buffer 0): refill the stage read in the previous step with
+  // slice it+NS-1, multiply slice it, and (unless it is the last) at its end
+  // cross the barrier that makes slice it+1 readable and read its first
+  // fragments.
+  auto step = [&](auto LAST, int j) {
+    constexpr bool last = decltype(LAST)::value;
+    const int jn = j + 1 == NS ? 0 : j + 1, jl = j == 0 ? NS - 1 : j - 1;
+    const int sbyte = j * (R::STAGE * 2), snext = jn * (R::STAGE * 2);
+    slice_bases();
+    sfor<KS>([&](auto KSI) {
+      constexpr int ks = decltype(KSI)::value;
+      constexpr int bf = ks & 1;
+      using BF = std::integral_constant<int, bf>;
+      using BN = std::integral_constant<int, bf ^ 1>;
+      if constexpr (ks + 1 < KS) {
+        // interleave: matrix instruction t, then its share of the fragment
+        // reads of the next K step (and, in the first, of the slice loads)
+        constexpr int NO = NRD + (ks == 0 ? PW : 0);
+        sfor<NMF>([&](auto T) {
+          constexpr int t = decltype(T)::value;
+          mfma(BF(), T);
+          constexpr int o0 = t * NO / NMF, o1 = (t + 1) * NO / NMF;
+          sfor<o1 - o0>([&](auto O) {
+            constexpr int o = o0 + decltype(O)::value;
+            if constexpr (o < NRD) frag(BN(), sbyte, std::integral_constant<int, ks + 1>(), std::integral_constant<int, o>());
+            else dma(jl, std::integral_constant<int, o - NRD>());
+          });
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      } else if constexpr (!last) {
+        constexpr int H = NMF / 2;
+        sfor<H>([&](auto T) { mfma(BF(), T); });
+        __builtin_amdgcn_sched_barrier(0);
+        // slice it+1 has landed once at most the NS-2 slices issued after it are in flight
+        __builtin_amdgcn_s_waitcnt(WaitVmLgkm<(NS - 2) * PW>::imm);
+        ring_barrier();
+        sfor<NMF - H>([&](auto T) {
+          constexpr int t = H + decltype(T)::value;
+          mfma(BF(), std::integral_constant<int, t>());
+          constexpr int o0 = (t - H) * NRD / (NMF - H), o1 = (t - H + 1) * NRD / (NMF - H);
+          sfor<o1 - o0>([&](auto O) {
+            frag(std::integral_constant<int, 0>(), snext, std::integral_constant<int, 0>(),
+                 std::integral_constant<int, o0 + decltype(O)::value>());
+          });
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      } else {
+        sfor<NMF>([&](auto T) { mfma(BF(), T); });
+      }
+    });
+  };
+
+  if (n > 0) {
+    // prologue: slices 0 .. NS-2 in flight, slice 0 readable, its first fragments read
+    sfor<NS - 1>([&](auto S0) {
+      slice_bases();
+      sfor<PW>([&](auto Q) { dma(decltype(S0)::value, Q); });
+    });
+    __builtin_amdgcn_s_waitcnt(WaitVmLgkm<(NS - 2) * PW>::imm);
+    ring_barrier();
+    sfor<NRD>([&](auto U) { frag(std::integral_constant<int, 0>(), 0, std::integral_constant<int, 0>(), U); });
+    int j = 0;
+    for (int it = 0; it < n - 1; ++it) {
+      step(std::false_type(), j);
+      j = j + 1 == NS ? 0 : j + 1;
+    }
+    step(std::true_type(), j);
+  }
+  __builtin_amdgcn_s_waitcnt(0);       // no load may still target LDS past this point
 
   // ---- split-K: the last workgroup of a tile adds the partials in order -----
   // Partials are published with device-scope atomic stores (written through
   // to the device coherence point, so no cache-wide write-back is needed),
   // completed (vmcnt 0) before the arrival counter moves; the last arrival
-  // reads them back with device-scope atomic loads.  A __threadfence() here
-  // would write back and invalidate the whole L2 of the XCD under every
-  // other workgroup still streaming operands through it.
+  // reads every partial back with device-scope atomic loads, in split order.
   if (EPI != EPI_PARAM && S > 1) {
-    constexpr int NREG = FM * FN * 16;
     float* mine = a.partials + ((int64_t)tile * S + split) * (NREG * 256);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -337,111 +450,183 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
     __syncthreads();
     if (!last_flag) return;
     const float* base = a.partials + (int64_t)tile * S * (NREG * 256);
+    // in chunks of up to 64 registers: every load of a chunk in flight at once
+    constexpr int CH = NREG < 64 ? NREG : 64;
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int c0 = 0; c0 < NREG; c0 += CH) {
+      float sum[CH];
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
+      for (int x = 0; x < CH; ++x)
+        sum[x] = __hip_atomic_load(base + (c0 + x) * 256 + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int q = 1; q < S; ++q) {
+        float t[CH];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int idx = ((i * FN + j) * 16 + r) * 256 + tid;
-          const float own = acc[i][j][r];
-          float sum = 0.0f;
-          for (int q = 0; q < S; ++q)
-            sum += (q == split) ? own
-                                : __hip_atomic_load(base + (int64_t)q * (NREG * 256) + idx, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-          acc[i][j][r] = sum;
-        }
+        for (int x = 0; x < CH; ++x)
+          t[x] = __hip_atomic_load(base + (int64_t)q * (NREG * 256) + (c0 + x) * 256 + tid, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int x = 0; x < CH; ++x) sum[x] += t[x];
+      }
+#pragma unroll
+      for (int x = 0; x < CH; ++x) {
+        const int reg = c0 + x, blk = reg / 16;
+        acc[blk / FN][blk % FN][reg % 16] = sum[x];
+      }
+    }
     if (tid == 0) __hip_atomic_store(a.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // ---- epilogue ------------------------------------------------------------
   // accumulator register r of lane l holds row (r/4)*8 + (l/32)*4 + r%4 and
-  // column l%32 of its 32 x 32 block.
+  // column l%32 of its 32 x 32 block.  Per-column shifts and per-row child
+  // nodes are staged in LDS (the ring is free once every load has landed and
+  // every wave is past its last fragment read).
   const int B = a.B;
+  float* sh_col = (float*)ring;                // [NT]
+  int* ch_row = (int*)ring + NT;               // [MT]
+  if (EPI == EPI_FWD || EPI == EPI_ELEM) {
+    __syncthreads();
+    for (int t = tid; t < NT; t += 256) {
+      const int col = n0 + t;
+      sh_col[t] = col < B ? key_to_shift(a.mkeys[(int64_t)gr.m_row * B + col]) : 0.0f;
+    }
+    if (EPI == EPI_ELEM)
+      for (int t = tid; t < MT; t += 256) {
+        const int row = m0 + t;
+        ch_row[t] = row < gr.N ? a.chblocks[gr.blk_off + row / gr.cbs] + row % gr.cbs : -1;
+      }
+    __syncthreads();
+  }
+  const int lr0 = wm0 + (lane >> 5) * 4, lc = wn0 + (lane & 31);
+  if (EPI == EPI_FWD) {
+    float* vals = a.vals + (int64_t)gr.out_start * B;
+    float* ssum = a.ssum + gr.s_row * B;
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+    for (int j = 0; j < FN; ++j) {
+      const int cl = lc + j * 32, col = n0 + cl;
+      const float sh = sh_col[cl];
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        const int col = n0 + wn0 + j * 32 + (lane & 31);
-        const float v = acc[i][j][r];
-        if (EPI == EPI_FWD) {
-          if (row < gr->M && col < B) {
-            const float sh = key_to_shift(a.mkeys[(int64_t)gr->m_row * B + col]);
-            a.vals[(int64_t)(gr->out_start + row) * B + col] = sh + logf(v);
-            a.ssum[(gr->s_row + row) * B + col] = v;
-          }
-        } else if (EPI == EPI_ELEM) {
-          if (row < gr->N && col < B) {
-            const int child = a.chblocks[gr->blk_off + row / gr->cbs] + row % gr->cbs;
-            const float sh = key_to_shift(a.mkeys[(int64_t)gr->m_row * B + col]);
-            const float e = expf(a.vals[(int64_t)child * B + col] - sh);
-            const float c = (e == 0.0f) ? 0.0f : e * v;
-            if (gr->scratch_row >= 0)
-              a.scratch[(int64_t)(gr->scratch_row + row) * B + col] = c;
-            else if (a.store)
-              a.flows[(int64_t)child * B + col] = c;
-            else
-              a.flows[(int64_t)child * B + col] += c;
-          }
-        } else {
-          if (row < bl->M && col < bl->N) {
-            const int64_t idx = bl->param_offset + (int64_t)row * bl->N + col;
-            a.pflows[idx] += a.params[idx] * v;
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + lr0 + i * 32 + (r >> 2) * 8 + (r & 3);
+          const float v = acc[i][j][r];
+          if (row < gr.M && col < B) {
+            vals[(int64_t)row * B + col] = sh + logf(v);
+            ssum[(int64_t)row * B + col] = v;
           }
         }
+    }
+  } else if (EPI == EPI_ELEM) {
+    // batches of up to 4 blocks: every load of a batch in flight before any store
+    constexpr int NB = FM * FN, BT = NB < 4 ? NB : 4;
+    const bool to_scratch = gr.scratch_row >= 0;
+    const bool add = !to_scratch && !a.store;
+    float* dst_base = to_scratch ? a.scratch + (int64_t)gr.scratch_row * B : a.flows;
+#pragma unroll
+    for (int b0 = 0; b0 < NB; b0 += BT) {
+      float x[BT][16], old[BT][16];
+      int64_t at[BT][16];
+#pragma unroll
+      for (int bb = 0; bb < BT; ++bb) {
+        const int i = (b0 + bb) / FN, j = (b0 + bb) % FN;
+        const int col = n0 + lc + j * 32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rl = lr0 + i * 32 + (r >> 2) * 8 + (r & 3);
+          const int child = ch_row[rl];
+          const bool ok = child >= 0 && col < B;
+          at[bb][r] = ok ? (to_scratch ? (int64_t)(m0 + rl) * B + col : (int64_t)child * B + col) : -1;
+          x[bb][r] = ok ? a.vals[(int64_t)child * B + col] : 0.0f;
+          old[bb][r] = (ok && add) ? dst_base[at[bb][r]] : 0.0f;
+        }
       }
+#pragma unroll
+      for (int bb = 0; bb < BT; ++bb) {
+        const int i = (b0 + bb) / FN, j = (b0 + bb) % FN;
+        const float sh = sh_col[lc + j * 32];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if (at[bb][r] < 0) continue;
+          const float e = expf(x[bb][r] - sh);
+          const float c = (e == 0.0f) ? 0.0f : e * acc[i][j][r];
+          dst_base[at[bb][r]] = add ? old[bb][r] + c : c;
+        }
+      }
+    }
+  } else {
+    constexpr int NB = FM * FN, BT = NB < 4 ? NB : (NREG >= 256 ? 1 : 4);
+    const float* params = a.params + bl.param_offset;
+    float* pflows = a.pflows + bl.param_offset;
+#pragma unroll
+    for (int b0 = 0; b0 < NB; b0 += BT) {
+      float th[BT][16], old[BT][16];
+#pragma unroll
+      for (int bb = 0; bb < BT; ++bb) {
+        const int i = (b0 + bb) / FN, j = (b0 + bb) % FN;
+        const int col = n0 + lc + j * 32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + lr0 + i * 32 + (r >> 2) * 8 + (r & 3);
+          const bool ok = row < bl.M && col < bl.N;
+          const int64_t idx = (int64_t)row * bl.N + col;
+          th[bb][r] = ok ? params[idx] : 0.0f;
+          old[bb][r] = ok ? pflows[idx] : 0.0f;
+        }
+      }
+#pragma unroll
+      for (int bb = 0; bb < BT; ++bb) {
+        const int i = (b0 + bb) / FN, j = (b0 + bb) % FN;
+        const int col = n0 + lc + j * 32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + lr0 + i * 32 + (r >> 2) * 8 + (r & 3);
+          if (row < bl.M && col < bl.N) pflows[(int64_t)row * bl.N + col] = old[bb][r] + th[bb][r] * acc[i][j][r];
+        }
+      }
+    }
+  }
 }
 
-// Tile shapes: forward / element flows 128 x 128 (split over K when the
-// output has few tiles); parameter flows 256 x 256 when every block is at
-// least that large and the planes fit LDS, else 128 x 128.  KT is 64 when a
-// stage of that width is at most 48 KB, else 32; NS stages fill up to 160 KB.
-template <int PA, int PB, int MT, int NT>
-struct Shape {
-  static constexpr int KT = ((PA * MT + PB * NT) * 64 * 2 <= 48 * 1024) ? 64 : 32;
-  static constexpr int STAGE_BYTES = (PA * MT + PB * NT) * KT * 2;
-  static constexpr int NSR = (160 * 1024 - 1024) / STAGE_BYTES;
-  static constexpr int NS = NSR > 4 ? 4 : NSR;
-};
-
-template <int EPI, int PA, int PB, int MT, int NT>
+template <int EPI, int PA, int PB, int MT, int NT, int WM>
 static void launch_shape(int grid, const GemmArgs& a, hipStream_t s) {
-  using Sh = Shape<PA, PB, MT, NT>;
-  static_assert(Sh::NS >= 2, "LDS ring needs two stages");
-  hipLaunchKernelGGL((k_gemm<EPI, PA, PB, MT, NT, Sh::KT, Sh::NS>), dim3(grid), dim3(256), 0, s, a);
+  constexpr int KT = gemm_kt(PA, PB, MT, NT);
+  constexpr int NS = gemm_stages(PA, PB, MT, NT);
+  static_assert(NS >= 2, "LDS ring needs two stages");
+  hipLaunchKernelGGL((k_gemm<EPI, PA, PB, MT, NT, WM, KT, NS>), dim3(grid), dim3(256), 0, s, a);
 }
 
 template <int EPI, int PA, int PB>
-static void launch3(int tiles, int big, const GemmArgs& a, hipStream_t s) {
-  constexpr bool wide = (PA + PB) <= 3;
-  const int grid = tiles * (EPI == EPI_PARAM ? 1 : a.splitk);
-  if constexpr (EPI == EPI_PARAM && wide) {
-    if (big) {
-      launch_shape<EPI, PA, PB, 256, 256>(grid, a, s);
-      return;
+static void launch_tile(int tile, int grid, const GemmArgs& a, hipStream_t s) {
+  if constexpr (EPI == EPI_PARAM) {
+    if constexpr (PA + PB <= 3) {
+      if (tile == TILE_256x256) {
+        launch_shape<EPI, PA, PB, 256, 256, 2>(grid, a, s);
+        return;
+      }
     }
+    launch_shape<EPI, PA, PB, 128, 128, 2>(grid, a, s);
+  } else {
+    if (tile == TILE_256x128) launch_shape<EPI, PA, PB, 256, 128, 2>(grid, a, s);
+    else launch_shape<EPI, PA, PB, 128, 128, 2>(grid, a, s);
   }
-  launch_shape<EPI, PA, PB, 128, 128>(grid, a, s);
 }
 
 template <int EPI>
-static void launch_planes(int pa, int pb, int tiles, int big, const GemmArgs& a, hipStream_t s) {
-  if (pa == 1 && pb == 1) launch3<EPI, 1, 1>(tiles, big, a, s);
-  else if (pa == 2 && pb == 1) launch3<EPI, 2, 1>(tiles, big, a, s);
-  else if (pa == 1 && pb == 2) launch3<EPI, 1, 2>(tiles, big, a, s);
-  else if (pa == 2 && pb == 2) launch3<EPI, 2, 2>(tiles, big, a, s);
-  else launch3<EPI, 3, 3>(tiles, big, a, s);
+static void launch_planes(int pa, int pb, int tile, int grid, const GemmArgs& a, hipStream_t s) {
+  if (pa == 1 && pb == 1) launch_tile<EPI, 1, 1>(tile, grid, a, s);
+  else if (pa == 2 && pb == 1) launch_tile<EPI, 2, 1>(tile, grid, a, s);
+  else if (pa == 1 && pb == 2) launch_tile<EPI, 1, 2>(tile, grid, a, s);
+  else if (pa == 2 && pb == 2) launch_tile<EPI, 2, 2>(tile, grid, a, s);
+  else launch_tile<EPI, 3, 3>(tile, grid, a, s);
 }
 
-void launch_gemm(int epi, int pa, int pb, int tiles, int big, const GemmArgs& a, hipStream_t s) {
-  if (tiles <= 0) return;
-  if (epi == EPI_FWD) launch_planes<EPI_FWD>(pa, pb, tiles, 0, a, s);
-  else if (epi == EPI_ELEM) launch_planes<EPI_ELEM>(pa, pb, tiles, 0, a, s);
-  else launch_planes<EPI_PARAM>(pa, pb, tiles, big, a, s);
+void launch_gemm(int epi, int pa, int pb, const GemmShape& sh, const GemmArgs& a, hipStream_t s) {
+  if (sh.tiles <= 0) return;
+  const int grid = sh.tiles * (epi == EPI_PARAM ? 1 : sh.splitk);
+  if (epi == EPI_FWD) launch_planes<EPI_FWD>(pa, pb, sh.tile, grid, a, s);
+  else if (epi == EPI_ELEM) launch_planes<EPI_ELEM>(pa, pb, sh.tile, grid, a, s);
+  else launch_planes<EPI_PARAM>(pa, pb, sh.tile, grid, a, s);
 }
 
 }  // namespace pc

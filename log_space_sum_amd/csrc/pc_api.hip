@@ -166,6 +166,21 @@ void free_tables(Handle* h) {
   if (prev >= 0) (void)hipSetDevice(prev);
 }
 
+GemmShape layer_gemm_shape(const Handle* h, const SumPlan& sp, int kind, int B_pad, int pa, int pb) {
+  return layer_shape(kind == GK_FWD ? sp.mtiles : sp.ctiles, B_pad, kind == GK_FWD ? sp.max_npk : sp.max_mpk, pa,
+                     pb, h->opt_layer_tile, h->opt_split_max);
+}
+
+GemmShape param_gemm_shape(const Handle* h, int pa, int pb) {
+  GemmShape g{};
+  const bool big = pa + pb <= 3 && h->opt_param_tile != TILE_128x128;   // rows are padded to 256
+  g.tile = big ? TILE_256x256 : TILE_128x128;
+  g.mt = g.nt = big ? 256 : 128;
+  g.splitk = 1;
+  g.tiles = big ? h->param_tiles256 : h->param_tiles128;
+  return g;
+}
+
 WsPlan plan_workspace(const Handle* h, int B) {
   WsPlan p{};
   p.B = B;
@@ -198,15 +213,12 @@ WsPlan plan_workspace(const Handle* h, int B) {
   {
     int64_t pel = 0;
     int32_t nct = 0;
-    const int ntl = p.B_pad / 128;
     for (const auto& sp : h->sums) {
       if (sp.lowrank) continue;
       for (int e = 0; e < 2; ++e) {
-        const int kt = gemm_kt(p.pl[e][0], p.pl[e][1]);
-        const int tiles = (e == 0 ? sp.mtiles : sp.ctiles) * (ROW_PAD / 128) * ntl;
-        const int S = choose_split(tiles, (e == 0 ? sp.max_npk : sp.max_mpk) / kt);
-        if (S > 1) pel = std::max<int64_t>(pel, (int64_t)tiles * S * 128 * 128);
-        nct = std::max(nct, tiles);
+        const GemmShape g = layer_gemm_shape(h, sp, e, p.B_pad, p.pl[e][0], p.pl[e][1]);
+        if (g.splitk > 1) pel = std::max<int64_t>(pel, (int64_t)g.tiles * g.splitk * g.mt * g.nt);
+        nct = std::max(nct, g.tiles);
       }
     }
     p.partial_elems = pel;
@@ -426,6 +438,27 @@ int pc_set_split(pc_handle hh, int mode, int gemm_kind, int planes_a, int planes
   }
 }
 
+int pc_set_option(pc_handle hh, int option, int value) {
+  try {
+    Handle* h = checked(hh);
+    if (option == PC_OPT_LAYER_TILE) {
+      if (value < 0 || value > 2) fail(PC_ERR_INVALID_ARG, "layer tile must be 0, 1 or 2");
+      h->opt_layer_tile = value == 1 ? TILE_128x128 : value == 2 ? TILE_256x128 : TILE_AUTO;
+    } else if (option == PC_OPT_PARAM_TILE) {
+      if (value < 0 || value > 1) fail(PC_ERR_INVALID_ARG, "parameter tile must be 0 or 1");
+      h->opt_param_tile = value == 1 ? TILE_128x128 : TILE_AUTO;
+    } else if (option == PC_OPT_SPLIT_MAX) {
+      if (value != 1 && value != 2 && value != 4 && value != 8) fail(PC_ERR_INVALID_ARG, "split must be 1, 2, 4 or 8");
+      h->opt_split_max = value;
+    } else {
+      fail(PC_ERR_INVALID_ARG, "unknown option");
+    }
+    return PC_OK;
+  } catch (const Error& e) {
+    return set_error(e.code, e.msg);
+  }
+}
+
 int pc_workspace_bytes(pc_handle hh, int batch, size_t* bytes) {
   try {
     Handle* h = checked(hh);
@@ -549,10 +582,11 @@ int pc_forward(pc_handle hh, int batch, const int32_t* tokens, const float* para
         g.vals = node_vals;
         g.mkeys = v.mkeys;
         g.ssum = v.ssum;
-        const int tiles = sp.mtiles * (ROW_PAD / 128) * g.ntiles;
-        g.splitk = choose_split(tiles, sp.max_npk / gemm_kt(p.pl[GK_FWD][0], p.pl[GK_FWD][1]));
+        const GemmShape shp = layer_gemm_shape(h, sp, GK_FWD, v.B_pad, p.pl[GK_FWD][0], p.pl[GK_FWD][1]);
+        g.ntiles = v.B_pad / shp.nt;
+        g.splitk = shp.splitk;
         Timed t(h, KK_FWD, c.s);
-        launch_gemm(EPI_FWD, p.pl[GK_FWD][0], p.pl[GK_FWD][1], tiles, 0, g, c.s);
+        launch_gemm(EPI_FWD, p.pl[GK_FWD][0], p.pl[GK_FWD][1], shp, g, c.s);
       }
     }
     if (ll) {
@@ -633,10 +667,11 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
         g.mkeys = v.mkeys;
         g.store = sp.store ? 1 : 0;
         {
-          const int tiles = sp.ctiles * (ROW_PAD / 128) * g.ntiles;
-          g.splitk = choose_split(tiles, sp.max_mpk / gemm_kt(p.pl[GK_ELEM][0], p.pl[GK_ELEM][1]));
+          const GemmShape shp = layer_gemm_shape(h, sp, GK_ELEM, v.B_pad, p.pl[GK_ELEM][0], p.pl[GK_ELEM][1]);
+          g.ntiles = v.B_pad / shp.nt;
+          g.splitk = shp.splitk;
           Timed t(h, KK_ELEM, c.s);
-          launch_gemm(EPI_ELEM, p.pl[GK_ELEM][0], p.pl[GK_ELEM][1], tiles, 0, g, c.s);
+          launch_gemm(EPI_ELEM, p.pl[GK_ELEM][0], p.pl[GK_ELEM][1], shp, g, c.s);
         }
         if (sp.overlap) {
           SumArgs ra = sum_common(c, sp);
@@ -672,12 +707,10 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
       g.planeB = v.earena_plane;
       g.params = params;
       g.pflows = param_flows;
-      // operand rows are padded to 256, so 256 x 256 tiles fit every block
-      const bool big = p.pl[GK_PARAM][0] + p.pl[GK_PARAM][1] <= 3;
+      const GemmShape shp = param_gemm_shape(h, p.pl[GK_PARAM][0], p.pl[GK_PARAM][1]);
       g.splitk = 1;
       Timed t(h, KK_PARAM, c.s);
-      launch_gemm(EPI_PARAM, p.pl[GK_PARAM][0], p.pl[GK_PARAM][1], big ? h->param_tiles256 : h->param_tiles128,
-                  big ? 1 : 0, g, c.s);
+      launch_gemm(EPI_PARAM, p.pl[GK_PARAM][0], p.pl[GK_PARAM][1], shp, g, c.s);
     }
     check_launch();
     return PC_OK;

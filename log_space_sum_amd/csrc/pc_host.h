@@ -78,6 +78,7 @@ struct Handle {
   int mode = PC_PREC_AUTO;
   // planes[mode][gemm kind][0: first operand, 1: second operand]
   int planes[2][3][2] = {{{2, 1}, {2, 1}, {2, 1}}, {{3, 3}, {3, 3}, {3, 3}}};
+  int opt_layer_tile = 0, opt_param_tile = 0, opt_split_max = 8;   // pc_set_option
   int32_t num_nodes = 0, num_vars = 0, root = -1, lowrank_rank = 0;
   int64_t num_params = 0;
   std::vector<LayerRef> layers;

@@ -35,18 +35,45 @@ struct GemmArgs {
   uint32_t* counters;           // split-K arrival counters, zero between launches
 };
 
-// Launch the product kernel for `tiles` tiles with the given operand split.
-// `big`: parameter flows may use 256 x 256 tiles (every block at least that large).
-void launch_gemm(int epi, int pa, int pb, int tiles, int big, const GemmArgs& a, hipStream_t s);
+// Output tile shapes of the product kernel (M x N per workgroup).
+enum GemmTile { TILE_AUTO = 0, TILE_128x128 = 1, TILE_256x128 = 2, TILE_256x256 = 3 };
 
-// K splits for a forward / element-flow launch of `tiles` 128 x 128 tiles
-// with `ksteps` K slices: enough workgroups for the 256 CUs, >= 4 slices each.
-inline int choose_split(int tiles, int ksteps) {
-  int S = 1;
-  while (tiles * S < 256 && S < 8 && ksteps / (S * 2) >= 4) S *= 2;
-  return S;
+struct GemmShape {
+  int tile;      // GemmTile
+  int mt, nt;    // tile rows / columns
+  int splitk;    // workgroups sharing one tile's K range (forward / element flows)
+  int tiles;     // output tiles of the launch
+};
+
+// K slice width: 64 when a stage of that width holds at most 48 KB, else 32.
+constexpr int gemm_kt(int pa, int pb, int mt, int nt) { return (pa * mt + pb * nt) * 64 * 2 <= 48 * 1024 ? 64 : 32; }
+// LDS ring stages (at most 4) that fit 160 KB with 2 KB to spare.
+constexpr int gemm_stages(int pa, int pb, int mt, int nt) {
+  return ((160 - 2) * 1024) / ((pa * mt + pb * nt) * gemm_kt(pa, pb, mt, nt) * 2) > 4
+             ? 4
+             : ((160 - 2) * 1024) / ((pa * mt + pb * nt) * gemm_kt(pa, pb, mt, nt) * 2);
 }
-// K slice width of a forward / element-flow launch for the given planes.
-inline int gemm_kt(int pa, int pb) { return (pa + pb) <= 3 ? 64 : 32; }
+
+// Shape of a forward / element-flow launch over a layer whose outputs span
+// `rows256` 256-row blocks, batch padded to B_pad, largest padded K `kpad`:
+// 128 x 128 tiles unless 256 x 128 are asked for (measured faster on the
+// 4096-node layers at batch 512: the K split is half as deep), K split (a
+// power of two up to split_max) until the launch has 256 workgroups, keeping
+// >= 4 slices per split.
+inline GemmShape layer_shape(int rows256, int B_pad, int kpad, int pa, int pb, int opt_tile, int split_max) {
+  GemmShape g{};
+  g.tile = opt_tile == TILE_256x128 ? TILE_256x128 : TILE_128x128;
+  g.mt = g.tile == TILE_128x128 ? 128 : 256;
+  g.nt = 128;
+  g.tiles = rows256 * (256 / g.mt) * (B_pad / g.nt);
+  const int ksteps = kpad / gemm_kt(pa, pb, g.mt, g.nt);
+  int S = 1;
+  while (g.tiles * S < 256 && S * 2 <= split_max && ksteps / (S * 2) >= 4) S *= 2;
+  g.splitk = S;
+  return g;
+}
+
+// Launch the product kernel with the given operand split and shape.
+void launch_gemm(int epi, int pa, int pb, const GemmShape& shape, const GemmArgs& a, hipStream_t s);
 
 }  // namespace pc
