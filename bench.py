@@ -92,7 +92,7 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=32)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--layer-tile", type=int, default=0, help="product-kernel option: 0 auto (128x128), 1 128x128, 2 256x128")
-    ap.add_argument("--param-tile", type=int, default=0, help="product-kernel option: 0 auto, 1 128x128")
+    ap.add_argument("--param-tile", type=int, default=0, help="product-kernel option: 0 auto (128x128), 1 128x128, 2 256x256")
     ap.add_argument("--split-max", type=int, default=8, help="largest K split of a per-layer product")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="only run a plain device copy of this many bytes (3 times): the reference "

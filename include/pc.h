@@ -197,7 +197,7 @@ int pc_set_split(pc_handle h, int mode, int gemm_kind, int planes_a, int planes_
  * order).  PC_OPT_LAYER_TILE: output tile of the per-layer forward and
  * element-flow products, 0 automatic (128 x 128), 1 128 x 128, 2 256 x 128.
  * PC_OPT_PARAM_TILE: tile of the parameter-flow product, 0 automatic
- * (256 x 256 when the operand split allows, else 128 x 128), 1 128 x 128.
+ * (128 x 128), 1 128 x 128, 2 256 x 256 (when the operand split allows).
  * PC_OPT_SPLIT_MAX: largest K split of a per-layer product (1, 2, 4 or 8;
  * default 8).  Changing an option can change pc_workspace_bytes.
  * Errors: PC_ERR_INVALID_ARG (unknown option or value). */

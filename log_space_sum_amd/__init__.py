@@ -217,7 +217,7 @@ OPTIONS = {"layer_tile": 0, "param_tile": 1, "split_max": 2}
 
 def pc_set_option(h: Handle, option, value: int):
     """Product-kernel tuning: layer_tile (0 auto, 1 128x128, 2 256x128),
-    param_tile (0 auto, 1 128x128), split_max (1, 2, 4, 8)."""
+    param_tile (0 auto, 1 128x128, 2 256x256), split_max (1, 2, 4, 8)."""
     option = OPTIONS.get(option, option) if isinstance(option, str) else option
     _check(lib().pc_set_option(h.ptr, int(option), int(value)))
 

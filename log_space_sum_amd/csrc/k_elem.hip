@@ -89,18 +89,67 @@ __global__ void k_tokens_t(const int32_t* tok, int32_t* tokT, int B, int V) {
   }
 }
 
+// ---- batch vectors -------------------------------------------------------------
+// Element-wise kernels give each thread V consecutive samples of one row: V = 4
+// (16-byte loads and stores) when the batch is a multiple of 4, so every row
+// of a [nodes, B] array starts 16-byte aligned, else V = 1.
+template <int V>
+struct Row {
+  float x[V];
+  __device__ __forceinline__ void load(const float* p) {
+    if constexpr (V == 4) {
+      const float4 t = *(const float4*)p;
+      x[0] = t.x; x[1] = t.y; x[2] = t.z; x[3] = t.w;
+    } else {
+#pragma unroll
+      for (int k = 0; k < V; ++k) x[k] = p[k];
+    }
+  }
+  __device__ __forceinline__ void store(float* p) const {
+    if constexpr (V == 4) *(float4*)p = make_float4(x[0], x[1], x[2], x[3]);
+    else
+#pragma unroll
+      for (int k = 0; k < V; ++k) p[k] = x[k];
+  }
+};
+
+// s += rows ids[q0..q1) of x at samples [b, b + V), added in q order; the
+// loads of each chunk of 4 rows are all issued before the first add.
+template <int V>
+__device__ __forceinline__ void sum_rows(Row<V>& s, const float* x, const int32_t* ids, int q0, int q1, int B,
+                                         int b) {
+  for (int q = q0; q < q1; q += 4) {
+    Row<V> c[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (q + u < q1) c[u].load(x + (int64_t)ids[q + u] * B + b);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (q + u < q1)
+#pragma unroll
+        for (int e = 0; e < V; ++e) s.x[e] += c[u].x[e];
+  }
+}
+
 // ---- categorical input layer ---------------------------------------------------
 // v[u,b] = log theta_in[row(u), x[b, var(u)]]; a token outside [0, K) gives NaN
 // (and never an out-of-range read).
+template <int V>
 __global__ void k_input_fwd(InputArgs a) {
-  const int64_t n = (int64_t)a.num_nodes * a.B;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
-    const int u = (int)(i / a.B), b = (int)(i - (int64_t)u * a.B);
-    const int x = a.tokT[(int64_t)a.var[u] * a.B + b];
-    float v;
-    if (x >= 0 && x < a.K) v = logf(a.params[a.param_offset + (int64_t)a.row[u] * a.K + x]);
-    else v = __uint_as_float(0x7fc00000u);
-    a.vals[(int64_t)(a.node_start + u) * a.B + b] = v;
+  const uint32_t QB = (uint32_t)(a.B / V), n = (uint32_t)a.num_nodes * QB;
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+    const uint32_t u = i / QB, b = (i - u * QB) * V;
+    const int32_t* tok = a.tokT + (int64_t)a.var[u] * a.B + b;
+    const float* th = a.params + a.param_offset + (int64_t)a.row[u] * a.K;
+    Row<V> xs;
+    xs.load((const float*)tok);   // the V tokens, as raw 32-bit words
+    Row<V> r;
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+      const int x = __float_as_int(xs.x[k]);
+      r.x[k] = (x >= 0 && x < a.K) ? logf(th[x]) : __uint_as_float(0x7fc00000u);
+    }
+    r.store(a.vals + (int64_t)(a.node_start + u) * a.B + b);
   }
 }
 
@@ -134,132 +183,286 @@ __global__ void k_bucket(const int32_t* tokT, int B, int Kmax, int32_t* bptr, in
   }
 }
 
-// F_in[row, k] += sum over the row's nodes u (ascending) and the samples b
-// with x[b, var(u)] = k (ascending) of f[u, b].
-__global__ void k_input_bwd(InputArgs a) {
-  const int64_t n = (int64_t)a.num_rows * a.K;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
-    const int r = (int)(i / a.K), k = (int)(i - (int64_t)r * a.K);
-    float acc = 0.0f;
-    for (int q = a.row_ptr[r]; q < a.row_ptr[r + 1]; ++q) {
+// F_in[row, k] += sum over the row's nodes u (ascending) of n_u[k], with
+// n_u[k] the sum over the samples b with x[b, var(u)] = k (ascending) of
+// f[u, b].  One workgroup of NW waves per parameter row: each wave takes one
+// of the row's nodes at a time (NW in flight), stages its flow row and its
+// variable's category buckets in its own LDS region and sums every bucket;
+// the per-node sums are then added in node order.  Needs K <= 1024 and the
+// LDS regions to fit (see launch_input_bwd).
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void k_input_bwd(InputArgs a) {
+  extern __shared__ float ib_sm[];
+  constexpr int NT = 64 * NW, J = 1024 / NT;
+  const int B = a.B, K = a.K;
+  const int per = 2 * B + 2 * K + 1;          // f[B], idx[B], ptr[K + 1], n[K]
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  float* f = ib_sm + w * per;
+  int32_t* idx = (int32_t*)(f + B);
+  int32_t* ptr = idx + B;
+  const int r = blockIdx.x, q0 = a.row_ptr[r], q1 = a.row_ptr[r + 1];
+  float acc[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) acc[j] = 0.0f;
+  for (int qb = q0; qb < q1; qb += NW) {
+    const int q = qb + w;
+    if (q < q1) {
       const int node = a.row_nodes[q];
       const int v = a.var[node - a.node_start];
+      const float* F = a.flows + (int64_t)node * B;
+      const int32_t* I = a.bidx + (int64_t)v * B;
+      const int32_t* P = a.bptr + (int64_t)v * (a.Kmax + 1);
+#pragma unroll 4
+      for (int b = lane; b < B; b += 64) {
+        f[b] = F[b];
+        idx[b] = I[b];
+      }
+#pragma unroll 4
+      for (int k = lane; k <= K; k += 64) ptr[k] = P[k];
+      // a wave's LDS operations complete in order: its own writes are visible here
+      float* n = (float*)(ptr + K + 1);
+      for (int k = lane; k < K; k += 64) {
+        float t = 0.0f;
+        for (int e = ptr[k]; e < ptr[k + 1]; ++e) t += f[idx[e]];
+        n[k] = t;
+      }
+    }
+    __syncthreads();
+    const int nq = min(NW, q1 - qb);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int k = j * NT + tid;
+      if (k < K)
+        for (int u = 0; u < nq; ++u) acc[j] += ((const float*)((const int32_t*)(ib_sm + u * per + 2 * B) + K + 1))[k];
+    }
+    __syncthreads();                             // regions free for the next nodes
+  }
+  float* out = a.pflows + a.param_offset + (int64_t)r * K;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int k = j * NT + tid;
+    if (k < K) out[k] += acc[j];
+  }
+}
+
+// The same sums for rows whose regions do not fit: the row's nodes one at a
+// time, the flow row staged in LDS, buckets read from global memory.
+__global__ void k_input_bwd_wide(InputArgs a) {
+  extern __shared__ float frow[];   // [B]
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int q0 = a.row_ptr[r], q1 = a.row_ptr[r + 1];
+  float* out = a.pflows + a.param_offset + (int64_t)r * a.K;
+  for (int kc = 0; kc < a.K; kc += 1024) {
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int q = q0; q < q1; ++q) {
+      const int node = a.row_nodes[q];
+      const int v = a.var[node - a.node_start];
+      const float* f = a.flows + (int64_t)node * a.B;
+      __syncthreads();                          // previous row fully read
+      for (int b = tid; b < a.B; b += blockDim.x) frow[b] = f[b];
+      __syncthreads();
       const int32_t* ptr = a.bptr + (int64_t)v * (a.Kmax + 1);
       const int32_t* idx = a.bidx + (int64_t)v * a.B;
-      const float* f = a.flows + (int64_t)node * a.B;
-      for (int t = ptr[k]; t < ptr[k + 1]; ++t) acc += f[idx[t]];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int k = kc + j * 256 + tid;
+        if (k < a.K) {
+          float t = 0.0f;
+          for (int e = ptr[k]; e < ptr[k + 1]; ++e) t += frow[idx[e]];
+          acc[j] += t;
+        }
+      }
     }
-    a.pflows[a.param_offset + i] += acc;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = kc + j * 256 + tid;
+      if (k < a.K) out[k] += acc[j];
+    }
   }
 }
 
 // ---- product layer -------------------------------------------------------------
+template <int V>
 __global__ void k_prod_fwd(ProdArgs a) {
-  const int64_t n = (int64_t)a.num_nodes * a.B;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
-    const int p = (int)(i / a.B), b = (int)(i - (int64_t)p * a.B);
-    float s = 0.0f;
-    for (int q = a.ch_ptr[p]; q < a.ch_ptr[p + 1]; ++q) s += a.vals[(int64_t)a.ch_ids[q] * a.B + b];
-    a.vals[(int64_t)(a.node_start + p) * a.B + b] = s;
+  const uint32_t QB = (uint32_t)(a.B / V), n = (uint32_t)a.num_nodes * QB;
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+    const uint32_t p = i / QB, b = (i - p * QB) * V;
+    Row<V> s;
+#pragma unroll
+    for (int k = 0; k < V; ++k) s.x[k] = 0.0f;
+    sum_rows<V>(s, a.vals, a.ch_ids, a.ch_ptr[p], a.ch_ptr[p + 1], a.B, b);
+    s.store(a.vals + (int64_t)(a.node_start + p) * a.B + b);
   }
 }
 
 // f[c] (=|+=) sum of the flows of c's parents in this layer (parent order).
+template <int V>
 __global__ void k_prod_bwd(ProdArgs a) {
-  const int64_t n = (int64_t)a.nuniq * a.B;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
-    const int k = (int)(i / a.B), b = (int)(i - (int64_t)k * a.B);
-    float s = 0.0f;
-    for (int q = a.pptr[k]; q < a.pptr[k + 1]; ++q) s += a.flows[(int64_t)a.parents[q] * a.B + b];
+  const uint32_t QB = (uint32_t)(a.B / V), n = (uint32_t)a.nuniq * QB;
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+    const uint32_t k = i / QB, b = (i - k * QB) * V;
+    Row<V> s;
+#pragma unroll
+    for (int e = 0; e < V; ++e) s.x[e] = 0.0f;
+    sum_rows<V>(s, a.flows, a.parents, a.pptr[k], a.pptr[k + 1], a.B, b);
     float* dst = a.flows + (int64_t)a.uchild[k] * a.B + b;
-    if (a.store) *dst = s; else *dst += s;
+    if (!a.store) {
+      Row<V> o;
+      o.load(dst);
+#pragma unroll
+      for (int e = 0; e < V; ++e) s.x[e] = o.x[e] + s.x[e];
+    }
+    s.store(dst);
   }
 }
 
 // ---- sum layer: column maxima, exponentiated children, scaled flows -------------
-// Tiles of 64 children x 64 samples over the source groups of a layer.
+// Column maxima: a workgroup takes 64 children (one packing tile) x 64*V
+// samples; each wave reduces 16 children, the waves combine in LDS and one
+// integer atomic max per sample publishes the tile's maximum.
+template <int V>
 __global__ void k_colmax(SumArgs a) {
-  __shared__ float red[4][64];
+  __shared__ float red[4][64 * V];
+  const int sbt = (a.B + 64 * V - 1) / (64 * V);
   const int t = blockIdx.x;
-  const int rt = t / a.btiles, bt = t - rt * a.btiles;
+  const int rt = t / sbt, st = t - rt * sbt;
   const int g = last_le(a.groups, a.ngroups, rt, [](const GroupRec& r) { return r.pk_start; });
   const GroupRec gr = a.groups[g];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int b = bt * 64 + lane;
+  const int b = st * 64 * V + lane * V;
   const int k0 = (rt - gr.pk_start) * 64 + w * 16;
-  float m = -INFINITY;
-  if (b < a.B)
-    for (int k = k0; k < k0 + 16 && k < gr.N; ++k)
-      m = fmaxf(m, a.vals[(int64_t)child_of(gr, a.chblocks, k) * a.B + b]);
-  red[w][lane] = m;
+  Row<V> m;
+#pragma unroll
+  for (int e = 0; e < V; ++e) m.x[e] = -INFINITY;
+  if (b < a.B) {
+    Row<V> c[16];
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk)      // every load in flight at once
+      if (k0 + kk < gr.N) c[kk].load(a.vals + (int64_t)child_of(gr, a.chblocks, k0 + kk) * a.B + b);
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk)
+      if (k0 + kk < gr.N)
+#pragma unroll
+        for (int e = 0; e < V; ++e) m.x[e] = fmaxf(m.x[e], c[kk].x[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < V; ++e) red[w][lane * V + e] = m.x[e];
   __syncthreads();
-  if (w == 0 && b < a.B) {
-    m = fmaxf(fmaxf(red[0][lane], red[1][lane]), fmaxf(red[2][lane], red[3][lane]));
-    if (k0 < gr.N) atomicMax(a.mkeys + (int64_t)gr.m_row * a.B + b, float_key(m));
-  }
-}
-
-// e[j,b] = exp(v[child j, b] - m[b]) split into planes, written node-major
-// (kept for the parameter flows) and batch-major (forward operand).
-__global__ void k_exp_pack(SumArgs a) {
-  __shared__ float tile[64][65];
-  const int t = blockIdx.x;
-  const int rt = t / a.btiles, bt = t - rt * a.btiles;
-  const int g = last_le(a.groups, a.ngroups, rt, [](const GroupRec& r) { return r.pk_start; });
-  const GroupRec gr = a.groups[g];
-  const int k0 = (rt - gr.pk_start) * 64, b0 = bt * 64;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int b = b0 + lane;
-  const float sh = (b < a.B) ? key_shift(a.mkeys[(int64_t)gr.m_row * a.B + b]) : 0.0f;
-  for (int r = w; r < 64; r += 4) {
-    const int k = k0 + r;
-    float e = 0.0f;
-    if (k < gr.N && b < a.B) e = expf(a.vals[(int64_t)child_of(gr, a.chblocks, k) * a.B + b] - sh);
-    tile[r][lane] = e;
-    if (b < a.B_padK)     // node-major copy for every group sharing these children
-      for (int q = g; q >= 0; q = a.groups[q].share_next)
-        split_store(e, a.np_direct, a.direct + panel(a.groups[q].e_row + k, b, a.direct_rows), a.direct_plane);
-  }
-  __syncthreads();
-  const int NpK = (gr.N + K_PAD - 1) / K_PAD * K_PAD;
-  for (int r = w; r < 64; r += 4) {          // r = sample within the tile, lane = child
-    const int bb = b0 + r, k = k0 + lane;
-    if (k < NpK && bb < a.B_pad)
-      split_store(tile[lane][r], a.np_trans, a.trans + panel(bb, gr.e_koff + k, a.B_pad), a.trans_plane);
-  }
-}
-
-// g[i,b] = f[i,b] / S[i,b] = f[i,b] * exp(m[b] - v[i,b]) (0 where f = 0 or
-// S = 0), with S the scaled sum kept by the forward (dividing by it avoids the
-// rounding of the absolute log-value v), split into planes and written
-// node-major (kept) and batch-major (element-flow operand).
-__global__ void k_g_pack(SumArgs a) {
-  __shared__ float tile[64][65];
-  const int t = blockIdx.x;
-  const int rt = t / a.btiles, bt = t - rt * a.btiles;
-  const int g = last_le(a.groups, a.ngroups, rt, [](const GroupRec& r) { return r.pg_start; });
-  const GroupRec gr = a.groups[g];
-  const int i0 = (rt - gr.pg_start) * 64, b0 = bt * 64;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int b = b0 + lane;
-  for (int r = w; r < 64; r += 4) {
-    const int i = i0 + r;
-    float gv = 0.0f;
-    if (i < gr.M && b < a.B) {
-      const float f = a.flows[(int64_t)(gr.out_start + i) * a.B + b];
-      const float S = a.ssum[(gr.s_row + i) * a.B + b];
-      gv = (f == 0.0f || !(S > 0.0f)) ? 0.0f : f / S;
+  if ((rt - gr.pk_start) * 64 >= gr.N) return;   // a padding tile: no child
+  for (int x = threadIdx.x; x < 64 * V; x += blockDim.x) {
+    const int bb = st * 64 * V + x;
+    if (bb < a.B) {
+      const float mx = fmaxf(fmaxf(red[0][x], red[1][x]), fmaxf(red[2][x], red[3][x]));
+      atomicMax(a.mkeys + (int64_t)gr.m_row * a.B + bb, float_key(mx));
     }
-    tile[r][lane] = gv;
-    if (b < a.B_padK)
-      split_store(gv, a.np_direct, a.direct + panel(gr.g_row + i, b, a.direct_rows), a.direct_plane);
+  }
+}
+
+// Split 8 values into np bfloat16 planes and store each plane as 16 bytes.
+__device__ __forceinline__ void split_store8(const float (&x)[8], int np, uint16_t* dst, int64_t plane) {
+  float r[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = x[e];
+  for (int p = 0; p < np; ++p) {
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint16_t h0 = f2bf(r[2 * e]), h1 = f2bf(r[2 * e + 1]);
+      r[2 * e] -= bf2f(h0);
+      r[2 * e + 1] -= bf2f(h1);
+      w[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+    }
+    *(uint4*)(dst + p * plane) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// Packing of a 64-row x 64-sample tile of an operand computed on the fly
+// (KIND 0: e = exp(v[child] - m[b]); KIND 1: g = f / S) into
+//   the node-major panel ("direct": rows drow0 + r, K = sample), 8 samples per
+//   16-byte store, for every group in the sharing chain (exp only), and
+//   the batch-major panel ("trans": rows = samples, K = tk0 + r), through an
+//   LDS transpose, 8 rows per 16-byte store.
+template <int KIND>
+__global__ void k_pack(SumArgs a) {
+  __shared__ float tile[64][65];
+  const int t = blockIdx.x;
+  const int rt = t / a.btiles, bt = t - rt * a.btiles;
+  const int g = KIND == 0 ? last_le(a.groups, a.ngroups, rt, [](const GroupRec& r) { return r.pk_start; })
+                          : last_le(a.groups, a.ngroups, rt, [](const GroupRec& r) { return r.pg_start; });
+  const GroupRec gr = a.groups[g];
+  const int r0 = (rt - (KIND == 0 ? gr.pk_start : gr.pg_start)) * 64, b0 = bt * 64;
+  const int nrows = KIND == 0 ? gr.N : gr.M;
+  const int tid = threadIdx.x;
+  // phase 1: item = (row, 8-sample chunk), 512 items
+  for (int it = tid; it < 512; it += 256) {
+    const int r = it >> 3, c = it & 7;
+    const int k = r0 + r, bs = b0 + c * 8;
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+    if (k < nrows && bs < a.B) {
+      // the 8 samples' inputs: two 16-byte loads per array when the chunk is
+      // whole and rows are 16-byte aligned (B % 4 == 0), else one by one
+      const bool vec = (a.B & 3) == 0 && bs + 8 <= a.B;
+      const float* p0;
+      const float* p1;
+      if (KIND == 0) {
+        p0 = a.vals + (int64_t)child_of(gr, a.chblocks, k) * a.B + bs;
+        p1 = (const float*)(a.mkeys + (int64_t)gr.m_row * a.B + bs);
+      } else {
+        p0 = a.flows + (int64_t)(gr.out_start + k) * a.B + bs;
+        p1 = a.ssum + (gr.s_row + k) * a.B + bs;
+      }
+      float u0[8], u1[8];
+      if (vec) {
+        Row<4> t;
+        t.load(p0); for (int e = 0; e < 4; ++e) u0[e] = t.x[e];
+        t.load(p0 + 4); for (int e = 0; e < 4; ++e) u0[4 + e] = t.x[e];
+        t.load(p1); for (int e = 0; e < 4; ++e) u1[e] = t.x[e];
+        t.load(p1 + 4); for (int e = 0; e < 4; ++e) u1[4 + e] = t.x[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const bool in = bs + e < a.B;
+          u0[e] = in ? p0[e] : 0.0f;
+          u1[e] = in ? p1[e] : 0.0f;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (bs + e >= a.B) continue;
+        if (KIND == 0) {
+          x[e] = expf(u0[e] - key_shift(__float_as_uint(u1[e])));
+        } else {
+          const float fv = u0[e], sv = u1[e];
+          x[e] = (fv == 0.0f || !(sv > 0.0f)) ? 0.0f : fv / sv;
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tile[r][c * 8 + e] = x[e];
+    if (bs < a.B_padK) {
+      if (KIND == 0) {
+        for (int q = g; q >= 0; q = a.groups[q].share_next)
+          split_store8(x, a.np_direct, a.direct + panel(a.groups[q].e_row + k, bs, a.direct_rows), a.direct_plane);
+      } else {
+        split_store8(x, a.np_direct, a.direct + panel(gr.g_row + k, bs, a.direct_rows), a.direct_plane);
+      }
+    }
   }
   __syncthreads();
-  const int MpK = (gr.M + K_PAD - 1) / K_PAD * K_PAD;
-  for (int r = w; r < 64; r += 4) {
-    const int bb = b0 + r, i = i0 + lane;
-    if (i < MpK && bb < a.B_pad)
-      split_store(tile[lane][r], a.np_trans, a.trans + panel(bb, gr.g_koff + i, a.B_pad), a.trans_plane);
+  // phase 2: item = (sample, 8-row chunk); K columns up to the padded row count
+  const int kpad = (nrows + K_PAD - 1) / K_PAD * K_PAD;
+  const int tk0 = KIND == 0 ? gr.e_koff : gr.g_koff;
+  if (r0 >= kpad) return;
+  for (int it = tid; it < 512; it += 256) {
+    const int bl = it & 63, c = it >> 6;
+    const int bb = b0 + bl;
+    if (bb >= a.B_pad) continue;
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = tile[c * 8 + e][bl];
+    split_store8(x, a.np_trans, a.trans + panel(bb, tk0 + r0 + c * 8, a.B_pad), a.trans_plane);
   }
 }
 
@@ -291,14 +494,23 @@ __global__ void k_theta_pack(ThetaArgs a) {
 }
 
 // Overlapping children: f[c] (=|+=) sum of the scratch rows of c (group order).
+template <int V>
 __global__ void k_elem_reduce(SumArgs a) {
-  const int64_t n = (int64_t)a.nuniq * a.B;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
-    const int k = (int)(i / a.B), b = (int)(i - (int64_t)k * a.B);
-    float s = 0.0f;
-    for (int q = a.red_ptr[k]; q < a.red_ptr[k + 1]; ++q) s += a.scratch[(int64_t)a.red_src[q] * a.B + b];
+  const uint32_t QB = (uint32_t)(a.B / V), n = (uint32_t)a.nuniq * QB;
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+    const uint32_t k = i / QB, b = (i - k * QB) * V;
+    Row<V> s;
+#pragma unroll
+    for (int e = 0; e < V; ++e) s.x[e] = 0.0f;
+    sum_rows<V>(s, a.scratch, a.red_src, a.red_ptr[k], a.red_ptr[k + 1], a.B, b);
     float* dst = a.out_flows + (int64_t)a.red_child[k] * a.B + b;
-    if (a.store) *dst = s; else *dst += s;
+    if (!a.store) {
+      Row<V> o;
+      o.load(dst);
+#pragma unroll
+      for (int e = 0; e < V; ++e) s.x[e] = o.x[e] + s.x[e];
+    }
+    s.store(dst);
   }
 }
 
@@ -347,37 +559,51 @@ void launch_copy_row(const float* src, float* dst, int B, hipStream_t s) {
 void launch_tokens_t(const int32_t* tok, int32_t* tokT, int B, int V, hipStream_t s) {
   hipLaunchKernelGGL(k_tokens_t, dim3((V + 31) / 32, (B + 31) / 32), dim3(256), 0, s, tok, tokT, B, V);
 }
-void launch_input_fwd(const InputArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_input_fwd, dim3(grid_for((int64_t)a.num_nodes * a.B)), dim3(256), 0, s, a);
-}
+// V = 4 needs B % 4 == 0 (rows 16-byte aligned); the base pointers come
+// from the caller's allocations, aligned far beyond 16 bytes.
+#define PC_LAUNCH_V(kern, n_items, args, s)                                                       \
+  do {                                                                                          \
+    if ((args).B % 4 == 0)                                                                      \
+      hipLaunchKernelGGL(kern<4>, dim3(grid_for((int64_t)(n_items) * ((args).B / 4))), dim3(256), 0, s, args); \
+    else                                                                                        \
+      hipLaunchKernelGGL(kern<1>, dim3(grid_for((int64_t)(n_items) * (args).B)), dim3(256), 0, s, args);       \
+  } while (0)
+
+void launch_input_fwd(const InputArgs& a, hipStream_t s) { PC_LAUNCH_V(k_input_fwd, a.num_nodes, a, s); }
 void launch_bucket(const int32_t* tokT, int V, int B, int Kmax, int32_t* bptr, int32_t* bidx, hipStream_t s) {
   const size_t sh = (size_t)(Kmax + 1 + B) * sizeof(int32_t);
   hipLaunchKernelGGL(k_bucket, dim3(V), dim3(256), sh, s, tokT, B, Kmax, bptr, bidx);
 }
 void launch_input_bwd(const InputArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_input_bwd, dim3(grid_for((int64_t)a.num_rows * a.K)), dim3(256), 0, s, a);
+  if (a.num_rows <= 0) return;
+  const size_t per = (size_t)(2 * a.B + 2 * a.K + 1) * sizeof(float);
+  const int nw = a.max_row_nodes >= 2 ? 4 : 1;
+  if (a.K <= 1024 && per * nw <= 64 * 1024) {
+    if (nw == 4) hipLaunchKernelGGL(k_input_bwd<4>, dim3(a.num_rows), dim3(256), per * 4, s, a);
+    else hipLaunchKernelGGL(k_input_bwd<1>, dim3(a.num_rows), dim3(64), per, s, a);
+  } else {
+    hipLaunchKernelGGL(k_input_bwd_wide, dim3(a.num_rows), dim3(256), (size_t)a.B * sizeof(float), s, a);
+  }
 }
-void launch_prod_fwd(const ProdArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_prod_fwd, dim3(grid_for((int64_t)a.num_nodes * a.B)), dim3(256), 0, s, a);
+void launch_prod_fwd(const ProdArgs& a, hipStream_t s) { PC_LAUNCH_V(k_prod_fwd, a.num_nodes, a, s); }
+void launch_prod_bwd(const ProdArgs& a, hipStream_t s) { PC_LAUNCH_V(k_prod_bwd, a.nuniq, a, s); }
+void launch_colmax(const SumArgs& a, int row_tiles, hipStream_t s) {
+  if (row_tiles <= 0) return;
+  if (a.B % 4 == 0)
+    hipLaunchKernelGGL(k_colmax<4>, dim3(row_tiles * ((a.B + 255) / 256)), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_colmax<1>, dim3(row_tiles * ((a.B + 63) / 64)), dim3(256), 0, s, a);
 }
-void launch_prod_bwd(const ProdArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_prod_bwd, dim3(grid_for((int64_t)a.nuniq * a.B)), dim3(256), 0, s, a);
+void launch_exp_pack(const SumArgs& a, int row_tiles, hipStream_t s) {
+  if (row_tiles > 0) hipLaunchKernelGGL(k_pack<0>, dim3(row_tiles * a.btiles), dim3(256), 0, s, a);
 }
-void launch_colmax(const SumArgs& a, int tiles, hipStream_t s) {
-  if (tiles > 0) hipLaunchKernelGGL(k_colmax, dim3(tiles), dim3(256), 0, s, a);
-}
-void launch_exp_pack(const SumArgs& a, int tiles, hipStream_t s) {
-  if (tiles > 0) hipLaunchKernelGGL(k_exp_pack, dim3(tiles), dim3(256), 0, s, a);
-}
-void launch_g_pack(const SumArgs& a, int tiles, hipStream_t s) {
-  if (tiles > 0) hipLaunchKernelGGL(k_g_pack, dim3(tiles), dim3(256), 0, s, a);
+void launch_g_pack(const SumArgs& a, int row_tiles, hipStream_t s) {
+  if (row_tiles > 0) hipLaunchKernelGGL(k_pack<1>, dim3(row_tiles * a.btiles), dim3(256), 0, s, a);
 }
 void launch_theta_pack(const ThetaArgs& a, int tiles, hipStream_t s) {
   if (tiles > 0) hipLaunchKernelGGL(k_theta_pack, dim3(tiles), dim3(256), 0, s, a);
 }
-void launch_elem_reduce(const SumArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_elem_reduce, dim3(grid_for((int64_t)a.nuniq * a.B)), dim3(256), 0, s, a);
-}
+void launch_elem_reduce(const SumArgs& a, hipStream_t s) { PC_LAUNCH_V(k_elem_reduce, a.nuniq, a, s); }
 void launch_em(const EmArgs& a, int rows, hipStream_t s) {
   if (rows > 0) hipLaunchKernelGGL(k_em, dim3(rows), dim3(256), 0, s, a);
 }

@@ -138,6 +138,31 @@ struct Pairs {
   }
 };
 
+// Fragment reads of one K step in the order the matrix instructions first
+// use them (read u < PA*FM: A plane u/FM, row block u%FM; else B).
+template <int PA, int PB, int FM, int FN>
+struct ReadOrder {
+  using PP = Pairs<PA, PB>;
+  static constexpr int NRD = PA * FM + PB * FN;
+  static constexpr int at(int o) {
+    bool seen[NRD] = {};
+    int n = 0;
+    for (int t = 0; t < PP::N * FM * FN; ++t) {
+      const int pr = t / (FM * FN), i = (t / FN) % FM, j = t % FN;
+      const int ua = PP::at(pr, 0) * FM + i, ub = PA * FM + PP::at(pr, 1) * FN + j;
+      if (!seen[ua]) {
+        seen[ua] = true;
+        if (n++ == o) return ua;
+      }
+      if (!seen[ub]) {
+        seen[ub] = true;
+        if (n++ == o) return ub;
+      }
+    }
+    return 0;
+  }
+};
+
 // LDS ring geometry.  A stage holds one K slice (KT wide) of every plane of
 // both operands, rows unpadded (KT * 2 bytes), 16-byte chunks XOR-swizzled by
 // row so that the 128-bit fragment reads of 16 consecutive rows touch 16
@@ -358,9 +383,14 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
 
   // One pipeline step on slice `it` held in stage j (its first fragments are
   // already in buffer 0): refill the stage read in the previous step with
-  // slice it+NS-1, multiply slice it, and (unless it is the last) at its end
-  // cross the barrier that makes slice it+1 readable and read its first
-  // fragments.
+  // slice it+NS-1, multiply slice it, and (unless it is the last) cross the
+  // barrier that makes slice it+1 readable at the start of the last K step
+  // and read the next slice's first fragments during it.  Fragment reads go
+  // into the first half of a K step's matrix instructions, in order of first
+  // use, so each has half a K step to land; the slice loads into the second
+  // half of the first K step.
+  using RO = ReadOrder<PA, PB, FM, FN>;
+  constexpr int H = NMF / 2;
   auto step = [&](auto LAST, int j) {
     constexpr bool last = decltype(LAST)::value;
     const int jn = j + 1 == NS ? 0 : j + 1, jl = j == 0 ? NS - 1 : j - 1;
@@ -371,41 +401,29 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
       constexpr int bf = ks & 1;
       using BF = std::integral_constant<int, bf>;
       using BN = std::integral_constant<int, bf ^ 1>;
-      if constexpr (ks + 1 < KS) {
-        // interleave: matrix instruction t, then its share of the fragment
-        // reads of the next K step (and, in the first, of the slice loads)
-        constexpr int NO = NRD + (ks == 0 ? PW : 0);
-        sfor<NMF>([&](auto T) {
-          constexpr int t = decltype(T)::value;
-          mfma(BF(), T);
-          constexpr int o0 = t * NO / NMF, o1 = (t + 1) * NO / NMF;
-          sfor<o1 - o0>([&](auto O) {
-            constexpr int o = o0 + decltype(O)::value;
-            if constexpr (o < NRD) frag(BN(), sbyte, std::integral_constant<int, ks + 1>(), std::integral_constant<int, o>());
-            else dma(jl, std::integral_constant<int, o - NRD>());
-          });
-          __builtin_amdgcn_sched_barrier(0);
-        });
-      } else if constexpr (!last) {
-        constexpr int H = NMF / 2;
-        sfor<H>([&](auto T) { mfma(BF(), T); });
-        __builtin_amdgcn_sched_barrier(0);
+      constexpr bool lastks = ks + 1 == KS;
+      if constexpr (lastks && !last) {
         // slice it+1 has landed once at most the NS-2 slices issued after it are in flight
+        __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(WaitVmLgkm<(NS - 2) * PW>::imm);
         ring_barrier();
-        sfor<NMF - H>([&](auto T) {
-          constexpr int t = H + decltype(T)::value;
-          mfma(BF(), std::integral_constant<int, t>());
-          constexpr int o0 = (t - H) * NRD / (NMF - H), o1 = (t - H + 1) * NRD / (NMF - H);
-          sfor<o1 - o0>([&](auto O) {
-            frag(std::integral_constant<int, 0>(), snext, std::integral_constant<int, 0>(),
-                 std::integral_constant<int, o0 + decltype(O)::value>());
-          });
-          __builtin_amdgcn_sched_barrier(0);
-        });
-      } else {
-        sfor<NMF>([&](auto T) { mfma(BF(), T); });
       }
+      sfor<NMF>([&](auto T) {
+        constexpr int t = decltype(T)::value;
+        mfma(BF(), T);
+        if constexpr (t < H) {
+          constexpr int o0 = t * NRD / H, o1 = (t + 1) * NRD / H;
+          sfor<o1 - o0>([&](auto O) {
+            constexpr int u = RO::at(o0 + decltype(O)::value);
+            if constexpr (!lastks) frag(BN(), sbyte, std::integral_constant<int, ks + 1>(), std::integral_constant<int, u>());
+            else if constexpr (!last) frag(std::integral_constant<int, 0>(), snext, std::integral_constant<int, 0>(), std::integral_constant<int, u>());
+          });
+        } else if constexpr (ks == 0) {
+          constexpr int o0 = (t - H) * PW / (NMF - H), o1 = (t - H + 1) * PW / (NMF - H);
+          sfor<o1 - o0>([&](auto O) { dma(jl, std::integral_constant<int, o0 + decltype(O)::value>()); });
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
     });
   };
 

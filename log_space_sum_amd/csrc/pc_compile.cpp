@@ -98,7 +98,10 @@ Handle* compile_layout(const pc_circuit_desc* d) {
       // row -> nodes CSR (ascending node order)
       ip.row_ptr.assign(ly.num_rows + 1, 0);
       for (int32_t i = 0; i < ly.num_nodes; ++i) ip.row_ptr[ip.row[i] + 1]++;
-      for (int32_t r = 0; r < ly.num_rows; ++r) ip.row_ptr[r + 1] += ip.row_ptr[r];
+      for (int32_t r = 0; r < ly.num_rows; ++r) {
+        ip.max_row_nodes = std::max(ip.max_row_nodes, ip.row_ptr[r + 1]);
+        ip.row_ptr[r + 1] += ip.row_ptr[r];
+      }
       ip.row_nodes.assign(ly.num_nodes, 0);
       std::vector<int32_t> fillp(ip.row_ptr.begin(), ip.row_ptr.end() - 1);
       for (int32_t i = 0; i < ly.num_nodes; ++i) ip.row_nodes[fillp[ip.row[i]]++] = ly.node_start + i;

@@ -7,7 +7,7 @@
 namespace pc {
 
 struct InputArgs {
-  int32_t B, node_start, num_nodes, K, num_rows, Kmax;
+  int32_t B, node_start, num_nodes, K, num_rows, Kmax, max_row_nodes;
   int64_t param_offset;
   const int32_t* var;
   const int32_t* row;
@@ -86,9 +86,9 @@ void launch_bucket(const int32_t* tokT, int V, int B, int Kmax, int32_t* bptr, i
 void launch_input_bwd(const InputArgs& a, hipStream_t s);
 void launch_prod_fwd(const ProdArgs& a, hipStream_t s);
 void launch_prod_bwd(const ProdArgs& a, hipStream_t s);
-void launch_colmax(const SumArgs& a, int tiles, hipStream_t s);
-void launch_exp_pack(const SumArgs& a, int tiles, hipStream_t s);
-void launch_g_pack(const SumArgs& a, int tiles, hipStream_t s);
+void launch_colmax(const SumArgs& a, int row_tiles, hipStream_t s);     // row_tiles: 64-child packing tiles
+void launch_exp_pack(const SumArgs& a, int row_tiles, hipStream_t s);
+void launch_g_pack(const SumArgs& a, int row_tiles, hipStream_t s);
 void launch_theta_pack(const ThetaArgs& a, int tiles, hipStream_t s);
 void launch_elem_reduce(const SumArgs& a, hipStream_t s);
 void launch_em(const EmArgs& a, int rows, hipStream_t s);

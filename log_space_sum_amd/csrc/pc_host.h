@@ -28,6 +28,7 @@ struct InputPlan {
   int64_t param_offset;
   std::vector<int32_t> var, row;
   std::vector<int32_t> row_ptr, row_nodes;  // row -> nodes using it (ascending)
+  int32_t max_row_nodes = 0;                 // most nodes sharing one parameter row
   int32_t* d_var = nullptr;
   int32_t* d_row = nullptr;
   int32_t* d_row_ptr = nullptr;
