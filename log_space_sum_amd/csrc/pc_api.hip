@@ -228,8 +228,22 @@ WsPlan plan_workspace(const Handle* h, int B) {
     p.partials = take((size_t)pel * 4);
     p.counters = take((size_t)nct * 4);
   }
-  p.lowrank = take(0);
-  p.lowrank_bytes = 0;
+  // LowRank: exp of the children (per layer), kept Z/S/U/W, per-layer
+  // coefficients, parameter-flow partials (ceil(B/8) copies of each block)
+  p.lr_nsg = (B + 7) / 8;
+  const bool lr = h->lowrank_slots > 0;
+  const size_t kr = (size_t)h->lowrank_rank;
+  const size_t lr0 = off;
+  p.lrE = take(lr ? Bs * h->max_ebt_cols * 4 : 0);
+  p.lrZ = take(lr ? (size_t)h->lr_rows * Bs * 4 : 0);
+  p.lrS = take(lr ? (size_t)h->lr_rows * Bs * 4 : 0);
+  p.lrU = take(lr ? (size_t)h->lr_rows * Bs * kr * 4 : 0);
+  p.lrW = take(lr ? (size_t)h->lr_rows * Bs * kr * 4 : 0);
+  p.lrC1 = take(lr ? (size_t)h->lr_max_m * Bs * 4 : 0);
+  p.lrC2 = take(lr ? (size_t)h->lr_max_m * Bs * 4 : 0);
+  p.lrP = take(lr ? (size_t)p.lr_nsg * h->lr_p_elems * 4 : 0);
+  p.lowrank = lr0;
+  p.lowrank_bytes = off - lr0;
   p.total = off;
   return p;
 }
@@ -281,16 +295,16 @@ struct Call {
   WsPlan p;
   WsView v;
   hipStream_t s;
+  void* ws;
 };
 
 Call begin_call(pc_handle hh, int B, void* ws, size_t ws_bytes, void* stream) {
   Handle* h = checked(hh);
   if (h->device < 0) fail(PC_ERR_NO_DEVICE, "handle was compiled without a device");
   if (B < 1) fail(PC_ERR_INVALID_ARG, "batch must be >= 1");
-  if (h->lowrank_slots > 0) fail(PC_ERR_UNSUPPORTED, "LowRank layers are not available in this build");
   if (!h->inputs.empty() && (size_t)(h->max_cats + 1 + B) * 4 > 65536)
     fail(PC_ERR_UNSUPPORTED, "categories + batch too large for the input-flow bucketing (limit 16383)");
-  Call c{h, plan_workspace(h, B), {}, (hipStream_t)stream};
+  Call c{h, plan_workspace(h, B), {}, (hipStream_t)stream, ws};
   if (c.p.total > 0 && !ws) fail(PC_ERR_INVALID_ARG, "null workspace");
   if (ws_bytes < c.p.total)
     fail(PC_ERR_WORKSPACE, "workspace too small: need " + std::to_string(c.p.total) + " bytes, got " +
@@ -344,6 +358,61 @@ InputArgs input_args(const Call& c, const InputPlan& ip, const float* params) {
   a.bptr = c.v.bucket_ptr;
   a.bidx = c.v.bucket_idx;
   a.params = params;
+  return a;
+}
+
+void check_lowrank_io(const Handle* h, const pc_lowrank_io* io, bool backward) {
+  if (h->lowrank_slots == 0) return;
+  if (!io) fail(PC_ERR_INVALID_ARG, "the circuit has LowRank groups: lowrank factors are required");
+  if (io->num_slots < h->lowrank_slots || !io->A || !io->B)
+    fail(PC_ERR_INVALID_ARG, "lowrank: need A and B for " + std::to_string(h->lowrank_slots) + " slots");
+  if (backward && (!io->dA || !io->dB)) fail(PC_ERR_INVALID_ARG, "lowrank: pc_backward needs dA and dB");
+  for (const auto& sp : h->sums)
+    for (const auto& r : sp.groups)
+      if (r.lowrank >= 0) {
+        if (!io->A[r.lowrank] || !io->B[r.lowrank]) fail(PC_ERR_INVALID_ARG, "lowrank: null factor");
+        if (backward && (!io->dA[r.lowrank] || !io->dB[r.lowrank])) fail(PC_ERR_INVALID_ARG, "lowrank: null gradient");
+      }
+}
+
+LRArgs lr_args(const Call& c, const SumPlan& sp, int g, const pc_lowrank_io* io, const float* params, float* vals,
+               float* flows) {
+  const Handle* h = c.h;
+  const GroupRec& r = sp.groups[g];
+  char* base = (char*)c.ws;
+  const int64_t B = c.v.B, kr = h->lowrank_rank;
+  LRArgs a{};
+  a.B = c.v.B;
+  a.M = r.M;
+  a.N = r.N;
+  a.krank = h->lowrank_rank;
+  a.out_start = r.out_start;
+  a.m_row = r.m_row;
+  a.e_koff = r.e_koff;
+  a.ldE = h->max_ebt_cols;
+  a.cbs = r.cbs;
+  a.blk_off = r.blk_off;
+  a.scratch_row = r.scratch_row;
+  a.store = sp.store ? 1 : 0;
+  a.chblocks = sp.d_blocks;
+  a.theta = params + r.param_offset;
+  a.A = io->A[r.lowrank];
+  a.Bf = io->B[r.lowrank];
+  a.mkeys = c.v.mkeys;
+  a.vals = vals;
+  a.flows = flows;
+  a.out_flows = flows;
+  a.scratch = c.v.scratch;
+  a.E = (float*)(base + c.p.lrE);
+  a.Z = (float*)(base + c.p.lrZ) + sp.lr_row[g] * B;
+  a.S = (float*)(base + c.p.lrS) + sp.lr_row[g] * B;
+  a.U = (float*)(base + c.p.lrU) + sp.lr_row[g] * B * kr;
+  a.W = (float*)(base + c.p.lrW) + sp.lr_row[g] * B * kr;
+  a.C1 = (float*)(base + c.p.lrC1);
+  a.C2 = (float*)(base + c.p.lrC2);
+  a.P = (float*)(base + c.p.lrP) + h->lr_p_off[r.block] * c.p.lr_nsg;
+  if (io->dA) a.dA = io->dA[r.lowrank];
+  if (io->dB) a.dB = io->dB[r.lowrank];
   return a;
 }
 
@@ -509,7 +578,7 @@ int pc_forward(pc_handle hh, int batch, const int32_t* tokens, const float* para
   try {
     Call c = begin_call(hh, batch, ws, ws_bytes, stream);
     Handle* h = c.h;
-    (void)lowrank;
+    check_lowrank_io(h, lowrank, false);
     if (!params || !node_vals) fail(PC_ERR_INVALID_ARG, "null params or node_vals");
     if (!h->inputs.empty() && !tokens) fail(PC_ERR_INVALID_ARG, "null tokens");
     if (ll && h->root < 0) fail(PC_ERR_INVALID_ARG, "ll requested but the circuit has no root");
@@ -569,6 +638,18 @@ int pc_forward(pc_handle hh, int batch, const int32_t* tokens, const float* para
           Timed t(h, KK_COLMAX, c.s);
           launch_colmax(a, sp.pktiles, c.s);
         }
+        if (sp.lowrank) {
+          for (int gi = 0; gi < (int)sp.groups.size(); ++gi) {
+            LRArgs la = lr_args(c, sp, gi, lowrank, params, node_vals, nullptr);
+            {
+              Timed t(h, KK_EXP, c.s);
+              launch_lr_exp(la, c.s);
+            }
+            Timed t(h, KK_LRFWD, c.s);
+            launch_lr_fwd(la, p.mode == PC_PREC_FP32, c.s);
+          }
+          continue;
+        }
         {
           Timed t(h, KK_EXP, c.s);
           launch_exp_pack(a, sp.pktiles, c.s);
@@ -609,7 +690,7 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
   try {
     Call c = begin_call(hh, batch, ws, ws_bytes, stream);
     Handle* h = c.h;
-    (void)lowrank;
+    check_lowrank_io(h, lowrank, true);
     (void)tokens;
     if (!params || !node_vals || !node_flows || !param_flows) fail(PC_ERR_INVALID_ARG, "null buffer");
     if (flags & ~PC_BWD_SEEDED) fail(PC_ERR_INVALID_ARG, "unknown flags");
@@ -636,9 +717,38 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
       Timed t(h, KK_OTHER, c.s);
       launch_bucket(v.tokT, h->num_vars, B, h->max_cats, v.bucket_ptr, v.bucket_idx, c.s);
     }
+    if (h->lowrank_slots > 0) {
+      Timed t(h, KK_OTHER, c.s);
+      launch_fill_u32((uint32_t*)((char*)c.ws + p.lrP), (int64_t)p.lr_nsg * h->lr_p_elems, 0u, c.s);
+    }
     for (int li = (int)h->layers.size() - 1; li >= 0; --li) {
       const LayerRef& r = h->layers[li];
-      if (r.kind == PC_LAYER_SUM) {
+      if (r.kind == PC_LAYER_SUM && h->sums[r.idx].lowrank) {
+        const SumPlan& sp = h->sums[r.idx];
+        for (int gi = 0; gi < (int)sp.groups.size(); ++gi) {
+          LRArgs la = lr_args(c, sp, gi, lowrank, params, vals, node_flows);
+          {
+            Timed t(h, KK_EXP, c.s);   // the forward reuses one buffer for every layer's exp
+            launch_lr_exp(la, c.s);
+          }
+          Timed t(h, KK_LRBWD, c.s);
+          launch_lr_coef(la, c.s);
+          launch_lr_bwd(la, p.mode == PC_PREC_FP32, c.s);
+          launch_lr_dA(la, c.s);
+        }
+        if (sp.overlap) {
+          SumArgs ra = sum_common(c, sp);
+          ra.nuniq = (int)sp.red_child.size();
+          ra.store = sp.store ? 1 : 0;
+          ra.red_child = sp.d_red_child;
+          ra.red_ptr = sp.d_red_ptr;
+          ra.red_src = sp.d_red_src;
+          ra.scratch = v.scratch;
+          ra.out_flows = node_flows;
+          Timed t(h, KK_OTHER, c.s);
+          launch_elem_reduce(ra, c.s);
+        }
+      } else if (r.kind == PC_LAYER_SUM) {
         const SumPlan& sp = h->sums[r.idx];
         SumArgs a = sum_common(c, sp);
         a.vals = vals;
@@ -700,6 +810,13 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
         Timed t(h, KK_INBWD, c.s);
         launch_input_bwd(a, c.s);
       }
+    }
+    for (size_t bi = 0; bi < h->blocks.size(); ++bi) {
+      if (h->lr_p_off[bi] < 0) continue;
+      const BlockRec& bl = h->blocks[bi];
+      Timed t(h, KK_LRBWD, c.s);
+      launch_lr_fplus((float*)((char*)c.ws + p.lrP) + h->lr_p_off[bi] * p.lr_nsg, p.lr_nsg, (int64_t)bl.M * bl.N,
+                      param_flows + bl.param_offset, c.s);
     }
     if (h->has_plain_sums) {
       GemmArgs g = gemm_common(c);

@@ -33,8 +33,8 @@ Handle* compile_layout(const pc_circuit_desc* d) {
   need(d->num_params >= 0, "num_params must be >= 0");
   need(d->num_layers >= 1 && d->layers != nullptr, "need at least one layer");
   need(d->root >= -1 && d->root < d->num_nodes, "root out of range");
-  if (d->lowrank_rank < 0 || d->lowrank_rank > 64)
-    fail(PC_ERR_UNSUPPORTED, "LowRank rank must be in 1..64 (the fused exp_sum kernels)");
+  if (d->lowrank_rank < 0 || d->lowrank_rank > 32)
+    fail(PC_ERR_UNSUPPORTED, "LowRank rank must be in 1..32 (the fused exp_sum kernels)");
 
   Handle* h = new Handle();
   h->num_nodes = d->num_nodes;
@@ -174,7 +174,7 @@ Handle* compile_layout(const pc_circuit_desc* d) {
         param_range(li, G.param_offset, (int64_t)G.num_nodes * N);
         need(G.lowrank_slot >= -1, gs + "bad lowrank slot");
         if (G.lowrank_slot >= 0) {
-          if (d->lowrank_rank < 1) fail(PC_ERR_UNSUPPORTED, gs + "LowRank group needs lowrank_rank in 1..64");
+          if (d->lowrank_rank < 1) fail(PC_ERR_UNSUPPORTED, gs + "LowRank group needs lowrank_rank in 1..32");
           ++n_lr;
           lowrank_slots = std::max(lowrank_slots, G.lowrank_slot + 1);
         }
@@ -397,6 +397,22 @@ Handle* compile_layout(const pc_circuit_desc* d) {
     h->earena_rows = erow;
     h->garena_rows = grow;
     for (auto& sp : h->sums) h->max_sum_groups = std::max<int32_t>(h->max_sum_groups, (int32_t)sp.groups.size());
+  }
+
+  // LowRank groups: rows of their kept forward records, and the parameter-flow
+  // partials of each distinct LowRank weight block
+  h->lr_p_off.assign(h->blocks.size(), -1);
+  for (auto& sp : h->sums) {
+    if (!sp.lowrank) continue;
+    for (auto& r : sp.groups) {
+      sp.lr_row.push_back(h->lr_rows);
+      h->lr_rows += r.M;
+      h->lr_max_m = std::max(h->lr_max_m, r.M);
+      if (h->lr_p_off[r.block] < 0) {
+        h->lr_p_off[r.block] = h->lr_p_elems;
+        h->lr_p_elems += (int64_t)r.M * r.N;
+      }
+    }
   }
 
   // EM row segments: every distinct block and input table

@@ -76,6 +76,42 @@ struct EmArgs {
   float step, pseudo;
 };
 
+// One LowRank exp_sum group (k_lowrank.hip).  Row-major weights theta [M, N];
+// factors A [B, M, krank], Bf [B, krank, N] (the slot's tensors); E: exp of
+// the children, float32 [B, ldE] at column e_koff; Z, S: [B, M] kept by the
+// forward; U, W: [B, M, krank] kept by the forward; C1, C2: [B, M]; P: the
+// group's block of ceil(B/8) parameter-flow partials [ceil(B/8), M, N].
+struct LRArgs {
+  int32_t B, M, N, krank;
+  int32_t out_start, m_row, e_koff, ldE, cbs, blk_off, scratch_row, store;
+  const int32_t* chblocks;
+  const float* theta;
+  const float* A;
+  const float* Bf;
+  const uint32_t* mkeys;
+  float* vals;
+  const float* flows;
+  float* out_flows;
+  float* scratch;
+  float* E;
+  float* Z;
+  float* S;
+  float* U;
+  float* W;
+  float* C1;
+  float* C2;
+  float* P;
+  float* dA;
+  float* dB;
+};
+
+void launch_lr_exp(const LRArgs& a, hipStream_t s);
+void launch_lr_fwd(const LRArgs& a, int fp32, hipStream_t s);
+void launch_lr_coef(const LRArgs& a, hipStream_t s);
+void launch_lr_bwd(const LRArgs& a, int fp32, hipStream_t s);
+void launch_lr_dA(const LRArgs& a, hipStream_t s);
+void launch_lr_fplus(const float* P, int nsg, int64_t elems, float* pflows, hipStream_t s);
+
 void launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
 void launch_fill_ranges(float* flows, const FillRange* d_ranges, int nranges, int64_t max_count, int B,
                         hipStream_t s);

@@ -62,6 +62,7 @@ struct SumPlan {
   int32_t scratch_rows = 0;
   int32_t max_npk = 0, max_mpk = 0;            // widest contraction of the forward / element flows
   std::vector<int32_t> red_child, red_ptr, red_src;   // overlap reduction CSR
+  std::vector<int64_t> lr_row;                 // LowRank: first row of each group's Z/S/U/W records
   GroupRec* d_groups = nullptr;
   int32_t* d_blocks = nullptr;
   int32_t* d_red_child = nullptr;
@@ -97,6 +98,10 @@ struct Handle {
   int32_t max_ebt_cols = 0, max_gbt_cols = 0, max_scratch_rows = 0;
   int32_t max_cats = 0;
   int32_t lowrank_slots = 0;
+  int64_t lr_rows = 0;                 // LowRank: rows of the kept Z/S/U/W records (sum of group M)
+  int32_t lr_max_m = 0;                // LowRank: largest group M (per-layer coefficients)
+  int64_t lr_p_elems = 0;              // LowRank: elements of the distinct LowRank weight blocks
+  std::vector<int64_t> lr_p_off;       // per weight block: offset of its LowRank partials, -1 if none
   std::vector<RowSeg> rowsegs;
   int32_t total_rows = 0;
   std::vector<int32_t> outputs;
@@ -134,6 +139,8 @@ struct WsPlan {
   int B, B_pad, B_padK, mode;
   int pl[3][2];
   size_t theta, thetaT, ebt, gbt, earena, garena, mkeys, ssum, scratch, tokT, bptr, bidx, lowrank;
+  size_t lrE, lrZ, lrS, lrU, lrW, lrC1, lrC2, lrP;   // LowRank regions (float32)
+  int lr_nsg;                                        // LowRank parameter-flow partials: ceil(B/8)
   size_t partials, counters;
   int64_t partial_elems;
   int32_t ncounters;

@@ -58,14 +58,21 @@ def run_gpu(cfg, mode="auto", splits=None, B=None, em=None, timing=False, device
     pflows = T.zeros(circ.num_params, device=dev)
     ll = T.empty(B, device=dev) if circ.root >= 0 else None
     ws = L.workspace(h, B, dev)
+    lr = grads = None
+    if cfg.get("lowrank") is not None:
+        lr = [(T.tensor(a[:B], device=dev), T.tensor(b[:B], device=dev)) for a, b in cfg["lowrank"]]
+        grads = [(T.full_like(a, float("nan")), T.full_like(b, float("nan"))) for a, b in lr]
     out = []
     for _ in range(repeat):
         pflows.zero_()
-        L.pc_forward(h, B, tokens, params, vals, ll, None, ws)
-        L.pc_backward(h, B, tokens, params, vals, flows, pflows, flags, None, None, ws)
+        L.pc_forward(h, B, tokens, params, vals, ll, lr, ws)
+        L.pc_backward(h, B, tokens, params, vals, flows, pflows, flags, lr, grads, ws)
         T.cuda.synchronize()
         r = dict(vals=vals.cpu().numpy().copy(), flows=flows.cpu().numpy().copy(),
                  pflows=pflows.cpu().numpy().copy(), ll=None if ll is None else ll.cpu().numpy().copy())
+        if grads is not None:
+            r["dA"] = [a.cpu().numpy().copy() for a, _ in grads]
+            r["dB"] = [b.cpu().numpy().copy() for _, b in grads]
         out.append(r)
     if em is not None:
         newp = params.clone()
@@ -94,9 +101,17 @@ def run_oracle(cfg, B=None, samples=None):
         ext = None if ext is None else ext[:, samples]
         seeds = None if seeds is None else seeds[:, samples]
     Bo = (len(samples) if samples is not None else (B or cfg["B"]))
-    V, ll = oracle.forward(circ, p, Bo, tokens=tok, external=ext)
-    r = oracle.backward(circ, p, V, tokens=tok, seed_flows=seeds)
-    return dict(vals=V, ll=ll, flows=r["flows"], pflows=r["param_flows"])
+    lr = cfg.get("lowrank")
+    if lr is not None:
+        sel = samples if samples is not None else slice(0, Bo)
+        lr = [(a[sel], b[sel]) for a, b in lr]
+    V, ll = oracle.forward(circ, p, Bo, tokens=tok, external=ext, lowrank=lr)
+    r = oracle.backward(circ, p, V, tokens=tok, seed_flows=seeds, lowrank=lr)
+    out = dict(vals=V, ll=ll, flows=r["flows"], pflows=r["param_flows"])
+    if lr is not None:
+        out["dA"] = [r["dA"][s] for s in range(len(lr))]
+        out["dB"] = [r["dB"][s] for s in range(len(lr))]
+    return out
 
 
 def rel_err(got, ref, floor=1e-6):
@@ -122,6 +137,27 @@ def check_values(got, ref, mode, what):
     say(f"  {what}: max abs err {worst:.3e} (mode {mode})")
     assert not bad.any(), f"{what}: {int(bad.sum())} entries out of tolerance, worst {worst:.3e} at {np.argwhere(bad)[0]}"
     return worst
+
+
+# dLL/dA and dLL/dB of LowRank slots: compared normwise and against the
+# array's largest entry (the gradient is a difference of two products, so
+# entries near zero carry the rounding of the terms that cancel):
+#   fp32-level: ||x - x*|| <= 1e-5 ||x*|| and max|x - x*| <= 1e-5 max|x*|;
+#   auto (gradient products in one bfloat16 term): 1e-2 and 3e-2.
+GRAD_TOL = {"fp32": (1e-5, 1e-5), "auto": (1e-2, 3e-2)}
+
+
+def check_grads(got, ref, mode, what):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    scale = max(np.abs(ref).max(), 1e-300)
+    en = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+    em = float(np.abs(got - ref).max() / scale)
+    say(f"  {what}: normwise {en:.3e}, max/max|ref| {em:.3e} (mode {mode})")
+    tn, tm = GRAD_TOL[mode]
+    assert np.isfinite(got).all(), f"{what}: non-finite entries"
+    assert en <= tn and em <= tm, f"{what}: normwise {en:.3e} (bound {tn}), max {em:.3e} (bound {tm})"
+    return en, em
 
 
 def num_sum_layers(circ):
@@ -178,12 +214,20 @@ def _sub_sum_circuit(circ, layer):
     return sub, kids, np.concatenate(outs)
 
 
-def local_oracle(cfg, gpu, samples=None):
+def local_oracle(cfg, gpu, samples=None, own_values=False):
     """Expected values, flows and parameter flows, layer by layer, from the
-    GPU's own inputs to each layer: a sum layer's values and its contributions
-    to its children's flows and to the parameter flows are recomputed by the
-    oracle from the GPU's children values and the GPU's flows at its outputs;
-    products and inputs likewise from theirs."""
+    GPU's own inputs to each step: a sum layer's values are recomputed by the
+    oracle from the GPU's children values; its backward step (contributions
+    to its children's flows, parameter flows, LowRank gradients) from the
+    GPU's children values, the GPU's values of the layer's own nodes and the
+    GPU's flows at its outputs -- the inputs of that step; products and
+    inputs likewise from theirs.  The layer's own values enter the backward
+    step as the exact recomputation (own_values=False: the GPU keeps the scaled
+    sums S of the forward and divides by them, so for fp32-level products its
+    backward sees S to float32 precision, while its stored float32 node values
+    carry an absolute rounding of |v| 2^-24 that it does not use), or as the
+    GPU's own stored values (own_values=True: the step given the forward's
+    outputs, for bf16 products whose forward error the value check covers)."""
     from workloads import circuits as W
     circ = cfg["circuit"]
     p = cfg["params"].astype(np.float64)
@@ -201,14 +245,25 @@ def local_oracle(cfg, gpu, samples=None):
     pflows = np.zeros(circ.num_params)
     tok = cfg.get("tokens")
     tok = None if tok is None else tok[cols]
+    lr = cfg.get("lowrank")
+    if lr is not None:
+        lr = [(a[cols], b[cols]) for a, b in lr]
+    dA, dB = {}, {}
     for layer in circ.layers:
         if isinstance(layer, W.Sum):
             sub, kids, outs = _sub_sum_circuit(circ, layer)
-            V, _ = oracle.forward(sub, p, Bs, external=GV[kids])
+            V, _ = oracle.forward(sub, p, Bs, external=GV[kids], lowrank=lr)
             vals[outs] = V[len(kids):]
-            r = oracle.backward(sub, p, V, seed_flows=GF[outs])
+            # the backward step of the layer from its GPU inputs: children
+            # values, the layer's own output values and its output flows
+            Vb = V.copy()
+            if own_values:
+                Vb[len(kids):] = GV[outs]
+            r = oracle.backward(sub, p, Vb, seed_flows=GF[outs], lowrank=lr)
             flows[kids] += r["flows"][:len(kids)]
             pflows += r["param_flows"]
+            dA.update(r["dA"])
+            dB.update(r["dB"])
         elif isinstance(layer, W.Product):
             ptr = layer.ch_ptr.astype(np.int64)
             ids = layer.ch_ids.astype(np.int64)
@@ -223,12 +278,13 @@ def local_oracle(cfg, gpu, samples=None):
             vals[rng_] = V[rng_]
             r = oracle.backward(sub, p, V, tokens=tok, seed_flows=GF[rng_])
             pflows += r["param_flows"]
-    return dict(vals=vals, flows=flows, pflows=pflows)
+    return dict(vals=vals, flows=flows, pflows=pflows, dA=dA, dB=dB)
 
 
 def check_local(cfg, gpu, mode, what, samples=None, pflows=True):
-    """Per-layer parity at the stated tolerances."""
-    loc = local_oracle(cfg, gpu, samples)
+    """Per-layer parity at the stated tolerances (the backward steps of auto
+    mode from the GPU's own forward outputs, see local_oracle)."""
+    loc = local_oracle(cfg, gpu, samples, own_values=(mode == "auto"))
     cols = slice(None) if samples is None else np.asarray(samples)
     check_values(gpu["vals"][:, cols], loc["vals"], mode, f"{what} per-layer values")
     check_flows(gpu["flows"][:, cols], loc["flows"], mode, f"{what} per-layer element flows")

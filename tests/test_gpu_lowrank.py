@@ -1,0 +1,92 @@
+"""GPU parity of the LowRank exp_sum scaled sum layers
+(pyjuice.parameterizations.LowRank, definition and Training): the fused
+forward and backward kernels through the C ABI against the float64 oracle, in
+both precision modes, on HMMs with a LowRank transition per position copy
+(ragged sizes, ranks 4..32, log-scale spreads 0.3..4 nats, batches around the
+sample groups of the kernels)."""
+import numpy as np
+import pytest
+
+from tests import gpu_util as G
+from workloads import make_config
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import log_space_sum_amd as L
+    L.lib()
+
+
+def _lowrank_full(cfg, mode, what):
+    """Values and log-likelihood end to end; values, element flows, parameter
+    flows, dLL/dA and dLL/dB per layer (recomputed by the oracle from each
+    layer's GPU inputs); flows end to end at the tolerance times the depth."""
+    G.say(f"case {what} mode={mode} B={cfg['B']}")
+    gpu = G.run_gpu(cfg, mode)
+    orc = G.run_oracle(cfg)
+    G.check_values(gpu["vals"], orc["vals"], mode, f"{what} node values")
+    G.check_values(gpu["ll"], orc["ll"], mode, f"{what} log-likelihood")
+    loc = G.check_local(cfg, gpu, mode, what)
+    depth = G.num_sum_layers(cfg["circuit"])
+    G.check_flows(gpu["flows"], orc["flows"], mode, f"{what} element flows end to end", scale=depth)
+    G.check_flows(gpu["pflows"], orc["pflows"], mode, f"{what} parameter flows end to end", scale=depth)
+    for s in range(len(gpu["dA"])):
+        G.check_grads(gpu["dA"][s], loc["dA"][s], mode, f"{what} slot {s} dLL/dA per layer")
+        G.check_grads(gpu["dB"][s], loc["dB"][s], mode, f"{what} slot {s} dLL/dB per layer")
+    return gpu, orc
+
+
+@pytest.mark.parametrize("mode", ["auto", "fp32"])
+@pytest.mark.parametrize("H,T,V,rank,B,spread", [
+    (8, 4, 5, 4, 20, 1.0),        # tiny: one partial 32-row strip
+    (64, 5, 16, 16, 37, 1.0),     # two strips, ragged sample groups
+    (40, 4, 7, 5, 23, 1.0),       # ragged rows and children
+    (96, 3, 9, 32, 24, 4.0),      # rank 32 (two K steps), 4-nat spread
+    (64, 4, 9, 16, 20, 0.3),      # 0.3-nat spread
+])
+def test_lowrank_hmm(mode, H, T, V, rank, B, spread):
+    cfg = make_config("lowrank", H=H, T=T, V=V, rank=rank, B=B, spread=spread)
+    _lowrank_full(cfg, mode, f"lowrank hmm H{H} T{T} r{rank} s{spread}")
+
+
+def test_lowrank_small_batch_runs_fp32():
+    """Batches below 16 run fp32-level products (the LowRank kernels included)."""
+    cfg = make_config("lowrank", H=40, T=3, V=6, rank=8, B=9)
+    _lowrank_full(cfg, "fp32", "lowrank small batch (auto requested)")
+
+
+def test_lowrank_requires_factors():
+    import torch
+    import log_space_sum_amd as L
+    cfg = make_config("lowrank", H=8, T=3, V=4, rank=4, B=16)
+    circ, B = cfg["circuit"], cfg["B"]
+    h = L.pc_compile_layout(circ, device=0)
+    params = torch.tensor(cfg["params"], device="cuda:0")
+    tokens = torch.tensor(cfg["tokens"], device="cuda:0")
+    vals = torch.empty((circ.num_nodes, B), device="cuda:0")
+    ws = L.workspace(h, B, "cuda:0")
+    with pytest.raises(L.PCError):
+        L.pc_forward(h, B, tokens, params, vals, None, None, ws)
+
+
+def test_lowrank_full_size_sampled():
+    """The LowRank workload at its full size (HMM 1024 states, 64 positions,
+    rank 16, batch 64): values, log-likelihood, element flows and dA, dB of
+    every slot on 3 samples against the oracle (samples are independent)."""
+    cfg = make_config("lowrank")
+    mode = "auto"
+    G.say(f"case lowrank full size mode={mode} B={cfg['B']}")
+    gpu = G.run_gpu(cfg, mode)
+    samples = np.array([0, 31, 63])
+    orc = G.run_oracle(cfg, samples=samples)
+    G.check_values(gpu["vals"][:, samples], orc["vals"], mode, "full-size node values (sampled)")
+    G.check_values(gpu["ll"][samples], orc["ll"], mode, "full-size log-likelihood (sampled)")
+    depth = G.num_sum_layers(cfg["circuit"])
+    G.check_flows(gpu["flows"][:, samples], orc["flows"], mode, "full-size element flows (sampled, e2e)", scale=depth)
+    for s in (0, 31, 62):
+        G.check_grads(gpu["dA"][s][samples], orc["dA"][s], mode, f"full-size slot {s} dLL/dA (sampled, e2e)")
+        G.check_grads(gpu["dB"][s][samples], orc["dB"][s], mode, f"full-size slot {s} dLL/dB (sampled, e2e)")
