@@ -80,11 +80,105 @@ def cpu_baseline(cfg, sample_B, budget_s=30.0):
             "seconds": dt}
 
 
+PEAK_EXP_G = 19660.0   # MI355X VALU transcendental rate: 157.3 TFLOP/s fp32 vector = 78.6 T FMA/s, exp at 1/4
+
+
+def bench_lowrank(args):
+    """The LowRank exp_sum workload: HMM 1024 states x 64 positions, 512
+    symbols, rank 16, batch 64, a (A, B) factor pair per position copy.  A step
+    is forward + backward (+ dLL/dA, dLL/dB) + EM.  The fused kernels are
+    bound by the exp rate: one exp per (sample, node, child) in the forward
+    and one in the backward's recomputation."""
+    import torch
+    import log_space_sum_amd as L
+    from workloads import make_config
+    cfg = make_config("lowrank")
+    circ, B = cfg["circuit"], cfg["B"]
+    dev = "cuda:0"
+    h = L.pc_compile_layout(circ, device=0)
+    L.pc_set_precision(h, args.mode)
+    params = torch.tensor(cfg["params"], device=dev)
+    tokens = torch.tensor(cfg["tokens"], device=dev)
+    vals = torch.empty((circ.num_nodes, B), device=dev)
+    flows = torch.empty((circ.num_nodes, B), device=dev)
+    pflows = torch.zeros(circ.num_params, device=dev)
+    ll = torch.empty(B, device=dev)
+    lr = [(torch.tensor(a, device=dev), torch.tensor(b, device=dev)) for a, b in cfg["lowrank"]]
+    grads = [(torch.empty_like(a), torch.empty_like(b)) for a, b in lr]
+    ws = L.workspace(h, B, dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        pflows.zero_()
+        L.pc_forward(h, B, tokens, params, vals, ll, lr, ws, stream.cuda_stream)
+        L.pc_backward(h, B, tokens, params, vals, flows, pflows, 0, lr, grads, ws, stream.cuda_stream)
+        L.pc_em_step(h, params, pflows, 1.0, 0.0, stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / args.steps * 1e3
+    L.pc_set_timing(h, True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kt = L.pc_kernel_times(h)
+    L.pc_set_timing(h, False)
+    pairs_per_sample = sum(g.num_nodes * g.num_children for ly in circ.layers if type(ly).__name__ == "Sum"
+                           for g in ly.groups if g.lowrank >= 0)
+    pairs = B * pairs_per_sample                       # (sample, node, child) triples per pass
+    exps = 2 * pairs                                   # forward + backward recomputation
+    value = exps / (ms * 1e-3) / 1e9
+    dom = max(("lowrank_fwd", "lowrank_bwd"), key=lambda k: kt[k][1])
+    n_launch, tot_ms = kt[dom]
+    per_launch_exps = pairs * args.steps / max(n_launch, 1)
+    avg_ms = tot_ms / max(n_launch, 1)
+    achieved = per_launch_exps / (avg_ms * 1e-3) / 1e9
+    out = {
+        "metric": "LowRank exp_sum fwd+bwd exp throughput (frac of VALU exp peak), HMM 1024 lat x 64 pos, rank 16, batch 64",
+        "value": round(value, 2), "unit": "Gexp/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16-split" if args.mode == "auto" else "bf16x6-split", "data": "synthetic",
+        "config": {"workload": "lowrank hmm1024x64 symbols 512 rank 16 batch 64 fwd+bwd+em", "precision_mode": args.mode,
+                   "global_batch": B},
+        "kernel_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in kt.items() if v[0]},
+        "roofline": {"kernel": dom, "bound": "alu", "achieved": round(achieved, 2), "peak": PEAK_EXP_G,
+                     "unit": "Gexp/s", "frac": round(achieved / PEAK_EXP_G, 4), "traffic": None,
+                     "avg_launch_ms": round(avg_ms, 5)},
+    }
+    if not args.no_cpu:
+        import numpy as np
+        import oracle
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        except Exception:  # noqa: BLE001
+            threads = os.cpu_count()
+        sb = 2
+        p = cfg["params"].astype(np.float64)
+        lrs = [(a[:sb], b[:sb]) for a, b in cfg["lowrank"]]
+        t0 = time.perf_counter()
+        V, _ = oracle.forward(circ, p, sb, tokens=cfg["tokens"][:sb], lowrank=lrs)
+        oracle.backward(circ, p, V, tokens=cfg["tokens"][:sb], lowrank=lrs)
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(2 * pairs_per_sample * sb / dt / 1e9, 4),
+                               "unit": "Gexp/s", "cores": int(threads), "kind": "oracle",
+                               "sample": f"float64 oracle forward+backward on {sb} of the {B} samples, {dt:.1f} s"}
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="hmm4096", choices=["hmm4096", "lowrank"],
+                    help="hmm4096: the metric's workload (default); lowrank: the LowRank exp_sum HMM "
+                         "(1024 states, 64 positions, rank 16, batch 64)")
     ap.add_argument("--mode", default="auto", choices=["auto", "fp32"])
     ap.add_argument("--batch", type=int, default=512)
     ap.add_argument("--H", type=int, default=4096)
@@ -119,6 +213,8 @@ def main():
     import log_space_sum_amd as L
     from workloads import make_config
 
+    if args.workload == "lowrank":
+        return bench_lowrank(args)
     cfg = make_config("hmm4096", H=args.H, T=args.T, B=args.batch)
     circ, B = cfg["circuit"], cfg["B"]
     dev = "cuda:0"

@@ -37,8 +37,10 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kChunk = 1024;        // columns (forward) or rows (backward) of one staged weight slab
-constexpr int kSlab = 32 * (kChunk + 4);
+// weight slabs staged in LDS: 512 columns (forward) or 448 rows (backward) of
+// a 32-wide strip, so that two workgroups share a CU
+constexpr int kChunkF = 512, kChunkB = 448;
+constexpr int kSlabF = 32 * (kChunkF + 4), kSlabB = 32 * (kChunkB + 4);
 
 __device__ __forceinline__ float key_to_shift_lr(uint32_t k) {
   const uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
@@ -106,7 +108,7 @@ __global__ void k_lr_exp(LRArgs a) {
 // Forward: workgroup = 32 rows x 4 samples (one per wave), all children.
 template <int PH, int PG, int KC>
 __global__ __launch_bounds__(256) void k_lr_fwd(LRArgs a) {
-  __shared__ __attribute__((aligned(16))) float slab[kSlab];   // theta rows [32][C + 4]
+  __shared__ __attribute__((aligned(16))) float slab[kSlabF];   // theta rows [32][C + 4]
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int mt = (a.M + 31) / 32;
@@ -133,32 +135,63 @@ __global__ __launch_bounds__(256) void k_lr_fwd(LRArgs a) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) U[r] = W[r] = 0.0f;
 
-  for (int c0 = 0; c0 < N; c0 += kChunk) {
+  for (int c0 = 0; c0 < N; c0 += kChunkF) {
     // weights of the strip, zero outside the block (rows >= M, columns >= N)
-    const int cw = (min(kChunk, N - c0) + 31) / 32 * 32, CP = cw + 4;
+    const int cw = (min(kChunkF, N - c0) + 31) / 32 * 32, CP = cw + 4;
     __syncthreads();
-    for (int idx = tid; idx < 32 * cw; idx += 256) {
-      const int r = idx / cw, c = idx - r * cw;
-      slab[r * CP + c] = (i0 + r < M && c0 + c < N) ? a.theta[(int64_t)(i0 + r) * N + c0 + c] : 0.0f;
+    for (int base = tid; base < 32 * cw; base += 256 * 8) {   // 8 loads in flight per thread
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int idx = base + u * 256, r = idx / cw, c = idx - r * cw;
+        v[u] = (idx < 32 * cw && i0 + r < M && c0 + c < N) ? a.theta[(int64_t)(i0 + r) * N + c0 + c] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int idx = base + u * 256, r = idx / cw, c = idx - r * cw;
+        if (idx < 32 * cw) slab[r * CP + c] = v[u];
+      }
     }
     __syncthreads();
     if (!act) continue;
-    for (int jb = 0; jb < cw / 32; ++jb) {
+    // global operands of one 32-child block, loaded a block ahead
+    struct Ld {
+      float xh[KC][8];    // B_b[k, j] for h^T: row j = j0 + l32, k = kc*16 + h*8 + e
+      float4 ev[4];       // e[j, b] at rows j0 + g*8 + h*4 .. +3
+      float xb[2][8];     // B_b[k, j] for U, W: row k = l32, K chunk cc
+    };
+    auto load = [&](int j0, Ld& L) {
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int k = kc * 16 + h * 8 + e;
+          L.xh[kc][e] = (k < kr && j0 + l32 < N) ? Bb[(int64_t)k * N + j0 + l32] : 0.0f;
+        }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) L.ev[g] = ld4(Eb + j0 + g * 8 + h * 4);
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = j0 + 16 * cc + (e / 4) * 8 + h * 4 + (e % 4);
+          L.xb[cc][e] = (l32 < kr && j < N) ? Bb[(int64_t)l32 * N + j] : 0.0f;
+        }
+    };
+    const int nb = cw / 32;
+    // one 32-child block from the operands in `cur`, with the block two ahead
+    // loaded into the other buffer meanwhile (ping-pong: no register copies)
+    auto block = [&](int jb, const Ld& cur, Ld& fill) {
       const int j0 = c0 + jb * 32;
+      if (jb + 1 < nb) load(j0 + 32, fill);
       // h^T[j, i] = sum_k B_b[k, j] A_b[i, k]: first operand rows j = j0 + l32
       f32x16_t H;
 #pragma unroll
       for (int r = 0; r < 16; ++r) H[r] = 0.0f;
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int k = kc * 16 + h * 8 + e;
-          x[e] = (k < kr && j0 + l32 < N) ? Bb[(int64_t)k * N + j0 + l32] : 0.0f;
-        }
         bf16x8_t pb[PH];
-        split8<PH>(x, pb);
+        split8<PH>(cur.xh[kc], pb);
         mfma_planes<PH>(H, pb, bA[kc]);
       }
       // register r: row j = j0 + (r/4)*8 + h*4 + r%4, column i = i0 + l32
@@ -167,12 +200,11 @@ __global__ __launch_bounds__(256) void k_lr_fwd(LRArgs a) {
       for (int g = 0; g < 4; ++g) {
         const int jr = g * 8 + h * 4;
         const float4 th = *(const float4*)&slab[l32 * CP + (j0 - c0) + jr];
-        const float4 ev = ld4(Eb + j0 + jr);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = g * 4 + e;
           q[r] = at4(th, e) * __builtin_amdgcn_exp2f(H[r]);
-          qe[r] = q[r] * at4(ev, e);
+          qe[r] = q[r] * at4(cur.ev[g], e);
           Zp += q[r];
           Sp += qe[r];
         }
@@ -182,24 +214,25 @@ __global__ __launch_bounds__(256) void k_lr_fwd(LRArgs a) {
       // is register 8cc + e, row j0 + 16cc + (e/4)*8 + h*4 + e%4)
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
-        float xb[8], xq[8], xw[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int j = j0 + 16 * cc + (e / 4) * 8 + h * 4 + (e % 4);
-          xb[e] = (l32 < kr && j < N) ? Bb[(int64_t)l32 * N + j] : 0.0f;
-        }
+        float xq[8], xw[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           xq[e] = qe[8 * cc + e];
           xw[e] = q[8 * cc + e];
         }
         bf16x8_t pb[PG], pq[PG], pw[PG];
-        split8<PG>(xb, pb);
+        split8<PG>(cur.xb[cc], pb);
         split8<PG>(xq, pq);
         split8<PG>(xw, pw);
         mfma_planes<PG>(U, pb, pq);
         mfma_planes<PG>(W, pb, pw);
       }
+    };
+    Ld b0, b1;
+    load(c0, b0);
+    for (int jb = 0; jb < nb; jb += 2) {
+      block(jb, b0, b1);
+      if (jb + 1 < nb) block(jb + 1, b1, b0);
     }
   }
   const float Z = Zp + __shfl_xor(Zp, 32), S = Sp + __shfl_xor(Sp, 32);
@@ -239,7 +272,7 @@ __global__ void k_lr_coef(LRArgs a) {
 // Backward: workgroup = 32 children x 8 samples (two per wave), all rows.
 template <int PH, int PG, int KC>
 __global__ __launch_bounds__(256) void k_lr_bwd(LRArgs a) {
-  __shared__ __attribute__((aligned(16))) float slab[kSlab];   // theta^T [32][R + 4]
+  __shared__ __attribute__((aligned(16))) float slab[kSlabB];   // theta^T [32][R + 4]
   __shared__ float xch[4][1024];                                 // parameter flows of a 32 x 32 tile per wave
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -278,74 +311,112 @@ __global__ __launch_bounds__(256) void k_lr_bwd(LRArgs a) {
     for (int r = 0; r < 16; ++r) dB[s][r] = 0.0f;
   float* P = a.P + (int64_t)sg * M * N;
 
-  for (int r0 = 0; r0 < M; r0 += kChunk) {
+  for (int r0 = 0; r0 < M; r0 += kChunkB) {
     // transposed weights of the strip, zero outside the block
-    const int rw = (min(kChunk, M - r0) + 31) / 32 * 32, RP = rw + 4;
+    const int rw = (min(kChunkB, M - r0) + 31) / 32 * 32, RP = rw + 4;
     __syncthreads();
-    for (int idx = tid; idx < rw * 32; idx += 256) {
-      const int ii = idx >> 5, jj = idx & 31;
-      slab[jj * RP + ii] = (r0 + ii < M && j0 + jj < N) ? a.theta[(int64_t)(r0 + ii) * N + j0 + jj] : 0.0f;
+    for (int base = tid; base < rw * 32; base += 256 * 8) {   // 8 loads in flight per thread
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int idx = base + u * 256, ii = idx >> 5, jj = idx & 31;
+        v[u] = (idx < rw * 32 && r0 + ii < M && j0 + jj < N) ? a.theta[(int64_t)(r0 + ii) * N + j0 + jj] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int idx = base + u * 256, ii = idx >> 5, jj = idx & 31;
+        if (idx < rw * 32) slab[jj * RP + ii] = v[u];
+      }
     }
     __syncthreads();
+    // global operands of one (32-row block, sample) step, loaded a step ahead
+    struct Ld {
+      float xa[KC][8];    // A_b[i, k] log2(e) for h: row i = i0 + l32, k = kc*16 + h*8 + e
+      float c1[16], c2[16];
+      float xk[2][8];     // A_b[i, k] for dB: row k = l32, K chunk cc
+    };
+    auto load = [&](int i0, int s, Ld& L) {
+      const int b = bs[s];
+      const float* Ab = a.A + (int64_t)b * M * kr;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int k = kc * 16 + h * 8 + e;
+          L.xa[kc][e] = (k < kr && i0 + l32 < M) ? Ab[(int64_t)(i0 + l32) * kr + k] * kLog2e : 0.0f;
+        }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = i0 + (r / 4) * 8 + h * 4 + (r % 4);
+        L.c1[r] = i < M ? a.C1[(int64_t)b * M + i] : 0.0f;
+        L.c2[r] = i < M ? a.C2[(int64_t)b * M + i] : 0.0f;
+      }
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int i = i0 + 16 * cc + (e / 4) * 8 + h * 4 + (e % 4);
+          L.xk[cc][e] = (l32 < kr && i < M) ? Ab[(int64_t)i * kr + l32] : 0.0f;
+        }
+    };
+    // the wave's steps: (row block ib, sample s) for its active samples
+    const int nsteps = (rw / 32) * (act[1] ? 2 : act[0] ? 1 : 0);
+    const int per = act[1] ? 2 : 1;
+    Ld buf[2];
+    if (nsteps > 0) load(r0, 0, buf[0]);
     for (int ib = 0; ib < rw / 32; ++ib) {
       const int i0 = r0 + ib * 32;
       float fp[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) fp[r] = 0.0f;
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        if (!act[s]) continue;
-        const int b = bs[s];
-        const float* Ab = a.A + (int64_t)b * M * kr;
-        // h[i, j] = sum_k A_b[i, k] B_b[k, j]: first operand rows i = i0 + l32
-        f32x16_t H;
+      for (int s = 0; s < 2; ++s) {      // static sample index: the per-sample operands stay in registers
+        if (s >= per || nsteps == 0) continue;
+        const int t = ib * per + s;
+        // ping-pong: step t reads buf[t & 1] and fills the other with step t + 1
+        auto stepk = [&](const Ld& cur, Ld& fill) {
+          if (t + 1 < nsteps) load(r0 + ((t + 1) / per) * 32, (t + 1) % per, fill);
+          // h[i, j] = sum_k A_b[i, k] B_b[k, j]: first operand rows i = i0 + l32
+          f32x16_t H;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) H[r] = 0.0f;
+          for (int r = 0; r < 16; ++r) H[r] = 0.0f;
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-          float x[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int k = kc * 16 + h * 8 + e;
-            x[e] = (k < kr && i0 + l32 < M) ? Ab[(int64_t)(i0 + l32) * kr + k] * kLog2e : 0.0f;
+          for (int kc = 0; kc < KC; ++kc) {
+            bf16x8_t pa[PH];
+            split8<PH>(cur.xa[kc], pa);
+            mfma_planes<PH>(H, pa, bB[s][kc]);
           }
-          bf16x8_t pa[PH];
-          split8<PH>(x, pa);
-          mfma_planes<PH>(H, pa, bB[s][kc]);
-        }
-        // register r: row i = i0 + (r/4)*8 + h*4 + r%4, column j = j0 + l32
-        float X[16];
+          // register r: row i = i0 + (r/4)*8 + h*4 + r%4, column j = j0 + l32
+          float X[16];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int ir = g * 8 + h * 4;
-          const float4 th = *(const float4*)&slab[l32 * RP + (i0 - r0) + ir];
+          for (int g = 0; g < 4; ++g) {
+            const int ir = g * 8 + h * 4;
+            const float4 th = *(const float4*)&slab[l32 * RP + (i0 - r0) + ir];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = g * 4 + e, i = i0 + ir + e;
-            const float c1 = i < M ? a.C1[(int64_t)b * M + i] : 0.0f, c2 = i < M ? a.C2[(int64_t)b * M + i] : 0.0f;
-            const float q = at4(th, e) * __builtin_amdgcn_exp2f(H[r]);
-            const float eps = q * ev[s] * c1;
-            X[r] = q * (ev[s] * c1 - c2);
-            fcp[s] += eps;
-            fp[r] += eps;
+            for (int e = 0; e < 4; ++e) {
+              const int r = g * 4 + e;
+              const float q = at4(th, e) * __builtin_amdgcn_exp2f(H[r]);
+              const float eps = q * ev[s] * cur.c1[r];
+              X[r] = q * (ev[s] * cur.c1[r] - cur.c2[r]);
+              fcp[s] += eps;
+              fp[r] += eps;
+            }
           }
-        }
-        // dB[k, j] += sum_i A_b[i, k] X[i, j]: K index 8h + e of chunk cc is
-        // register 8cc + e, row i0 + 16cc + (e/4)*8 + h*4 + e%4
+          // dB[k, j] += sum_i A_b[i, k] X[i, j]: K index 8h + e of chunk cc is
+          // register 8cc + e, row i0 + 16cc + (e/4)*8 + h*4 + e%4
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          float xa[8], xx[8];
+          for (int cc = 0; cc < 2; ++cc) {
+            float xx[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int i = i0 + 16 * cc + (e / 4) * 8 + h * 4 + (e % 4);
-            xa[e] = (l32 < kr && i < M) ? Ab[(int64_t)i * kr + l32] : 0.0f;
-            xx[e] = X[8 * cc + e];
+            for (int e = 0; e < 8; ++e) xx[e] = X[8 * cc + e];
+            bf16x8_t pa[PG], px[PG];
+            split8<PG>(cur.xk[cc], pa);
+            split8<PG>(xx, px);
+            mfma_planes<PG>(dB[s], pa, px);
           }
-          bf16x8_t pa[PG], px[PG];
-          split8<PG>(xa, pa);
-          split8<PG>(xx, px);
-          mfma_planes<PG>(dB[s], pa, px);
-        }
+        };
+        if (t & 1) stepk(buf[1], buf[0]);
+        else stepk(buf[0], buf[1]);
       }
       // parameter flows of the tile, summed over the waves in order
 #pragma unroll
