@@ -195,15 +195,22 @@ int pc_set_split(pc_handle h, int mode, int gemm_kind, int planes_a, int planes_
 
 /* Product-kernel tuning (advanced; results change only by float32 summation
  * order).  PC_OPT_LAYER_TILE: output tile of the per-layer forward and
- * element-flow products, 0 automatic (128 x 128), 1 128 x 128, 2 256 x 128.
+ * element-flow products, 0 automatic (128 x 128), 1 128 x 128, 2 256 x 128,
+ * 3 128 x 256.
  * PC_OPT_PARAM_TILE: tile of the parameter-flow product, 0 automatic
  * (128 x 128), 1 128 x 128, 2 256 x 256 (when the operand split allows).
  * PC_OPT_SPLIT_MAX: largest K split of a per-layer product (1, 2, 4 or 8;
- * default 8).  Changing an option can change pc_workspace_bytes.
+ * default 8).  PC_OPT_FUSE: 1 (default) evaluates a product layer inside the
+ * adjacent sum layer's memory-bound kernels where the layout allows it (the
+ * forward in the next sum layer's column maxima, the backward in the previous
+ * sum layer's scaled-flow packing; identical results), 0 launches the
+ * product kernels separately.  Changing an option can change
+ * pc_workspace_bytes.
  * Errors: PC_ERR_INVALID_ARG (unknown option or value). */
 #define PC_OPT_LAYER_TILE 0
 #define PC_OPT_PARAM_TILE 1
 #define PC_OPT_SPLIT_MAX  2
+#define PC_OPT_FUSE       3
 int pc_set_option(pc_handle h, int option, int value);
 
 /* Bytes of workspace pc_forward / pc_backward need for `batch` samples in the

@@ -100,6 +100,9 @@ struct Row {
     if constexpr (V == 4) {
       const float4 t = *(const float4*)p;
       x[0] = t.x; x[1] = t.y; x[2] = t.z; x[3] = t.w;
+    } else if constexpr (V == 2) {
+      const float2 t = *(const float2*)p;
+      x[0] = t.x; x[1] = t.y;
     } else {
 #pragma unroll
       for (int k = 0; k < V; ++k) x[k] = p[k];
@@ -107,6 +110,7 @@ struct Row {
   }
   __device__ __forceinline__ void store(float* p) const {
     if constexpr (V == 4) *(float4*)p = make_float4(x[0], x[1], x[2], x[3]);
+    else if constexpr (V == 2) *(float2*)p = make_float2(x[0], x[1]);
     else
 #pragma unroll
       for (int k = 0; k < V; ++k) p[k] = x[k];
@@ -290,7 +294,19 @@ __global__ void k_prod_fwd(ProdArgs a) {
     Row<V> s;
 #pragma unroll
     for (int k = 0; k < V; ++k) s.x[k] = 0.0f;
-    sum_rows<V>(s, a.vals, a.ch_ids, a.ch_ptr[p], a.ch_ptr[p + 1], a.B, b);
+    if (a.affine) {   // child q at abase[q] + p: every load issued before the first add
+      Row<V> c[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (q < a.deg) c[q].load(a.vals + (int64_t)(a.abase[q] + (int)p) * a.B + b);
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (q < a.deg)
+#pragma unroll
+          for (int e = 0; e < V; ++e) s.x[e] += c[q].x[e];
+    } else {
+      sum_rows<V>(s, a.vals, a.ch_ids, a.ch_ptr[p], a.ch_ptr[p + 1], a.B, b);
+    }
     s.store(a.vals + (int64_t)(a.node_start + p) * a.B + b);
   }
 }
@@ -319,9 +335,13 @@ __global__ void k_prod_bwd(ProdArgs a) {
 // ---- sum layer: column maxima, exponentiated children, scaled flows -------------
 // Column maxima: a workgroup takes 64 children (one packing tile) x 64*V
 // samples; each wave reduces 16 children, the waves combine in LDS and one
-// integer atomic max per sample publishes the tile's maximum.
-template <int V>
-__global__ void k_colmax(SumArgs a) {
+// integer atomic max per sample publishes the tile's maximum.  With PROD the
+// children that are nodes of the preceding product layer are evaluated here:
+// each is the sum of its own children in child-list order (as the product
+// kernel adds them), stored, and used for the maximum.  The loads of all 16
+// rows go out together, one child slot at a time.
+template <int V, bool PROD>
+__global__ __launch_bounds__(256) void k_colmax(SumArgs a) {
   __shared__ float red[4][64 * V];
   const int sbt = (a.B + 64 * V - 1) / (64 * V);
   const int t = blockIdx.x;
@@ -336,9 +356,89 @@ __global__ void k_colmax(SumArgs a) {
   for (int e = 0; e < V; ++e) m.x[e] = -INFINITY;
   if (b < a.B) {
     Row<V> c[16];
+    if constexpr (!PROD) {
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk)      // every load in flight at once
-      if (k0 + kk < gr.N) c[kk].load(a.vals + (int64_t)child_of(gr, a.chblocks, k0 + kk) * a.B + b);
+      for (int kk = 0; kk < 16; ++kk)      // every load in flight at once
+        if (k0 + kk < gr.N) c[kk].load(a.vals + (int64_t)child_of(gr, a.chblocks, k0 + kk) * a.B + b);
+    } else {
+      int32_t node[16], q0[16], q1[16];
+      if (a.fp_affine) {   // child q of product node i at fp_abase[q] + i: no index loads
+        bool isp[16];
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+          isp[kk] = false;
+          if (k0 + kk < gr.N) {
+            node[kk] = child_of(gr, a.chblocks, k0 + kk);
+            const uint32_t p = (uint32_t)(node[kk] - a.fp_start);
+            isp[kk] = p < (uint32_t)a.fp_count;
+            q0[kk] = (int32_t)p;
+            if (!isp[kk]) c[kk].load(a.vals + (int64_t)node[kk] * a.B + b);
+          }
+        }
+        Row<V> u[16][2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q)      // the first two child slots of all 16 rows at once
+#pragma unroll
+          for (int kk = 0; kk < 16; ++kk)
+            if (isp[kk] && q < a.fp_maxdeg) u[kk][q].load(a.vals + (int64_t)(a.fp_abase[q] + q0[kk]) * a.B + b);
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk)
+          if (isp[kk]) {
+#pragma unroll
+            for (int e = 0; e < V; ++e) c[kk].x[e] = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+              if (q < a.fp_maxdeg)
+#pragma unroll
+                for (int e = 0; e < V; ++e) c[kk].x[e] += u[kk][q].x[e];
+          }
+        for (int q = 2; q < a.fp_maxdeg; ++q) {
+#pragma unroll
+          for (int kk = 0; kk < 16; ++kk)
+            if (isp[kk]) u[kk][0].load(a.vals + (int64_t)(a.fp_abase[q] + q0[kk]) * a.B + b);
+#pragma unroll
+          for (int kk = 0; kk < 16; ++kk)
+            if (isp[kk])
+#pragma unroll
+              for (int e = 0; e < V; ++e) c[kk].x[e] += u[kk][0].x[e];
+        }
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk)
+          if (isp[kk]) c[kk].store(a.wvals + (int64_t)node[kk] * a.B + b);
+      } else {
+#pragma unroll
+      for (int kk = 0; kk < 16; ++kk) {
+        node[kk] = -1;
+        q0[kk] = q1[kk] = 0;
+        if (k0 + kk < gr.N) {
+          node[kk] = child_of(gr, a.chblocks, k0 + kk);
+          const uint32_t p = (uint32_t)(node[kk] - a.fp_start);
+          if (p < (uint32_t)a.fp_count) {
+            q0[kk] = a.fp_ptr[p];
+            q1[kk] = a.fp_ptr[p + 1];
+#pragma unroll
+            for (int e = 0; e < V; ++e) c[kk].x[e] = 0.0f;
+          } else {
+            c[kk].load(a.vals + (int64_t)node[kk] * a.B + b);
+          }
+        }
+      }
+      for (int q = 0; q < a.fp_maxdeg; ++q) {
+        Row<V> u[16];
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk)
+          if (q0[kk] + q < q1[kk]) u[kk].load(a.vals + (int64_t)a.fp_ids[q0[kk] + q] * a.B + b);
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk)
+          if (q0[kk] + q < q1[kk])
+#pragma unroll
+            for (int e = 0; e < V; ++e) c[kk].x[e] += u[kk].x[e];
+      }
+#pragma unroll
+      for (int kk = 0; kk < 16; ++kk)
+        if (q1[kk] > q0[kk]) c[kk].store(a.wvals + (int64_t)node[kk] * a.B + b);
+      }
+    }
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk)
       if (k0 + kk < gr.N)
@@ -376,16 +476,90 @@ __device__ __forceinline__ void split_store8(const float (&x)[8], int np, uint16
   }
 }
 
+// 8 consecutive samples [bs, bs + 8) of a row: two 16-byte accesses when the
+// chunk is whole and 16-byte aligned (vec), else one by one within the batch
+// (missing samples read as 0 and are not written).
+__device__ __forceinline__ void load8(const float* p, bool vec, int bs, int B, float (&x)[8]) {
+  if (vec) {
+    const float4 t0 = *(const float4*)p, t1 = *(const float4*)(p + 4);
+    x[0] = t0.x; x[1] = t0.y; x[2] = t0.z; x[3] = t0.w;
+    x[4] = t1.x; x[5] = t1.y; x[6] = t1.z; x[7] = t1.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = bs + e < B ? p[e] : 0.0f;
+  }
+}
+__device__ __forceinline__ void store8(float* p, bool vec, int bs, int B, const float (&x)[8]) {
+  if (vec) {
+    *(float4*)p = make_float4(x[0], x[1], x[2], x[3]);
+    *(float4*)(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (bs + e < B) p[e] = x[e];
+  }
+}
+
+// Product-layer backward for the distinct children listed in fp_rest (the ones
+// the packing tiles do not cover): f[c] (=|+=) its parents' flows, in parent
+// order, 4 samples per item; workgroup `wg` of `nwg`.
+__device__ __forceinline__ void prod_bwd_rest(const SumArgs& a, int wg, int nwg) {
+  const int QB = (a.B + 3) / 4;
+  const int64_t n = (int64_t)a.fp_nrest * QB;
+  const bool vec = (a.B & 3) == 0;
+  for (int64_t i = (int64_t)wg * blockDim.x + threadIdx.x; i < n; i += (int64_t)nwg * blockDim.x) {
+    const int ri = (int)(i / QB), b = (int)(i - (int64_t)ri * QB) * 4;
+    const int u = a.fp_rest[ri];
+    const int q0 = a.fp_single ? 0 : a.fp_ptr[u], q1 = a.fp_single ? 1 : a.fp_ptr[u + 1];
+    float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int q = q0; q < q1; ++q) {
+      const float* pf = a.wflows + (int64_t)(a.fp_single ? a.fp_rest_par[ri] : a.fp_ids[q]) * a.B + b;
+      if (vec) {
+        const float4 y = *(const float4*)pf;
+        s[0] += y.x; s[1] += y.y; s[2] += y.z; s[3] += y.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (b + e < a.B) s[e] += pf[e];
+      }
+    }
+    float* dst = a.wflows + (int64_t)(a.fp_single ? u : a.fp_uchild[u]) * a.B + b;
+    if (vec) {
+      if (!a.fp_store) {
+        const float4 o = *(const float4*)dst;
+        s[0] = o.x + s[0]; s[1] = o.y + s[1]; s[2] = o.z + s[2]; s[3] = o.w + s[3];
+      }
+      *(float4*)dst = make_float4(s[0], s[1], s[2], s[3]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (b + e < a.B) dst[e] = a.fp_store ? s[e] : dst[e] + s[e];
+    }
+  }
+}
+
 // Packing of a 64-row x 64-sample tile of an operand computed on the fly
 // (KIND 0: e = exp(v[child] - m[b]); KIND 1: g = f / S) into
 //   the node-major panel ("direct": rows drow0 + r, K = sample), 8 samples per
 //   16-byte store, for every group in the sharing chain (exp only), and
 //   the batch-major panel ("trans": rows = samples, K = tk0 + r), through an
 //   LDS transpose, 8 rows per 16-byte store.
-template <int KIND>
-__global__ void k_pack(SumArgs a) {
+//
+// With PROD (KIND 1 only) the backward of the product layer that follows the
+// sum layer runs here too: an output row whose node is a child of that layer
+// first gathers its parents' flows (parent order, then added to the old flow
+// unless the layer stores), stores the flow and packs f / S; workgroups past
+// the packing tiles push the flows of the product layer's other children.
+template <int KIND, bool PROD>
+__global__ __launch_bounds__(256) void k_pack(SumArgs a) {
   __shared__ float tile[64][65];
   const int t = blockIdx.x;
+  if constexpr (PROD) {
+    if (t >= a.fp_tiles) {
+      prod_bwd_rest(a, t - a.fp_tiles, (int)gridDim.x - a.fp_tiles);
+      return;
+    }
+  }
   const int rt = t / a.btiles, bt = t - rt * a.btiles;
   const int g = KIND == 0 ? last_le(a.groups, a.ngroups, rt, [](const GroupRec& r) { return r.pk_start; })
                           : last_le(a.groups, a.ngroups, rt, [](const GroupRec& r) { return r.pg_start; });
@@ -414,7 +588,32 @@ __global__ void k_pack(SumArgs a) {
         p1 = a.ssum + (gr.s_row + k) * a.B + bs;
       }
       float u0[8], u1[8];
-      if (vec) {
+      const int up = PROD ? a.fp_up[rt * 64 + r] : -1;
+      if (PROD && up >= 0) {
+        // this output's flow: its parents in the product layer, in order
+        float f[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = 0.0f;
+        const int q0 = a.fp_single ? 0 : a.fp_ptr[up], q1 = a.fp_single ? 1 : a.fp_ptr[up + 1];
+        for (int q = q0; q < q1; ++q) {
+          const float* pf = a.wflows + (int64_t)(a.fp_single ? up : a.fp_ids[q]) * a.B + bs;
+          float y[8];
+          load8(pf, vec, bs, a.B, y);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) f[e] += y[e];
+        }
+        float* pw = a.wflows + (int64_t)(gr.out_start + k) * a.B + bs;
+        if (!a.fp_store) {
+          float o[8];
+          load8(pw, vec, bs, a.B, o);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) f[e] = o[e] + f[e];
+        }
+        store8(pw, vec, bs, a.B, f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) u0[e] = f[e];
+        load8(p1, vec, bs, a.B, u1);
+      } else if (vec) {
         Row<4> t;
         t.load(p0); for (int e = 0; e < 4; ++e) u0[e] = t.x[e];
         t.load(p0 + 4); for (int e = 0; e < 4; ++e) u0[4 + e] = t.x[e];
@@ -587,18 +786,38 @@ void launch_input_bwd(const InputArgs& a, hipStream_t s) {
 }
 void launch_prod_fwd(const ProdArgs& a, hipStream_t s) { PC_LAUNCH_V(k_prod_fwd, a.num_nodes, a, s); }
 void launch_prod_bwd(const ProdArgs& a, hipStream_t s) { PC_LAUNCH_V(k_prod_bwd, a.nuniq, a, s); }
+// Column maxima (and the preceding product layer when a.fp_on): 4 samples
+// per lane when the batch is a multiple of 4, else 2 (8-byte accesses) or 1.
+template <bool PROD>
+static void launch_colmax_v(const SumArgs& a, int row_tiles, hipStream_t s) {
+  const int g4 = row_tiles * ((a.B + 255) / 256), g2 = row_tiles * ((a.B + 127) / 128);
+  if (a.B % 4 == 0)
+    hipLaunchKernelGGL((k_colmax<4, PROD>), dim3(g4), dim3(256), 0, s, a);
+  else if (a.B % 2 == 0)
+    hipLaunchKernelGGL((k_colmax<2, PROD>), dim3(g2), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_colmax<1, PROD>), dim3(row_tiles * ((a.B + 63) / 64)), dim3(256), 0, s, a);
+}
 void launch_colmax(const SumArgs& a, int row_tiles, hipStream_t s) {
   if (row_tiles <= 0) return;
-  if (a.B % 4 == 0)
-    hipLaunchKernelGGL(k_colmax<4>, dim3(row_tiles * ((a.B + 255) / 256)), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(k_colmax<1>, dim3(row_tiles * ((a.B + 63) / 64)), dim3(256), 0, s, a);
+  if (a.fp_on) launch_colmax_v<true>(a, row_tiles, s);
+  else launch_colmax_v<false>(a, row_tiles, s);
 }
 void launch_exp_pack(const SumArgs& a, int row_tiles, hipStream_t s) {
-  if (row_tiles > 0) hipLaunchKernelGGL(k_pack<0>, dim3(row_tiles * a.btiles), dim3(256), 0, s, a);
+  if (row_tiles > 0) hipLaunchKernelGGL((k_pack<0, false>), dim3(row_tiles * a.btiles), dim3(256), 0, s, a);
 }
+// Scaled flows; with a.fp_on also the following product layer's backward, its
+// other children on up to 1024 extra workgroups.
 void launch_g_pack(const SumArgs& a, int row_tiles, hipStream_t s) {
-  if (row_tiles > 0) hipLaunchKernelGGL(k_pack<1>, dim3(row_tiles * a.btiles), dim3(256), 0, s, a);
+  if (row_tiles <= 0) return;
+  if (!a.fp_on) {
+    hipLaunchKernelGGL((k_pack<1, false>), dim3(row_tiles * a.btiles), dim3(256), 0, s, a);
+    return;
+  }
+  SumArgs b = a;
+  b.fp_tiles = row_tiles * a.btiles;
+  const int rest = b.fp_nrest > 0 ? grid_for((int64_t)b.fp_nrest * ((a.B + 3) / 4), 256, 1024) : 0;
+  hipLaunchKernelGGL((k_pack<1, true>), dim3(b.fp_tiles + rest), dim3(256), 0, s, b);
 }
 void launch_theta_pack(const ThetaArgs& a, int tiles, hipStream_t s) {
   if (tiles > 0) hipLaunchKernelGGL(k_theta_pack, dim3(tiles), dim3(256), 0, s, a);

@@ -101,6 +101,7 @@ __device__ __forceinline__ void lds_load16(const void* sbase, uint32_t voff, uin
 // LDS operation outstanding (expcnt left at its maximum).
 template <int vm>
 struct WaitVmLgkm {
+  static_assert(vm >= 0 && vm <= 63, "vmcnt is a 6-bit counter");
   static constexpr int imm = (vm & 15) | ((vm >> 4) << 14) | (7 << 4);
 };
 
@@ -468,42 +469,59 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
     __syncthreads();
     if (!last_flag) return;
     const float* base = a.partials + (int64_t)tile * S * (NREG * 256);
-    // in chunks of up to 64 registers: every load of a chunk in flight at once
-    constexpr int CH = NREG < 64 ? NREG : 64;
+    // in chunks of CH registers over all SM >= S splits (about 128 values
+    // per lane): every load of a chunk in flight at once, then the splits
+    // added in order
+    auto reduce = [&](auto ch_c, auto sm_c) {
+      constexpr int CH = decltype(ch_c)::value < NREG ? decltype(ch_c)::value : NREG;
+      constexpr int SM = decltype(sm_c)::value;
 #pragma unroll
-    for (int c0 = 0; c0 < NREG; c0 += CH) {
-      float sum[CH];
+      for (int c0 = 0; c0 < NREG; c0 += CH) {
+        float t[SM][CH];
 #pragma unroll
-      for (int x = 0; x < CH; ++x)
-        sum[x] = __hip_atomic_load(base + (c0 + x) * 256 + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      for (int q = 1; q < S; ++q) {
-        float t[CH];
+        for (int q = 0; q < SM; ++q)
+          if (q < S)
 #pragma unroll
-        for (int x = 0; x < CH; ++x)
-          t[x] = __hip_atomic_load(base + (int64_t)q * (NREG * 256) + (c0 + x) * 256 + tid, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+            for (int x = 0; x < CH; ++x)
+              t[q][x] = __hip_atomic_load(base + (int64_t)q * (NREG * 256) + (c0 + x) * 256 + tid,
+                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-        for (int x = 0; x < CH; ++x) sum[x] += t[x];
+        for (int q = 1; q < SM; ++q)
+          if (q < S)
+#pragma unroll
+            for (int x = 0; x < CH; ++x) t[0][x] += t[q][x];
+#pragma unroll
+        for (int x = 0; x < CH; ++x) {
+          const int reg = c0 + x, blk = reg / 16;
+          acc[blk / FN][blk % FN][reg % 16] = t[0][x];
+        }
       }
-#pragma unroll
-      for (int x = 0; x < CH; ++x) {
-        const int reg = c0 + x, blk = reg / 16;
-        acc[blk / FN][blk % FN][reg % 16] = sum[x];
-      }
-    }
+    };
+    if (S <= 2) reduce(std::integral_constant<int, 64>(), std::integral_constant<int, 2>());
+    else if (S <= 4) reduce(std::integral_constant<int, 32>(), std::integral_constant<int, 4>());
+    else reduce(std::integral_constant<int, 16>(), std::integral_constant<int, 8>());
     if (tid == 0) __hip_atomic_store(a.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // ---- epilogue ------------------------------------------------------------
   // accumulator register r of lane l holds row (r/4)*8 + (l/32)*4 + r%4 and
-  // column l%32 of its 32 x 32 block.  Per-column shifts and per-row child
-  // nodes are staged in LDS (the ring is free once every load has landed and
-  // every wave is past its last fragment read).
+  // column l%32 of its 32 x 32 block.  The tile goes through LDS (free once
+  // every load has landed and every wave is past its last fragment read) in
+  // passes of WM*32 rows, one row block of every wave row at a time, so that
+  // the loads and stores of node values, flows and parameters are 16-byte
+  // runs along a row; per-column shifts and per-row child nodes are staged
+  // beside it.
+  constexpr int LDT = NT + 8;                  // row pitch: the two half-waves' rows 4 apart hit other banks
+  constexpr int PR = WM * 32;                  // rows per pass
+  constexpr int NCH = PR * NT / 4 / 256;       // 4-column chunks per thread per pass
+  static_assert(PR * NT % 1024 == 0, "whole chunks per thread");
+  static_assert((PR * LDT + NT + MT) * 4 <= NS * R::STAGE * 2, "epilogue tile fits the ring");
   const int B = a.B;
-  float* sh_col = (float*)ring;                // [NT]
-  int* ch_row = (int*)ring + NT;               // [MT]
+  float* tl = (float*)ring;                    // [PR][LDT]
+  float* sh_col = tl + PR * LDT;               // [NT]
+  int* ch_row = (int*)(sh_col + NT);           // [MT]
+  __syncthreads();
   if (EPI == EPI_FWD || EPI == EPI_ELEM) {
-    __syncthreads();
     for (int t = tid; t < NT; t += 256) {
       const int col = n0 + t;
       sh_col[t] = col < B ? key_to_shift(a.mkeys[(int64_t)gr.m_row * B + col]) : 0.0f;
@@ -513,96 +531,115 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
         const int row = m0 + t;
         ch_row[t] = row < gr.N ? a.chblocks[gr.blk_off + row / gr.cbs] + row % gr.cbs : -1;
       }
-    __syncthreads();
   }
-  const int lr0 = wm0 + (lane >> 5) * 4, lc = wn0 + (lane & 31);
-  if (EPI == EPI_FWD) {
-    float* vals = a.vals + (int64_t)gr.out_start * B;
-    float* ssum = a.ssum + gr.s_row * B;
+  const int wr = wave / WN;
+  const bool to_scratch = EPI == EPI_ELEM && gr.scratch_row >= 0;
+  const bool add = EPI == EPI_ELEM && !to_scratch && !a.store;
+  float* dst_base = to_scratch ? a.scratch + (int64_t)gr.scratch_row * B : a.flows;
+  const int ncol = EPI == EPI_PARAM ? bl.N : B;
+  const bool vec = EPI == EPI_PARAM ? ((bl.param_offset | (int64_t)bl.N) & 3) == 0 : (B & 3) == 0;
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int cl = lc + j * 32, col = n0 + cl;
-      const float sh = sh_col[cl];
+  for (int i = 0; i < FM; ++i) {
+    // write row block i of every wave into the pass tile
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = m0 + lr0 + i * 32 + (r >> 2) * 8 + (r & 3);
-          const float v = acc[i][j][r];
-          if (row < gr.M && col < B) {
-            vals[(int64_t)row * B + col] = sh + logf(v);
-            ssum[(int64_t)row * B + col] = v;
+      for (int r = 0; r < 16; ++r) {
+        const int lr = wr * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        tl[lr * LDT + wn0 + j * 32 + (lane & 31)] = acc[i][j][r];
+      }
+    __syncthreads();
+    // chunk q = tid + 256 c: pass row q / (NT/4), columns 4 (q % (NT/4)) + 0..3
+    int trow[NCH], c4[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int q = tid + 256 * c, lr = q / (NT / 4);
+      trow[c] = (lr >> 5) * WTM + i * 32 + (lr & 31);
+      c4[c] = (q % (NT / 4)) * 4;
+    }
+    // every load of the pass in flight before the first store
+    float x[NCH][4], old[NCH][4];
+    int64_t at[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int row = m0 + trow[c], col = n0 + c4[c];
+      bool ok;
+      if (EPI == EPI_FWD) {
+        ok = row < gr.M;
+        at[c] = (int64_t)row * B + col;
+      } else if (EPI == EPI_ELEM) {
+        const int child = ch_row[trow[c]];
+        ok = child >= 0;
+        at[c] = to_scratch ? (int64_t)row * B + col : (int64_t)child * B + col;
+        const float* src = a.vals + (int64_t)(ok ? child : 0) * B + col;
+        if (ok && vec && col + 3 < B) {
+          const float4 t = *(const float4*)src;
+          x[c][0] = t.x; x[c][1] = t.y; x[c][2] = t.z; x[c][3] = t.w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[c][e] = (ok && col + e < B) ? src[e] : 0.0f;
+        }
+      } else {
+        ok = row < bl.M;
+        at[c] = (int64_t)row * bl.N + col;
+        const float* src = a.params + bl.param_offset + (ok ? at[c] : 0);
+        if (ok && vec && col + 3 < bl.N) {
+          const float4 t = *(const float4*)src;
+          x[c][0] = t.x; x[c][1] = t.y; x[c][2] = t.z; x[c][3] = t.w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[c][e] = (ok && col + e < bl.N) ? src[e] : 0.0f;
+        }
+      }
+      if (!ok) at[c] = -1;
+      const bool rd_old = EPI == EPI_PARAM || add;
+      if (rd_old) {
+        const float* src = (EPI == EPI_PARAM ? a.pflows + bl.param_offset : dst_base) + (ok ? at[c] : 0);
+        if (ok && vec && col + 3 < ncol) {
+          const float4 t = *(const float4*)src;
+          old[c][0] = t.x; old[c][1] = t.y; old[c][2] = t.z; old[c][3] = t.w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) old[c][e] = (ok && col + e < ncol) ? src[e] : 0.0f;
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      if (at[c] < 0) continue;
+      const int col = n0 + c4[c];
+      const float* pv = tl + (trow[c] - (trow[c] / WTM) * WTM - i * 32 + (trow[c] / WTM) * 32) * LDT + c4[c];
+      const float4 pt = *(const float4*)pv;
+      const float acc4[4] = {pt.x, pt.y, pt.z, pt.w};
+      float o[4], o2[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (EPI == EPI_FWD) {
+          o[e] = sh_col[c4[c] + e] + logf(acc4[e]);
+          o2[e] = acc4[e];
+        } else if (EPI == EPI_ELEM) {
+          const float ex = expf(x[c][e] - sh_col[c4[c] + e]);
+          const float cc = (ex == 0.0f) ? 0.0f : ex * acc4[e];
+          o[e] = add ? old[c][e] + cc : cc;
+        } else {
+          o[e] = old[c][e] + x[c][e] * acc4[e];
+        }
+      }
+      float* d0 = EPI == EPI_FWD ? a.vals + (int64_t)gr.out_start * B + at[c]
+                : EPI == EPI_ELEM ? dst_base + at[c] : a.pflows + bl.param_offset + at[c];
+      if (vec && col + 3 < ncol) {
+        *(float4*)d0 = make_float4(o[0], o[1], o[2], o[3]);
+        if (EPI == EPI_FWD) *(float4*)(a.ssum + gr.s_row * B + at[c]) = make_float4(o2[0], o2[1], o2[2], o2[3]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (col + e < ncol) {
+            d0[e] = o[e];
+            if (EPI == EPI_FWD) a.ssum[gr.s_row * B + at[c] + e] = o2[e];
           }
-        }
-    }
-  } else if (EPI == EPI_ELEM) {
-    // batches of up to 4 blocks: every load of a batch in flight before any store
-    constexpr int NB = FM * FN, BT = NB < 4 ? NB : 4;
-    const bool to_scratch = gr.scratch_row >= 0;
-    const bool add = !to_scratch && !a.store;
-    float* dst_base = to_scratch ? a.scratch + (int64_t)gr.scratch_row * B : a.flows;
-#pragma unroll
-    for (int b0 = 0; b0 < NB; b0 += BT) {
-      float x[BT][16], old[BT][16];
-      int64_t at[BT][16];
-#pragma unroll
-      for (int bb = 0; bb < BT; ++bb) {
-        const int i = (b0 + bb) / FN, j = (b0 + bb) % FN;
-        const int col = n0 + lc + j * 32;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int rl = lr0 + i * 32 + (r >> 2) * 8 + (r & 3);
-          const int child = ch_row[rl];
-          const bool ok = child >= 0 && col < B;
-          at[bb][r] = ok ? (to_scratch ? (int64_t)(m0 + rl) * B + col : (int64_t)child * B + col) : -1;
-          x[bb][r] = ok ? a.vals[(int64_t)child * B + col] : 0.0f;
-          old[bb][r] = (ok && add) ? dst_base[at[bb][r]] : 0.0f;
-        }
-      }
-#pragma unroll
-      for (int bb = 0; bb < BT; ++bb) {
-        const int i = (b0 + bb) / FN, j = (b0 + bb) % FN;
-        const float sh = sh_col[lc + j * 32];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if (at[bb][r] < 0) continue;
-          const float e = expf(x[bb][r] - sh);
-          const float c = (e == 0.0f) ? 0.0f : e * acc[i][j][r];
-          dst_base[at[bb][r]] = add ? old[bb][r] + c : c;
-        }
       }
     }
-  } else {
-    constexpr int NB = FM * FN, BT = NB < 4 ? NB : (NREG >= 256 ? 1 : 4);
-    const float* params = a.params + bl.param_offset;
-    float* pflows = a.pflows + bl.param_offset;
-#pragma unroll
-    for (int b0 = 0; b0 < NB; b0 += BT) {
-      float th[BT][16], old[BT][16];
-#pragma unroll
-      for (int bb = 0; bb < BT; ++bb) {
-        const int i = (b0 + bb) / FN, j = (b0 + bb) % FN;
-        const int col = n0 + lc + j * 32;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = m0 + lr0 + i * 32 + (r >> 2) * 8 + (r & 3);
-          const bool ok = row < bl.M && col < bl.N;
-          const int64_t idx = (int64_t)row * bl.N + col;
-          th[bb][r] = ok ? params[idx] : 0.0f;
-          old[bb][r] = ok ? pflows[idx] : 0.0f;
-        }
-      }
-#pragma unroll
-      for (int bb = 0; bb < BT; ++bb) {
-        const int i = (b0 + bb) / FN, j = (b0 + bb) % FN;
-        const int col = n0 + lc + j * 32;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = m0 + lr0 + i * 32 + (r >> 2) * 8 + (r & 3);
-          if (row < bl.M && col < bl.N) pflows[(int64_t)row * bl.N + col] = old[bb][r] + th[bb][r] * acc[i][j][r];
-        }
-      }
-    }
+    if (i + 1 < FM) __syncthreads();           // the pass tile is rewritten next
   }
 }
 
@@ -626,6 +663,7 @@ static void launch_tile(int tile, int grid, const GemmArgs& a, hipStream_t s) {
     launch_shape<EPI, PA, PB, 128, 128, 2>(grid, a, s);
   } else {
     if (tile == TILE_256x128) launch_shape<EPI, PA, PB, 256, 128, 2>(grid, a, s);
+    else if (tile == TILE_128x256) launch_shape<EPI, PA, PB, 128, 256, 2>(grid, a, s);
     else launch_shape<EPI, PA, PB, 128, 128, 2>(grid, a, s);
   }
 }

@@ -122,6 +122,9 @@ void upload_tables(Handle* h, int device) {
     sp.d_red_child = upload(sp.red_child);
     sp.d_red_ptr = upload(sp.red_ptr);
     sp.d_red_src = upload(sp.red_src);
+    sp.d_up_idx = upload(sp.up_idx);
+    sp.d_up_rest = upload(sp.up_rest);
+    sp.d_up_rest_par = upload(sp.up_rest_par);
   }
   h->d_blocks = upload(h->blocks);
   h->d_rowsegs = upload(h->rowsegs);
@@ -153,6 +156,9 @@ void free_tables(Handle* h) {
     release(sp.d_red_child);
     release(sp.d_red_ptr);
     release(sp.d_red_src);
+    release(sp.d_up_idx);
+    release(sp.d_up_rest);
+    release(sp.d_up_rest_par);
   }
   release(h->d_blocks);
   release(h->d_rowsegs);
@@ -428,6 +434,9 @@ ProdArgs prod_args(const Call& c, const ProductPlan& pp) {
   a.uchild = pp.d_uchild;
   a.pptr = pp.d_pptr;
   a.parents = pp.d_parents;
+  a.affine = pp.affine ? 1 : 0;
+  a.deg = pp.max_deg;
+  for (int q = 0; q < 8; ++q) a.abase[q] = pp.abase[q];
   return a;
 }
 
@@ -514,14 +523,17 @@ int pc_set_option(pc_handle hh, int option, int value) {
   try {
     Handle* h = checked(hh);
     if (option == PC_OPT_LAYER_TILE) {
-      if (value < 0 || value > 2) fail(PC_ERR_INVALID_ARG, "layer tile must be 0, 1 or 2");
-      h->opt_layer_tile = value == 1 ? TILE_128x128 : value == 2 ? TILE_256x128 : TILE_AUTO;
+      if (value < 0 || value > 3) fail(PC_ERR_INVALID_ARG, "layer tile must be 0, 1, 2 or 3");
+      h->opt_layer_tile = value == 1 ? TILE_128x128 : value == 2 ? TILE_256x128 : value == 3 ? TILE_128x256 : TILE_AUTO;
     } else if (option == PC_OPT_PARAM_TILE) {
       if (value < 0 || value > 2) fail(PC_ERR_INVALID_ARG, "parameter tile must be 0, 1 or 2");
       h->opt_param_tile = value == 2 ? TILE_256x256 : value == 1 ? TILE_128x128 : TILE_AUTO;
     } else if (option == PC_OPT_SPLIT_MAX) {
       if (value != 1 && value != 2 && value != 4 && value != 8) fail(PC_ERR_INVALID_ARG, "split must be 1, 2, 4 or 8");
       h->opt_split_max = value;
+    } else if (option == PC_OPT_FUSE) {
+      if (value != 0 && value != 1) fail(PC_ERR_INVALID_ARG, "fuse must be 0 or 1");
+      h->opt_fuse = value;
     } else {
       fail(PC_ERR_INVALID_ARG, "unknown option");
     }
@@ -619,6 +631,7 @@ int pc_forward(pc_handle hh, int batch, const int32_t* tokens, const float* para
         Timed t(h, KK_INFWD, c.s);
         launch_input_fwd(a, c.s);
       } else if (r.kind == PC_LAYER_PRODUCT) {
+        if (h->opt_fuse && h->prods[r.idx].fwd_fused) continue;   // evaluated by the next layer's column maxima
         ProdArgs a = prod_args(c, h->prods[r.idx]);
         a.vals = node_vals;
         Timed t(h, KK_PRODFWD, c.s);
@@ -634,10 +647,23 @@ int pc_forward(pc_handle hh, int batch, const int32_t* tokens, const float* para
         a.trans_plane = v.ebt_plane;
         a.direct_rows = h->earena_rows;
         a.np_trans = p.pl[GK_FWD][1];
+        if (h->opt_fuse && sp.fwd_prod >= 0) {
+          const ProductPlan& pp = h->prods[sp.fwd_prod];
+          a.fp_on = 1;
+          a.fp_start = pp.node_start;
+          a.fp_count = pp.num_nodes;
+          a.fp_maxdeg = pp.max_deg;
+          a.fp_ptr = pp.d_ch_ptr;
+          a.fp_ids = pp.d_ch_ids;
+          a.fp_affine = pp.affine ? 1 : 0;
+          for (int q = 0; q < 8; ++q) a.fp_abase[q] = pp.abase[q];
+          a.wvals = node_vals;
+        }
         {
           Timed t(h, KK_COLMAX, c.s);
           launch_colmax(a, sp.pktiles, c.s);
         }
+        a.fp_on = 0;
         if (sp.lowrank) {
           for (int gi = 0; gi < (int)sp.groups.size(); ++gi) {
             LRArgs la = lr_args(c, sp, gi, lowrank, params, node_vals, nullptr);
@@ -761,6 +787,20 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
         a.trans_plane = v.gbt_plane;
         a.direct_rows = h->garena_rows;
         a.np_trans = p.pl[GK_ELEM][1];
+        if (h->opt_fuse && sp.bwd_prod >= 0) {
+          const ProductPlan& pp = h->prods[sp.bwd_prod];
+          a.fp_on = 1;
+          a.fp_store = pp.store ? 1 : 0;
+          a.fp_nrest = (int)sp.up_rest.size();
+          a.fp_ptr = pp.d_pptr;
+          a.fp_ids = pp.d_parents;
+          a.fp_uchild = pp.d_uchild;
+          a.fp_up = sp.d_up_idx;
+          a.fp_rest = sp.d_up_rest;
+          a.fp_rest_par = sp.d_up_rest_par;
+          a.fp_single = pp.single_parent ? 1 : 0;
+          a.wflows = node_flows;
+        }
         {
           Timed t(h, KK_GPACK, c.s);
           launch_g_pack(a, sp.pgtiles, c.s);
@@ -799,6 +839,7 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
           launch_elem_reduce(ra, c.s);
         }
       } else if (r.kind == PC_LAYER_PRODUCT) {
+        if (h->opt_fuse && h->prods[r.idx].bwd_fused) continue;   // runs in the previous layer's scaled-flow packing
         ProdArgs a = prod_args(c, h->prods[r.idx]);
         a.flows = node_flows;
         Timed t(h, KK_PRODBWD, c.s);

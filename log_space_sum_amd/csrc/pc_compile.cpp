@@ -131,6 +131,7 @@ Handle* compile_layout(const pc_circuit_desc* d) {
       pp.ch_ptr.assign(ly.ch_ptr, ly.ch_ptr + ly.num_nodes + 1);
       pp.ch_ids.assign(ly.ch_ids, ly.ch_ids + ly.ch_ptr[ly.num_nodes]);
       for (int32_t c : pp.ch_ids) use(li, c);
+      for (int32_t i = 0; i < ly.num_nodes; ++i) pp.max_deg = std::max(pp.max_deg, pp.ch_ptr[i + 1] - pp.ch_ptr[i]);
       define(li, ly.node_start, ly.num_nodes);
       // parent CSR over distinct children
       std::vector<std::pair<int32_t, int32_t>> cp;
@@ -147,6 +148,19 @@ Handle* compile_layout(const pc_circuit_desc* d) {
         pp.parents.push_back(cp[k].second);
       }
       pp.pptr.push_back((int32_t)cp.size());
+      pp.single_parent = pp.parents.size() == pp.uchild.size();
+      {   // affine: uniform degree, child q of node i at abase[q] + i, disjoint ranges
+        const int32_t D = pp.ch_ptr[1] - pp.ch_ptr[0];
+        bool af = D <= 8 && pp.single_parent;
+        for (int32_t i = 0; af && i < ly.num_nodes; ++i) {
+          af = pp.ch_ptr[i + 1] - pp.ch_ptr[i] == D;
+          for (int32_t q = 0; af && q < D; ++q) af = pp.ch_ids[(int64_t)i * D + q] == pp.ch_ids[q] + i;
+        }
+        if (af) {
+          pp.affine = true;
+          for (int32_t q = 0; q < D; ++q) pp.abase[q] = pp.ch_ids[q];
+        }
+      }
       ref.idx = (int)h->prods.size();
       h->prods.push_back(std::move(pp));
     } else if (ly.kind == PC_LAYER_SUM) {
@@ -479,6 +493,62 @@ Handle* compile_layout(const pc_circuit_desc* d) {
     h->seed_ranges.push_back(FillRange{s0, n, (s0 == h->root) ? 1.0f : 0.0f, 0});
     h->max_seed_count = std::max<int64_t>(h->max_seed_count, n);
     k = q + 1;
+  }
+
+  // ---- pass 4: product layers computed inside an adjacent sum layer's kernels --
+  // Forward: a product layer directly followed by a sum layer whose column-max
+  // tiles cover each of its nodes exactly once is evaluated by those tiles
+  // (each tile row sums its product node's children, stores it and takes the
+  // maximum), saving a launch and a re-read.  Backward: a product layer
+  // directly after a plain sum layer runs inside that layer's scaled-flow
+  // packing, which comes next in reverse order; the packing rows of the sum
+  // layer's outputs gather their parents' flows, the other distinct children
+  // of the product layer get extra workgroups.  Both keep every sum in the
+  // product kernels' order, so the results are the same bits.
+  for (size_t li = 0; li + 1 < h->layers.size(); ++li) {
+    const LayerRef a = h->layers[li], b = h->layers[li + 1];
+    if (a.kind == PC_LAYER_PRODUCT && b.kind == PC_LAYER_SUM) {
+      ProductPlan& pp = h->prods[a.idx];
+      SumPlan& sp = h->sums[b.idx];
+      std::vector<int32_t> cnt(pp.num_nodes, 0);
+      for (size_t g = 0; g < sp.groups.size(); ++g) {
+        const GroupRec& r = sp.groups[g];
+        if (r.share_src != (int32_t)g) continue;   // sharing groups have no column-max tiles
+        for (int k = 0; k < r.nblk; ++k)
+          for (int64_t c = sp.blocks[r.blk_off + k]; c < sp.blocks[r.blk_off + k] + r.cbs; ++c) {
+            const int64_t q = c - pp.node_start;
+            if (q >= 0 && q < pp.num_nodes) ++cnt[q];
+          }
+      }
+      bool once = true;
+      for (int32_t x : cnt) once = once && x == 1;
+      if (once) {
+        pp.fwd_fused = true;
+        sp.fwd_prod = a.idx;
+      }
+    }
+    if (a.kind == PC_LAYER_SUM && b.kind == PC_LAYER_PRODUCT && !h->sums[a.idx].lowrank) {
+      SumPlan& sp = h->sums[a.idx];
+      ProductPlan& pp = h->prods[b.idx];
+      sp.up_idx.assign((size_t)sp.pgtiles * 64, -1);
+      std::vector<char> is_out(pp.uchild.size(), 0);
+      for (const GroupRec& r : sp.groups)
+        for (int32_t k = 0; k < r.M; ++k) {
+          const int32_t n = r.out_start + k;
+          auto it = std::lower_bound(pp.uchild.begin(), pp.uchild.end(), n);
+          if (it == pp.uchild.end() || *it != n) continue;
+          const int32_t u = (int32_t)(it - pp.uchild.begin());
+          sp.up_idx[(size_t)r.pg_start * 64 + k] = pp.single_parent ? pp.parents[pp.pptr[u]] : u;
+          is_out[u] = 1;
+        }
+      for (size_t u = 0; u < pp.uchild.size(); ++u)
+        if (!is_out[u]) {
+          sp.up_rest.push_back(pp.single_parent ? pp.uchild[u] : (int32_t)u);
+          sp.up_rest_par.push_back(pp.single_parent ? pp.parents[pp.pptr[u]] : -1);
+        }
+      pp.bwd_fused = true;
+      sp.bwd_prod = b.idx;
+    }
   }
   return h;
 }

@@ -24,6 +24,8 @@ struct InputArgs {
 
 struct ProdArgs {
   int32_t B, node_start, num_nodes, nuniq, store;
+  int32_t affine, deg;          // affine layer: child q of node i is abase[q] + i
+  int32_t abase[8];
   const int32_t* ch_ptr;
   const int32_t* ch_ids;
   const int32_t* uchild;
@@ -56,6 +58,28 @@ struct SumArgs {
   const int32_t* red_src;
   const float* scratch;
   float* out_flows;
+  // A product layer computed in the same launch.  Forward (column maxima):
+  // children of the sum layer inside [fp_start, fp_start + fp_count) are that
+  // layer's nodes, summed from their own children (fp_ptr / fp_ids = its
+  // child CSR, at most fp_maxdeg each) and written to wvals.  Backward
+  // (scaled flows): output row r of the packing tiles takes its flow from the
+  // product layer's parents when fp_up[r] >= 0 (the single parent node when
+  // fp_single, else a distinct-child index into the parent CSR fp_ptr /
+  // fp_ids over fp_uchild; stored to wflows, added to the old flow unless
+  // fp_store), and the workgroups past the fp_tiles packing tiles handle the
+  // fp_nrest other distinct children fp_rest (child node with its parent
+  // fp_rest_par when fp_single, else distinct-child indices).  fp_affine:
+  // the product layer is affine (child q of node i at fp_abase[q] + i).
+  int32_t fp_on, fp_start, fp_count, fp_maxdeg, fp_store, fp_nrest, fp_tiles, fp_affine, fp_single;
+  int32_t fp_abase[8];
+  const int32_t* fp_ptr;
+  const int32_t* fp_ids;
+  const int32_t* fp_uchild;
+  const int32_t* fp_up;
+  const int32_t* fp_rest;
+  const int32_t* fp_rest_par;
+  float* wvals;
+  float* wflows;
 };
 
 struct ThetaArgs {

@@ -41,6 +41,15 @@ struct ProductPlan {
   std::vector<int32_t> ch_ptr, ch_ids;
   std::vector<int32_t> uchild, pptr, parents;  // distinct children, their parents (CSR)
   bool store = false;                          // flows: first writer of every child
+  int32_t max_deg = 0;                         // most children of one node
+  // Affine layer: every node has max_deg <= 8 children, child q of node i is
+  // abase[q] + i, and the max_deg child ranges are disjoint (so each child
+  // has exactly one parent); addresses then need no index loads.
+  bool affine = false;
+  int32_t abase[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  bool single_parent = false;                  // every distinct child has exactly one parent here
+  bool fwd_fused = false;                      // forward computed by the next sum layer's column-max kernel
+  bool bwd_fused = false;                      // backward computed by the previous sum layer's flow packing
   int32_t* d_ch_ptr = nullptr;
   int32_t* d_ch_ids = nullptr;
   int32_t* d_uchild = nullptr;
@@ -63,6 +72,20 @@ struct SumPlan {
   int32_t max_npk = 0, max_mpk = 0;            // widest contraction of the forward / element flows
   std::vector<int32_t> red_child, red_ptr, red_src;   // overlap reduction CSR
   std::vector<int64_t> lr_row;                 // LowRank: first row of each group's Z/S/U/W records
+  // Adjacent product layers computed inside this layer's memory-bound kernels:
+  // the one before it in the column-max kernel (forward), the one after it in
+  // the scaled-flow packing (backward).
+  int fwd_prod = -1, bwd_prod = -1;
+  // Per 64-row output tile row: the parent node in bwd_prod when that layer
+  // gives each child a single parent, else the distinct-child index; -1 when
+  // the output is not a child of bwd_prod.
+  std::vector<int32_t> up_idx;
+  // bwd_prod's distinct children that are not outputs of this layer: child
+  // node and its single parent, or the distinct-child index (and -1).
+  std::vector<int32_t> up_rest, up_rest_par;
+  int32_t* d_up_idx = nullptr;
+  int32_t* d_up_rest = nullptr;
+  int32_t* d_up_rest_par = nullptr;
   GroupRec* d_groups = nullptr;
   int32_t* d_blocks = nullptr;
   int32_t* d_red_child = nullptr;
@@ -80,7 +103,7 @@ struct Handle {
   int mode = PC_PREC_AUTO;
   // planes[mode][gemm kind][0: first operand, 1: second operand]
   int planes[2][3][2] = {{{2, 1}, {2, 1}, {2, 1}}, {{3, 3}, {3, 3}, {3, 3}}};
-  int opt_layer_tile = 0, opt_param_tile = 0, opt_split_max = 8;   // pc_set_option
+  int opt_layer_tile = 0, opt_param_tile = 0, opt_split_max = 8, opt_fuse = 1;   // pc_set_option
   int32_t num_nodes = 0, num_vars = 0, root = -1, lowrank_rank = 0;
   int64_t num_params = 0;
   std::vector<LayerRef> layers;

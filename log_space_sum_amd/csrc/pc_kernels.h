@@ -36,7 +36,7 @@ struct GemmArgs {
 };
 
 // Output tile shapes of the product kernel (M x N per workgroup).
-enum GemmTile { TILE_AUTO = 0, TILE_128x128 = 1, TILE_256x128 = 2, TILE_256x256 = 3 };
+enum GemmTile { TILE_AUTO = 0, TILE_128x128 = 1, TILE_256x128 = 2, TILE_256x256 = 3, TILE_128x256 = 4 };
 
 struct GemmShape {
   int tile;      // GemmTile
@@ -45,12 +45,14 @@ struct GemmShape {
   int tiles;     // output tiles of the launch
 };
 
-// K slice width: 64 when a stage of that width holds at most 48 KB, else 32.
-constexpr int gemm_kt(int pa, int pb, int mt, int nt) { return (pa * mt + pb * nt) * 64 * 2 <= 48 * 1024 ? 64 : 32; }
-// LDS ring stages (at most 4) that fit 160 KB with 2 KB to spare.
+// K slice width: 32.  Narrow slices give the ring more stages, so more bytes
+// are in flight per CU (measured faster than 64-wide slices on every product
+// of the HMM-4096 step: the loads, not the matrix instructions, set the pace).
+constexpr int gemm_kt(int pa, int pb, int mt, int nt) { return 32; }
+// LDS ring stages (at most 6) that fit 160 KB with 2 KB to spare.
 constexpr int gemm_stages(int pa, int pb, int mt, int nt) {
-  return ((160 - 2) * 1024) / ((pa * mt + pb * nt) * gemm_kt(pa, pb, mt, nt) * 2) > 4
-             ? 4
+  return ((160 - 2) * 1024) / ((pa * mt + pb * nt) * gemm_kt(pa, pb, mt, nt) * 2) > 6
+             ? 6
              : ((160 - 2) * 1024) / ((pa * mt + pb * nt) * gemm_kt(pa, pb, mt, nt) * 2);
 }
 
@@ -62,9 +64,9 @@ constexpr int gemm_stages(int pa, int pb, int mt, int nt) {
 // >= 4 slices per split.
 inline GemmShape layer_shape(int rows256, int B_pad, int kpad, int pa, int pb, int opt_tile, int split_max) {
   GemmShape g{};
-  g.tile = opt_tile == TILE_256x128 ? TILE_256x128 : TILE_128x128;
-  g.mt = g.tile == TILE_128x128 ? 128 : 256;
-  g.nt = 128;
+  g.tile = opt_tile == TILE_256x128 ? TILE_256x128 : opt_tile == TILE_128x256 ? TILE_128x256 : TILE_128x128;
+  g.mt = g.tile == TILE_256x128 ? 256 : 128;
+  g.nt = g.tile == TILE_128x256 ? 256 : 128;
   g.tiles = rows256 * (256 / g.mt) * (B_pad / g.nt);
   const int ksteps = kpad / gemm_kt(pa, pb, g.mt, g.nt);
   int S = 1;

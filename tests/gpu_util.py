@@ -33,8 +33,9 @@ def torch():
     return T
 
 
-def run_gpu(cfg, mode="auto", splits=None, B=None, em=None, timing=False, device=0, repeat=1):
-    """Forward + backward (+ optional EM) on the GPU.  Returns numpy arrays."""
+def run_gpu(cfg, mode="auto", splits=None, B=None, em=None, timing=False, device=0, repeat=1, options=None):
+    """Forward + backward (+ optional EM) on the GPU.  Returns numpy arrays
+    (with timing: also the per-kind kernel counts and times, key "times")."""
     T = torch()
     circ = cfg["circuit"]
     B = B or cfg["B"]
@@ -43,6 +44,10 @@ def run_gpu(cfg, mode="auto", splits=None, B=None, em=None, timing=False, device
     L.pc_set_precision(h, mode)
     for (m, k, pa, pb) in (splits or []):
         L.pc_set_split(h, m, k, pa, pb)
+    for (name, value) in (options or []):
+        L.pc_set_option(h, name, value)
+    if timing:
+        L.pc_set_timing(h, True)
     params = T.tensor(cfg["params"], device=dev)
     tokens = T.tensor(cfg["tokens"], device=dev) if cfg.get("tokens") is not None else None
     vals = T.full((circ.num_nodes, B), float("nan"), device=dev)
@@ -70,6 +75,8 @@ def run_gpu(cfg, mode="auto", splits=None, B=None, em=None, timing=False, device
         T.cuda.synchronize()
         r = dict(vals=vals.cpu().numpy().copy(), flows=flows.cpu().numpy().copy(),
                  pflows=pflows.cpu().numpy().copy(), ll=None if ll is None else ll.cpu().numpy().copy())
+        if timing:
+            r["times"] = L.pc_kernel_times(h)
         if grads is not None:
             r["dA"] = [a.cpu().numpy().copy() for a, _ in grads]
             r["dB"] = [b.cpu().numpy().copy() for _, b in grads]

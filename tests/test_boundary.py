@@ -142,6 +142,17 @@ def test_modes_and_workspace():
     assert L.pc_workspace_bytes(h, 16) > L.pc_workspace_bytes(h, 15) - 1
 
 
+def test_options():
+    h = L.pc_compile_layout(W.hmm(64, 6, 9), device=-1)
+    for name, good, bad in (("layer_tile", (0, 1, 2, 3), (4, -1)), ("param_tile", (0, 1, 2), (3,)),
+                            ("split_max", (1, 2, 4, 8), (0, 3, 16)), ("fuse", (0, 1), (2, -1))):
+        for v in good:
+            L.pc_set_option(h, name, v)
+        for v in bad:
+            _expect(L.PC_ERR_INVALID_ARG, L.pc_set_option, h, name, v)
+    _expect(L.PC_ERR_INVALID_ARG, L.pc_set_option, h, 9, 0)
+
+
 def test_host_only_handle_refuses_device_calls():
     h = L.pc_compile_layout(W.hmm(8, 3, 4), device=-1)
     lib = L.lib()

@@ -21,13 +21,13 @@ def _gpu():
     L.lib()          # fails loudly when libpc.so is missing
 
 
-def _full(cfg, mode, what, em=None):
+def _full(cfg, mode, what, em=None, options=None):
     """Values and log-likelihood end to end at the stated tolerances; element
     and parameter flows per layer (each layer's flows recomputed by the
     oracle from that layer's GPU inputs) at the stated tolerances; flows end
     to end at the stated tolerance times the number of sum layers."""
     G.say(f"case {what} mode={mode} B={cfg['B']}")
-    gpu = G.run_gpu(cfg, mode, em=em)
+    gpu = G.run_gpu(cfg, mode, em=em, options=options)
     orc = G.run_oracle(cfg)
     G.check_values(gpu["vals"], orc["vals"], mode, f"{what} node values")
     if orc["ll"] is not None:
@@ -144,3 +144,42 @@ def test_fp32_needs_split(kind):
         except AssertionError as e:
             errs.append(str(e))
     assert errs, f"a 1-term {kind} product still met the fp32-level tolerance"
+
+
+@pytest.mark.parametrize("what,cfg_args,mode,all_fused", [
+    ("hmm", dict(name="hmm4096", H=320, T=7, V=50, B=70), "auto", True),
+    ("hmm ragged batch", dict(name="hmm4096", H=96, T=4, V=11, B=23), "fp32", True),
+    ("hclt", dict(name="hclt", num_vars=30, H=48, K=12, B=33), "auto", False),
+    ("block-sparse", dict(kind="block_sparse", seed=2, num_vars=6, K=5, in_blocks=3, block=24,
+                          sum_blocks=3, depth_sums=2, B=29), "auto", False),
+    ("lowrank hmm", dict(name="lowrank", H=40, T=4, V=7, B=23, rank=5), "auto", False),
+])
+def test_fused_product_layers_identical(what, cfg_args, mode, all_fused):
+    """Product layers evaluated inside the adjacent sum layers' column-max and
+    scaled-flow kernels give the same bits as their own launches: values,
+    log-likelihoods, flows and parameter flows (and LowRank gradients)."""
+    cfg = make_config(**cfg_args)
+    G.say(f"case fused product layers: {what} mode={mode} B={cfg['B']}")
+    fused = G.run_gpu(cfg, mode, timing=True)
+    plain = G.run_gpu(cfg, mode, timing=True, options=[("fuse", 0)])
+    for k in ("vals", "ll", "flows", "pflows"):
+        if fused[k] is not None:
+            np.testing.assert_array_equal(fused[k], plain[k], err_msg=f"{what}: {k}")
+    for k in ("dA", "dB"):
+        for x, y in zip(fused.get(k, []), plain.get(k, [])):
+            np.testing.assert_array_equal(x, y, err_msg=f"{what}: {k}")
+    tf, tp = fused["times"], plain["times"]
+    G.say(f"  launches fused/plain: product fwd {tf['product_fwd'][0]}/{tp['product_fwd'][0]}, "
+          f"product bwd {tf['product_bwd'][0]}/{tp['product_bwd'][0]}")
+    assert tp["product_fwd"][0] > 0 and tp["product_bwd"][0] > 0
+    if all_fused:   # every product layer of an HMM sits between two sum layers
+        assert tf["product_fwd"][0] == 0 and tf["product_bwd"][0] == 0
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("tile", [1, 2, 3])
+def test_layer_tile_options(tile, mode):
+    """Every per-layer product tile shape (128x128, 256x128, 128x256) meets the
+    tolerances; a batch of 300 leaves a ragged last column tile."""
+    cfg = make_config("hmm4096", H=320, T=5, V=50, B=300)
+    _full(cfg, mode, f"hmm 320x5 layer tile {tile}", options=[("layer_tile", tile)])
