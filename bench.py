@@ -188,6 +188,8 @@ def main():
     ap.add_argument("--layer-tile", type=int, default=0, help="product-kernel option: 0 auto (128x128), 1 128x128, 2 256x128, 3 128x256")
     ap.add_argument("--param-tile", type=int, default=0, help="product-kernel option: 0 auto (128x128), 1 128x128, 2 256x256")
     ap.add_argument("--split-max", type=int, default=8, help="largest K split of a per-layer product")
+    ap.add_argument("--param-chunk", type=int, default=0,
+                    help="tied copies per parameter-flow launch on a second stream (0: one launch at the end)")
     ap.add_argument("--fuse", type=int, default=1, choices=[0, 1],
                     help="1: product layers inside the adjacent sum layers' memory-bound kernels; 0: own launches")
     ap.add_argument("--copy-calibration", type=int, default=0,
@@ -226,6 +228,7 @@ def main():
     L.pc_set_option(h, "param_tile", args.param_tile)
     L.pc_set_option(h, "split_max", args.split_max)
     L.pc_set_option(h, "fuse", args.fuse)
+    L.pc_set_option(h, "param_chunk", args.param_chunk)
     params = torch.tensor(cfg["params"], device=dev)
     params0 = params.clone()
     tokens = torch.tensor(cfg["tokens"], device=dev)

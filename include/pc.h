@@ -204,13 +204,20 @@ int pc_set_split(pc_handle h, int mode, int gemm_kind, int planes_a, int planes_
  * adjacent sum layer's memory-bound kernels where the layout allows it (the
  * forward in the next sum layer's column maxima, the backward in the previous
  * sum layer's scaled-flow packing; identical results), 0 launches the
- * product kernels separately.  Changing an option can change
+ * product kernels separately.  PC_OPT_PARAM_CHUNK: 0 (default) computes the
+ * parameter flows in one product after the layers; n > 0 computes them in
+ * chunks of n tied copies per weight block on a second stream of the
+ * handle, each as soon as its copies' scaled flows exist, overlapping the
+ * element flows (deterministic; the float32 sum is grouped by chunk, so the
+ * bits differ from n = 0).  pc_backward joins that stream into the caller's
+ * before it returns.  Changing an option can change
  * pc_workspace_bytes.
  * Errors: PC_ERR_INVALID_ARG (unknown option or value). */
 #define PC_OPT_LAYER_TILE 0
 #define PC_OPT_PARAM_TILE 1
 #define PC_OPT_SPLIT_MAX  2
 #define PC_OPT_FUSE       3
+#define PC_OPT_PARAM_CHUNK 4
 int pc_set_option(pc_handle h, int option, int value);
 
 /* Bytes of workspace pc_forward / pc_backward need for `batch` samples in the

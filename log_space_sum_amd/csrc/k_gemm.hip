@@ -215,6 +215,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
 
   // ---- locate the problem, the tile and the K range ------------------------
   int S = 1, split = 0, tile = logical;
+  if (EPI == EPI_PARAM) tile += a.tile0;
   if (EPI != EPI_PARAM) {
     S = a.splitk;
     tile = logical / S;
@@ -265,13 +266,24 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
     bl = a.blocks[b];
     const int Mp = (bl.M + ROW_PAD - 1) / ROW_PAD * ROW_PAD;
     const int Np = (bl.N + ROW_PAD - 1) / ROW_PAD * ROW_PAD;
-    const int ntn = Np / NT;
+    const int ntn = Np / NT, mtn = Mp / MT;
     const int lt = tile - ((MT == 256) ? bl.pt256 : bl.pt128);
-    m0 = (lt / ntn) * MT;
-    n0 = (lt % ntn) * NT;
+    // tiles in groups of up to 4 tile rows, column-major inside a group, so
+    // the 32 workgroups an XCD runs at once cover about 4 x 8 tiles and
+    // share both operands' panels in its L2
+    constexpr int GM = 4;
+    const int grp = lt / (GM * ntn), r0g = grp * GM;
+    const int rows = mtn - r0g < GM ? mtn - r0g : GM;
+    const int in = lt - grp * GM * ntn;
+    m0 = (r0g + in % rows) * MT;
+    n0 = (in / rows) * NT;
     kst = a.B_padK / KT;
-    kbeg = 0;
-    kend = bl.ncopies * kst;
+    {
+      const int c0 = a.copy_lo < bl.ncopies ? a.copy_lo : bl.ncopies;
+      const int c1 = a.copy_hi < bl.ncopies ? a.copy_hi : bl.ncopies;
+      kbeg = c0 * kst;
+      kend = (c1 > c0 ? c1 : c0) * kst;
+    }
     Ab = a.opA;
     Bb = a.opB;
     RA = a.rowsA;

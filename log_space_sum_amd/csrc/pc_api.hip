@@ -330,6 +330,9 @@ GemmArgs gemm_common(const Call& c) {
   a.blocks = c.h->d_blocks;
   a.partials = c.v.partials;
   a.counters = c.v.counters;
+  a.copy_lo = 0;
+  a.copy_hi = 1 << 30;
+  a.tile0 = 0;
   return a;
 }
 
@@ -476,6 +479,17 @@ int pc_compile_layout(const pc_circuit_desc* desc, int device, pc_handle* out) {
 int pc_destroy(pc_handle hh) {
   if (!hh) return PC_OK;
   Handle* h = reinterpret_cast<Handle*>(hh);
+  if (h->device >= 0 && (h->side_stream || !h->chunk_events.empty())) {
+    int prev = -1;
+    (void)hipGetDevice(&prev);
+    (void)hipSetDevice(h->device);
+    if (h->side_stream) {
+      (void)hipStreamSynchronize((hipStream_t)h->side_stream);
+      (void)hipStreamDestroy((hipStream_t)h->side_stream);
+    }
+    for (void* e : h->chunk_events) (void)hipEventDestroy((hipEvent_t)e);
+    if (prev >= 0) (void)hipSetDevice(prev);
+  }
   free_tables(h);
   delete h;
   return PC_OK;
@@ -531,6 +545,9 @@ int pc_set_option(pc_handle hh, int option, int value) {
     } else if (option == PC_OPT_SPLIT_MAX) {
       if (value != 1 && value != 2 && value != 4 && value != 8) fail(PC_ERR_INVALID_ARG, "split must be 1, 2, 4 or 8");
       h->opt_split_max = value;
+    } else if (option == PC_OPT_PARAM_CHUNK) {
+      if (value < 0) fail(PC_ERR_INVALID_ARG, "parameter-flow chunk must be >= 0");
+      h->opt_param_chunk = value;
     } else if (option == PC_OPT_FUSE) {
       if (value != 0 && value != 1) fail(PC_ERR_INVALID_ARG, "fuse must be 0 or 1");
       h->opt_fuse = value;
@@ -747,7 +764,69 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
       Timed t(h, KK_OTHER, c.s);
       launch_fill_u32((uint32_t*)((char*)c.ws + p.lrP), (int64_t)p.lr_nsg * h->lr_p_elems, 0u, c.s);
     }
+    // Parameter flows: one product over every tied copy after the layers, or
+    // (opt_param_chunk > 0) chunks of that many copies per weight block on a
+    // second stream, each launched once the last of its copies has its
+    // scaled flows packed, in a fixed order (chunks of a block add into its
+    // parameter flows one after another), joined before returning.
+    GemmArgs pg = gemm_common(c);
+    pg.ngroups = (int)h->blocks.size();
+    pg.opA = v.garena;
+    pg.planeA = v.garena_plane;
+    pg.opB = v.earena;
+    pg.planeB = v.earena_plane;
+    pg.params = params;
+    pg.pflows = param_flows;
+    pg.splitk = 1;
+    const GemmShape pshp = param_gemm_shape(h, p.pl[GK_PARAM][0], p.pl[GK_PARAM][1]);
+    struct Chunk {
+      int ready, block, lo, hi;
+    };
+    std::vector<Chunk> chunks;
+    const int CC = h->opt_param_chunk;
+    if (h->has_plain_sums && CC > 0) {
+      for (size_t b = 0; b < h->blocks.size(); ++b)
+        for (int lo = 0; lo < h->blocks[b].ncopies; lo += CC) {
+          const int hi = std::min(lo + CC, (int)h->blocks[b].ncopies);
+          int ready = 1 << 30;
+          for (int q = lo; q < hi; ++q) ready = std::min(ready, h->copy_layer[b][q]);
+          chunks.push_back(Chunk{ready, (int)b, lo, hi});
+        }
+      std::stable_sort(chunks.begin(), chunks.end(), [](const Chunk& x, const Chunk& y) { return x.ready > y.ready; });
+      if (!h->side_stream) {
+        hipStream_t ss;
+        HIPCHECK(hipStreamCreateWithFlags(&ss, hipStreamNonBlocking));
+        h->side_stream = ss;
+      }
+      while (h->chunk_events.size() < chunks.size() + 1) {
+        hipEvent_t e;
+        HIPCHECK(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+        h->chunk_events.push_back(e);
+      }
+    }
+    hipStream_t side = (hipStream_t)h->side_stream;
+    size_t next_chunk = 0;
+    auto launch_ready_chunks = [&](int li) {
+      while (next_chunk < chunks.size() && chunks[next_chunk].ready >= li) {
+        const Chunk& ch = chunks[next_chunk];
+        hipEvent_t e = (hipEvent_t)h->chunk_events[next_chunk];
+        HIPCHECK(hipEventRecord(e, c.s));
+        HIPCHECK(hipStreamWaitEvent(side, e, 0));
+        const BlockRec& bl = h->blocks[ch.block];
+        GemmArgs g = pg;
+        g.copy_lo = ch.lo;
+        g.copy_hi = ch.hi;
+        GemmShape shp = pshp;
+        const int64_t Mp = round_up(bl.M, ROW_PAD), Np = round_up(bl.N, ROW_PAD);
+        g.tile0 = shp.mt == 256 ? bl.pt256 : bl.pt128;
+        shp.tiles = (int)((Mp / shp.mt) * (Np / shp.nt));
+        Timed t(h, KK_PARAM, side);
+        launch_gemm(EPI_PARAM, p.pl[GK_PARAM][0], p.pl[GK_PARAM][1], shp, g, side);
+        ++next_chunk;
+      }
+    };
     for (int li = (int)h->layers.size() - 1; li >= 0; --li) {
+      launch_ready_chunks(li + 1);
       const LayerRef& r = h->layers[li];
       if (r.kind == PC_LAYER_SUM && h->sums[r.idx].lowrank) {
         const SumPlan& sp = h->sums[r.idx];
@@ -859,19 +938,14 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
       launch_lr_fplus((float*)((char*)c.ws + p.lrP) + h->lr_p_off[bi] * p.lr_nsg, p.lr_nsg, (int64_t)bl.M * bl.N,
                       param_flows + bl.param_offset, c.s);
     }
-    if (h->has_plain_sums) {
-      GemmArgs g = gemm_common(c);
-      g.ngroups = (int)h->blocks.size();
-      g.opA = v.garena;
-      g.planeA = v.garena_plane;
-      g.opB = v.earena;
-      g.planeB = v.earena_plane;
-      g.params = params;
-      g.pflows = param_flows;
-      const GemmShape shp = param_gemm_shape(h, p.pl[GK_PARAM][0], p.pl[GK_PARAM][1]);
-      g.splitk = 1;
+    if (!chunks.empty()) {
+      launch_ready_chunks(-(1 << 29));
+      hipEvent_t e = (hipEvent_t)h->chunk_events[chunks.size()];
+      HIPCHECK(hipEventRecord(e, side));
+      HIPCHECK(hipStreamWaitEvent(c.s, e, 0));
+    } else if (h->has_plain_sums) {
       Timed t(h, KK_PARAM, c.s);
-      launch_gemm(EPI_PARAM, p.pl[GK_PARAM][0], p.pl[GK_PARAM][1], shp, g, c.s);
+      launch_gemm(EPI_PARAM, p.pl[GK_PARAM][0], p.pl[GK_PARAM][1], pshp, pg, c.s);
     }
     check_launch();
     return PC_OK;

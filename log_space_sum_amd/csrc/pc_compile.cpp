@@ -373,6 +373,7 @@ Handle* compile_layout(const pc_circuit_desc* d) {
     }
     int64_t th = 0, tht = 0, erow = 0, grow = 0;
     int32_t pk = 0, p256 = 0, p128 = 0;
+    h->copy_layer.assign(h->blocks.size(), {});
     for (size_t b = 0; b < h->blocks.size(); ++b) {
       BlockRec& B = h->blocks[b];
       const int64_t Mp = round_up(B.M, ROW_PAD), Np = round_up(B.N, ROW_PAD);
@@ -380,6 +381,8 @@ Handle* compile_layout(const pc_circuit_desc* d) {
       B.ncopies = (int32_t)per[b].size();
       B.g_base = grow;
       B.e_base = erow;
+      h->copy_layer[b].clear();
+      for (int c = 0; c < B.ncopies; ++c) h->copy_layer[b].push_back(h->sums[per[b][c].first].layer);
       for (int c = 0; c < B.ncopies; ++c) {
         GroupRec& r = h->sums[per[b][c].first].groups[per[b][c].second];
         r.g_row = grow + c * Mp;

@@ -104,6 +104,10 @@ struct Handle {
   // planes[mode][gemm kind][0: first operand, 1: second operand]
   int planes[2][3][2] = {{{2, 1}, {2, 1}, {2, 1}}, {{3, 3}, {3, 3}, {3, 3}}};
   int opt_layer_tile = 0, opt_param_tile = 0, opt_split_max = 8, opt_fuse = 1;   // pc_set_option
+  int opt_param_chunk = 0;             // tied copies per parameter-flow launch (0: one launch at the end)
+  std::vector<std::vector<int32_t>> copy_layer;   // per weight block: the layer of each tied copy
+  void* side_stream = nullptr;         // parameter-flow chunks run here, beside the element flows
+  std::vector<void*> chunk_events;
   int32_t num_nodes = 0, num_vars = 0, root = -1, lowrank_rank = 0;
   int64_t num_params = 0;
   std::vector<LayerRef> layers;

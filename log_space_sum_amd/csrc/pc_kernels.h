@@ -33,6 +33,9 @@ struct GemmArgs {
   float* pflows;
   float* partials;              // split-K partial tiles
   uint32_t* counters;           // split-K arrival counters, zero between launches
+  // parameter flows: tied copies [copy_lo, copy_hi) of each block; the launch
+  // covers product tiles tile0 .. tile0 + grid - 1 of the block sequence
+  int32_t copy_lo, copy_hi, tile0;
 };
 
 // Output tile shapes of the product kernel (M x N per workgroup).

@@ -183,3 +183,22 @@ def test_layer_tile_options(tile, mode):
     tolerances; a batch of 300 leaves a ragged last column tile."""
     cfg = make_config("hmm4096", H=320, T=5, V=50, B=300)
     _full(cfg, mode, f"hmm 320x5 layer tile {tile}", options=[("layer_tile", tile)])
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("what,cfg_args,chunk", [
+    ("hmm", dict(name="hmm4096", H=320, T=7, V=50, B=70), 1),
+    ("hmm", dict(name="hmm4096", H=320, T=7, V=50, B=70), 4),
+    ("block-sparse", dict(kind="block_sparse", seed=2, num_vars=6, K=5, in_blocks=3, block=24,
+                          sum_blocks=3, depth_sums=2, B=29), 2),
+    ("hclt", dict(name="hclt", num_vars=30, H=48, K=12, B=33), 3),
+])
+def test_param_flow_chunks(what, cfg_args, chunk, mode):
+    """Parameter flows in chunks of tied copies on the handle's second stream
+    meet the tolerances, and repeat bit for bit."""
+    cfg = make_config(**cfg_args)
+    opts = [("param_chunk", chunk)]
+    gpu, orc = _full(cfg, mode, f"{what} parameter flows in chunks of {chunk}", options=opts)
+    again = G.run_gpu(cfg, mode, options=opts)
+    np.testing.assert_array_equal(gpu["pflows"], again["pflows"])
+    np.testing.assert_array_equal(gpu["flows"], again["flows"])
