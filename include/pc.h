@@ -116,7 +116,7 @@ typedef struct pc_layer_desc {
 /* The circuit: layers in topological order (every child is defined by an
  * earlier layer), every node id in [0, num_nodes) defined exactly once.
  * root: node whose value pc_forward copies to `ll` (-1: none).
- * lowrank_rank: rank k of every LowRank slot (1..64), 0 if none. */
+ * lowrank_rank: rank k of every LowRank slot (1..32), 0 if none. */
 typedef struct pc_circuit_desc {
   int32_t num_nodes;
   int32_t num_vars;
@@ -169,7 +169,7 @@ typedef struct pc_layout_summary {
  * Errors: PC_ERR_INVALID_ARG (null pointers, ids out of range, a node defined
  * twice or used before it is defined, empty product, tied groups of different
  * shape, parameters out of range, overlapping parameter blocks),
- * PC_ERR_UNSUPPORTED (LowRank rank > 64 or < 1), PC_ERR_HIP. */
+ * PC_ERR_UNSUPPORTED (LowRank rank > 32 or < 1), PC_ERR_HIP. */
 int pc_compile_layout(const pc_circuit_desc* desc, int device, pc_handle* out);
 
 /* Free a handle and its device tables (null is accepted). */

@@ -187,19 +187,21 @@ __global__ void k_bucket(const int32_t* tokT, int B, int Kmax, int32_t* bptr, in
   }
 }
 
-// F_in[row, k] += sum over the row's nodes u (ascending) of n_u[k], with
-// n_u[k] the sum over the samples b with x[b, var(u)] = k (ascending) of
-// f[u, b].  One workgroup of NW waves per parameter row: each wave takes one
-// of the row's nodes at a time (NW in flight), stages its flow row and its
-// variable's category buckets in its own LDS region and sums every bucket;
-// the per-node sums are then added in node order.  Needs K <= 1024 and the
-// LDS regions to fit (see launch_input_bwd).
+// F_in[row, k] += sum over the row's nodes u of n_u[k], with n_u[k] the sum
+// over the samples b with x[b, var(u)] = k (ascending) of f[u, b].  One
+// workgroup of NW waves per parameter row; wave w takes the row's nodes
+// w, w + NW, ... on its own (no workgroup barrier between nodes): it stages
+// the node's flow row and its variable's category buckets in its own LDS
+// region and adds every bucket's sum to its per-category registers.  At the
+// end the NW partial sums are added in wave order, so the result does not
+// depend on timing.  Needs K <= 1024 and the LDS regions to fit (see
+// launch_input_bwd).
 template <int NW>
 __global__ __launch_bounds__(64 * NW) void k_input_bwd(InputArgs a) {
   extern __shared__ float ib_sm[];
-  constexpr int NT = 64 * NW, J = 1024 / NT;
+  constexpr int J = 1024 / 64;
   const int B = a.B, K = a.K;
-  const int per = 2 * B + 2 * K + 1;          // f[B], idx[B], ptr[K + 1], n[K]
+  const int per = 2 * B + K + 1;              // f[B], idx[B], ptr[K + 1]
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   float* f = ib_sm + w * per;
   int32_t* idx = (int32_t*)(f + B);
@@ -208,44 +210,54 @@ __global__ __launch_bounds__(64 * NW) void k_input_bwd(InputArgs a) {
   float acc[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) acc[j] = 0.0f;
-  for (int qb = q0; qb < q1; qb += NW) {
-    const int q = qb + w;
-    if (q < q1) {
-      const int node = a.row_nodes[q];
-      const int v = a.var[node - a.node_start];
-      const float* F = a.flows + (int64_t)node * B;
-      const int32_t* I = a.bidx + (int64_t)v * B;
-      const int32_t* P = a.bptr + (int64_t)v * (a.Kmax + 1);
+  for (int q = q0 + w; q < q1; q += NW) {
+    const int node = a.row_nodes[q];
+    const int v = a.var[node - a.node_start];
+    const float* F = a.flows + (int64_t)node * B;
+    const int32_t* I = a.bidx + (int64_t)v * B;
+    const int32_t* P = a.bptr + (int64_t)v * (a.Kmax + 1);
+    // a wave's LDS operations complete in order: the previous node's reads
+    // are done before these writes land, and these writes before the reads below
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll 4
-      for (int b = lane; b < B; b += 64) {
-        f[b] = F[b];
-        idx[b] = I[b];
-      }
-#pragma unroll 4
-      for (int k = lane; k <= K; k += 64) ptr[k] = P[k];
-      // a wave's LDS operations complete in order: its own writes are visible here
-      float* n = (float*)(ptr + K + 1);
-      for (int k = lane; k < K; k += 64) {
-        float t = 0.0f;
-        for (int e = ptr[k]; e < ptr[k + 1]; ++e) t += f[idx[e]];
-        n[k] = t;
-      }
+    for (int b = lane; b < B; b += 64) {
+      f[b] = F[b];
+      idx[b] = I[b];
     }
-    __syncthreads();
-    const int nq = min(NW, q1 - qb);
+#pragma unroll 4
+    for (int k = lane; k <= K; k += 64) ptr[k] = P[k];
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int k = j * NT + tid;
-      if (k < K)
-        for (int u = 0; u < nq; ++u) acc[j] += ((const float*)((const int32_t*)(ib_sm + u * per + 2 * B) + K + 1))[k];
+      const int k = j * 64 + lane;
+      if (k < K) {
+        float t = 0.0f;
+        for (int e = ptr[k]; e < ptr[k + 1]; ++e) t += f[idx[e]];
+        acc[j] += t;
+      }
     }
-    __syncthreads();                             // regions free for the next nodes
   }
   float* out = a.pflows + a.param_offset + (int64_t)r * K;
+  if constexpr (NW == 1) {
 #pragma unroll
-  for (int j = 0; j < J; ++j) {
-    const int k = j * NT + tid;
-    if (k < K) out[k] += acc[j];
+    for (int j = 0; j < J; ++j) {
+      const int k = j * 64 + lane;
+      if (k < K) out[k] += acc[j];
+    }
+  } else {
+    __syncthreads();                            // every wave done with its region
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int k = j * 64 + lane;
+      if (k < K) f[k] = acc[j];                 // K <= per: the partial fits the region
+    }
+    __syncthreads();
+    for (int k = tid; k < K; k += 64 * NW) {
+      float t = 0.0f;
+#pragma unroll
+      for (int u = 0; u < NW; ++u) t += ib_sm[u * per + k];
+      out[k] += t;
+    }
   }
 }
 
@@ -775,7 +787,7 @@ void launch_bucket(const int32_t* tokT, int V, int B, int Kmax, int32_t* bptr, i
 }
 void launch_input_bwd(const InputArgs& a, hipStream_t s) {
   if (a.num_rows <= 0) return;
-  const size_t per = (size_t)(2 * a.B + 2 * a.K + 1) * sizeof(float);
+  const size_t per = (size_t)(2 * a.B + a.K + 1) * sizeof(float);
   const int nw = a.max_row_nodes >= 2 ? 4 : 1;
   if (a.K <= 1024 && per * nw <= 64 * 1024) {
     if (nw == 4) hipLaunchKernelGGL(k_input_bwd<4>, dim3(a.num_rows), dim3(256), per * 4, s, a);
@@ -786,17 +798,20 @@ void launch_input_bwd(const InputArgs& a, hipStream_t s) {
 }
 void launch_prod_fwd(const ProdArgs& a, hipStream_t s) { PC_LAUNCH_V(k_prod_fwd, a.num_nodes, a, s); }
 void launch_prod_bwd(const ProdArgs& a, hipStream_t s) { PC_LAUNCH_V(k_prod_bwd, a.nuniq, a, s); }
-// Column maxima (and the preceding product layer when a.fp_on): 4 samples
-// per lane when the batch is a multiple of 4, else 2 (8-byte accesses) or 1.
+// Column maxima (and the preceding product layer when a.fp_on): V samples per
+// lane, the widest of 4 (16-byte accesses, batch a multiple of 4), 2 and 1
+// that still gives 512 workgroups (two per CU), else 1: a 4096-child layer at
+// batch 512 is 64 row tiles, only 128 workgroups of 256 samples.
 template <bool PROD>
 static void launch_colmax_v(const SumArgs& a, int row_tiles, hipStream_t s) {
   const int g4 = row_tiles * ((a.B + 255) / 256), g2 = row_tiles * ((a.B + 127) / 128);
-  if (a.B % 4 == 0)
+  const int g1 = row_tiles * ((a.B + 63) / 64);
+  if (a.B % 4 == 0 && g4 >= 512)
     hipLaunchKernelGGL((k_colmax<4, PROD>), dim3(g4), dim3(256), 0, s, a);
-  else if (a.B % 2 == 0)
+  else if (a.B % 2 == 0 && g2 >= 512)
     hipLaunchKernelGGL((k_colmax<2, PROD>), dim3(g2), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((k_colmax<1, PROD>), dim3(row_tiles * ((a.B + 63) / 64)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_colmax<1, PROD>), dim3(g1), dim3(256), 0, s, a);
 }
 void launch_colmax(const SumArgs& a, int row_tiles, hipStream_t s) {
   if (row_tiles <= 0) return;

@@ -78,62 +78,247 @@ __device__ __forceinline__ float at4(const float4& v, int e) { return e == 0 ? v
 
 }  // namespace
 
-// e[j, b] = exp(v[child j, b] - m[b]), float32, sample-major [B][ldE] at column
-// e_koff + j (zero for N <= j < N rounded up to 32).  64 children x 64
-// samples per workgroup through an LDS transpose.
-__global__ void k_lr_exp(LRArgs a) {
-  __shared__ float t[64][65];
-  const int ncols = (a.N + 31) / 32 * 32, nj = (ncols + 63) / 64;
-  const int jt = blockIdx.x % nj, bt = blockIdx.x / nj;
-  const int j0 = jt * 64, b0 = bt * 64;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int b = b0 + lane;
-  const float sh = b < a.B ? key_to_shift_lr(a.mkeys[(int64_t)a.m_row * a.B + b]) : 0.0f;
-  for (int r = w; r < 64; r += 4) {
-    const int j = j0 + r;
-    float e = 0.0f;
-    if (j < a.N && b < a.B) {
-      const int child = a.chblocks[a.blk_off + j / a.cbs] + j % a.cbs;
-      e = expf(a.vals[(int64_t)child * a.B + b] - sh);
-    }
-    t[r][lane] = e;
+// ---- per-layer preparation ---------------------------------------------------
+// Fragment records: the factors of one sample and one 32-wide block of rows (A)
+// or columns (B), split into bfloat16 planes and stored in the order the
+// matrix instructions read them (64 lanes x 8 values, 16 bytes per lane), so
+// that the fused kernels load each operand with one 16-byte access per lane:
+//   A side, block ib of rows, per sample b:
+//     h form, K chunk kc (PH planes): lane l: A[ib*32 + l%32][kc*16 + (l/32)*8 + e] * log2(e)
+//     d form, chunk cc (PG planes):   lane l: A[ib*32 + 16cc + (e/4)*8 + (l/32)*4 + e%4][l%32]
+//   B side, block jb of columns, per sample b:
+//     h form, K chunk kc (PH planes): lane l: B[kc*16 + (l/32)*8 + e][jb*32 + l%32]
+//     u form, chunk cc (PG planes):   lane l: B[l%32][jb*32 + 16cc + (e/4)*8 + (l/32)*4 + e%4]
+// (zero outside the factor).  The h forms are the two operands of h = A B (or
+// of its transpose); the d form is the first operand of dB = A^T X and the u
+// form that of U^T, W^T = B (q e)^T, B q^T, whose second operands come from h's
+// accumulator registers, hence the permuted order along the contraction.
+// Records of a block: the h forms (kc, plane), then the d / u forms (cc, plane).
+constexpr int kFrag = 512;   // bfloat16 elements per record
+
+template <int PH, int PG, int KC>
+struct LrPack {
+  static constexpr int FB = KC * PH + 2 * PG;     // records per block
+  static __device__ __forceinline__ const uint16_t* bside(const LRArgs& a, int b, int jb) {
+    const int nJB = (a.N + 31) / 32;
+    return a.pk + ((int64_t)b * nJB + jb) * FB * kFrag;
   }
-  __syncthreads();
-  for (int r = w; r < 64; r += 4) {
-    const int bb = b0 + r, j = j0 + lane;
-    if (bb < a.B && j < ncols) a.E[(int64_t)bb * a.ldE + a.e_koff + j] = t[lane][r];   // zeros past N
+  static __device__ __forceinline__ const uint16_t* aside(const LRArgs& a, int b, int ib) {
+    const int nJB = (a.N + 31) / 32, nIB = (a.M + 31) / 32;
+    return a.pk + ((int64_t)a.B * nJB + (int64_t)b * nIB + ib) * FB * kFrag;
+  }
+};
+
+// One 16-byte fragment: `ub` is uniform over the wave (held in scalar
+// registers), `lane_bytes` the lane's 32-bit offset.
+__device__ __forceinline__ bf16x8_t ldfrag(const uint16_t* ub, uint32_t lane_bytes) {
+  return *(const bf16x8_t*)((const char*)ub + lane_bytes);
+}
+
+// Round x into P bfloat16 planes (each the rounding of what the previous
+// planes leave) and store plane p as 16 bytes at dst + p * kFrag.
+template <int P>
+__device__ __forceinline__ void split_store_frag(const float (&x)[8], uint16_t* dst) {
+  bf16x8_t o[P];
+  split8<P>(x, o);
+#pragma unroll
+  for (int p = 0; p < P; ++p) *(bf16x8_t*)(dst + p * kFrag) = o[p];
+}
+
+// One launch per LowRank group and pass, three roles by workgroup range:
+//  (1) e[j, b] = exp(v[child j, b] - m[b]), float32, sample-major [B][ldE] at
+//      column e_koff + j (zero for N <= j < N rounded up to 32); 32 children x
+//      32 samples per workgroup through an LDS transpose;
+//  (2) the fragment records of A_b and B_b (four record sets per workgroup);
+//  (3) backward only: c1 = f / Sraw, c2 = f / Z per (sample, row) (zero where
+//      the flow is zero or the node's value is -inf) and
+//      dLL/dA_b[i, k] = c1 U[i, k] - c2 W[i, k], one (sample, row) per thread.
+template <int PH, int PG, int KC>
+__global__ __launch_bounds__(256) void k_lr_prep(LRArgs a, int backward) {
+  using PK = LrPack<PH, PG, KC>;
+  __shared__ float t[32][33];
+  const int tid = threadIdx.x;
+  const int ncols = (a.N + 31) / 32 * 32;
+  const int nEj = ncols / 32, nE = nEj * ((a.B + 31) / 32);
+  const int nJB = (a.N + 31) / 32, nIB = (a.M + 31) / 32;
+  const int64_t nsets = (int64_t)a.B * (nJB + nIB) * (KC + 2);
+  const int nP = (int)((nsets + 3) / 4);
+  int wg = blockIdx.x;
+  if (wg < nE) {
+    const int j0 = (wg % nEj) * 32, b0 = (wg / nEj) * 32;
+    {
+      const int jj = tid >> 3, bq = (tid & 7) * 4, j = j0 + jj;
+      const int child = j < a.N ? a.chblocks[a.blk_off + j / a.cbs] + j % a.cbs : 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int b = b0 + bq + e;
+        float v = 0.0f;
+        if (j < a.N && b < a.B)
+          v = expf(a.vals[(int64_t)child * a.B + b] - key_to_shift_lr(a.mkeys[(int64_t)a.m_row * a.B + b]));
+        t[jj][bq + e] = v;
+      }
+    }
+    __syncthreads();
+    const int bb = tid >> 3, jq = (tid & 7) * 4, b = b0 + bb;
+    if (b < a.B)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a.E[(int64_t)b * a.ldE + a.e_koff + j0 + jq + e] = t[jq + e][bb];   // zeros past N
+    return;
+  }
+  wg -= nE;
+  if (wg < nP) {
+    const int64_t set = (int64_t)wg * 4 + (tid >> 6);
+    if (set >= nsets) return;
+    const int lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+    const int form = (int)(set % (KC + 2));
+    const int64_t rest = set / (KC + 2);
+    const int blk = (int)(rest % (nJB + nIB)), b = (int)(rest / (nJB + nIB));
+    const int kr = a.krank;
+    float x[8];
+    if (blk < nJB) {
+      const int jb = blk;
+      const float* Bb = a.Bf + (int64_t)b * kr * a.N;
+      uint16_t* dst = const_cast<uint16_t*>(PK::bside(a, b, jb)) + lane * 8;
+      if (form < KC) {
+        const int j = jb * 32 + l32;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int k = form * 16 + h * 8 + e;
+          x[e] = (k < kr && j < a.N) ? Bb[(int64_t)k * a.N + j] : 0.0f;
+        }
+        split_store_frag<PH>(x, dst + form * PH * kFrag);
+      } else {
+        const int cc = form - KC;
+        const int jq = jb * 32 + 16 * cc + h * 4;     // values e of runs jq + (e/4)*8 + e%4
+        if ((a.N & 3) == 0 && l32 < kr && jq + 11 < a.N) {
+          const float4 u0 = ld4(Bb + (int64_t)l32 * a.N + jq), u1 = ld4(Bb + (int64_t)l32 * a.N + jq + 8);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[e] = at4(u0, e);
+            x[4 + e] = at4(u1, e);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int j = jq + (e / 4) * 8 + (e % 4);
+            x[e] = (l32 < kr && j < a.N) ? Bb[(int64_t)l32 * a.N + j] : 0.0f;
+          }
+        }
+        split_store_frag<PG>(x, dst + (KC * PH + cc * PG) * kFrag);
+      }
+    } else {
+      const int ib = blk - nJB;
+      const float* Ab = a.A + (int64_t)b * a.M * kr;
+      uint16_t* dst = const_cast<uint16_t*>(PK::aside(a, b, ib)) + lane * 8;
+      if (form < KC) {
+        const int i = ib * 32 + l32, k0 = form * 16 + h * 8;
+        if ((kr & 3) == 0 && i < a.M && k0 + 8 <= kr) {
+          const float4 u0 = ld4(Ab + (int64_t)i * kr + k0), u1 = ld4(Ab + (int64_t)i * kr + k0 + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[e] = at4(u0, e) * kLog2e;
+            x[4 + e] = at4(u1, e) * kLog2e;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int k = k0 + e;
+            x[e] = (k < kr && i < a.M) ? Ab[(int64_t)i * kr + k] * kLog2e : 0.0f;
+          }
+        }
+        split_store_frag<PH>(x, dst + form * PH * kFrag);
+      } else {
+        const int cc = form - KC;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int i = ib * 32 + 16 * cc + (e / 4) * 8 + h * 4 + (e % 4);
+          x[e] = (l32 < kr && i < a.M) ? Ab[(int64_t)i * kr + l32] : 0.0f;
+        }
+        split_store_frag<PG>(x, dst + (KC * PH + cc * PG) * kFrag);
+      }
+    }
+    return;
+  }
+  wg -= nP;
+  if (!backward) return;
+  const int ldC = (a.M + 31) / 32 * 32;
+  const int64_t xc = (int64_t)wg * 256 + tid;
+  if (xc >= (int64_t)a.B * ldC) return;
+  const int b = (int)(xc / ldC), i = (int)(xc - (int64_t)b * ldC);
+  if (i >= a.M) {
+    a.C1[xc] = 0.0f;
+    a.C2[xc] = 0.0f;
+    return;
+  }
+  const int64_t x = (int64_t)b * a.M + i;
+  const float f = a.flows[(int64_t)(a.out_start + i) * a.B + b];
+  const float Z = a.Z[x], S = a.S[x];
+  const bool ok = f != 0.0f && Z > 0.0f && S > 0.0f;
+  const float c1 = ok ? f / S : 0.0f, c2 = ok ? f / Z : 0.0f;
+  a.C1[xc] = c1;
+  a.C2[xc] = c2;
+  const int kr = a.krank;
+  if ((kr & 3) == 0) {        // rows of U, W, dA 16-byte aligned
+    for (int k = 0; k < kr; k += 4) {
+      const float4 u = ld4(a.U + x * kr + k), w = ld4(a.W + x * kr + k);
+      *(float4*)(a.dA + x * kr + k) =
+          make_float4(c1 * u.x - c2 * w.x, c1 * u.y - c2 * w.y, c1 * u.z - c2 * w.z, c1 * u.w - c2 * w.w);
+    }
+  } else {
+    for (int k = 0; k < kr; ++k) a.dA[x * kr + k] = c1 * a.U[x * kr + k] - c2 * a.W[x * kr + k];
   }
 }
 
 // Forward: workgroup = 32 rows x 4 samples (one per wave), all children.
+// The weights of the row strip are staged in LDS (shared by the 4 samples);
+// a wave streams its sample's B records and e one 32-child block ahead.
 template <int PH, int PG, int KC>
 __global__ __launch_bounds__(256) void k_lr_fwd(LRArgs a) {
+  using PK = LrPack<PH, PG, KC>;
   __shared__ __attribute__((aligned(16))) float slab[kSlabF];   // theta rows [32][C + 4]
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int mt = (a.M + 31) / 32;
-  const int i0 = (blockIdx.x % mt) * 32, b = (blockIdx.x / mt) * 4 + wave;
+  const int ib = blockIdx.x % mt, i0 = ib * 32, b = (blockIdx.x / mt) * 4 + wave;
   const bool act = b < a.B;
   const int M = a.M, N = a.N, kr = a.krank;
-  const float* Bb = a.Bf + (int64_t)(act ? b : 0) * kr * N;
-  const float* Eb = a.E + (int64_t)(act ? b : 0) * a.ldE + a.e_koff;
+  const int bq = act ? b : 0;
+  const float* Eb = a.E + (int64_t)bq * a.ldE + a.e_koff;
+  const uint16_t* Bp = PK::bside(a, bq, 0);                  // block jb at + jb * FB * kFrag
+  const uint32_t lb = (uint32_t)lane * 16;
 
-  // second operand of h^T: A_b[i, k] log2(e), i = i0 + l32, k = kc*16 + h*8 + e
+  // second operand of h^T: the h form of A_b for this row strip
   bf16x8_t bA[KC][PH];
+  {
+    const uint16_t* ap = PK::aside(a, bq, ib);
 #pragma unroll
-  for (int kc = 0; kc < KC; ++kc) {
-    float x[8];
+    for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int k = kc * 16 + h * 8 + e;
-      x[e] = (act && k < kr && i0 + l32 < M) ? a.A[((int64_t)b * M + i0 + l32) * kr + k] * kLog2e : 0.0f;
-    }
-    split8<PH>(x, bA[kc]);
+      for (int p = 0; p < PH; ++p) bA[kc][p] = ldfrag(ap + (kc * PH + p) * kFrag, lb);
   }
   float Zp = 0.0f, Sp = 0.0f;
   f32x16_t U, W;
 #pragma unroll
   for (int r = 0; r < 16; ++r) U[r] = W[r] = 0.0f;
+
+  struct Ld {
+    bf16x8_t bh[KC][PH];   // h form of B_b (first operand of h^T: rows j)
+    bf16x8_t bu[2][PG];    // u form of B_b (first operand of U^T, W^T: rows k)
+    float4 ev[4];          // e[j, b] at rows j0 + g*8 + h*4 .. +3
+  };
+  auto load = [&](int jb, Ld& L) {
+    const uint16_t* r = Bp + (int64_t)jb * PK::FB * kFrag;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+      for (int p = 0; p < PH; ++p) L.bh[kc][p] = ldfrag(r + (kc * PH + p) * kFrag, lb);
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int p = 0; p < PG; ++p) L.bu[cc][p] = ldfrag(r + (KC * PH + cc * PG + p) * kFrag, lb);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) L.ev[g] = ld4(Eb + jb * 32 + g * 8 + h * 4);
+  };
 
   for (int c0 = 0; c0 < N; c0 += kChunkF) {
     // weights of the strip, zero outside the block (rows >= M, columns >= N)
@@ -154,64 +339,45 @@ __global__ __launch_bounds__(256) void k_lr_fwd(LRArgs a) {
     }
     __syncthreads();
     if (!act) continue;
-    // global operands of one 32-child block, loaded a block ahead
-    struct Ld {
-      float xh[KC][8];    // B_b[k, j] for h^T: row j = j0 + l32, k = kc*16 + h*8 + e
-      float4 ev[4];       // e[j, b] at rows j0 + g*8 + h*4 .. +3
-      float xb[2][8];     // B_b[k, j] for U, W: row k = l32, K chunk cc
-    };
-    auto load = [&](int j0, Ld& L) {
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int k = kc * 16 + h * 8 + e;
-          L.xh[kc][e] = (k < kr && j0 + l32 < N) ? Bb[(int64_t)k * N + j0 + l32] : 0.0f;
-        }
-#pragma unroll
-      for (int g = 0; g < 4; ++g) L.ev[g] = ld4(Eb + j0 + g * 8 + h * 4);
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int j = j0 + 16 * cc + (e / 4) * 8 + h * 4 + (e % 4);
-          L.xb[cc][e] = (l32 < kr && j < N) ? Bb[(int64_t)l32 * N + j] : 0.0f;
-        }
-    };
-    const int nb = cw / 32;
-    // one 32-child block from the operands in `cur`, with the block two ahead
-    // loaded into the other buffer meanwhile (ping-pong: no register copies)
-    auto block = [&](int jb, const Ld& cur, Ld& fill) {
-      const int j0 = c0 + jb * 32;
-      if (jb + 1 < nb) load(j0 + 32, fill);
-      // h^T[j, i] = sum_k B_b[k, j] A_b[i, k]: first operand rows j = j0 + l32
+    const int nb = cw / 32, jb0 = c0 / 32;
+    const float* srow = slab + l32 * CP + h * 4;
+    // one 32-child block from the operands in `cur`, the next block loading
+    // into the other buffer meanwhile (ping-pong: no register copies).  The
+    // load is unconditional (the last block reloads itself) so that the count
+    // of loads in flight is the same on every path and the wait before the
+    // next block's matrix instructions leaves this block's loads outstanding.
+    // A block past the strip's last one (odd block counts: the second half
+    // of the last pair) runs on the reloaded last block with zero weights.
+    auto block = [&](int jl, const Ld& cur, Ld& fill) {
+      // no instruction moves across a block boundary: the scheduler would
+      // otherwise hoist the next block's work next to the loads feeding it
+      __builtin_amdgcn_sched_barrier(0);
+      load(jb0 + min(jl + 1, nb - 1), fill);
+      const float live = jl < nb ? 1.0f : 0.0f;
+      const int jc = min(jl, nb - 1);
+      // h^T[j, i] = sum_k B_b[k, j] A_b[i, k] log2(e)
       f32x16_t H;
 #pragma unroll
       for (int r = 0; r < 16; ++r) H[r] = 0.0f;
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        bf16x8_t pb[PH];
-        split8<PH>(cur.xh[kc], pb);
-        mfma_planes<PH>(H, pb, bA[kc]);
-      }
+      for (int kc = 0; kc < KC; ++kc) mfma_planes<PH>(H, cur.bh[kc], bA[kc]);
       // register r: row j = j0 + (r/4)*8 + h*4 + r%4, column i = i0 + l32
       float q[16], qe[16];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int jr = g * 8 + h * 4;
-        const float4 th = *(const float4*)&slab[l32 * CP + (j0 - c0) + jr];
+        const float4 th = *(const float4*)(srow + jc * 32 + g * 8);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = g * 4 + e;
-          q[r] = at4(th, e) * __builtin_amdgcn_exp2f(H[r]);
+          q[r] = (at4(th, e) * live) * __builtin_amdgcn_exp2f(H[r]);
           qe[r] = q[r] * at4(cur.ev[g], e);
           Zp += q[r];
           Sp += qe[r];
         }
       }
-      // U[k, i] += sum_j B_b[k, j] qe[j, i], W[k, i] += sum_j B_b[k, j] q[j, i]:
-      // the second operand is the accumulator itself (K index 8h + e of chunk cc
-      // is register 8cc + e, row j0 + 16cc + (e/4)*8 + h*4 + e%4)
+      // U^T[k, i] += sum_j B_b[k, j] qe[j, i], W^T[k, i] += sum_j B_b[k, j] q[j, i]:
+      // the second operand is the accumulator itself (K index 8h + e of chunk
+      // cc is register 8cc + e), the u form follows the same order of j
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
         float xq[8], xw[8];
@@ -220,19 +386,19 @@ __global__ __launch_bounds__(256) void k_lr_fwd(LRArgs a) {
           xq[e] = qe[8 * cc + e];
           xw[e] = q[8 * cc + e];
         }
-        bf16x8_t pb[PG], pq[PG], pw[PG];
-        split8<PG>(cur.xb[cc], pb);
+        bf16x8_t pq[PG], pw[PG];
         split8<PG>(xq, pq);
         split8<PG>(xw, pw);
-        mfma_planes<PG>(U, pb, pq);
-        mfma_planes<PG>(W, pb, pw);
+        mfma_planes<PG>(U, cur.bu[cc], pq);
+        mfma_planes<PG>(W, cur.bu[cc], pw);
       }
+      __builtin_amdgcn_sched_barrier(0);
     };
-    Ld b0, b1;
-    load(c0, b0);
-    for (int jb = 0; jb < nb; jb += 2) {
-      block(jb, b0, b1);
-      if (jb + 1 < nb) block(jb + 1, b1, b0);
+    Ld L0, L1;
+    load(jb0, L0);
+    for (int jl = 0; jl < nb; jl += 2) {
+      block(jl, L0, L1);
+      block(jl + 1, L1, L0);
     }
   }
   const float Z = Zp + __shfl_xor(Zp, 32), S = Sp + __shfl_xor(Sp, 32);
@@ -255,211 +421,193 @@ __global__ __launch_bounds__(256) void k_lr_fwd(LRArgs a) {
   }
 }
 
-// c1 = f / Sraw, c2 = f / Z per (sample, row); zero where the flow is zero or
-// the node's value is -inf (Sraw = 0 or Z = 0).
-__global__ void k_lr_coef(LRArgs a) {
-  const int64_t n = (int64_t)a.B * a.M;
-  for (int64_t x = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; x < n; x += (int64_t)gridDim.x * blockDim.x) {
-    const int b = (int)(x / a.M), i = (int)(x - (int64_t)b * a.M);
-    const float f = a.flows[(int64_t)(a.out_start + i) * a.B + b];
-    const float Z = a.Z[x], S = a.S[x];
-    const bool ok = f != 0.0f && Z > 0.0f && S > 0.0f;
-    a.C1[x] = ok ? f / S : 0.0f;
-    a.C2[x] = ok ? f / Z : 0.0f;
-  }
-}
-
-// Backward: workgroup = 32 children x 8 samples (two per wave), all rows.
+// Backward: workgroup = 32 children x 8 samples (8 waves, one sample each),
+// all rows.  The transposed weights of the column strip are staged in LDS; a
+// wave streams its sample's A records and coefficients one row block ahead.
+// The parameter flows of each 32 x 32 tile are summed over the 8 waves in
+// order (through one of two LDS exchange tiles, so one barrier per row block
+// suffices) and added to the workgroup's partial matrix, whose tile is read a
+// row block ahead so that the read overlaps the block's work.
 template <int PH, int PG, int KC>
-__global__ __launch_bounds__(256) void k_lr_bwd(LRArgs a) {
+__global__ __launch_bounds__(512) void k_lr_bwd(LRArgs a) {
+  using PK = LrPack<PH, PG, KC>;
   __shared__ __attribute__((aligned(16))) float slab[kSlabB];   // theta^T [32][R + 4]
-  __shared__ float xch[4][1024];                                 // parameter flows of a 32 x 32 tile per wave
+  __shared__ float xch[2][8][1024];                              // per wave: parameter flows of a 32 x 32 tile
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nt = (a.N + 31) / 32;
-  const int j0 = (blockIdx.x % nt) * 32, sg = blockIdx.x / nt;
+  const int jb = blockIdx.x % nt, j0 = jb * 32, sg = blockIdx.x / nt;
   const int M = a.M, N = a.N, kr = a.krank;
-  int bs[2];
-  bool act[2];
-  bs[0] = sg * 8 + wave;
-  bs[1] = sg * 8 + 4 + wave;
-  act[0] = bs[0] < a.B;
-  act[1] = bs[1] < a.B;
-  // second operand of h, per sample: B_b[k, j], j = j0 + l32
-  bf16x8_t bB[2][KC][PH];
-  float ev[2];
+  const int b = sg * 8 + wave;
+  const bool act = b < a.B;
+  const int bq = act ? b : 0;
+  const uint32_t lb = (uint32_t)lane * 16;
+  // second operand of h: the h form of B_b for this column strip
+  bf16x8_t bB[KC][PH];
+  {
+    const uint16_t* bp = PK::bside(a, bq, jb);
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const float* Bb = a.Bf + (int64_t)(act[s] ? bs[s] : 0) * kr * N;
+    for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int k = kc * 16 + h * 8 + e;
-        x[e] = (act[s] && k < kr && j0 + l32 < N) ? Bb[(int64_t)k * N + j0 + l32] : 0.0f;
-      }
-      split8<PH>(x, bB[s][kc]);
-    }
-    ev[s] = act[s] ? a.E[(int64_t)bs[s] * a.ldE + a.e_koff + j0 + l32] : 0.0f;   // zero past N
+      for (int p = 0; p < PH; ++p) bB[kc][p] = ldfrag(bp + (kc * PH + p) * kFrag, lb);
   }
-  float fcp[2] = {0.0f, 0.0f};
-  f32x16_t dB[2];
+  const float ev = act ? a.E[(int64_t)b * a.ldE + a.e_koff + j0 + l32] : 0.0f;   // zero past N
+  float fcp = 0.0f;
+  f32x16_t dB;
 #pragma unroll
-  for (int s = 0; s < 2; ++s)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) dB[s][r] = 0.0f;
+  for (int r = 0; r < 16; ++r) dB[r] = 0.0f;
   float* P = a.P + (int64_t)sg * M * N;
+  const int ldC = (M + 31) / 32 * 32;
+  const float* C1 = a.C1 + (int64_t)bq * ldC + h * 4;   // rows padded with zeros to ldC
+  const float* C2 = a.C2 + (int64_t)bq * ldC + h * 4;
+  const uint16_t* Ap = PK::aside(a, bq, 0);             // row block ib at + ib * FB * kFrag
+  // this thread's two entries of a parameter-flow tile: rows pr[u] of the
+  // block, column pj
+  int pr[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int x = tid + u * 512, r = x >> 6, ll = x & 63;
+    pr[u] = (r / 4) * 8 + (ll >> 5) * 4 + (r % 4);
+  }
+  const int pj = j0 + (tid & 31);
+
+  struct Ld {
+    bf16x8_t ah[KC][PH];   // h form of A_b (first operand of h: rows i)
+    bf16x8_t ad[2][PG];    // d form of A_b (first operand of dB: rows k)
+    float4 c1[4], c2[4];   // rows ib*32 + g*8 + h*4 .. +3
+  };
+  auto load = [&](int ib, Ld& L) {
+    const uint16_t* r = Ap + (int64_t)ib * PK::FB * kFrag;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+      for (int p = 0; p < PH; ++p) L.ah[kc][p] = ldfrag(r + (kc * PH + p) * kFrag, lb);
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int p = 0; p < PG; ++p) L.ad[cc][p] = ldfrag(r + (KC * PH + cc * PG + p) * kFrag, lb);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      L.c1[g] = ld4(C1 + ib * 32 + g * 8);
+      L.c2[g] = ld4(C2 + ib * 32 + g * 8);
+    }
+  };
+  auto pload = [&](int ib, float (&po)[2]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {   // clamped address, always loaded
+      const int i = min(ib * 32 + pr[u], M - 1);
+      po[u] = P[(int64_t)i * N + min(pj, N - 1)];
+    }
+  };
 
   for (int r0 = 0; r0 < M; r0 += kChunkB) {
     // transposed weights of the strip, zero outside the block
     const int rw = (min(kChunkB, M - r0) + 31) / 32 * 32, RP = rw + 4;
     __syncthreads();
-    for (int base = tid; base < rw * 32; base += 256 * 8) {   // 8 loads in flight per thread
-      float v[8];
+    for (int base = tid; base < rw * 32; base += 512 * 4) {   // 4 loads in flight per thread
+      float v[4];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int idx = base + u * 256, ii = idx >> 5, jj = idx & 31;
+      for (int u = 0; u < 4; ++u) {
+        const int idx = base + u * 512, ii = idx >> 5, jj = idx & 31;
         v[u] = (idx < rw * 32 && r0 + ii < M && j0 + jj < N) ? a.theta[(int64_t)(r0 + ii) * N + j0 + jj] : 0.0f;
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int idx = base + u * 256, ii = idx >> 5, jj = idx & 31;
+      for (int u = 0; u < 4; ++u) {
+        const int idx = base + u * 512, ii = idx >> 5, jj = idx & 31;
         if (idx < rw * 32) slab[jj * RP + ii] = v[u];
       }
     }
     __syncthreads();
-    // global operands of one (32-row block, sample) step, loaded a step ahead
-    struct Ld {
-      float xa[KC][8];    // A_b[i, k] log2(e) for h: row i = i0 + l32, k = kc*16 + h*8 + e
-      float c1[16], c2[16];
-      float xk[2][8];     // A_b[i, k] for dB: row k = l32, K chunk cc
-    };
-    auto load = [&](int i0, int s, Ld& L) {
-      const int b = bs[s];
-      const float* Ab = a.A + (int64_t)b * M * kr;
+    const int nrb = rw / 32, ib0 = r0 / 32;
+    const float* srow = slab + l32 * RP + h * 4;
+    // row block il from `cur` (row block il + 1 loading into `fill`, its
+    // partial tile into `pn`), exchange tile xb
+    auto blockk = [&](int il, const Ld& cur, Ld& fill, const float (&po)[2], float (&pn)[2], int xb) {
+      // unconditional loads (the last block reloads itself; an idle wave
+      // reads sample 0): the same count in flight on every path; no
+      // instruction moves across a block boundary
+      __builtin_amdgcn_sched_barrier(0);
+      load(ib0 + min(il + 1, nrb - 1), fill);
+      pload(ib0 + min(il + 1, nrb - 1), pn);
+      const int i0 = (ib0 + il) * 32;
+      float* xw = &xch[xb][wave][lane];
+      if (act) {
+        // h[i, j] = sum_k A_b[i, k] log2(e) B_b[k, j]
+        f32x16_t H;
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc)
+        for (int r = 0; r < 16; ++r) H[r] = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int k = kc * 16 + h * 8 + e;
-          L.xa[kc][e] = (k < kr && i0 + l32 < M) ? Ab[(int64_t)(i0 + l32) * kr + k] * kLog2e : 0.0f;
+        for (int kc = 0; kc < KC; ++kc) mfma_planes<PH>(H, cur.ah[kc], bB[kc]);
+        // register r: row i = i0 + (r/4)*8 + h*4 + r%4, column j = j0 + l32
+        float X[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 th = *(const float4*)(srow + il * 32 + g * 8);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = g * 4 + e;
+            const float q = at4(th, e) * __builtin_amdgcn_exp2f(H[r]);
+            const float u1 = ev * at4(cur.c1[g], e);
+            const float eps = q * u1;
+            X[r] = q * (u1 - at4(cur.c2[g], e));
+            fcp += eps;
+            xw[r * 64] = eps;
+          }
         }
+        // dB[k, j] += sum_i A_b[i, k] X[i, j]: K index 8h + e of chunk cc is
+        // register 8cc + e (the d form follows the same order of i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = i0 + (r / 4) * 8 + h * 4 + (r % 4);
-        L.c1[r] = i < M ? a.C1[(int64_t)b * M + i] : 0.0f;
-        L.c2[r] = i < M ? a.C2[(int64_t)b * M + i] : 0.0f;
-      }
+        for (int cc = 0; cc < 2; ++cc) {
+          float xx[8];
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int i = i0 + 16 * cc + (e / 4) * 8 + h * 4 + (e % 4);
-          L.xk[cc][e] = (l32 < kr && i < M) ? Ab[(int64_t)i * kr + l32] : 0.0f;
+          for (int e = 0; e < 8; ++e) xx[e] = X[8 * cc + e];
+          bf16x8_t px[PG];
+          split8<PG>(xx, px);
+          mfma_planes<PG>(dB, cur.ad[cc], px);
         }
-    };
-    // the wave's steps: (row block ib, sample s) for its active samples
-    const int nsteps = (rw / 32) * (act[1] ? 2 : act[0] ? 1 : 0);
-    const int per = act[1] ? 2 : 1;
-    Ld buf[2];
-    if (nsteps > 0) load(r0, 0, buf[0]);
-    for (int ib = 0; ib < rw / 32; ++ib) {
-      const int i0 = r0 + ib * 32;
-      float fp[16];
+      } else {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) fp[r] = 0.0f;
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {      // static sample index: the per-sample operands stay in registers
-        if (s >= per || nsteps == 0) continue;
-        const int t = ib * per + s;
-        // ping-pong: step t reads buf[t & 1] and fills the other with step t + 1
-        auto stepk = [&](const Ld& cur, Ld& fill) {
-          if (t + 1 < nsteps) load(r0 + ((t + 1) / per) * 32, (t + 1) % per, fill);
-          // h[i, j] = sum_k A_b[i, k] B_b[k, j]: first operand rows i = i0 + l32
-          f32x16_t H;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) H[r] = 0.0f;
-#pragma unroll
-          for (int kc = 0; kc < KC; ++kc) {
-            bf16x8_t pa[PH];
-            split8<PH>(cur.xa[kc], pa);
-            mfma_planes<PH>(H, pa, bB[s][kc]);
-          }
-          // register r: row i = i0 + (r/4)*8 + h*4 + r%4, column j = j0 + l32
-          float X[16];
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int ir = g * 8 + h * 4;
-            const float4 th = *(const float4*)&slab[l32 * RP + (i0 - r0) + ir];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = g * 4 + e;
-              const float q = at4(th, e) * __builtin_amdgcn_exp2f(H[r]);
-              const float eps = q * ev[s] * cur.c1[r];
-              X[r] = q * (ev[s] * cur.c1[r] - cur.c2[r]);
-              fcp[s] += eps;
-              fp[r] += eps;
-            }
-          }
-          // dB[k, j] += sum_i A_b[i, k] X[i, j]: K index 8h + e of chunk cc is
-          // register 8cc + e, row i0 + 16cc + (e/4)*8 + h*4 + e%4
-#pragma unroll
-          for (int cc = 0; cc < 2; ++cc) {
-            float xx[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) xx[e] = X[8 * cc + e];
-            bf16x8_t pa[PG], px[PG];
-            split8<PG>(cur.xk[cc], pa);
-            split8<PG>(xx, px);
-            mfma_planes<PG>(dB[s], pa, px);
-          }
-        };
-        if (t & 1) stepk(buf[1], buf[0]);
-        else stepk(buf[0], buf[1]);
+        for (int r = 0; r < 16; ++r) xw[r * 64] = 0.0f;
       }
+      __syncthreads();
       // parameter flows of the tile, summed over the waves in order
 #pragma unroll
-      for (int r = 0; r < 16; ++r) xch[wave][r * 64 + lane] = fp[r];
-      __syncthreads();
-      for (int x = tid; x < 1024; x += 256) {
-        const int r = x >> 6, ll = x & 63;
-        const float v = ((xch[0][x] + xch[1][x]) + xch[2][x]) + xch[3][x];
-        const int i = i0 + (r / 4) * 8 + (ll >> 5) * 4 + (r % 4), j = j0 + (ll & 31);
-        if (i < M && j < N) P[(int64_t)i * N + j] += v;
+      for (int u = 0; u < 2; ++u) {
+        const int x = tid + u * 512;
+        float v = xch[xb][0][x];
+#pragma unroll
+        for (int w = 1; w < 8; ++w) v += xch[xb][w][x];
+        const int i = i0 + pr[u];
+        if (i < M && pj < N) P[(int64_t)i * N + pj] = po[u] + v;
       }
-      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    Ld L0, L1;
+    float p0[2], p1[2];
+    load(ib0, L0);
+    pload(ib0, p0);
+    for (int il = 0; il < nrb; il += 2) {
+      blockk(il, L0, L1, p0, p1, 0);
+      if (il + 1 < nrb) blockk(il + 1, L1, L0, p1, p0, 1);
     }
   }
   // child flows, dB
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const float tot = fcp[s] + __shfl_xor(fcp[s], 32);
-    const int b = bs[s], j = j0 + l32;
-    if (!act[s] || j >= N) continue;
-    if (h == 0) {
-      if (a.scratch_row >= 0) {
-        a.scratch[(int64_t)(a.scratch_row + j) * a.B + b] = tot;
-      } else {
-        const int child = a.chblocks[a.blk_off + j / a.cbs] + j % a.cbs;
-        float* dst = a.out_flows + (int64_t)child * a.B + b;
-        *dst = a.store ? tot : *dst + tot;
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int k = (r / 4) * 8 + h * 4 + (r % 4);
-      if (k < kr) a.dB[((int64_t)b * kr + k) * N + j] = dB[s][r];
+  const float tot = fcp + __shfl_xor(fcp, 32);
+  const int j = j0 + l32;
+  if (!act || j >= N) return;
+  if (h == 0) {
+    if (a.scratch_row >= 0) {
+      a.scratch[(int64_t)(a.scratch_row + j) * a.B + b] = tot;
+    } else {
+      const int child = a.chblocks[a.blk_off + j / a.cbs] + j % a.cbs;
+      float* dst = a.out_flows + (int64_t)child * a.B + b;
+      *dst = a.store ? tot : *dst + tot;
     }
   }
-}
-
-// dLL/dA_b[i, k] = c1[i] U[i, k] - c2[i] W[i, k]
-__global__ void k_lr_dA(LRArgs a) {
-  const int64_t n = (int64_t)a.B * a.M * a.krank;
-  for (int64_t x = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; x < n; x += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t bi = x / a.krank;
-    a.dA[x] = a.C1[bi] * a.U[x] - a.C2[bi] * a.W[x];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int k = (r / 4) * 8 + h * 4 + (r % 4);
+    if (k < kr) a.dB[((int64_t)b * kr + k) * N + j] = dB[r];
   }
 }
 
@@ -478,11 +626,21 @@ static int grid_lr(int64_t n) {
   return (int)(g < 1 ? 1 : g > 65536 ? 65536 : g);
 }
 
-void launch_lr_exp(const LRArgs& a, hipStream_t s) {
+// Precision of the fused kernels: h with PH planes per operand, the gradient
+// products with PG (auto: 2 and 1; fp32-level: 3 and 3); KC K chunks of 16
+// cover the rank.
+template <int PH, int PG>
+static void lr_prep_k(const LRArgs& a, int backward, hipStream_t s) {
   const int ncols = (a.N + 31) / 32 * 32;
-  hipLaunchKernelGGL(k_lr_exp, dim3(((ncols + 63) / 64) * ((a.B + 63) / 64)), dim3(256), 0, s, a);
+  const int nE = (ncols / 32) * ((a.B + 31) / 32);
+  const int KC = a.krank <= 16 ? 1 : 2;
+  const int64_t nsets = (int64_t)a.B * ((a.N + 31) / 32 + (a.M + 31) / 32) * (KC + 2);
+  const int nP = (int)((nsets + 3) / 4);
+  const int nC = backward ? (int)(((int64_t)a.B * ((a.M + 31) / 32 * 32) + 255) / 256) : 0;
+  const dim3 grid(nE + nP + nC);
+  if (KC == 1) hipLaunchKernelGGL((k_lr_prep<PH, PG, 1>), grid, dim3(256), 0, s, a, backward);
+  else hipLaunchKernelGGL((k_lr_prep<PH, PG, 2>), grid, dim3(256), 0, s, a, backward);
 }
-
 template <int PH, int PG>
 static void lr_fwd_k(const LRArgs& a, hipStream_t s) {
   const dim3 grid(((a.M + 31) / 32) * ((a.B + 3) / 4));
@@ -492,23 +650,25 @@ static void lr_fwd_k(const LRArgs& a, hipStream_t s) {
 template <int PH, int PG>
 static void lr_bwd_k(const LRArgs& a, hipStream_t s) {
   const dim3 grid(((a.N + 31) / 32) * ((a.B + 7) / 8));
-  if (a.krank <= 16) hipLaunchKernelGGL((k_lr_bwd<PH, PG, 1>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((k_lr_bwd<PH, PG, 2>), grid, dim3(256), 0, s, a);
+  if (a.krank <= 16) hipLaunchKernelGGL((k_lr_bwd<PH, PG, 1>), grid, dim3(512), 0, s, a);
+  else hipLaunchKernelGGL((k_lr_bwd<PH, PG, 2>), grid, dim3(512), 0, s, a);
 }
 
+int64_t lr_pack_bytes(int B, int M, int N, int krank, int fp32) {
+  const int PH = fp32 ? 3 : 2, PG = fp32 ? 3 : 1, KC = krank <= 16 ? 1 : 2;
+  return (int64_t)B * ((N + 31) / 32 + (M + 31) / 32) * (KC * PH + 2 * PG) * kFrag * 2;
+}
+void launch_lr_prep(const LRArgs& a, int fp32, int backward, hipStream_t s) {
+  if (fp32) lr_prep_k<3, 3>(a, backward, s);
+  else lr_prep_k<2, 1>(a, backward, s);
+}
 void launch_lr_fwd(const LRArgs& a, int fp32, hipStream_t s) {
   if (fp32) lr_fwd_k<3, 3>(a, s);
   else lr_fwd_k<2, 1>(a, s);
 }
-void launch_lr_coef(const LRArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_lr_coef, dim3(grid_lr((int64_t)a.B * a.M)), dim3(256), 0, s, a);
-}
 void launch_lr_bwd(const LRArgs& a, int fp32, hipStream_t s) {
   if (fp32) lr_bwd_k<3, 3>(a, s);
   else lr_bwd_k<2, 1>(a, s);
-}
-void launch_lr_dA(const LRArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_lr_dA, dim3(grid_lr((int64_t)a.B * a.M * a.krank)), dim3(256), 0, s, a);
 }
 void launch_lr_fplus(const float* P, int nsg, int64_t elems, float* pflows, hipStream_t s) {
   hipLaunchKernelGGL(k_lr_fplus, dim3(grid_lr(elems)), dim3(256), 0, s, P, nsg, elems, pflows);

@@ -245,9 +245,10 @@ WsPlan plan_workspace(const Handle* h, int B) {
   p.lrS = take(lr ? (size_t)h->lr_rows * Bs * 4 : 0);
   p.lrU = take(lr ? (size_t)h->lr_rows * Bs * kr * 4 : 0);
   p.lrW = take(lr ? (size_t)h->lr_rows * Bs * kr * 4 : 0);
-  p.lrC1 = take(lr ? (size_t)h->lr_max_m * Bs * 4 : 0);
-  p.lrC2 = take(lr ? (size_t)h->lr_max_m * Bs * 4 : 0);
+  p.lrC1 = take(lr ? (size_t)round_up(h->lr_max_m, 32) * Bs * 4 : 0);   // rows padded to 32 (zeros)
+  p.lrC2 = take(lr ? (size_t)round_up(h->lr_max_m, 32) * Bs * 4 : 0);
   p.lrP = take(lr ? (size_t)p.lr_nsg * h->lr_p_elems * 4 : 0);
+  p.lrPK = take(lr ? (size_t)lr_pack_bytes(B, h->lr_max_m, h->lr_max_n, (int)kr, p.mode == PC_PREC_FP32) : 0);
   p.lowrank = lr0;
   p.lowrank_bytes = off - lr0;
   p.total = off;
@@ -420,6 +421,7 @@ LRArgs lr_args(const Call& c, const SumPlan& sp, int g, const pc_lowrank_io* io,
   a.C1 = (float*)(base + c.p.lrC1);
   a.C2 = (float*)(base + c.p.lrC2);
   a.P = (float*)(base + c.p.lrP) + h->lr_p_off[r.block] * c.p.lr_nsg;
+  a.pk = (uint16_t*)(base + c.p.lrPK);
   if (io->dA) a.dA = io->dA[r.lowrank];
   if (io->dB) a.dB = io->dB[r.lowrank];
   return a;
@@ -686,7 +688,7 @@ int pc_forward(pc_handle hh, int batch, const int32_t* tokens, const float* para
             LRArgs la = lr_args(c, sp, gi, lowrank, params, node_vals, nullptr);
             {
               Timed t(h, KK_EXP, c.s);
-              launch_lr_exp(la, c.s);
+              launch_lr_prep(la, p.mode == PC_PREC_FP32, 0, c.s);
             }
             Timed t(h, KK_LRFWD, c.s);
             launch_lr_fwd(la, p.mode == PC_PREC_FP32, c.s);
@@ -833,13 +835,12 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
         for (int gi = 0; gi < (int)sp.groups.size(); ++gi) {
           LRArgs la = lr_args(c, sp, gi, lowrank, params, vals, node_flows);
           {
-            Timed t(h, KK_EXP, c.s);   // the forward reuses one buffer for every layer's exp
-            launch_lr_exp(la, c.s);
+            // the forward reuses one buffer for every layer's exp and records
+            Timed t(h, KK_EXP, c.s);
+            launch_lr_prep(la, p.mode == PC_PREC_FP32, 1, c.s);
           }
           Timed t(h, KK_LRBWD, c.s);
-          launch_lr_coef(la, c.s);
           launch_lr_bwd(la, p.mode == PC_PREC_FP32, c.s);
-          launch_lr_dA(la, c.s);
         }
         if (sp.overlap) {
           SumArgs ra = sum_common(c, sp);

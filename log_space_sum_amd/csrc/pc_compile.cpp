@@ -425,6 +425,7 @@ Handle* compile_layout(const pc_circuit_desc* d) {
       sp.lr_row.push_back(h->lr_rows);
       h->lr_rows += r.M;
       h->lr_max_m = std::max(h->lr_max_m, r.M);
+      h->lr_max_n = std::max(h->lr_max_n, r.N);
       if (h->lr_p_off[r.block] < 0) {
         h->lr_p_off[r.block] = h->lr_p_elems;
         h->lr_p_elems += (int64_t)r.M * r.N;

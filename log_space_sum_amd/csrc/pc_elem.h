@@ -103,8 +103,10 @@ struct EmArgs {
 // One LowRank exp_sum group (k_lowrank.hip).  Row-major weights theta [M, N];
 // factors A [B, M, krank], Bf [B, krank, N] (the slot's tensors); E: exp of
 // the children, float32 [B, ldE] at column e_koff; Z, S: [B, M] kept by the
-// forward; U, W: [B, M, krank] kept by the forward; C1, C2: [B, M]; P: the
-// group's block of ceil(B/8) parameter-flow partials [ceil(B/8), M, N].
+// forward; U, W: [B, M, krank] kept by the forward; C1, C2: [B, M rounded up
+// to 32] (zero past M); P: the
+// group's block of ceil(B/8) parameter-flow partials [ceil(B/8), M, N]; pk:
+// the factors' fragment records of the current layer (lr_pack_bytes).
 struct LRArgs {
   int32_t B, M, N, krank;
   int32_t out_start, m_row, e_koff, ldE, cbs, blk_off, scratch_row, store;
@@ -127,13 +129,16 @@ struct LRArgs {
   float* P;
   float* dA;
   float* dB;
+  uint16_t* pk;
 };
 
-void launch_lr_exp(const LRArgs& a, hipStream_t s);
+// Bytes of the fragment records of one group's factors (per layer, reused).
+int64_t lr_pack_bytes(int B, int M, int N, int krank, int fp32);
+// Per layer and pass: exp of the children and the factors' fragment records;
+// with backward also c1, c2 and dLL/dA.
+void launch_lr_prep(const LRArgs& a, int fp32, int backward, hipStream_t s);
 void launch_lr_fwd(const LRArgs& a, int fp32, hipStream_t s);
-void launch_lr_coef(const LRArgs& a, hipStream_t s);
 void launch_lr_bwd(const LRArgs& a, int fp32, hipStream_t s);
-void launch_lr_dA(const LRArgs& a, hipStream_t s);
 void launch_lr_fplus(const float* P, int nsg, int64_t elems, float* pflows, hipStream_t s);
 
 void launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);

@@ -127,6 +127,7 @@ struct Handle {
   int32_t lowrank_slots = 0;
   int64_t lr_rows = 0;                 // LowRank: rows of the kept Z/S/U/W records (sum of group M)
   int32_t lr_max_m = 0;                // LowRank: largest group M (per-layer coefficients)
+  int32_t lr_max_n = 0;                // LowRank: largest group N
   int64_t lr_p_elems = 0;              // LowRank: elements of the distinct LowRank weight blocks
   std::vector<int64_t> lr_p_off;       // per weight block: offset of its LowRank partials, -1 if none
   std::vector<RowSeg> rowsegs;
@@ -167,6 +168,7 @@ struct WsPlan {
   int pl[3][2];
   size_t theta, thetaT, ebt, gbt, earena, garena, mkeys, ssum, scratch, tokT, bptr, bidx, lowrank;
   size_t lrE, lrZ, lrS, lrU, lrW, lrC1, lrC2, lrP;   // LowRank regions (float32)
+  size_t lrPK;                                       // LowRank fragment records of the current layer
   int lr_nsg;                                        // LowRank parameter-flow partials: ceil(B/8)
   size_t partials, counters;
   int64_t partial_elems;
