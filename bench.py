@@ -97,6 +97,7 @@ def bench_lowrank(args):
     dev = "cuda:0"
     h = L.pc_compile_layout(circ, device=0)
     L.pc_set_precision(h, args.mode)
+    L.pc_set_option(h, "lr_pack", args.lr_pack)
     params = torch.tensor(cfg["params"], device=dev)
     tokens = torch.tensor(cfg["tokens"], device=dev)
     vals = torch.empty((circ.num_nodes, B), device=dev)
@@ -190,6 +191,8 @@ def main():
     ap.add_argument("--split-max", type=int, default=8, help="largest K split of a per-layer product")
     ap.add_argument("--param-chunk", type=int, default=0,
                     help="tied copies per parameter-flow launch on a second stream (0: one launch at the end)")
+    ap.add_argument("--lr-pack", type=int, default=0, choices=[0, 1],
+                    help="LowRank factor records: 0 made once per forward, 1 per layer and pass")
     ap.add_argument("--fuse", type=int, default=1, choices=[0, 1],
                     help="1: product layers inside the adjacent sum layers' memory-bound kernels; 0: own launches")
     ap.add_argument("--copy-calibration", type=int, default=0,

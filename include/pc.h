@@ -210,7 +210,10 @@ int pc_set_split(pc_handle h, int mode, int gemm_kind, int planes_a, int planes_
  * handle, each as soon as its copies' scaled flows exist, overlapping the
  * element flows (deterministic; the float32 sum is grouped by chunk, so the
  * bits differ from n = 0).  pc_backward joins that stream into the caller's
- * before it returns.  Changing an option can change
+ * before it returns.  PC_OPT_LR_PACK: when the bfloat16 fragment records of
+ * the LowRank factors are made: 0 (default) all at once at the start of
+ * pc_forward, kept for pc_backward; 1 each group's just before its layer, in
+ * both passes (identical results).  Changing an option can change
  * pc_workspace_bytes.
  * Errors: PC_ERR_INVALID_ARG (unknown option or value). */
 #define PC_OPT_LAYER_TILE 0
@@ -218,6 +221,7 @@ int pc_set_split(pc_handle h, int mode, int gemm_kind, int planes_a, int planes_
 #define PC_OPT_SPLIT_MAX  2
 #define PC_OPT_FUSE       3
 #define PC_OPT_PARAM_CHUNK 4
+#define PC_OPT_LR_PACK    5
 int pc_set_option(pc_handle h, int option, int value);
 
 /* Bytes of workspace pc_forward / pc_backward need for `batch` samples in the

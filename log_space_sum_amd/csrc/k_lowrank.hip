@@ -39,7 +39,7 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 // weight slabs staged in LDS: 512 columns (forward) or 448 rows (backward) of
 // a 32-wide strip, so that two workgroups share a CU
-constexpr int kChunkF = 512, kChunkB = 448;
+constexpr int kChunkF = 512, kChunkB = 512;
 constexpr int kSlabF = 32 * (kChunkF + 4), kSlabB = 32 * (kChunkB + 4);
 
 __device__ __forceinline__ float key_to_shift_lr(uint32_t k) {
@@ -99,13 +99,13 @@ constexpr int kFrag = 512;   // bfloat16 elements per record
 template <int PH, int PG, int KC>
 struct LrPack {
   static constexpr int FB = KC * PH + 2 * PG;     // records per block
-  static __device__ __forceinline__ const uint16_t* bside(const LRArgs& a, int b, int jb) {
-    const int nJB = (a.N + 31) / 32;
-    return a.pk + ((int64_t)b * nJB + jb) * FB * kFrag;
+  static __device__ __forceinline__ const uint16_t* bside(const uint16_t* pk, int N, int b, int jb) {
+    const int nJB = (N + 31) / 32;
+    return pk + ((int64_t)b * nJB + jb) * FB * kFrag;
   }
-  static __device__ __forceinline__ const uint16_t* aside(const LRArgs& a, int b, int ib) {
-    const int nJB = (a.N + 31) / 32, nIB = (a.M + 31) / 32;
-    return a.pk + ((int64_t)a.B * nJB + (int64_t)b * nIB + ib) * FB * kFrag;
+  static __device__ __forceinline__ const uint16_t* aside(const uint16_t* pk, int Bn, int M, int N, int b, int ib) {
+    const int nJB = (N + 31) / 32, nIB = (M + 31) / 32;
+    return pk + ((int64_t)Bn * nJB + (int64_t)b * nIB + ib) * FB * kFrag;
   }
 };
 
@@ -125,124 +125,95 @@ __device__ __forceinline__ void split_store_frag(const float (&x)[8], uint16_t* 
   for (int p = 0; p < P; ++p) *(bf16x8_t*)(dst + p * kFrag) = o[p];
 }
 
-// One launch per LowRank group and pass, three roles by workgroup range:
-//  (1) e[j, b] = exp(v[child j, b] - m[b]), float32, sample-major [B][ldE] at
-//      column e_koff + j (zero for N <= j < N rounded up to 32); 32 children x
-//      32 samples per workgroup through an LDS transpose;
-//  (2) the fragment records of A_b and B_b (four record sets per workgroup);
-//  (3) backward only: c1 = f / Sraw, c2 = f / Z per (sample, row) (zero where
-//      the flow is zero or the node's value is -inf) and
-//      dLL/dA_b[i, k] = c1 U[i, k] - c2 W[i, k], one (sample, row) per thread.
+// The fragment records of every LowRank group of the circuit, made once per
+// forward and kept for the backward: workgroups [wg0[g], wg0[g + 1]) pack
+// group g, four record sets (64 lanes each) per workgroup.
 template <int PH, int PG, int KC>
-__global__ __launch_bounds__(256) void k_lr_prep(LRArgs a, int backward) {
+__global__ __launch_bounds__(256) void k_lr_pack(LRPackArgs pa) {
   using PK = LrPack<PH, PG, KC>;
-  __shared__ float t[32][33];
   const int tid = threadIdx.x;
-  const int ncols = (a.N + 31) / 32 * 32;
-  const int nEj = ncols / 32, nE = nEj * ((a.B + 31) / 32);
-  const int nJB = (a.N + 31) / 32, nIB = (a.M + 31) / 32;
-  const int64_t nsets = (int64_t)a.B * (nJB + nIB) * (KC + 2);
-  const int nP = (int)((nsets + 3) / 4);
-  int wg = blockIdx.x;
-  if (wg < nE) {
-    const int j0 = (wg % nEj) * 32, b0 = (wg / nEj) * 32;
-    {
-      const int jj = tid >> 3, bq = (tid & 7) * 4, j = j0 + jj;
-      const int child = j < a.N ? a.chblocks[a.blk_off + j / a.cbs] + j % a.cbs : 0;
+  int g = 0;
+  while (g + 1 < pa.ngroups && (int)blockIdx.x >= pa.wg0[g + 1]) ++g;
+  const int M = pa.M[g], N = pa.N[g], Bn = pa.B, kr = pa.krank;
+  const int nJB = (N + 31) / 32, nIB = (M + 31) / 32;
+  const int64_t nsets = (int64_t)Bn * (nJB + nIB) * (KC + 2);
+  const int64_t set = (int64_t)(blockIdx.x - pa.wg0[g]) * 4 + (tid >> 6);
+  if (set >= nsets) return;
+  const int lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+  const int form = (int)(set % (KC + 2));
+  const int64_t rest = set / (KC + 2);
+  const int blk = (int)(rest % (nJB + nIB)), b = (int)(rest / (nJB + nIB));
+  float x[8];
+  if (blk < nJB) {
+    const int jb = blk;
+    const float* Bb = pa.Bf[g] + (int64_t)b * kr * N;
+    uint16_t* dst = const_cast<uint16_t*>(PK::bside(pa.pk[g], N, b, jb)) + lane * 8;
+    if (form < KC) {
+      const int j = jb * 32 + l32;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int b = b0 + bq + e;
-        float v = 0.0f;
-        if (j < a.N && b < a.B)
-          v = expf(a.vals[(int64_t)child * a.B + b] - key_to_shift_lr(a.mkeys[(int64_t)a.m_row * a.B + b]));
-        t[jj][bq + e] = v;
+      for (int e = 0; e < 8; ++e) {
+        const int k = form * 16 + h * 8 + e;
+        x[e] = (k < kr && j < N) ? Bb[(int64_t)k * N + j] : 0.0f;
       }
-    }
-    __syncthreads();
-    const int bb = tid >> 3, jq = (tid & 7) * 4, b = b0 + bb;
-    if (b < a.B)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) a.E[(int64_t)b * a.ldE + a.e_koff + j0 + jq + e] = t[jq + e][bb];   // zeros past N
-    return;
-  }
-  wg -= nE;
-  if (wg < nP) {
-    const int64_t set = (int64_t)wg * 4 + (tid >> 6);
-    if (set >= nsets) return;
-    const int lane = tid & 63, l32 = lane & 31, h = lane >> 5;
-    const int form = (int)(set % (KC + 2));
-    const int64_t rest = set / (KC + 2);
-    const int blk = (int)(rest % (nJB + nIB)), b = (int)(rest / (nJB + nIB));
-    const int kr = a.krank;
-    float x[8];
-    if (blk < nJB) {
-      const int jb = blk;
-      const float* Bb = a.Bf + (int64_t)b * kr * a.N;
-      uint16_t* dst = const_cast<uint16_t*>(PK::bside(a, b, jb)) + lane * 8;
-      if (form < KC) {
-        const int j = jb * 32 + l32;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int k = form * 16 + h * 8 + e;
-          x[e] = (k < kr && j < a.N) ? Bb[(int64_t)k * a.N + j] : 0.0f;
-        }
-        split_store_frag<PH>(x, dst + form * PH * kFrag);
-      } else {
-        const int cc = form - KC;
-        const int jq = jb * 32 + 16 * cc + h * 4;     // values e of runs jq + (e/4)*8 + e%4
-        if ((a.N & 3) == 0 && l32 < kr && jq + 11 < a.N) {
-          const float4 u0 = ld4(Bb + (int64_t)l32 * a.N + jq), u1 = ld4(Bb + (int64_t)l32 * a.N + jq + 8);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            x[e] = at4(u0, e);
-            x[4 + e] = at4(u1, e);
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int j = jq + (e / 4) * 8 + (e % 4);
-            x[e] = (l32 < kr && j < a.N) ? Bb[(int64_t)l32 * a.N + j] : 0.0f;
-          }
-        }
-        split_store_frag<PG>(x, dst + (KC * PH + cc * PG) * kFrag);
-      }
+      split_store_frag<PH>(x, dst + form * PH * kFrag);
     } else {
-      const int ib = blk - nJB;
-      const float* Ab = a.A + (int64_t)b * a.M * kr;
-      uint16_t* dst = const_cast<uint16_t*>(PK::aside(a, b, ib)) + lane * 8;
-      if (form < KC) {
-        const int i = ib * 32 + l32, k0 = form * 16 + h * 8;
-        if ((kr & 3) == 0 && i < a.M && k0 + 8 <= kr) {
-          const float4 u0 = ld4(Ab + (int64_t)i * kr + k0), u1 = ld4(Ab + (int64_t)i * kr + k0 + 4);
+      const int cc = form - KC;
+      const int jq = jb * 32 + 16 * cc + h * 4;     // values e of runs jq + (e/4)*8 + e%4
+      if ((N & 3) == 0 && l32 < kr && jq + 11 < N) {
+        const float4 u0 = ld4(Bb + (int64_t)l32 * N + jq), u1 = ld4(Bb + (int64_t)l32 * N + jq + 8);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            x[e] = at4(u0, e) * kLog2e;
-            x[4 + e] = at4(u1, e) * kLog2e;
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int k = k0 + e;
-            x[e] = (k < kr && i < a.M) ? Ab[(int64_t)i * kr + k] * kLog2e : 0.0f;
-          }
+        for (int e = 0; e < 4; ++e) {
+          x[e] = at4(u0, e);
+          x[4 + e] = at4(u1, e);
         }
-        split_store_frag<PH>(x, dst + form * PH * kFrag);
       } else {
-        const int cc = form - KC;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int i = ib * 32 + 16 * cc + (e / 4) * 8 + h * 4 + (e % 4);
-          x[e] = (l32 < kr && i < a.M) ? Ab[(int64_t)i * kr + l32] : 0.0f;
+          const int j = jq + (e / 4) * 8 + (e % 4);
+          x[e] = (l32 < kr && j < N) ? Bb[(int64_t)l32 * N + j] : 0.0f;
         }
-        split_store_frag<PG>(x, dst + (KC * PH + cc * PG) * kFrag);
       }
+      split_store_frag<PG>(x, dst + (KC * PH + cc * PG) * kFrag);
     }
-    return;
+  } else {
+    const int ib = blk - nJB;
+    const float* Ab = pa.A[g] + (int64_t)b * M * kr;
+    uint16_t* dst = const_cast<uint16_t*>(PK::aside(pa.pk[g], Bn, M, N, b, ib)) + lane * 8;
+    if (form < KC) {
+      const int i = ib * 32 + l32, k0 = form * 16 + h * 8;
+      if ((kr & 3) == 0 && i < M && k0 + 8 <= kr) {
+        const float4 u0 = ld4(Ab + (int64_t)i * kr + k0), u1 = ld4(Ab + (int64_t)i * kr + k0 + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[e] = at4(u0, e) * kLog2e;
+          x[4 + e] = at4(u1, e) * kLog2e;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int k = k0 + e;
+          x[e] = (k < kr && i < M) ? Ab[(int64_t)i * kr + k] * kLog2e : 0.0f;
+        }
+      }
+      split_store_frag<PH>(x, dst + form * PH * kFrag);
+    } else {
+      const int cc = form - KC;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = ib * 32 + 16 * cc + (e / 4) * 8 + h * 4 + (e % 4);
+        x[e] = (l32 < kr && i < M) ? Ab[(int64_t)i * kr + l32] : 0.0f;
+      }
+      split_store_frag<PG>(x, dst + (KC * PH + cc * PG) * kFrag);
+    }
   }
-  wg -= nP;
-  if (!backward) return;
+}
+
+// Backward coefficients, one (sample, row) per thread over rows padded to 32:
+// c1 = f / Sraw, c2 = f / Z (zero where the flow is zero or the node's value
+// is -inf, and on the padding rows) and dLL/dA_b[i, k] = c1 U[i, k] - c2 W[i, k].
+__global__ __launch_bounds__(256) void k_lr_coef(LRArgs a) {
   const int ldC = (a.M + 31) / 32 * 32;
-  const int64_t xc = (int64_t)wg * 256 + tid;
+  const int64_t xc = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (xc >= (int64_t)a.B * ldC) return;
   const int b = (int)(xc / ldC), i = (int)(xc - (int64_t)b * ldC);
   if (i >= a.M) {
@@ -269,28 +240,32 @@ __global__ __launch_bounds__(256) void k_lr_prep(LRArgs a, int backward) {
   }
 }
 
-// Forward: workgroup = 32 rows x 4 samples (one per wave), all children.
-// The weights of the row strip are staged in LDS (shared by the 4 samples);
-// a wave streams its sample's B records and e one 32-child block ahead.
+// Forward: workgroup = 32 rows x 4 samples (one per wave), all children, in
+// chunks of kChunkF children.  Per chunk the weights of the row strip and
+// e[j, b] = exp(v[child j, b] - m[b]) of the 4 samples are staged in LDS; a
+// wave streams its sample's B records one 32-child block ahead.
 template <int PH, int PG, int KC>
 __global__ __launch_bounds__(256) void k_lr_fwd(LRArgs a) {
   using PK = LrPack<PH, PG, KC>;
   __shared__ __attribute__((aligned(16))) float slab[kSlabF];   // theta rows [32][C + 4]
+  __shared__ __attribute__((aligned(16))) float el[4][kChunkF]; // e of the chunk, per sample
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int mt = (a.M + 31) / 32;
-  const int ib = blockIdx.x % mt, i0 = ib * 32, b = (blockIdx.x / mt) * 4 + wave;
+  const int ib = blockIdx.x % mt, i0 = ib * 32, b0 = (blockIdx.x / mt) * 4, b = b0 + wave;
   const bool act = b < a.B;
   const int M = a.M, N = a.N, kr = a.krank;
   const int bq = act ? b : 0;
-  const float* Eb = a.E + (int64_t)bq * a.ldE + a.e_koff;
-  const uint16_t* Bp = PK::bside(a, bq, 0);                  // block jb at + jb * FB * kFrag
+  const uint16_t* Bp = PK::bside(a.pk, N, bq, 0);           // block jb at + jb * FB * kFrag
   const uint32_t lb = (uint32_t)lane * 16;
+  // this thread's sample for staging e: b0 + (tid & 3), its shift
+  const int es = tid & 3;
+  const float esh = b0 + es < a.B ? key_to_shift_lr(a.mkeys[(int64_t)a.m_row * a.B + b0 + es]) : 0.0f;
 
   // second operand of h^T: the h form of A_b for this row strip
   bf16x8_t bA[KC][PH];
   {
-    const uint16_t* ap = PK::aside(a, bq, ib);
+    const uint16_t* ap = PK::aside(a.pk, a.B, M, N, bq, ib);
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
@@ -304,7 +279,6 @@ __global__ __launch_bounds__(256) void k_lr_fwd(LRArgs a) {
   struct Ld {
     bf16x8_t bh[KC][PH];   // h form of B_b (first operand of h^T: rows j)
     bf16x8_t bu[2][PG];    // u form of B_b (first operand of U^T, W^T: rows k)
-    float4 ev[4];          // e[j, b] at rows j0 + g*8 + h*4 .. +3
   };
   auto load = [&](int jb, Ld& L) {
     const uint16_t* r = Bp + (int64_t)jb * PK::FB * kFrag;
@@ -316,31 +290,65 @@ __global__ __launch_bounds__(256) void k_lr_fwd(LRArgs a) {
     for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
       for (int p = 0; p < PG; ++p) L.bu[cc][p] = ldfrag(r + (KC * PH + cc * PG + p) * kFrag, lb);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) L.ev[g] = ld4(Eb + jb * 32 + g * 8 + h * 4);
   };
 
   for (int c0 = 0; c0 < N; c0 += kChunkF) {
     // weights of the strip, zero outside the block (rows >= M, columns >= N)
     const int cw = (min(kChunkF, N - c0) + 31) / 32 * 32, CP = cw + 4;
     __syncthreads();
-    for (int base = tid; base < 32 * cw; base += 256 * 8) {   // 8 loads in flight per thread
-      float v[8];
+    // item = (row r, 4 columns c): 16-byte loads when rows are 16-byte
+    // aligned and the 4 columns are inside the block; 4 items in flight
+    for (int base = tid; base < 32 * (kChunkF / 4); base += 256 * 4) {
+      float4 v[4];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int idx = base + u * 256, r = idx / cw, c = idx - r * cw;
-        v[u] = (idx < 32 * cw && i0 + r < M && c0 + c < N) ? a.theta[(int64_t)(i0 + r) * N + c0 + c] : 0.0f;
+      for (int u = 0; u < 4; ++u) {
+        const int idx = base + u * 256, r = idx / (kChunkF / 4), c = (idx % (kChunkF / 4)) * 4;
+        const float* src = a.theta + (int64_t)(i0 + r) * N + c0 + c;
+        v[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (c < cw && i0 + r < M) {
+          if ((N & 3) == 0 && c0 + c + 3 < N) {
+            v[u] = ld4(src);
+          } else {
+            v[u].x = c0 + c < N ? src[0] : 0.0f;
+            v[u].y = c0 + c + 1 < N ? src[1] : 0.0f;
+            v[u].z = c0 + c + 2 < N ? src[2] : 0.0f;
+            v[u].w = c0 + c + 3 < N ? src[3] : 0.0f;
+          }
+        }
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int idx = base + u * 256, r = idx / cw, c = idx - r * cw;
-        if (idx < 32 * cw) slab[r * CP + c] = v[u];
+      for (int u = 0; u < 4; ++u) {
+        const int idx = base + u * 256, r = idx / (kChunkF / 4), c = (idx % (kChunkF / 4)) * 4;
+        if (c < cw) *(float4*)&slab[r * CP + c] = v[u];
+      }
+    }
+    // e of the chunk: thread t takes child columns c = t/4 + 64 u, sample es
+    // (the 4 samples of a child are one 16-byte run of its value row); every
+    // index and value load of the chunk in flight before the first exp
+    {
+      constexpr int U8 = kChunkF / 64;
+      int child[U8];
+      float v[U8];
+#pragma unroll
+      for (int u = 0; u < U8; ++u) {
+        const int j = c0 + (tid >> 2) + 64 * u;
+        child[u] = (j < N) ? a.chblocks[a.blk_off + j / a.cbs] + j % a.cbs : -1;
+      }
+      const bool bin = b0 + es < a.B;
+#pragma unroll
+      for (int u = 0; u < U8; ++u)
+        v[u] = (child[u] >= 0 && bin) ? a.vals[(int64_t)child[u] * a.B + b0 + es] : -INFINITY;
+#pragma unroll
+      for (int u = 0; u < U8; ++u) {
+        const int c = (tid >> 2) + 64 * u;
+        if (c < cw) el[es][c] = (child[u] >= 0 && bin) ? expf(v[u] - esh) : 0.0f;
       }
     }
     __syncthreads();
     if (!act) continue;
     const int nb = cw / 32, jb0 = c0 / 32;
     const float* srow = slab + l32 * CP + h * 4;
+    const float* erow = el[wave] + h * 4;
     // one 32-child block from the operands in `cur`, the next block loading
     // into the other buffer meanwhile (ping-pong: no register copies).  The
     // load is unconditional (the last block reloads itself) so that the count
@@ -366,11 +374,12 @@ __global__ __launch_bounds__(256) void k_lr_fwd(LRArgs a) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const float4 th = *(const float4*)(srow + jc * 32 + g * 8);
+        const float4 ev = *(const float4*)(erow + jc * 32 + g * 8);   // e at rows j0 + g*8 + h*4 .. +3
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = g * 4 + e;
           q[r] = (at4(th, e) * live) * __builtin_amdgcn_exp2f(H[r]);
-          qe[r] = q[r] * at4(cur.ev[g], e);
+          qe[r] = q[r] * at4(ev, e);
           Zp += q[r];
           Sp += qe[r];
         }
@@ -445,13 +454,18 @@ __global__ __launch_bounds__(512) void k_lr_bwd(LRArgs a) {
   // second operand of h: the h form of B_b for this column strip
   bf16x8_t bB[KC][PH];
   {
-    const uint16_t* bp = PK::bside(a, bq, jb);
+    const uint16_t* bp = PK::bside(a.pk, N, bq, jb);
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
       for (int p = 0; p < PH; ++p) bB[kc][p] = ldfrag(bp + (kc * PH + p) * kFrag, lb);
   }
-  const float ev = act ? a.E[(int64_t)b * a.ldE + a.e_koff + j0 + l32] : 0.0f;   // zero past N
+  // e[j, b] = exp(v[child j, b] - m[b]) of this lane's child (zero past N)
+  float ev = 0.0f;
+  if (act && j0 + l32 < N) {
+    const int j = j0 + l32, child = a.chblocks[a.blk_off + j / a.cbs] + j % a.cbs;
+    ev = expf(a.vals[(int64_t)child * a.B + b] - key_to_shift_lr(a.mkeys[(int64_t)a.m_row * a.B + b]));
+  }
   float fcp = 0.0f;
   f32x16_t dB;
 #pragma unroll
@@ -460,7 +474,7 @@ __global__ __launch_bounds__(512) void k_lr_bwd(LRArgs a) {
   const int ldC = (M + 31) / 32 * 32;
   const float* C1 = a.C1 + (int64_t)bq * ldC + h * 4;   // rows padded with zeros to ldC
   const float* C2 = a.C2 + (int64_t)bq * ldC + h * 4;
-  const uint16_t* Ap = PK::aside(a, bq, 0);             // row block ib at + ib * FB * kFrag
+  const uint16_t* Ap = PK::aside(a.pk, a.B, M, N, bq, 0);   // row block ib at + ib * FB * kFrag
   // this thread's two entries of a parameter-flow tile: rows pr[u] of the
   // block, column pj
   int pr[2];
@@ -471,12 +485,14 @@ __global__ __launch_bounds__(512) void k_lr_bwd(LRArgs a) {
   }
   const int pj = j0 + (tid & 31);
 
-  struct Ld {
+  struct Fr {
     bf16x8_t ah[KC][PH];   // h form of A_b (first operand of h: rows i)
     bf16x8_t ad[2][PG];    // d form of A_b (first operand of dB: rows k)
+  };
+  struct Cf {
     float4 c1[4], c2[4];   // rows ib*32 + g*8 + h*4 .. +3
   };
-  auto load = [&](int ib, Ld& L) {
+  auto loadF = [&](int ib, Fr& L) {
     const uint16_t* r = Ap + (int64_t)ib * PK::FB * kFrag;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc)
@@ -486,6 +502,8 @@ __global__ __launch_bounds__(512) void k_lr_bwd(LRArgs a) {
     for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
       for (int p = 0; p < PG; ++p) L.ad[cc][p] = ldfrag(r + (KC * PH + cc * PG + p) * kFrag, lb);
+  };
+  auto loadC = [&](int ib, Cf& L) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       L.c1[g] = ld4(C1 + ib * 32 + g * 8);
@@ -501,94 +519,124 @@ __global__ __launch_bounds__(512) void k_lr_bwd(LRArgs a) {
   };
 
   for (int r0 = 0; r0 < M; r0 += kChunkB) {
-    // transposed weights of the strip, zero outside the block
+    // transposed weights of the strip, zero outside the block: item = (row
+    // ii, 4 columns jq), one 16-byte load when the row is 16-byte aligned
     const int rw = (min(kChunkB, M - r0) + 31) / 32 * 32, RP = rw + 4;
     __syncthreads();
-    for (int base = tid; base < rw * 32; base += 512 * 4) {   // 4 loads in flight per thread
-      float v[4];
+    for (int base = tid; base < rw * 8; base += 512 * 4) {
+      float4 v[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int idx = base + u * 512, ii = idx >> 5, jj = idx & 31;
-        v[u] = (idx < rw * 32 && r0 + ii < M && j0 + jj < N) ? a.theta[(int64_t)(r0 + ii) * N + j0 + jj] : 0.0f;
+        const int idx = base + u * 512, ii = idx >> 3, jq = (idx & 7) * 4;
+        const float* src = a.theta + (int64_t)(r0 + ii) * N + j0 + jq;
+        v[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (idx < rw * 8 && r0 + ii < M) {
+          if ((N & 3) == 0 && j0 + jq + 3 < N) {
+            v[u] = ld4(src);
+          } else {
+            v[u].x = j0 + jq < N ? src[0] : 0.0f;
+            v[u].y = j0 + jq + 1 < N ? src[1] : 0.0f;
+            v[u].z = j0 + jq + 2 < N ? src[2] : 0.0f;
+            v[u].w = j0 + jq + 3 < N ? src[3] : 0.0f;
+          }
+        }
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int idx = base + u * 512, ii = idx >> 5, jj = idx & 31;
-        if (idx < rw * 32) slab[jj * RP + ii] = v[u];
+        const int idx = base + u * 512, ii = idx >> 3, jq = (idx & 7) * 4;
+        if (idx < rw * 8) {
+          slab[(jq + 0) * RP + ii] = v[u].x;
+          slab[(jq + 1) * RP + ii] = v[u].y;
+          slab[(jq + 2) * RP + ii] = v[u].z;
+          slab[(jq + 3) * RP + ii] = v[u].w;
+        }
       }
     }
     __syncthreads();
     const int nrb = rw / 32, ib0 = r0 / 32;
     const float* srow = slab + l32 * RP + h * 4;
-    // row block il from `cur` (row block il + 1 loading into `fill`, its
-    // partial tile into `pn`), exchange tile xb
-    auto blockk = [&](int il, const Ld& cur, Ld& fill, const float (&po)[2], float (&pn)[2], int xb) {
-      // unconditional loads (the last block reloads itself; an idle wave
-      // reads sample 0): the same count in flight on every path; no
-      // instruction moves across a block boundary
+    auto clampb = [&](int il) { return ib0 + min(il, nrb - 1); };
+    // row block il from fragments `fc` (row block il + 3 loading into `ff`)
+    // and coefficients `cc_` (row block il + 1 loading into `cn`, its
+    // partial tile into `pn`), exchange tile xb.  Loads are unconditional (the
+    // last block reloads itself; an idle wave reads sample 0), so the count in
+    // flight is the same on every path; blocks past the last one (the end of
+    // an unrolled group) only load.  No instruction moves across a block
+    // boundary.
+    auto blockk = [&](int il, const Fr& fc, Fr& ff, const Cf& cc_, Cf& cn, const float (&po)[2], float (&pn)[2],
+                      int xb) {
       __builtin_amdgcn_sched_barrier(0);
-      load(ib0 + min(il + 1, nrb - 1), fill);
-      pload(ib0 + min(il + 1, nrb - 1), pn);
-      const int i0 = (ib0 + il) * 32;
-      float* xw = &xch[xb][wave][lane];
-      if (act) {
-        // h[i, j] = sum_k A_b[i, k] log2(e) B_b[k, j]
-        f32x16_t H;
+      loadF(clampb(il + 3), ff);
+      loadC(clampb(il + 1), cn);
+      pload(clampb(il + 1), pn);
+      if (il < nrb) {
+        const int i0 = (ib0 + il) * 32;
+        float* xw = &xch[xb][wave][lane];
+        if (act) {
+          // h[i, j] = sum_k A_b[i, k] log2(e) B_b[k, j]
+          f32x16_t H;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) H[r] = 0.0f;
+          for (int r = 0; r < 16; ++r) H[r] = 0.0f;
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) mfma_planes<PH>(H, cur.ah[kc], bB[kc]);
-        // register r: row i = i0 + (r/4)*8 + h*4 + r%4, column j = j0 + l32
-        float X[16];
+          for (int kc = 0; kc < KC; ++kc) mfma_planes<PH>(H, fc.ah[kc], bB[kc]);
+          // register r: row i = i0 + (r/4)*8 + h*4 + r%4, column j = j0 + l32
+          float X[16];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const float4 th = *(const float4*)(srow + il * 32 + g * 8);
+          for (int g = 0; g < 4; ++g) {
+            const float4 th = *(const float4*)(srow + il * 32 + g * 8);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = g * 4 + e;
-            const float q = at4(th, e) * __builtin_amdgcn_exp2f(H[r]);
-            const float u1 = ev * at4(cur.c1[g], e);
-            const float eps = q * u1;
-            X[r] = q * (u1 - at4(cur.c2[g], e));
-            fcp += eps;
-            xw[r * 64] = eps;
+            for (int e = 0; e < 4; ++e) {
+              const int r = g * 4 + e;
+              const float q = at4(th, e) * __builtin_amdgcn_exp2f(H[r]);
+              const float u1 = ev * at4(cc_.c1[g], e);
+              const float eps = q * u1;
+              X[r] = q * (u1 - at4(cc_.c2[g], e));
+              fcp += eps;
+              xw[r * 64] = eps;
+            }
           }
+          // dB[k, j] += sum_i A_b[i, k] X[i, j]: K index 8h + e of chunk cc is
+          // register 8cc + e (the d form follows the same order of i)
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc) {
+            float xx[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xx[e] = X[8 * cc + e];
+            bf16x8_t px[PG];
+            split8<PG>(xx, px);
+            mfma_planes<PG>(dB, fc.ad[cc], px);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) xw[r * 64] = 0.0f;
         }
-        // dB[k, j] += sum_i A_b[i, k] X[i, j]: K index 8h + e of chunk cc is
-        // register 8cc + e (the d form follows the same order of i)
+        __syncthreads();
+        // parameter flows of the tile, summed over the waves in order
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          float xx[8];
+        for (int u = 0; u < 2; ++u) {
+          const int x = tid + u * 512;
+          float v = xch[xb][0][x];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) xx[e] = X[8 * cc + e];
-          bf16x8_t px[PG];
-          split8<PG>(xx, px);
-          mfma_planes<PG>(dB, cur.ad[cc], px);
+          for (int w = 1; w < 8; ++w) v += xch[xb][w][x];
+          const int i = i0 + pr[u];
+          if (i < M && pj < N) P[(int64_t)i * N + pj] = po[u] + v;
         }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) xw[r * 64] = 0.0f;
-      }
-      __syncthreads();
-      // parameter flows of the tile, summed over the waves in order
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int x = tid + u * 512;
-        float v = xch[xb][0][x];
-#pragma unroll
-        for (int w = 1; w < 8; ++w) v += xch[xb][w][x];
-        const int i = i0 + pr[u];
-        if (i < M && pj < N) P[(int64_t)i * N + pj] = po[u] + v;
       }
       __builtin_amdgcn_sched_barrier(0);
     };
-    Ld L0, L1;
+    Fr F0, F1, F2, F3;
+    Cf Ca, Cb;
     float p0[2], p1[2];
-    load(ib0, L0);
-    pload(ib0, p0);
-    for (int il = 0; il < nrb; il += 2) {
-      blockk(il, L0, L1, p0, p1, 0);
-      if (il + 1 < nrb) blockk(il + 1, L1, L0, p1, p0, 1);
+    loadF(clampb(0), F0);
+    loadF(clampb(1), F1);
+    loadF(clampb(2), F2);
+    loadC(clampb(0), Ca);
+    pload(clampb(0), p0);
+    for (int il = 0; il < nrb; il += 4) {
+      blockk(il, F0, F3, Ca, Cb, p0, p1, 0);
+      blockk(il + 1, F1, F0, Cb, Ca, p1, p0, 1);
+      blockk(il + 2, F2, F1, Ca, Cb, p0, p1, 0);
+      blockk(il + 3, F3, F2, Cb, Ca, p1, p0, 1);
     }
   }
   // child flows, dB
@@ -630,18 +678,6 @@ static int grid_lr(int64_t n) {
 // products with PG (auto: 2 and 1; fp32-level: 3 and 3); KC K chunks of 16
 // cover the rank.
 template <int PH, int PG>
-static void lr_prep_k(const LRArgs& a, int backward, hipStream_t s) {
-  const int ncols = (a.N + 31) / 32 * 32;
-  const int nE = (ncols / 32) * ((a.B + 31) / 32);
-  const int KC = a.krank <= 16 ? 1 : 2;
-  const int64_t nsets = (int64_t)a.B * ((a.N + 31) / 32 + (a.M + 31) / 32) * (KC + 2);
-  const int nP = (int)((nsets + 3) / 4);
-  const int nC = backward ? (int)(((int64_t)a.B * ((a.M + 31) / 32 * 32) + 255) / 256) : 0;
-  const dim3 grid(nE + nP + nC);
-  if (KC == 1) hipLaunchKernelGGL((k_lr_prep<PH, PG, 1>), grid, dim3(256), 0, s, a, backward);
-  else hipLaunchKernelGGL((k_lr_prep<PH, PG, 2>), grid, dim3(256), 0, s, a, backward);
-}
-template <int PH, int PG>
 static void lr_fwd_k(const LRArgs& a, hipStream_t s) {
   const dim3 grid(((a.M + 31) / 32) * ((a.B + 3) / 4));
   if (a.krank <= 16) hipLaunchKernelGGL((k_lr_fwd<PH, PG, 1>), grid, dim3(256), 0, s, a);
@@ -658,9 +694,26 @@ int64_t lr_pack_bytes(int B, int M, int N, int krank, int fp32) {
   const int PH = fp32 ? 3 : 2, PG = fp32 ? 3 : 1, KC = krank <= 16 ? 1 : 2;
   return (int64_t)B * ((N + 31) / 32 + (M + 31) / 32) * (KC * PH + 2 * PG) * kFrag * 2;
 }
-void launch_lr_prep(const LRArgs& a, int fp32, int backward, hipStream_t s) {
-  if (fp32) lr_prep_k<3, 3>(a, backward, s);
-  else lr_prep_k<2, 1>(a, backward, s);
+int lr_pack_workgroups(int B, int M, int N, int krank) {
+  const int KC = krank <= 16 ? 1 : 2;
+  const int64_t nsets = (int64_t)B * ((N + 31) / 32 + (M + 31) / 32) * (KC + 2);
+  return (int)((nsets + 3) / 4);
+}
+void launch_lr_pack(const LRPackArgs& pa, int fp32, hipStream_t s) {
+  if (pa.ngroups <= 0) return;
+  const dim3 grid(pa.wg0[pa.ngroups]);
+  const bool k2 = pa.krank > 16;
+  if (fp32) {
+    if (k2) hipLaunchKernelGGL((k_lr_pack<3, 3, 2>), grid, dim3(256), 0, s, pa);
+    else hipLaunchKernelGGL((k_lr_pack<3, 3, 1>), grid, dim3(256), 0, s, pa);
+  } else {
+    if (k2) hipLaunchKernelGGL((k_lr_pack<2, 1, 2>), grid, dim3(256), 0, s, pa);
+    else hipLaunchKernelGGL((k_lr_pack<2, 1, 1>), grid, dim3(256), 0, s, pa);
+  }
+}
+void launch_lr_coef(const LRArgs& a, hipStream_t s) {
+  const int64_t n = (int64_t)a.B * ((a.M + 31) / 32 * 32);
+  hipLaunchKernelGGL(k_lr_coef, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
 }
 void launch_lr_fwd(const LRArgs& a, int fp32, hipStream_t s) {
   if (fp32) lr_fwd_k<3, 3>(a, s);

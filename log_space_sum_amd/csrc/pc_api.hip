@@ -240,7 +240,6 @@ WsPlan plan_workspace(const Handle* h, int B) {
   const bool lr = h->lowrank_slots > 0;
   const size_t kr = (size_t)h->lowrank_rank;
   const size_t lr0 = off;
-  p.lrE = take(lr ? Bs * h->max_ebt_cols * 4 : 0);
   p.lrZ = take(lr ? (size_t)h->lr_rows * Bs * 4 : 0);
   p.lrS = take(lr ? (size_t)h->lr_rows * Bs * 4 : 0);
   p.lrU = take(lr ? (size_t)h->lr_rows * Bs * kr * 4 : 0);
@@ -248,7 +247,16 @@ WsPlan plan_workspace(const Handle* h, int B) {
   p.lrC1 = take(lr ? (size_t)round_up(h->lr_max_m, 32) * Bs * 4 : 0);   // rows padded to 32 (zeros)
   p.lrC2 = take(lr ? (size_t)round_up(h->lr_max_m, 32) * Bs * 4 : 0);
   p.lrP = take(lr ? (size_t)p.lr_nsg * h->lr_p_elems * 4 : 0);
-  p.lrPK = take(lr ? (size_t)lr_pack_bytes(B, h->lr_max_m, h->lr_max_n, (int)kr, p.mode == PC_PREC_FP32) : 0);
+  {
+    size_t pk = 0;
+    for (const auto& sp : h->sums)
+      for (const auto& r : sp.groups)
+        if (r.lowrank >= 0) {
+          p.lr_pk_off.push_back((int64_t)pk);
+          pk += (size_t)round_up(lr_pack_bytes(B, r.M, r.N, (int)kr, p.mode == PC_PREC_FP32), 256);
+        }
+    p.lrPK = take(pk);
+  }
   p.lowrank = lr0;
   p.lowrank_bytes = off - lr0;
   p.total = off;
@@ -398,8 +406,6 @@ LRArgs lr_args(const Call& c, const SumPlan& sp, int g, const pc_lowrank_io* io,
   a.krank = h->lowrank_rank;
   a.out_start = r.out_start;
   a.m_row = r.m_row;
-  a.e_koff = r.e_koff;
-  a.ldE = h->max_ebt_cols;
   a.cbs = r.cbs;
   a.blk_off = r.blk_off;
   a.scratch_row = r.scratch_row;
@@ -413,7 +419,6 @@ LRArgs lr_args(const Call& c, const SumPlan& sp, int g, const pc_lowrank_io* io,
   a.flows = flows;
   a.out_flows = flows;
   a.scratch = c.v.scratch;
-  a.E = (float*)(base + c.p.lrE);
   a.Z = (float*)(base + c.p.lrZ) + sp.lr_row[g] * B;
   a.S = (float*)(base + c.p.lrS) + sp.lr_row[g] * B;
   a.U = (float*)(base + c.p.lrU) + sp.lr_row[g] * B * kr;
@@ -421,10 +426,27 @@ LRArgs lr_args(const Call& c, const SumPlan& sp, int g, const pc_lowrank_io* io,
   a.C1 = (float*)(base + c.p.lrC1);
   a.C2 = (float*)(base + c.p.lrC2);
   a.P = (float*)(base + c.p.lrP) + h->lr_p_off[r.block] * c.p.lr_nsg;
-  a.pk = (uint16_t*)(base + c.p.lrPK);
+  a.pk = (uint16_t*)(base + c.p.lrPK + c.p.lr_pk_off[sp.lr_gidx[g]]);
   if (io->dA) a.dA = io->dA[r.lowrank];
   if (io->dB) a.dB = io->dB[r.lowrank];
   return a;
+}
+
+// Fragment records of LowRank group g of `sp`, in its own launch.
+void lr_pack_group(const Call& c, const SumPlan& sp, int g, const pc_lowrank_io* io) {
+  const GroupRec& r = sp.groups[g];
+  LRPackArgs pa{};
+  pa.B = c.v.B;
+  pa.krank = c.h->lowrank_rank;
+  pa.ngroups = 1;
+  pa.M[0] = r.M;
+  pa.N[0] = r.N;
+  pa.A[0] = io->A[r.lowrank];
+  pa.Bf[0] = io->B[r.lowrank];
+  pa.pk[0] = (uint16_t*)((char*)c.ws + c.p.lrPK + c.p.lr_pk_off[sp.lr_gidx[g]]);
+  pa.wg0[0] = 0;
+  pa.wg0[1] = lr_pack_workgroups(c.v.B, r.M, r.N, c.h->lowrank_rank);
+  launch_lr_pack(pa, c.p.mode == PC_PREC_FP32, c.s);
 }
 
 ProdArgs prod_args(const Call& c, const ProductPlan& pp) {
@@ -550,6 +572,9 @@ int pc_set_option(pc_handle hh, int option, int value) {
     } else if (option == PC_OPT_PARAM_CHUNK) {
       if (value < 0) fail(PC_ERR_INVALID_ARG, "parameter-flow chunk must be >= 0");
       h->opt_param_chunk = value;
+    } else if (option == PC_OPT_LR_PACK) {
+      if (value != 0 && value != 1) fail(PC_ERR_INVALID_ARG, "lr_pack must be 0 or 1");
+      h->opt_lr_pack = value;
     } else if (option == PC_OPT_FUSE) {
       if (value != 0 && value != 1) fail(PC_ERR_INVALID_ARG, "fuse must be 0 or 1");
       h->opt_fuse = value;
@@ -643,6 +668,33 @@ int pc_forward(pc_handle hh, int batch, const int32_t* tokens, const float* para
       Timed t(h, KK_OTHER, c.s);
       launch_fill_u32(v.counters, p.ncounters, 0u, c.s);
     }
+    if (h->lowrank_slots > 0 && h->opt_lr_pack == 0) {
+      // the fragment records of every LowRank group's factors, kept for the backward
+      LRPackArgs pa{};
+      pa.B = B;
+      pa.krank = h->lowrank_rank;
+      auto flush = [&]() {
+        if (pa.ngroups == 0) return;
+        Timed t(h, KK_SPLIT, c.s);
+        launch_lr_pack(pa, p.mode == PC_PREC_FP32, c.s);
+        pa.ngroups = 0;
+      };
+      for (const auto& sp : h->sums)
+        for (size_t gi = 0; gi < sp.groups.size(); ++gi) {
+          const GroupRec& r = sp.groups[gi];
+          if (r.lowrank < 0) continue;
+          const int q = pa.ngroups;
+          if (q == 0) pa.wg0[0] = 0;
+          pa.M[q] = r.M;
+          pa.N[q] = r.N;
+          pa.A[q] = lowrank->A[r.lowrank];
+          pa.Bf[q] = lowrank->B[r.lowrank];
+          pa.pk[q] = (uint16_t*)((char*)c.ws + p.lrPK + p.lr_pk_off[sp.lr_gidx[gi]]);
+          pa.wg0[q + 1] = pa.wg0[q] + lr_pack_workgroups(B, r.M, r.N, h->lowrank_rank);
+          if (++pa.ngroups == kMaxPackGroups) flush();
+        }
+      flush();
+    }
     for (const LayerRef& r : h->layers) {
       if (r.kind == PC_LAYER_INPUT_CAT) {
         InputArgs a = input_args(c, h->inputs[r.idx], params);
@@ -686,9 +738,9 @@ int pc_forward(pc_handle hh, int batch, const int32_t* tokens, const float* para
         if (sp.lowrank) {
           for (int gi = 0; gi < (int)sp.groups.size(); ++gi) {
             LRArgs la = lr_args(c, sp, gi, lowrank, params, node_vals, nullptr);
-            {
-              Timed t(h, KK_EXP, c.s);
-              launch_lr_prep(la, p.mode == PC_PREC_FP32, 0, c.s);
+            if (h->opt_lr_pack == 1) {
+              Timed t(h, KK_SPLIT, c.s);
+              lr_pack_group(c, sp, gi, lowrank);
             }
             Timed t(h, KK_LRFWD, c.s);
             launch_lr_fwd(la, p.mode == PC_PREC_FP32, c.s);
@@ -834,12 +886,12 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
         const SumPlan& sp = h->sums[r.idx];
         for (int gi = 0; gi < (int)sp.groups.size(); ++gi) {
           LRArgs la = lr_args(c, sp, gi, lowrank, params, vals, node_flows);
-          {
-            // the forward reuses one buffer for every layer's exp and records
-            Timed t(h, KK_EXP, c.s);
-            launch_lr_prep(la, p.mode == PC_PREC_FP32, 1, c.s);
+          if (h->opt_lr_pack == 1) {
+            Timed t(h, KK_SPLIT, c.s);
+            lr_pack_group(c, sp, gi, lowrank);
           }
           Timed t(h, KK_LRBWD, c.s);
+          launch_lr_coef(la, c.s);
           launch_lr_bwd(la, p.mode == PC_PREC_FP32, c.s);
         }
         if (sp.overlap) {

@@ -423,6 +423,7 @@ Handle* compile_layout(const pc_circuit_desc* d) {
     if (!sp.lowrank) continue;
     for (auto& r : sp.groups) {
       sp.lr_row.push_back(h->lr_rows);
+      sp.lr_gidx.push_back(h->lr_groups++);
       h->lr_rows += r.M;
       h->lr_max_m = std::max(h->lr_max_m, r.M);
       h->lr_max_n = std::max(h->lr_max_n, r.N);

@@ -101,15 +101,14 @@ struct EmArgs {
 };
 
 // One LowRank exp_sum group (k_lowrank.hip).  Row-major weights theta [M, N];
-// factors A [B, M, krank], Bf [B, krank, N] (the slot's tensors); E: exp of
-// the children, float32 [B, ldE] at column e_koff; Z, S: [B, M] kept by the
-// forward; U, W: [B, M, krank] kept by the forward; C1, C2: [B, M rounded up
-// to 32] (zero past M); P: the
-// group's block of ceil(B/8) parameter-flow partials [ceil(B/8), M, N]; pk:
-// the factors' fragment records of the current layer (lr_pack_bytes).
+// factors A [B, M, krank], Bf [B, krank, N] (the slot's tensors); Z, S: [B, M]
+// kept by the forward; U, W: [B, M, krank] kept by the forward; C1, C2: [B, M
+// rounded up to 32] (zero past M); P: the group's block of ceil(B/8)
+// parameter-flow partials [ceil(B/8), M, N]; pk: the group's fragment records
+// of the factors (lr_pack_bytes), made by the forward's pack launch.
 struct LRArgs {
   int32_t B, M, N, krank;
-  int32_t out_start, m_row, e_koff, ldE, cbs, blk_off, scratch_row, store;
+  int32_t out_start, m_row, cbs, blk_off, scratch_row, store;
   const int32_t* chblocks;
   const float* theta;
   const float* A;
@@ -119,7 +118,6 @@ struct LRArgs {
   const float* flows;
   float* out_flows;
   float* scratch;
-  float* E;
   float* Z;
   float* S;
   float* U;
@@ -132,11 +130,25 @@ struct LRArgs {
   uint16_t* pk;
 };
 
-// Bytes of the fragment records of one group's factors (per layer, reused).
+// Fragment packing of up to kMaxPackGroups LowRank groups in one launch:
+// group g takes workgroups [wg0[g], wg0[g + 1]).
+constexpr int kMaxPackGroups = 48;
+struct LRPackArgs {
+  int32_t B, krank, ngroups;
+  int32_t M[kMaxPackGroups], N[kMaxPackGroups];
+  int32_t wg0[kMaxPackGroups + 1];
+  const float* A[kMaxPackGroups];
+  const float* Bf[kMaxPackGroups];
+  uint16_t* pk[kMaxPackGroups];
+};
+
+// Bytes of the fragment records of one group's factors.
 int64_t lr_pack_bytes(int B, int M, int N, int krank, int fp32);
-// Per layer and pass: exp of the children and the factors' fragment records;
-// with backward also c1, c2 and dLL/dA.
-void launch_lr_prep(const LRArgs& a, int fp32, int backward, hipStream_t s);
+// Workgroups of one group's packing.
+int lr_pack_workgroups(int B, int M, int N, int krank);
+void launch_lr_pack(const LRPackArgs& pa, int fp32, hipStream_t s);
+// Backward per layer: c1, c2 and dLL/dA.
+void launch_lr_coef(const LRArgs& a, hipStream_t s);
 void launch_lr_fwd(const LRArgs& a, int fp32, hipStream_t s);
 void launch_lr_bwd(const LRArgs& a, int fp32, hipStream_t s);
 void launch_lr_fplus(const float* P, int nsg, int64_t elems, float* pflows, hipStream_t s);

@@ -72,6 +72,7 @@ struct SumPlan {
   int32_t max_npk = 0, max_mpk = 0;            // widest contraction of the forward / element flows
   std::vector<int32_t> red_child, red_ptr, red_src;   // overlap reduction CSR
   std::vector<int64_t> lr_row;                 // LowRank: first row of each group's Z/S/U/W records
+  std::vector<int32_t> lr_gidx;                // LowRank: index of each group among all LowRank groups
   // Adjacent product layers computed inside this layer's memory-bound kernels:
   // the one before it in the column-max kernel (forward), the one after it in
   // the scaled-flow packing (backward).
@@ -105,6 +106,7 @@ struct Handle {
   int planes[2][3][2] = {{{2, 1}, {2, 1}, {2, 1}}, {{3, 3}, {3, 3}, {3, 3}}};
   int opt_layer_tile = 0, opt_param_tile = 0, opt_split_max = 8, opt_fuse = 1;   // pc_set_option
   int opt_param_chunk = 0;             // tied copies per parameter-flow launch (0: one launch at the end)
+  int opt_lr_pack = 0;                 // LowRank fragment records: 0 once per forward, 1 per layer and pass
   std::vector<std::vector<int32_t>> copy_layer;   // per weight block: the layer of each tied copy
   void* side_stream = nullptr;         // parameter-flow chunks run here, beside the element flows
   std::vector<void*> chunk_events;
@@ -128,6 +130,7 @@ struct Handle {
   int64_t lr_rows = 0;                 // LowRank: rows of the kept Z/S/U/W records (sum of group M)
   int32_t lr_max_m = 0;                // LowRank: largest group M (per-layer coefficients)
   int32_t lr_max_n = 0;                // LowRank: largest group N
+  int32_t lr_groups = 0;               // LowRank: number of LowRank groups
   int64_t lr_p_elems = 0;              // LowRank: elements of the distinct LowRank weight blocks
   std::vector<int64_t> lr_p_off;       // per weight block: offset of its LowRank partials, -1 if none
   std::vector<RowSeg> rowsegs;
@@ -168,7 +171,8 @@ struct WsPlan {
   int pl[3][2];
   size_t theta, thetaT, ebt, gbt, earena, garena, mkeys, ssum, scratch, tokT, bptr, bidx, lowrank;
   size_t lrE, lrZ, lrS, lrU, lrW, lrC1, lrC2, lrP;   // LowRank regions (float32)
-  size_t lrPK;                                       // LowRank fragment records of the current layer
+  size_t lrPK;                                       // LowRank fragment records of every LowRank group
+  std::vector<int64_t> lr_pk_off;                    // per LowRank group: byte offset of its records
   int lr_nsg;                                        // LowRank parameter-flow partials: ceil(B/8)
   size_t partials, counters;
   int64_t partial_elems;
