@@ -345,39 +345,42 @@ __global__ void k_prod_bwd(ProdArgs a) {
 }
 
 // ---- sum layer: column maxima, exponentiated children, scaled flows -------------
-// Column maxima: a workgroup takes 64 children (one packing tile) x 64*V
-// samples; each wave reduces 16 children, the waves combine in LDS and one
-// integer atomic max per sample publishes the tile's maximum.  With PROD the
+// Column maxima: a workgroup takes 4*RW children (a part of one 64-child
+// packing tile) x 64*V samples; each wave reduces RW children, the waves
+// combine in LDS and one integer atomic max per sample publishes the
+// workgroup's maximum.  With PROD the
 // children that are nodes of the preceding product layer are evaluated here:
 // each is the sum of its own children in child-list order (as the product
 // kernel adds them), stored, and used for the maximum.  The loads of all 16
 // rows go out together, one child slot at a time.
-template <int V, bool PROD>
+template <int V, bool PROD, int RW>
 __global__ __launch_bounds__(256) void k_colmax(SumArgs a) {
   __shared__ float red[4][64 * V];
+  constexpr int NSUB = 16 / RW;              // workgroups per 64-child tile
   const int sbt = (a.B + 64 * V - 1) / (64 * V);
   const int t = blockIdx.x;
-  const int rt = t / sbt, st = t - rt * sbt;
+  const int st = t % sbt, rs = t / sbt, sub = rs % NSUB, rt = rs / NSUB;
   const int g = last_le(a.groups, a.ngroups, rt, [](const GroupRec& r) { return r.pk_start; });
   const GroupRec gr = a.groups[g];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int b = st * 64 * V + lane * V;
-  const int k0 = (rt - gr.pk_start) * 64 + w * 16;
+  const int kw = (rt - gr.pk_start) * 64 + sub * 4 * RW;   // the workgroup's first child
+  const int k0 = kw + w * RW;
   Row<V> m;
 #pragma unroll
   for (int e = 0; e < V; ++e) m.x[e] = -INFINITY;
   if (b < a.B) {
-    Row<V> c[16];
+    Row<V> c[RW];
     if constexpr (!PROD) {
 #pragma unroll
-      for (int kk = 0; kk < 16; ++kk)      // every load in flight at once
+      for (int kk = 0; kk < RW; ++kk)      // every load in flight at once
         if (k0 + kk < gr.N) c[kk].load(a.vals + (int64_t)child_of(gr, a.chblocks, k0 + kk) * a.B + b);
     } else {
-      int32_t node[16], q0[16], q1[16];
+      int32_t node[RW], q0[RW], q1[RW];
       if (a.fp_affine) {   // child q of product node i at fp_abase[q] + i: no index loads
-        bool isp[16];
+        bool isp[RW];
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk) {
+        for (int kk = 0; kk < RW; ++kk) {
           isp[kk] = false;
           if (k0 + kk < gr.N) {
             node[kk] = child_of(gr, a.chblocks, k0 + kk);
@@ -387,14 +390,14 @@ __global__ __launch_bounds__(256) void k_colmax(SumArgs a) {
             if (!isp[kk]) c[kk].load(a.vals + (int64_t)node[kk] * a.B + b);
           }
         }
-        Row<V> u[16][2];
+        Row<V> u[RW][2];
 #pragma unroll
-        for (int q = 0; q < 2; ++q)      // the first two child slots of all 16 rows at once
+        for (int q = 0; q < 2; ++q)      // the first two child slots of all RW rows at once
 #pragma unroll
-          for (int kk = 0; kk < 16; ++kk)
+          for (int kk = 0; kk < RW; ++kk)
             if (isp[kk] && q < a.fp_maxdeg) u[kk][q].load(a.vals + (int64_t)(a.fp_abase[q] + q0[kk]) * a.B + b);
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk)
+        for (int kk = 0; kk < RW; ++kk)
           if (isp[kk]) {
 #pragma unroll
             for (int e = 0; e < V; ++e) c[kk].x[e] = 0.0f;
@@ -406,20 +409,20 @@ __global__ __launch_bounds__(256) void k_colmax(SumArgs a) {
           }
         for (int q = 2; q < a.fp_maxdeg; ++q) {
 #pragma unroll
-          for (int kk = 0; kk < 16; ++kk)
+          for (int kk = 0; kk < RW; ++kk)
             if (isp[kk]) u[kk][0].load(a.vals + (int64_t)(a.fp_abase[q] + q0[kk]) * a.B + b);
 #pragma unroll
-          for (int kk = 0; kk < 16; ++kk)
+          for (int kk = 0; kk < RW; ++kk)
             if (isp[kk])
 #pragma unroll
               for (int e = 0; e < V; ++e) c[kk].x[e] += u[kk][0].x[e];
         }
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk)
+        for (int kk = 0; kk < RW; ++kk)
           if (isp[kk]) c[kk].store(a.wvals + (int64_t)node[kk] * a.B + b);
       } else {
 #pragma unroll
-      for (int kk = 0; kk < 16; ++kk) {
+      for (int kk = 0; kk < RW; ++kk) {
         node[kk] = -1;
         q0[kk] = q1[kk] = 0;
         if (k0 + kk < gr.N) {
@@ -436,23 +439,23 @@ __global__ __launch_bounds__(256) void k_colmax(SumArgs a) {
         }
       }
       for (int q = 0; q < a.fp_maxdeg; ++q) {
-        Row<V> u[16];
+        Row<V> u[RW];
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk)
+        for (int kk = 0; kk < RW; ++kk)
           if (q0[kk] + q < q1[kk]) u[kk].load(a.vals + (int64_t)a.fp_ids[q0[kk] + q] * a.B + b);
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk)
+        for (int kk = 0; kk < RW; ++kk)
           if (q0[kk] + q < q1[kk])
 #pragma unroll
             for (int e = 0; e < V; ++e) c[kk].x[e] += u[kk].x[e];
       }
 #pragma unroll
-      for (int kk = 0; kk < 16; ++kk)
+      for (int kk = 0; kk < RW; ++kk)
         if (q1[kk] > q0[kk]) c[kk].store(a.wvals + (int64_t)node[kk] * a.B + b);
       }
     }
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk)
+    for (int kk = 0; kk < RW; ++kk)
       if (k0 + kk < gr.N)
 #pragma unroll
         for (int e = 0; e < V; ++e) m.x[e] = fmaxf(m.x[e], c[kk].x[e]);
@@ -460,7 +463,7 @@ __global__ __launch_bounds__(256) void k_colmax(SumArgs a) {
 #pragma unroll
   for (int e = 0; e < V; ++e) red[w][lane * V + e] = m.x[e];
   __syncthreads();
-  if ((rt - gr.pk_start) * 64 >= gr.N) return;   // a padding tile: no child
+  if (kw >= gr.N) return;   // past the group's children: nothing to publish
   for (int x = threadIdx.x; x < 64 * V; x += blockDim.x) {
     const int bb = st * 64 * V + x;
     if (bb < a.B) {
@@ -799,19 +802,25 @@ void launch_input_bwd(const InputArgs& a, hipStream_t s) {
 void launch_prod_fwd(const ProdArgs& a, hipStream_t s) { PC_LAUNCH_V(k_prod_fwd, a.num_nodes, a, s); }
 void launch_prod_bwd(const ProdArgs& a, hipStream_t s) { PC_LAUNCH_V(k_prod_bwd, a.nuniq, a, s); }
 // Column maxima (and the preceding product layer when a.fp_on): V samples per
-// lane, the widest of 4 (16-byte accesses, batch a multiple of 4), 2 and 1
-// that still gives 512 workgroups (two per CU), else 1: a 4096-child layer at
-// batch 512 is 64 row tiles, only 128 workgroups of 256 samples.
+// lane and RW children per wave, the first of (V, RW) = (4, 16) (16-byte
+// accesses, batch a multiple of 4), (2, 16), (1, 16), (1, 4), (1, 1) that
+// still gives 512 workgroups (two per CU), else (1, 1): a 4096-child layer
+// at batch 512 is 64 tiles of 64 children, only 128 workgroups of 256
+// samples; a 1024-child layer at batch 64 only 16 workgroups of 64 rows.
 template <bool PROD>
 static void launch_colmax_v(const SumArgs& a, int row_tiles, hipStream_t s) {
   const int g4 = row_tiles * ((a.B + 255) / 256), g2 = row_tiles * ((a.B + 127) / 128);
   const int g1 = row_tiles * ((a.B + 63) / 64);
   if (a.B % 4 == 0 && g4 >= 512)
-    hipLaunchKernelGGL((k_colmax<4, PROD>), dim3(g4), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_colmax<4, PROD, 16>), dim3(g4), dim3(256), 0, s, a);
   else if (a.B % 2 == 0 && g2 >= 512)
-    hipLaunchKernelGGL((k_colmax<2, PROD>), dim3(g2), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_colmax<2, PROD, 16>), dim3(g2), dim3(256), 0, s, a);
+  else if (g1 >= 512)
+    hipLaunchKernelGGL((k_colmax<1, PROD, 16>), dim3(g1), dim3(256), 0, s, a);
+  else if (g1 * 4 >= 512)
+    hipLaunchKernelGGL((k_colmax<1, PROD, 4>), dim3(g1 * 4), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((k_colmax<1, PROD>), dim3(g1), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_colmax<1, PROD, 1>), dim3(g1 * 16), dim3(256), 0, s, a);
 }
 void launch_colmax(const SumArgs& a, int row_tiles, hipStream_t s) {
   if (row_tiles <= 0) return;
