@@ -61,6 +61,12 @@ __device__ __forceinline__ float key_to_shift(uint32_t k) {
   return (m == m && fabsf(m) <= 3.0e38f) ? m : 0.0f;   // -inf / unset column -> 0
 }
 
+// Order-preserving 32-bit key of a float (integer atomic max = float max).
+__device__ __forceinline__ uint32_t float_to_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 __device__ __forceinline__ int xcd_remap(int bid, int n) {
   const int q = n >> 3, r = n & 7;
   const int x = bid & 7, local = bid >> 3;
@@ -526,12 +532,18 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
   constexpr int LDT = NT + 8;                  // row pitch: the two half-waves' rows 4 apart hit other banks
   constexpr int PR = WM * 32;                  // rows per pass
   constexpr int NCH = PR * NT / 4 / 256;       // 4-column chunks per thread per pass
+  constexpr int TPC = 256 / (NT / 4);          // threads sharing a 4-column chunk (product-epilogue maxima)
   static_assert(PR * NT % 1024 == 0, "whole chunks per thread");
-  static_assert((PR * LDT + NT + MT) * 4 <= NS * R::STAGE * 2, "epilogue tile fits the ring");
+  static_assert((PR * LDT + NT + MT + TPC * NT) * 4 <= NS * R::STAGE * 2, "epilogue tile fits the ring");
   const int B = a.B;
   float* tl = (float*)ring;                    // [PR][LDT]
   float* sh_col = tl + PR * LDT;               // [NT]
   int* ch_row = (int*)(sh_col + NT);           // [MT]
+  float* red = (float*)(ch_row + MT);          // [TPC][NT]
+  // product epilogue: this thread's running column maxima (its 4 columns are
+  // the same in every chunk: (tid % (NT/4)) * 4)
+  const bool ep = EPI == EPI_FWD && a.ep_on;
+  float pm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   __syncthreads();
   if (EPI == EPI_FWD || EPI == EPI_ELEM) {
     for (int t = tid; t < NT; t += 256) {
@@ -572,6 +584,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
     // every load of the pass in flight before the first store
     float x[NCH][4], old[NCH][4];
     int64_t at[NCH];
+    int32_t pi[NCH];                           // product node of the row (product epilogue), -1 if none
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int row = m0 + trow[c], col = n0 + c4[c];
@@ -579,6 +592,22 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
       if (EPI == EPI_FWD) {
         ok = row < gr.M;
         at[c] = (int64_t)row * B + col;
+        pi[c] = -1;
+        if (ep && ok) {
+          const int i = gr.out_start + row - a.ep_base_s;
+          if (i >= 0 && i < a.ep_pcount) {
+            pi[c] = i;
+            // the product node's other child
+            const float* src = a.vals + (int64_t)(a.ep_base_o + i) * B + col;
+            if (vec && col + 3 < B) {
+              const float4 t = *(const float4*)src;
+              x[c][0] = t.x; x[c][1] = t.y; x[c][2] = t.z; x[c][3] = t.w;
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) x[c][e] = col + e < B ? src[e] : 0.0f;
+            }
+          }
+        }
       } else if (EPI == EPI_ELEM) {
         const int child = ch_row[trow[c]];
         ok = child >= 0;
@@ -650,8 +679,39 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
             if (EPI == EPI_FWD) a.ssum[gr.s_row * B + at[c] + e] = o2[e];
           }
       }
+      if (EPI == EPI_FWD && ep && pi[c] >= 0) {
+        // product node = its children added in child order, as the product kernel does
+        float pv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pv[e] = a.ep_qs == 0 ? (0.0f + o[e]) + x[c][e] : (0.0f + x[c][e]) + o[e];
+          if (col + e < B) pm[e] = fmaxf(pm[e], pv[e]);
+        }
+        float* dp = a.vals + (int64_t)(a.ep_pstart + pi[c]) * B + col;
+        if (vec && col + 3 < B) {
+          *(float4*)dp = make_float4(pv[0], pv[1], pv[2], pv[3]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (col + e < B) dp[e] = pv[e];
+        }
+      }
     }
     if (i + 1 < FM) __syncthreads();           // the pass tile is rewritten next
+  }
+  if (EPI == EPI_FWD && ep) {
+    // column maxima of the tile's product nodes: the TPC threads of each
+    // 4-column chunk through LDS, then one integer atomic max per column
+    const int c4 = (tid % (NT / 4)) * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[(tid / (NT / 4)) * NT + c4 + e] = pm[e];
+    __syncthreads();
+    for (int t = tid; t < NT; t += 256) {
+      float m = red[t];
+#pragma unroll
+      for (int k = 1; k < TPC; ++k) m = fmaxf(m, red[k * NT + t]);
+      if (n0 + t < B) atomicMax(a.mkeys_out + (int64_t)a.ep_mrow * B + n0 + t, float_to_key(m));
+    }
   }
 }
 

@@ -730,7 +730,7 @@ int pc_forward(pc_handle hh, int batch, const int32_t* tokens, const float* para
           for (int q = 0; q < 8; ++q) a.fp_abase[q] = pp.abase[q];
           a.wvals = node_vals;
         }
-        {
+        if (!(h->opt_fuse && sp.epi_max)) {   // else published by the previous layer's product epilogue
           Timed t(h, KK_COLMAX, c.s);
           launch_colmax(a, sp.pktiles, c.s);
         }
@@ -762,7 +762,18 @@ int pc_forward(pc_handle hh, int batch, const int32_t* tokens, const float* para
         g.ldb = sp.ebt_cols;
         g.vals = node_vals;
         g.mkeys = v.mkeys;
+        g.mkeys_out = v.mkeys;
         g.ssum = v.ssum;
+        if (h->opt_fuse && sp.epi_prod >= 0) {
+          const ProductPlan& pp = h->prods[sp.epi_prod];
+          g.ep_on = 1;
+          g.ep_qs = sp.epi_qs;
+          g.ep_base_s = pp.abase[sp.epi_qs];
+          g.ep_base_o = pp.abase[1 - sp.epi_qs];
+          g.ep_pstart = pp.node_start;
+          g.ep_pcount = pp.num_nodes;
+          g.ep_mrow = sp.epi_mrow;
+        }
         const GemmShape shp = layer_gemm_shape(h, sp, GK_FWD, v.B_pad, p.pl[GK_FWD][0], p.pl[GK_FWD][1]);
         g.ntiles = v.B_pad / shp.nt;
         g.splitk = shp.splitk;

@@ -9,6 +9,7 @@
 // groups sharing a child go through a scratch buffer and a fixed-order
 // reduction, so the flows are deterministic).
 #include <algorithm>
+#include <climits>
 #include <map>
 #include <numeric>
 #include <string>
@@ -554,6 +555,57 @@ Handle* compile_layout(const pc_circuit_desc* d) {
       pp.bwd_fused = true;
       sp.bwd_prod = b.idx;
     }
+  }
+  // Forward product epilogues (see SumPlan::epi_prod): plain sum layer L1,
+  // affine product layer P of two children per node evaluated by the next sum
+  // layer's column maxima (fwd_fused), plain sum layer L3 with a single group
+  // whose children are
+  // exactly P's nodes.  P's child range q_s must be L1's outputs node for
+  // node, its other child ranges must avoid L1's outputs.
+  for (size_t li = 0; li + 2 < h->layers.size(); ++li) {
+    const LayerRef a = h->layers[li], b = h->layers[li + 1], c = h->layers[li + 2];
+    if (a.kind != PC_LAYER_SUM || b.kind != PC_LAYER_PRODUCT || c.kind != PC_LAYER_SUM) continue;
+    SumPlan& s1 = h->sums[a.idx];
+    ProductPlan& pp = h->prods[b.idx];
+    SumPlan& s3 = h->sums[c.idx];
+    if (s1.lowrank || s3.lowrank || !pp.affine || pp.max_deg != 2 || !pp.fwd_fused || s3.fwd_prod != b.idx)
+      continue;
+    if (s3.groups.size() != 1 || s3.groups[0].N != pp.num_nodes) continue;
+    {   // L3's children: P's nodes, each once
+      const GroupRec& r = s3.groups[0];
+      std::vector<char> seen(pp.num_nodes, 0);
+      bool ok = true;
+      for (int k = 0; ok && k < r.nblk; ++k)
+        for (int64_t ch = s3.blocks[r.blk_off + k]; ok && ch < s3.blocks[r.blk_off + k] + r.cbs; ++ch) {
+          const int64_t q = ch - pp.node_start;
+          ok = q >= 0 && q < pp.num_nodes && !seen[q];
+          if (ok) seen[q] = 1;
+        }
+      if (!ok) continue;
+    }
+    // L1's outputs as a node mask
+    int32_t lo = INT32_MAX, hi = -1;
+    for (const GroupRec& r : s1.groups) {
+      lo = std::min(lo, r.out_start);
+      hi = std::max(hi, r.out_start + r.M);
+    }
+    std::vector<char> out((size_t)(hi - lo), 0);
+    for (const GroupRec& r : s1.groups)
+      for (int32_t k = 0; k < r.M; ++k) out[(size_t)(r.out_start + k - lo)] = 1;
+    auto is_out = [&](int64_t n) { return n >= lo && n < hi && out[(size_t)(n - lo)]; };
+    int qs = -1;
+    bool ok = true;
+    for (int32_t q = 0; ok && q < pp.max_deg; ++q) {
+      int64_t inside = 0;
+      for (int32_t i = 0; i < pp.num_nodes; ++i) inside += is_out((int64_t)pp.abase[q] + i);
+      if (inside == pp.num_nodes && qs < 0) qs = q;
+      else if (inside != 0) ok = false;
+    }
+    if (!ok || qs < 0) continue;
+    s1.epi_prod = b.idx;
+    s1.epi_qs = qs;
+    s1.epi_mrow = s3.groups[0].m_row;
+    s3.epi_max = true;
   }
   return h;
 }

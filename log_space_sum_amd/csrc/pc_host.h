@@ -77,6 +77,15 @@ struct SumPlan {
   // the one before it in the column-max kernel (forward), the one after it in
   // the scaled-flow packing (backward).
   int fwd_prod = -1, bwd_prod = -1;
+  // Forward product epilogue: this layer's forward product also evaluates the
+  // affine product layer epi_prod that follows it (its nodes i take child
+  // epi_qs, abase[epi_qs] + i, from this layer's outputs; their other
+  // children come from earlier layers) and publishes the column maxima of the
+  // next sum layer, whose one group's children are exactly those product
+  // nodes (keys row epi_mrow).  That layer then skips its column-max launch
+  // (epi_max).
+  int epi_prod = -1, epi_qs = -1, epi_mrow = -1;
+  bool epi_max = false;
   // Per 64-row output tile row: the parent node in bwd_prod when that layer
   // gives each child a single parent, else the distinct-child index; -1 when
   // the output is not a child of bwd_prod.

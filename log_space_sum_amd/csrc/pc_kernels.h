@@ -27,6 +27,7 @@ struct GemmArgs {
   float* flows;                 // node flows
   float* scratch;               // element-flow scratch of overlapping layers
   const uint32_t* mkeys;        // column-max keys
+  uint32_t* mkeys_out;          // the same keys, published by a product epilogue
   float* ssum;                  // scaled sums kept by the forward
   int32_t store;                // element flows: store instead of add
   const float* params;
@@ -36,6 +37,12 @@ struct GemmArgs {
   // parameter flows: tied copies [copy_lo, copy_hi) of each block; the launch
   // covers product tiles tile0 .. tile0 + grid - 1 of the block sequence
   int32_t copy_lo, copy_hi, tile0;
+  // forward: the following affine two-child product layer evaluated in the
+  // epilogue (ep_on).  Output node n is child ep_qs of product node
+  // i = n - ep_base_s when 0 <= i < ep_pcount; i's other child is
+  // ep_base_o + i; node i is stored at ep_pstart + i, and the column maxima of
+  // the product nodes go to keys row ep_mrow.
+  int32_t ep_on, ep_qs, ep_base_s, ep_base_o, ep_pstart, ep_pcount, ep_mrow;
 };
 
 // Output tile shapes of the product kernel (M x N per workgroup).
