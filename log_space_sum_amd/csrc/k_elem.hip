@@ -522,33 +522,71 @@ __device__ __forceinline__ void prod_bwd_rest(const SumArgs& a, int wg, int nwg)
   const int QB = (a.B + 3) / 4;
   const int64_t n = (int64_t)a.fp_nrest * QB;
   const bool vec = (a.B & 3) == 0;
-  for (int64_t i = (int64_t)wg * blockDim.x + threadIdx.x; i < n; i += (int64_t)nwg * blockDim.x) {
-    const int ri = (int)(i / QB), b = (int)(i - (int64_t)ri * QB) * 4;
-    const int u = a.fp_rest[ri];
-    const int q0 = a.fp_single ? 0 : a.fp_ptr[u], q1 = a.fp_single ? 1 : a.fp_ptr[u + 1];
-    float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int q = q0; q < q1; ++q) {
-      const float* pf = a.wflows + (int64_t)(a.fp_single ? a.fp_rest_par[ri] : a.fp_ids[q]) * a.B + b;
+  const int64_t step = (int64_t)nwg * blockDim.x;
+  // two items per pass, the single-parent loads of both issued first
+  for (int64_t i0 = (int64_t)wg * blockDim.x + threadIdx.x; i0 < n; i0 += 2 * step) {
+    float s[2][4], o[2][4];
+    int b[2], u[2];
+    float* dst[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t i = i0 + h * step;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[h][e] = o[h][e] = 0.0f;
+      dst[h] = nullptr;
+      if (i >= n) continue;
+      const int ri = (int)(i / QB);
+      b[h] = (int)(i - (int64_t)ri * QB) * 4;
+      u[h] = a.fp_rest[ri];
+      dst[h] = a.wflows + (int64_t)(a.fp_single ? u[h] : a.fp_uchild[u[h]]) * a.B + b[h];
+      if (a.fp_single) {
+        const float* pf = a.wflows + (int64_t)a.fp_rest_par[ri] * a.B + b[h];
+        if (vec) {
+          const float4 y = *(const float4*)pf;
+          s[h][0] = 0.0f + y.x; s[h][1] = 0.0f + y.y; s[h][2] = 0.0f + y.z; s[h][3] = 0.0f + y.w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (b[h] + e < a.B) s[h][e] = 0.0f + pf[e];
+        }
+      }
+      if (!a.fp_store) {
+        if (vec) {
+          const float4 y = *(const float4*)dst[h];
+          o[h][0] = y.x; o[h][1] = y.y; o[h][2] = y.z; o[h][3] = y.w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (b[h] + e < a.B) o[h][e] = dst[h][e];
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (!dst[h]) continue;
+      if (!a.fp_single) {
+        for (int q = a.fp_ptr[u[h]]; q < a.fp_ptr[u[h] + 1]; ++q) {
+          const float* pf = a.wflows + (int64_t)a.fp_ids[q] * a.B + b[h];
+          if (vec) {
+            const float4 y = *(const float4*)pf;
+            s[h][0] += y.x; s[h][1] += y.y; s[h][2] += y.z; s[h][3] += y.w;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (b[h] + e < a.B) s[h][e] += pf[e];
+          }
+        }
+      }
+      if (!a.fp_store)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[h][e] = o[h][e] + s[h][e];
       if (vec) {
-        const float4 y = *(const float4*)pf;
-        s[0] += y.x; s[1] += y.y; s[2] += y.z; s[3] += y.w;
+        *(float4*)dst[h] = make_float4(s[h][0], s[h][1], s[h][2], s[h][3]);
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (b + e < a.B) s[e] += pf[e];
+          if (b[h] + e < a.B) dst[h][e] = s[h][e];
       }
-    }
-    float* dst = a.wflows + (int64_t)(a.fp_single ? u : a.fp_uchild[u]) * a.B + b;
-    if (vec) {
-      if (!a.fp_store) {
-        const float4 o = *(const float4*)dst;
-        s[0] = o.x + s[0]; s[1] = o.y + s[1]; s[2] = o.z + s[2]; s[3] = o.w + s[3];
-      }
-      *(float4*)dst = make_float4(s[0], s[1], s[2], s[3]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (b + e < a.B) dst[e] = a.fp_store ? s[e] : dst[e] + s[e];
     }
   }
 }
@@ -582,73 +620,85 @@ __global__ __launch_bounds__(256) void k_pack(SumArgs a) {
   const int r0 = (rt - (KIND == 0 ? gr.pk_start : gr.pg_start)) * 64, b0 = bt * 64;
   const int nrows = KIND == 0 ? gr.N : gr.M;
   const int tid = threadIdx.x;
-  // phase 1: item = (row, 8-sample chunk), 512 items
-  for (int it = tid; it < 512; it += 256) {
-    const int r = it >> 3, c = it & 7;
+  // phase 1: item = (row, 8-sample chunk), 512 items, two per thread: every
+  // load of both items is issued before the first store (the stores could
+  // alias the loads, so the compiler would not hoist the second item's loads)
+  constexpr int U = 2;
+  int kq[U], bsq[U], upq[U];
+  bool okq[U], vq[U];
+  float u0[U][8], u1[U][8], uo[U][8];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int it = tid + 256 * u, r = it >> 3, c = it & 7;
     const int k = r0 + r, bs = b0 + c * 8;
+    kq[u] = k;
+    bsq[u] = bs;
+    okq[u] = k < nrows && bs < a.B;
+    // the 8 samples' inputs: two 16-byte loads per array when the chunk is
+    // whole and rows are 16-byte aligned (B % 4 == 0), else one by one
+    vq[u] = (a.B & 3) == 0 && bs + 8 <= a.B;
+    upq[u] = (PROD && okq[u]) ? a.fp_up[rt * 64 + r] : -1;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) u0[u][e] = u1[u][e] = uo[u][e] = 0.0f;
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (!okq[u]) continue;
+    const int k = kq[u], bs = bsq[u];
+    if (KIND == 0) {
+      load8(a.vals + (int64_t)child_of(gr, a.chblocks, k) * a.B + bs, vq[u], bs, a.B, u0[u]);
+      load8((const float*)(a.mkeys + (int64_t)gr.m_row * a.B + bs), vq[u], bs, a.B, u1[u]);
+    } else {
+      if (PROD && upq[u] >= 0) {
+        // single parent: its flow now; several: gathered below in parent order
+        if (a.fp_single) load8(a.wflows + (int64_t)upq[u] * a.B + bs, vq[u], bs, a.B, u0[u]);
+        if (!a.fp_store) load8(a.wflows + (int64_t)(gr.out_start + k) * a.B + bs, vq[u], bs, a.B, uo[u]);
+      } else {
+        load8(a.flows + (int64_t)(gr.out_start + k) * a.B + bs, vq[u], bs, a.B, u0[u]);
+      }
+      load8(a.ssum + (gr.s_row + k) * a.B + bs, vq[u], bs, a.B, u1[u]);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int it = tid + 256 * u, r = it >> 3, c = it & 7;
+    const int k = kq[u], bs = bsq[u];
     float x[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = 0.0f;
-    if (k < nrows && bs < a.B) {
-      // the 8 samples' inputs: two 16-byte loads per array when the chunk is
-      // whole and rows are 16-byte aligned (B % 4 == 0), else one by one
-      const bool vec = (a.B & 3) == 0 && bs + 8 <= a.B;
-      const float* p0;
-      const float* p1;
-      if (KIND == 0) {
-        p0 = a.vals + (int64_t)child_of(gr, a.chblocks, k) * a.B + bs;
-        p1 = (const float*)(a.mkeys + (int64_t)gr.m_row * a.B + bs);
-      } else {
-        p0 = a.flows + (int64_t)(gr.out_start + k) * a.B + bs;
-        p1 = a.ssum + (gr.s_row + k) * a.B + bs;
-      }
-      float u0[8], u1[8];
-      const int up = PROD ? a.fp_up[rt * 64 + r] : -1;
-      if (PROD && up >= 0) {
-        // this output's flow: its parents in the product layer, in order
+    if (okq[u]) {
+      if (PROD && upq[u] >= 0) {
+        // this output's flow: its parents in the product layer, in order,
+        // added to the old flow unless the layer stores
         float f[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) f[e] = 0.0f;
-        const int q0 = a.fp_single ? 0 : a.fp_ptr[up], q1 = a.fp_single ? 1 : a.fp_ptr[up + 1];
-        for (int q = q0; q < q1; ++q) {
-          const float* pf = a.wflows + (int64_t)(a.fp_single ? up : a.fp_ids[q]) * a.B + bs;
-          float y[8];
-          load8(pf, vec, bs, a.B, y);
+        if (a.fp_single) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) f[e] += y[e];
+          for (int e = 0; e < 8; ++e) f[e] += u0[u][e];
+        } else {
+          const int up = upq[u];
+          for (int q = a.fp_ptr[up]; q < a.fp_ptr[up + 1]; ++q) {
+            float y[8];
+            load8(a.wflows + (int64_t)a.fp_ids[q] * a.B + bs, vq[u], bs, a.B, y);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[e] += y[e];
+          }
         }
-        float* pw = a.wflows + (int64_t)(gr.out_start + k) * a.B + bs;
-        if (!a.fp_store) {
-          float o[8];
-          load8(pw, vec, bs, a.B, o);
+        if (!a.fp_store)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) f[e] = o[e] + f[e];
-        }
-        store8(pw, vec, bs, a.B, f);
+          for (int e = 0; e < 8; ++e) f[e] = uo[u][e] + f[e];
+        store8(a.wflows + (int64_t)(gr.out_start + k) * a.B + bs, vq[u], bs, a.B, f);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) u0[e] = f[e];
-        load8(p1, vec, bs, a.B, u1);
-      } else if (vec) {
-        Row<4> t;
-        t.load(p0); for (int e = 0; e < 4; ++e) u0[e] = t.x[e];
-        t.load(p0 + 4); for (int e = 0; e < 4; ++e) u0[4 + e] = t.x[e];
-        t.load(p1); for (int e = 0; e < 4; ++e) u1[e] = t.x[e];
-        t.load(p1 + 4); for (int e = 0; e < 4; ++e) u1[4 + e] = t.x[e];
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const bool in = bs + e < a.B;
-          u0[e] = in ? p0[e] : 0.0f;
-          u1[e] = in ? p1[e] : 0.0f;
-        }
+        for (int e = 0; e < 8; ++e) u0[u][e] = f[e];
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         if (bs + e >= a.B) continue;
         if (KIND == 0) {
-          x[e] = expf(u0[e] - key_shift(__float_as_uint(u1[e])));
+          x[e] = expf(u0[u][e] - key_shift(__float_as_uint(u1[u][e])));
         } else {
-          const float fv = u0[e], sv = u1[e];
+          const float fv = u0[u][e], sv = u1[u][e];
           x[e] = (fv == 0.0f || !(sv > 0.0f)) ? 0.0f : fv / sv;
         }
       }
