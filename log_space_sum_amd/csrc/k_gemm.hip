@@ -736,6 +736,7 @@ static void launch_tile(int tile, int grid, const GemmArgs& a, hipStream_t s) {
   } else {
     if (tile == TILE_256x128) launch_shape<EPI, PA, PB, 256, 128, 2>(grid, a, s);
     else if (tile == TILE_128x256) launch_shape<EPI, PA, PB, 128, 256, 2>(grid, a, s);
+    else if (tile == TILE_128x64) launch_shape<EPI, PA, PB, 128, 64, 2>(grid, a, s);
     else launch_shape<EPI, PA, PB, 128, 128, 2>(grid, a, s);
   }
 }
