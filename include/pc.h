@@ -195,8 +195,7 @@ int pc_set_split(pc_handle h, int mode, int gemm_kind, int planes_a, int planes_
 
 /* Product-kernel tuning (advanced; results change only by float32 summation
  * order).  PC_OPT_LAYER_TILE: output tile of the per-layer forward and
- * element-flow products, 0 automatic (128 x 64 when that gives at least 256
- * tiles, else 128 x 128 with the K split), 1 128 x 128, 2 256 x 128,
+ * element-flow products, 0 automatic (128 x 64), 1 128 x 128, 2 256 x 128,
  * 3 128 x 256, 4 128 x 64.
  * PC_OPT_PARAM_TILE: tile of the parameter-flow product, 0 automatic
  * (128 x 128), 1 128 x 128, 2 256 x 256 (when the operand split allows).

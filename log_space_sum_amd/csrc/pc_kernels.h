@@ -68,14 +68,15 @@ constexpr int gemm_stages(int pa, int pb, int mt, int nt) {
 
 // Shape of a forward / element-flow launch over a layer whose outputs span
 // `rows256` 256-row blocks, batch padded to B_pad, largest padded K `kpad`.
-// Automatic: 128 x 64 tiles when they alone give 256 workgroups (no K split:
-// no partial tiles, and every CU runs an epilogue; measured 3% faster per
-// step than 128 x 128 split in two on the 4096-node layers at batch 512),
-// else 128 x 128 tiles.  The K split (a power of two up to split_max) grows
-// until the launch has 256 workgroups, keeping >= 4 slices per split.
+// Automatic: 128 x 64 tiles (on the 4096-node HMM layers: at batch 512, 256
+// tiles with the full K, no partial tiles and every CU running an epilogue,
+// 3% faster per step than 128 x 128 split in two; at batch 128, split in four,
+// 8% faster than 128 x 128 split in eight).  The K split (a power of two up to
+// split_max) grows until the launch has 256 workgroups, keeping >= 4 slices
+// per split.
 inline GemmShape layer_shape(int rows256, int B_pad, int kpad, int pa, int pb, int opt_tile, int split_max) {
   GemmShape g{};
-  if (opt_tile == TILE_AUTO && rows256 * 2 * (B_pad / 64) >= 256) opt_tile = TILE_128x64;
+  if (opt_tile == TILE_AUTO) opt_tile = TILE_128x64;
   g.tile = opt_tile == TILE_256x128 ? TILE_256x128
          : opt_tile == TILE_128x256 ? TILE_128x256
          : opt_tile == TILE_128x64 ? TILE_128x64 : TILE_128x128;
