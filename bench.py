@@ -57,7 +57,7 @@ def kernel_traffic(kernel_kind):
     return rec["bytes_per_launch"]
 
 
-def cpu_baseline(cfg, sample_B, min_s=10.0, max_passes=5):
+def cpu_baseline(cfg, sample_B, min_s=10.0, max_passes=100000):
     """The float64 oracle (as it stands) on the first `sample_B` samples,
     repeated (at most `max_passes` passes) until `min_s` seconds have passed;
     the rate is per pass."""
@@ -70,19 +70,21 @@ def cpu_baseline(cfg, sample_B, min_s=10.0, max_passes=5):
         threads = os.cpu_count()
     circ = cfg["circuit"]
     p = cfg["params"].astype(np.float64)
-    tok = cfg["tokens"][:sample_B]
+    tok = cfg["tokens"][:sample_B] if cfg.get("tokens") is not None else None
+    ext = cfg["external"][:, :sample_B] if cfg.get("external") is not None else None
+    seeds = cfg["seed_flows"][:, :sample_B] if cfg.get("seed_flows") is not None else None
     t0 = time.perf_counter()
     passes = 0
     while passes < max_passes and (passes == 0 or time.perf_counter() - t0 < min_s):
-        V, ll = oracle.forward(circ, p, sample_B, tokens=tok)
-        oracle.backward(circ, p, V, tokens=tok)
+        V, ll = oracle.forward(circ, p, sample_B, tokens=tok, external=ext)
+        oracle.backward(circ, p, V, tokens=tok, seed_flows=seeds)
         passes += 1
     total = time.perf_counter() - t0
     dt = total / passes
     fl = sum_flops(circ, sample_B)
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"float64 oracle forward+backward on {sample_B} of the {cfg['B']} samples "
-                      f"(all 32 positions), {passes} pass(es) in {total:.2f} s; sum-layer algorithmic "
+                      f"(the whole circuit), {passes} pass(es) in {total:.2f} s; sum-layer algorithmic "
                       f"flops per pass / time per pass",
             "seconds": total}
 
@@ -184,16 +186,21 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="hmm4096", choices=["hmm4096", "lowrank"],
+    ap.add_argument("--workload", default="hmm4096", choices=["hmm4096", "lowrank", "hclt", "dense"],
                     help="hmm4096: the metric's workload (default); lowrank: the LowRank exp_sum HMM "
-                         "(1024 states, 64 positions, rank 16, batch 64)")
+                         "(1024 states, 64 positions, rank 16, batch 64); hclt: the HCLT-like circuit (768 "
+                         "variables x 1024 latents x 512 categories, batch 512); dense: one 1024 x 1024 dense "
+                         "layer over external children, batch 128")
     ap.add_argument("--mode", default="auto", choices=["auto", "fp32"])
-    ap.add_argument("--batch", type=int, default=512)
+    ap.add_argument("--batch", type=int, default=None, help="batch (default: the workload's)")
     ap.add_argument("--H", type=int, default=4096)
     ap.add_argument("--T", type=int, default=32)
     ap.add_argument("--cpu-sample", type=int, default=512,
                     help="samples of the batch the float64 oracle baseline runs on (the default, the whole "
                          "batch of 512, is about 10-20 s on a 16-core host)")
+    ap.add_argument("--cpu-sample-other", type=int, default=None,
+                    help="samples the oracle baseline of the hclt / dense workloads runs on "
+                         "(default: 8 for hclt, the whole batch for dense)")
     ap.add_argument("--lr-cpu-sample", type=int, default=24,
                     help="samples of the LowRank workload the oracle baseline runs on")
     ap.add_argument("--no-cpu", action="store_true")
@@ -233,7 +240,32 @@ def main():
 
     if args.workload == "lowrank":
         return bench_lowrank(args)
-    cfg = make_config("hmm4096", H=args.H, T=args.T, B=args.batch)
+    bsz = {} if args.batch is None else {"B": args.batch}
+    if args.workload == "hmm4096":
+        cfg = make_config("hmm4096", H=args.H, T=args.T, **bsz)
+        metric = "sum-layer fwd+bwd ms & TFLOP/s (frac of MFMA peak), HMM 4096 lat×32 pos, batch 512"
+        workload = f"hmm{args.H}x{args.T} symbols 512 batch {cfg['B']} fwd+bwd+em"
+        context = "pages (RTX PRO 6000, whole circuit, auto): 32.1 ms fwd+bwd at batch 512"
+    elif args.workload == "hclt":
+        print("building the HCLT workload (768 variables x 1024 latents, 512 categories; about a minute)",
+              file=sys.stderr, flush=True)
+        cfg = make_config("hclt", **bsz)
+        metric = "sum-layer fwd+bwd TFLOP/s (frac of MFMA peak), HCLT 768 vars x 1024 latents x 512 cats"
+        workload = f"hclt 768 vars x 1024 latents x 512 categories, random tree, batch {cfg['B']} fwd+bwd+em"
+        context = "pages (RTX PRO 6000, whole circuit, auto): 48.1 ms fwd+bwd at batch 512"
+    else:
+        cfg = make_config("dense_layer", **bsz)
+        metric = "sum-layer fwd+bwd TFLOP/s (frac of MFMA peak), one dense 1024x1024 layer"
+        workload = f"dense layer 1024 nodes x 1024 shared children, batch {cfg['B']} fwd+bwd+em"
+        context = None
+    return bench_circuit(args, cfg, metric, workload, context)
+
+
+def bench_circuit(args, cfg, metric, workload, context):
+    """One forward + backward + EM per step on a plain (non-LowRank) circuit;
+    `value` = the sum layers' algorithmic TFLOP/s over the step's wall time."""
+    import torch
+    import log_space_sum_amd as L
     circ, B = cfg["circuit"], cfg["B"]
     dev = "cuda:0"
     h = L.pc_compile_layout(circ, device=0)
@@ -244,19 +276,26 @@ def main():
     L.pc_set_option(h, "fuse", args.fuse)
     L.pc_set_option(h, "param_chunk", args.param_chunk)
     params = torch.tensor(cfg["params"], device=dev)
-    params0 = params.clone()
-    tokens = torch.tensor(cfg["tokens"], device=dev)
+    tokens = torch.tensor(cfg["tokens"], device=dev) if cfg.get("tokens") is not None else None
     vals = torch.empty((circ.num_nodes, B), device=dev)
     flows = torch.empty((circ.num_nodes, B), device=dev)
+    flags = 0
+    ext = [l for l in circ.layers if type(l).__name__ == "InputExternal"]
+    if ext:      # external child values (the dense layer), set once: the passes never write them
+        rows = torch.cat([torch.arange(l.node_start, l.node_start + l.num_nodes) for l in ext]).to(dev)
+        vals[rows] = torch.tensor(cfg["external"], device=dev)
+    if cfg.get("seed_flows") is not None:   # incoming flows of the output nodes, set once
+        flows[torch.tensor(circ.output_nodes(), device=dev)] = torch.tensor(cfg["seed_flows"], device=dev)
+        flags = L.PC_BWD_SEEDED
     pflows = torch.zeros(circ.num_params, device=dev)
-    ll = torch.empty(B, device=dev)
+    ll = torch.empty(B, device=dev) if circ.root >= 0 else None
     ws = L.workspace(h, B, dev)
     stream = torch.cuda.current_stream()
 
     def step():
         pflows.zero_()
         L.pc_forward(h, B, tokens, params, vals, ll, None, ws, stream.cuda_stream)
-        L.pc_backward(h, B, tokens, params, vals, flows, pflows, 0, None, None, ws, stream.cuda_stream)
+        L.pc_backward(h, B, tokens, params, vals, flows, pflows, flags, None, None, ws, stream.cuda_stream)
         L.pc_em_step(h, params, pflows, 1.0, 0.0, stream.cuda_stream)
 
     for _ in range(args.warmup):
@@ -268,7 +307,7 @@ def main():
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     ms = dt / args.steps * 1e3
-    finite = bool(torch.isfinite(ll).all().item())
+    finite = bool(torch.isfinite(ll).all().item()) if ll is not None else bool(torch.isfinite(vals).all().item())
 
     # second timed pass with per-launch HIP events
     L.pc_set_timing(h, True)
@@ -291,7 +330,7 @@ def main():
     avg_ms = tot_ms / max(n_launch, 1)
     achieved = per_launch_flops / (avg_ms * 1e-3) / 1e12
     out = {
-        "metric": "sum-layer fwd+bwd ms & TFLOP/s (frac of MFMA peak), HMM 4096 lat×32 pos, batch 512",
+        "metric": metric,
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -303,8 +342,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if args.mode == "auto" else "bf16x3-split",
         "data": "synthetic",
-        "config": {"workload": f"hmm{args.H}x{args.T} symbols 512 batch {B} fwd+bwd+em",
-                   "precision_mode": args.mode, "global_batch": B},
+        "config": {"workload": workload, "precision_mode": args.mode, "global_batch": B},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "sum_layer_kernels_ms": round(sum_ms, 4),
         "sum_layer_kernels_tflops": round(flops / (sum_ms * 1e-3) / 1e12, 3) if sum_ms > 0 else None,
@@ -313,16 +351,23 @@ def main():
         "kernel_launches_per_step": {k: v[0] // args.steps for k, v in kt.items() if v[0]},
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 3),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": kernel_traffic(dom),
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": kernel_traffic(dom) if args.workload == "hmm4096" else None,
                      "per_launch_gflop": round(per_launch_flops / 1e9, 4),
                      "avg_launch_ms": round(avg_ms, 5)},
-        "ll_finite": finite,
-        "context": "pages (RTX PRO 6000, whole circuit, auto): 32.1 ms fwd+bwd at batch 512",
+        "finite": finite,
     }
+    if context:
+        out["context"] = context
     if not args.no_cpu:
-        cpu_cfg = make_config("hmm4096", H=args.H, T=args.T, B=args.batch)
-        out["cpu_baseline"] = cpu_baseline(cpu_cfg, min(args.cpu_sample, B))
-    del params0
+        if args.workload == "hmm4096":
+            sample = args.cpu_sample
+        elif args.cpu_sample_other is not None:
+            sample = args.cpu_sample_other
+        else:
+            sample = 8 if args.workload == "hclt" else B
+        sample = min(sample, B)
+        out["cpu_baseline"] = cpu_baseline(cfg, sample)
     print(json.dumps(out))
 
 

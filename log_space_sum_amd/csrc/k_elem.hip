@@ -779,28 +779,50 @@ __global__ void k_elem_reduce(SumArgs a) {
 }
 
 // ---- EM ------------------------------------------------------------------------
-__global__ void k_em(EmArgs a) {
-  __shared__ float red[256];
-  const int row = blockIdx.x;
+__global__ __launch_bounds__(256) void k_em(EmArgs a, int total_rows) {
+  // one wave per parameter row, four rows per workgroup: the row sum is a
+  // per-lane sum in index order then a fixed butterfly over the wave, so the
+  // result does not depend on timing
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= total_rows) return;
   const int s = last_le(a.segs, a.nsegs, row, [](const RowSeg& r) { return r.row_start; });
   const RowSeg sg = a.segs[s];
   const int64_t off = sg.offset + (int64_t)(row - sg.row_start) * sg.rlen;
+  const bool vec = ((off | (int64_t)sg.rlen) & 3) == 0;   // 16-byte rows
   float acc = 0.0f;
-  for (int j = threadIdx.x; j < sg.rlen; j += 256) acc += a.pflows[off + j];
-  red[threadIdx.x] = acc;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
-    __syncthreads();
+  if (vec) {
+    for (int j = lane * 4; j < sg.rlen; j += 256) {
+      const float4 f = *(const float4*)(a.pflows + off + j);
+      acc += ((f.x + f.y) + f.z) + f.w;
+    }
+  } else {
+    for (int j = lane; j < sg.rlen; j += 64) acc += a.pflows[off + j];
   }
-  const float tot = red[0] + a.pseudo;
-  if (!(tot > 0.0f)) return;
+#pragma unroll
+  for (int w = 32; w > 0; w >>= 1) acc += __shfl_xor(acc, w);
+  const float tot = acc + a.pseudo;
+  if (!(tot > 0.0f)) return;                    // a row without flow (and no pseudocount) keeps theta
   const float add = a.pseudo / (float)sg.rlen;
-  for (int j = threadIdx.x; j < sg.rlen; j += 256) {
-    const float nw = (a.pflows[off + j] + add) / tot;
-    a.params[off + j] = (1.0f - a.step) * a.params[off + j] + a.step * nw;
+  const float keep = 1.0f - a.step;
+  if (vec) {
+    for (int j = lane * 4; j < sg.rlen; j += 256) {
+      const float4 f = *(const float4*)(a.pflows + off + j);
+      float4 p = *(const float4*)(a.params + off + j);
+      p.x = keep * p.x + a.step * ((f.x + add) / tot);
+      p.y = keep * p.y + a.step * ((f.y + add) / tot);
+      p.z = keep * p.z + a.step * ((f.z + add) / tot);
+      p.w = keep * p.w + a.step * ((f.w + add) / tot);
+      *(float4*)(a.params + off + j) = p;
+    }
+  } else {
+    for (int j = lane; j < sg.rlen; j += 64) {
+      const float nw = (a.pflows[off + j] + add) / tot;
+      a.params[off + j] = keep * a.params[off + j] + a.step * nw;
+    }
   }
 }
+
 
 // ---- launchers -------------------------------------------------------------------
 static int grid_for(int64_t n, int per = 256, int cap = 65536) {
@@ -898,7 +920,7 @@ void launch_theta_pack(const ThetaArgs& a, int tiles, hipStream_t s) {
 }
 void launch_elem_reduce(const SumArgs& a, hipStream_t s) { PC_LAUNCH_V(k_elem_reduce, a.nuniq, a, s); }
 void launch_em(const EmArgs& a, int rows, hipStream_t s) {
-  if (rows > 0) hipLaunchKernelGGL(k_em, dim3(rows), dim3(256), 0, s, a);
+  if (rows > 0) hipLaunchKernelGGL(k_em, dim3((rows + 3) / 4), dim3(256), 0, s, a, rows);
 }
 
 }  // namespace pc
