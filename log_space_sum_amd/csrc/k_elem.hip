@@ -140,20 +140,44 @@ __device__ __forceinline__ void sum_rows(Row<V>& s, const float* x, const int32_
 // (and never an out-of-range read).
 template <int V>
 __global__ void k_input_fwd(InputArgs a) {
+  // U items (node, V samples) per thread per pass, every load of the pass
+  // issued before the first log
+  constexpr int U = 4;
   const uint32_t QB = (uint32_t)(a.B / V), n = (uint32_t)a.num_nodes * QB;
-  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
-    const uint32_t u = i / QB, b = (i - u * QB) * V;
-    const int32_t* tok = a.tokT + (int64_t)a.var[u] * a.B + b;
-    const float* th = a.params + a.param_offset + (int64_t)a.row[u] * a.K;
-    Row<V> xs;
-    xs.load((const float*)tok);   // the V tokens, as raw 32-bit words
-    Row<V> r;
+  const uint32_t stride = gridDim.x * blockDim.x;
+  for (uint32_t i0 = blockIdx.x * blockDim.x + threadIdx.x; i0 < n; i0 += U * stride) {
+    Row<V> xs[U];
+    const float* th[U];
 #pragma unroll
-    for (int k = 0; k < V; ++k) {
-      const int x = __float_as_int(xs.x[k]);
-      r.x[k] = (x >= 0 && x < a.K) ? logf(th[x]) : __uint_as_float(0x7fc00000u);
+    for (int q = 0; q < U; ++q) {
+      const uint32_t i = i0 + q * stride;
+      th[q] = nullptr;
+      if (i >= n) continue;
+      const uint32_t u = i / QB, b = (i - u * QB) * V;
+      xs[q].load((const float*)(a.tokT + (int64_t)a.var[u] * a.B + b));   // the V tokens, as raw 32-bit words
+      th[q] = a.params + a.param_offset + (int64_t)a.row[u] * a.K;
     }
-    r.store(a.vals + (int64_t)(a.node_start + u) * a.B + b);
+    float g[U][V];
+#pragma unroll
+    for (int q = 0; q < U; ++q)
+#pragma unroll
+      for (int k = 0; k < V; ++k) {
+        const int x = __float_as_int(xs[q].x[k]);
+        g[q][k] = (th[q] && x >= 0 && x < a.K) ? th[q][x] : -1.0f;
+      }
+#pragma unroll
+    for (int q = 0; q < U; ++q) {
+      const uint32_t i = i0 + q * stride;
+      if (i >= n) continue;
+      const uint32_t u = i / QB, b = (i - u * QB) * V;
+      Row<V> r;
+#pragma unroll
+      for (int k = 0; k < V; ++k) {
+        const int x = __float_as_int(xs[q].x[k]);
+        r.x[k] = (x >= 0 && x < a.K) ? logf(g[q][k]) : __uint_as_float(0x7fc00000u);
+      }
+      r.store(a.vals + (int64_t)(a.node_start + u) * a.B + b);
+    }
   }
 }
 
@@ -256,6 +280,45 @@ __global__ __launch_bounds__(64 * NW) void k_input_bwd(InputArgs a) {
       float t = 0.0f;
 #pragma unroll
       for (int u = 0; u < NW; ++u) t += ib_sm[u * per + k];
+      out[k] += t;
+    }
+  }
+}
+
+// The same sums when every parameter row has one node (an untied input
+// layer): workgroup = one variable and a chunk of 64 of its nodes; the
+// variable's category buckets are staged in LDS once, and each wave streams
+// 16 of the nodes, one flow row at a time in its own LDS region, adding each
+// category's bucket sum to its node's row.
+constexpr int kVarChunk = 64;
+__global__ __launch_bounds__(256) void k_input_bwd_var(InputArgs a) {
+  extern __shared__ float ib_sm[];
+  const int B = a.B, K = a.K;
+  int32_t* idx = (int32_t*)ib_sm;             // [B]
+  int32_t* ptr = idx + B;                     // [K + 1]
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float* f = ib_sm + B + K + 1 + w * B;       // [B] per wave
+  const int nchunk = (a.max_var_nodes + kVarChunk - 1) / kVarChunk;
+  const int v = blockIdx.x / nchunk, c = blockIdx.x - v * nchunk;
+  const int q0 = a.var_ptr[v] + c * kVarChunk, q1 = min(a.var_ptr[v + 1], q0 + kVarChunk);
+  if (q0 >= q1) return;
+  const int32_t* I = a.bidx + (int64_t)v * B;
+  const int32_t* P = a.bptr + (int64_t)v * (a.Kmax + 1);
+  for (int b = threadIdx.x; b < B; b += blockDim.x) idx[b] = I[b];
+  for (int k = threadIdx.x; k <= K; k += blockDim.x) ptr[k] = P[k];
+  __syncthreads();
+  for (int q = q0 + w; q < q1; q += 4) {
+    const int u = a.var_nodes[q];
+    const float* F = a.flows + (int64_t)(a.node_start + u) * B;
+    // a wave's LDS operations complete in order
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll 4
+    for (int b = lane; b < B; b += 64) f[b] = F[b];
+    __builtin_amdgcn_wave_barrier();
+    float* out = a.pflows + a.param_offset + (int64_t)a.row[u] * K;
+    for (int k = lane; k < K; k += 64) {
+      float t = 0.0f;
+      for (int e = ptr[k]; e < ptr[k + 1]; ++e) t += f[idx[e]];
       out[k] += t;
     }
   }
@@ -863,10 +926,15 @@ void launch_bucket(const int32_t* tokT, int V, int B, int Kmax, int32_t* bptr, i
 void launch_input_bwd(const InputArgs& a, hipStream_t s) {
   if (a.num_rows <= 0) return;
   const size_t per = (size_t)(2 * a.B + a.K + 1) * sizeof(float);
-  const int nw = a.max_row_nodes >= 2 ? 4 : 1;
-  if (a.K <= 1024 && per * nw <= 64 * 1024) {
-    if (nw == 4) hipLaunchKernelGGL(k_input_bwd<4>, dim3(a.num_rows), dim3(256), per * 4, s, a);
-    else hipLaunchKernelGGL(k_input_bwd<1>, dim3(a.num_rows), dim3(64), per, s, a);
+  if (a.K <= 1024 && per * 4 <= 64 * 1024) {
+    // rows of several nodes: the row's nodes over 4 waves; else one row per wave
+    if (a.max_row_nodes >= 2) {
+      hipLaunchKernelGGL(k_input_bwd<4>, dim3(a.num_rows), dim3(256), per * 4, s, a);
+    } else {
+      const size_t sh = (size_t)(5 * a.B + a.K + 1) * sizeof(float);
+      const int nchunk = (a.max_var_nodes + kVarChunk - 1) / kVarChunk;
+      hipLaunchKernelGGL(k_input_bwd_var, dim3(a.num_vars * nchunk), dim3(256), sh, s, a);
+    }
   } else {
     hipLaunchKernelGGL(k_input_bwd_wide, dim3(a.num_rows), dim3(256), (size_t)a.B * sizeof(float), s, a);
   }

@@ -108,6 +108,8 @@ void upload_tables(Handle* h, int device) {
     ip.d_row = upload(ip.row);
     ip.d_row_ptr = upload(ip.row_ptr);
     ip.d_row_nodes = upload(ip.row_nodes);
+    ip.d_var_ptr = upload(ip.var_ptr);
+    ip.d_var_nodes = upload(ip.var_nodes);
   }
   for (auto& pp : h->prods) {
     pp.d_ch_ptr = upload(pp.ch_ptr);
@@ -142,6 +144,8 @@ void free_tables(Handle* h) {
     release(ip.d_row);
     release(ip.d_row_ptr);
     release(ip.d_row_nodes);
+    release(ip.d_var_ptr);
+    release(ip.d_var_nodes);
   }
   for (auto& pp : h->prods) {
     release(pp.d_ch_ptr);
@@ -372,6 +376,10 @@ InputArgs input_args(const Call& c, const InputPlan& ip, const float* params) {
   a.row = ip.d_row;
   a.row_ptr = ip.d_row_ptr;
   a.row_nodes = ip.d_row_nodes;
+  a.var_ptr = ip.d_var_ptr;
+  a.var_nodes = ip.d_var_nodes;
+  a.num_vars = c.h->num_vars;
+  a.max_var_nodes = ip.max_var_nodes;
   a.tokT = c.v.tokT;
   a.bptr = c.v.bucket_ptr;
   a.bidx = c.v.bucket_idx;

@@ -106,6 +106,16 @@ Handle* compile_layout(const pc_circuit_desc* d) {
       ip.row_nodes.assign(ly.num_nodes, 0);
       std::vector<int32_t> fillp(ip.row_ptr.begin(), ip.row_ptr.end() - 1);
       for (int32_t i = 0; i < ly.num_nodes; ++i) ip.row_nodes[fillp[ip.row[i]]++] = ly.node_start + i;
+      // nodes of each variable (ascending), for the input flows of layers whose rows have one node each
+      ip.var_ptr.assign(d->num_vars + 1, 0);
+      for (int32_t i = 0; i < ly.num_nodes; ++i) ip.var_ptr[ip.var[i] + 1]++;
+      for (int32_t v = 0; v < d->num_vars; ++v) {
+        ip.max_var_nodes = std::max(ip.max_var_nodes, ip.var_ptr[v + 1]);
+        ip.var_ptr[v + 1] += ip.var_ptr[v];
+      }
+      ip.var_nodes.assign(ly.num_nodes, 0);
+      std::vector<int32_t> fillv(ip.var_ptr.begin(), ip.var_ptr.end() - 1);
+      for (int32_t i = 0; i < ly.num_nodes; ++i) ip.var_nodes[fillv[ip.var[i]]++] = i;
       auto it = table_shape.find(ly.param_offset);
       if (it == table_shape.end()) {
         table_shape[ly.param_offset] = {ly.num_rows, ly.num_cats};

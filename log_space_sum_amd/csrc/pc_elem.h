@@ -8,6 +8,9 @@ namespace pc {
 
 struct InputArgs {
   int32_t B, node_start, num_nodes, K, num_rows, Kmax, max_row_nodes;
+  int32_t num_vars, max_var_nodes;
+  const int32_t* var_ptr;       // variable -> layer-local nodes (CSR, ascending)
+  const int32_t* var_nodes;
   int64_t param_offset;
   const int32_t* var;
   const int32_t* row;

@@ -29,6 +29,10 @@ struct InputPlan {
   std::vector<int32_t> var, row;
   std::vector<int32_t> row_ptr, row_nodes;  // row -> nodes using it (ascending)
   int32_t max_row_nodes = 0;                 // most nodes sharing one parameter row
+  std::vector<int32_t> var_ptr, var_nodes;   // variable -> layer-local node indices (ascending)
+  int32_t max_var_nodes = 0;
+  int32_t* d_var_ptr = nullptr;
+  int32_t* d_var_nodes = nullptr;
   int32_t* d_var = nullptr;
   int32_t* d_row = nullptr;
   int32_t* d_row_ptr = nullptr;
