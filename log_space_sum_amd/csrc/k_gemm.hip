@@ -67,6 +67,36 @@ __device__ __forceinline__ uint32_t float_to_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// float32 -> bfloat16, round to nearest even (NaN kept quiet), and back.
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ float bf16_value(uint32_t h) { return __uint_as_float(h << 16); }
+// Split N values into np bfloat16 planes (each the rounding of what the
+// previous planes leave) and store each plane's N values as one run.
+template <int N>
+__device__ __forceinline__ void split_planes(const float* x, int np, uint16_t* dst, int64_t plane) {
+  static_assert(N == 4 || N == 8, "4 or 8 values");
+  float r[N];
+#pragma unroll
+  for (int e = 0; e < N; ++e) r[e] = x[e];
+  for (int p = 0; p < np; ++p) {
+    uint32_t w[N / 2];
+#pragma unroll
+    for (int e = 0; e < N / 2; ++e) {
+      const uint32_t h0 = bf16_bits(r[2 * e]), h1 = bf16_bits(r[2 * e + 1]);
+      r[2 * e] -= bf16_value(h0);
+      r[2 * e + 1] -= bf16_value(h1);
+      w[e] = h0 | (h1 << 16);
+    }
+    if constexpr (N == 4) *(uint2*)(dst + p * plane) = make_uint2(w[0], w[1]);
+    else *(uint4*)(dst + p * plane) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 __device__ __forceinline__ int xcd_remap(int bid, int n) {
   const int q = n >> 3, r = n & 7;
   const int x = bid & 7, local = bid >> 3;
@@ -543,6 +573,9 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
   // product epilogue: this thread's running column maxima (its 4 columns are
   // the same in every chunk: (tid % (NT/4)) * 4)
   const bool ep = EPI == EPI_FWD && a.ep_on;
+  // element-flow product epilogue packing the next layer's G (needs a whole
+  // tile of samples: the batch is a multiple of 256)
+  const bool gp = EPI == EPI_ELEM && a.gp_on;
   float pm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   __syncthreads();
   if (EPI == EPI_FWD || EPI == EPI_ELEM) {
@@ -582,7 +615,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
       c4[c] = (q % (NT / 4)) * 4;
     }
     // every load of the pass in flight before the first store
-    float x[NCH][4], old[NCH][4];
+    float x[NCH][4], old[NCH][4], sv[NCH][4];
     int64_t at[NCH];
     int32_t pi[NCH];                           // product node of the row (product epilogue), -1 if none
 #pragma unroll
@@ -620,6 +653,11 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) x[c][e] = (ok && col + e < B) ? src[e] : 0.0f;
         }
+        if (gp && ok) {
+          // scaled sums of the packed layer's node `row`
+          const float4 t = *(const float4*)(a.ssum + (a.gp_s_row + row) * B + col);
+          sv[c][0] = t.x; sv[c][1] = t.y; sv[c][2] = t.z; sv[c][3] = t.w;
+        }
       } else {
         ok = row < bl.M;
         at[c] = (int64_t)row * bl.N + col;
@@ -649,7 +687,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
     for (int c = 0; c < NCH; ++c) {
       if (at[c] < 0) continue;
       const int col = n0 + c4[c];
-      const float* pv = tl + (trow[c] - (trow[c] / WTM) * WTM - i * 32 + (trow[c] / WTM) * 32) * LDT + c4[c];
+      float* pv = tl + (trow[c] - (trow[c] / WTM) * WTM - i * 32 + (trow[c] / WTM) * 32) * LDT + c4[c];
       const float4 pt = *(const float4*)pv;
       const float acc4[4] = {pt.x, pt.y, pt.z, pt.w};
       float o[4], o2[4];
@@ -679,6 +717,24 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
             if (EPI == EPI_FWD) a.ssum[gr.s_row * B + at[c] + e] = o2[e];
           }
       }
+      if (EPI == EPI_ELEM && gp) {
+        // the product node's flow (this output) to both its children, and
+        // g = f / S of the packed layer's node into its node-major G rows;
+        // g goes back into this chunk's tile slot for the batch-major G
+        const int row = m0 + trow[c];
+        float f[4], gq[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          f[e] = 0.0f + o[e];
+          gq[e] = (f[e] == 0.0f || !(sv[c][e] > 0.0f)) ? 0.0f : f[e] / sv[c][e];
+        }
+        const float4 f4 = make_float4(f[0], f[1], f[2], f[3]);
+        *(float4*)(a.flows + (int64_t)(a.gp_out_start + row) * B + col) = f4;
+        *(float4*)(a.flows + (int64_t)(a.gp_other + row) * B + col) = f4;
+        split_planes<4>(gq, a.gp_np_direct, a.gp_direct + panel(a.gp_g_row + row, col, a.gp_direct_rows),
+                        a.gp_direct_plane);
+        *(float4*)pv = make_float4(gq[0], gq[1], gq[2], gq[3]);
+      }
       if (EPI == EPI_FWD && ep && pi[c] >= 0) {
         // product node = its children added in child order, as the product kernel does
         float pv[4];
@@ -695,6 +751,19 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
           for (int e = 0; e < 4; ++e)
             if (col + e < B) dp[e] = pv[e];
         }
+      }
+    }
+    if (EPI == EPI_ELEM && gp) {
+      // batch-major G: item = (sample, 8 consecutive rows of one 32-row run)
+      __syncthreads();
+      for (int it = tid; it < PR * NT / 8; it += 256) {
+        const int bl = it % NT, lr0 = (it / NT) * 8;
+        const int row = m0 + (lr0 >> 5) * WTM + i * 32 + (lr0 & 31);
+        if (row >= gr.N) continue;
+        float y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = tl[(lr0 + e) * LDT + bl];
+        split_planes<8>(y, a.gp_np_trans, a.gp_trans + panel(n0 + bl, a.gp_g_koff + row, a.B_pad), a.gp_trans_plane);
       }
     }
     if (i + 1 < FM) __syncthreads();           // the pass tile is rewritten next

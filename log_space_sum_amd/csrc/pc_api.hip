@@ -212,6 +212,8 @@ WsPlan plan_workspace(const Handle* h, int B) {
   p.thetaT = take((size_t)p.pl[GK_ELEM][0] * h->thetaT_elems * 2);
   p.ebt = take((size_t)p.pl[GK_FWD][1] * Bp * h->max_ebt_cols * 2);
   p.gbt = take((size_t)p.pl[GK_ELEM][1] * Bp * h->max_gbt_cols * 2);
+  p.gbt2 = take(h->gbt_slots > 1 && B % 256 == 0 ?   // independent of the fusion option
+                  (size_t)p.pl[GK_ELEM][1] * Bp * h->max_gbt_cols * 2 : 0);
   p.earena = take((size_t)p.pl[GK_PARAM][1] * h->earena_rows * BpK * 2);
   p.garena = take((size_t)p.pl[GK_PARAM][0] * h->garena_rows * BpK * 2);
   p.mkeys = take((size_t)h->m_rows * Bs * 4);
@@ -276,6 +278,7 @@ WsView make_view(const Handle* h, const WsPlan& p, void* ws) {
   v.thetaT_plane = h->thetaT_elems;
   v.ebt = (uint16_t*)(base + p.ebt);
   v.gbt = (uint16_t*)(base + p.gbt);
+  v.gbt2 = (uint16_t*)(base + p.gbt2);
   v.ebt_plane = (int64_t)p.B_pad * h->max_ebt_cols;
   v.gbt_plane = (int64_t)p.B_pad * h->max_gbt_cols;
   v.earena = (uint16_t*)(base + p.earena);
@@ -818,6 +821,7 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
     const WsPlan& p = c.p;
     const WsView& v = c.v;
     float* vals = const_cast<float*>(node_vals);
+    const bool gp = gp_active(h, B);
     {
       Timed t(h, KK_OTHER, c.s);
       launch_fill_ranges(node_flows, h->d_zero, (int)h->zero_ranges.size(), h->max_zero_count, B, c.s);
@@ -928,6 +932,7 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
         }
       } else if (r.kind == PC_LAYER_SUM) {
         const SumPlan& sp = h->sums[r.idx];
+        uint16_t* gbt = gp && sp.gbt_slot ? v.gbt2 : v.gbt;
         SumArgs a = sum_common(c, sp);
         a.vals = vals;
         a.flows = node_flows;
@@ -935,7 +940,7 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
         a.direct = v.garena;
         a.direct_plane = v.garena_plane;
         a.np_direct = p.pl[GK_PARAM][0];
-        a.trans = v.gbt;
+        a.trans = gbt;
         a.trans_plane = v.gbt_plane;
         a.direct_rows = h->garena_rows;
         a.np_trans = p.pl[GK_ELEM][1];
@@ -953,7 +958,7 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
           a.fp_single = pp.single_parent ? 1 : 0;
           a.wflows = node_flows;
         }
-        {
+        if (!(gp && sp.gp_done)) {   // else packed by the next layer's element-flow product
           Timed t(h, KK_GPACK, c.s);
           launch_g_pack(a, sp.pgtiles, c.s);
         }
@@ -963,9 +968,31 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
         g.chblocks = sp.d_blocks;
         g.opA = v.thetaT;
         g.planeA = v.thetaT_plane;
-        g.opB = v.gbt;
+        g.opB = gbt;
         g.planeB = v.gbt_plane;
         g.ldb = sp.gbt_cols;
+        if (gp && sp.gp_sum >= 0) {
+          const SumPlan& sa = h->sums[sp.gp_sum];
+          const ProductPlan& pp = h->prods[sp.gp_prod];
+          const GroupRec& ra = sa.groups[0];
+          g.gp_on = 1;
+          g.gp_qs = sp.gp_qs;
+          g.gp_out_start = ra.out_start;
+          g.gp_other = pp.abase[1 - sp.gp_qs];
+          g.gp_np_direct = p.pl[GK_PARAM][0];
+          g.gp_np_trans = p.pl[GK_ELEM][1];
+          g.gp_g_koff = ra.g_koff;
+          g.gp_s_row = ra.s_row;
+          g.gp_g_row = ra.g_row;
+          g.gp_direct_rows = h->garena_rows;
+          g.gp_direct_plane = v.garena_plane;
+          g.gp_trans_plane = v.gbt_plane;
+          g.gp_direct = v.garena;
+          g.gp_trans = sa.gbt_slot ? v.gbt2 : v.gbt;
+          g.ssum = v.ssum;   // the packed layer's kept scaled sums
+          if (!g.ssum || !g.gp_direct || !g.gp_trans || B % 256 != 0 || ra.s_row < 0)
+            fail(PC_ERR_INVALID_ARG, "internal: element-flow product epilogue without its operands");
+        }
         g.vals = vals;
         g.flows = node_flows;
         g.scratch = v.scratch;

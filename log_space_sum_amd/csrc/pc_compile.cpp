@@ -617,6 +617,50 @@ Handle* compile_layout(const pc_circuit_desc* d) {
     s1.epi_mrow = s3.groups[0].m_row;
     s3.epi_max = true;
   }
+  // Element-flow product epilogues (see SumPlan::gp_sum): plain single-group
+  // sum layer A (M a multiple of 64), affine two-child product layer P fused
+  // into A's scaled-flow packing (every child of P with P as its only parent,
+  // P the first writer of their flows), plain single-group sum layer C whose
+  // children are P's nodes in order, C the only writer of their flows.  P's
+  // child range q_s must be A's outputs in order.
+  for (size_t li = 0; li + 2 < h->layers.size(); ++li) {
+    const LayerRef a = h->layers[li], b = h->layers[li + 1], c = h->layers[li + 2];
+    if (a.kind != PC_LAYER_SUM || b.kind != PC_LAYER_PRODUCT || c.kind != PC_LAYER_SUM) continue;
+    SumPlan& sa = h->sums[a.idx];
+    ProductPlan& pp = h->prods[b.idx];
+    SumPlan& sc = h->sums[c.idx];
+    if (sa.lowrank || sc.lowrank || sa.groups.size() != 1 || sc.groups.size() != 1) continue;
+    if (!pp.affine || pp.max_deg != 2 || !pp.single_parent || !pp.store || sa.bwd_prod != b.idx) continue;
+    const GroupRec& ra = sa.groups[0];
+    const GroupRec& rc = sc.groups[0];
+    if (ra.M % 64 != 0 || pp.num_nodes != ra.M) continue;
+    int qs = -1;
+    for (int q = 0; q < 2; ++q)
+      if (pp.abase[q] == ra.out_start) qs = q;
+    if (qs < 0) continue;
+    const int32_t ob = pp.abase[1 - qs];
+    if (ob < ra.out_start + ra.M && ob + pp.num_nodes > ra.out_start) continue;   // other child range overlaps A
+    if (!sc.store || sc.overlap || rc.scratch_row >= 0 || rc.N != pp.num_nodes) continue;
+    bool inorder = true;
+    for (int32_t j = 0; inorder && j < rc.N; ++j)
+      inorder = sc.blocks[rc.blk_off + j / rc.cbs] + j % rc.cbs == pp.node_start + j;
+    if (!inorder) continue;
+    if (ra.s_row < 0) continue;
+    sc.gp_sum = a.idx;
+    sc.gp_prod = b.idx;
+    sc.gp_qs = qs;
+    sa.gp_done = true;
+    h->gbt_slots = 2;
+  }
+  // G buffers, from the last layer down: a layer packed by the element-flow
+  // product of the layer after it takes the other buffer.
+  int next_slot = 0;
+  for (int li = (int)h->layers.size() - 1; li >= 0; --li) {
+    if (h->layers[li].kind != PC_LAYER_SUM) continue;
+    SumPlan& sp = h->sums[h->layers[li].idx];
+    sp.gbt_slot = sp.gp_done ? 1 - next_slot : 0;
+    next_slot = sp.gbt_slot;
+  }
   return h;
 }
 

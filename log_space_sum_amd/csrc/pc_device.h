@@ -94,6 +94,7 @@ struct WsView {
   int64_t theta_plane, thetaT_plane;
   uint16_t* ebt;        // batch-major E of the current layer [B_pad, ebt_cols] per plane
   uint16_t* gbt;        // batch-major G of the current layer [B_pad, gbt_cols] per plane
+  uint16_t* gbt2;       // the second G buffer (element-flow product epilogues)
   int64_t ebt_plane, gbt_plane;
   int32_t ebt_cols, gbt_cols;
   uint16_t* earena;     // node-major E rows [rows, B_padK] per plane (kept)

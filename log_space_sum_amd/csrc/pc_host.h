@@ -90,6 +90,18 @@ struct SumPlan {
   // (epi_max).
   int epi_prod = -1, epi_qs = -1, epi_mrow = -1;
   bool epi_max = false;
+  // Element-flow product epilogue: this layer's element-flow product also does
+  // the scaled-flow packing of sum layer gp_sum (the backward of the affine
+  // two-child product layer gp_prod between them: the product node's flow
+  // goes to both its children, g = f / S of gp_sum's nodes into both operand
+  // layouts).  gp_sum's own packing launch is then skipped (gp_done), when the
+  // batch is a multiple of 256 (no padded samples in either layout).
+  int gp_sum = -1, gp_prod = -1, gp_qs = -1;
+  bool gp_done = false;
+  // Batch-major G buffer of the layer while those epilogues run: a layer whose
+  // G is written during the next layer's element-flow product uses the other
+  // buffer than that product's operand.
+  int gbt_slot = 0;
   // Per 64-row output tile row: the parent node in bwd_prod when that layer
   // gives each child a single parent, else the distinct-child index; -1 when
   // the output is not a child of bwd_prod.
@@ -138,6 +150,7 @@ struct Handle {
   int64_t earena_rows = 0, garena_rows = 0, s_rows = 0;
   int32_t m_rows = 0;
   int32_t max_ebt_cols = 0, max_gbt_cols = 0, max_scratch_rows = 0;
+  int gbt_slots = 1;                                   // 2 when an element-flow product epilogue packs G
   int32_t max_cats = 0;
   int32_t lowrank_slots = 0;
   int64_t lr_rows = 0;                 // LowRank: rows of the kept Z/S/U/W records (sum of group M)
@@ -178,11 +191,15 @@ void free_tables(Handle* h);
 // Effective precision mode for a batch (batches below 16 run fp32-level).
 inline int effective_mode(const Handle* h, int B) { return B < 16 ? PC_PREC_FP32 : h->mode; }
 
+// Element-flow product epilogues pack the next layer's G when fusion is on and
+// the batch needs no padded samples in either G layout.
+inline bool gp_active(const Handle* h, int B) { return h->opt_fuse && h->gbt_slots > 1 && B % 256 == 0; }
+
 // Workspace plan for a batch: byte offsets of every region.
 struct WsPlan {
   int B, B_pad, B_padK, mode;
   int pl[3][2];
-  size_t theta, thetaT, ebt, gbt, earena, garena, mkeys, ssum, scratch, tokT, bptr, bidx, lowrank;
+  size_t theta, thetaT, ebt, gbt, gbt2, earena, garena, mkeys, ssum, scratch, tokT, bptr, bidx, lowrank;
   size_t lrE, lrZ, lrS, lrU, lrW, lrC1, lrC2, lrP;   // LowRank regions (float32)
   size_t lrPK;                                       // LowRank fragment records of every LowRank group
   std::vector<int64_t> lr_pk_off;                    // per LowRank group: byte offset of its records

@@ -43,6 +43,17 @@ struct GemmArgs {
   // ep_base_o + i; node i is stored at ep_pstart + i, and the column maxima of
   // the product nodes go to keys row ep_mrow.
   int32_t ep_on, ep_qs, ep_base_s, ep_base_o, ep_pstart, ep_pcount, ep_mrow;
+  // element flows: the scaled-flow packing of the sum layer below the
+  // following product layer, done in the epilogue (gp_on).  Output row j (a
+  // product node, child j of this layer) passes its flow f to node
+  // gp_out_start + j of that sum layer (child gp_qs of the product node) and to
+  // node gp_other + j (its other child); g = f / S (S at row gp_s_row + j of
+  // the kept scaled sums) goes to node-major rows gp_g_row + j (gp_np_direct
+  // planes) and to batch-major columns gp_g_koff + j (gp_np_trans planes).
+  int32_t gp_on, gp_qs, gp_out_start, gp_other, gp_np_direct, gp_np_trans, gp_g_koff;
+  int64_t gp_s_row, gp_g_row, gp_direct_rows, gp_direct_plane, gp_trans_plane;
+  uint16_t* gp_direct;
+  uint16_t* gp_trans;
 };
 
 // Output tile shapes of the product kernel (M x N per workgroup).

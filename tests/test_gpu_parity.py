@@ -149,6 +149,10 @@ def test_fp32_needs_split(kind):
 @pytest.mark.parametrize("what,cfg_args,mode,all_fused", [
     ("hmm", dict(name="hmm4096", H=320, T=7, V=50, B=70), "auto", True),
     ("hmm ragged batch", dict(name="hmm4096", H=96, T=4, V=11, B=23), "fp32", True),
+    # batches of multiples of 256: the element-flow products also pack the
+    # next layer's scaled flows
+    ("hmm batch 256", dict(name="hmm4096", H=320, T=6, V=50, B=256), "auto", True),
+    ("hmm batch 512", dict(name="hmm4096", H=128, T=5, V=20, B=512), "fp32", True),
     ("hclt", dict(name="hclt", num_vars=30, H=48, K=12, B=33), "auto", False),
     ("block-sparse", dict(kind="block_sparse", seed=2, num_vars=6, K=5, in_blocks=3, block=24,
                           sum_blocks=3, depth_sums=2, B=29), "auto", False),
@@ -174,6 +178,10 @@ def test_fused_product_layers_identical(what, cfg_args, mode, all_fused):
     assert tp["product_fwd"][0] > 0 and tp["product_bwd"][0] > 0
     if all_fused:   # every product layer of an HMM sits between two sum layers
         assert tf["product_fwd"][0] == 0 and tf["product_bwd"][0] == 0
+    if all_fused and cfg["B"] % 256 == 0:
+        # every sum layer below a product layer is packed by the layer above
+        G.say(f"  scaled-flow launches fused/plain: {tf['scaled_flows'][0]}/{tp['scaled_flows'][0]}")
+        assert tf["scaled_flows"][0] < tp["scaled_flows"][0]
 
 
 @pytest.mark.parametrize("mode", MODES)
