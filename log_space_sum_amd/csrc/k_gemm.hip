@@ -805,7 +805,10 @@ static void launch_tile(int tile, int grid, const GemmArgs& a, hipStream_t s) {
   } else {
     if (tile == TILE_256x128) launch_shape<EPI, PA, PB, 256, 128, 2>(grid, a, s);
     else if (tile == TILE_128x256) launch_shape<EPI, PA, PB, 128, 256, 2>(grid, a, s);
-    else if (tile == TILE_128x64) launch_shape<EPI, PA, PB, 128, 64, 2>(grid, a, s);
+    // 128 x 64: waves side by side along M (32 x 64 each) when the first
+    // operand has more planes, else 2 x 2 (64 x 32 each): the fewer fragment
+    // reads per K step (LDS reads, not the matrix instructions, set the pace)
+    else if (tile == TILE_128x64) launch_shape<EPI, PA, PB, 128, 64, (PA > PB ? 4 : 2)>(grid, a, s);
     else launch_shape<EPI, PA, PB, 128, 128, 2>(grid, a, s);
   }
 }
