@@ -197,8 +197,9 @@ int pc_set_split(pc_handle h, int mode, int gemm_kind, int planes_a, int planes_
 
 /* Product-kernel tuning (advanced; results change only by float32 summation
  * order).  PC_OPT_LAYER_TILE: output tile of the per-layer forward and
- * element-flow products, 0 automatic (128 x 64), 1 128 x 128, 2 256 x 128,
- * 3 128 x 256, 4 128 x 64.
+ * element-flow products, 0 automatic (64 x 128 when the first operand has
+ * more bfloat16 planes than the second, else 128 x 64), 1 128 x 128,
+ * 2 256 x 128, 3 128 x 256, 4 128 x 64, 5 64 x 128.
  * PC_OPT_PARAM_TILE: tile of the parameter-flow product, 0 automatic
  * (128 x 128), 1 128 x 128, 2 256 x 256 (when the operand split allows).
  * PC_OPT_SPLIT_MAX: largest K split of a per-layer product (1, 2, 4 or 8;

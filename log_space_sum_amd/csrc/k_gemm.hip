@@ -809,6 +809,7 @@ static void launch_tile(int tile, int grid, const GemmArgs& a, hipStream_t s) {
     // operand has more planes, else 2 x 2 (64 x 32 each): the fewer fragment
     // reads per K step (LDS reads, not the matrix instructions, set the pace)
     else if (tile == TILE_128x64) launch_shape<EPI, PA, PB, 128, 64, (PA > PB ? 4 : 2)>(grid, a, s);
+    else if (tile == TILE_64x128) launch_shape<EPI, PA, PB, 64, 128, 2>(grid, a, s);
     else launch_shape<EPI, PA, PB, 128, 128, 2>(grid, a, s);
   }
 }

@@ -572,9 +572,9 @@ int pc_set_option(pc_handle hh, int option, int value) {
   try {
     Handle* h = checked(hh);
     if (option == PC_OPT_LAYER_TILE) {
-      if (value < 0 || value > 4) fail(PC_ERR_INVALID_ARG, "layer tile must be 0, 1, 2, 3 or 4");
+      if (value < 0 || value > 5) fail(PC_ERR_INVALID_ARG, "layer tile must be 0, 1, 2, 3, 4 or 5");
       h->opt_layer_tile = value == 1 ? TILE_128x128 : value == 2 ? TILE_256x128 : value == 3 ? TILE_128x256
-                        : value == 4 ? TILE_128x64 : TILE_AUTO;
+                        : value == 4 ? TILE_128x64 : value == 5 ? TILE_64x128 : TILE_AUTO;
     } else if (option == PC_OPT_PARAM_TILE) {
       if (value < 0 || value > 2) fail(PC_ERR_INVALID_ARG, "parameter tile must be 0, 1 or 2");
       h->opt_param_tile = value == 2 ? TILE_256x256 : value == 1 ? TILE_128x128 : TILE_AUTO;

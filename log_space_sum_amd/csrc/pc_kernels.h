@@ -57,7 +57,7 @@ struct GemmArgs {
 };
 
 // Output tile shapes of the product kernel (M x N per workgroup).
-enum GemmTile { TILE_AUTO = 0, TILE_128x128 = 1, TILE_256x128 = 2, TILE_256x256 = 3, TILE_128x256 = 4, TILE_128x64 = 5 };
+enum GemmTile { TILE_AUTO = 0, TILE_128x128 = 1, TILE_256x128 = 2, TILE_256x256 = 3, TILE_128x256 = 4, TILE_128x64 = 5, TILE_64x128 = 6 };
 
 struct GemmShape {
   int tile;      // GemmTile
@@ -79,19 +79,24 @@ constexpr int gemm_stages(int pa, int pb, int mt, int nt) {
 
 // Shape of a forward / element-flow launch over a layer whose outputs span
 // `rows256` 256-row blocks, batch padded to B_pad, largest padded K `kpad`.
-// Automatic: 128 x 64 tiles (on the 4096-node HMM layers: at batch 512, 256
-// tiles with the full K, no partial tiles and every CU running an epilogue,
-// 3% faster per step than 128 x 128 split in two; at batch 128, split in four,
-// 8% faster than 128 x 128 split in eight).  The K split (a power of two up to
-// split_max) grows until the launch has 256 workgroups, keeping >= 4 slices
-// per split.
+// Automatic: 8192-output tiles, 64 x 128 when the first operand has more
+// planes than the second, else 128 x 64.  A tile loads pa * MT + pb * NT
+// elements per K step, least at MT / NT = pb / pa, and the per-CU request
+// rate, not the matrix instructions, sets the pace (on the 4096-node HMM
+// layers at batch 512, 256 tiles with the full K: forward products 64 x 128
+// 8.6% faster than 128 x 64, element flows 128 x 64 2% faster than 64 x 128;
+// 128 x 64 was 3% faster per step than 128 x 128 split in two and, at batch
+// 128 split in four, 8% faster than 128 x 128 split in eight).  The K split
+// (a power of two up to split_max) grows until the launch has 256 workgroups,
+// keeping >= 4 slices per split.
 inline GemmShape layer_shape(int rows256, int B_pad, int kpad, int pa, int pb, int opt_tile, int split_max) {
   GemmShape g{};
-  if (opt_tile == TILE_AUTO) opt_tile = TILE_128x64;
+  if (opt_tile == TILE_AUTO) opt_tile = pa > pb ? TILE_64x128 : TILE_128x64;
   g.tile = opt_tile == TILE_256x128 ? TILE_256x128
          : opt_tile == TILE_128x256 ? TILE_128x256
-         : opt_tile == TILE_128x64 ? TILE_128x64 : TILE_128x128;
-  g.mt = g.tile == TILE_256x128 ? 256 : 128;
+         : opt_tile == TILE_128x64 ? TILE_128x64
+         : opt_tile == TILE_64x128 ? TILE_64x128 : TILE_128x128;
+  g.mt = g.tile == TILE_256x128 ? 256 : g.tile == TILE_64x128 ? 64 : 128;
   g.nt = g.tile == TILE_128x256 ? 256 : g.tile == TILE_128x64 ? 64 : 128;
   g.tiles = rows256 * (256 / g.mt) * (B_pad / g.nt);
   const int ksteps = kpad / gemm_kt(pa, pb, g.mt, g.nt);

@@ -185,9 +185,9 @@ def test_fused_product_layers_identical(what, cfg_args, mode, all_fused):
 
 
 @pytest.mark.parametrize("mode", MODES)
-@pytest.mark.parametrize("tile", [1, 2, 3, 4])
+@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5])
 def test_layer_tile_options(tile, mode):
-    """Every per-layer product tile shape (128x128, 256x128, 128x256, 128x64)
+    """Every per-layer product tile shape (128x128, 256x128, 128x256, 128x64, 64x128)
     meets the tolerances; a batch of 300 leaves a ragged last column tile."""
     cfg = make_config("hmm4096", H=320, T=5, V=50, B=300)
     _full(cfg, mode, f"hmm 320x5 layer tile {tile}", options=[("layer_tile", tile)])
