@@ -205,7 +205,7 @@ def main():
                     help="samples of the LowRank workload the oracle baseline runs on")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--layer-tile", type=int, default=0, help="product-kernel option: 0 auto, 1 128x128, 2 256x128, 3 128x256, 4 128x64, 5 64x128")
-    ap.add_argument("--param-tile", type=int, default=0, help="product-kernel option: 0 auto (128x128), 1 128x128, 2 256x256")
+    ap.add_argument("--param-tile", type=int, default=0, help="product-kernel option: 0 auto, 1 128x128, 2 256x256, 3 128x256")
     ap.add_argument("--split-max", type=int, default=8, help="largest K split of a per-layer product")
     ap.add_argument("--param-chunk", type=int, default=0,
                     help="tied copies per parameter-flow launch on a second stream (0: one launch at the end)")

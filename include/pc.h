@@ -201,7 +201,9 @@ int pc_set_split(pc_handle h, int mode, int gemm_kind, int planes_a, int planes_
  * more bfloat16 planes than the second, else 128 x 64), 1 128 x 128,
  * 2 256 x 128, 3 128 x 256, 4 128 x 64, 5 64 x 128.
  * PC_OPT_PARAM_TILE: tile of the parameter-flow product, 0 automatic
- * (128 x 128), 1 128 x 128, 2 256 x 256 (when the operand split allows).
+ * (128 x 256 when the first operand has more bfloat16 planes than the
+ * second, else 128 x 128), 1 128 x 128, 2 256 x 256 (when the operand split
+ * allows), 3 128 x 256.
  * PC_OPT_SPLIT_MAX: largest K split of a per-layer product (1, 2, 4 or 8;
  * default 8).  PC_OPT_FUSE: 1 (default) evaluates a product layer inside the
  * adjacent sum layer's memory-bound kernels where the layout allows it (the

@@ -296,14 +296,18 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
     kbeg = split * kst / S;
     kend = (split + 1) * kst / S;
   } else {
+    // tile prefix of the block sequence: 256 x 256 tiles, twice as many
+    // 128 x 256 tiles (blocks are padded to 256 both ways), or 128 x 128
     const int b = (MT == 256)
         ? find_last_le(a.blocks, a.ngroups, tile, [](const BlockRec& r) { return r.pt256; })
+        : (NT == 256)
+        ? find_last_le(a.blocks, a.ngroups, tile, [](const BlockRec& r) { return 2 * r.pt256; })
         : find_last_le(a.blocks, a.ngroups, tile, [](const BlockRec& r) { return r.pt128; });
     bl = a.blocks[b];
     const int Mp = (bl.M + ROW_PAD - 1) / ROW_PAD * ROW_PAD;
     const int Np = (bl.N + ROW_PAD - 1) / ROW_PAD * ROW_PAD;
     const int ntn = Np / NT, mtn = Mp / MT;
-    const int lt = tile - ((MT == 256) ? bl.pt256 : bl.pt128);
+    const int lt = tile - ((MT == 256) ? bl.pt256 : (NT == 256) ? 2 * bl.pt256 : bl.pt128);
     // tiles in groups of up to 4 tile rows, column-major inside a group, so
     // the 32 workgroups an XCD runs at once cover about 4 x 8 tiles and
     // share both operands' panels in its L2
@@ -801,7 +805,8 @@ static void launch_tile(int tile, int grid, const GemmArgs& a, hipStream_t s) {
         return;
       }
     }
-    launch_shape<EPI, PA, PB, 128, 128, 2>(grid, a, s);
+    if (tile == TILE_128x256) launch_shape<EPI, PA, PB, 128, 256, 2>(grid, a, s);
+    else launch_shape<EPI, PA, PB, 128, 128, 2>(grid, a, s);
   } else {
     if (tile == TILE_256x128) launch_shape<EPI, PA, PB, 256, 128, 2>(grid, a, s);
     else if (tile == TILE_128x256) launch_shape<EPI, PA, PB, 128, 256, 2>(grid, a, s);

@@ -183,13 +183,17 @@ GemmShape layer_gemm_shape(const Handle* h, const SumPlan& sp, int kind, int B_p
 
 GemmShape param_gemm_shape(const Handle* h, int pa, int pb) {
   GemmShape g{};
-  // 128 x 128 measured faster than 256 x 256 on the HMM-4096 parameter flows
-  // (4x the workgroups: the tail of one full wave of long tiles is gone)
+  // Automatic: 128 x 256 when the first operand (G) has more planes than the
+  // second, else 128 x 128: fewer bytes per output at the same K (HMM-4096
+  // parameter flows, G split in two: 128 x 256 7% faster than 128 x 128, which
+  // was faster than 256 x 256, whose one long tile per CU leaves a tail)
   const bool big = pa + pb <= 3 && h->opt_param_tile == TILE_256x256;   // rows are padded to 256
-  g.tile = big ? TILE_256x256 : TILE_128x128;
-  g.mt = g.nt = big ? 256 : 128;
+  const bool wide = !big && (h->opt_param_tile == TILE_128x256 || (h->opt_param_tile == TILE_AUTO && pa > pb));
+  g.tile = big ? TILE_256x256 : wide ? TILE_128x256 : TILE_128x128;
+  g.mt = big ? 256 : 128;
+  g.nt = big || wide ? 256 : 128;
   g.splitk = 1;
-  g.tiles = big ? h->param_tiles256 : h->param_tiles128;
+  g.tiles = big ? h->param_tiles256 : wide ? 2 * h->param_tiles256 : h->param_tiles128;
   return g;
 }
 
@@ -576,8 +580,8 @@ int pc_set_option(pc_handle hh, int option, int value) {
       h->opt_layer_tile = value == 1 ? TILE_128x128 : value == 2 ? TILE_256x128 : value == 3 ? TILE_128x256
                         : value == 4 ? TILE_128x64 : value == 5 ? TILE_64x128 : TILE_AUTO;
     } else if (option == PC_OPT_PARAM_TILE) {
-      if (value < 0 || value > 2) fail(PC_ERR_INVALID_ARG, "parameter tile must be 0, 1 or 2");
-      h->opt_param_tile = value == 2 ? TILE_256x256 : value == 1 ? TILE_128x128 : TILE_AUTO;
+      if (value < 0 || value > 3) fail(PC_ERR_INVALID_ARG, "parameter tile must be 0, 1, 2 or 3");
+      h->opt_param_tile = value == 3 ? TILE_128x256 : value == 2 ? TILE_256x256 : value == 1 ? TILE_128x128 : TILE_AUTO;
     } else if (option == PC_OPT_SPLIT_MAX) {
       if (value != 1 && value != 2 && value != 4 && value != 8) fail(PC_ERR_INVALID_ARG, "split must be 1, 2, 4 or 8");
       h->opt_split_max = value;
@@ -896,7 +900,7 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
         g.copy_hi = ch.hi;
         GemmShape shp = pshp;
         const int64_t Mp = round_up(bl.M, ROW_PAD), Np = round_up(bl.N, ROW_PAD);
-        g.tile0 = shp.mt == 256 ? bl.pt256 : bl.pt128;
+        g.tile0 = shp.mt == 256 ? bl.pt256 : shp.nt == 256 ? 2 * bl.pt256 : bl.pt128;
         shp.tiles = (int)((Mp / shp.mt) * (Np / shp.nt));
         Timed t(h, KK_PARAM, side);
         launch_gemm(EPI_PARAM, p.pl[GK_PARAM][0], p.pl[GK_PARAM][1], shp, g, side);

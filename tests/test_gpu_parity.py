@@ -194,6 +194,20 @@ def test_layer_tile_options(tile, mode):
 
 
 @pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("tile", [1, 2, 3])
+@pytest.mark.parametrize("what,cfg_args", [
+    ("hmm", dict(name="hmm4096", H=320, T=5, V=50, B=300)),
+    ("hclt", dict(name="hclt", num_vars=30, H=48, K=12, B=33)),
+])
+def test_param_tile_options(what, cfg_args, tile, mode):
+    """Every parameter-flow tile shape (128x128, 256x256 where the operand
+    split allows it, 128x256) meets the tolerances, on one tied block (HMM)
+    and on many blocks (HCLT)."""
+    cfg = make_config(**cfg_args)
+    _full(cfg, mode, f"{what} param tile {tile}", options=[("param_tile", tile)])
+
+
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("what,cfg_args,chunk", [
     ("hmm", dict(name="hmm4096", H=320, T=7, V=50, B=70), 1),
     ("hmm", dict(name="hmm4096", H=320, T=7, V=50, B=70), 4),
