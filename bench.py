@@ -127,9 +127,16 @@ def bench_lowrank(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    run = step
+    if args.graph:
+        g = L.StepGraph(h, B, tokens, params, vals, flows, pflows, ll, 0, lowrank=lr, grads=grads, ws=ws,
+                        em=(1.0, 0.0))
+        run = g.replay
+        run()
+        torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        run()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) / args.steps * 1e3
     L.pc_set_timing(h, True)
@@ -154,6 +161,7 @@ def bench_lowrank(args):
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16-split" if args.mode == "auto" else "bf16x6-split", "data": "synthetic",
         "config": {"workload": "lowrank hmm1024x64 symbols 512 rank 16 batch 64 fwd+bwd+em", "precision_mode": args.mode,
+                   "hip_graph": bool(args.graph),
                    "global_batch": B},
         "kernel_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in kt.items() if v[0]},
         "roofline": {"kernel": dom, "bound": "alu", "achieved": round(achieved, 2), "peak": PEAK_EXP_G,
@@ -204,6 +212,8 @@ def main():
     ap.add_argument("--lr-cpu-sample", type=int, default=24,
                     help="samples of the LowRank workload the oracle baseline runs on")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--graph", type=int, default=0, choices=[0, 1],
+                    help="time replays of the step recorded as a HIP graph (1) or eager launches (0; measured the same: the queue already runs ahead of the host)")
     ap.add_argument("--layer-tile", type=int, default=0, help="product-kernel option: 0 auto, 1 128x128, 2 256x128, 3 128x256, 4 128x64, 5 64x128")
     ap.add_argument("--param-tile", type=int, default=0, help="product-kernel option: 0 auto, 1 128x128, 2 256x256, 3 128x256")
     ap.add_argument("--split-max", type=int, default=8, help="largest K split of a per-layer product")
@@ -301,9 +311,16 @@ def bench_circuit(args, cfg, metric, workload, context):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    run = step
+    if args.graph:
+        # the whole step recorded once as a HIP graph, replayed per step
+        g = L.StepGraph(h, B, tokens, params, vals, flows, pflows, ll, flags, ws=ws, em=(1.0, 0.0))
+        run = g.replay
+        run()
+        torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        run()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     ms = dt / args.steps * 1e3
@@ -342,7 +359,7 @@ def bench_circuit(args, cfg, metric, workload, context):
         "vs_baseline": None,
         "dtype": "bf16" if args.mode == "auto" else "bf16x3-split",
         "data": "synthetic",
-        "config": {"workload": workload, "precision_mode": args.mode, "global_batch": B},
+        "config": {"workload": workload, "precision_mode": args.mode, "global_batch": B, "hip_graph": bool(args.graph)},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "sum_layer_kernels_ms": round(sum_ms, 4),
         "sum_layer_kernels_tflops": round(flops / (sum_ms * 1e-3) / 1e12, 3) if sum_ms > 0 else None,

@@ -340,7 +340,69 @@ def pc_em_step(h: Handle, params, param_flows, step_size=1.0, pseudocount=0.0, s
                             C.c_float(step_size), C.c_float(pseudocount), _stream(stream)))
 
 
-def workspace(h: Handle, batch: int, device="cuda"):
-    """A workspace tensor (uint8) of pc_workspace_bytes(h, batch) bytes."""
+def workspace(h: Handle, batch: int, device="cuda", all_modes=False):
+    """A workspace tensor (uint8) of pc_workspace_bytes(h, batch) bytes; with
+    all_modes, the largest over both precision modes (so the handle's mode
+    can change while the workspace stays)."""
     n = pc_workspace_bytes(h, batch)
+    if all_modes:
+        mode = pc_get_precision(h)
+        for m in (PC_PREC_AUTO, PC_PREC_FP32):
+            pc_set_precision(h, m)
+            n = max(n, pc_workspace_bytes(h, batch))
+        pc_set_precision(h, mode)
     return _torch().empty(max(n, 1), dtype=_torch().uint8, device=device)
+
+
+class StepGraph:
+    """One pass (forward, backward and, with ``em=(step_size, pseudocount)``,
+    the EM update) recorded once as a HIP graph on fixed buffers and replayed
+    by ``replay()``: every launch of the pass is one graph node, so a replay
+    pays no per-launch host cost.  The graph is recorded again when the
+    handle's precision mode changed since (the pass's kernels depend on it);
+    after any other pc_set_option, make a new StepGraph.  Recording turns the
+    handle's per-kernel timing off (its events cannot be graph nodes).  The
+    buffers and the workspace must stay allocated, and are read and written in
+    place at every replay (a workspace passed in must be large enough for every
+    mode the handle will run in: ``workspace(..., all_modes=True)``); ``zero_param_flows`` clears the parameter flows at
+    the start of each pass (a fill kernel, not a memset node)."""
+
+    def __init__(self, h: Handle, batch: int, tokens, params, node_vals, node_flows, param_flows,
+                 ll=None, flags=0, lowrank=None, grads=None, ws=None, em=None, zero_param_flows=True):
+        self.h, self.batch = h, int(batch)
+        self.args = (tokens, params, node_vals, node_flows, param_flows, ll, flags, lowrank, grads)
+        self.ws = ws if ws is not None else workspace(h, batch, node_vals.device, all_modes=True)
+        self.em = em
+        self.zero = zero_param_flows
+        self.graph = None
+        self.mode = None
+        # one eager forward + backward first: anything the library sets up on
+        # its first call (a second stream for chunked parameter flows) exists
+        # before recording; the EM update is left out so parameters do not move
+        pc_set_timing(h, False)
+        self._pass(None, with_em=False)
+        _torch().cuda.synchronize()
+        self._record()
+
+    def _pass(self, stream, with_em=True):
+        tokens, params, vals, flows, pflows, ll, flags, lowrank, grads = self.args
+        s = stream.cuda_stream if stream is not None else None
+        if self.zero:
+            pflows.zero_()
+        pc_forward(self.h, self.batch, tokens, params, vals, ll, lowrank, self.ws, s)
+        pc_backward(self.h, self.batch, tokens, params, vals, flows, pflows, flags, lowrank, grads, self.ws, s)
+        if with_em and self.em is not None:
+            pc_em_step(self.h, params, pflows, self.em[0], self.em[1], s)
+
+    def _record(self):
+        torch = _torch()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self._pass(torch.cuda.current_stream())
+        self.graph = g
+        self.mode = pc_get_precision(self.h)
+
+    def replay(self):
+        if pc_get_precision(self.h) != self.mode:
+            self._record()
+        self.graph.replay()
