@@ -793,9 +793,29 @@ __global__ __launch_bounds__(256) void k_pack(SumArgs a) {
   }
 }
 
+// Split 4 values into np bfloat16 planes and store each plane as 8 bytes.
+__device__ __forceinline__ void split_store4(const float (&x)[4], int np, uint16_t* dst, int64_t plane) {
+  float r[4] = {x[0], x[1], x[2], x[3]};
+  for (int p = 0; p < np; ++p) {
+    uint32_t w[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const uint16_t h0 = f2bf(r[2 * e]), h1 = f2bf(r[2 * e + 1]);
+      r[2 * e] -= bf2f(h0);
+      r[2 * e + 1] -= bf2f(h1);
+      w[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+    }
+    *(uint2*)(dst + p * plane) = make_uint2(w[0], w[1]);
+  }
+}
+
 // Weights of every block split into planes, row-major [M_pad, N_padK] (forward
-// operand) and transposed [N_pad, M_padK] (element-flow operand).
-__global__ void k_theta_pack(ThetaArgs a) {
+// operand) and transposed [N_pad, M_padK] (element-flow operand).  A 64 x 64
+// tile per workgroup; each thread takes 4 consecutive columns of 4 rows (all
+// four loads issued first, 16-byte loads when the block's rows are 16-byte
+// aligned), and after the LDS transpose 4 consecutive rows of 4 columns, so
+// every plane store is 8 bytes.
+__global__ __launch_bounds__(256) void k_theta_pack(ThetaArgs a) {
   __shared__ float tile[64][65];
   const int t = blockIdx.x;
   const int bi = last_le(a.blocks, a.nblocks, t, [](const BlockRec& r) { return r.pk_start; });
@@ -803,20 +823,39 @@ __global__ void k_theta_pack(ThetaArgs a) {
   const int ntj = (bl.N + ROW_PAD - 1) / ROW_PAD * (ROW_PAD / 64);
   const int lt = t - bl.pk_start;
   const int i0 = (lt / ntj) * 64, j0 = (lt % ntj) * 64;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int NpK = (bl.N + K_PAD - 1) / K_PAD * K_PAD, MpK = (bl.M + K_PAD - 1) / K_PAD * K_PAD;
   const int64_t Mp = (bl.M + ROW_PAD - 1) / ROW_PAD * ROW_PAD, Np = (bl.N + ROW_PAD - 1) / ROW_PAD * ROW_PAD;
-  const int j = j0 + lane;
-  for (int r = w; r < 64; r += 4) {
-    const int i = i0 + r;
-    const float x = (i < bl.M && j < bl.N) ? a.params[bl.param_offset + (int64_t)i * bl.N + j] : 0.0f;
-    tile[r][lane] = x;
-    if (j < NpK) split_store(x, a.np_fwd, a.theta + bl.th_off + panel(i, j, Mp), a.theta_plane);
+  const bool vec = ((bl.param_offset | (int64_t)bl.N) & 3) == 0;
+  const int tid = threadIdx.x, rr = tid >> 4, c4 = (tid & 15) * 4;
+  const int j = j0 + c4;
+  float x[4][4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = i0 + rr + 16 * q;
+    const float* src = a.params + bl.param_offset + (int64_t)i * bl.N + j;
+    if (vec) {
+      const float4 v = (i < bl.M && j < bl.N) ? *(const float4*)src : make_float4(0.f, 0.f, 0.f, 0.f);
+      x[q][0] = v.x; x[q][1] = v.y; x[q][2] = v.z; x[q][3] = v.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[q][e] = (i < bl.M && j + e < bl.N) ? src[e] : 0.0f;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = rr + 16 * q;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tile[r][c4 + e] = x[q][e];
+    if (j < NpK) split_store4(x[q], a.np_fwd, a.theta + bl.th_off + panel(i0 + r, j, Mp), a.theta_plane);
   }
   __syncthreads();
-  for (int r = w; r < 64; r += 4) {
-    const int jj = j0 + r, i = i0 + lane;
-    if (i < MpK) split_store(tile[lane][r], a.np_elem, a.thetaT + bl.tht_off + panel(jj, i, Np), a.thetaT_plane);
+  const int i = i0 + c4;                       // 4 consecutive rows of the block
+  if (i >= MpK) return;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int jl = rr + 16 * q;
+    const float y[4] = {tile[c4][jl], tile[c4 + 1][jl], tile[c4 + 2][jl], tile[c4 + 3][jl]};
+    split_store4(y, a.np_elem, a.thetaT + bl.tht_off + panel(j0 + jl, i, Np), a.thetaT_plane);
   }
 }
 
@@ -853,8 +892,23 @@ __global__ __launch_bounds__(256) void k_em(EmArgs a, int total_rows) {
   const RowSeg sg = a.segs[s];
   const int64_t off = sg.offset + (int64_t)(row - sg.row_start) * sg.rlen;
   const bool vec = ((off | (int64_t)sg.rlen) & 3) == 0;   // 16-byte rows
+  // rows of up to 1024 (16-byte aligned): the lane's four 16-byte chunks are
+  // loaded at once and kept for the update, along with the parameters
+  constexpr int RU = 4;
+  const bool held = vec && sg.rlen <= RU * 256;
+  float4 fh[RU], ph[RU];
   float acc = 0.0f;
-  if (vec) {
+  if (held) {
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+      const int j = lane * 4 + u * 256;
+      fh[u] = j < sg.rlen ? *(const float4*)(a.pflows + off + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+      ph[u] = j < sg.rlen ? *(const float4*)(a.params + off + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < RU; ++u)
+      if (lane * 4 + u * 256 < sg.rlen) acc += ((fh[u].x + fh[u].y) + fh[u].z) + fh[u].w;
+  } else if (vec) {
     for (int j = lane * 4; j < sg.rlen; j += 256) {
       const float4 f = *(const float4*)(a.pflows + off + j);
       acc += ((f.x + f.y) + f.z) + f.w;
@@ -868,7 +922,20 @@ __global__ __launch_bounds__(256) void k_em(EmArgs a, int total_rows) {
   if (!(tot > 0.0f)) return;                    // a row without flow (and no pseudocount) keeps theta
   const float add = a.pseudo / (float)sg.rlen;
   const float keep = 1.0f - a.step;
-  if (vec) {
+  if (held) {
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+      const int j = lane * 4 + u * 256;
+      if (j >= sg.rlen) continue;
+      const float4 f = fh[u];
+      float4 p = ph[u];
+      p.x = keep * p.x + a.step * ((f.x + add) / tot);
+      p.y = keep * p.y + a.step * ((f.y + add) / tot);
+      p.z = keep * p.z + a.step * ((f.z + add) / tot);
+      p.w = keep * p.w + a.step * ((f.w + add) / tot);
+      *(float4*)(a.params + off + j) = p;
+    }
+  } else if (vec) {
     for (int j = lane * 4; j < sg.rlen; j += 256) {
       const float4 f = *(const float4*)(a.pflows + off + j);
       float4 p = *(const float4*)(a.params + off + j);
