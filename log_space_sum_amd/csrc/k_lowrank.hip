@@ -222,7 +222,16 @@ __global__ __launch_bounds__(256) void k_lr_coef(LRArgs a) {
     return;
   }
   const int64_t x = (int64_t)b * a.M + i;
-  const float f = a.flows[(int64_t)(a.out_start + i) * a.B + b];
+  float f;
+  if (a.fp_on) {
+    // the product node's flow, added to zero as the product backward does,
+    // stored for both its children
+    f = 0.0f + a.flows[(int64_t)(a.fp_pstart + i) * a.B + b];
+    a.out_flows[(int64_t)(a.out_start + i) * a.B + b] = f;
+    a.out_flows[(int64_t)(a.fp_other + i) * a.B + b] = f;
+  } else {
+    f = a.flows[(int64_t)(a.out_start + i) * a.B + b];
+  }
   const float Z = a.Z[x], S = a.S[x];
   const bool ok = f != 0.0f && Z > 0.0f && S > 0.0f;
   const float c1 = ok ? f / S : 0.0f, c2 = ok ? f / Z : 0.0f;

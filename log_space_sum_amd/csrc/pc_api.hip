@@ -914,6 +914,12 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
         const SumPlan& sp = h->sums[r.idx];
         for (int gi = 0; gi < (int)sp.groups.size(); ++gi) {
           LRArgs la = lr_args(c, sp, gi, lowrank, params, vals, node_flows);
+          if (h->opt_fuse && sp.lr_prod >= 0) {
+            const ProductPlan& pp = h->prods[sp.lr_prod];
+            la.fp_on = 1;
+            la.fp_pstart = pp.node_start;
+            la.fp_other = pp.abase[1 - sp.lr_qs];
+          }
           if (h->opt_lr_pack == 1) {
             Timed t(h, KK_SPLIT, c.s);
             lr_pack_group(c, sp, gi, lowrank);

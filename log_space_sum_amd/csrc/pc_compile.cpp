@@ -652,6 +652,29 @@ Handle* compile_layout(const pc_circuit_desc* d) {
     sa.gp_done = true;
     h->gbt_slots = 2;
   }
+  // LowRank coefficient kernels with the product backward (see
+  // SumPlan::lr_prod): single-group LowRank layer A, affine two-child product
+  // layer P right after it whose child range q_s is A's outputs in order, P
+  // the single parent and first writer of every child.
+  for (size_t li = 0; li + 1 < h->layers.size(); ++li) {
+    const LayerRef a = h->layers[li], b = h->layers[li + 1];
+    if (a.kind != PC_LAYER_SUM || b.kind != PC_LAYER_PRODUCT) continue;
+    SumPlan& sa = h->sums[a.idx];
+    ProductPlan& pp = h->prods[b.idx];
+    if (!sa.lowrank || sa.groups.size() != 1 || pp.bwd_fused) continue;
+    if (!pp.affine || pp.max_deg != 2 || !pp.single_parent || !pp.store) continue;
+    const GroupRec& ra = sa.groups[0];
+    if (pp.num_nodes != ra.M) continue;
+    int qs = -1;
+    for (int q = 0; q < 2; ++q)
+      if (pp.abase[q] == ra.out_start) qs = q;
+    if (qs < 0) continue;
+    const int32_t ob = pp.abase[1 - qs];
+    if (ob < ra.out_start + ra.M && ob + pp.num_nodes > ra.out_start) continue;
+    sa.lr_prod = b.idx;
+    sa.lr_qs = qs;
+    pp.bwd_fused = true;
+  }
   // G buffers, from the last layer down: a layer packed by the element-flow
   // product of the layer after it takes the other buffer.
   int next_slot = 0;

@@ -112,6 +112,9 @@ struct EmArgs {
 struct LRArgs {
   int32_t B, M, N, krank;
   int32_t out_start, m_row, cbs, blk_off, scratch_row, store;
+  // coefficients: the following product layer's backward first (fp_on): the
+  // flow of product node fp_pstart + i goes to output i and to node fp_other + i
+  int32_t fp_on, fp_pstart, fp_other;
   const int32_t* chblocks;
   const float* theta;
   const float* A;

@@ -98,6 +98,10 @@ struct SumPlan {
   // batch is a multiple of 256 (no padded samples in either layout).
   int gp_sum = -1, gp_prod = -1, gp_qs = -1;
   bool gp_done = false;
+  // LowRank layer: the affine two-child product layer lr_prod after it, fed by
+  // its outputs as child lr_qs, runs its backward in this layer's coefficient
+  // kernel (the node's flow copied to both children before f / S, f / Z).
+  int lr_prod = -1, lr_qs = -1;
   // Batch-major G buffer of the layer while those epilogues run: a layer whose
   // G is written during the next layer's element-flow product uses the other
   // buffer than that product's operand.

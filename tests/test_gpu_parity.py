@@ -156,7 +156,7 @@ def test_fp32_needs_split(kind):
     ("hclt", dict(name="hclt", num_vars=30, H=48, K=12, B=33), "auto", False),
     ("block-sparse", dict(kind="block_sparse", seed=2, num_vars=6, K=5, in_blocks=3, block=24,
                           sum_blocks=3, depth_sums=2, B=29), "auto", False),
-    ("lowrank hmm", dict(name="lowrank", H=40, T=4, V=7, B=23, rank=5), "auto", False),
+    ("lowrank hmm", dict(name="lowrank", H=40, T=4, V=7, B=23, rank=5), "auto", True),
 ])
 def test_fused_product_layers_identical(what, cfg_args, mode, all_fused):
     """Product layers evaluated inside the adjacent sum layers' column-max and
@@ -176,7 +176,7 @@ def test_fused_product_layers_identical(what, cfg_args, mode, all_fused):
     G.say(f"  launches fused/plain: product fwd {tf['product_fwd'][0]}/{tp['product_fwd'][0]}, "
           f"product bwd {tf['product_bwd'][0]}/{tp['product_bwd'][0]}")
     assert tp["product_fwd"][0] > 0 and tp["product_bwd"][0] > 0
-    if all_fused:   # every product layer of an HMM sits between two sum layers
+    if all_fused:   # every product layer of an HMM (LowRank or not) sits between two sum layers
         assert tf["product_fwd"][0] == 0 and tf["product_bwd"][0] == 0
     if all_fused and cfg["B"] % 256 == 0:
         # every sum layer below a product layer is packed by the layer above
