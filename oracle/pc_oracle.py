@@ -31,7 +31,13 @@ What it computes (plain definitions, float64, numpy):
   theta_b = theta * exp(A_b B_b) / Z_b, Z_b[i] = sum_j theta[i,j] exp(A_b B_b)[i,j],
   built explicitly per sample; the layer is the sum layer above with theta_b.
   Its backward (Training) writes the element flows, the parameter flows
-  F+ = sum_b of the edge flows under theta_b, and dLL/dA, dLL/dB.
+  F+ = sum_b of the edge flows under theta_b, and dLL/dA, dLL/dB;
+* LowRank denominator statistic (pyjuice.parameterizations.LowRank, Training,
+  apply_z_correction): W[i,j] = sum over samples and tied copies of
+  f_b[i] * exp(A_b B_b)[i,j] / Z_b[i], in the parameter flows' layout, and the
+  conditional M-step theta <- normalize(theta * F+ / F-) with F- = theta * W,
+  i.e. normalize(F+ / W) on the entries with theta > 0 and W > 0 (0 elsewhere),
+  normalised as the plain EM step (same step size and pseudocount).
 """
 from __future__ import annotations
 
@@ -138,6 +144,7 @@ def backward(circ: Circuit, params, V, tokens=None, lowrank=None, seed_flows=Non
     else:
         F[circ.root] = 1.0
     PF = np.zeros(circ.num_params)
+    ZF = np.zeros(circ.num_params)
     dA = {}
     dB = {}
     for layer in reversed(circ.layers):
@@ -158,11 +165,12 @@ def backward(circ: Circuit, params, V, tokens=None, lowrank=None, seed_flows=Non
                     dAg = np.zeros(A.shape)
                     dBg = np.zeros(Bf.shape)
                     pf = np.zeros_like(th)
+                    zf = np.zeros_like(th)
                     fc = np.zeros_like(C)
                     for b in range(B):
                         Ab = np.asarray(A[b], np.float64)
                         Bb = np.asarray(Bf[b], np.float64)
-                        tb, _, _ = lowrank_effective(th, Ab, Bb)
+                        tb, _, Z = lowrank_effective(th, Ab, Bb)
                         eps = tb * E[:, b][None, :] * gm[:, b][:, None]  # edge flows
                         fc[:, b] = eps.sum(axis=0)
                         pf += eps
@@ -170,8 +178,13 @@ def backward(circ: Circuit, params, V, tokens=None, lowrank=None, seed_flows=Non
                         D = eps - fi[:, None] * tb                       # dLL/d(A_b B_b)
                         dAg[b] = D @ Bb.T
                         dBg[b] = Ab.T @ D
+                        # denominator statistic: f_b[i] exp(A_b B_b)[i, j] / Z_b[i]
+                        with np.errstate(divide="ignore", invalid="ignore"):
+                            fz = np.where((fi != 0) & (Z > 0), fi / Z, 0.0)
+                        zf += fz[:, None] * np.exp(Ab @ Bb)
                     F[ch] += fc
                     PF[g.param_offset:g.param_offset + th.size] += pf.reshape(-1)
+                    ZF[g.param_offset:g.param_offset + th.size] += zf.reshape(-1)
                     dA[g.lowrank] = dAg
                     dB[g.lowrank] = dBg
                 else:
@@ -188,7 +201,33 @@ def backward(circ: Circuit, params, V, tokens=None, lowrank=None, seed_flows=Non
             np.add.at(PF, idx.reshape(-1), F[layer.node_start:layer.node_start + layer.num_nodes].reshape(-1))
         elif isinstance(layer, InputExternal):
             pass
-    return dict(flows=F, param_flows=PF, dA=dA, dB=dB)
+    return dict(flows=F, param_flows=PF, dA=dA, dB=dB, z_flows=ZF)
+
+
+def lowrank_param_ranges(circ: Circuit):
+    """(offset, length) of the weight block of every LowRank group."""
+    out = []
+    for layer in circ.layers:
+        if isinstance(layer, Sum):
+            for g in layer.groups:
+                if g.lowrank >= 0:
+                    out.append((g.param_offset, g.num_nodes * g.num_children))
+    return sorted(set(out))
+
+
+def em_step_corrected(circ: Circuit, params, param_flows, z_flows, step_size: float = 1.0,
+                      pseudocount: float = 0.0):
+    """The EM update with the LowRank conditional M-step: the rows of LowRank
+    weight blocks take R = F+ / W (entries with theta > 0 and W > 0, else 0)
+    in place of F, every other row the plain step."""
+    p = np.asarray(params, dtype=np.float64)
+    F = np.array(param_flows, dtype=np.float64)
+    W = np.asarray(z_flows, dtype=np.float64)
+    for off, n in lowrank_param_ranges(circ):
+        th, fp, w = p[off:off + n], F[off:off + n], W[off:off + n]
+        with np.errstate(divide="ignore", invalid="ignore"):
+            F[off:off + n] = np.where((th > 0) & (w > 0), fp / w, 0.0)
+    return em_step(circ, p, F, step_size, pseudocount)
 
 
 def em_step(circ: Circuit, params, param_flows, step_size: float = 1.0, pseudocount: float = 0.0):

@@ -457,6 +457,80 @@ def check_lowrank_grad_fd(orc):
         _close(r["flows"][node, 1], d, 1e-6, 1e-9, f"lowrank element flow {node}")
 
 
+def check_lowrank_zstat_fd(orc):
+    """LowRank denominator statistic (pyjuice.parameterizations.LowRank,
+    Training): with the element flows f held fixed, W = dJ/dtheta for
+    J(theta) = sum over LowRank layers, samples and nodes of
+    f_b[i] log Z_b[i](theta), Z_b[i] = sum_j theta[i,j] exp(A_b B_b)[i,j]
+    (central differences on the tied transition block)."""
+    circ, p, x, fac = _lowrank_case(B=3)
+    B = x.shape[0]
+    V, _ = orc.forward(circ, p, B, tokens=x, lowrank=fac)
+    r = orc.backward(circ, p, V, tokens=x, lowrank=fac)
+    groups = [g for ly in circ.layers if isinstance(ly, C.Sum) for g in ly.groups if g.lowrank >= 0]
+    off, M, N = groups[0].param_offset, groups[0].num_nodes, groups[0].num_children
+
+    def J(theta):
+        tot = 0.0
+        for g in groups:
+            f = r["flows"][g.out_start:g.out_start + M]
+            A, Bf = fac[g.lowrank]
+            for b in range(B):
+                Z = (theta * np.exp(A[b] @ Bf[b])).sum(axis=1)
+                tot += float((f[:, b] * np.log(Z)).sum())
+        return tot
+
+    th = p[off:off + M * N].reshape(M, N)
+    h = 1e-6
+    for (i, j) in ((0, 0), (1, 3), (3, 2), (2, 1)):
+        tp, tm = th.copy(), th.copy()
+        tp[i, j] += h
+        tm[i, j] -= h
+        _close(r["z_flows"][off + i * N + j], (J(tp) - J(tm)) / (2 * h), 1e-6, 1e-9, f"W[{i},{j}]")
+    # nothing outside the LowRank blocks
+    mask = np.ones(circ.num_params, bool)
+    mask[off:off + M * N] = False
+    assert not r["z_flows"][mask].any()
+
+
+def check_lowrank_zstat_reduction(orc):
+    """With A = 0 (no scale) Z_b[i] is the row sum of theta (1), so W[i, :] is
+    the node's flow summed over samples and copies, and the conditional
+    M-step without pseudocount is the plain EM step."""
+    circ, p, x, fac = _lowrank_case()
+    B = x.shape[0]
+    zeroA = [(np.zeros_like(a), b) for a, b in fac]
+    V, _ = orc.forward(circ, p, B, tokens=x, lowrank=zeroA)
+    r = orc.backward(circ, p, V, tokens=x, lowrank=zeroA)
+    groups = [g for ly in circ.layers if isinstance(ly, C.Sum) for g in ly.groups if g.lowrank >= 0]
+    off, M, N = groups[0].param_offset, groups[0].num_nodes, groups[0].num_children
+    fsum = sum(r["flows"][g.out_start:g.out_start + M].sum(axis=1) for g in groups)
+    _close(r["z_flows"][off:off + M * N].reshape(M, N), np.repeat(fsum[:, None], N, axis=1), 1e-12, 1e-12,
+           "W with A = 0")
+    # (without a pseudocount: alpha / n does not scale with the row)
+    for eta in (1.0, 0.5):
+        _close(orc.em_step_corrected(circ, p, r["param_flows"], r["z_flows"], eta, 0.0),
+               orc.em_step(circ, p, r["param_flows"], eta, 0.0), 1e-12, 1e-14, "corrected M-step with A = 0")
+
+
+def check_em_corrected_row(orc):
+    """Conditional M-step on a hand-computed row of a one-node LowRank layer:
+    theta = (0.5, 0.25, 0.25, 0), F+ = (1, 2, 0.5, 0), W = (4, 2, 1, 3):
+    F+ / W = (0.25, 1, 0.5, 0) -> (1/7, 4/7, 2/7, 0); with eta = 0.5 and
+    alpha = 0.2: (0.5 theta + 0.5 (R + 0.05) / 1.95)."""
+    ext = C.InputExternal(0, 4)
+    g = C.SumGroup(4, 1, np.array([0]), 4, 0, lowrank=0)
+    circ = C.Circuit("row", 5, 0, 4, [ext, C.Sum([g])], root=4, lowrank_rank=1)
+    th = np.array([0.5, 0.25, 0.25, 0.0])
+    Fp = np.array([1.0, 2.0, 0.5, 0.0])
+    W = np.array([4.0, 2.0, 1.0, 3.0])
+    _close(orc.em_step_corrected(circ, th, Fp, W, 1.0, 0.0), np.array([1, 4, 2, 0]) / 7.0, 1e-15, 1e-15,
+           "corrected row")
+    R = np.array([0.25, 1.0, 0.5, 0.0])
+    _close(orc.em_step_corrected(circ, th, Fp, W, 0.5, 0.2), 0.5 * th + 0.5 * (R + 0.05) / 1.95, 1e-15, 1e-15,
+           "corrected row with step and pseudocount")
+
+
 # ---------------------------------------------------------------------------
 # Invariants
 # ---------------------------------------------------------------------------
@@ -504,5 +578,6 @@ ALL_CHECKS = [check_dense_logsumexp, check_dense_flows_fd, check_hmm_bruteforce,
               check_hmm_forward_algorithm, check_hmm_posteriors, check_baum_welch,
               check_em_blend_and_pseudocount, check_hclt_bruteforce, check_hclt_tree_recursion,
               check_block_sparse_normalized, check_flows_fd, check_lowrank_reductions,
-              check_lowrank_inhomogeneous_hmm, check_lowrank_grad_fd, check_invariants,
+              check_lowrank_inhomogeneous_hmm, check_lowrank_grad_fd, check_lowrank_zstat_fd,
+              check_lowrank_zstat_reduction, check_em_corrected_row, check_invariants,
               check_neg_inf_flows]

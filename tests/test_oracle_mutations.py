@@ -30,6 +30,11 @@ MUTATIONS = [
     ("lowrank_grad_sign", "D = eps - fi[:, None] * tb", "D = eps + fi[:, None] * tb", 0),
     ("lowrank_dB_without_z_term", "dBg[b] = Ab.T @ D", "dBg[b] = Ab.T @ eps", 0),
     ("lowrank_dA_wrong_factor", "dAg[b] = D @ Bb.T", "dAg[b] = D @ Bb.T[::-1]", 0),
+    ("zstat_without_z", "fz = np.where((fi != 0) & (Z > 0), fi / Z, 0.0)", "fz = fi", 0),
+    ("zstat_without_scale", "zf += fz[:, None] * np.exp(Ab @ Bb)", "zf += fz[:, None] * np.ones_like(th)", 0),
+    ("zstat_per_copy_overwrite", "ZF[g.param_offset:g.param_offset + th.size] += zf", "ZF[g.param_offset:g.param_offset + th.size] = zf", 0),
+    ("em_corrected_not_ratio", "np.where((th > 0) & (w > 0), fp / w, 0.0)", "np.where((th > 0) & (w > 0), fp, 0.0)", 0),
+    ("em_corrected_inverted", "np.where((th > 0) & (w > 0), fp / w, 0.0)", "np.where((th > 0) & (w > 0), w / np.maximum(fp, 1e-300), 0.0)", 0),
 ]
 
 
