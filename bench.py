@@ -117,18 +117,26 @@ def bench_lowrank(args):
     grads = [(torch.empty_like(a), torch.empty_like(b)) for a, b in lr]
     ws = L.workspace(h, B, dev)
     stream = torch.cuda.current_stream()
+    # with --z-correction: the denominator statistic and the conditional M-step
+    zf = torch.zeros(circ.num_params, device=dev) if args.z_correction else None
 
     def step():
         pflows.zero_()
         L.pc_forward(h, B, tokens, params, vals, ll, lr, ws, stream.cuda_stream)
-        L.pc_backward(h, B, tokens, params, vals, flows, pflows, 0, lr, grads, ws, stream.cuda_stream)
-        L.pc_em_step(h, params, pflows, 1.0, 0.0, stream.cuda_stream)
+        if zf is None:
+            L.pc_backward(h, B, tokens, params, vals, flows, pflows, 0, lr, grads, ws, stream.cuda_stream)
+            L.pc_em_step(h, params, pflows, 1.0, 0.0, stream.cuda_stream)
+        else:
+            zf.zero_()
+            L.pc_backward(h, B, tokens, params, vals, flows, pflows, 0, lr, grads, ws, stream.cuda_stream,
+                          z_flows=zf)
+            L.pc_em_step_corrected(h, params, pflows, zf, 1.0, 0.0, stream.cuda_stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     run = step
-    if args.graph:
+    if args.graph and zf is None:
         g = L.StepGraph(h, B, tokens, params, vals, flows, pflows, ll, 0, lowrank=lr, grads=grads, ws=ws,
                         em=(1.0, 0.0))
         run = g.replay
@@ -160,8 +168,9 @@ def bench_lowrank(args):
         "value": round(value, 2), "unit": "Gexp/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16-split" if args.mode == "auto" else "bf16x6-split", "data": "synthetic",
-        "config": {"workload": "lowrank hmm1024x64 symbols 512 rank 16 batch 64 fwd+bwd+em", "precision_mode": args.mode,
-                   "hip_graph": bool(args.graph),
+        "config": {"workload": "lowrank hmm1024x64 symbols 512 rank 16 batch 64 fwd+bwd+em"
+                               + (" (z-corrected)" if args.z_correction else ""), "precision_mode": args.mode,
+                   "hip_graph": bool(args.graph and zf is None),
                    "global_batch": B},
         "kernel_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in kt.items() if v[0]},
         "roofline": {"kernel": dom, "bound": "alu", "achieved": round(achieved, 2), "peak": PEAK_EXP_G,
@@ -212,6 +221,8 @@ def main():
     ap.add_argument("--lr-cpu-sample", type=int, default=24,
                     help="samples of the LowRank workload the oracle baseline runs on")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--z-correction", type=int, default=0, choices=[0, 1],
+                    help="LowRank workload: also accumulate the denominator statistic W and take the conditional M-step")
     ap.add_argument("--graph", type=int, default=0, choices=[0, 1],
                     help="time replays of the step recorded as a HIP graph (1) or eager launches (0; measured the same: the queue already runs ahead of the host)")
     ap.add_argument("--layer-tile", type=int, default=0, help="product-kernel option: 0 auto, 1 128x128, 2 256x128, 3 128x256, 4 128x64, 5 64x128")

@@ -132,13 +132,21 @@ typedef struct pc_handle_s* pc_handle;
 /* LowRank factors and gradients, one entry per slot (host arrays of device
  * pointers).  A[s]: [batch, M_s, k], B[s]: [batch, k, N_s] float32, in this
  * order (pyjuice.parameterizations.LowRank, "Tensor layout").  dA[s], dB[s]:
- * same shapes, written (overwritten) by pc_backward with dLL/dA and dLL/dB. */
+ * same shapes, written (overwritten) by pc_backward with dLL/dA and dLL/dB.
+ * z_flows (nullable, device, [num_params] float32): the denominator statistic
+ * of the conditional M-step (pyjuice.parameterizations.LowRank, Training,
+ * apply_z_correction), W[i,j] = sum over samples and tied copies of
+ * f_b[i] * exp(A_b B_b)[i,j] / Z_b[i] for every LowRank weight block, in the
+ * parameter flows' layout; pc_backward ADDS it (like param_flows; only the
+ * LowRank blocks' entries are touched; 0 where f = 0 or Z = 0).  NULL skips
+ * it (the statistic costs one more pass over every (sample, node, child)). */
 typedef struct pc_lowrank_io {
   int32_t num_slots;
   const float* const* A;
   const float* const* B;
   float* const* dA;
   float* const* dB;
+  float* z_flows;
 } pc_lowrank_io;
 
 /* Read-only summary of a compiled layout (for inspection and tests). */
@@ -264,7 +272,8 @@ int pc_forward(pc_handle h, int batch, const int32_t* tokens, const float* param
  *              weight sum over samples and tied copies of
  *              f[i] * theta[i,j] * exp(v[j] - v[i]); for every input weight the
  *              summed flow of the samples showing that category.
- *  lowrank     with dA / dB outputs for LowRank groups (overwritten).
+ *  lowrank     with dA / dB outputs for LowRank groups (overwritten) and,
+ *              if z_flows is set, the denominator statistic W (accumulated).
  * Errors: as pc_forward. */
 #define PC_BWD_SEEDED 1
 int pc_backward(pc_handle h, int batch, const int32_t* tokens, const float* params,
@@ -280,6 +289,18 @@ int pc_backward(pc_handle h, int batch, const int32_t* tokens, const float* para
  * Errors: PC_ERR_INVALID_ARG (step_size outside [0, 1], pseudocount < 0). */
 int pc_em_step(pc_handle h, float* params, const float* param_flows, float step_size,
                float pseudocount, void* stream);
+
+/* The EM update with the LowRank conditional M-step
+ * (pyjuice.parameterizations.LowRank, Training, compute_em_correction):
+ * theta <- normalize(theta * F+ / F-) with F- = theta * W.  Every row of a
+ * LowRank weight block takes R[j] = F+[j] / W[j] (entries with theta > 0 and
+ * W > 0; 0 elsewhere) in place of F in pc_em_step's formula (same step size
+ * and pseudocount); every other row is exactly pc_em_step.  z_flows: device
+ * float32 [num_params], the W that pc_backward accumulated.  In place on
+ * params; clears neither statistic.
+ * Errors: as pc_em_step; PC_ERR_INVALID_ARG for a null z_flows. */
+int pc_em_step_corrected(pc_handle h, float* params, const float* param_flows, const float* z_flows,
+                         float step_size, float pseudocount, void* stream);
 
 /* Message of the calling thread's last failed call ("" if none). */
 const char* pc_last_error(void);

@@ -52,7 +52,7 @@ class pc_circuit_desc(C.Structure):
 
 class pc_lowrank_io(C.Structure):
     _fields_ = [("num_slots", C.c_int32), ("A", C.POINTER(C.c_void_p)), ("B", C.POINTER(C.c_void_p)),
-                ("dA", C.POINTER(C.c_void_p)), ("dB", C.POINTER(C.c_void_p))]
+                ("dA", C.POINTER(C.c_void_p)), ("dB", C.POINTER(C.c_void_p)), ("z_flows", C.c_void_p)]
 
 
 class pc_layout_summary(C.Structure):
@@ -75,6 +75,8 @@ EXPORTS = {
                               C.c_void_p, C.c_int, C.POINTER(pc_lowrank_io), C.c_void_p, C.c_size_t,
                               C.c_void_p]),
     "pc_em_step": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_float, C.c_float, C.c_void_p]),
+    "pc_em_step_corrected": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_float, C.c_float,
+                                       C.c_void_p]),
     "pc_last_error": (C.c_char_p, []),
     "pc_layout_info": (C.c_int, [C.c_void_p, C.POINTER(pc_layout_summary)]),
     "pc_layer_class": (C.c_int, [C.c_void_p, C.c_int, C.POINTER(C.c_int)]),
@@ -286,8 +288,9 @@ def _stream(stream):
     return C.c_void_p(_torch().cuda.current_stream().cuda_stream)
 
 
-def _lowrank_io(lowrank, grads=None):
-    """lowrank: list of (A, B) device tensors per slot; grads: list of (dA, dB)."""
+def _lowrank_io(lowrank, grads=None, z_flows=None, num_params=None):
+    """lowrank: list of (A, B) device tensors per slot; grads: list of (dA, dB);
+    z_flows: the LowRank denominator statistic's accumulator ([num_params])."""
     if lowrank is None:
         return None, None
     torch = _torch()
@@ -299,7 +302,8 @@ def _lowrank_io(lowrank, grads=None):
         dB = (C.c_void_p * n)(*[_ptr(b, torch.float32, what="dB").value for _, b in grads])
     else:
         dA = dB = None
-    io = pc_lowrank_io(num_slots=n, A=A, B=Bf, dA=dA, dB=dB)
+    z = _ptr(z_flows, torch.float32, num_params, "z_flows") if z_flows is not None else None
+    io = pc_lowrank_io(num_slots=n, A=A, B=Bf, dA=dA, dB=dB, z_flows=z)
     return io, (A, Bf, dA, dB)
 
 
@@ -318,9 +322,9 @@ def pc_forward(h: Handle, batch: int, tokens, params, node_vals, ll=None, lowran
 
 
 def pc_backward(h: Handle, batch: int, tokens, params, node_vals, node_flows, param_flows, flags=0,
-                lowrank=None, grads=None, ws=None, stream=None):
+                lowrank=None, grads=None, ws=None, stream=None, z_flows=None):
     torch = _torch()
-    io, keep = _lowrank_io(lowrank, grads)
+    io, keep = _lowrank_io(lowrank, grads, z_flows, h.num_params)
     need = pc_workspace_bytes(h, batch)
     _check(lib().pc_backward(
         h.ptr, int(batch), _ptr(tokens, torch.int32, batch * h.num_vars, "tokens"),
@@ -338,6 +342,14 @@ def pc_em_step(h: Handle, params, param_flows, step_size=1.0, pseudocount=0.0, s
     _check(lib().pc_em_step(h.ptr, _ptr(params, torch.float32, h.num_params, "params"),
                             _ptr(param_flows, torch.float32, h.num_params, "param_flows"),
                             C.c_float(step_size), C.c_float(pseudocount), _stream(stream)))
+
+
+def pc_em_step_corrected(h: Handle, params, param_flows, z_flows, step_size=1.0, pseudocount=0.0, stream=None):
+    torch = _torch()
+    _check(lib().pc_em_step_corrected(h.ptr, _ptr(params, torch.float32, h.num_params, "params"),
+                                      _ptr(param_flows, torch.float32, h.num_params, "param_flows"),
+                                      _ptr(z_flows, torch.float32, h.num_params, "z_flows"),
+                                      C.c_float(step_size), C.c_float(pseudocount), _stream(stream)))
 
 
 def workspace(h: Handle, batch: int, device="cuda", all_modes=False):

@@ -884,7 +884,9 @@ __global__ void k_elem_reduce(SumArgs a) {
 __global__ __launch_bounds__(256) void k_em(EmArgs a, int total_rows) {
   // one wave per parameter row, four rows per workgroup: the row sum is a
   // per-lane sum in index order then a fixed butterfly over the wave, so the
-  // result does not depend on timing
+  // result does not depend on timing.  Rows of LowRank weight blocks under
+  // the conditional M-step use R = F+ / W (theta > 0 and W > 0, else 0) in
+  // place of F.
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= total_rows) return;
@@ -892,6 +894,11 @@ __global__ __launch_bounds__(256) void k_em(EmArgs a, int total_rows) {
   const RowSeg sg = a.segs[s];
   const int64_t off = sg.offset + (int64_t)(row - sg.row_start) * sg.rlen;
   const bool vec = ((off | (int64_t)sg.rlen) & 3) == 0;   // 16-byte rows
+  const bool corr = a.zflows != nullptr && sg.lowrank != 0;
+  auto ratio = [](float f, float w, float p) { return (p > 0.0f && w > 0.0f) ? f / w : 0.0f; };
+  auto ratio4 = [&](float4 f, float4 w, float4 p) {
+    return make_float4(ratio(f.x, w.x, p.x), ratio(f.y, w.y, p.y), ratio(f.z, w.z, p.z), ratio(f.w, w.w, p.w));
+  };
   // rows of up to 1024 (16-byte aligned): the lane's four 16-byte chunks are
   // loaded at once and kept for the update, along with the parameters
   constexpr int RU = 4;
@@ -899,22 +906,30 @@ __global__ __launch_bounds__(256) void k_em(EmArgs a, int total_rows) {
   float4 fh[RU], ph[RU];
   float acc = 0.0f;
   if (held) {
+    float4 wh[RU];
 #pragma unroll
     for (int u = 0; u < RU; ++u) {
       const int j = lane * 4 + u * 256;
-      fh[u] = j < sg.rlen ? *(const float4*)(a.pflows + off + j) : make_float4(0.f, 0.f, 0.f, 0.f);
-      ph[u] = j < sg.rlen ? *(const float4*)(a.params + off + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const bool in = j < sg.rlen;
+      fh[u] = in ? *(const float4*)(a.pflows + off + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+      ph[u] = in ? *(const float4*)(a.params + off + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+      wh[u] = (in && corr) ? *(const float4*)(a.zflows + off + j) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    if (corr)
+#pragma unroll
+      for (int u = 0; u < RU; ++u) fh[u] = ratio4(fh[u], wh[u], ph[u]);
 #pragma unroll
     for (int u = 0; u < RU; ++u)
       if (lane * 4 + u * 256 < sg.rlen) acc += ((fh[u].x + fh[u].y) + fh[u].z) + fh[u].w;
   } else if (vec) {
     for (int j = lane * 4; j < sg.rlen; j += 256) {
-      const float4 f = *(const float4*)(a.pflows + off + j);
+      float4 f = *(const float4*)(a.pflows + off + j);
+      if (corr) f = ratio4(f, *(const float4*)(a.zflows + off + j), *(const float4*)(a.params + off + j));
       acc += ((f.x + f.y) + f.z) + f.w;
     }
   } else {
-    for (int j = lane; j < sg.rlen; j += 64) acc += a.pflows[off + j];
+    for (int j = lane; j < sg.rlen; j += 64)
+      acc += corr ? ratio(a.pflows[off + j], a.zflows[off + j], a.params[off + j]) : a.pflows[off + j];
   }
 #pragma unroll
   for (int w = 32; w > 0; w >>= 1) acc += __shfl_xor(acc, w);
@@ -937,8 +952,9 @@ __global__ __launch_bounds__(256) void k_em(EmArgs a, int total_rows) {
     }
   } else if (vec) {
     for (int j = lane * 4; j < sg.rlen; j += 256) {
-      const float4 f = *(const float4*)(a.pflows + off + j);
+      float4 f = *(const float4*)(a.pflows + off + j);
       float4 p = *(const float4*)(a.params + off + j);
+      if (corr) f = ratio4(f, *(const float4*)(a.zflows + off + j), p);
       p.x = keep * p.x + a.step * ((f.x + add) / tot);
       p.y = keep * p.y + a.step * ((f.y + add) / tot);
       p.z = keep * p.z + a.step * ((f.z + add) / tot);
@@ -947,7 +963,8 @@ __global__ __launch_bounds__(256) void k_em(EmArgs a, int total_rows) {
     }
   } else {
     for (int j = lane; j < sg.rlen; j += 64) {
-      const float nw = (a.pflows[off + j] + add) / tot;
+      const float f = corr ? ratio(a.pflows[off + j], a.zflows[off + j], a.params[off + j]) : a.pflows[off + j];
+      const float nw = (f + add) / tot;
       a.params[off + j] = keep * a.params[off + j] + a.step * nw;
     }
   }

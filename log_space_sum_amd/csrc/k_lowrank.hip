@@ -446,7 +446,11 @@ __global__ __launch_bounds__(256) void k_lr_fwd(LRArgs a) {
 // order (through one of two LDS exchange tiles, so one barrier per row block
 // suffices) and added to the workgroup's partial matrix, whose tile is read a
 // row block ahead so that the read overlaps the block's work.
-template <int PH, int PG, int KC>
+// With WS (the denominator statistic of the conditional M-step) the same walk
+// computes only w[i, j] = c2[i] * exp(h[i, j]) per sample (c2 = f / Z), summed
+// over the 8 waves into the partial matrices at a.P like the parameter flows;
+// no weights, element flows or dB.
+template <int PH, int PG, int KC, bool WS = false>
 __global__ __launch_bounds__(512) void k_lr_bwd(LRArgs a) {
   using PK = LrPack<PH, PG, KC>;
   __shared__ __attribute__((aligned(16))) float slab[kSlabB];   // theta^T [32][R + 4]
@@ -471,7 +475,7 @@ __global__ __launch_bounds__(512) void k_lr_bwd(LRArgs a) {
   }
   // e[j, b] = exp(v[child j, b] - m[b]) of this lane's child (zero past N)
   float ev = 0.0f;
-  if (act && j0 + l32 < N) {
+  if (!WS && act && j0 + l32 < N) {
     const int j = j0 + l32, child = a.chblocks[a.blk_off + j / a.cbs] + j % a.cbs;
     ev = expf(a.vals[(int64_t)child * a.B + b] - key_to_shift_lr(a.mkeys[(int64_t)a.m_row * a.B + b]));
   }
@@ -507,10 +511,11 @@ __global__ __launch_bounds__(512) void k_lr_bwd(LRArgs a) {
     for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
       for (int p = 0; p < PH; ++p) L.ah[kc][p] = ldfrag(r + (kc * PH + p) * kFrag, lb);
+    if constexpr (!WS)
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc)
+      for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-      for (int p = 0; p < PG; ++p) L.ad[cc][p] = ldfrag(r + (KC * PH + cc * PG + p) * kFrag, lb);
+        for (int p = 0; p < PG; ++p) L.ad[cc][p] = ldfrag(r + (KC * PH + cc * PG + p) * kFrag, lb);
   };
   auto loadC = [&](int ib, Cf& L) {
 #pragma unroll
@@ -532,7 +537,7 @@ __global__ __launch_bounds__(512) void k_lr_bwd(LRArgs a) {
     // ii, 4 columns jq), one 16-byte load when the row is 16-byte aligned
     const int rw = (min(kChunkB, M - r0) + 31) / 32 * 32, RP = rw + 4;
     __syncthreads();
-    for (int base = tid; base < rw * 8; base += 512 * 4) {
+    for (int base = tid; !WS && base < rw * 8; base += 512 * 4) {
       float4 v[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -589,6 +594,15 @@ __global__ __launch_bounds__(512) void k_lr_bwd(LRArgs a) {
 #pragma unroll
           for (int kc = 0; kc < KC; ++kc) mfma_planes<PH>(H, fc.ah[kc], bB[kc]);
           // register r: row i = i0 + (r/4)*8 + h*4 + r%4, column j = j0 + l32
+          if constexpr (WS) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int r = g * 4 + e;
+                xw[r * 64] = at4(cc_.c2[g], e) * __builtin_amdgcn_exp2f(H[r]);
+              }
+          } else {
           float X[16];
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
@@ -614,6 +628,7 @@ __global__ __launch_bounds__(512) void k_lr_bwd(LRArgs a) {
             bf16x8_t px[PG];
             split8<PG>(xx, px);
             mfma_planes<PG>(dB, fc.ad[cc], px);
+          }
           }
         } else {
 #pragma unroll
@@ -648,6 +663,7 @@ __global__ __launch_bounds__(512) void k_lr_bwd(LRArgs a) {
       blockk(il + 3, F3, F2, Cb, Ca, p1, p0, 1);
     }
   }
+  if constexpr (WS) return;
   // child flows, dB
   const float tot = fcp + __shfl_xor(fcp, 32);
   const int j = j0 + l32;
@@ -692,11 +708,11 @@ static void lr_fwd_k(const LRArgs& a, hipStream_t s) {
   if (a.krank <= 16) hipLaunchKernelGGL((k_lr_fwd<PH, PG, 1>), grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL((k_lr_fwd<PH, PG, 2>), grid, dim3(256), 0, s, a);
 }
-template <int PH, int PG>
+template <int PH, int PG, bool WS = false>
 static void lr_bwd_k(const LRArgs& a, hipStream_t s) {
   const dim3 grid(((a.N + 31) / 32) * ((a.B + 7) / 8));
-  if (a.krank <= 16) hipLaunchKernelGGL((k_lr_bwd<PH, PG, 1>), grid, dim3(512), 0, s, a);
-  else hipLaunchKernelGGL((k_lr_bwd<PH, PG, 2>), grid, dim3(512), 0, s, a);
+  if (a.krank <= 16) hipLaunchKernelGGL((k_lr_bwd<PH, PG, 1, WS>), grid, dim3(512), 0, s, a);
+  else hipLaunchKernelGGL((k_lr_bwd<PH, PG, 2, WS>), grid, dim3(512), 0, s, a);
 }
 
 int64_t lr_pack_bytes(int B, int M, int N, int krank, int fp32) {
@@ -731,6 +747,10 @@ void launch_lr_fwd(const LRArgs& a, int fp32, hipStream_t s) {
 void launch_lr_bwd(const LRArgs& a, int fp32, hipStream_t s) {
   if (fp32) lr_bwd_k<3, 3>(a, s);
   else lr_bwd_k<2, 1>(a, s);
+}
+void launch_lr_zstat(const LRArgs& a, int fp32, hipStream_t s) {
+  if (fp32) lr_bwd_k<3, 3, true>(a, s);
+  else lr_bwd_k<2, 1, true>(a, s);
 }
 void launch_lr_fplus(const float* P, int nsg, int64_t elems, float* pflows, hipStream_t s) {
   hipLaunchKernelGGL(k_lr_fplus, dim3(grid_lr(elems)), dim3(256), 0, s, P, nsg, elems, pflows);

@@ -257,6 +257,7 @@ WsPlan plan_workspace(const Handle* h, int B) {
   p.lrC1 = take(lr ? (size_t)round_up(h->lr_max_m, 32) * Bs * 4 : 0);   // rows padded to 32 (zeros)
   p.lrC2 = take(lr ? (size_t)round_up(h->lr_max_m, 32) * Bs * 4 : 0);
   p.lrP = take(lr ? (size_t)p.lr_nsg * h->lr_p_elems * 4 : 0);
+  p.lrPz = take(lr ? (size_t)p.lr_nsg * h->lr_p_elems * 4 : 0);
   {
     size_t pk = 0;
     for (const auto& sp : h->sums)
@@ -842,9 +843,12 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
       Timed t(h, KK_OTHER, c.s);
       launch_bucket(v.tokT, h->num_vars, B, h->max_cats, v.bucket_ptr, v.bucket_idx, c.s);
     }
+    // LowRank denominator statistic W of the conditional M-step (on request)
+    const bool zstat = h->lowrank_slots > 0 && lowrank && lowrank->z_flows;
     if (h->lowrank_slots > 0) {
       Timed t(h, KK_OTHER, c.s);
       launch_fill_u32((uint32_t*)((char*)c.ws + p.lrP), (int64_t)p.lr_nsg * h->lr_p_elems, 0u, c.s);
+      if (zstat) launch_fill_u32((uint32_t*)((char*)c.ws + p.lrPz), (int64_t)p.lr_nsg * h->lr_p_elems, 0u, c.s);
     }
     // Parameter flows: one product over every tied copy after the layers, or
     // (opt_param_chunk > 0) chunks of that many copies per weight block on a
@@ -927,6 +931,11 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
           Timed t(h, KK_LRBWD, c.s);
           launch_lr_coef(la, c.s);
           launch_lr_bwd(la, p.mode == PC_PREC_FP32, c.s);
+          if (zstat) {   // W's partials, from this layer's c2 = f / Z before the next layer rewrites it
+            LRArgs lz = la;
+            lz.P = (float*)((char*)c.ws + p.lrPz) + h->lr_p_off[sp.groups[gi].block] * p.lr_nsg;
+            launch_lr_zstat(lz, p.mode == PC_PREC_FP32, c.s);
+          }
         }
         if (sp.overlap) {
           SumArgs ra = sum_common(c, sp);
@@ -1047,6 +1056,9 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
       Timed t(h, KK_LRBWD, c.s);
       launch_lr_fplus((float*)((char*)c.ws + p.lrP) + h->lr_p_off[bi] * p.lr_nsg, p.lr_nsg, (int64_t)bl.M * bl.N,
                       param_flows + bl.param_offset, c.s);
+      if (zstat)
+        launch_lr_fplus((float*)((char*)c.ws + p.lrPz) + h->lr_p_off[bi] * p.lr_nsg, p.lr_nsg, (int64_t)bl.M * bl.N,
+                        lowrank->z_flows + bl.param_offset, c.s);
     }
     if (!chunks.empty()) {
       launch_ready_chunks(-(1 << 29));
@@ -1064,12 +1076,13 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
   }
 }
 
-int pc_em_step(pc_handle hh, float* params, const float* param_flows, float step_size, float pseudocount,
-               void* stream) {
+static int em_common(pc_handle hh, float* params, const float* param_flows, const float* z_flows, bool corrected,
+                     float step_size, float pseudocount, void* stream) {
   try {
     Handle* h = checked(hh);
     if (h->device < 0) fail(PC_ERR_NO_DEVICE, "handle was compiled without a device");
     if (!params || !param_flows) fail(PC_ERR_INVALID_ARG, "null params or param_flows");
+    if (corrected && !z_flows) fail(PC_ERR_INVALID_ARG, "null z_flows");
     if (!(step_size >= 0.0f && step_size <= 1.0f)) fail(PC_ERR_INVALID_ARG, "step_size must be in [0, 1]");
     if (!(pseudocount >= 0.0f)) fail(PC_ERR_INVALID_ARG, "pseudocount must be >= 0");
     DeviceGuard dg(h->device);
@@ -1078,6 +1091,7 @@ int pc_em_step(pc_handle hh, float* params, const float* param_flows, float step
     a.segs = h->d_rowsegs;
     a.params = params;
     a.pflows = param_flows;
+    a.zflows = corrected ? z_flows : nullptr;
     a.step = step_size;
     a.pseudo = pseudocount;
     hipStream_t s = (hipStream_t)stream;
@@ -1088,6 +1102,16 @@ int pc_em_step(pc_handle hh, float* params, const float* param_flows, float step
   } catch (const Error& e) {
     return set_error(e.code, e.msg);
   }
+}
+
+int pc_em_step(pc_handle hh, float* params, const float* param_flows, float step_size, float pseudocount,
+               void* stream) {
+  return em_common(hh, params, param_flows, nullptr, false, step_size, pseudocount, stream);
+}
+
+int pc_em_step_corrected(pc_handle hh, float* params, const float* param_flows, const float* z_flows,
+                         float step_size, float pseudocount, void* stream) {
+  return em_common(hh, params, param_flows, z_flows, true, step_size, pseudocount, stream);
 }
 
 int pc_set_timing(pc_handle hh, int enable) {

@@ -448,7 +448,10 @@ Handle* compile_layout(const pc_circuit_desc* d) {
   // EM row segments: every distinct block and input table
   {
     std::map<int64_t, RowSeg> segs;
-    for (auto& B : h->blocks) segs[B.param_offset] = RowSeg{B.param_offset, B.M, B.N, 0, 0};
+    for (size_t bi = 0; bi < h->blocks.size(); ++bi) {
+      const BlockRec& B = h->blocks[bi];
+      segs[B.param_offset] = RowSeg{B.param_offset, B.M, B.N, 0, h->lr_p_off[bi] >= 0 ? 1 : 0};
+    }
     for (auto& kv : table_shape) segs[kv.first] = RowSeg{kv.first, kv.second.first, kv.second.second, 0, 0};
     int32_t rows = 0;
     for (auto& kv : segs) {

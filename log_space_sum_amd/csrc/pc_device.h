@@ -76,7 +76,7 @@ struct RowSeg {
   int32_t nrows;
   int32_t rlen;
   int32_t row_start;     // prefix of rows over segments
-  int32_t pad_;
+  int32_t lowrank;       // 1: a LowRank weight block (conditional M-step rows)
 };
 
 // Node range [start, start + count) with one fill value (flow seeding).

@@ -100,6 +100,7 @@ struct EmArgs {
   const RowSeg* segs;
   float* params;
   const float* pflows;
+  const float* zflows;   // LowRank denominator statistic (conditional M-step), or null
   float step, pseudo;
 };
 
@@ -157,6 +158,8 @@ void launch_lr_pack(const LRPackArgs& pa, int fp32, hipStream_t s);
 void launch_lr_coef(const LRArgs& a, hipStream_t s);
 void launch_lr_fwd(const LRArgs& a, int fp32, hipStream_t s);
 void launch_lr_bwd(const LRArgs& a, int fp32, hipStream_t s);
+// The denominator statistic W of the conditional M-step into the partials at a.P.
+void launch_lr_zstat(const LRArgs& a, int fp32, hipStream_t s);
 void launch_lr_fplus(const float* P, int nsg, int64_t elems, float* pflows, hipStream_t s);
 
 void launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);

@@ -205,6 +205,7 @@ struct WsPlan {
   int pl[3][2];
   size_t theta, thetaT, ebt, gbt, gbt2, earena, garena, mkeys, ssum, scratch, tokT, bptr, bidx, lowrank;
   size_t lrE, lrZ, lrS, lrU, lrW, lrC1, lrC2, lrP;   // LowRank regions (float32)
+  size_t lrPz;                                       // partials of the denominator statistic W
   size_t lrPK;                                       // LowRank fragment records of every LowRank group
   std::vector<int64_t> lr_pk_off;                    // per LowRank group: byte offset of its records
   int lr_nsg;                                        // LowRank parameter-flow partials: ceil(B/8)

@@ -33,9 +33,13 @@ def torch():
     return T
 
 
-def run_gpu(cfg, mode="auto", splits=None, B=None, em=None, timing=False, device=0, repeat=1, options=None):
+def run_gpu(cfg, mode="auto", splits=None, B=None, em=None, timing=False, device=0, repeat=1, options=None,
+            z_init=None, em_corrected=None):
     """Forward + backward (+ optional EM) on the GPU.  Returns numpy arrays
-    (with timing: also the per-kind kernel counts and times, key "times")."""
+    (with timing: also the per-kind kernel counts and times, key "times").
+    z_init: initial contents of the LowRank denominator statistic's buffer
+    (key "z_flows" after the pass); em_corrected = (step, pseudocount): the
+    conditional M-step from the pass's F+ and W (key "em_corrected")."""
     T = torch()
     circ = cfg["circuit"]
     B = B or cfg["B"]
@@ -67,11 +71,12 @@ def run_gpu(cfg, mode="auto", splits=None, B=None, em=None, timing=False, device
     if cfg.get("lowrank") is not None:
         lr = [(T.tensor(a[:B], device=dev), T.tensor(b[:B], device=dev)) for a, b in cfg["lowrank"]]
         grads = [(T.full_like(a, float("nan")), T.full_like(b, float("nan"))) for a, b in lr]
+    zf = T.tensor(np.asarray(z_init, np.float32), device=dev) if z_init is not None else None
     out = []
     for _ in range(repeat):
         pflows.zero_()
         L.pc_forward(h, B, tokens, params, vals, ll, lr, ws)
-        L.pc_backward(h, B, tokens, params, vals, flows, pflows, flags, lr, grads, ws)
+        L.pc_backward(h, B, tokens, params, vals, flows, pflows, flags, lr, grads, ws, z_flows=zf)
         T.cuda.synchronize()
         r = dict(vals=vals.cpu().numpy().copy(), flows=flows.cpu().numpy().copy(),
                  pflows=pflows.cpu().numpy().copy(), ll=None if ll is None else ll.cpu().numpy().copy())
@@ -80,7 +85,14 @@ def run_gpu(cfg, mode="auto", splits=None, B=None, em=None, timing=False, device
         if grads is not None:
             r["dA"] = [a.cpu().numpy().copy() for a, _ in grads]
             r["dB"] = [b.cpu().numpy().copy() for _, b in grads]
+        if zf is not None:
+            r["z_flows"] = zf.cpu().numpy().copy()
         out.append(r)
+    if em_corrected is not None:
+        newp = params.clone()
+        L.pc_em_step_corrected(h, newp, pflows, zf, em_corrected[0], em_corrected[1])
+        T.cuda.synchronize()
+        out[-1]["em_corrected"] = newp.cpu().numpy()
     if em is not None:
         newp = params.clone()
         L.pc_em_step(h, newp, pflows, em[0], em[1])
@@ -118,6 +130,7 @@ def run_oracle(cfg, B=None, samples=None):
     if lr is not None:
         out["dA"] = [r["dA"][s] for s in range(len(lr))]
         out["dB"] = [r["dB"][s] for s in range(len(lr))]
+        out["z_flows"] = r["z_flows"]
     return out
 
 

@@ -53,6 +53,40 @@ def test_lowrank_hmm(mode, H, T, V, rank, B, spread):
     _lowrank_full(cfg, mode, f"lowrank hmm H{H} T{T} r{rank} s{spread}")
 
 
+@pytest.mark.parametrize("mode", ["auto", "fp32"])
+@pytest.mark.parametrize("H,T,V,rank,B,spread", [
+    (64, 5, 16, 16, 37, 1.0),     # two strips, ragged sample groups
+    (40, 4, 7, 5, 23, 4.0),       # ragged rows and children, 4-nat spread
+    (96, 3, 9, 32, 24, 0.3),      # rank 32
+])
+def test_lowrank_z_correction(mode, H, T, V, rank, B, spread):
+    """The denominator statistic W of the conditional M-step
+    (pyjuice.parameterizations.LowRank, Training, apply_z_correction): added
+    by pc_backward to what the buffer held, only on the LowRank weights, and
+    equal to the oracle's end to end (flow tolerance times the depth); then
+    pc_em_step_corrected against the oracle's conditional M-step on the GPU's
+    own F+ and W, every other row the plain step (fp32-level tolerance)."""
+    import oracle
+    cfg = make_config("lowrank", H=H, T=T, V=V, rank=rank, B=B, spread=spread)
+    circ = cfg["circuit"]
+    what = f"lowrank z-correction H{H} T{T} r{rank} s{spread}"
+    G.say(f"case {what} mode={mode} B={B}")
+    z0 = np.full(circ.num_params, 0.25, np.float32)
+    gpu = G.run_gpu(cfg, mode, z_init=z0, em_corrected=(0.7, 0.1))
+    orc = G.run_oracle(cfg)
+    inside = np.zeros(circ.num_params, bool)
+    for off, n in oracle.lowrank_param_ranges(circ):
+        inside[off:off + n] = True
+    assert inside.any()
+    assert np.array_equal(gpu["z_flows"][~inside], z0[~inside]), "W touched outside the LowRank blocks"
+    depth = G.num_sum_layers(circ)
+    G.check_flows(gpu["z_flows"][inside].astype(np.float64) - 0.25, orc["z_flows"][inside], mode,
+                  f"{what} W end to end", scale=depth)
+    ref = oracle.em_step_corrected(circ, cfg["params"], gpu["pflows"].astype(np.float64),
+                                   gpu["z_flows"].astype(np.float64), step_size=0.7, pseudocount=0.1)
+    G.check_flows(gpu["em_corrected"], ref, "fp32", f"{what} conditional M-step")
+
+
 def test_lowrank_small_batch_runs_fp32():
     """Batches below 16 run fp32-level products (the LowRank kernels included)."""
     cfg = make_config("lowrank", H=40, T=3, V=6, rank=8, B=9)
