@@ -27,9 +27,11 @@ What it computes (plain definitions, float64, numpy):
 * EM (pyjuice.parameterizations.LowRank, Training: plain EM is normalize(F)):
   theta <- (1-eta)*theta + eta*(F + alpha/n)/(sum F + alpha) per row; a row with
   zero total keeps its weights;
-* LowRank exp_sum (pyjuice.parameterizations.LowRank, definition):
-  theta_b = theta * exp(A_b B_b) / Z_b, Z_b[i] = sum_j theta[i,j] exp(A_b B_b)[i,j],
-  built explicitly per sample; the layer is the sum layer above with theta_b.
+* LowRank (pyjuice.parameterizations.LowRank, definition):
+  theta_b = theta * g_b / Z_b, Z_b[i] = sum_j theta[i,j] g_b[i,j], with the
+  scale g_b = exp(A_b B_b) ("exp_sum") or g_b[i,j] = sum_r exp(A_b[i,r])
+  exp(B_b[r,j]) ("sum_exp"), built explicitly per sample; the layer is the sum
+  layer above with theta_b.  The gradients go through dLL/dg (chain rule).
   Its backward (Training) writes the element flows, the parameter flows
   F+ = sum_b of the edge flows under theta_b, and dLL/dA, dLL/dB;
 * LowRank denominator statistic (pyjuice.parameterizations.LowRank, Training,
@@ -62,11 +64,21 @@ def _theta(params, g):
     return params[g.param_offset:g.param_offset + M * N].reshape(M, N)
 
 
-def lowrank_effective(theta, A_b, B_b):
-    """theta_b = theta * exp(A_b @ B_b) normalised over each row's children
+def lowrank_scale(A_b, B_b, form="exp_sum"):
+    """g_b of pyjuice.parameterizations.LowRank: exp(A_b B_b) for "exp_sum",
+    sum_r exp(A_b[:, r]) exp(B_b[r, :]) for "sum_exp"."""
+    if form == "exp_sum":
+        return np.exp(A_b @ B_b)
+    if form == "sum_exp":
+        return np.exp(A_b) @ np.exp(B_b)
+    raise ValueError(form)
+
+
+def lowrank_effective(theta, A_b, B_b, form="exp_sum"):
+    """theta_b = theta * g_b normalised over each row's children
     (pyjuice.parameterizations.LowRank, definition).  Returns (theta_b, q, Z)
-    with q = theta * exp(A_b B_b) and Z its row sums."""
-    q = theta * np.exp(A_b @ B_b)
+    with q = theta * g_b and Z its row sums."""
+    q = theta * lowrank_scale(A_b, B_b, form)
     Z = q.sum(axis=1)
     with np.errstate(invalid="ignore", divide="ignore"):
         tb = np.where(Z[:, None] > 0, q / Z[:, None], 0.0)
@@ -112,7 +124,7 @@ def forward(circ: Circuit, params, B: int, tokens=None, external=None, lowrank=N
                     S = np.empty((g.num_nodes, B))
                     for b in range(B):
                         tb, _, _ = lowrank_effective(th, np.asarray(A[b], np.float64),
-                                                     np.asarray(Bf[b], np.float64))
+                                                     np.asarray(Bf[b], np.float64), circ.lowrank_form)
                         S[:, b] = tb @ E[:, b]
                 else:
                     S = th @ E
@@ -170,18 +182,25 @@ def backward(circ: Circuit, params, V, tokens=None, lowrank=None, seed_flows=Non
                     for b in range(B):
                         Ab = np.asarray(A[b], np.float64)
                         Bb = np.asarray(Bf[b], np.float64)
-                        tb, _, Z = lowrank_effective(th, Ab, Bb)
+                        gb = lowrank_scale(Ab, Bb, circ.lowrank_form)
+                        tb, _, Z = lowrank_effective(th, Ab, Bb, circ.lowrank_form)
                         eps = tb * E[:, b][None, :] * gm[:, b][:, None]  # edge flows
                         fc[:, b] = eps.sum(axis=0)
                         pf += eps
                         fi = np.where(np.isfinite(n[:, b]), f[:, b], 0.0)
-                        D = eps - fi[:, None] * tb                       # dLL/d(A_b B_b)
-                        dAg[b] = D @ Bb.T
-                        dBg[b] = Ab.T @ D
+                        D = eps - fi[:, None] * tb                       # dLL/dg * g
+                        if circ.lowrank_form == "exp_sum":               # g = exp(h), h = A_b B_b
+                            dAg[b] = D @ Bb.T
+                            dBg[b] = Ab.T @ D
+                        else:                                            # g = exp(A_b) exp(B_b)
+                            G = D / gb                                   # dLL/dg (g > 0)
+                            eA, eB = np.exp(Ab), np.exp(Bb)
+                            dAg[b] = eA * (G @ eB.T)
+                            dBg[b] = eB * (eA.T @ G)
                         # denominator statistic: f_b[i] exp(A_b B_b)[i, j] / Z_b[i]
                         with np.errstate(divide="ignore", invalid="ignore"):
                             fz = np.where((fi != 0) & (Z > 0), fi / Z, 0.0)
-                        zf += fz[:, None] * np.exp(Ab @ Bb)
+                        zf += fz[:, None] * gb
                     F[ch] += fc
                     PF[g.param_offset:g.param_offset + th.size] += pf.reshape(-1)
                     ZF[g.param_offset:g.param_offset + th.size] += zf.reshape(-1)

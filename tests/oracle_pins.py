@@ -362,8 +362,8 @@ def check_flows_fd(orc):
 # LowRank exp_sum
 # ---------------------------------------------------------------------------
 
-def _lowrank_case(B=5, seed=8, H=4, T=4, V=3, rank=2, sigma=0.7):
-    circ = C.hmm(H, T, V, lowrank_rank=rank)
+def _lowrank_case(B=5, seed=8, H=4, T=4, V=3, rank=2, sigma=0.7, form="exp_sum"):
+    circ = C.hmm(H, T, V, lowrank_rank=rank, lowrank_form=form)
     rng = np.random.default_rng(seed)
     p = _renorm(circ, I.softmax_rows_params(circ, rng))
     x = I.uniform_tokens(circ, B, V, rng)
@@ -389,12 +389,17 @@ def check_lowrank_reductions(orc):
         _close(r1["flows"], r0["flows"], 1e-10, 1e-12, "lowrank reduction flows")
 
 
-def check_lowrank_inhomogeneous_hmm(orc):
+def _scale(a, b, form):
+    """The scale of pyjuice.parameterizations.LowRank, definition, per form."""
+    return np.exp(a @ b) if form == "exp_sum" else np.exp(a) @ np.exp(b)
+
+
+def check_lowrank_inhomogeneous_hmm(orc, form="exp_sum"):
     """Scaled HMM = a per-sample time-inhomogeneous HMM with transition
-    normalize(A * exp(A_b B_b)) at each step: LL by the forward algorithm,
-    F+ by summed xi, probabilities of all sequences (one sample's factors)
-    sum to one."""
-    circ, p, x, fac = _lowrank_case(B=5)
+    normalize(A * g_b) at each step (g_b the form's scale): LL by the forward
+    algorithm, F+ by summed xi, probabilities of all sequences (one sample's
+    factors) sum to one."""
+    circ, p, x, fac = _lowrank_case(B=5, form=form)
     m = circ.meta
     H, T = m["H"], m["T"]
     A, pi, E = _hmm_tables(circ, p)
@@ -406,7 +411,7 @@ def check_lowrank_inhomogeneous_hmm(orc):
         # transition from position t to t+1 uses the slot of sum layer t
         At = []
         for t in range(T - 1):
-            q = A * np.exp(fac[t][0][b] @ fac[t][1][b])
+            q = A * _scale(fac[t][0][b], fac[t][1][b], form)
             At.append(q / q.sum(1, keepdims=True))
         alpha = pi * E[:, x[b, 0]]
         al = [alpha]
@@ -428,10 +433,10 @@ def check_lowrank_inhomogeneous_hmm(orc):
     assert abs(np.exp(lla).sum() - 1.0) < 1e-12
 
 
-def check_lowrank_grad_fd(orc):
+def check_lowrank_grad_fd(orc, form="exp_sum"):
     """dLL/dA and dLL/dB and the element flows of the scaled layer's children
     against central finite differences."""
-    circ, p, x, fac = _lowrank_case(B=3)
+    circ, p, x, fac = _lowrank_case(B=3, form=form)
     B = x.shape[0]
 
     def L(f, perturb=None):
@@ -457,13 +462,42 @@ def check_lowrank_grad_fd(orc):
         _close(r["flows"][node, 1], d, 1e-6, 1e-9, f"lowrank element flow {node}")
 
 
-def check_lowrank_zstat_fd(orc):
+def check_lowrank_sumexp_inhomogeneous_hmm(orc):
+    """The "sum_exp" form (g = sum_r exp(A_b[:, r]) exp(B_b[r, :])) against the
+    per-sample inhomogeneous HMM."""
+    check_lowrank_inhomogeneous_hmm(orc, "sum_exp")
+
+
+def check_lowrank_sumexp_grad_fd(orc):
+    """The "sum_exp" form's dLL/dA, dLL/dB and element flows against central
+    finite differences."""
+    check_lowrank_grad_fd(orc, "sum_exp")
+
+
+def check_lowrank_sumexp_reduction(orc):
+    """"sum_exp" with B = 0: g[i, j] = sum_r exp(A_b[i, r]) is constant along a
+    row and cancels in the normalisation, so the circuit equals the plain
+    one (values, flows, parameter flows)."""
+    circ, p, x, fac = _lowrank_case(form="sum_exp")
+    plain = C.hmm(4, 4, 3)
+    B = x.shape[0]
+    V0, ll0 = orc.forward(plain, p, B, tokens=x)
+    r0 = orc.backward(plain, p, V0, tokens=x)
+    zeroB = [(a, np.zeros_like(b)) for a, b in fac]
+    V1, ll1 = orc.forward(circ, p, B, tokens=x, lowrank=zeroB)
+    r1 = orc.backward(circ, p, V1, tokens=x, lowrank=zeroB)
+    _close(ll1, ll0, 1e-12, 1e-12, "sum_exp reduction LL")
+    _close(r1["param_flows"], r0["param_flows"], 1e-10, 1e-12, "sum_exp reduction param flows")
+    _close(r1["flows"], r0["flows"], 1e-10, 1e-12, "sum_exp reduction flows")
+
+
+def check_lowrank_zstat_fd(orc, form="exp_sum"):
     """LowRank denominator statistic (pyjuice.parameterizations.LowRank,
     Training): with the element flows f held fixed, W = dJ/dtheta for
     J(theta) = sum over LowRank layers, samples and nodes of
     f_b[i] log Z_b[i](theta), Z_b[i] = sum_j theta[i,j] exp(A_b B_b)[i,j]
     (central differences on the tied transition block)."""
-    circ, p, x, fac = _lowrank_case(B=3)
+    circ, p, x, fac = _lowrank_case(B=3, form=form)
     B = x.shape[0]
     V, _ = orc.forward(circ, p, B, tokens=x, lowrank=fac)
     r = orc.backward(circ, p, V, tokens=x, lowrank=fac)
@@ -476,7 +510,7 @@ def check_lowrank_zstat_fd(orc):
             f = r["flows"][g.out_start:g.out_start + M]
             A, Bf = fac[g.lowrank]
             for b in range(B):
-                Z = (theta * np.exp(A[b] @ Bf[b])).sum(axis=1)
+                Z = (theta * _scale(A[b], Bf[b], form)).sum(axis=1)
                 tot += float((f[:, b] * np.log(Z)).sum())
         return tot
 
@@ -491,6 +525,11 @@ def check_lowrank_zstat_fd(orc):
     mask = np.ones(circ.num_params, bool)
     mask[off:off + M * N] = False
     assert not r["z_flows"][mask].any()
+
+
+def check_lowrank_sumexp_zstat_fd(orc):
+    """W of the "sum_exp" form against finite differences of sum f log Z."""
+    check_lowrank_zstat_fd(orc, "sum_exp")
 
 
 def check_lowrank_zstat_reduction(orc):
@@ -579,5 +618,7 @@ ALL_CHECKS = [check_dense_logsumexp, check_dense_flows_fd, check_hmm_bruteforce,
               check_em_blend_and_pseudocount, check_hclt_bruteforce, check_hclt_tree_recursion,
               check_block_sparse_normalized, check_flows_fd, check_lowrank_reductions,
               check_lowrank_inhomogeneous_hmm, check_lowrank_grad_fd, check_lowrank_zstat_fd,
+              check_lowrank_sumexp_inhomogeneous_hmm, check_lowrank_sumexp_grad_fd,
+              check_lowrank_sumexp_reduction, check_lowrank_sumexp_zstat_fd,
               check_lowrank_zstat_reduction, check_em_corrected_row, check_invariants,
               check_neg_inf_flows]

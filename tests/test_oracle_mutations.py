@@ -31,7 +31,11 @@ MUTATIONS = [
     ("lowrank_dB_without_z_term", "dBg[b] = Ab.T @ D", "dBg[b] = Ab.T @ eps", 0),
     ("lowrank_dA_wrong_factor", "dAg[b] = D @ Bb.T", "dAg[b] = D @ Bb.T[::-1]", 0),
     ("zstat_without_z", "fz = np.where((fi != 0) & (Z > 0), fi / Z, 0.0)", "fz = fi", 0),
-    ("zstat_without_scale", "zf += fz[:, None] * np.exp(Ab @ Bb)", "zf += fz[:, None] * np.ones_like(th)", 0),
+    ("zstat_without_scale", "zf += fz[:, None] * gb", "zf += fz[:, None] * np.ones_like(th)", 0),
+    ("sumexp_scale_as_exp_of_sum", "return np.exp(A_b) @ np.exp(B_b)", "return np.exp(A_b @ B_b)", 0),
+    ("sumexp_dA_without_expA", "dAg[b] = eA * (G @ eB.T)", "dAg[b] = (G @ eB.T)", 0),
+    ("sumexp_dB_without_expB", "dBg[b] = eB * (eA.T @ G)", "dBg[b] = (eA.T @ G)", 0),
+    ("sumexp_grad_through_h", "G = D / gb", "G = D", 0),
     ("zstat_per_copy_overwrite", "ZF[g.param_offset:g.param_offset + th.size] += zf", "ZF[g.param_offset:g.param_offset + th.size] = zf", 0),
     ("em_corrected_not_ratio", "np.where((th > 0) & (w > 0), fp / w, 0.0)", "np.where((th > 0) & (w > 0), fp, 0.0)", 0),
     ("em_corrected_inverted", "np.where((th > 0) & (w > 0), fp / w, 0.0)", "np.where((th > 0) & (w > 0), w / np.maximum(fp, 1e-300), 0.0)", 0),

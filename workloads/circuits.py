@@ -88,6 +88,7 @@ class Circuit:
     layers: list
     root: int = -1                      # node whose value is the log-likelihood (-1: none)
     lowrank_rank: int = 0               # rank k of every LowRank factor pair
+    lowrank_form: str = "exp_sum"       # how the factors make the scale: "exp_sum" or "sum_exp"
     meta: dict = field(default_factory=dict)
 
     # --- structural helpers (no arithmetic of the method) -----------------
@@ -151,7 +152,7 @@ def node_ranges(layer):
 # Builders
 # ---------------------------------------------------------------------------
 
-def hmm(H: int, T: int, V: int, lowrank_rank: int = 0) -> Circuit:
+def hmm(H: int, T: int, V: int, lowrank_rank: int = 0, lowrank_form: str = "exp_sum") -> Circuit:
     """Homogeneous HMM with H hidden states, T positions, V symbols, written as
     a circuit in backward-recursion form.
 
@@ -206,7 +207,7 @@ def hmm(H: int, T: int, V: int, lowrank_rank: int = 0) -> Circuit:
                                 ch_block_start=np.array([child_start], dtype=np.int32),
                                 ch_block_size=H, param_offset=off_init)]))
     c = Circuit(name=f"hmm{H}x{T}v{V}", num_nodes=nxt, num_vars=T, num_params=num_params,
-                layers=layers, root=root, lowrank_rank=lowrank_rank)
+                layers=layers, root=root, lowrank_rank=lowrank_rank, lowrank_form=lowrank_form)
     c.meta = dict(kind="hmm", H=H, T=T, V=V, off_trans=off_trans, off_init=off_init,
                   off_emit=off_emit, sum_starts=sum_starts, prod_starts=prod_starts)
     return c

@@ -37,7 +37,7 @@ def make_config(name: str = None, **over):
     out = dict(B=B, cfg=cfg, tokens=None, external=None, seed_flows=None, lowrank=None)
     if kind == "hmm":
         rank = int(cfg.get("rank", 0))
-        circ = C.hmm(cfg["H"], cfg["T"], cfg["V"], lowrank_rank=rank)
+        circ = C.hmm(cfg["H"], cfg["T"], cfg["V"], lowrank_rank=rank, lowrank_form=cfg.get("form", "exp_sum"))
         out["params"] = I.softmax_rows_params(circ, rng)
         out["tokens"] = I.uniform_tokens(circ, B, cfg["V"], rng)
         if rank > 0:
