@@ -101,7 +101,7 @@ def bench_lowrank(args):
     import torch
     import log_space_sum_amd as L
     from workloads import make_config
-    cfg = make_config("lowrank")
+    cfg = make_config("lowrank", form=args.lowrank_form)
     circ, B = cfg["circuit"], cfg["B"]
     dev = "cuda:0"
     h = L.pc_compile_layout(circ, device=0)
@@ -168,7 +168,7 @@ def bench_lowrank(args):
         "value": round(value, 2), "unit": "Gexp/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16-split" if args.mode == "auto" else "bf16x6-split", "data": "synthetic",
-        "config": {"workload": "lowrank hmm1024x64 symbols 512 rank 16 batch 64 fwd+bwd+em"
+        "config": {"workload": f"lowrank {args.lowrank_form} hmm1024x64 symbols 512 rank 16 batch 64 fwd+bwd+em"
                                + (" (z-corrected)" if args.z_correction else ""), "precision_mode": args.mode,
                    "hip_graph": bool(args.graph and zf is None),
                    "global_batch": B},
@@ -221,6 +221,8 @@ def main():
     ap.add_argument("--lr-cpu-sample", type=int, default=24,
                     help="samples of the LowRank workload the oracle baseline runs on")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--lowrank-form", default="exp_sum", choices=["exp_sum", "sum_exp"],
+                    help="LowRank workload: how the factors make the scale")
     ap.add_argument("--z-correction", type=int, default=0, choices=[0, 1],
                     help="LowRank workload: also accumulate the denominator statistic W and take the conditional M-step")
     ap.add_argument("--graph", type=int, default=0, choices=[0, 1],

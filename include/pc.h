@@ -74,9 +74,10 @@ extern "C" {
  * weights are a row-major [M, N] float32 matrix at params[param_offset].
  * Groups with equal param_offset share (tie) their weights and must have equal
  * M and N; their parameter flows are summed.  lowrank_slot >= 0 makes the
- * group a LowRank exp_sum scaled group (pyjuice.parameterizations.LowRank):
- * per sample b its weights are theta * exp(A_b B_b) normalised over the
- * children, with A_b, B_b read from slot `lowrank_slot` of pc_lowrank_io.
+ * group a LowRank scaled group (pyjuice.parameterizations.LowRank): per
+ * sample b its weights are theta * g_b normalised over the children, with the
+ * scale g_b made from A_b, B_b (slot `lowrank_slot` of pc_lowrank_io) by the
+ * circuit's lowrank_form: exp(A_b B_b) or sum_r exp(A_b[:, r]) exp(B_b[r, :]).
  * A group's children must be distinct nodes. */
 typedef struct pc_sum_group {
   int32_t out_start;
@@ -116,7 +117,13 @@ typedef struct pc_layer_desc {
 /* The circuit: layers in topological order (every child is defined by an
  * earlier layer), every node id in [0, num_nodes) defined exactly once.
  * root: node whose value pc_forward copies to `ll` (-1: none).
- * lowrank_rank: rank k of every LowRank slot (1..32), 0 if none. */
+ * lowrank_rank: rank k of every LowRank slot (1..32), 0 if none.
+ * lowrank_form: how every LowRank slot's factors make the scale
+ *   (pyjuice.parameterizations.LowRank, definition): PC_LOWRANK_EXP_SUM
+ *   g_b = exp(A_b B_b), PC_LOWRANK_SUM_EXP g_b[i,j] = sum_r exp(A_b[i,r])
+ *   exp(B_b[r,j]); other values: PC_ERR_UNSUPPORTED. */
+#define PC_LOWRANK_EXP_SUM 0
+#define PC_LOWRANK_SUM_EXP 1
 typedef struct pc_circuit_desc {
   int32_t num_nodes;
   int32_t num_vars;
@@ -125,6 +132,7 @@ typedef struct pc_circuit_desc {
   const pc_layer_desc* layers;     /* host, [num_layers] */
   int32_t root;
   int32_t lowrank_rank;
+  int32_t lowrank_form;
 } pc_circuit_desc;
 
 typedef struct pc_handle_s* pc_handle;

@@ -21,6 +21,8 @@ PC_PREC_AUTO, PC_PREC_FP32, PC_PREC_TF32 = 0, 1, 2
 PC_LAYER_INPUT_CAT, PC_LAYER_INPUT_EXTERNAL, PC_LAYER_PRODUCT, PC_LAYER_SUM = 0, 1, 2, 3
 PC_CLASS_SHARED, PC_CLASS_STRIDED, PC_CLASS_GENERAL, PC_CLASS_LOWRANK = 0, 1, 2, 3
 PC_BWD_SEEDED = 1
+PC_LOWRANK_EXP_SUM, PC_LOWRANK_SUM_EXP = 0, 1
+LOWRANK_FORMS = {"exp_sum": PC_LOWRANK_EXP_SUM, "sum_exp": PC_LOWRANK_SUM_EXP}
 PC_NUM_KERNEL_KINDS = 15
 KERNEL_KINDS = ["sum_fwd_gemm", "elem_flow_gemm", "param_flow_gemm", "weight_split", "column_max",
                 "exp_children", "scaled_flows", "input_fwd", "input_bwd", "product_fwd",
@@ -47,7 +49,7 @@ class pc_layer_desc(C.Structure):
 class pc_circuit_desc(C.Structure):
     _fields_ = [("num_nodes", C.c_int32), ("num_vars", C.c_int32), ("num_params", C.c_int64),
                 ("num_layers", C.c_int32), ("layers", C.POINTER(pc_layer_desc)), ("root", C.c_int32),
-                ("lowrank_rank", C.c_int32)]
+                ("lowrank_rank", C.c_int32), ("lowrank_form", C.c_int32)]
 
 
 class pc_lowrank_io(C.Structure):
@@ -186,7 +188,8 @@ def pc_compile_layout(circuit, device: int = 0) -> Handle:
     desc = pc_circuit_desc(num_nodes=int(circuit.num_nodes), num_vars=int(circuit.num_vars),
                            num_params=int(circuit.num_params), num_layers=len(circuit.layers),
                            layers=layers, root=int(circuit.root),
-                           lowrank_rank=int(getattr(circuit, "lowrank_rank", 0)))
+                           lowrank_rank=int(getattr(circuit, "lowrank_rank", 0)),
+                           lowrank_form=LOWRANK_FORMS[getattr(circuit, "lowrank_form", "exp_sum")])
     out = C.c_void_p()
     _check(lib().pc_compile_layout(C.byref(desc), int(device), C.byref(out)))
     return Handle(out, circuit)

@@ -132,6 +132,11 @@ template <int PH, int PG, int KC>
 __global__ __launch_bounds__(256) void k_lr_pack(LRPackArgs pa) {
   using PK = LrPack<PH, PG, KC>;
   const int tid = threadIdx.x;
+  // "sum_exp": every record holds exp of the factor (the matrix instructions
+  // then sum exp(A) exp(B) over the rank, no log2(e) on the h form); padding
+  // stays 0
+  const bool se = pa.sumexp != 0;
+  auto fv = [se](float v) { return se ? expf(v) : v; };
   int g = 0;
   while (g + 1 < pa.ngroups && (int)blockIdx.x >= pa.wg0[g + 1]) ++g;
   const int M = pa.M[g], N = pa.N[g], Bn = pa.B, kr = pa.krank;
@@ -153,7 +158,7 @@ __global__ __launch_bounds__(256) void k_lr_pack(LRPackArgs pa) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int k = form * 16 + h * 8 + e;
-        x[e] = (k < kr && j < N) ? Bb[(int64_t)k * N + j] : 0.0f;
+        x[e] = (k < kr && j < N) ? fv(Bb[(int64_t)k * N + j]) : 0.0f;
       }
       split_store_frag<PH>(x, dst + form * PH * kFrag);
     } else {
@@ -163,14 +168,14 @@ __global__ __launch_bounds__(256) void k_lr_pack(LRPackArgs pa) {
         const float4 u0 = ld4(Bb + (int64_t)l32 * N + jq), u1 = ld4(Bb + (int64_t)l32 * N + jq + 8);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          x[e] = at4(u0, e);
-          x[4 + e] = at4(u1, e);
+          x[e] = fv(at4(u0, e));
+          x[4 + e] = fv(at4(u1, e));
         }
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int j = jq + (e / 4) * 8 + (e % 4);
-          x[e] = (l32 < kr && j < N) ? Bb[(int64_t)l32 * N + j] : 0.0f;
+          x[e] = (l32 < kr && j < N) ? fv(Bb[(int64_t)l32 * N + j]) : 0.0f;
         }
       }
       split_store_frag<PG>(x, dst + (KC * PH + cc * PG) * kFrag);
@@ -185,14 +190,14 @@ __global__ __launch_bounds__(256) void k_lr_pack(LRPackArgs pa) {
         const float4 u0 = ld4(Ab + (int64_t)i * kr + k0), u1 = ld4(Ab + (int64_t)i * kr + k0 + 4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          x[e] = at4(u0, e) * kLog2e;
-          x[4 + e] = at4(u1, e) * kLog2e;
+          x[e] = se ? expf(at4(u0, e)) : at4(u0, e) * kLog2e;
+          x[4 + e] = se ? expf(at4(u1, e)) : at4(u1, e) * kLog2e;
         }
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int k = k0 + e;
-          x[e] = (k < kr && i < M) ? Ab[(int64_t)i * kr + k] * kLog2e : 0.0f;
+          x[e] = (k < kr && i < M) ? (se ? expf(Ab[(int64_t)i * kr + k]) : Ab[(int64_t)i * kr + k] * kLog2e) : 0.0f;
         }
       }
       split_store_frag<PH>(x, dst + form * PH * kFrag);
@@ -201,7 +206,7 @@ __global__ __launch_bounds__(256) void k_lr_pack(LRPackArgs pa) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int i = ib * 32 + 16 * cc + (e / 4) * 8 + h * 4 + (e % 4);
-        x[e] = (l32 < kr && i < M) ? Ab[(int64_t)i * kr + l32] : 0.0f;
+        x[e] = (l32 < kr && i < M) ? fv(Ab[(int64_t)i * kr + l32]) : 0.0f;
       }
       split_store_frag<PG>(x, dst + (KC * PH + cc * PG) * kFrag);
     }
@@ -210,7 +215,9 @@ __global__ __launch_bounds__(256) void k_lr_pack(LRPackArgs pa) {
 
 // Backward coefficients, one (sample, row) per thread over rows padded to 32:
 // c1 = f / Sraw, c2 = f / Z (zero where the flow is zero or the node's value
-// is -inf, and on the padding rows) and dLL/dA_b[i, k] = c1 U[i, k] - c2 W[i, k].
+// is -inf, and on the padding rows) and dLL/dA_b[i, k] = c1 U[i, k] - c2 W[i, k]
+// ("exp_sum"), exp(A_b[i, k]) (c1 U[i, k] - c2 W[i, k]) ("sum_exp", whose U and
+// W sum theta e exp(B) and theta exp(B) over the children).
 __global__ __launch_bounds__(256) void k_lr_coef(LRArgs a) {
   const int ldC = (a.M + 31) / 32 * 32;
   const int64_t xc = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -238,7 +245,10 @@ __global__ __launch_bounds__(256) void k_lr_coef(LRArgs a) {
   a.C1[xc] = c1;
   a.C2[xc] = c2;
   const int kr = a.krank;
-  if ((kr & 3) == 0) {        // rows of U, W, dA 16-byte aligned
+  if (a.sumexp) {
+    for (int k = 0; k < kr; ++k)
+      a.dA[x * kr + k] = expf(a.A[x * kr + k]) * (c1 * a.U[x * kr + k] - c2 * a.W[x * kr + k]);
+  } else if ((kr & 3) == 0) {        // rows of U, W, dA 16-byte aligned
     for (int k = 0; k < kr; k += 4) {
       const float4 u = ld4(a.U + x * kr + k), w = ld4(a.W + x * kr + k);
       *(float4*)(a.dA + x * kr + k) =
@@ -252,8 +262,11 @@ __global__ __launch_bounds__(256) void k_lr_coef(LRArgs a) {
 // Forward: workgroup = 32 rows x 4 samples (one per wave), all children, in
 // chunks of kChunkF children.  Per chunk the weights of the row strip and
 // e[j, b] = exp(v[child j, b] - m[b]) of the 4 samples are staged in LDS; a
-// wave streams its sample's B records one 32-child block ahead.
-template <int PH, int PG, int KC>
+// wave streams its sample's B records one 32-child block ahead.  SE: the
+// "sum_exp" form, whose records hold exp(A), exp(B), so the matrix product is
+// the scale g itself (no exp per pair) and U, W sum theta e and theta against
+// exp(B) (the coefficient kernel multiplies by exp(A)).
+template <int PH, int PG, int KC, bool SE = false>
 __global__ __launch_bounds__(256) void k_lr_fwd(LRArgs a) {
   using PK = LrPack<PH, PG, KC>;
   __shared__ __attribute__((aligned(16))) float slab[kSlabF];   // theta rows [32][C + 4]
@@ -387,10 +400,19 @@ __global__ __launch_bounds__(256) void k_lr_fwd(LRArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = g * 4 + e;
-          q[r] = (at4(th, e) * live) * __builtin_amdgcn_exp2f(H[r]);
-          qe[r] = q[r] * at4(ev, e);
-          Zp += q[r];
-          Sp += qe[r];
+          if constexpr (SE) {
+            const float tl = at4(th, e) * live;
+            const float qq = tl * H[r];
+            Zp += qq;
+            Sp += qq * at4(ev, e);
+            q[r] = tl;                          // U, W operands: theta e and theta
+            qe[r] = tl * at4(ev, e);
+          } else {
+            q[r] = (at4(th, e) * live) * __builtin_amdgcn_exp2f(H[r]);
+            qe[r] = q[r] * at4(ev, e);
+            Zp += q[r];
+            Sp += qe[r];
+          }
         }
       }
       // U^T[k, i] += sum_j B_b[k, j] qe[j, i], W^T[k, i] += sum_j B_b[k, j] q[j, i]:
@@ -450,7 +472,10 @@ __global__ __launch_bounds__(256) void k_lr_fwd(LRArgs a) {
 // computes only w[i, j] = c2[i] * exp(h[i, j]) per sample (c2 = f / Z), summed
 // over the 8 waves into the partial matrices at a.P like the parameter flows;
 // no weights, element flows or dB.
-template <int PH, int PG, int KC, bool WS = false>
+// SE: the "sum_exp" form (records of exp(A), exp(B): the product is g), whose
+// dB term is theta (c1 e - c2) against exp(A) and is multiplied by exp(B) at
+// the end.
+template <int PH, int PG, int KC, bool WS = false, bool SE = false>
 __global__ __launch_bounds__(512) void k_lr_bwd(LRArgs a) {
   using PK = LrPack<PH, PG, KC>;
   __shared__ __attribute__((aligned(16))) float slab[kSlabB];   // theta^T [32][R + 4]
@@ -600,7 +625,7 @@ __global__ __launch_bounds__(512) void k_lr_bwd(LRArgs a) {
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 const int r = g * 4 + e;
-                xw[r * 64] = at4(cc_.c2[g], e) * __builtin_amdgcn_exp2f(H[r]);
+                xw[r * 64] = at4(cc_.c2[g], e) * (SE ? H[r] : __builtin_amdgcn_exp2f(H[r]));
               }
           } else {
           float X[16];
@@ -610,10 +635,10 @@ __global__ __launch_bounds__(512) void k_lr_bwd(LRArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int r = g * 4 + e;
-              const float q = at4(th, e) * __builtin_amdgcn_exp2f(H[r]);
+              const float q = at4(th, e) * (SE ? H[r] : __builtin_amdgcn_exp2f(H[r]));
               const float u1 = ev * at4(cc_.c1[g], e);
               const float eps = q * u1;
-              X[r] = q * (u1 - at4(cc_.c2[g], e));
+              X[r] = (SE ? at4(th, e) : q) * (u1 - at4(cc_.c2[g], e));
               fcp += eps;
               xw[r * 64] = eps;
             }
@@ -680,7 +705,8 @@ __global__ __launch_bounds__(512) void k_lr_bwd(LRArgs a) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int k = (r / 4) * 8 + h * 4 + (r % 4);
-    if (k < kr) a.dB[((int64_t)b * kr + k) * N + j] = dB[r];
+    const int64_t o = ((int64_t)b * kr + k) * N + j;
+    if (k < kr) a.dB[o] = SE ? expf(a.Bf[o]) * dB[r] : dB[r];
   }
 }
 
@@ -705,12 +731,22 @@ static int grid_lr(int64_t n) {
 template <int PH, int PG>
 static void lr_fwd_k(const LRArgs& a, hipStream_t s) {
   const dim3 grid(((a.M + 31) / 32) * ((a.B + 3) / 4));
+  if (a.sumexp) {
+    if (a.krank <= 16) hipLaunchKernelGGL((k_lr_fwd<PH, PG, 1, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_lr_fwd<PH, PG, 2, true>), grid, dim3(256), 0, s, a);
+    return;
+  }
   if (a.krank <= 16) hipLaunchKernelGGL((k_lr_fwd<PH, PG, 1>), grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL((k_lr_fwd<PH, PG, 2>), grid, dim3(256), 0, s, a);
 }
 template <int PH, int PG, bool WS = false>
 static void lr_bwd_k(const LRArgs& a, hipStream_t s) {
   const dim3 grid(((a.N + 31) / 32) * ((a.B + 7) / 8));
+  if (a.sumexp) {
+    if (a.krank <= 16) hipLaunchKernelGGL((k_lr_bwd<PH, PG, 1, WS, true>), grid, dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((k_lr_bwd<PH, PG, 2, WS, true>), grid, dim3(512), 0, s, a);
+    return;
+  }
   if (a.krank <= 16) hipLaunchKernelGGL((k_lr_bwd<PH, PG, 1, WS>), grid, dim3(512), 0, s, a);
   else hipLaunchKernelGGL((k_lr_bwd<PH, PG, 2, WS>), grid, dim3(512), 0, s, a);
 }

@@ -420,6 +420,7 @@ LRArgs lr_args(const Call& c, const SumPlan& sp, int g, const pc_lowrank_io* io,
   a.M = r.M;
   a.N = r.N;
   a.krank = h->lowrank_rank;
+  a.sumexp = h->lowrank_form == PC_LOWRANK_SUM_EXP ? 1 : 0;
   a.out_start = r.out_start;
   a.m_row = r.m_row;
   a.cbs = r.cbs;
@@ -454,6 +455,7 @@ void lr_pack_group(const Call& c, const SumPlan& sp, int g, const pc_lowrank_io*
   LRPackArgs pa{};
   pa.B = c.v.B;
   pa.krank = c.h->lowrank_rank;
+  pa.sumexp = c.h->lowrank_form == PC_LOWRANK_SUM_EXP ? 1 : 0;
   pa.ngroups = 1;
   pa.M[0] = r.M;
   pa.N[0] = r.N;
@@ -690,6 +692,7 @@ int pc_forward(pc_handle hh, int batch, const int32_t* tokens, const float* para
       LRPackArgs pa{};
       pa.B = B;
       pa.krank = h->lowrank_rank;
+      pa.sumexp = h->lowrank_form == PC_LOWRANK_SUM_EXP ? 1 : 0;
       auto flush = [&]() {
         if (pa.ngroups == 0) return;
         Timed t(h, KK_SPLIT, c.s);

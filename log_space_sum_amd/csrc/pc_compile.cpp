@@ -35,7 +35,9 @@ Handle* compile_layout(const pc_circuit_desc* d) {
   need(d->num_layers >= 1 && d->layers != nullptr, "need at least one layer");
   need(d->root >= -1 && d->root < d->num_nodes, "root out of range");
   if (d->lowrank_rank < 0 || d->lowrank_rank > 32)
-    fail(PC_ERR_UNSUPPORTED, "LowRank rank must be in 1..32 (the fused exp_sum kernels)");
+    fail(PC_ERR_UNSUPPORTED, "LowRank rank must be in 1..32 (the fused LowRank kernels)");
+  if (d->lowrank_form != PC_LOWRANK_EXP_SUM && d->lowrank_form != PC_LOWRANK_SUM_EXP)
+    fail(PC_ERR_UNSUPPORTED, "LowRank form must be PC_LOWRANK_EXP_SUM or PC_LOWRANK_SUM_EXP");
 
   Handle* h = new Handle();
   h->num_nodes = d->num_nodes;
@@ -43,6 +45,7 @@ Handle* compile_layout(const pc_circuit_desc* d) {
   h->num_params = d->num_params;
   h->root = d->root;
   h->lowrank_rank = d->lowrank_rank;
+  h->lowrank_form = d->lowrank_form;
   const int64_t NN = d->num_nodes;
 
   std::vector<int32_t> defined_at(NN, -1);

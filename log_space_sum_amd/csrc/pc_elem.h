@@ -116,6 +116,7 @@ struct LRArgs {
   // coefficients: the following product layer's backward first (fp_on): the
   // flow of product node fp_pstart + i goes to output i and to node fp_other + i
   int32_t fp_on, fp_pstart, fp_other;
+  int32_t sumexp;        // the "sum_exp" form (records of exp(A), exp(B))
   const int32_t* chblocks;
   const float* theta;
   const float* A;
@@ -142,6 +143,7 @@ struct LRArgs {
 constexpr int kMaxPackGroups = 48;
 struct LRPackArgs {
   int32_t B, krank, ngroups;
+  int32_t sumexp;                  // records of exp(A), exp(B) ("sum_exp" form)
   int32_t M[kMaxPackGroups], N[kMaxPackGroups];
   int32_t wg0[kMaxPackGroups + 1];
   const float* A[kMaxPackGroups];

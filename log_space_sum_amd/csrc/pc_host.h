@@ -140,6 +140,7 @@ struct Handle {
   void* side_stream = nullptr;         // parameter-flow chunks run here, beside the element flows
   std::vector<void*> chunk_events;
   int32_t num_nodes = 0, num_vars = 0, root = -1, lowrank_rank = 0;
+  int32_t lowrank_form = PC_LOWRANK_EXP_SUM;
   int64_t num_params = 0;
   std::vector<LayerRef> layers;
   std::vector<InputPlan> inputs;

@@ -230,7 +230,7 @@ def _sub_sum_circuit(circ, layer):
         outs.append(np.arange(g.out_start, g.out_start + g.num_nodes))
         nxt += g.num_nodes
     sub = W.Circuit("sub", nxt, 0, circ.num_params, [W.InputExternal(0, n_ext), W.Sum(groups)],
-                    root=-1, lowrank_rank=circ.lowrank_rank)
+                    root=-1, lowrank_rank=circ.lowrank_rank, lowrank_form=circ.lowrank_form)
     return sub, kids, np.concatenate(outs)
 
 

@@ -123,6 +123,15 @@ def test_descriptor_errors():
     c = W.hmm(4, 3, 2, lowrank_rank=33)
     _expect(L.PC_ERR_UNSUPPORTED, L.pc_compile_layout, c, -1)
     L.pc_compile_layout(W.hmm(4, 3, 2, lowrank_rank=32), -1)
+    # LowRank forms: exp_sum and sum_exp compile, any other value is refused
+    L.pc_compile_layout(W.hmm(4, 3, 2, lowrank_rank=4, lowrank_form="sum_exp"), -1)
+    c = W.hmm(4, 3, 2, lowrank_rank=4)
+    L.LOWRANK_FORMS["bogus"] = 7
+    try:
+        c.lowrank_form = "bogus"
+        _expect(L.PC_ERR_UNSUPPORTED, L.pc_compile_layout, c, -1)
+    finally:
+        del L.LOWRANK_FORMS["bogus"]
 
 
 def test_modes_and_workspace():

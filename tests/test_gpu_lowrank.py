@@ -87,6 +87,39 @@ def test_lowrank_z_correction(mode, H, T, V, rank, B, spread):
     G.check_flows(gpu["em_corrected"], ref, "fp32", f"{what} conditional M-step")
 
 
+@pytest.mark.parametrize("mode", ["auto", "fp32"])
+@pytest.mark.parametrize("H,T,V,rank,B,spread", [
+    (8, 4, 5, 4, 20, 1.0),        # tiny: one partial 32-row strip
+    (64, 5, 16, 16, 37, 1.0),     # two strips, ragged sample groups
+    (40, 4, 7, 5, 23, 1.0),       # ragged rows and children
+    (96, 3, 9, 32, 24, 4.0),      # rank 32 (two K steps), 4-nat spread
+])
+def test_lowrank_sum_exp(mode, H, T, V, rank, B, spread):
+    """The "sum_exp" form (g_b[i, j] = sum_r exp(A_b[i, r]) exp(B_b[r, j])):
+    the same checks as the exp_sum form."""
+    cfg = make_config("lowrank", H=H, T=T, V=V, rank=rank, B=B, spread=spread, form="sum_exp")
+    _lowrank_full(cfg, mode, f"lowrank sum_exp H{H} T{T} r{rank} s{spread}")
+
+
+def test_lowrank_sum_exp_z_correction():
+    """W and the conditional M-step under the "sum_exp" form (auto)."""
+    import oracle
+    cfg = make_config("lowrank", H=64, T=4, V=9, rank=16, B=29, spread=1.0, form="sum_exp")
+    circ = cfg["circuit"]
+    what = "lowrank sum_exp z-correction"
+    G.say(f"case {what} mode=auto B={cfg['B']}")
+    gpu = G.run_gpu(cfg, "auto", z_init=np.zeros(circ.num_params, np.float32), em_corrected=(1.0, 0.0))
+    orc = G.run_oracle(cfg)
+    inside = np.zeros(circ.num_params, bool)
+    for off, n in oracle.lowrank_param_ranges(circ):
+        inside[off:off + n] = True
+    G.check_flows(gpu["z_flows"][inside], orc["z_flows"][inside], "auto", f"{what} W end to end",
+                  scale=G.num_sum_layers(circ))
+    ref = oracle.em_step_corrected(circ, cfg["params"], gpu["pflows"].astype(np.float64),
+                                   gpu["z_flows"].astype(np.float64))
+    G.check_flows(gpu["em_corrected"], ref, "fp32", f"{what} conditional M-step")
+
+
 def test_lowrank_small_batch_runs_fp32():
     """Batches below 16 run fp32-level products (the LowRank kernels included)."""
     cfg = make_config("lowrank", H=40, T=3, V=6, rank=8, B=9)
