@@ -203,12 +203,12 @@ int pc_get_precision(pc_handle h, int* mode);
  * operand; the products of planes whose order is below the larger count are
  * accumulated: (1,1) one bf16 product; (2,1) or (1,2) one operand split,
  * two products; (2,2) hi/lo split, three products; (3,3) hi/mid/lo split,
- * six products.  Defaults: auto (2,1) forward (weights split, exp operand
- * rounded), (1,2) element flows (transposed weights rounded, scaled flows g
- * split), (2,1) parameter flows (g split, exp operand rounded), so that every
- * value or flow dominated by one product carries a single bf16 rounding (at
- * most 2^-8 relative) and the weights' own rounding, the same for every
- * sample, enters the parameter flows once; fp32-level (3,3) everywhere.  Errors: PC_ERR_INVALID_ARG for other counts or kinds. */
+ * six products.  Defaults: auto (2,1) for all three (forward and element
+ * flows split the weights, parameter flows split the scaled flows g), so that
+ * every value or flow dominated by one product carries a single bf16
+ * rounding (at most 2^-8 relative) and the weights, whose rounding would be
+ * the same for every sample, are never rounded alone; fp32-level (3,3)
+ * everywhere.  Errors: PC_ERR_INVALID_ARG for other counts or kinds. */
 int pc_set_split(pc_handle h, int mode, int gemm_kind, int planes_a, int planes_b);
 
 /* Product-kernel tuning (advanced; results change only by float32 summation
