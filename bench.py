@@ -230,8 +230,8 @@ def main():
     ap.add_argument("--layer-tile", type=int, default=0, help="product-kernel option: 0 auto, 1 128x128, 2 256x128, 3 128x256, 4 128x64, 5 64x128")
     ap.add_argument("--param-tile", type=int, default=0, help="product-kernel option: 0 auto, 1 128x128, 2 256x256, 3 128x256")
     ap.add_argument("--split-max", type=int, default=8, help="largest K split of a per-layer product")
-    ap.add_argument("--param-chunk", type=int, default=0,
-                    help="tied copies per parameter-flow launch on a second stream (0: one launch at the end)")
+    ap.add_argument("--param-chunk", type=int, default=-1,
+                    help="tied copies per parameter-flow launch on a second stream (-1: automatic, 0: one launch at the end)")
     ap.add_argument("--lr-pack", type=int, default=0, choices=[0, 1],
                     help="LowRank factor records: 0 made once per forward, 1 per layer and pass")
     ap.add_argument("--fuse", type=int, default=1, choices=[0, 1],

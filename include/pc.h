@@ -225,13 +225,15 @@ int pc_set_split(pc_handle h, int mode, int gemm_kind, int planes_a, int planes_
  * adjacent sum layer's memory-bound kernels where the layout allows it (the
  * forward in the next sum layer's column maxima, the backward in the previous
  * sum layer's scaled-flow packing; identical results), 0 launches the
- * product kernels separately.  PC_OPT_PARAM_CHUNK: 0 (default) computes the
+ * product kernels separately.  PC_OPT_PARAM_CHUNK: 0 computes the
  * parameter flows in one product after the layers; n > 0 computes them in
  * chunks of n tied copies per weight block on a second stream of the
  * handle, each as soon as its copies' scaled flows exist, overlapping the
  * element flows (deterministic; the float32 sum is grouped by chunk, so the
- * bits differ from n = 0).  pc_backward joins that stream into the caller's
- * before it returns.  PC_OPT_LR_PACK: when the bfloat16 fragment records of
+ * bits can differ from n = 0); -1 (default) chooses: one chunk of all the
+ * copies of each block when the layout has at most 8 weight blocks and one of
+ * them is tied (2 or more copies), else 0.  pc_backward joins that stream
+ * into the caller's before it returns.  PC_OPT_LR_PACK: when the bfloat16 fragment records of
  * the LowRank factors are made: 0 (default) all at once at the start of
  * pc_forward, kept for pc_backward; 1 each group's just before its layer, in
  * both passes (identical results).  Changing an option can change

@@ -224,8 +224,9 @@ def pc_set_option(h: Handle, option, value: int):
     """Kernel tuning: layer_tile (0 auto, 1 128x128, 2 256x128, 3 128x256, 4 128x64, 5 64x128), param_tile
     (0 auto, 1 128x128, 2 256x256, 3 128x256), split_max (1, 2, 4, 8), fuse (1: product
     layers inside the adjacent sum layer's kernels, 0: separate launches),
-    param_chunk (0: parameter flows in one product at the end; n: in chunks of
-    n tied copies on a second stream, overlapping the element flows)."""
+    param_chunk (-1 automatic; 0: parameter flows in one product at the end;
+    n: in chunks of n tied copies on a second stream, overlapping the element
+    flows)."""
     option = OPTIONS.get(option, option) if isinstance(option, str) else option
     _check(lib().pc_set_option(h.ptr, int(option), int(value)))
 

@@ -134,7 +134,7 @@ struct Handle {
   // planes[mode][gemm kind][0: first operand, 1: second operand]
   int planes[2][3][2] = {{{2, 1}, {2, 1}, {2, 1}}, {{3, 3}, {3, 3}, {3, 3}}};
   int opt_layer_tile = 0, opt_param_tile = 0, opt_split_max = 8, opt_fuse = 1;   // pc_set_option
-  int opt_param_chunk = 0;             // tied copies per parameter-flow launch (0: one launch at the end)
+  int opt_param_chunk = -1;            // tied copies per parameter-flow launch (0: one launch at the end, -1: automatic)
   int opt_lr_pack = 0;                 // LowRank fragment records: 0 once per forward, 1 per layer and pass
   std::vector<std::vector<int32_t>> copy_layer;   // per weight block: the layer of each tied copy
   void* side_stream = nullptr;         // parameter-flow chunks run here, beside the element flows

@@ -156,7 +156,7 @@ def test_options():
     h = L.pc_compile_layout(W.hmm(64, 6, 9), device=-1)
     for name, good, bad in (("layer_tile", (0, 1, 2, 3, 4, 5), (6, -1)), ("param_tile", (0, 1, 2, 3), (4,)),
                             ("split_max", (1, 2, 4, 8), (0, 3, 16)), ("fuse", (0, 1), (2, -1)),
-                            ("param_chunk", (0, 1, 8, 100), (-1,)), ("lr_pack", (0, 1), (2, -1))):
+                            ("param_chunk", (-1, 0, 1, 8, 100), (-2,)), ("lr_pack", (0, 1), (2, -1))):
         for v in good:
             L.pc_set_option(h, name, v)
         for v in bad:
