@@ -20,8 +20,11 @@
  *    or keeps it beyond the call.
  *  - `stream` is a hipStream_t (0 = the null stream).  Device work is
  *    enqueued on it and the call returns without synchronising; the library
- *    allocates no device memory inside pc_forward / pc_backward / pc_em_step:
- *    every scratch byte comes from the caller's workspace.
+ *    allocates no device memory inside pc_forward / pc_backward / pc_em_step /
+ *    pc_em_step_corrected: every scratch byte comes from the caller's
+ *    workspace.  (With parameter-flow chunks, PC_OPT_PARAM_CHUNK, the first
+ *    pc_backward of a handle creates the handle's second stream and events;
+ *    pc_backward joins that stream into `stream` before it returns.)
  *  - Return value: PC_OK or a PC_ERR_* code; pc_last_error() gives a message
  *    for the calling thread.  A failed call enqueues no device work.
  *  - Calls on one handle must not overlap in time (they share the handle's
