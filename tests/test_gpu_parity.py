@@ -224,3 +224,19 @@ def test_param_flow_chunks(what, cfg_args, chunk, mode):
     again = G.run_gpu(cfg, mode, options=opts)
     np.testing.assert_array_equal(gpu["pflows"], again["pflows"])
     np.testing.assert_array_equal(gpu["flows"], again["flows"])
+
+
+@pytest.mark.parametrize("what,cfg_args", [
+    ("hmm", dict(name="hmm4096", H=320, T=7, V=50, B=70)),                      # tied: one chunk per block
+    ("hclt", dict(name="hclt", num_vars=30, H=48, K=12, B=33)),                 # many blocks: one product
+])
+def test_param_flow_automatic_chunks_same_bits(what, cfg_args):
+    """The automatic choice (one chunk of all copies per block on the second
+    stream, or the single product after the layers) gives the same bits as
+    the single product: the same K order over every block's copies."""
+    cfg = make_config(**cfg_args)
+    G.say(f"case automatic parameter-flow chunks: {what} B={cfg['B']}")
+    auto = G.run_gpu(cfg, "auto")
+    single = G.run_gpu(cfg, "auto", options=[("param_chunk", 0)])
+    np.testing.assert_array_equal(auto["pflows"], single["pflows"], err_msg=f"{what}: parameter flows")
+    np.testing.assert_array_equal(auto["flows"], single["flows"], err_msg=f"{what}: flows")
