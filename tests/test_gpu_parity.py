@@ -185,6 +185,17 @@ def test_fused_product_layers_identical(what, cfg_args, mode, all_fused):
 
 
 @pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("H,T,V,B,skew", [(96, 6, 37, 264, 0.0), (64, 5, 500, 512, 0.5), (80, 4, 512, 256, 0.9)])
+def test_input_rows_of_several_nodes(mode, H, T, V, B, skew):
+    """Input-layer parameter flows of rows shared by several nodes (an HMM's
+    emission row of a hidden state, one node per position) at the batches
+    taken one row per wave (256 to 512 samples, a multiple of 8), with
+    uniform categories and with one large bucket per variable."""
+    cfg = make_config("hmm4096", H=H, T=T, V=V, B=B, skew=skew)
+    _full(cfg, mode, f"hmm {H}x{T} V={V} skew={skew} input rows")
+
+
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("tile", [1, 2, 3, 4, 5])
 def test_layer_tile_options(tile, mode):
     """Every per-layer product tile shape (128x128, 256x128, 128x256, 128x64, 64x128)

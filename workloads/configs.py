@@ -39,7 +39,10 @@ def make_config(name: str = None, **over):
         rank = int(cfg.get("rank", 0))
         circ = C.hmm(cfg["H"], cfg["T"], cfg["V"], lowrank_rank=rank, lowrank_form=cfg.get("form", "exp_sum"))
         out["params"] = I.softmax_rows_params(circ, rng)
-        out["tokens"] = I.uniform_tokens(circ, B, cfg["V"], rng)
+        if cfg.get("skew"):
+            out["tokens"] = I.skewed_tokens(circ, B, cfg["V"], float(cfg["skew"]), rng)
+        else:
+            out["tokens"] = I.uniform_tokens(circ, B, cfg["V"], rng)
         if rank > 0:
             sigma = cfg.get("sigma") or I.lowrank_sigma_for_spread(cfg.get("spread", 1.0), rank)
             out["lowrank"] = I.lowrank_factors(circ, B, sigma, rng)

@@ -27,6 +27,15 @@ def uniform_tokens(circ: Circuit, B: int, num_cats: int, rng: np.random.Generato
     return rng.integers(0, num_cats, size=(B, circ.num_vars)).astype(np.int32)
 
 
+def skewed_tokens(circ: Circuit, B: int, num_cats: int, frac: float, rng: np.random.Generator) -> np.ndarray:
+    """Tokens [B, num_vars] int32: uniform over [0, num_cats), then each entry
+    replaced by the last category with probability ``frac`` (one large bucket
+    per variable beside small ones)."""
+    tok = rng.integers(0, num_cats, size=(B, circ.num_vars))
+    tok[rng.random(tok.shape) < frac] = num_cats - 1
+    return tok.astype(np.int32)
+
+
 def external_values(circ: Circuit, B: int, rng: np.random.Generator,
                     shift_hi: float = 300.0, spread_hi: float = 50.0) -> np.ndarray:
     """Values for every InputExternal layer, stacked in layer order: a
