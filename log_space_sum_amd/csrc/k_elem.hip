@@ -1002,7 +1002,13 @@ void launch_tokens_t(const int32_t* tok, int32_t* tokT, int B, int V, hipStream_
       hipLaunchKernelGGL(kern<1>, dim3(grid_for((int64_t)(n_items) * (args).B)), dim3(256), 0, s, args);       \
   } while (0)
 
-void launch_input_fwd(const InputArgs& a, hipStream_t s) { PC_LAUNCH_V(k_input_fwd, a.num_nodes, a, s); }
+void launch_input_fwd(const InputArgs& a, hipStream_t s) {
+  // a lane takes the kernel's 4 items per pass (their loads in flight together)
+  if ((a.B & 3) == 0)
+    hipLaunchKernelGGL(k_input_fwd<4>, dim3(grid_for((int64_t)a.num_nodes * (a.B / 4), 256 * 4)), dim3(256), 0, s, a);
+  else
+    PC_LAUNCH_V(k_input_fwd, a.num_nodes, a, s);
+}
 void launch_bucket(const int32_t* tokT, int V, int B, int Kmax, int32_t* bptr, int32_t* bidx, hipStream_t s) {
   const size_t sh = (size_t)(Kmax + 1 + B) * sizeof(int32_t);
   hipLaunchKernelGGL(k_bucket, dim3(V), dim3(256), sh, s, tokT, B, Kmax, bptr, bidx);
