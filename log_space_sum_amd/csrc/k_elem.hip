@@ -52,7 +52,7 @@ __device__ __forceinline__ int last_le(const Rec* recs, int n, int x, F field) {
 }
 
 __device__ __forceinline__ int child_of(const GroupRec& g, const int32_t* blocks, int k) {
-  return blocks[g.blk_off + k / g.cbs] + k % g.cbs;
+  return g.ch_start >= 0 ? g.ch_start + k : blocks[g.blk_off + k / g.cbs] + k % g.cbs;
 }
 
 // ---- fills, copies, transposes ----------------------------------------------
@@ -778,12 +778,14 @@ __global__ __launch_bounds__(256) void k_pack(SumArgs a) {
     }
   }
   __syncthreads();
-  // phase 2: item = (sample, 8-row chunk); K columns up to the padded row count
+  // phase 2: item = (sample, 8-row chunk); K columns up to the padded row count.
+  // Four consecutive lanes take the four chunks of one sample's 32-row block,
+  // so each store instruction writes whole 64-byte runs.
   const int kpad = (nrows + K_PAD - 1) / K_PAD * K_PAD;
   const int tk0 = KIND == 0 ? gr.e_koff : gr.g_koff;
   if (r0 >= kpad) return;
   for (int it = tid; it < 512; it += 256) {
-    const int bl = it & 63, c = it >> 6;
+    const int bl = (it >> 2) & 63, c = (it >> 8) * 4 + (it & 3);
     const int bb = b0 + bl;
     if (bb >= a.B_pad) continue;
     float x[8];

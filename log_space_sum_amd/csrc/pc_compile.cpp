@@ -222,6 +222,9 @@ Handle* compile_layout(const pc_circuit_desc* d) {
         r.nblk = G.num_ch_blocks;
         r.param_offset = G.param_offset;
         r.lowrank = G.lowrank_slot;
+        r.ch_start = G.num_ch_blocks > 0 ? G.ch_block_start[0] : -1;
+        for (int32_t b = 1; b < G.num_ch_blocks && r.ch_start >= 0; ++b)
+          if (G.ch_block_start[b] != G.ch_block_start[0] + (int64_t)b * G.ch_block_size) r.ch_start = -1;
         sp.blocks.insert(sp.blocks.end(), G.ch_block_start, G.ch_block_start + G.num_ch_blocks);
         sp.groups.push_back(r);
       }

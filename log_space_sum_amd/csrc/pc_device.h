@@ -52,6 +52,7 @@ struct GroupRec {
   int32_t lowrank;       // LowRank slot or -1
   int32_t share_src;     // group whose E slice this group reuses (SHARED layers), or itself
   int32_t share_next;    // next group sharing this group's children (its E rows get a copy), or -1
+  int32_t ch_start;      // child k is node ch_start + k when the child blocks are consecutive, else -1
   int64_t s_row;         // first row of the group's scaled sums S (kept from the forward), -1 if none
 };
 
