@@ -770,7 +770,10 @@ __global__ __launch_bounds__(256) void k_pack(SumArgs a) {
     for (int e = 0; e < 8; ++e) tile[r][c * 8 + e] = x[e];
     if (bs < a.B_padK) {
       if (KIND == 0) {
-        for (int q = g; q >= 0; q = a.groups[q].share_next)
+        // this group's rows from the record already in registers (a table
+        // read after a store would wait for it), then the sharing chain's
+        split_store8(x, a.np_direct, a.direct + panel(gr.e_row + k, bs, a.direct_rows), a.direct_plane);
+        for (int q = gr.share_next; q >= 0; q = a.groups[q].share_next)
           split_store8(x, a.np_direct, a.direct + panel(a.groups[q].e_row + k, bs, a.direct_rows), a.direct_plane);
       } else {
         split_store8(x, a.np_direct, a.direct + panel(gr.g_row + k, bs, a.direct_rows), a.direct_plane);
