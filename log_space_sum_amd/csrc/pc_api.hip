@@ -365,6 +365,7 @@ SumArgs sum_common(const Call& c, const SumPlan& sp) {
   a.btiles = c.v.B_pad / 64;
   a.ngroups = (int)sp.groups.size();
   a.groups = sp.d_groups;
+  if (sp.groups.size() == 1) a.group0 = sp.groups[0];
   a.chblocks = sp.d_blocks;
   a.mkeys = c.v.mkeys;
   return a;

@@ -41,6 +41,7 @@ struct ProdArgs {
 struct SumArgs {
   int32_t B, B_pad, B_padK, btiles, ngroups;
   const GroupRec* groups;
+  GroupRec group0;          // a copy of the layer's only group when ngroups == 1 (no table read)
   const int32_t* chblocks;
   const float* vals;
   const float* flows;
