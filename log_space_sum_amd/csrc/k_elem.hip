@@ -900,6 +900,10 @@ __global__ __launch_bounds__(256) void k_em(EmArgs a, int total_rows) {
   const int64_t off = sg.offset + (int64_t)(row - sg.row_start) * sg.rlen;
   const bool vec = ((off | (int64_t)sg.rlen) & 3) == 0;   // 16-byte rows
   const bool corr = a.zflows != nullptr && sg.lowrank != 0;
+  // the old weights enter only through the step's (1 - step) share and the
+  // conditional M-step's test: a plain step of 1 writes without reading them
+  // (0 stands in for them, which leaves the same bits for finite weights)
+  const bool need_p = corr || a.step != 1.0f;
   auto ratio = [](float f, float w, float p) { return (p > 0.0f && w > 0.0f) ? f / w : 0.0f; };
   auto ratio4 = [&](float4 f, float4 w, float4 p) {
     return make_float4(ratio(f.x, w.x, p.x), ratio(f.y, w.y, p.y), ratio(f.z, w.z, p.z), ratio(f.w, w.w, p.w));
@@ -917,7 +921,7 @@ __global__ __launch_bounds__(256) void k_em(EmArgs a, int total_rows) {
       const int j = lane * 4 + u * 256;
       const bool in = j < sg.rlen;
       fh[u] = in ? *(const float4*)(a.pflows + off + j) : make_float4(0.f, 0.f, 0.f, 0.f);
-      ph[u] = in ? *(const float4*)(a.params + off + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+      ph[u] = (in && need_p) ? *(const float4*)(a.params + off + j) : make_float4(0.f, 0.f, 0.f, 0.f);
       wh[u] = (in && corr) ? *(const float4*)(a.zflows + off + j) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     if (corr)
@@ -958,7 +962,7 @@ __global__ __launch_bounds__(256) void k_em(EmArgs a, int total_rows) {
   } else if (vec) {
     for (int j = lane * 4; j < sg.rlen; j += 256) {
       float4 f = *(const float4*)(a.pflows + off + j);
-      float4 p = *(const float4*)(a.params + off + j);
+      float4 p = need_p ? *(const float4*)(a.params + off + j) : make_float4(0.f, 0.f, 0.f, 0.f);
       if (corr) f = ratio4(f, *(const float4*)(a.zflows + off + j), p);
       p.x = keep * p.x + a.step * ((f.x + add) / tot);
       p.y = keep * p.y + a.step * ((f.y + add) / tot);
@@ -970,7 +974,7 @@ __global__ __launch_bounds__(256) void k_em(EmArgs a, int total_rows) {
     for (int j = lane; j < sg.rlen; j += 64) {
       const float f = corr ? ratio(a.pflows[off + j], a.zflows[off + j], a.params[off + j]) : a.pflows[off + j];
       const float nw = (f + add) / tot;
-      a.params[off + j] = keep * a.params[off + j] + a.step * nw;
+      a.params[off + j] = keep * (need_p ? a.params[off + j] : 0.0f) + a.step * nw;
     }
   }
 }
