@@ -423,8 +423,7 @@ __global__ __launch_bounds__(256) void k_colmax(SumArgs a) {
   const int sbt = (a.B + 64 * V - 1) / (64 * V);
   const int t = blockIdx.x;
   const int st = t % sbt, rs = t / sbt, sub = rs % NSUB, rt = rs / NSUB;
-  const int g = last_le(a.groups, a.ngroups, rt, [](const GroupRec& r) { return r.pk_start; });
-  const GroupRec gr = a.ngroups == 1 ? a.group0 : a.groups[g];
+  const GroupRec gr = a.ngroups == 1 ? a.group0 : a.groups[a.pk_group[rt]];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int b = st * 64 * V + lane * V;
   const int kw = (rt - gr.pk_start) * 64 + sub * 4 * RW;   // the workgroup's first child
@@ -677,8 +676,7 @@ __global__ __launch_bounds__(256) void k_pack(SumArgs a) {
     }
   }
   const int rt = t / a.btiles, bt = t - rt * a.btiles;
-  const int g = KIND == 0 ? last_le(a.groups, a.ngroups, rt, [](const GroupRec& r) { return r.pk_start; })
-                          : last_le(a.groups, a.ngroups, rt, [](const GroupRec& r) { return r.pg_start; });
+  const int g = a.ngroups == 1 ? 0 : KIND == 0 ? a.pk_group[rt] : a.pg_group[rt];
   const GroupRec gr = a.ngroups == 1 ? a.group0 : a.groups[g];
   const int r0 = (rt - (KIND == 0 ? gr.pk_start : gr.pg_start)) * 64, b0 = bt * 64;
   const int nrows = KIND == 0 ? gr.N : gr.M;

@@ -127,6 +127,8 @@ void upload_tables(Handle* h, int device) {
     sp.d_up_idx = upload(sp.up_idx);
     sp.d_up_rest = upload(sp.up_rest);
     sp.d_up_rest_par = upload(sp.up_rest_par);
+    sp.d_pk_group = upload(sp.pk_group);
+    sp.d_pg_group = upload(sp.pg_group);
   }
   h->d_blocks = upload(h->blocks);
   h->d_rowsegs = upload(h->rowsegs);
@@ -163,6 +165,8 @@ void free_tables(Handle* h) {
     release(sp.d_up_idx);
     release(sp.d_up_rest);
     release(sp.d_up_rest_par);
+    release(sp.d_pk_group);
+    release(sp.d_pg_group);
   }
   release(h->d_blocks);
   release(h->d_rowsegs);
@@ -365,6 +369,8 @@ SumArgs sum_common(const Call& c, const SumPlan& sp) {
   a.btiles = c.v.B_pad / 64;
   a.ngroups = (int)sp.groups.size();
   a.groups = sp.d_groups;
+  a.pk_group = sp.d_pk_group;
+  a.pg_group = sp.d_pg_group;
   if (sp.groups.size() == 1) a.group0 = sp.groups[0];
   a.chblocks = sp.d_blocks;
   a.mkeys = c.v.mkeys;

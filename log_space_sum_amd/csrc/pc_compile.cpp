@@ -350,6 +350,12 @@ Handle* compile_layout(const pc_circuit_desc* d) {
     sp.ctiles = ct;
     sp.pktiles = pk;
     sp.pgtiles = pg;
+    sp.pk_group.assign(pk, 0);
+    sp.pg_group.assign(pg, 0);
+    for (int32_t q = 0; q < (int32_t)sp.groups.size(); ++q) {   // later groups win ties (empty ranges)
+      for (int32_t t = sp.groups[q].pk_start; t < pk; ++t) sp.pk_group[t] = q;
+      for (int32_t t = sp.groups[q].pg_start; t < pg; ++t) sp.pg_group[t] = q;
+    }
     sp.scratch_rows = srow;
     h->max_ebt_cols = std::max(h->max_ebt_cols, ekoff);
     h->max_gbt_cols = std::max(h->max_gbt_cols, gkoff);

@@ -42,6 +42,8 @@ struct SumArgs {
   int32_t B, B_pad, B_padK, btiles, ngroups;
   const GroupRec* groups;
   GroupRec group0;          // a copy of the layer's only group when ngroups == 1 (no table read)
+  const int32_t* pk_group;  // group of each 64-row child tile (column maxima, exp packing)
+  const int32_t* pg_group;  // group of each 64-row output tile (scaled-flow packing)
   const int32_t* chblocks;
   const float* vals;
   const float* flows;

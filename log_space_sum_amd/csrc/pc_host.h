@@ -113,6 +113,11 @@ struct SumPlan {
   // bwd_prod's distinct children that are not outputs of this layer: child
   // node and its single parent, or the distinct-child index (and -1).
   std::vector<int32_t> up_rest, up_rest_par;
+  // Per 64-row child tile / output tile: its group (the last group whose
+  // pk_start / pg_start is at most the tile), so kernels need no search.
+  std::vector<int32_t> pk_group, pg_group;
+  int32_t* d_pk_group = nullptr;
+  int32_t* d_pg_group = nullptr;
   int32_t* d_up_idx = nullptr;
   int32_t* d_up_rest = nullptr;
   int32_t* d_up_rest_par = nullptr;
