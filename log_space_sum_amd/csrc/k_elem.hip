@@ -324,6 +324,136 @@ __global__ __launch_bounds__(256) void k_input_bwd_var(InputArgs a) {
   }
 }
 
+// The two input-layer parameter-flow kernels above with the next node's rows
+// loading into registers while the current node is summed, for batches of at
+// most 512 and at most 512 categories (a lane's share: 8 samples, 9 bounds).
+constexpr int kPfB = 8, kPfK = 9;
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void k_input_bwd_pf(InputArgs a) {
+  extern __shared__ float ib_sm[];
+  constexpr int J = 512 / 64;
+  const int B = a.B, K = a.K;
+  const int per = 2 * B + K + 1;              // f[B], idx[B], ptr[K + 1]
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  float* f = ib_sm + w * per;
+  int32_t* idx = (int32_t*)(f + B);
+  int32_t* ptr = idx + B;
+  const int r = blockIdx.x, q0 = a.row_ptr[r], q1 = a.row_ptr[r + 1];
+  float nf[kPfB];
+  int ni[kPfB], np[kPfK];
+  auto fetch = [&](int q) {
+    const int node = a.row_nodes[q];
+    const int v = a.var[node - a.node_start];
+    const float* F = a.flows + (int64_t)node * B;
+    const int32_t* I = a.bidx + (int64_t)v * B;
+    const int32_t* P = a.bptr + (int64_t)v * (a.Kmax + 1);
+#pragma unroll
+    for (int i = 0; i < kPfB; ++i) {
+      const int b = lane + 64 * i;
+      nf[i] = b < B ? F[b] : 0.0f;
+      ni[i] = b < B ? I[b] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < kPfK; ++i) {
+      const int k = lane + 64 * i;
+      np[i] = k <= K ? P[k] : 0;
+    }
+  };
+  float acc[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) acc[j] = 0.0f;
+  if (q0 + w < q1) fetch(q0 + w);
+  for (int q = q0 + w; q < q1; q += NW) {
+    // a wave's LDS operations complete in order: the previous node's reads
+    // are done before these writes land, and these writes before the reads below
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < kPfB; ++i) {
+      const int b = lane + 64 * i;
+      if (b < B) {
+        f[b] = nf[i];
+        idx[b] = ni[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kPfK; ++i) {
+      const int k = lane + 64 * i;
+      if (k <= K) ptr[k] = np[i];
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (q + NW < q1) fetch(q + NW);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int k = j * 64 + lane;
+      if (k < K) {
+        float t = 0.0f;
+        for (int e = ptr[k]; e < ptr[k + 1]; ++e) t += f[idx[e]];
+        acc[j] += t;
+      }
+    }
+  }
+  float* out = a.pflows + a.param_offset + (int64_t)r * K;
+  __syncthreads();                            // every wave done with its region
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int k = j * 64 + lane;
+    if (k < K) f[k] = acc[j];                 // K <= per: the partial fits the region
+  }
+  __syncthreads();
+  for (int k = tid; k < K; k += 64 * NW) {
+    float t = 0.0f;
+#pragma unroll
+    for (int u = 0; u < NW; ++u) t += ib_sm[u * per + k];
+    out[k] += t;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_input_bwd_var_pf(InputArgs a) {
+  extern __shared__ float ib_sm[];
+  const int B = a.B, K = a.K;
+  int32_t* idx = (int32_t*)ib_sm;             // [B]
+  int32_t* ptr = idx + B;                     // [K + 1]
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float* f = ib_sm + B + K + 1 + w * B;       // [B] per wave
+  const int nchunk = (a.max_var_nodes + kVarChunk - 1) / kVarChunk;
+  const int v = blockIdx.x / nchunk, c = blockIdx.x - v * nchunk;
+  const int q0 = a.var_ptr[v] + c * kVarChunk, q1 = min(a.var_ptr[v + 1], q0 + kVarChunk);
+  if (q0 >= q1) return;
+  const int32_t* I = a.bidx + (int64_t)v * B;
+  const int32_t* P = a.bptr + (int64_t)v * (a.Kmax + 1);
+  float nf[kPfB];
+  auto fetch = [&](int q) {
+    const float* F = a.flows + (int64_t)(a.node_start + a.var_nodes[q]) * B;
+#pragma unroll
+    for (int i = 0; i < kPfB; ++i) {
+      const int b = lane + 64 * i;
+      nf[i] = b < B ? F[b] : 0.0f;
+    }
+  };
+  if (q0 + w < q1) fetch(q0 + w);
+  for (int b = threadIdx.x; b < B; b += blockDim.x) idx[b] = I[b];
+  for (int k = threadIdx.x; k <= K; k += blockDim.x) ptr[k] = P[k];
+  __syncthreads();
+  for (int q = q0 + w; q < q1; q += 4) {
+    const int u = a.var_nodes[q];
+    // a wave's LDS operations complete in order
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < kPfB; ++i) {
+      const int b = lane + 64 * i;
+      if (b < B) f[b] = nf[i];
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (q + 4 < q1) fetch(q + 4);
+    float* out = a.pflows + a.param_offset + (int64_t)a.row[u] * K;
+    for (int k = lane; k < K; k += 64) {
+      float t = 0.0f;
+      for (int e = ptr[k]; e < ptr[k + 1]; ++e) t += f[idx[e]];
+      out[k] += t;
+    }
+  }
+}
+
 // The same sums for rows whose regions do not fit: the row's nodes one at a
 // time, the flow row staged in LDS, buckets read from global memory.
 __global__ void k_input_bwd_wide(InputArgs a) {
@@ -1026,11 +1156,17 @@ void launch_input_bwd(const InputArgs& a, hipStream_t s) {
   if (a.K <= 1024 && per * 4 <= 64 * 1024) {
     // rows of several nodes: the row's nodes over 4 waves; else one row per wave
     if (a.max_row_nodes >= 2) {
-      hipLaunchKernelGGL(k_input_bwd<4>, dim3(a.num_rows), dim3(256), per * 4, s, a);
+      if (a.B <= 64 * kPfB && a.K <= 512)
+        hipLaunchKernelGGL(k_input_bwd_pf<4>, dim3(a.num_rows), dim3(256), per * 4, s, a);
+      else
+        hipLaunchKernelGGL(k_input_bwd<4>, dim3(a.num_rows), dim3(256), per * 4, s, a);
     } else {
       const size_t sh = (size_t)(5 * a.B + a.K + 1) * sizeof(float);
       const int nchunk = (a.max_var_nodes + kVarChunk - 1) / kVarChunk;
-      hipLaunchKernelGGL(k_input_bwd_var, dim3(a.num_vars * nchunk), dim3(256), sh, s, a);
+      if (a.B <= 64 * kPfB)
+        hipLaunchKernelGGL(k_input_bwd_var_pf, dim3(a.num_vars * nchunk), dim3(256), sh, s, a);
+      else
+        hipLaunchKernelGGL(k_input_bwd_var, dim3(a.num_vars * nchunk), dim3(256), sh, s, a);
     }
   } else {
     hipLaunchKernelGGL(k_input_bwd_wide, dim3(a.num_rows), dim3(256), (size_t)a.B * sizeof(float), s, a);
