@@ -1213,7 +1213,8 @@ void launch_g_pack(const SumArgs& a, int row_tiles, hipStream_t s) {
   }
   SumArgs b = a;
   b.fp_tiles = row_tiles * a.btiles;
-  const int rest = b.fp_nrest > 0 ? grid_for((int64_t)b.fp_nrest * ((a.B + 3) / 4), 256, 1024) : 0;
+  // up to 16 workgroups per CU for the other children (2 items per lane per pass)
+  const int rest = b.fp_nrest > 0 ? grid_for((int64_t)b.fp_nrest * ((a.B + 3) / 4), 256, 4096) : 0;
   hipLaunchKernelGGL((k_pack<1, true>), dim3(b.fp_tiles + rest), dim3(256), 0, s, b);
 }
 void launch_theta_pack(const ThetaArgs& a, int tiles, hipStream_t s) {
