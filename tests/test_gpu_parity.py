@@ -87,6 +87,37 @@ def test_hmm_medium(mode):
     G.check_flows(gpu2["em"], newp_or, mode, "hmm EM parameters")
 
 
+@pytest.mark.parametrize("step,pseudo", [(1.0, 0.0), (0.6, 0.0), (1.0, 0.2)])
+def test_em_rows_without_flow(step, pseudo):
+    """EM on parameter flows whose every other row is zero: without a
+    pseudocount such rows keep their weights (also under a plain step of 1,
+    which writes the other rows without reading the old weights); with one
+    they move toward the uniform row."""
+    import torch
+    import log_space_sum_amd as L
+    cfg = make_config("hmm4096", H=96, T=3, V=40, B=16)
+    circ = cfg["circuit"]
+    G.say(f"case EM rows without flow: step={step} pseudocount={pseudo}")
+    h = L.pc_compile_layout(circ, device=0)
+    rng = np.random.default_rng(5)
+    F = rng.uniform(0.0, 2.0, size=circ.num_params)
+    for off, nrows, rlen in circ.param_row_segments():
+        F[off:off + nrows * rlen].reshape(nrows, rlen)[::2] = 0.0
+    F = F.astype(np.float32)
+    params = torch.tensor(cfg["params"], device="cuda")
+    pflows = torch.tensor(F, device="cuda")
+    L.pc_em_step(h, params, pflows, step, pseudo, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    ref = __import__("oracle").em_step(circ, cfg["params"], F.astype(np.float64),
+                                       step_size=step, pseudocount=pseudo)
+    G.check_flows(params.cpu().numpy(), ref, "fp32", "EM with rows without flow")
+    if pseudo == 0.0:
+        kept = np.zeros(circ.num_params, dtype=bool)
+        for off, nrows, rlen in circ.param_row_segments():
+            kept[off:off + nrows * rlen].reshape(nrows, rlen)[::2] = True
+        np.testing.assert_array_equal(params.cpu().numpy()[kept], cfg["params"][kept])
+
+
 @pytest.mark.parametrize("mode", MODES)
 def test_em_pseudocount(mode):
     cfg = make_config("hmm4096", H=64, T=5, V=20, B=32)
