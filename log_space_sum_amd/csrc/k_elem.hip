@@ -796,7 +796,7 @@ __device__ __forceinline__ void prod_bwd_rest(const SumArgs& a, int wg, int nwg)
 // unless the layer stores), stores the flow and packs f / S; workgroups past
 // the packing tiles push the flows of the product layer's other children.
 template <int KIND, bool PROD>
-__global__ __launch_bounds__(256) void k_pack(SumArgs a) {
+__global__ __launch_bounds__(512) void k_pack(SumArgs a) {
   __shared__ float tile[64][65];
   const int t = blockIdx.x;
   if constexpr (PROD) {
@@ -811,16 +811,18 @@ __global__ __launch_bounds__(256) void k_pack(SumArgs a) {
   const int r0 = (rt - (KIND == 0 ? gr.pk_start : gr.pg_start)) * 64, b0 = bt * 64;
   const int nrows = KIND == 0 ? gr.N : gr.M;
   const int tid = threadIdx.x;
-  // phase 1: item = (row, 8-sample chunk), 512 items, two per thread: every
-  // load of both items is issued before the first store (the stores could
-  // alias the loads, so the compiler would not hoist the second item's loads)
-  constexpr int U = 2;
+  // phase 1: item = (row, 8-sample chunk), 512 items, one per thread of the
+  // 512-thread workgroup (16 waves per CU at two workgroups; two items per
+  // thread on 256 threads measured slower): every load of the items is
+  // issued before the first store (the stores could alias the loads, so the
+  // compiler would not hoist a later item's loads)
+  constexpr int U = 1;
   int kq[U], bsq[U], upq[U];
   bool okq[U], vq[U];
   float u0[U][8], u1[U][8], uo[U][8];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int it = tid + 256 * u, r = it >> 3, c = it & 7;
+    const int it = tid + 512 * u, r = it >> 3, c = it & 7;
     const int k = r0 + r, bs = b0 + c * 8;
     kq[u] = k;
     bsq[u] = bs;
@@ -852,7 +854,7 @@ __global__ __launch_bounds__(256) void k_pack(SumArgs a) {
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int it = tid + 256 * u, r = it >> 3, c = it & 7;
+    const int it = tid + 512 * u, r = it >> 3, c = it & 7;
     const int k = kq[u], bs = bsq[u];
     float x[8];
 #pragma unroll
@@ -915,7 +917,7 @@ __global__ __launch_bounds__(256) void k_pack(SumArgs a) {
   const int kpad = (nrows + K_PAD - 1) / K_PAD * K_PAD;
   const int tk0 = KIND == 0 ? gr.e_koff : gr.g_koff;
   if (r0 >= kpad) return;
-  for (int it = tid; it < 512; it += 256) {
+  for (int it = tid; it < 512; it += 512) {
     const int bl = (it >> 2) & 63, c = (it >> 8) * 4 + (it & 3);
     const int bb = b0 + bl;
     if (bb >= a.B_pad) continue;
@@ -1201,21 +1203,21 @@ void launch_colmax(const SumArgs& a, int row_tiles, hipStream_t s) {
   else launch_colmax_v<false>(a, row_tiles, s);
 }
 void launch_exp_pack(const SumArgs& a, int row_tiles, hipStream_t s) {
-  if (row_tiles > 0) hipLaunchKernelGGL((k_pack<0, false>), dim3(row_tiles * a.btiles), dim3(256), 0, s, a);
+  if (row_tiles > 0) hipLaunchKernelGGL((k_pack<0, false>), dim3(row_tiles * a.btiles), dim3(512), 0, s, a);
 }
 // Scaled flows; with a.fp_on also the following product layer's backward, its
 // other children on up to 1024 extra workgroups.
 void launch_g_pack(const SumArgs& a, int row_tiles, hipStream_t s) {
   if (row_tiles <= 0) return;
   if (!a.fp_on) {
-    hipLaunchKernelGGL((k_pack<1, false>), dim3(row_tiles * a.btiles), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_pack<1, false>), dim3(row_tiles * a.btiles), dim3(512), 0, s, a);
     return;
   }
   SumArgs b = a;
   b.fp_tiles = row_tiles * a.btiles;
   // up to 16 workgroups per CU for the other children (2 items per lane per pass)
   const int rest = b.fp_nrest > 0 ? grid_for((int64_t)b.fp_nrest * ((a.B + 3) / 4), 256, 4096) : 0;
-  hipLaunchKernelGGL((k_pack<1, true>), dim3(b.fp_tiles + rest), dim3(256), 0, s, b);
+  hipLaunchKernelGGL((k_pack<1, true>), dim3(b.fp_tiles + rest), dim3(512), 0, s, b);
 }
 void launch_theta_pack(const ThetaArgs& a, int tiles, hipStream_t s) {
   if (tiles > 0) hipLaunchKernelGGL(k_theta_pack, dim3(tiles), dim3(256), 0, s, a);
