@@ -234,6 +234,9 @@ def main():
                     help="tied copies per parameter-flow launch on a second stream (-1: automatic, 0: one launch at the end)")
     ap.add_argument("--lr-pack", type=int, default=0, choices=[0, 1],
                     help="LowRank factor records: 0 made once per forward, 1 per layer and pass")
+    ap.add_argument("--splits", default="",
+                    help="operand splits of the current mode, e.g. 'fwd=2,2;elem=2,1' (product kind = planes of "
+                         "the first, second operand; default: the library's)")
     ap.add_argument("--fuse", type=int, default=1, choices=[0, 1],
                     help="1: product layers inside the adjacent sum layers' memory-bound kernels; 0: own launches")
     ap.add_argument("--copy-calibration", type=int, default=0,
@@ -266,7 +269,8 @@ def main():
     bsz = {} if args.batch is None else {"B": args.batch}
     if args.workload == "hmm4096":
         cfg = make_config("hmm4096", H=args.H, T=args.T, **bsz)
-        metric = "sum-layer fwd+bwd ms & TFLOP/s (frac of MFMA peak), HMM 4096 lat×32 pos, batch 512"
+        metric = (f"sum-layer fwd+bwd ms & TFLOP/s (frac of MFMA peak), HMM {args.H} lat×{args.T} pos, "
+                  f"batch {cfg['B']}")
         workload = f"hmm{args.H}x{args.T} symbols 512 batch {cfg['B']} fwd+bwd+em"
         context = "pages (RTX PRO 6000, whole circuit, auto): 32.1 ms fwd+bwd at batch 512"
     elif args.workload == "hclt":
@@ -298,6 +302,10 @@ def bench_circuit(args, cfg, metric, workload, context):
     L.pc_set_option(h, "split_max", args.split_max)
     L.pc_set_option(h, "fuse", args.fuse)
     L.pc_set_option(h, "param_chunk", args.param_chunk)
+    for item in filter(None, args.splits.split(";")):
+        kind, planes = item.split("=")
+        pa, pb = (int(x) for x in planes.split(","))
+        L.pc_set_split(h, args.mode, kind.strip(), pa, pb)
     params = torch.tensor(cfg["params"], device=dev)
     tokens = torch.tensor(cfg["tokens"], device=dev) if cfg.get("tokens") is not None else None
     vals = torch.empty((circ.num_nodes, B), device=dev)
@@ -372,7 +380,8 @@ def bench_circuit(args, cfg, metric, workload, context):
         "vs_baseline": None,
         "dtype": "bf16" if args.mode == "auto" else "bf16x3-split",
         "data": "synthetic",
-        "config": {"workload": workload, "precision_mode": args.mode, "global_batch": B, "hip_graph": bool(args.graph)},
+        "config": {"workload": workload, "precision_mode": args.mode, "global_batch": B, "hip_graph": bool(args.graph),
+                   **({"splits": args.splits} if args.splits else {})},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "sum_layer_kernels_ms": round(sum_ms, 4),
         "sum_layer_kernels_tflops": round(flops / (sum_ms * 1e-3) / 1e12, 3) if sum_ms > 0 else None,

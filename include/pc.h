@@ -206,12 +206,14 @@ int pc_get_precision(pc_handle h, int* mode);
  * operand; the products of planes whose order is below the larger count are
  * accumulated: (1,1) one bf16 product; (2,1) or (1,2) one operand split,
  * two products; (2,2) hi/lo split, three products; (3,3) hi/mid/lo split,
- * six products.  Defaults: auto (2,1) for all three (forward and element
- * flows split the weights, parameter flows split the scaled flows g), so that
- * every value or flow dominated by one product carries a single bf16
- * rounding (at most 2^-8 relative) and the weights, whose rounding would be
- * the same for every sample, are never rounded alone; fp32-level (3,3)
- * everywhere.  Errors: PC_ERR_INVALID_ARG for other counts or kinds. */
+ * six products.  Defaults: auto (2,1) for the forward (the weights split, the
+ * exponentiated children rounded), (2,2) for the element flows (both split:
+ * a child's flow dominated by one parent then carries no bf16 rounding of
+ * g = f / S, the rounding that otherwise compounds from layer to layer past
+ * 5e-3 end to end) and (2,1) for the parameter flows (g split, e rounded);
+ * the weights, whose rounding would be the same for every sample, are never
+ * rounded alone; fp32-level (3,3) everywhere.  Errors: PC_ERR_INVALID_ARG for
+ * other counts or kinds. */
 int pc_set_split(pc_handle h, int mode, int gemm_kind, int planes_a, int planes_b);
 
 /* Product-kernel tuning (advanced; results change only by float32 summation

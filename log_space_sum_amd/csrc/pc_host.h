@@ -137,7 +137,8 @@ struct Handle {
   int device = -1;
   int mode = PC_PREC_AUTO;
   // planes[mode][gemm kind][0: first operand, 1: second operand]
-  int planes[2][3][2] = {{{2, 1}, {2, 1}, {2, 1}}, {{3, 3}, {3, 3}, {3, 3}}};
+  // auto: forward (2,1), element flows (2,2), parameter flows (2,1); fp32-level (3,3)
+  int planes[2][3][2] = {{{2, 1}, {2, 2}, {2, 1}}, {{3, 3}, {3, 3}, {3, 3}}};
   int opt_layer_tile = 0, opt_param_tile = 0, opt_split_max = 8, opt_fuse = 1;   // pc_set_option
   int opt_param_chunk = -1;            // tied copies per parameter-flow launch (0: one launch at the end, -1: automatic)
   int opt_lr_pack = 0;                 // LowRank fragment records: 0 once per forward, 1 per layer and pass

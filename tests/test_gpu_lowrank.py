@@ -24,16 +24,17 @@ def _gpu():
 def _lowrank_full(cfg, mode, what):
     """Values and log-likelihood end to end; values, element flows, parameter
     flows, dLL/dA and dLL/dB per layer (recomputed by the oracle from each
-    layer's GPU inputs); flows end to end at the tolerance times the depth."""
+    layer's GPU inputs); flows end to end at gpu_util.e2e_flow_tol (the stated
+    tolerance in auto mode; plus the float32-storage term at fp32 level)."""
     G.say(f"case {what} mode={mode} B={cfg['B']}")
     gpu = G.run_gpu(cfg, mode)
     orc = G.run_oracle(cfg)
     G.check_values(gpu["vals"], orc["vals"], mode, f"{what} node values")
     G.check_values(gpu["ll"], orc["ll"], mode, f"{what} log-likelihood")
     loc = G.check_local(cfg, gpu, mode, what)
-    depth = G.num_sum_layers(cfg["circuit"])
-    G.check_flows(gpu["flows"], orc["flows"], mode, f"{what} element flows end to end", scale=depth)
-    G.check_flows(gpu["pflows"], orc["pflows"], mode, f"{what} parameter flows end to end", scale=depth)
+    tol = G.e2e_flow_tol(cfg["circuit"], orc["vals"], mode)
+    G.check_flows(gpu["flows"], orc["flows"], mode, f"{what} element flows end to end", rtol=tol)
+    G.check_flows(gpu["pflows"], orc["pflows"], mode, f"{what} parameter flows end to end", rtol=tol)
     for s in range(len(gpu["dA"])):
         G.check_grads(gpu["dA"][s], loc["dA"][s], mode, f"{what} slot {s} dLL/dA per layer")
         G.check_grads(gpu["dB"][s], loc["dB"][s], mode, f"{what} slot {s} dLL/dB per layer")
@@ -63,7 +64,7 @@ def test_lowrank_z_correction(mode, H, T, V, rank, B, spread):
     """The denominator statistic W of the conditional M-step
     (pyjuice.parameterizations.LowRank, Training, apply_z_correction): added
     by pc_backward to what the buffer held, only on the LowRank weights, and
-    equal to the oracle's end to end (flow tolerance times the depth); then
+    equal to the oracle's end to end (gpu_util.e2e_flow_tol); then
     pc_em_step_corrected against the oracle's conditional M-step on the GPU's
     own F+ and W, every other row the plain step (fp32-level tolerance)."""
     import oracle
@@ -79,9 +80,8 @@ def test_lowrank_z_correction(mode, H, T, V, rank, B, spread):
         inside[off:off + n] = True
     assert inside.any()
     assert np.array_equal(gpu["z_flows"][~inside], z0[~inside]), "W touched outside the LowRank blocks"
-    depth = G.num_sum_layers(circ)
     G.check_flows(gpu["z_flows"][inside].astype(np.float64) - 0.25, orc["z_flows"][inside], mode,
-                  f"{what} W end to end", scale=depth)
+                  f"{what} W end to end", rtol=G.e2e_flow_tol(circ, orc["vals"], mode))
     ref = oracle.em_step_corrected(circ, cfg["params"], gpu["pflows"].astype(np.float64),
                                    gpu["z_flows"].astype(np.float64), step_size=0.7, pseudocount=0.1)
     G.check_flows(gpu["em_corrected"], ref, "fp32", f"{what} conditional M-step")
@@ -114,7 +114,7 @@ def test_lowrank_sum_exp_z_correction():
     for off, n in oracle.lowrank_param_ranges(circ):
         inside[off:off + n] = True
     G.check_flows(gpu["z_flows"][inside], orc["z_flows"][inside], "auto", f"{what} W end to end",
-                  scale=G.num_sum_layers(circ))
+                  rtol=G.e2e_flow_tol(circ, orc["vals"], "auto"))
     ref = oracle.em_step_corrected(circ, cfg["params"], gpu["pflows"].astype(np.float64),
                                    gpu["z_flows"].astype(np.float64))
     G.check_flows(gpu["em_corrected"], ref, "fp32", f"{what} conditional M-step")
@@ -140,20 +140,69 @@ def test_lowrank_requires_factors():
         L.pc_forward(h, B, tokens, params, vals, None, None, ws)
 
 
-def test_lowrank_full_size_sampled():
+def _fplus_rows_local(cfg, gpu, rows, mode):
+    """F+ of the tied transition's rows `rows`, summed over every copy and
+    sample, from the oracle's backward step of each LowRank layer on the
+    GPU's inputs to that step (children values, the layer's values -- the
+    GPU's own in auto mode -- and its output flows), restricted to those rows:
+    a row's values and edge flows depend on that row alone."""
+    from workloads import circuits as W
+    import oracle
+    circ = cfg["circuit"]
+    H = circ.meta["H"]
+    rows = np.asarray(rows)
+    th = cfg["params"][circ.meta["off_trans"]:circ.meta["off_trans"] + H * H].reshape(H, H)
+    ps = np.ascontiguousarray(th[rows]).reshape(-1).astype(np.float64)
+    V, F = gpu["vals"], gpu["flows"]
+    B = V.shape[1]
+    ext, groups, seeds, outv, factors = [], [], [], [], []
+    n_ext = 0
+    lr_groups = [g for ly in circ.layers if type(ly).__name__ == "Sum" for g in ly.groups if g.lowrank >= 0]
+    n_out0 = len(lr_groups) * H
+    for k, g in enumerate(lr_groups):
+        ext.append(V[g.child_ids()])
+        groups.append(W.SumGroup(n_out0 + k * len(rows), len(rows), np.array([k * H], np.int32), H, 0, k))
+        seeds.append(F[g.out_start + rows])
+        outv.append(V[g.out_start + rows])
+        A, Bf = cfg["lowrank"][g.lowrank]
+        factors.append((np.ascontiguousarray(A[:, rows, :]), Bf))
+        n_ext += H
+    sub = W.Circuit("rows", n_out0 + len(lr_groups) * len(rows), 0, ps.size,
+                    [W.InputExternal(0, n_ext), W.Sum(groups)], root=-1,
+                    lowrank_rank=circ.lowrank_rank, lowrank_form=circ.lowrank_form)
+    Vs, _ = oracle.forward(sub, ps, B, external=np.concatenate(ext).astype(np.float64), lowrank=factors)
+    if mode == "auto":
+        Vs[n_out0:] = np.concatenate(outv)
+    r = oracle.backward(sub, ps, Vs, seed_flows=np.concatenate(seeds).astype(np.float64), lowrank=factors)
+    return r["param_flows"].reshape(len(rows), H)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("mode", ["auto", "fp32"])
+def test_lowrank_full_size_sampled(mode):
     """The LowRank workload at its full size (HMM 1024 states, 64 positions,
     rank 16, batch 64): values, log-likelihood, element flows and dA, dB of
-    every slot on 3 samples against the oracle (samples are independent)."""
+    sampled slots on 3 samples against the oracle end to end (samples are
+    independent); F+ (the transition's parameter flows) of sampled rows over
+    every copy and all 64 samples against the oracle's per-layer step."""
     cfg = make_config("lowrank")
-    mode = "auto"
+    circ = cfg["circuit"]
     G.say(f"case lowrank full size mode={mode} B={cfg['B']}")
     gpu = G.run_gpu(cfg, mode)
     samples = np.array([0, 31, 63])
     orc = G.run_oracle(cfg, samples=samples)
     G.check_values(gpu["vals"][:, samples], orc["vals"], mode, "full-size node values (sampled)")
     G.check_values(gpu["ll"][samples], orc["ll"], mode, "full-size log-likelihood (sampled)")
-    depth = G.num_sum_layers(cfg["circuit"])
-    G.check_flows(gpu["flows"][:, samples], orc["flows"], mode, "full-size element flows (sampled, e2e)", scale=depth)
+    tol = G.e2e_flow_tol(circ, orc["vals"], mode)
+    G.check_flows(gpu["flows"][:, samples], orc["flows"], mode, "full-size element flows (sampled, e2e)", rtol=tol)
     for s in (0, 31, 62):
-        G.check_grads(gpu["dA"][s][samples], orc["dA"][s], mode, f"full-size slot {s} dLL/dA (sampled, e2e)")
-        G.check_grads(gpu["dB"][s][samples], orc["dB"][s], mode, f"full-size slot {s} dLL/dB (sampled, e2e)")
+        G.check_grads(gpu["dA"][s][samples], orc["dA"][s], mode, f"full-size slot {s} dLL/dA (sampled, e2e)",
+                      e2e_tol=tol)
+        G.check_grads(gpu["dB"][s][samples], orc["dB"][s], mode, f"full-size slot {s} dLL/dB (sampled, e2e)",
+                      e2e_tol=tol)
+    H = circ.meta["H"]
+    rows = [0, 517, H - 1]
+    ref = _fplus_rows_local(cfg, gpu, rows, mode)
+    off = circ.meta["off_trans"]
+    got = gpu["pflows"][off:off + H * H].reshape(H, H)[rows]
+    G.check_flows(got, ref, mode, "full-size F+ rows (all copies and samples, per layer)")
