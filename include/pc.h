@@ -275,6 +275,27 @@ int pc_forward(pc_handle h, int batch, const int32_t* tokens, const float* param
                float* node_vals, float* ll, const pc_lowrank_io* lowrank,
                void* ws, size_t ws_bytes, void* stream);
 
+/* Forward pass that allocates nothing and takes no workspace, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same arguments and results
+ * as pc_forward (node values and log-likelihoods; LowRank factors read),
+ * minus the workspace: the scratch is a static device array of
+ * PC_STATIC_SCRATCH_BYTES that each device the library runs on holds until
+ * the process ends.  Forward only: nothing is kept for pc_backward (the
+ * transposed weights, the operands of the parameter flows and the scaled sums
+ * are not written), so a pc_backward needs its own pc_forward.
+ * Every call on one device shares that device's array (and leaves its content
+ * behind; the call clears what must start at zero), so calls that overlap in
+ * time on one device -- other streams, other threads, other handles -- race
+ * and give wrong results.  No timing events are recorded.
+ * Errors: PC_ERR_WORKSPACE when the forward of `batch` samples needs more than
+ * PC_STATIC_SCRATCH_BYTES of scratch (the message gives the size; use
+ * pc_forward with a workspace); PC_ERR_HIP when the array's device address
+ * could not be resolved; otherwise as pc_forward. */
+#define PC_STATIC_SCRATCH_BYTES (128u * 1024u * 1024u)
+int pc_forward_static(pc_handle h, int batch, const int32_t* tokens, const float* params,
+                      float* node_vals, float* ll, const pc_lowrank_io* lowrank, void* stream);
+
 /* Backward pass (element flows and parameter flows; PyJuice pull request #62,
  * Summary item 3) after pc_forward on the same batch, tokens, params, node_vals,
  * workspace and precision mode.

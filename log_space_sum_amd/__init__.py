@@ -73,6 +73,8 @@ EXPORTS = {
     "pc_workspace_bytes": (C.c_int, [C.c_void_p, C.c_int, C.POINTER(C.c_size_t)]),
     "pc_forward": (C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                              C.POINTER(pc_lowrank_io), C.c_void_p, C.c_size_t, C.c_void_p]),
+    "pc_forward_static": (C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                    C.POINTER(pc_lowrank_io), C.c_void_p]),
     "pc_backward": (C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                               C.c_void_p, C.c_int, C.POINTER(pc_lowrank_io), C.c_void_p, C.c_size_t,
                               C.c_void_p]),
@@ -323,6 +325,18 @@ def pc_forward(h: Handle, batch: int, tokens, params, node_vals, ll=None, lowran
         _ptr(ll, torch.float32, batch, "ll"), C.byref(io) if io is not None else None,
         _ptr(ws, torch.uint8, need, "ws"), C.c_size_t(ws.numel() if ws is not None else 0),
         _stream(stream)))
+
+
+def pc_forward_static(h: Handle, batch: int, tokens, params, node_vals, ll=None, lowrank=None, stream=None):
+    """pc_forward without a workspace: the library's static device scratch
+    (forward only; calls overlapping on one device race)."""
+    torch = _torch()
+    io, keep = _lowrank_io(lowrank)
+    _check(lib().pc_forward_static(
+        h.ptr, int(batch), _ptr(tokens, torch.int32, batch * h.num_vars, "tokens"),
+        _ptr(params, torch.float32, h.num_params, "params"),
+        _ptr(node_vals, torch.float32, h.num_nodes * batch, "node_vals"),
+        _ptr(ll, torch.float32, batch, "ll"), C.byref(io) if io is not None else None, _stream(stream)))
 
 
 def pc_backward(h: Handle, batch: int, tokens, params, node_vals, node_flows, param_flows, flags=0,

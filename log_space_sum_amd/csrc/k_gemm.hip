@@ -712,13 +712,13 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
                 : EPI == EPI_ELEM ? dst_base + at[c] : a.pflows + bl.param_offset + at[c];
       if (vec && col + 3 < ncol) {
         *(float4*)d0 = make_float4(o[0], o[1], o[2], o[3]);
-        if (EPI == EPI_FWD) *(float4*)(a.ssum + gr.s_row * B + at[c]) = make_float4(o2[0], o2[1], o2[2], o2[3]);
+        if (EPI == EPI_FWD && a.ssum) *(float4*)(a.ssum + gr.s_row * B + at[c]) = make_float4(o2[0], o2[1], o2[2], o2[3]);
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           if (col + e < ncol) {
             d0[e] = o[e];
-            if (EPI == EPI_FWD) a.ssum[gr.s_row * B + at[c] + e] = o2[e];
+            if (EPI == EPI_FWD && a.ssum) a.ssum[gr.s_row * B + at[c] + e] = o2[e];
           }
       }
       if (EPI == EPI_ELEM && gp) {

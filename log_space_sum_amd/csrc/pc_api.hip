@@ -8,6 +8,7 @@
 
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -70,7 +71,7 @@ struct Timed {
   hipStream_t s;
   size_t slot = 0;
   Timed(Handle* h_, int kind, hipStream_t s_) : h(h_), s(s_) {
-    if (!h->timing) return;
+    if (!h->timing || h->no_events) return;
     if (h->events_used == h->events.size()) {
       Handle::Ev ev{kind, nullptr, nullptr};
       HIPCHECK(hipEventCreate((hipEvent_t*)&ev.start));
@@ -82,7 +83,7 @@ struct Timed {
     HIPCHECK(hipEventRecord((hipEvent_t)h->events[slot].start, s));
   }
   ~Timed() {
-    if (h->timing) (void)hipEventRecord((hipEvent_t)h->events[slot].stop, s);
+    if (h->timing && !h->no_events) (void)hipEventRecord((hipEvent_t)h->events[slot].stop, s);
   }
 };
 
@@ -201,9 +202,10 @@ GemmShape param_gemm_shape(const Handle* h, int pa, int pb) {
   return g;
 }
 
-WsPlan plan_workspace(const Handle* h, int B) {
+WsPlan plan_workspace(const Handle* h, int B, bool fwd_only) {
   WsPlan p{};
   p.B = B;
+  p.fwd_only = fwd_only;
   p.B_pad = (int)round_up(B, ROW_PAD);
   p.B_padK = (int)round_up(B, K_PAD);
   p.mode = effective_mode(h, B);
@@ -216,21 +218,25 @@ WsPlan plan_workspace(const Handle* h, int B) {
     return o;
   };
   const size_t Bp = p.B_pad, BpK = p.B_padK, Bs = B;
+  // regions only the backward reads (the transposed weights, the operands
+  // kept for the parameter flows, the scaled sums, the element-flow scratch,
+  // the input-flow buckets) are left out of a forward-only plan
+  const size_t bw = fwd_only ? 0 : 1;
   p.theta = take((size_t)p.pl[GK_FWD][0] * h->theta_elems * 2);
-  p.thetaT = take((size_t)p.pl[GK_ELEM][0] * h->thetaT_elems * 2);
+  p.thetaT = take(bw * p.pl[GK_ELEM][0] * h->thetaT_elems * 2);
   p.ebt = take((size_t)p.pl[GK_FWD][1] * Bp * h->max_ebt_cols * 2);
-  p.gbt = take((size_t)p.pl[GK_ELEM][1] * Bp * h->max_gbt_cols * 2);
-  p.gbt2 = take(h->gbt_slots > 1 && B % 256 == 0 ?   // independent of the fusion option
-                  (size_t)p.pl[GK_ELEM][1] * Bp * h->max_gbt_cols * 2 : 0);
-  p.earena = take((size_t)p.pl[GK_PARAM][1] * h->earena_rows * BpK * 2);
-  p.garena = take((size_t)p.pl[GK_PARAM][0] * h->garena_rows * BpK * 2);
+  p.gbt = take(bw * p.pl[GK_ELEM][1] * Bp * h->max_gbt_cols * 2);
+  p.gbt2 = take(bw * (h->gbt_slots > 1 && B % 256 == 0 ?   // independent of the fusion option
+                        (size_t)p.pl[GK_ELEM][1] * Bp * h->max_gbt_cols * 2 : 0));
+  p.earena = take(bw * p.pl[GK_PARAM][1] * h->earena_rows * BpK * 2);
+  p.garena = take(bw * p.pl[GK_PARAM][0] * h->garena_rows * BpK * 2);
   p.mkeys = take((size_t)h->m_rows * Bs * 4);
-  p.ssum = take((size_t)h->s_rows * Bs * 4);
-  p.scratch = take((size_t)h->max_scratch_rows * Bs * 4);
+  p.ssum = take(bw * h->s_rows * Bs * 4);
+  p.scratch = take(bw * h->max_scratch_rows * Bs * 4);
   const bool inp = !h->inputs.empty();
   p.tokT = take(inp ? (size_t)h->num_vars * Bs * 4 : 0);
-  p.bptr = take(inp ? (size_t)h->num_vars * (h->max_cats + 1) * 4 : 0);
-  p.bidx = take(inp ? (size_t)h->num_vars * Bs * 4 : 0);
+  p.bptr = take(inp ? bw * h->num_vars * (h->max_cats + 1) * 4 : 0);
+  p.bidx = take(inp ? bw * h->num_vars * Bs * 4 : 0);
   // split-K partial tiles and arrival counters (forward / element flows)
   {
     int64_t pel = 0;
@@ -258,10 +264,10 @@ WsPlan plan_workspace(const Handle* h, int B) {
   p.lrS = take(lr ? (size_t)h->lr_rows * Bs * 4 : 0);
   p.lrU = take(lr ? (size_t)h->lr_rows * Bs * kr * 4 : 0);
   p.lrW = take(lr ? (size_t)h->lr_rows * Bs * kr * 4 : 0);
-  p.lrC1 = take(lr ? (size_t)round_up(h->lr_max_m, 32) * Bs * 4 : 0);   // rows padded to 32 (zeros)
-  p.lrC2 = take(lr ? (size_t)round_up(h->lr_max_m, 32) * Bs * 4 : 0);
-  p.lrP = take(lr ? (size_t)p.lr_nsg * h->lr_p_elems * 4 : 0);
-  p.lrPz = take(lr ? (size_t)p.lr_nsg * h->lr_p_elems * 4 : 0);
+  p.lrC1 = take(lr ? bw * round_up(h->lr_max_m, 32) * Bs * 4 : 0);   // rows padded to 32 (zeros)
+  p.lrC2 = take(lr ? bw * round_up(h->lr_max_m, 32) * Bs * 4 : 0);
+  p.lrP = take(lr ? bw * p.lr_nsg * h->lr_p_elems * 4 : 0);
+  p.lrPz = take(lr ? bw * p.lr_nsg * h->lr_p_elems * 4 : 0);
   {
     size_t pk = 0;
     for (const auto& sp : h->sums)
@@ -329,13 +335,13 @@ struct Call {
   void* ws;
 };
 
-Call begin_call(pc_handle hh, int B, void* ws, size_t ws_bytes, void* stream) {
+Call begin_call(pc_handle hh, int B, void* ws, size_t ws_bytes, void* stream, bool fwd_only = false) {
   Handle* h = checked(hh);
   if (h->device < 0) fail(PC_ERR_NO_DEVICE, "handle was compiled without a device");
   if (B < 1) fail(PC_ERR_INVALID_ARG, "batch must be >= 1");
   if (!h->inputs.empty() && (size_t)(h->max_cats + 1 + B) * 4 > 65536)
     fail(PC_ERR_UNSUPPORTED, "categories + batch too large for the input-flow bucketing (limit 16383)");
-  Call c{h, plan_workspace(h, B), {}, (hipStream_t)stream, ws};
+  Call c{h, plan_workspace(h, B, fwd_only), {}, (hipStream_t)stream, ws};
   if (c.p.total > 0 && !ws) fail(PC_ERR_INVALID_ARG, "null workspace");
   if (ws_bytes < c.p.total)
     fail(PC_ERR_WORKSPACE, "workspace too small: need " + std::to_string(c.p.total) + " bytes, got " +
@@ -494,6 +500,214 @@ ProdArgs prod_args(const Call& c, const ProductPlan& pp) {
 
 }  // namespace
 
+namespace {
+
+// Scratch of pc_forward_static, for callers that cannot allocate device
+// memory.  Each device holds its own copy until the process ends.  Host code
+// must not use the array's name as an address: the device address of each
+// device's copy is resolved once per device (with that device current) by
+// hipGetSymbolAddress and kept in g_static.
+__device__ __align__(256) unsigned char scratch[PC_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+struct StaticScratch {
+  std::mutex mu;
+  bool tried[kMaxDevices] = {};
+  hipError_t err[kMaxDevices] = {};
+  void* ptr[kMaxDevices] = {};
+};
+StaticScratch g_static;
+
+// Resolve `scratch` on `device`, which must be current (once per device).
+void resolve_static_scratch(int device) {
+  if (device < 0 || device >= kMaxDevices) return;
+  std::lock_guard<std::mutex> lk(g_static.mu);
+  if (g_static.tried[device]) return;
+  g_static.tried[device] = true;
+  void* ptr = nullptr;
+  g_static.err[device] = hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch));
+  g_static.ptr[device] = g_static.err[device] == hipSuccess ? ptr : nullptr;
+}
+
+void* static_scratch(int device) {
+  if (device < 0 || device >= kMaxDevices) fail(PC_ERR_UNSUPPORTED, "device id too large for the static scratch table");
+  std::lock_guard<std::mutex> lk(g_static.mu);
+  if (!g_static.tried[device]) fail(PC_ERR_HIP, "static scratch was not resolved for this device");
+  if (g_static.err[device] != hipSuccess)
+    fail(PC_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(g_static.err[device]));
+  return g_static.ptr[device];
+}
+
+// Clears Handle::no_events when the call ends (however it ends).
+struct NoEvents {
+  Handle* h;
+  explicit NoEvents(Handle* h_) : h(h_) { h->no_events = true; }
+  ~NoEvents() { h->no_events = false; }
+};
+
+// The forward pass of one call: every launch on c.s, nothing allocated.  A
+// forward-only call (c.p.fwd_only) writes none of what only the backward
+// reads: the transposed weight planes, the kept E planes and the scaled sums.
+void run_forward(const Call& c, const int32_t* tokens, const float* params, float* node_vals, float* ll,
+                 const pc_lowrank_io* lowrank) {
+  Handle* h = c.h;
+  check_lowrank_io(h, lowrank, false);
+  if (!params || !node_vals) fail(PC_ERR_INVALID_ARG, "null params or node_vals");
+  if (!h->inputs.empty() && !tokens) fail(PC_ERR_INVALID_ARG, "null tokens");
+  if (ll && h->root < 0) fail(PC_ERR_INVALID_ARG, "ll requested but the circuit has no root");
+  DeviceGuard dg(h->device);
+  const int B = c.v.B;
+  const WsPlan& p = c.p;
+  const WsView& v = c.v;
+  if (h->has_plain_sums) {
+    ThetaArgs ta{};
+    ta.nblocks = (int)h->blocks.size();
+    ta.np_fwd = p.pl[GK_FWD][0];
+    ta.np_elem = p.fwd_only ? 0 : p.pl[GK_ELEM][0];   // the transposed weights serve the backward only
+    ta.blocks = h->d_blocks;
+    ta.params = params;
+    ta.theta = v.theta;
+    ta.theta_plane = v.theta_plane;
+    ta.thetaT = v.thetaT;
+    ta.thetaT_plane = v.thetaT_plane;
+    Timed t(h, KK_SPLIT, c.s);
+    launch_theta_pack(ta, h->pk_block_tiles, c.s);
+  }
+  if (!h->inputs.empty()) {
+    Timed t(h, KK_OTHER, c.s);
+    launch_tokens_t(tokens, v.tokT, B, h->num_vars, c.s);
+  }
+  if (h->m_rows > 0) {
+    Timed t(h, KK_OTHER, c.s);
+    launch_fill_u32(v.mkeys, (int64_t)h->m_rows * B, 0u, c.s);
+  }
+  if (p.ncounters > 0) {
+    Timed t(h, KK_OTHER, c.s);
+    launch_fill_u32(v.counters, p.ncounters, 0u, c.s);
+  }
+  if (h->lowrank_slots > 0 && h->opt_lr_pack == 0) {
+    // the fragment records of every LowRank group's factors, kept for the backward
+    LRPackArgs pa{};
+    pa.B = B;
+    pa.krank = h->lowrank_rank;
+    pa.sumexp = h->lowrank_form == PC_LOWRANK_SUM_EXP ? 1 : 0;
+    auto flush = [&]() {
+      if (pa.ngroups == 0) return;
+      Timed t(h, KK_SPLIT, c.s);
+      launch_lr_pack(pa, p.mode == PC_PREC_FP32, c.s);
+      pa.ngroups = 0;
+    };
+    for (const auto& sp : h->sums)
+      for (size_t gi = 0; gi < sp.groups.size(); ++gi) {
+        const GroupRec& r = sp.groups[gi];
+        if (r.lowrank < 0) continue;
+        const int q = pa.ngroups;
+        if (q == 0) pa.wg0[0] = 0;
+        pa.M[q] = r.M;
+        pa.N[q] = r.N;
+        pa.A[q] = lowrank->A[r.lowrank];
+        pa.Bf[q] = lowrank->B[r.lowrank];
+        pa.pk[q] = (uint16_t*)((char*)c.ws + p.lrPK + p.lr_pk_off[sp.lr_gidx[gi]]);
+        pa.wg0[q + 1] = pa.wg0[q] + lr_pack_workgroups(B, r.M, r.N, h->lowrank_rank);
+        if (++pa.ngroups == kMaxPackGroups) flush();
+      }
+    flush();
+  }
+  for (const LayerRef& r : h->layers) {
+    if (r.kind == PC_LAYER_INPUT_CAT) {
+      InputArgs a = input_args(c, h->inputs[r.idx], params);
+      a.vals = node_vals;
+      Timed t(h, KK_INFWD, c.s);
+      launch_input_fwd(a, c.s);
+    } else if (r.kind == PC_LAYER_PRODUCT) {
+      if (h->opt_fuse && h->prods[r.idx].fwd_fused) continue;   // evaluated by the next layer's column maxima
+      ProdArgs a = prod_args(c, h->prods[r.idx]);
+      a.vals = node_vals;
+      Timed t(h, KK_PRODFWD, c.s);
+      launch_prod_fwd(a, c.s);
+    } else if (r.kind == PC_LAYER_SUM) {
+      const SumPlan& sp = h->sums[r.idx];
+      SumArgs a = sum_common(c, sp);
+      a.vals = node_vals;
+      a.direct = v.earena;
+      a.direct_plane = v.earena_plane;
+      a.np_direct = p.fwd_only ? 0 : p.pl[GK_PARAM][1];   // node-major E is kept for the parameter flows
+      a.trans = v.ebt;
+      a.trans_plane = v.ebt_plane;
+      a.direct_rows = h->earena_rows;
+      a.np_trans = p.pl[GK_FWD][1];
+      if (h->opt_fuse && sp.fwd_prod >= 0) {
+        const ProductPlan& pp = h->prods[sp.fwd_prod];
+        a.fp_on = 1;
+        a.fp_start = pp.node_start;
+        a.fp_count = pp.num_nodes;
+        a.fp_maxdeg = pp.max_deg;
+        a.fp_ptr = pp.d_ch_ptr;
+        a.fp_ids = pp.d_ch_ids;
+        a.fp_affine = pp.affine ? 1 : 0;
+        for (int q = 0; q < 8; ++q) a.fp_abase[q] = pp.abase[q];
+        a.wvals = node_vals;
+      }
+      if (!(h->opt_fuse && sp.epi_max)) {   // else published by the previous layer's product epilogue
+        Timed t(h, KK_COLMAX, c.s);
+        launch_colmax(a, sp.pktiles, c.s);
+      }
+      a.fp_on = 0;
+      if (sp.lowrank) {
+        for (int gi = 0; gi < (int)sp.groups.size(); ++gi) {
+          LRArgs la = lr_args(c, sp, gi, lowrank, params, node_vals, nullptr);
+          if (h->opt_lr_pack == 1) {
+            Timed t(h, KK_SPLIT, c.s);
+            lr_pack_group(c, sp, gi, lowrank);
+          }
+          Timed t(h, KK_LRFWD, c.s);
+          launch_lr_fwd(la, p.mode == PC_PREC_FP32, c.s);
+        }
+        continue;
+      }
+      {
+        Timed t(h, KK_EXP, c.s);
+        launch_exp_pack(a, sp.pktiles, c.s);
+      }
+      GemmArgs g = gemm_common(c);
+      g.ngroups = (int)sp.groups.size();
+      g.groups = sp.d_groups;
+      g.chblocks = sp.d_blocks;
+      g.opA = v.theta;
+      g.planeA = v.theta_plane;
+      g.opB = v.ebt;
+      g.planeB = v.ebt_plane;
+      g.ldb = sp.ebt_cols;
+      g.vals = node_vals;
+      g.mkeys = v.mkeys;
+      g.mkeys_out = v.mkeys;
+      g.ssum = p.fwd_only ? nullptr : v.ssum;           // S is kept for the backward
+      if (h->opt_fuse && sp.epi_prod >= 0) {
+        const ProductPlan& pp = h->prods[sp.epi_prod];
+        g.ep_on = 1;
+        g.ep_qs = sp.epi_qs;
+        g.ep_base_s = pp.abase[sp.epi_qs];
+        g.ep_base_o = pp.abase[1 - sp.epi_qs];
+        g.ep_pstart = pp.node_start;
+        g.ep_pcount = pp.num_nodes;
+        g.ep_mrow = sp.epi_mrow;
+      }
+      const GemmShape shp = layer_gemm_shape(h, sp, GK_FWD, v.B_pad, p.pl[GK_FWD][0], p.pl[GK_FWD][1]);
+      g.ntiles = v.B_pad / shp.nt;
+      g.splitk = shp.splitk;
+      Timed t(h, KK_FWD, c.s);
+      launch_gemm(EPI_FWD, p.pl[GK_FWD][0], p.pl[GK_FWD][1], shp, g, c.s);
+    }
+  }
+  if (ll) {
+    Timed t(h, KK_OTHER, c.s);
+    launch_copy_row(node_vals + (int64_t)h->root * B, ll, B, c.s);
+  }
+  check_launch();
+}
+
+}  // namespace
+
 // ---------------------------------------------------------------------------
 // C ABI
 // ---------------------------------------------------------------------------
@@ -507,7 +721,10 @@ int pc_compile_layout(const pc_circuit_desc* desc, int device, pc_handle* out) {
     if (!out) fail(PC_ERR_INVALID_ARG, "null output handle pointer");
     *out = nullptr;
     h = compile_layout(desc);
-    if (device >= 0) upload_tables(h, device);
+    if (device >= 0) {
+      upload_tables(h, device);       // leaves `device` current
+      resolve_static_scratch(device);
+    }
     *out = reinterpret_cast<pc_handle>(h);
     return PC_OK;
   } catch (const Error& e) {
@@ -659,160 +876,28 @@ int pc_forward(pc_handle hh, int batch, const int32_t* tokens, const float* para
                float* ll, const pc_lowrank_io* lowrank, void* ws, size_t ws_bytes, void* stream) {
   try {
     Call c = begin_call(hh, batch, ws, ws_bytes, stream);
-    Handle* h = c.h;
-    check_lowrank_io(h, lowrank, false);
-    if (!params || !node_vals) fail(PC_ERR_INVALID_ARG, "null params or node_vals");
-    if (!h->inputs.empty() && !tokens) fail(PC_ERR_INVALID_ARG, "null tokens");
-    if (ll && h->root < 0) fail(PC_ERR_INVALID_ARG, "ll requested but the circuit has no root");
-    DeviceGuard dg(h->device);
-    const int B = batch;
-    const WsPlan& p = c.p;
-    const WsView& v = c.v;
-    if (h->has_plain_sums) {
-      ThetaArgs ta{};
-      ta.nblocks = (int)h->blocks.size();
-      ta.np_fwd = p.pl[GK_FWD][0];
-      ta.np_elem = p.pl[GK_ELEM][0];
-      ta.blocks = h->d_blocks;
-      ta.params = params;
-      ta.theta = v.theta;
-      ta.theta_plane = v.theta_plane;
-      ta.thetaT = v.thetaT;
-      ta.thetaT_plane = v.thetaT_plane;
-      Timed t(h, KK_SPLIT, c.s);
-      launch_theta_pack(ta, h->pk_block_tiles, c.s);
-    }
-    if (!h->inputs.empty()) {
-      Timed t(h, KK_OTHER, c.s);
-      launch_tokens_t(tokens, v.tokT, B, h->num_vars, c.s);
-    }
-    if (h->m_rows > 0) {
-      Timed t(h, KK_OTHER, c.s);
-      launch_fill_u32(v.mkeys, (int64_t)h->m_rows * B, 0u, c.s);
-    }
-    if (p.ncounters > 0) {
-      Timed t(h, KK_OTHER, c.s);
-      launch_fill_u32(v.counters, p.ncounters, 0u, c.s);
-    }
-    if (h->lowrank_slots > 0 && h->opt_lr_pack == 0) {
-      // the fragment records of every LowRank group's factors, kept for the backward
-      LRPackArgs pa{};
-      pa.B = B;
-      pa.krank = h->lowrank_rank;
-      pa.sumexp = h->lowrank_form == PC_LOWRANK_SUM_EXP ? 1 : 0;
-      auto flush = [&]() {
-        if (pa.ngroups == 0) return;
-        Timed t(h, KK_SPLIT, c.s);
-        launch_lr_pack(pa, p.mode == PC_PREC_FP32, c.s);
-        pa.ngroups = 0;
-      };
-      for (const auto& sp : h->sums)
-        for (size_t gi = 0; gi < sp.groups.size(); ++gi) {
-          const GroupRec& r = sp.groups[gi];
-          if (r.lowrank < 0) continue;
-          const int q = pa.ngroups;
-          if (q == 0) pa.wg0[0] = 0;
-          pa.M[q] = r.M;
-          pa.N[q] = r.N;
-          pa.A[q] = lowrank->A[r.lowrank];
-          pa.Bf[q] = lowrank->B[r.lowrank];
-          pa.pk[q] = (uint16_t*)((char*)c.ws + p.lrPK + p.lr_pk_off[sp.lr_gidx[gi]]);
-          pa.wg0[q + 1] = pa.wg0[q] + lr_pack_workgroups(B, r.M, r.N, h->lowrank_rank);
-          if (++pa.ngroups == kMaxPackGroups) flush();
-        }
-      flush();
-    }
-    for (const LayerRef& r : h->layers) {
-      if (r.kind == PC_LAYER_INPUT_CAT) {
-        InputArgs a = input_args(c, h->inputs[r.idx], params);
-        a.vals = node_vals;
-        Timed t(h, KK_INFWD, c.s);
-        launch_input_fwd(a, c.s);
-      } else if (r.kind == PC_LAYER_PRODUCT) {
-        if (h->opt_fuse && h->prods[r.idx].fwd_fused) continue;   // evaluated by the next layer's column maxima
-        ProdArgs a = prod_args(c, h->prods[r.idx]);
-        a.vals = node_vals;
-        Timed t(h, KK_PRODFWD, c.s);
-        launch_prod_fwd(a, c.s);
-      } else if (r.kind == PC_LAYER_SUM) {
-        const SumPlan& sp = h->sums[r.idx];
-        SumArgs a = sum_common(c, sp);
-        a.vals = node_vals;
-        a.direct = v.earena;
-        a.direct_plane = v.earena_plane;
-        a.np_direct = p.pl[GK_PARAM][1];
-        a.trans = v.ebt;
-        a.trans_plane = v.ebt_plane;
-        a.direct_rows = h->earena_rows;
-        a.np_trans = p.pl[GK_FWD][1];
-        if (h->opt_fuse && sp.fwd_prod >= 0) {
-          const ProductPlan& pp = h->prods[sp.fwd_prod];
-          a.fp_on = 1;
-          a.fp_start = pp.node_start;
-          a.fp_count = pp.num_nodes;
-          a.fp_maxdeg = pp.max_deg;
-          a.fp_ptr = pp.d_ch_ptr;
-          a.fp_ids = pp.d_ch_ids;
-          a.fp_affine = pp.affine ? 1 : 0;
-          for (int q = 0; q < 8; ++q) a.fp_abase[q] = pp.abase[q];
-          a.wvals = node_vals;
-        }
-        if (!(h->opt_fuse && sp.epi_max)) {   // else published by the previous layer's product epilogue
-          Timed t(h, KK_COLMAX, c.s);
-          launch_colmax(a, sp.pktiles, c.s);
-        }
-        a.fp_on = 0;
-        if (sp.lowrank) {
-          for (int gi = 0; gi < (int)sp.groups.size(); ++gi) {
-            LRArgs la = lr_args(c, sp, gi, lowrank, params, node_vals, nullptr);
-            if (h->opt_lr_pack == 1) {
-              Timed t(h, KK_SPLIT, c.s);
-              lr_pack_group(c, sp, gi, lowrank);
-            }
-            Timed t(h, KK_LRFWD, c.s);
-            launch_lr_fwd(la, p.mode == PC_PREC_FP32, c.s);
-          }
-          continue;
-        }
-        {
-          Timed t(h, KK_EXP, c.s);
-          launch_exp_pack(a, sp.pktiles, c.s);
-        }
-        GemmArgs g = gemm_common(c);
-        g.ngroups = (int)sp.groups.size();
-        g.groups = sp.d_groups;
-        g.chblocks = sp.d_blocks;
-        g.opA = v.theta;
-        g.planeA = v.theta_plane;
-        g.opB = v.ebt;
-        g.planeB = v.ebt_plane;
-        g.ldb = sp.ebt_cols;
-        g.vals = node_vals;
-        g.mkeys = v.mkeys;
-        g.mkeys_out = v.mkeys;
-        g.ssum = v.ssum;
-        if (h->opt_fuse && sp.epi_prod >= 0) {
-          const ProductPlan& pp = h->prods[sp.epi_prod];
-          g.ep_on = 1;
-          g.ep_qs = sp.epi_qs;
-          g.ep_base_s = pp.abase[sp.epi_qs];
-          g.ep_base_o = pp.abase[1 - sp.epi_qs];
-          g.ep_pstart = pp.node_start;
-          g.ep_pcount = pp.num_nodes;
-          g.ep_mrow = sp.epi_mrow;
-        }
-        const GemmShape shp = layer_gemm_shape(h, sp, GK_FWD, v.B_pad, p.pl[GK_FWD][0], p.pl[GK_FWD][1]);
-        g.ntiles = v.B_pad / shp.nt;
-        g.splitk = shp.splitk;
-        Timed t(h, KK_FWD, c.s);
-        launch_gemm(EPI_FWD, p.pl[GK_FWD][0], p.pl[GK_FWD][1], shp, g, c.s);
-      }
-    }
-    if (ll) {
-      Timed t(h, KK_OTHER, c.s);
-      launch_copy_row(node_vals + (int64_t)h->root * B, ll, B, c.s);
-    }
-    check_launch();
+    run_forward(c, tokens, params, node_vals, ll, lowrank);
+    return PC_OK;
+  } catch (const Error& e) {
+    return set_error(e.code, e.msg);
+  }
+}
+
+int pc_forward_static(pc_handle hh, int batch, const int32_t* tokens, const float* params, float* node_vals,
+                      float* ll, const pc_lowrank_io* lowrank, void* stream) {
+  try {
+    Handle* h = checked(hh);
+    if (h->device < 0) fail(PC_ERR_NO_DEVICE, "handle was compiled without a device");
+    if (batch < 1) fail(PC_ERR_INVALID_ARG, "batch must be >= 1");
+    const WsPlan p = plan_workspace(h, batch, true);
+    if (p.total > PC_STATIC_SCRATCH_BYTES)
+      fail(PC_ERR_WORKSPACE, "pc_forward_static: the forward of " + std::to_string(batch) + " samples needs " +
+                                 std::to_string(p.total) + " bytes of scratch, more than the static " +
+                                 std::to_string((size_t)PC_STATIC_SCRATCH_BYTES) + " (use pc_forward with a workspace)");
+    void* ws = static_scratch(h->device);
+    Call c = begin_call(hh, batch, ws, PC_STATIC_SCRATCH_BYTES, stream, true);
+    NoEvents ne(h);                      // no timing events: creating them could allocate
+    run_forward(c, tokens, params, node_vals, ll, lowrank);
     return PC_OK;
   } catch (const Error& e) {
     return set_error(e.code, e.msg);

@@ -184,6 +184,7 @@ struct Handle {
   FillRange* d_seed = nullptr;
   // timing
   bool timing = false;
+  bool no_events = false;              // set during a call that records no timing events (pc_forward_static)
   struct Ev {
     int kind;
     void* start;
@@ -209,6 +210,7 @@ inline bool gp_active(const Handle* h, int B) { return h->opt_fuse && h->gbt_slo
 // Workspace plan for a batch: byte offsets of every region.
 struct WsPlan {
   int B, B_pad, B_padK, mode;
+  bool fwd_only;                                     // forward-only plan: no region the backward alone reads
   int pl[3][2];
   size_t theta, thetaT, ebt, gbt, gbt2, earena, garena, mkeys, ssum, scratch, tokT, bptr, bidx, lowrank;
   size_t lrE, lrZ, lrS, lrU, lrW, lrC1, lrC2, lrP;   // LowRank regions (float32)
@@ -222,7 +224,7 @@ struct WsPlan {
   size_t lowrank_bytes;
   size_t total;
 };
-WsPlan plan_workspace(const Handle* h, int B);
+WsPlan plan_workspace(const Handle* h, int B, bool fwd_only = false);
 WsView make_view(const Handle* h, const WsPlan& p, void* ws);
 
 }  // namespace pc
