@@ -203,11 +203,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="hmm4096", choices=["hmm4096", "lowrank", "hclt", "dense"],
+    ap.add_argument("--workload", default="hmm4096", choices=["hmm4096", "lowrank", "hclt", "dense", "pd"],
                     help="hmm4096: the metric's workload (default); lowrank: the LowRank exp_sum HMM "
                          "(1024 states, 64 positions, rank 16, batch 64); hclt: the HCLT-like circuit (768 "
                          "variables x 1024 latents x 512 categories, batch 512); dense: one 1024 x 1024 dense "
-                         "layer over external children, batch 128")
+                         "layer over external children, batch 128; pd: a Poon-Domingos region graph over a 28 x 28 "
+                         "grid of 256-category variables (4-pixel region lattice, 64 latents per region), batch 128")
     ap.add_argument("--mode", default="auto", choices=["auto", "fp32"])
     ap.add_argument("--batch", type=int, default=None, help="batch (default: the workload's)")
     ap.add_argument("--H", type=int, default=4096)
@@ -280,6 +281,13 @@ def main():
         metric = "sum-layer fwd+bwd TFLOP/s (frac of MFMA peak), HCLT 768 vars x 1024 latents x 512 cats"
         workload = f"hclt 768 vars x 1024 latents x 512 categories, random tree, batch {cfg['B']} fwd+bwd+em"
         context = "pages (RTX PRO 6000, whole circuit, auto): 48.1 ms fwd+bwd at batch 512"
+    elif args.workload == "pd":
+        cfg = make_config("pd", **bsz)
+        metric = ("sum-layer fwd+bwd TFLOP/s (frac of MFMA peak), PD 28x28 grid x 256 cats, 4-pixel regions, "
+                  f"64 latents, batch {cfg['B']}")
+        workload = (f"pd 28x28 grid, 256 categories, region lattice 4, 64 latents per region, batch {cfg['B']} "
+                    "fwd+bwd+em")
+        context = "pages: PD layouts are not taken by the dense path (forward and fwd+bwd x1.00)"
     else:
         cfg = make_config("dense_layer", **bsz)
         metric = "sum-layer fwd+bwd TFLOP/s (frac of MFMA peak), one dense 1024x1024 layer"
@@ -404,7 +412,7 @@ def bench_circuit(args, cfg, metric, workload, context):
         elif args.cpu_sample_other is not None:
             sample = args.cpu_sample_other
         else:
-            sample = 8 if args.workload == "hclt" else B
+            sample = 8 if args.workload == "hclt" else 32 if args.workload == "pd" else B
         sample = min(sample, B)
         out["cpu_baseline"] = cpu_baseline(cfg, sample)
     print(json.dumps(out))

@@ -120,7 +120,8 @@ typedef struct pc_layer_desc {
 /* The circuit: layers in topological order (every child is defined by an
  * earlier layer), every node id in [0, num_nodes) defined exactly once.
  * root: node whose value pc_forward copies to `ll` (-1: none).
- * lowrank_rank: rank k of every LowRank slot (1..32), 0 if none.
+ * lowrank_rank: rank k of every LowRank slot (1..64: the fused kernels'
+ *   limit, pyjuice.parameterizations.LowRank, Note), 0 if none.
  * lowrank_form: how every LowRank slot's factors make the scale
  *   (pyjuice.parameterizations.LowRank, definition): PC_LOWRANK_EXP_SUM
  *   g_b = exp(A_b B_b), PC_LOWRANK_SUM_EXP g_b[i,j] = sum_r exp(A_b[i,r])
@@ -188,7 +189,7 @@ typedef struct pc_layout_summary {
  * Errors: PC_ERR_INVALID_ARG (null pointers, ids out of range, a node defined
  * twice or used before it is defined, empty product, tied groups of different
  * shape, parameters out of range, overlapping parameter blocks),
- * PC_ERR_UNSUPPORTED (LowRank rank > 32 or < 1), PC_ERR_HIP. */
+ * PC_ERR_UNSUPPORTED (LowRank rank > 64 or < 1), PC_ERR_HIP. */
 int pc_compile_layout(const pc_circuit_desc* desc, int device, pc_handle* out);
 
 /* Free a handle and its device tables (null is accepted). */
@@ -206,14 +207,14 @@ int pc_get_precision(pc_handle h, int* mode);
  * operand; the products of planes whose order is below the larger count are
  * accumulated: (1,1) one bf16 product; (2,1) or (1,2) one operand split,
  * two products; (2,2) hi/lo split, three products; (3,3) hi/mid/lo split,
- * six products.  Defaults: auto (2,1) for the forward (the weights split, the
- * exponentiated children rounded), (2,2) for the element flows (both split:
- * a child's flow dominated by one parent then carries no bf16 rounding of
- * g = f / S, the rounding that otherwise compounds from layer to layer past
- * 5e-3 end to end) and (2,1) for the parameter flows (g split, e rounded);
- * the weights, whose rounding would be the same for every sample, are never
- * rounded alone; fp32-level (3,3) everywhere.  Errors: PC_ERR_INVALID_ARG for
- * other counts or kinds. */
+ * six products.  Defaults: auto (2,2) for the forward and the element flows
+ * (both operands split: a value dominated by one child, or a flow dominated
+ * by one parent, then carries no bf16 rounding of e or of g = f / S, the
+ * rounding -- up to 2^-8 -- that otherwise compounds from layer to layer past
+ * 5e-3 end to end) and (2,1) for the parameter flows (g split, e rounded:
+ * they are summed over samples); the weights, whose rounding would be the
+ * same for every sample, are never rounded alone; fp32-level (3,3)
+ * everywhere.  Errors: PC_ERR_INVALID_ARG for other counts or kinds. */
 int pc_set_split(pc_handle h, int mode, int gemm_kind, int planes_a, int planes_b);
 
 /* Product-kernel tuning (advanced; results change only by float32 summation

@@ -295,6 +295,9 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
     Bb = a.opB;
     kbeg = split * kst / S;
     kend = (split + 1) * kst / S;
+    // a tile wholly in the group's row padding has no output (every split of
+    // it leaves here, so its arrival counter is never touched)
+    if (m0 >= (EPI == EPI_FWD ? gr.M : gr.N)) return;
   } else {
     // tile prefix of the block sequence: 256 x 256 tiles, twice as many
     // 128 x 256 tiles (blocks are padded to 256 both ways), or 128 x 128
@@ -317,6 +320,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
     const int in = lt - grp * GM * ntn;
     m0 = (r0g + in % rows) * MT;
     n0 = (in / rows) * NT;
+    if (m0 >= bl.M || n0 >= bl.N) return;      // wholly in the block's padding
     kst = a.B_padK / KT;
     {
       const int c0 = a.copy_lo < bl.ncopies ? a.copy_lo : bl.ncopies;
@@ -658,9 +662,14 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
           for (int e = 0; e < 4; ++e) x[c][e] = (ok && col + e < B) ? src[e] : 0.0f;
         }
         if (gp && ok) {
-          // scaled sums of the packed layer's node `row`
-          const float4 t = *(const float4*)(a.ssum + (a.gp_s_row + row) * B + col);
-          sv[c][0] = t.x; sv[c][1] = t.y; sv[c][2] = t.z; sv[c][3] = t.w;
+          // scaled sums of the packed layer's node `row` (the batch is a
+          // multiple of 64: a 4-column chunk is all samples or all padding)
+          if (col < B) {
+            const float4 t = *(const float4*)(a.ssum + (a.gp_s_row + row) * B + col);
+            sv[c][0] = t.x; sv[c][1] = t.y; sv[c][2] = t.z; sv[c][3] = t.w;
+          } else {
+            sv[c][0] = sv[c][1] = sv[c][2] = sv[c][3] = 0.0f;
+          }
         }
       } else {
         ok = row < bl.M;
@@ -732,11 +741,13 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
           f[e] = 0.0f + o[e];
           gq[e] = (f[e] == 0.0f || !(sv[c][e] > 0.0f)) ? 0.0f : f[e] / sv[c][e];
         }
-        const float4 f4 = make_float4(f[0], f[1], f[2], f[3]);
-        *(float4*)(a.flows + (int64_t)(a.gp_out_start + row) * B + col) = f4;
-        *(float4*)(a.flows + (int64_t)(a.gp_other + row) * B + col) = f4;
-        split_planes<4>(gq, a.gp_np_direct, a.gp_direct + panel(a.gp_g_row + row, col, a.gp_direct_rows),
-                        a.gp_direct_plane);
+        if (col < B) {                         // padded samples: zeros in the batch-major G only
+          const float4 f4 = make_float4(f[0], f[1], f[2], f[3]);
+          *(float4*)(a.flows + (int64_t)(a.gp_out_start + row) * B + col) = f4;
+          *(float4*)(a.flows + (int64_t)(a.gp_other + row) * B + col) = f4;
+          split_planes<4>(gq, a.gp_np_direct, a.gp_direct + panel(a.gp_g_row + row, col, a.gp_direct_rows),
+                          a.gp_direct_plane);
+        }
         *(float4*)pv = make_float4(gq[0], gq[1], gq[2], gq[3]);
       }
       if (EPI == EPI_FWD && ep && pi[c] >= 0) {

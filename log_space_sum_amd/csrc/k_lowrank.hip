@@ -85,20 +85,24 @@ __device__ __forceinline__ float at4(const float4& v, int e) { return e == 0 ? v
 // that the fused kernels load each operand with one 16-byte access per lane:
 //   A side, block ib of rows, per sample b:
 //     h form, K chunk kc (PH planes): lane l: A[ib*32 + l%32][kc*16 + (l/32)*8 + e] * log2(e)
-//     d form, chunk cc (PG planes):   lane l: A[ib*32 + 16cc + (e/4)*8 + (l/32)*4 + e%4][l%32]
+//     d form, rank block kb, chunk cc (PG planes):
+//                                     lane l: A[ib*32 + 16cc + (e/4)*8 + (l/32)*4 + e%4][kb*32 + l%32]
 //   B side, block jb of columns, per sample b:
 //     h form, K chunk kc (PH planes): lane l: B[kc*16 + (l/32)*8 + e][jb*32 + l%32]
-//     u form, chunk cc (PG planes):   lane l: B[l%32][jb*32 + 16cc + (e/4)*8 + (l/32)*4 + e%4]
+//     u form, rank block kb, chunk cc (PG planes):
+//                                     lane l: B[kb*32 + l%32][jb*32 + 16cc + (e/4)*8 + (l/32)*4 + e%4]
 // (zero outside the factor).  The h forms are the two operands of h = A B (or
 // of its transpose); the d form is the first operand of dB = A^T X and the u
 // form that of U^T, W^T = B (q e)^T, B q^T, whose second operands come from h's
 // accumulator registers, hence the permuted order along the contraction.
-// Records of a block: the h forms (kc, plane), then the d / u forms (cc, plane).
+// Records of a block: the h forms (kc, plane), then the d / u forms (kb, cc,
+// plane).  KC chunks of 16 cover the rank in h; KB blocks of 32 cover it in
+// the gradient products (KB = 1 up to rank 32, 2 up to rank 64).
 constexpr int kFrag = 512;   // bfloat16 elements per record
 
-template <int PH, int PG, int KC>
+template <int PH, int PG, int KC, int KB>
 struct LrPack {
-  static constexpr int FB = KC * PH + 2 * PG;     // records per block
+  static constexpr int FB = KC * PH + 2 * KB * PG;     // records per block
   static __device__ __forceinline__ const uint16_t* bside(const uint16_t* pk, int N, int b, int jb) {
     const int nJB = (N + 31) / 32;
     return pk + ((int64_t)b * nJB + jb) * FB * kFrag;
@@ -128,9 +132,10 @@ __device__ __forceinline__ void split_store_frag(const float (&x)[8], uint16_t* 
 // The fragment records of every LowRank group of the circuit, made once per
 // forward and kept for the backward: workgroups [wg0[g], wg0[g + 1]) pack
 // group g, four record sets (64 lanes each) per workgroup.
-template <int PH, int PG, int KC>
+template <int PH, int PG, int KC, int KB>
 __global__ __launch_bounds__(256) void k_lr_pack(LRPackArgs pa) {
-  using PK = LrPack<PH, PG, KC>;
+  using PK = LrPack<PH, PG, KC, KB>;
+  constexpr int NF = KC + 2 * KB;                  // forms per block
   const int tid = threadIdx.x;
   // "sum_exp": every record holds exp of the factor (the matrix instructions
   // then sum exp(A) exp(B) over the rank, no log2(e) on the h form); padding
@@ -141,12 +146,12 @@ __global__ __launch_bounds__(256) void k_lr_pack(LRPackArgs pa) {
   while (g + 1 < pa.ngroups && (int)blockIdx.x >= pa.wg0[g + 1]) ++g;
   const int M = pa.M[g], N = pa.N[g], Bn = pa.B, kr = pa.krank;
   const int nJB = (N + 31) / 32, nIB = (M + 31) / 32;
-  const int64_t nsets = (int64_t)Bn * (nJB + nIB) * (KC + 2);
+  const int64_t nsets = (int64_t)Bn * (nJB + nIB) * NF;
   const int64_t set = (int64_t)(blockIdx.x - pa.wg0[g]) * 4 + (tid >> 6);
   if (set >= nsets) return;
   const int lane = tid & 63, l32 = lane & 31, h = lane >> 5;
-  const int form = (int)(set % (KC + 2));
-  const int64_t rest = set / (KC + 2);
+  const int form = (int)(set % NF);
+  const int64_t rest = set / NF;
   const int blk = (int)(rest % (nJB + nIB)), b = (int)(rest / (nJB + nIB));
   float x[8];
   if (blk < nJB) {
@@ -162,10 +167,10 @@ __global__ __launch_bounds__(256) void k_lr_pack(LRPackArgs pa) {
       }
       split_store_frag<PH>(x, dst + form * PH * kFrag);
     } else {
-      const int cc = form - KC;
+      const int kb = (form - KC) >> 1, cc = (form - KC) & 1, kk = kb * 32 + l32;
       const int jq = jb * 32 + 16 * cc + h * 4;     // values e of runs jq + (e/4)*8 + e%4
-      if ((N & 3) == 0 && l32 < kr && jq + 11 < N) {
-        const float4 u0 = ld4(Bb + (int64_t)l32 * N + jq), u1 = ld4(Bb + (int64_t)l32 * N + jq + 8);
+      if ((N & 3) == 0 && kk < kr && jq + 11 < N) {
+        const float4 u0 = ld4(Bb + (int64_t)kk * N + jq), u1 = ld4(Bb + (int64_t)kk * N + jq + 8);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           x[e] = fv(at4(u0, e));
@@ -175,10 +180,10 @@ __global__ __launch_bounds__(256) void k_lr_pack(LRPackArgs pa) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int j = jq + (e / 4) * 8 + (e % 4);
-          x[e] = (l32 < kr && j < N) ? fv(Bb[(int64_t)l32 * N + j]) : 0.0f;
+          x[e] = (kk < kr && j < N) ? fv(Bb[(int64_t)kk * N + j]) : 0.0f;
         }
       }
-      split_store_frag<PG>(x, dst + (KC * PH + cc * PG) * kFrag);
+      split_store_frag<PG>(x, dst + (KC * PH + (kb * 2 + cc) * PG) * kFrag);
     }
   } else {
     const int ib = blk - nJB;
@@ -202,13 +207,13 @@ __global__ __launch_bounds__(256) void k_lr_pack(LRPackArgs pa) {
       }
       split_store_frag<PH>(x, dst + form * PH * kFrag);
     } else {
-      const int cc = form - KC;
+      const int kb = (form - KC) >> 1, cc = (form - KC) & 1, kk = kb * 32 + l32;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int i = ib * 32 + 16 * cc + (e / 4) * 8 + h * 4 + (e % 4);
-        x[e] = (l32 < kr && i < M) ? fv(Ab[(int64_t)i * kr + l32]) : 0.0f;
+        x[e] = (kk < kr && i < M) ? fv(Ab[(int64_t)i * kr + kk]) : 0.0f;
       }
-      split_store_frag<PG>(x, dst + (KC * PH + cc * PG) * kFrag);
+      split_store_frag<PG>(x, dst + (KC * PH + (kb * 2 + cc) * PG) * kFrag);
     }
   }
 }
@@ -266,9 +271,9 @@ __global__ __launch_bounds__(256) void k_lr_coef(LRArgs a) {
 // "sum_exp" form, whose records hold exp(A), exp(B), so the matrix product is
 // the scale g itself (no exp per pair) and U, W sum theta e and theta against
 // exp(B) (the coefficient kernel multiplies by exp(A)).
-template <int PH, int PG, int KC, bool SE = false>
+template <int PH, int PG, int KC, int KB, bool SE = false>
 __global__ __launch_bounds__(256) void k_lr_fwd(LRArgs a) {
-  using PK = LrPack<PH, PG, KC>;
+  using PK = LrPack<PH, PG, KC, KB>;
   __shared__ __attribute__((aligned(16))) float slab[kSlabF];   // theta rows [32][C + 4]
   __shared__ __attribute__((aligned(16))) float el[4][kChunkF]; // e of the chunk, per sample
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
@@ -294,13 +299,15 @@ __global__ __launch_bounds__(256) void k_lr_fwd(LRArgs a) {
       for (int p = 0; p < PH; ++p) bA[kc][p] = ldfrag(ap + (kc * PH + p) * kFrag, lb);
   }
   float Zp = 0.0f, Sp = 0.0f;
-  f32x16_t U, W;
+  f32x16_t U[KB], W[KB];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) U[r] = W[r] = 0.0f;
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) U[kb][r] = W[kb][r] = 0.0f;
 
   struct Ld {
     bf16x8_t bh[KC][PH];   // h form of B_b (first operand of h^T: rows j)
-    bf16x8_t bu[2][PG];    // u form of B_b (first operand of U^T, W^T: rows k)
+    bf16x8_t bu[KB][2][PG];   // u form of B_b (first operand of U^T, W^T: rows k)
   };
   auto load = [&](int jb, Ld& L) {
     const uint16_t* r = Bp + (int64_t)jb * PK::FB * kFrag;
@@ -309,9 +316,11 @@ __global__ __launch_bounds__(256) void k_lr_fwd(LRArgs a) {
 #pragma unroll
       for (int p = 0; p < PH; ++p) L.bh[kc][p] = ldfrag(r + (kc * PH + p) * kFrag, lb);
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int p = 0; p < PG; ++p) L.bu[cc][p] = ldfrag(r + (KC * PH + cc * PG + p) * kFrag, lb);
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int p = 0; p < PG; ++p) L.bu[kb][cc][p] = ldfrag(r + (KC * PH + (kb * 2 + cc) * PG + p) * kFrag, lb);
   };
 
   for (int c0 = 0; c0 < N; c0 += kChunkF) {
@@ -429,8 +438,11 @@ __global__ __launch_bounds__(256) void k_lr_fwd(LRArgs a) {
         bf16x8_t pq[PG], pw[PG];
         split8<PG>(xq, pq);
         split8<PG>(xw, pw);
-        mfma_planes<PG>(U, cur.bu[cc], pq);
-        mfma_planes<PG>(W, cur.bu[cc], pw);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          mfma_planes<PG>(U[kb], cur.bu[kb][cc], pq);
+          mfma_planes<PG>(W[kb], cur.bu[kb][cc], pw);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -450,15 +462,17 @@ __global__ __launch_bounds__(256) void k_lr_fwd(LRArgs a) {
     a.S[(int64_t)b * M + i] = S;
     a.vals[(int64_t)(a.out_start + i) * a.B + b] = (Z > 0.0f && S > 0.0f) ? sh + logf(S / Z) : -INFINITY;
   }
-  // accumulator register r: row k = (r/4)*8 + h*4 + r%4, column i
+  // accumulator register r of rank block kb: row k = kb*32 + (r/4)*8 + h*4 + r%4, column i
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int k = (r / 4) * 8 + h * 4 + (r % 4);
-    if (k < kr) {
-      a.U[((int64_t)b * M + i) * kr + k] = U[r];
-      a.W[((int64_t)b * M + i) * kr + k] = W[r];
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int k = kb * 32 + (r / 4) * 8 + h * 4 + (r % 4);
+      if (k < kr) {
+        a.U[((int64_t)b * M + i) * kr + k] = U[kb][r];
+        a.W[((int64_t)b * M + i) * kr + k] = W[kb][r];
+      }
     }
-  }
 }
 
 // Backward: workgroup = 32 children x 8 samples (8 waves, one sample each),
@@ -475,9 +489,9 @@ __global__ __launch_bounds__(256) void k_lr_fwd(LRArgs a) {
 // SE: the "sum_exp" form (records of exp(A), exp(B): the product is g), whose
 // dB term is theta (c1 e - c2) against exp(A) and is multiplied by exp(B) at
 // the end.
-template <int PH, int PG, int KC, bool WS = false, bool SE = false>
+template <int PH, int PG, int KC, int KB, bool WS = false, bool SE = false>
 __global__ __launch_bounds__(512) void k_lr_bwd(LRArgs a) {
-  using PK = LrPack<PH, PG, KC>;
+  using PK = LrPack<PH, PG, KC, KB>;
   __shared__ __attribute__((aligned(16))) float slab[kSlabB];   // theta^T [32][R + 4]
   __shared__ float xch[2][8][1024];                              // per wave: parameter flows of a 32 x 32 tile
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
@@ -505,9 +519,11 @@ __global__ __launch_bounds__(512) void k_lr_bwd(LRArgs a) {
     ev = expf(a.vals[(int64_t)child * a.B + b] - key_to_shift_lr(a.mkeys[(int64_t)a.m_row * a.B + b]));
   }
   float fcp = 0.0f;
-  f32x16_t dB;
+  f32x16_t dB[KB];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) dB[r] = 0.0f;
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dB[kb][r] = 0.0f;
   float* P = a.P + (int64_t)sg * M * N;
   const int ldC = (M + 31) / 32 * 32;
   const float* C1 = a.C1 + (int64_t)bq * ldC + h * 4;   // rows padded with zeros to ldC
@@ -525,7 +541,7 @@ __global__ __launch_bounds__(512) void k_lr_bwd(LRArgs a) {
 
   struct Fr {
     bf16x8_t ah[KC][PH];   // h form of A_b (first operand of h: rows i)
-    bf16x8_t ad[2][PG];    // d form of A_b (first operand of dB: rows k)
+    bf16x8_t ad[KB][2][PG];   // d form of A_b (first operand of dB: rows k)
   };
   struct Cf {
     float4 c1[4], c2[4];   // rows ib*32 + g*8 + h*4 .. +3
@@ -538,9 +554,11 @@ __global__ __launch_bounds__(512) void k_lr_bwd(LRArgs a) {
       for (int p = 0; p < PH; ++p) L.ah[kc][p] = ldfrag(r + (kc * PH + p) * kFrag, lb);
     if constexpr (!WS)
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int p = 0; p < PG; ++p) L.ad[cc][p] = ldfrag(r + (KC * PH + cc * PG + p) * kFrag, lb);
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+          for (int p = 0; p < PG; ++p) L.ad[kb][cc][p] = ldfrag(r + (KC * PH + (kb * 2 + cc) * PG + p) * kFrag, lb);
   };
   auto loadC = [&](int ib, Cf& L) {
 #pragma unroll
@@ -652,7 +670,8 @@ __global__ __launch_bounds__(512) void k_lr_bwd(LRArgs a) {
             for (int e = 0; e < 8; ++e) xx[e] = X[8 * cc + e];
             bf16x8_t px[PG];
             split8<PG>(xx, px);
-            mfma_planes<PG>(dB, fc.ad[cc], px);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) mfma_planes<PG>(dB[kb], fc.ad[kb][cc], px);
           }
           }
         } else {
@@ -703,11 +722,13 @@ __global__ __launch_bounds__(512) void k_lr_bwd(LRArgs a) {
     }
   }
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int k = (r / 4) * 8 + h * 4 + (r % 4);
-    const int64_t o = ((int64_t)b * kr + k) * N + j;
-    if (k < kr) a.dB[o] = SE ? expf(a.Bf[o]) * dB[r] : dB[r];
-  }
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int k = kb * 32 + (r / 4) * 8 + h * 4 + (r % 4);
+      const int64_t o = ((int64_t)b * kr + k) * N + j;
+      if (k < kr) a.dB[o] = SE ? expf(a.Bf[o]) * dB[kb][r] : dB[kb][r];
+    }
 }
 
 // F+ += sum of the ceil(B/8) partial matrices, in order.
@@ -726,51 +747,60 @@ static int grid_lr(int64_t n) {
 }
 
 // Precision of the fused kernels: h with PH planes per operand, the gradient
-// products with PG (auto: 2 and 1; fp32-level: 3 and 3); KC K chunks of 16
-// cover the rank.
+// products with PG (auto: 2 and 1; fp32-level: 3 and 3).  KC K chunks of 16
+// cover the rank in h (1, 2 or 4: ranks up to 16, 32, 64) and KB blocks of
+// 32 in the gradient products (1 up to rank 32, else 2).
+static int lr_kc(int krank) { return krank <= 16 ? 1 : krank <= 32 ? 2 : 4; }
+static int lr_kb(int krank) { return krank <= 32 ? 1 : 2; }
+
+template <int PH, int PG, int KC, int KB>
+static void lr_fwd_kk(const LRArgs& a, const dim3& grid, hipStream_t s) {
+  if (a.sumexp) hipLaunchKernelGGL((k_lr_fwd<PH, PG, KC, KB, true>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((k_lr_fwd<PH, PG, KC, KB>), grid, dim3(256), 0, s, a);
+}
 template <int PH, int PG>
 static void lr_fwd_k(const LRArgs& a, hipStream_t s) {
   const dim3 grid(((a.M + 31) / 32) * ((a.B + 3) / 4));
-  if (a.sumexp) {
-    if (a.krank <= 16) hipLaunchKernelGGL((k_lr_fwd<PH, PG, 1, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_lr_fwd<PH, PG, 2, true>), grid, dim3(256), 0, s, a);
-    return;
-  }
-  if (a.krank <= 16) hipLaunchKernelGGL((k_lr_fwd<PH, PG, 1>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((k_lr_fwd<PH, PG, 2>), grid, dim3(256), 0, s, a);
+  const int kc = lr_kc(a.krank);
+  if (kc == 1) lr_fwd_kk<PH, PG, 1, 1>(a, grid, s);
+  else if (kc == 2) lr_fwd_kk<PH, PG, 2, 1>(a, grid, s);
+  else lr_fwd_kk<PH, PG, 4, 2>(a, grid, s);
+}
+template <int PH, int PG, int KC, int KB, bool WS>
+static void lr_bwd_kk(const LRArgs& a, const dim3& grid, hipStream_t s) {
+  if (a.sumexp) hipLaunchKernelGGL((k_lr_bwd<PH, PG, KC, KB, WS, true>), grid, dim3(512), 0, s, a);
+  else hipLaunchKernelGGL((k_lr_bwd<PH, PG, KC, KB, WS>), grid, dim3(512), 0, s, a);
 }
 template <int PH, int PG, bool WS = false>
 static void lr_bwd_k(const LRArgs& a, hipStream_t s) {
   const dim3 grid(((a.N + 31) / 32) * ((a.B + 7) / 8));
-  if (a.sumexp) {
-    if (a.krank <= 16) hipLaunchKernelGGL((k_lr_bwd<PH, PG, 1, WS, true>), grid, dim3(512), 0, s, a);
-    else hipLaunchKernelGGL((k_lr_bwd<PH, PG, 2, WS, true>), grid, dim3(512), 0, s, a);
-    return;
-  }
-  if (a.krank <= 16) hipLaunchKernelGGL((k_lr_bwd<PH, PG, 1, WS>), grid, dim3(512), 0, s, a);
-  else hipLaunchKernelGGL((k_lr_bwd<PH, PG, 2, WS>), grid, dim3(512), 0, s, a);
+  const int kc = lr_kc(a.krank);
+  if (kc == 1) lr_bwd_kk<PH, PG, 1, 1, WS>(a, grid, s);
+  else if (kc == 2) lr_bwd_kk<PH, PG, 2, 1, WS>(a, grid, s);
+  else lr_bwd_kk<PH, PG, 4, 2, WS>(a, grid, s);
 }
 
 int64_t lr_pack_bytes(int B, int M, int N, int krank, int fp32) {
-  const int PH = fp32 ? 3 : 2, PG = fp32 ? 3 : 1, KC = krank <= 16 ? 1 : 2;
-  return (int64_t)B * ((N + 31) / 32 + (M + 31) / 32) * (KC * PH + 2 * PG) * kFrag * 2;
+  const int PH = fp32 ? 3 : 2, PG = fp32 ? 3 : 1, KC = lr_kc(krank), KB = lr_kb(krank);
+  return (int64_t)B * ((N + 31) / 32 + (M + 31) / 32) * (KC * PH + 2 * KB * PG) * kFrag * 2;
 }
 int lr_pack_workgroups(int B, int M, int N, int krank) {
-  const int KC = krank <= 16 ? 1 : 2;
-  const int64_t nsets = (int64_t)B * ((N + 31) / 32 + (M + 31) / 32) * (KC + 2);
+  const int KC = lr_kc(krank), KB = lr_kb(krank);
+  const int64_t nsets = (int64_t)B * ((N + 31) / 32 + (M + 31) / 32) * (KC + 2 * KB);
   return (int)((nsets + 3) / 4);
+}
+template <int PH, int PG>
+static void lr_pack_k(const LRPackArgs& pa, const dim3& grid, hipStream_t s) {
+  const int kc = lr_kc(pa.krank);
+  if (kc == 1) hipLaunchKernelGGL((k_lr_pack<PH, PG, 1, 1>), grid, dim3(256), 0, s, pa);
+  else if (kc == 2) hipLaunchKernelGGL((k_lr_pack<PH, PG, 2, 1>), grid, dim3(256), 0, s, pa);
+  else hipLaunchKernelGGL((k_lr_pack<PH, PG, 4, 2>), grid, dim3(256), 0, s, pa);
 }
 void launch_lr_pack(const LRPackArgs& pa, int fp32, hipStream_t s) {
   if (pa.ngroups <= 0) return;
   const dim3 grid(pa.wg0[pa.ngroups]);
-  const bool k2 = pa.krank > 16;
-  if (fp32) {
-    if (k2) hipLaunchKernelGGL((k_lr_pack<3, 3, 2>), grid, dim3(256), 0, s, pa);
-    else hipLaunchKernelGGL((k_lr_pack<3, 3, 1>), grid, dim3(256), 0, s, pa);
-  } else {
-    if (k2) hipLaunchKernelGGL((k_lr_pack<2, 1, 2>), grid, dim3(256), 0, s, pa);
-    else hipLaunchKernelGGL((k_lr_pack<2, 1, 1>), grid, dim3(256), 0, s, pa);
-  }
+  if (fp32) lr_pack_k<3, 3>(pa, grid, s);
+  else lr_pack_k<2, 1>(pa, grid, s);
 }
 void launch_lr_coef(const LRArgs& a, hipStream_t s) {
   const int64_t n = (int64_t)a.B * ((a.M + 31) / 32 * 32);

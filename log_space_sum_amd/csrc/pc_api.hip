@@ -206,11 +206,17 @@ WsPlan plan_workspace(const Handle* h, int B, bool fwd_only) {
   WsPlan p{};
   p.B = B;
   p.fwd_only = fwd_only;
-  p.B_pad = (int)round_up(B, ROW_PAD);
   p.B_padK = (int)round_up(B, K_PAD);
   p.mode = effective_mode(h, B);
   for (int k = 0; k < 3; ++k)
     for (int j = 0; j < 2; ++j) p.pl[k][j] = h->planes[p.mode][k][j];
+  // the batch-major operands hold whole column tiles of the per-layer
+  // products (and whole 64-sample packing tiles), no more
+  {
+    const int nt = std::max(layer_tile_nt(p.pl[GK_FWD][0], p.pl[GK_FWD][1], h->opt_layer_tile),
+                            layer_tile_nt(p.pl[GK_ELEM][0], p.pl[GK_ELEM][1], h->opt_layer_tile));
+    p.B_pad = (int)round_up(B, std::max(nt, 64));
+  }
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -226,7 +232,7 @@ WsPlan plan_workspace(const Handle* h, int B, bool fwd_only) {
   p.thetaT = take(bw * p.pl[GK_ELEM][0] * h->thetaT_elems * 2);
   p.ebt = take((size_t)p.pl[GK_FWD][1] * Bp * h->max_ebt_cols * 2);
   p.gbt = take(bw * p.pl[GK_ELEM][1] * Bp * h->max_gbt_cols * 2);
-  p.gbt2 = take(bw * (h->gbt_slots > 1 && B % 256 == 0 ?   // independent of the fusion option
+  p.gbt2 = take(bw * (h->gbt_slots > 1 && gp_batch_ok(B) ?   // independent of the fusion option
                         (size_t)p.pl[GK_ELEM][1] * Bp * h->max_gbt_cols * 2 : 0));
   p.earena = take(bw * p.pl[GK_PARAM][1] * h->earena_rows * BpK * 2);
   p.garena = take(bw * p.pl[GK_PARAM][0] * h->garena_rows * BpK * 2);
@@ -1119,7 +1125,7 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
           g.gp_direct = v.garena;
           g.gp_trans = sa.gbt_slot ? v.gbt2 : v.gbt;
           g.ssum = v.ssum;   // the packed layer's kept scaled sums
-          if (!g.ssum || !g.gp_direct || !g.gp_trans || B % 256 != 0 || ra.s_row < 0)
+          if (!g.ssum || !g.gp_direct || !g.gp_trans || !gp_batch_ok(B) || ra.s_row < 0)
             fail(PC_ERR_INVALID_ARG, "internal: element-flow product epilogue without its operands");
         }
         g.vals = vals;

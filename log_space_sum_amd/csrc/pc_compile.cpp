@@ -34,8 +34,8 @@ Handle* compile_layout(const pc_circuit_desc* d) {
   need(d->num_params >= 0, "num_params must be >= 0");
   need(d->num_layers >= 1 && d->layers != nullptr, "need at least one layer");
   need(d->root >= -1 && d->root < d->num_nodes, "root out of range");
-  if (d->lowrank_rank < 0 || d->lowrank_rank > 32)
-    fail(PC_ERR_UNSUPPORTED, "LowRank rank must be in 1..32 (the fused LowRank kernels)");
+  if (d->lowrank_rank < 0 || d->lowrank_rank > 64)
+    fail(PC_ERR_UNSUPPORTED, "LowRank rank must be in 1..64 (the fused LowRank kernels)");
   if (d->lowrank_form != PC_LOWRANK_EXP_SUM && d->lowrank_form != PC_LOWRANK_SUM_EXP)
     fail(PC_ERR_UNSUPPORTED, "LowRank form must be PC_LOWRANK_EXP_SUM or PC_LOWRANK_SUM_EXP");
 
@@ -202,7 +202,7 @@ Handle* compile_layout(const pc_circuit_desc* d) {
         param_range(li, G.param_offset, (int64_t)G.num_nodes * N);
         need(G.lowrank_slot >= -1, gs + "bad lowrank slot");
         if (G.lowrank_slot >= 0) {
-          if (d->lowrank_rank < 1) fail(PC_ERR_UNSUPPORTED, gs + "LowRank group needs lowrank_rank in 1..32");
+          if (d->lowrank_rank < 1) fail(PC_ERR_UNSUPPORTED, gs + "LowRank group needs lowrank_rank in 1..64");
           ++n_lr;
           lowrank_slots = std::max(lowrank_slots, G.lowrank_slot + 1);
         }

@@ -137,8 +137,8 @@ struct Handle {
   int device = -1;
   int mode = PC_PREC_AUTO;
   // planes[mode][gemm kind][0: first operand, 1: second operand]
-  // auto: forward (2,1), element flows (2,2), parameter flows (2,1); fp32-level (3,3)
-  int planes[2][3][2] = {{{2, 1}, {2, 2}, {2, 1}}, {{3, 3}, {3, 3}, {3, 3}}};
+  // auto: forward (2,2), element flows (2,2), parameter flows (2,1); fp32-level (3,3)
+  int planes[2][3][2] = {{{2, 2}, {2, 2}, {2, 1}}, {{3, 3}, {3, 3}, {3, 3}}};
   int opt_layer_tile = 0, opt_param_tile = 0, opt_split_max = 8, opt_fuse = 1;   // pc_set_option
   int opt_param_chunk = -1;            // tied copies per parameter-flow launch (0: one launch at the end, -1: automatic)
   int opt_lr_pack = 0;                 // LowRank fragment records: 0 once per forward, 1 per layer and pass
@@ -204,8 +204,10 @@ void free_tables(Handle* h);
 inline int effective_mode(const Handle* h, int B) { return B < 16 ? PC_PREC_FP32 : h->mode; }
 
 // Element-flow product epilogues pack the next layer's G when fusion is on and
-// the batch needs no padded samples in either G layout.
-inline bool gp_active(const Handle* h, int B) { return h->opt_fuse && h->gbt_slots > 1 && B % 256 == 0; }
+// the batch is a multiple of 64 (the node-major G has no padded samples; the
+// epilogue masks the batch-major layout's padded ones).
+inline bool gp_batch_ok(int B) { return B % 64 == 0; }
+inline bool gp_active(const Handle* h, int B) { return h->opt_fuse && h->gbt_slots > 1 && gp_batch_ok(B); }
 
 // Workspace plan for a batch: byte offsets of every region.
 struct WsPlan {

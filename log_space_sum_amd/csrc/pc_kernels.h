@@ -89,6 +89,12 @@ constexpr int gemm_stages(int pa, int pb, int mt, int nt) {
 // 128 split in four, 8% faster than 128 x 128 split in eight).  The K split
 // (a power of two up to split_max) grows until the launch has 256 workgroups,
 // keeping >= 4 slices per split.
+// Columns (samples) of the tile a forward / element-flow launch uses.
+inline int layer_tile_nt(int pa, int pb, int opt_tile) {
+  if (opt_tile == TILE_AUTO) opt_tile = pa > pb ? TILE_64x128 : TILE_128x64;
+  return opt_tile == TILE_128x256 ? 256 : opt_tile == TILE_128x64 ? 64 : 128;
+}
+
 inline GemmShape layer_shape(int rows256, int B_pad, int kpad, int pa, int pb, int opt_tile, int split_max) {
   GemmShape g{};
   if (opt_tile == TILE_AUTO) opt_tile = pa > pb ? TILE_64x128 : TILE_128x64;

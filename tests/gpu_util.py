@@ -160,26 +160,35 @@ def check_values(got, ref, mode, what):
 
 
 # dLL/dA and dLL/dB of LowRank slots: compared normwise and against the
-# array's largest entry (the gradient is a difference of two products, so
-# entries near zero carry the rounding of the terms that cancel):
-#   fp32-level: ||x - x*|| <= 1e-5 ||x*|| and max|x - x*| <= 1e-5 max|x*|;
-#   auto (gradient products in one bfloat16 term): 1e-2 and 3e-2.
+# largest entry of the magnitude `mag` of the terms the gradient is a
+# difference of (dLL/dA_b = X B_b^T with X = eps - f theta_b, the edge flows
+# minus the normaliser's part: mag = |eps| |B_b|^T + |f theta_b| |B_b|^T, and
+# likewise for dB and for the "sum_exp" form; without mag, |x*| itself):
+# the products round each term, so where the two nearly cancel (wide or
+# offset factors) the error is relative to the terms, not to the difference:
+#   auto (gradient products in one bfloat16 term): ||x - x*|| <= 1e-2 ||mag||
+#     and max|x - x*| <= 3e-2 max mag;
+#   fp32-level (six-term products): 1e-5 of |x*| itself, normwise and max.
 GRAD_TOL = {"fp32": (1e-5, 1e-5), "auto": (1e-2, 3e-2)}
 
 
-def check_grads(got, ref, mode, what, e2e_tol=None):
+def check_grads(got, ref, mode, what, e2e_tol=None, mag=None):
     """e2e_tol: for gradients compared end to end at fp32 level, the flows'
     end-to-end bound (gpu_util.e2e_flow_tol) replaces 1e-5: the gradients are
     built from the end-to-end flows and carry their float32-storage term."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
-    scale = max(np.abs(ref).max(), 1e-300)
-    en = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+    if mode != "auto":
+        mag = None               # fp32-level: against |x*| itself
+    m = np.abs(ref) if mag is None else np.asarray(mag, np.float64)
+    scale = max(m.max(), 1e-300)
+    en = float(np.linalg.norm(got - ref) / max(np.linalg.norm(m), 1e-300))
     em = float(np.abs(got - ref).max() / scale)
     tn, tm = GRAD_TOL[mode]
     if e2e_tol is not None and mode == "fp32":
         tn = tm = e2e_tol
-    say(f"  {what}: normwise {en:.3e}, max/max|ref| {em:.3e} (mode {mode}, bounds {tn:.3e} {tm:.3e})")
+    say(f"  {what}: normwise {en:.3e}, max/max {em:.3e} of {'|ref|' if mag is None else 'the terms'} "
+        f"(mode {mode}, bounds {tn:.3e} {tm:.3e})")
     assert np.isfinite(got).all(), f"{what}: non-finite entries"
     assert en <= tn and em <= tm, f"{what}: normwise {en:.3e} (bound {tn}), max {em:.3e} (bound {tm})"
     return en, em
@@ -317,7 +326,7 @@ def local_oracle(cfg, gpu, samples=None, own_values=False, want_pflows=True):
     lr = cfg.get("lowrank")
     if lr is not None:
         lr = [(a[cols], b[cols]) for a, b in lr]
-    dA, dB = {}, {}
+    dA, dB, magA, magB = {}, {}, {}, {}
     for layer in circ.layers:
         if isinstance(layer, W.Sum):
             sub, kids, outs, blocks = _sub_sum_circuit(circ, layer)
@@ -336,6 +345,10 @@ def local_oracle(cfg, gpu, samples=None, own_values=False, want_pflows=True):
                     pflows[o:o + n] += r["param_flows"][q:q + n]
             dA.update(r["dA"])
             dB.update(r["dB"])
+            for g in sub.layers[1].groups:
+                if g.lowrank >= 0:
+                    ma, mb = _lowrank_grad_terms(sub, ps, Vb, _seed_rows(sub, GF[outs]), g, lr, circ.lowrank_form)
+                    magA[g.lowrank], magB[g.lowrank] = ma, mb
         elif isinstance(layer, W.Product):
             ptr = layer.ch_ptr.astype(np.int64)
             ids = layer.ch_ids.astype(np.int64)
@@ -356,7 +369,57 @@ def local_oracle(cfg, gpu, samples=None, own_values=False, want_pflows=True):
             if want_pflows:
                 r = oracle.backward(sub, ps, V, tokens=tok, seed_flows=GF[rng_])
                 pflows[layer.param_offset:layer.param_offset + size] += r["param_flows"]
-    return dict(vals=vals, flows=flows, pflows=pflows, dA=dA, dB=dB)
+    return dict(vals=vals, flows=flows, pflows=pflows, dA=dA, dB=dB, magA=magA, magB=magB)
+
+
+def _seed_rows(sub, seeds):
+    """Flows of the sub-circuit with the seeds on its output rows."""
+    F = np.zeros((sub.num_nodes, seeds.shape[1]))
+    F[sub.output_nodes()] = seeds
+    return F
+
+
+def _lowrank_grad_terms(sub, ps, V, F, g, lowrank, form):
+    """Magnitudes of the two terms dLL/dA_b and dLL/dB_b are differences of
+    (per sample, from the layer's inputs): with theta_b, edge flows eps and
+    the node's flow f as in the oracle's LowRank backward,
+      exp_sum: |eps| |B_b|^T + |f theta_b| |B_b|^T  and  |A_b|^T (|eps| + |f theta_b|);
+      sum_exp: exp(A_b) (theta (c1 e + c2) exp(B_b)^T), exp(B_b) (exp(A_b)^T theta (c1 e + c2))
+    with c1 = f / S, c2 = f / Z.  Returns ([B, M, k], [B, k, N])."""
+    import oracle
+    th = ps[g.param_offset:g.param_offset + g.num_nodes * g.num_children].reshape(g.num_nodes, g.num_children)
+    ch = g.child_ids()
+    C = V[ch]
+    m = C.max(axis=0)
+    m = np.where(np.isfinite(m), m, 0.0)
+    E = np.exp(C - m)
+    n = V[g.out_start:g.out_start + g.num_nodes]
+    f = F[g.out_start:g.out_start + g.num_nodes]
+    A, Bf = lowrank[g.lowrank]
+    Bn = V.shape[1]
+    MA = np.zeros(A.shape)
+    MB = np.zeros(Bf.shape)
+    for b in range(Bn):
+        Ab = np.asarray(A[b], np.float64)
+        Bb = np.asarray(Bf[b], np.float64)
+        tb, q, Z = oracle.lowrank_effective(th, Ab, Bb, form)
+        fi = np.where(np.isfinite(n[:, b]), f[:, b], 0.0)
+        S = tb @ E[:, b]
+        with np.errstate(divide="ignore", invalid="ignore"):
+            c1 = np.where((fi != 0) & (S > 0), fi / S, 0.0)
+        eps = tb * E[:, b][None, :] * c1[:, None]
+        norm = np.abs(fi)[:, None] * tb
+        if form == "exp_sum":
+            MA[b] = (np.abs(eps) + norm) @ np.abs(Bb).T
+            MB[b] = np.abs(Ab).T @ (np.abs(eps) + norm)
+        else:
+            with np.errstate(divide="ignore", invalid="ignore"):
+                c2 = np.where((fi != 0) & (Z > 0), fi / Z, 0.0)
+            Gm = th * (np.abs(c1)[:, None] * E[:, b][None, :] + np.abs(c2)[:, None])
+            eA, eB = np.exp(Ab), np.exp(Bb)
+            MA[b] = eA * (Gm @ eB.T)
+            MB[b] = eB * (eA.T @ Gm)
+    return MA, MB
 
 
 def check_local(cfg, gpu, mode, what, samples=None, pflows=True):

@@ -332,6 +332,55 @@ def check_block_sparse_normalized(orc):
         assert abs(np.exp(ll).sum() - 1.0) < 1e-12, (seed, np.exp(ll).sum())
 
 
+def check_pd_normalized(orc):
+    """PD region-graph circuits (2 x 2 pixel grid, three categories; 2 x 3 with
+    two; a 4 x 4 grid on a 2-pixel lattice whose leaf cells are products of
+    four pixels, two categories) sum to one over every assignment of their
+    variables, and every sample's LL equals the log of the brute-force sum over
+    the region graph's latent choices for the 2 x 2 grid."""
+    for (H, W, K, nc, split, seed) in [(2, 2, 2, 3, 1, 0), (2, 3, 3, 2, 1, 1), (4, 4, 2, 2, 2, 2)]:
+        circ = C.pd(H, W, K, nc, split)
+        p = _renorm(circ, I.softmax_rows_params(circ, np.random.default_rng(seed)))
+        xs = np.array(list(itertools.product(range(nc), repeat=H * W)), dtype=np.int32)
+        _, ll = orc.forward(circ, p, len(xs), tokens=xs)
+        assert abs(np.exp(ll).sum() - 1.0) < 1e-12, ((H, W, K), np.exp(ll).sum())
+    # 2 x 2 grid: regions are the 4 pixels, 2 + 2 dominoes and the square;
+    # the square's root mixes 2 cuts (rows, columns) x K latents, each cut's
+    # latent k multiplying the two dominoes' latent k, each domino mixing
+    # its one cut's latent k' of the two pixels.
+    circ = C.pd(2, 2, 2, 3, 1)
+    p = _renorm(circ, I.softmax_rows_params(circ, np.random.default_rng(0)))
+    xs = np.array(list(itertools.product(range(3), repeat=4)), dtype=np.int32)
+    _, ll = orc.forward(circ, p, len(xs), tokens=xs)
+    K = 2
+    emit = p[:4 * K * 3].reshape(4, K, 3)                  # pixel v, latent k, category
+    sums = {}
+    for layer in circ.layers:
+        if isinstance(layer, C.Sum):
+            for g in layer.groups:
+                sums[int(g.out_start)] = (g, p[g.param_offset:g.param_offset + g.num_nodes * g.num_children]
+                                          .reshape(g.num_nodes, g.num_children))
+    root_g, root_w = sums[circ.root]
+    # the domino sum groups, keyed by their pixel pairs, in the order the builder
+    # creates regions: sorted by (area, y0, y1, x0, x1)
+    dominoes = sorted([(0, 1, 0, 2), (1, 2, 0, 2), (0, 2, 0, 1), (0, 2, 1, 2)])
+    pix = {(0, 1, 0, 2): (0, 1), (1, 2, 0, 2): (2, 3), (0, 2, 0, 1): (0, 2), (0, 2, 1, 2): (1, 3)}
+    dom_groups = sorted([g for g, _ in sums.values() if g.num_nodes == K], key=lambda g: g.out_start)
+    dom_w = {r: sums[int(g.out_start)][1] for r, g in zip(dominoes, dom_groups)}
+    cuts = [((0, 1, 0, 2), (1, 2, 0, 2)), ((0, 2, 0, 1), (0, 2, 1, 2))]   # rows, then columns
+    expect = []
+    for x in xs:
+        def dom(r, k):
+            a, b = pix[r]
+            return sum(dom_w[r][k, q] * emit[a, q, x[a]] * emit[b, q, x[b]] for q in range(K))
+        tot = 0.0
+        for c, (r1, r2) in enumerate(cuts):
+            for k in range(K):
+                tot += root_w[0, c * K + k] * dom(r1, k) * dom(r2, k)
+        expect.append(np.log(tot))
+    _close(ll, expect, 1e-12, 1e-12, "pd 2x2 brute force")
+
+
 def check_flows_fd(orc):
     """On a block-sparse circuit: parameter flows = theta * dLL/dtheta (sum and
     input parameters) and element flows = dLL/dv (node-value perturbation)."""
@@ -356,6 +405,31 @@ def check_flows_fd(orc):
             dv[b] = h
             d = (L(p, {int(node): dv}) - L(p, {int(node): -dv})) / (2 * h)
             _close(r["flows"][node, b], d, 1e-6, 1e-9, f"element flow node {node} b {b}")
+
+
+def check_pd_flows_fd(orc):
+    """On a PD circuit (3 x 3 grid, 3 latents): parameter flows = theta *
+    dLL/dtheta and element flows = dLL/dv by central differences."""
+    circ = C.pd(3, 3, 3, 3, 1)
+    B = 3
+    rng = np.random.default_rng(4)
+    p = I.softmax_rows_params(circ, rng).astype(F64)
+    x = rng.integers(0, 3, size=(B, 9)).astype(np.int32)
+
+    def L(pp, perturb=None):
+        return float(orc.forward(circ, pp, B, tokens=x, perturb=perturb)[1].sum())
+
+    V, _ = orc.forward(circ, p, B, tokens=x)
+    r = orc.backward(circ, p, V, tokens=x)
+    for k in np.linspace(0, circ.num_params - 1, 19).astype(int):
+        d = _fd(lambda q: L(q), p, int(k), 1e-6)
+        _close(r["param_flows"][k], p[k] * d, 1e-6, 1e-9, f"pd param flow {k}")
+    for node in np.linspace(0, circ.num_nodes - 1, 13).astype(int):
+        h = 1e-5
+        dv = np.zeros(B)
+        dv[1] = h
+        d = (L(p, {int(node): dv}) - L(p, {int(node): -dv})) / (2 * h)
+        _close(r["flows"][node, 1], d, 1e-6, 1e-9, f"pd element flow node {node}")
 
 
 # ---------------------------------------------------------------------------
@@ -616,7 +690,8 @@ def check_neg_inf_flows(orc):
 ALL_CHECKS = [check_dense_logsumexp, check_dense_flows_fd, check_hmm_bruteforce,
               check_hmm_forward_algorithm, check_hmm_posteriors, check_baum_welch,
               check_em_blend_and_pseudocount, check_hclt_bruteforce, check_hclt_tree_recursion,
-              check_block_sparse_normalized, check_flows_fd, check_lowrank_reductions,
+              check_block_sparse_normalized, check_pd_normalized, check_flows_fd, check_pd_flows_fd,
+              check_lowrank_reductions,
               check_lowrank_inhomogeneous_hmm, check_lowrank_grad_fd, check_lowrank_zstat_fd,
               check_lowrank_sumexp_inhomogeneous_hmm, check_lowrank_sumexp_grad_fd,
               check_lowrank_sumexp_reduction, check_lowrank_sumexp_zstat_fd,

@@ -119,10 +119,11 @@ def test_descriptor_errors():
     # product without children
     p = W.Product(8, 2, np.array([0, 1, 1], dtype=np.int32), np.array([0], dtype=np.int32))
     _expect(L.PC_ERR_INVALID_ARG, L.pc_compile_layout, base([ext, p]), -1)
-    # LowRank rank above 32 (ranks up to 32 compile)
-    c = W.hmm(4, 3, 2, lowrank_rank=33)
+    # LowRank rank above 64 (ranks up to 64 compile)
+    c = W.hmm(4, 3, 2, lowrank_rank=65)
     _expect(L.PC_ERR_UNSUPPORTED, L.pc_compile_layout, c, -1)
-    L.pc_compile_layout(W.hmm(4, 3, 2, lowrank_rank=32), -1)
+    L.pc_compile_layout(W.hmm(4, 3, 2, lowrank_rank=64), -1)
+    L.pc_compile_layout(W.hmm(4, 3, 2, lowrank_rank=48), -1)
     # LowRank forms: exp_sum and sum_exp compile, any other value is refused
     L.pc_compile_layout(W.hmm(4, 3, 2, lowrank_rank=4, lowrank_form="sum_exp"), -1)
     c = W.hmm(4, 3, 2, lowrank_rank=4)

@@ -36,8 +36,8 @@ def _lowrank_full(cfg, mode, what):
     G.check_flows(gpu["flows"], orc["flows"], mode, f"{what} element flows end to end", rtol=tol)
     G.check_flows(gpu["pflows"], orc["pflows"], mode, f"{what} parameter flows end to end", rtol=tol)
     for s in range(len(gpu["dA"])):
-        G.check_grads(gpu["dA"][s], loc["dA"][s], mode, f"{what} slot {s} dLL/dA per layer")
-        G.check_grads(gpu["dB"][s], loc["dB"][s], mode, f"{what} slot {s} dLL/dB per layer")
+        G.check_grads(gpu["dA"][s], loc["dA"][s], mode, f"{what} slot {s} dLL/dA per layer", mag=loc["magA"][s])
+        G.check_grads(gpu["dB"][s], loc["dB"][s], mode, f"{what} slot {s} dLL/dB per layer", mag=loc["magB"][s])
     return gpu, orc
 
 
@@ -48,6 +48,9 @@ def _lowrank_full(cfg, mode, what):
     (40, 4, 7, 5, 23, 1.0),       # ragged rows and children
     (96, 3, 9, 32, 24, 4.0),      # rank 32 (two K steps), 4-nat spread
     (64, 4, 9, 16, 20, 0.3),      # 0.3-nat spread
+    (72, 3, 9, 48, 21, 1.0),      # rank 48: four K steps (the last half padding), two rank blocks
+    (100, 3, 7, 64, 33, 4.0),     # rank 64, ragged rows and samples
+    (64, 4, 9, 16, 24, 8.0),      # 8-nat spread: exp(A B) over about e^+-30
 ])
 def test_lowrank_hmm(mode, H, T, V, rank, B, spread):
     cfg = make_config("lowrank", H=H, T=T, V=V, rank=rank, B=B, spread=spread)
@@ -93,6 +96,7 @@ def test_lowrank_z_correction(mode, H, T, V, rank, B, spread):
     (64, 5, 16, 16, 37, 1.0),     # two strips, ragged sample groups
     (40, 4, 7, 5, 23, 1.0),       # ragged rows and children
     (96, 3, 9, 32, 24, 4.0),      # rank 32 (two K steps), 4-nat spread
+    (80, 3, 7, 64, 19, 1.0),      # rank 64
 ])
 def test_lowrank_sum_exp(mode, H, T, V, rank, B, spread):
     """The "sum_exp" form (g_b[i, j] = sum_r exp(A_b[i, r]) exp(B_b[r, j])):
@@ -118,6 +122,33 @@ def test_lowrank_sum_exp_z_correction():
     ref = oracle.em_step_corrected(circ, cfg["params"], gpu["pflows"].astype(np.float64),
                                    gpu["z_flows"].astype(np.float64))
     G.check_flows(gpu["em_corrected"], ref, "fp32", f"{what} conditional M-step")
+
+
+@pytest.mark.parametrize("mode", ["auto", "fp32"])
+def test_lowrank_offset_factors(mode):
+    """Factors with a common offset: every h = (A B)[i, j] near +60 nats (the
+    scale exp(h) far from 1 but inside float32's range; the normalisation by
+    Z cancels it)."""
+    cfg = make_config("lowrank", H=64, T=4, V=9, rank=16, B=20, spread=1.0)
+    cfg["lowrank"] = [(a + np.float32(1.9), b + np.float32(1.9)) for a, b in cfg["lowrank"]]
+    _lowrank_full(cfg, mode, "lowrank offset factors (h ~ +58)")
+
+
+@pytest.mark.parametrize("mode", ["auto", "fp32"])
+def test_lowrank_rank64_z_correction(mode):
+    """W and the conditional M-step at rank 64."""
+    import oracle
+    cfg = make_config("lowrank", H=72, T=3, V=9, rank=64, B=24, spread=1.0)
+    circ = cfg["circuit"]
+    what = "lowrank rank-64 z-correction"
+    G.say(f"case {what} mode={mode} B={cfg['B']}")
+    gpu = G.run_gpu(cfg, mode, z_init=np.zeros(circ.num_params, np.float32), em_corrected=(1.0, 0.0))
+    orc = G.run_oracle(cfg)
+    inside = np.zeros(circ.num_params, bool)
+    for off, n in oracle.lowrank_param_ranges(circ):
+        inside[off:off + n] = True
+    G.check_flows(gpu["z_flows"][inside], orc["z_flows"][inside], mode, f"{what} W end to end",
+                  rtol=G.e2e_flow_tol(circ, orc["vals"], mode))
 
 
 def test_lowrank_small_batch_runs_fp32():

@@ -152,6 +152,29 @@ def test_hclt_multi_unit_groups(mode):
 
 
 @pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("what,cfg_args", [
+    # node blocks of 16, every pixel a leaf, a full batch of 512
+    ("pd 6x6 k16", dict(name="pd", H=6, W=6, K=16, C=8, split=1, B=512)),
+    # node blocks of 32, leaf cells of 2 x 2 pixels, ragged batch
+    ("pd 8x8 k32", dict(name="pd", H=8, W=8, K=32, C=16, split=2, B=37)),
+    # node blocks of 128 over 4-pixel leaf cells
+    ("pd 12x12 k128", dict(name="pd", H=12, W=12, K=128, C=4, split=4, B=64)),
+    # the measured PD workload at its own size
+    ("pd 28x28 k64", dict(name="pd")),
+])
+def test_pd(what, cfg_args, mode):
+    """Poon-Domingos region-graph circuits: general block-sparse sum layers
+    whose groups (one per region) mix lists of K-node product blocks."""
+    import log_space_sum_amd as L
+    cfg = make_config(**cfg_args)
+    circ = cfg["circuit"]
+    h = L.pc_compile_layout(circ, device=-1)
+    cls = {L.pc_layer_class(h, i) for i, ly in enumerate(circ.layers) if type(ly).__name__ == "Sum"}
+    assert L.PC_CLASS_GENERAL in cls, cls
+    _full(cfg, mode, what)
+
+
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("seed", [0, 1])
 def test_block_sparse_layer(mode, seed):
     cfg = make_config(kind="block_layer", seed=seed, M_blocks=9, node_block=48, ch_blocks=7,
@@ -196,9 +219,12 @@ def test_fp32_needs_split(kind):
 @pytest.mark.parametrize("what,cfg_args,mode,all_fused", [
     ("hmm", dict(name="hmm4096", H=320, T=7, V=50, B=70), "auto", True),
     ("hmm ragged batch", dict(name="hmm4096", H=96, T=4, V=11, B=23), "fp32", True),
-    # batches of multiples of 256: the element-flow products also pack the
-    # next layer's scaled flows
+    # batches of multiples of 64: the element-flow products also pack the
+    # next layer's scaled flows (at 320 and 192 the last 128-sample column
+    # tile is half padding)
     ("hmm batch 256", dict(name="hmm4096", H=320, T=6, V=50, B=256), "auto", True),
+    ("hmm batch 320", dict(name="hmm4096", H=320, T=6, V=50, B=320), "auto", True),
+    ("hmm batch 192", dict(name="hmm4096", H=128, T=5, V=20, B=192), "fp32", True),
     ("hmm batch 512", dict(name="hmm4096", H=128, T=5, V=20, B=512), "fp32", True),
     ("hclt", dict(name="hclt", num_vars=30, H=48, K=12, B=33), "auto", False),
     ("block-sparse", dict(kind="block_sparse", seed=2, num_vars=6, K=5, in_blocks=3, block=24,
@@ -225,7 +251,7 @@ def test_fused_product_layers_identical(what, cfg_args, mode, all_fused):
     assert tp["product_fwd"][0] > 0 and tp["product_bwd"][0] > 0
     if all_fused:   # every product layer of an HMM (LowRank or not) sits between two sum layers
         assert tf["product_fwd"][0] == 0 and tf["product_bwd"][0] == 0
-    if all_fused and cfg["B"] % 256 == 0:
+    if all_fused and cfg["B"] % 64 == 0:
         # every sum layer below a product layer is packed by the layer above
         G.say(f"  scaled-flow launches fused/plain: {tf['scaled_flows'][0]}/{tp['scaled_flows'][0]}")
         assert tf["scaled_flows"][0] < tp["scaled_flows"][0]

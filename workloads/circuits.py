@@ -478,3 +478,106 @@ def random_block_layer(seed: int, M_blocks: int, node_block: int, ch_blocks: int
                 layers=[ext, Sum(groups)], root=-1)
     c.meta = dict(kind="block_layer")
     return c
+
+
+def pd(H: int, W: int, K: int, num_cats: int, split: int = 1) -> Circuit:
+    """Poon-Domingos (PD) region-graph circuit over an H x W grid of
+    categorical variables (variable r*W + c), with K latents per region.
+
+    Regions are the axis-aligned rectangles whose edges lie on multiples of
+    ``split`` (and on the grid's border); a region of one cell is a leaf.  A
+    leaf cell of one pixel is K categorical input nodes with their own rows; a
+    leaf cell of several pixels is K products of its pixels' input nodes
+    (node k of every pixel).  Every way of cutting a region in two along a
+    row or column line gives a product block of K nodes, node k adding node k
+    of the two halves; the region's K sum nodes mix all of its product blocks
+    (one sum group: node block K over a list of K-node child blocks, its own
+    [K, splits*K] weights).  The full grid's region is one root sum node over
+    its product blocks.  Sum and product layers are levelled by depth, so each
+    sum layer holds many groups with different child-block lists (the general
+    block-sparse layout).
+    """
+    ys = sorted(set(list(range(0, H, split)) + [H]))
+    xs = sorted(set(list(range(0, W, split)) + [W]))
+    regions = [(y0, y1, x0, x1) for i, y0 in enumerate(ys) for y1 in ys[i + 1:]
+               for j, x0 in enumerate(xs) for x1 in xs[j + 1:]]
+    # children before parents: by area, then position
+    regions.sort(key=lambda r: ((r[1] - r[0]) * (r[3] - r[2]), r))
+    nvar = H * W
+    inp = InputCat(node_start=0, num_nodes=nvar * K, num_cats=num_cats,
+                   var=np.repeat(np.arange(nvar, dtype=np.int32), K),
+                   row=np.arange(nvar * K, dtype=np.int32), param_offset=0, num_rows=nvar * K)
+    pcur = nvar * K * num_cats
+    nxt = nvar * K
+    block = {}     # region -> first node of its K-node block (value of the region)
+    level = {}     # region -> sum level (leaf pixels: 0)
+    prod_levels = {}   # level -> list of (first node placeholder, [child starts...]) filled later
+    sum_levels = {}    # level -> list of (region, [product block ids])
+    cell_prods = []    # leaf cells of several pixels: (region, [pixel input starts])
+    leaf = lambda r: len([y for y in ys if r[0] < y < r[1]]) == 0 and len([x for x in xs if r[2] < x < r[3]]) == 0
+    prod_blocks = []   # (level, child region a, child region b, owner region)
+    for r in regions:
+        y0, y1, x0, x1 = r
+        if leaf(r):
+            pix = [(y, x) for y in range(y0, y1) for x in range(x0, x1)]
+            if len(pix) == 1:
+                block[r] = (pix[0][0] * W + pix[0][1]) * K
+                level[r] = 0
+            else:
+                cell_prods.append((r, [(y * W + x) * K for y, x in pix]))
+                level[r] = 0
+            continue
+        cuts = [((y0, y, x0, x1), (y, y1, x0, x1)) for y in ys if y0 < y < y1] + \
+               [((y0, y1, x0, x), (y0, y1, x, x1)) for x in xs if x0 < x < x1]
+        lv = 1 + max(max(level[a], level[b]) for a, b in cuts)
+        level[r] = lv
+        for a, b in cuts:
+            prod_blocks.append((lv, a, b, r))
+    layers = [inp]
+    # leaf cells of several pixels: one product layer before everything else
+    if cell_prods:
+        start = nxt
+        ptr, ids = [0], []
+        for r, pstarts in cell_prods:
+            block[r] = nxt
+            for k in range(K):
+                ids.extend(s + k for s in pstarts)
+                ptr.append(len(ids))
+            nxt += K
+        layers.append(Product(node_start=start, num_nodes=nxt - start,
+                              ch_ptr=np.array(ptr, dtype=np.int32), ch_ids=np.array(ids, dtype=np.int32)))
+    maxlv = max(level.values())
+    full = (0, H, 0, W)
+    for lv in range(1, maxlv + 1):
+        # products of this level: node k of the block = node k of both halves
+        owners = {}
+        start = nxt
+        ptr, ids = [0], []
+        for (l, a, b, r) in prod_blocks:
+            if l != lv:
+                continue
+            owners.setdefault(r, []).append(nxt)
+            for k in range(K):
+                ids.extend([block[a] + k, block[b] + k])
+                ptr.append(len(ids))
+            nxt += K
+        if nxt > start:
+            layers.append(Product(node_start=start, num_nodes=nxt - start,
+                                  ch_ptr=np.array(ptr, dtype=np.int32), ch_ids=np.array(ids, dtype=np.int32)))
+        groups = []
+        for r in sorted(owners):
+            M = 1 if r == full else K
+            chs = np.array(owners[r], dtype=np.int32)
+            groups.append(SumGroup(out_start=nxt, num_nodes=M, ch_block_start=chs, ch_block_size=K,
+                                   param_offset=pcur))
+            block[r] = nxt
+            pcur += M * len(chs) * K
+            nxt += M
+        if groups:
+            layers.append(Sum(groups))
+    root = block[full]
+    c = Circuit(name=f"pd{H}x{W}k{K}c{num_cats}s{split}", num_nodes=nxt, num_vars=nvar, num_params=pcur,
+                layers=layers, root=root)
+    c.meta = dict(kind="pd", H=H, W=W, K=K, num_cats=num_cats, split=split, regions=len(regions),
+                  product_blocks=len(prod_blocks))
+    return c

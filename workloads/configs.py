@@ -7,7 +7,11 @@ helper that materialises one of them at a chosen batch size.
 3. HMM: 4096 states, 32 positions, 512 symbols, batch 128 / 512;
 4. HCLT-like: 768 variables x 512 categories, 1024 latents, random tree, batch 512;
 5. LowRank exp_sum: HMM with 1024 states, 64 positions, 512 symbols, rank 16,
-   batch 64, factor spread 0.3 .. 4 nats.
+   batch 64, factor spread 0.3 .. 4 nats;
+6. PD (Poon-Domingos region graph) over a 28 x 28 grid of 256-category
+   variables, regions on a 4-pixel lattice, 64 latents per region, batch 128:
+   general block-sparse sum layers (node blocks of 64 over lists of 64-node
+   child blocks).
 """
 from __future__ import annotations
 
@@ -22,6 +26,7 @@ CONFIGS = {
     "hmm4096": dict(seed=2, kind="hmm", H=4096, T=32, V=512, B=512),
     "hclt": dict(seed=3, kind="hclt", num_vars=768, H=1024, K=512, B=512),
     "lowrank": dict(seed=4, kind="hmm", H=1024, T=64, V=512, B=64, rank=16, spread=1.0),
+    "pd": dict(seed=5, kind="pd", H=28, W=28, K=64, C=256, split=4, B=128),
 }
 
 
@@ -55,6 +60,10 @@ def make_config(name: str = None, **over):
         circ = C.hclt(cfg["num_vars"], cfg["H"], cfg["K"], cfg.get("seed", 3))
         out["params"] = I.softmax_rows_params(circ, rng)
         out["tokens"] = I.uniform_tokens(circ, B, cfg["K"], rng)
+    elif kind == "pd":
+        circ = C.pd(cfg["H"], cfg["W"], cfg["K"], cfg["C"], cfg.get("split", 1))
+        out["params"] = I.softmax_rows_params(circ, rng)
+        out["tokens"] = I.uniform_tokens(circ, B, cfg["C"], rng)
     elif kind == "block_sparse":
         circ = C.block_sparse(cfg.get("seed", 0), **{k: cfg[k] for k in
                               ("num_vars", "K", "in_blocks", "block", "sum_blocks", "density",
