@@ -242,8 +242,13 @@ int pc_set_split(pc_handle h, int mode, int gemm_kind, int planes_a, int planes_
  * into the caller's before it returns.  PC_OPT_LR_PACK: when the bfloat16 fragment records of
  * the LowRank factors are made: 0 (default) all at once at the start of
  * pc_forward, kept for pc_backward; 1 each group's just before its layer, in
- * both passes (identical results).  Changing an option can change
- * pc_workspace_bytes.
+ * both passes (identical results).  PC_OPT_SUMEXP_FUSED: how LowRank
+ * groups of the "sum_exp" form run: 0 (default) as products with the shared
+ * weights on a virtual batch of batch x rank columns
+ * (pyjuice.parameterizations.LowRank, definition and Note: "sum_exp" is k
+ * matmuls with the shared parameters), 1 through the fused LowRank kernels
+ * (one visit per sample, node and child; results differ by rounding).
+ * Changing an option can change pc_workspace_bytes.
  * Errors: PC_ERR_INVALID_ARG (unknown option or value). */
 #define PC_OPT_LAYER_TILE 0
 #define PC_OPT_PARAM_TILE 1
@@ -251,6 +256,7 @@ int pc_set_split(pc_handle h, int mode, int gemm_kind, int planes_a, int planes_
 #define PC_OPT_FUSE       3
 #define PC_OPT_PARAM_CHUNK 4
 #define PC_OPT_LR_PACK    5
+#define PC_OPT_SUMEXP_FUSED 6
 int pc_set_option(pc_handle h, int option, int value);
 
 /* Bytes of workspace pc_forward / pc_backward need for `batch` samples in the

@@ -219,7 +219,8 @@ def pc_set_split(h: Handle, mode, gemm_kind, planes_a: int, planes_b: int):
     _check(lib().pc_set_split(h.ptr, int(mode), int(gemm_kind), int(planes_a), int(planes_b)))
 
 
-OPTIONS = {"layer_tile": 0, "param_tile": 1, "split_max": 2, "fuse": 3, "param_chunk": 4, "lr_pack": 5}
+OPTIONS = {"layer_tile": 0, "param_tile": 1, "split_max": 2, "fuse": 3, "param_chunk": 4, "lr_pack": 5,
+           "sumexp_fused": 6}
 
 
 def pc_set_option(h: Handle, option, value: int):

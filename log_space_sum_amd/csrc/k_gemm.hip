@@ -257,6 +257,9 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
     tile = logical / S;
     split = logical - tile * S;
   }
+  // the forward's operand layout: weights [M rows, K = N] (forward products,
+  // and virtual-batch stores with vs_elem == 0); else the transposed weights
+  const bool fwdA = EPI == EPI_FWD || (EPI == EPI_VSTORE && !a.vs_elem);
   const uint16_t* Ab;
   const uint16_t* Bb;
   int64_t RA, RB, ra0, rb0;
@@ -265,11 +268,11 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
   int ka0 = 0, kb0 = 0;
   GroupRec gr{};
   BlockRec bl{};
-  if (EPI == EPI_FWD || EPI == EPI_ELEM) {
+  if (EPI == EPI_FWD || EPI == EPI_ELEM || EPI == EPI_VSTORE) {
     const int gt = tile / a.ntiles, nt = tile - gt * a.ntiles;
     const int unit = gt / SUB;
     int g;
-    if (EPI == EPI_FWD)
+    if (fwdA)
       g = find_last_le(a.groups, a.ngroups, unit, [](const GroupRec& r) { return r.mt_start; });
     else
       g = find_last_le(a.groups, a.ngroups, unit, [](const GroupRec& r) { return r.ct_start; });
@@ -278,7 +281,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
     n0 = nt * NT;
     RB = a.B_pad;
     rb0 = n0;
-    if (EPI == EPI_FWD) {
+    if (fwdA) {
       m0 = (gt - gr.mt_start * SUB) * MT;
       kst = (gr.N + K_PAD - 1) / K_PAD * K_PAD / KT;
       Ab = a.opA + bl.th_off;
@@ -297,7 +300,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
     kend = (split + 1) * kst / S;
     // a tile wholly in the group's row padding has no output (every split of
     // it leaves here, so its arrival counter is never touched)
-    if (m0 >= (EPI == EPI_FWD ? gr.M : gr.N)) return;
+    if (m0 >= (fwdA ? gr.M : gr.N)) return;
   } else {
     // tile prefix of the block sequence: 256 x 256 tiles, twice as many
     // 128 x 256 tiles (blocks are padded to 256 both ways), or 128 x 128
@@ -559,6 +562,28 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
     if (tid == 0) __hip_atomic_store(a.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
+  if constexpr (EPI == EPI_VSTORE) {
+    // straight from the accumulators: register r of lane l holds row
+    // (r/4)*8 + (l/32)*4 + r%4 and column l%32 of its 32 x 32 block; output
+    // (row, q') to [b][row][r] of the q' < Q or the q' >= Q half
+    const int rows = fwdA ? gr.M : gr.N;
+    const int kr = a.vs_rank, Q = a.vs_half;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          const int q2 = n0 + wn0 + j * 32 + (lane & 31);
+          if (row >= rows || q2 >= 2 * Q) continue;
+          const int q = q2 < Q ? q2 : q2 - Q;
+          const int b = q / kr, rr = q - b * kr;
+          (q2 < Q ? a.vs_lo : a.vs_hi)[((int64_t)b * rows + row) * kr + rr] = acc[i][j][r];
+        }
+    return;
+  }
+
   // ---- epilogue ------------------------------------------------------------
   // accumulator register r of lane l holds row (r/4)*8 + (l/32)*4 + r%4 and
   // column l%32 of its 32 x 32 block.  The tile goes through LDS (free once
@@ -671,6 +696,12 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
             sv[c][0] = sv[c][1] = sv[c][2] = sv[c][3] = 0.0f;
           }
         }
+      } else if (!a.params) {
+        // no weights: F += P (the LowRank denominator statistic W)
+        ok = row < bl.M;
+        at[c] = (int64_t)row * bl.N + col;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[c][e] = 1.0f;
       } else {
         ok = row < bl.M;
         at[c] = (int64_t)row * bl.N + col;
@@ -830,8 +861,23 @@ static void launch_tile(int tile, int grid, const GemmArgs& a, hipStream_t s) {
   }
 }
 
+// virtual-batch stores: the automatic per-layer tiles only
+template <int PA, int PB>
+static void launch_vstore(int tile, int grid, const GemmArgs& a, hipStream_t s) {
+  if (tile == TILE_64x128) launch_shape<EPI_VSTORE, PA, PB, 64, 128, 2>(grid, a, s);
+  else launch_shape<EPI_VSTORE, PA, PB, 128, 64, (PA > PB ? 4 : 2)>(grid, a, s);
+}
+
 template <int EPI>
 static void launch_planes(int pa, int pb, int tile, int grid, const GemmArgs& a, hipStream_t s) {
+  if constexpr (EPI == EPI_VSTORE) {
+    if (pa == 1 && pb == 1) launch_vstore<1, 1>(tile, grid, a, s);
+    else if (pa == 2 && pb == 1) launch_vstore<2, 1>(tile, grid, a, s);
+    else if (pa == 1 && pb == 2) launch_vstore<1, 2>(tile, grid, a, s);
+    else if (pa == 2 && pb == 2) launch_vstore<2, 2>(tile, grid, a, s);
+    else launch_vstore<3, 3>(tile, grid, a, s);
+    return;
+  }
   if (pa == 1 && pb == 1) launch_tile<EPI, 1, 1>(tile, grid, a, s);
   else if (pa == 2 && pb == 1) launch_tile<EPI, 2, 1>(tile, grid, a, s);
   else if (pa == 1 && pb == 2) launch_tile<EPI, 1, 2>(tile, grid, a, s);
@@ -844,6 +890,7 @@ void launch_gemm(int epi, int pa, int pb, const GemmShape& sh, const GemmArgs& a
   const int grid = sh.tiles * (epi == EPI_PARAM ? 1 : sh.splitk);
   if (epi == EPI_FWD) launch_planes<EPI_FWD>(pa, pb, sh.tile, grid, a, s);
   else if (epi == EPI_ELEM) launch_planes<EPI_ELEM>(pa, pb, sh.tile, grid, a, s);
+  else if (epi == EPI_VSTORE) launch_planes<EPI_VSTORE>(pa, pb, sh.tile, grid, a, s);
   else launch_planes<EPI_PARAM>(pa, pb, sh.tile, grid, a, s);
 }
 

@@ -132,6 +132,8 @@ void upload_tables(Handle* h, int device) {
     sp.d_pg_group = upload(sp.pg_group);
   }
   h->d_blocks = upload(h->blocks);
+  h->d_vblocks = upload(h->vblocks);
+  h->d_vgroups = upload(h->vgroups);
   h->d_rowsegs = upload(h->rowsegs);
   h->d_zero = upload(h->zero_ranges);
   h->d_seed = upload(h->seed_ranges);
@@ -170,6 +172,8 @@ void free_tables(Handle* h) {
     release(sp.d_pg_group);
   }
   release(h->d_blocks);
+  release(h->d_vblocks);
+  release(h->d_vgroups);
   release(h->d_rowsegs);
   release(h->d_zero);
   release(h->d_seed);
@@ -186,7 +190,27 @@ GemmShape layer_gemm_shape(const Handle* h, const SumPlan& sp, int kind, int B_p
                      pb, h->opt_layer_tile, h->opt_split_max);
 }
 
+// The LowRank "sum_exp" virtual batch runs (no fused kernels asked for).
+bool vsum_active(const Handle* h) {
+  return h->lowrank_form == PC_LOWRANK_SUM_EXP && !h->vblocks.empty() && !h->opt_sumexp_fused;
+}
+
+// Shape of a virtual-batch product over one LowRank group: rows M (forward,
+// weights) or N (element side, transposed weights), Qpad virtual columns, K
+// the other dimension; the automatic tiles only.
+GemmShape vb_gemm_shape(const Handle* h, const GroupRec& r, bool elem, int Qpad, int pa, int pb) {
+  const int rows = elem ? r.N : r.M, K = elem ? r.M : r.N;
+  return layer_shape((int)(round_up(rows, ROW_PAD) / ROW_PAD), Qpad, (int)round_up(K, K_PAD), pa, pb, TILE_AUTO,
+                     h->opt_split_max);
+}
+
+GemmShape param_gemm_shape_tiles(const Handle* h, int pa, int pb, int tiles256, int tiles128);
+
 GemmShape param_gemm_shape(const Handle* h, int pa, int pb) {
+  return param_gemm_shape_tiles(h, pa, pb, h->param_tiles256, h->param_tiles128);
+}
+
+GemmShape param_gemm_shape_tiles(const Handle* h, int pa, int pb, int tiles256, int tiles128) {
   GemmShape g{};
   // Automatic: 128 x 256 when the first operand (G) has more planes than the
   // second, else 128 x 128: fewer bytes per output at the same K (HMM-4096
@@ -198,7 +222,7 @@ GemmShape param_gemm_shape(const Handle* h, int pa, int pb) {
   g.mt = big ? 256 : 128;
   g.nt = big || wide ? 256 : 128;
   g.splitk = 1;
-  g.tiles = big ? h->param_tiles256 : wide ? 2 * h->param_tiles256 : h->param_tiles128;
+  g.tiles = big ? tiles256 : wide ? 2 * tiles256 : tiles128;
   return g;
 }
 
@@ -255,6 +279,18 @@ WsPlan plan_workspace(const Handle* h, int B, bool fwd_only) {
         nct = std::max(nct, g.tiles);
       }
     }
+    if (vsum_active(h)) {
+      const int Qv = B * h->lowrank_rank;
+      const int nt = std::max(layer_tile_nt(p.pl[GK_FWD][0], p.pl[GK_FWD][1], TILE_AUTO),
+                              layer_tile_nt(p.pl[GK_ELEM][0], p.pl[GK_ELEM][1], TILE_AUTO));
+      const int Qpad = (int)round_up(2 * (int64_t)Qv, std::max(nt, 64));
+      for (const auto& r : h->vgroups)
+        for (int e = 0; e < 2; ++e) {
+          const GemmShape g = vb_gemm_shape(h, r, e == 1, Qpad, p.pl[e][0], p.pl[e][1]);
+          if (g.splitk > 1) pel = std::max<int64_t>(pel, (int64_t)g.tiles * g.splitk * g.mt * g.nt);
+          nct = std::max(nct, g.tiles);
+        }
+    }
     p.partial_elems = pel;
     p.ncounters = nct;
     p.partials = take((size_t)pel * 4);
@@ -272,17 +308,36 @@ WsPlan plan_workspace(const Handle* h, int B, bool fwd_only) {
   p.lrW = take(lr ? (size_t)h->lr_rows * Bs * kr * 4 : 0);
   p.lrC1 = take(lr ? bw * round_up(h->lr_max_m, 32) * Bs * 4 : 0);   // rows padded to 32 (zeros)
   p.lrC2 = take(lr ? bw * round_up(h->lr_max_m, 32) * Bs * 4 : 0);
-  p.lrP = take(lr ? bw * p.lr_nsg * h->lr_p_elems * 4 : 0);
-  p.lrPz = take(lr ? bw * p.lr_nsg * h->lr_p_elems * 4 : 0);
+  // the fused kernels' parameter-flow partials and fragment records (not
+  // used by the "sum_exp" virtual batch)
+  p.vsum = vsum_active(h);
+  const size_t fz = p.vsum ? 0 : 1;
+  p.lrP = take(lr ? fz * bw * p.lr_nsg * h->lr_p_elems * 4 : 0);
+  p.lrPz = take(lr ? fz * bw * p.lr_nsg * h->lr_p_elems * 4 : 0);
   {
     size_t pk = 0;
     for (const auto& sp : h->sums)
       for (const auto& r : sp.groups)
         if (r.lowrank >= 0) {
           p.lr_pk_off.push_back((int64_t)pk);
-          pk += (size_t)round_up(lr_pack_bytes(B, r.M, r.N, (int)kr, p.mode == PC_PREC_FP32), 256);
+          pk += fz * (size_t)round_up(lr_pack_bytes(B, r.M, r.N, (int)kr, p.mode == PC_PREC_FP32), 256);
         }
     p.lrPK = take(pk);
+  }
+  // "sum_exp" virtual batch: batch-major operand, node-major arenas, backward products
+  if (p.vsum) {
+    p.Qv = B * (int)kr;
+    p.QK = (int)round_up(p.Qv, K_PAD);
+    const int nt = std::max(layer_tile_nt(p.pl[GK_FWD][0], p.pl[GK_FWD][1], TILE_AUTO),
+                            layer_tile_nt(p.pl[GK_ELEM][0], p.pl[GK_ELEM][1], TILE_AUTO));
+    p.Qpad = (int)round_up(2 * (int64_t)p.Qv, std::max(nt, 64));
+    const size_t npb = (size_t)std::max(p.pl[GK_FWD][1], p.pl[GK_ELEM][1]);
+    p.vbt = take(npb * p.Qpad * h->v_max_k * 2);
+    p.vX = take(bw * p.pl[GK_PARAM][1] * h->vx_rows * p.QK * 2);
+    p.vC = take(bw * p.pl[GK_PARAM][1] * h->vx_rows * p.QK * 2);
+    p.vY1 = take(bw * p.pl[GK_PARAM][0] * h->vy_rows * p.QK * 2);
+    p.vY2 = take(bw * p.pl[GK_PARAM][0] * h->vy_rows * p.QK * 2);
+    p.vR = take(bw * 2 * (size_t)B * h->lr_max_n * kr * 4);
   }
   p.lowrank = lr0;
   p.lowrank_bytes = off - lr0;
@@ -486,6 +541,88 @@ void lr_pack_group(const Call& c, const SumPlan& sp, int g, const pc_lowrank_io*
   launch_lr_pack(pa, c.p.mode == PC_PREC_FP32, c.s);
 }
 
+// One LowRank group's virtual-batch arguments (forward: X / C operands;
+// backward: Y1 / Y2).
+VBArgs vb_args(const Call& c, const SumPlan& sp, int g, const pc_lowrank_io* io, float* vals, float* flows,
+               bool bwd) {
+  const Handle* h = c.h;
+  const GroupRec& r = sp.groups[g];
+  const GroupRec& vr = h->vgroups[sp.lr_gidx[g]];
+  char* base = (char*)c.ws;
+  const int64_t B = c.v.B, kr = h->lowrank_rank;
+  VBArgs a{};
+  a.B = c.v.B;
+  a.M = r.M;
+  a.N = r.N;
+  a.krank = h->lowrank_rank;
+  a.Q = c.p.Qv;
+  a.Qpad = c.p.Qpad;
+  a.QK = c.p.QK;
+  a.out_start = r.out_start;
+  a.m_row = r.m_row;
+  a.cbs = r.cbs;
+  a.blk_off = r.blk_off;
+  a.scratch_row = r.scratch_row;
+  a.store = sp.store ? 1 : 0;
+  a.chblocks = sp.d_blocks;
+  a.A = io->A[r.lowrank];
+  a.Bf = io->B[r.lowrank];
+  a.mkeys = c.v.mkeys;
+  a.vals = vals;
+  a.out_flows = flows;
+  a.scratch = c.v.scratch;
+  a.vbt = (uint16_t*)(base + c.p.vbt);
+  a.vbt_plane = (int64_t)c.p.Qpad * h->v_max_k;
+  a.np_bt = c.p.pl[bwd ? GK_ELEM : GK_FWD][1];
+  const int npn = c.p.pl[GK_PARAM][bwd ? 0 : 1];
+  a.np_n = c.p.fwd_only ? 0 : npn;
+  a.nlo = (uint16_t*)(base + (bwd ? c.p.vY1 : c.p.vX));
+  a.nhi = (uint16_t*)(base + (bwd ? c.p.vY2 : c.p.vC));
+  a.n_rows = bwd ? h->vy_rows : h->vx_rows;
+  a.n_plane = a.n_rows * c.p.QK;
+  a.n_row0 = bwd ? vr.g_row : vr.e_row;
+  a.C1 = (const float*)(base + c.p.lrC1);
+  a.C2 = (const float*)(base + c.p.lrC2);
+  a.Z = (float*)(base + c.p.lrZ) + sp.lr_row[g] * B;
+  a.S = (float*)(base + c.p.lrS) + sp.lr_row[g] * B;
+  a.U = (const float*)(base + c.p.lrU) + sp.lr_row[g] * B * kr;
+  a.W = (const float*)(base + c.p.lrW) + sp.lr_row[g] * B * kr;
+  a.R1 = (const float*)(base + c.p.vR);
+  a.R2 = (const float*)(base + c.p.vR) + (size_t)B * h->lr_max_n * kr;
+  if (io->dB) a.dB = io->dB[r.lowrank];
+  return a;
+}
+
+// The virtual-batch product of one LowRank group: weights (forward) or
+// transposed weights (backward) times the batch-major operand, stored to
+// lo / hi in [B, rows, k].
+void vb_product(const Call& c, const SumPlan& sp, int g, bool elem, float* lo, float* hi) {
+  const Handle* h = c.h;
+  const int gi = sp.lr_gidx[g];
+  const GroupRec& vr = h->vgroups[gi];
+  const int kind = elem ? GK_ELEM : GK_FWD;
+  const int pa = c.p.pl[kind][0], pb = c.p.pl[kind][1];
+  GemmArgs a = gemm_common(c);
+  a.B = 2 * c.p.Qv;
+  a.B_pad = c.p.Qpad;
+  a.ngroups = 1;
+  a.groups = h->d_vgroups + gi;
+  a.blocks = h->d_vblocks;
+  a.opA = elem ? c.v.thetaT : c.v.theta;
+  a.planeA = elem ? c.v.thetaT_plane : c.v.theta_plane;
+  a.opB = (const uint16_t*)((const char*)c.ws + c.p.vbt);
+  a.planeB = (int64_t)c.p.Qpad * h->v_max_k;
+  a.vs_elem = elem ? 1 : 0;
+  a.vs_rank = h->lowrank_rank;
+  a.vs_half = c.p.Qv;
+  a.vs_lo = lo;
+  a.vs_hi = hi;
+  const GemmShape shp = vb_gemm_shape(h, vr, elem, c.p.Qpad, pa, pb);
+  a.ntiles = c.p.Qpad / shp.nt;
+  a.splitk = shp.splitk;
+  launch_gemm(EPI_VSTORE, pa, pb, shp, a, c.s);
+}
+
 ProdArgs prod_args(const Call& c, const ProductPlan& pp) {
   ProdArgs a{};
   a.B = c.v.B;
@@ -579,6 +716,21 @@ void run_forward(const Call& c, const int32_t* tokens, const float* params, floa
     Timed t(h, KK_SPLIT, c.s);
     launch_theta_pack(ta, h->pk_block_tiles, c.s);
   }
+  if (p.vsum) {
+    // weight planes of the LowRank "sum_exp" blocks (virtual-batch products)
+    ThetaArgs ta{};
+    ta.nblocks = (int)h->vblocks.size();
+    ta.np_fwd = p.pl[GK_FWD][0];
+    ta.np_elem = p.fwd_only ? 0 : p.pl[GK_ELEM][0];
+    ta.blocks = h->d_vblocks;
+    ta.params = params;
+    ta.theta = v.theta;
+    ta.theta_plane = v.theta_plane;
+    ta.thetaT = v.thetaT;
+    ta.thetaT_plane = v.thetaT_plane;
+    Timed t(h, KK_SPLIT, c.s);
+    launch_theta_pack(ta, h->v_pk_tiles, c.s);
+  }
   if (!h->inputs.empty()) {
     Timed t(h, KK_OTHER, c.s);
     launch_tokens_t(tokens, v.tokT, B, h->num_vars, c.s);
@@ -591,7 +743,7 @@ void run_forward(const Call& c, const int32_t* tokens, const float* params, floa
     Timed t(h, KK_OTHER, c.s);
     launch_fill_u32(v.counters, p.ncounters, 0u, c.s);
   }
-  if (h->lowrank_slots > 0 && h->opt_lr_pack == 0) {
+  if (h->lowrank_slots > 0 && h->opt_lr_pack == 0 && !p.vsum) {
     // the fragment records of every LowRank group's factors, kept for the backward
     LRPackArgs pa{};
     pa.B = B;
@@ -661,6 +813,22 @@ void run_forward(const Call& c, const int32_t* tokens, const float* params, floa
       a.fp_on = 0;
       if (sp.lowrank) {
         for (int gi = 0; gi < (int)sp.groups.size(); ++gi) {
+          if (p.vsum) {
+            // "sum_exp" on the virtual batch: X, C operands; theta [X | C]^T
+            // into U, W; the rank reduction and the node values
+            VBArgs va = vb_args(c, sp, gi, lowrank, node_vals, nullptr, false);
+            {
+              Timed t(h, KK_EXP, c.s);
+              launch_vb_fwd_pack(va, c.s);
+            }
+            {
+              Timed t(h, KK_FWD, c.s);
+              vb_product(c, sp, gi, false, const_cast<float*>(va.U), const_cast<float*>(va.W));
+            }
+            Timed t(h, KK_LRFWD, c.s);
+            launch_vb_fwd_reduce(va, c.s);
+            continue;
+          }
           LRArgs la = lr_args(c, sp, gi, lowrank, params, node_vals, nullptr);
           if (h->opt_lr_pack == 1) {
             Timed t(h, KK_SPLIT, c.s);
@@ -827,6 +995,9 @@ int pc_set_option(pc_handle hh, int option, int value) {
     } else if (option == PC_OPT_FUSE) {
       if (value != 0 && value != 1) fail(PC_ERR_INVALID_ARG, "fuse must be 0 or 1");
       h->opt_fuse = value;
+    } else if (option == PC_OPT_SUMEXP_FUSED) {
+      if (value != 0 && value != 1) fail(PC_ERR_INVALID_ARG, "sumexp_fused must be 0 or 1");
+      h->opt_sumexp_fused = value;
     } else {
       fail(PC_ERR_INVALID_ARG, "unknown option");
     }
@@ -946,7 +1117,7 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
     }
     // LowRank denominator statistic W of the conditional M-step (on request)
     const bool zstat = h->lowrank_slots > 0 && lowrank && lowrank->z_flows;
-    if (h->lowrank_slots > 0) {
+    if (h->lowrank_slots > 0 && !p.vsum) {
       Timed t(h, KK_OTHER, c.s);
       launch_fill_u32((uint32_t*)((char*)c.ws + p.lrP), (int64_t)p.lr_nsg * h->lr_p_elems, 0u, c.s);
       if (zstat) launch_fill_u32((uint32_t*)((char*)c.ws + p.lrPz), (int64_t)p.lr_nsg * h->lr_p_elems, 0u, c.s);
@@ -1039,6 +1210,26 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
             la.fp_on = 1;
             la.fp_pstart = pp.node_start;
             la.fp_other = pp.abase[1 - sp.lr_qs];
+          }
+          if (p.vsum) {
+            // "sum_exp" on the virtual batch: c1, c2 and dA; Y1, Y2 operands;
+            // theta^T [Y1 | Y2]^T; child flows and dB
+            {
+              Timed t(h, KK_LRBWD, c.s);
+              launch_lr_coef(la, c.s);
+            }
+            VBArgs vb = vb_args(c, sp, gi, lowrank, vals, node_flows, true);
+            {
+              Timed t(h, KK_GPACK, c.s);
+              launch_vb_bwd_pack(vb, c.s);
+            }
+            {
+              Timed t(h, KK_ELEM, c.s);
+              vb_product(c, sp, gi, true, const_cast<float*>(vb.R1), const_cast<float*>(vb.R2));
+            }
+            Timed t(h, KK_LRBWD, c.s);
+            launch_vb_bwd_reduce(vb, c.s);
+            continue;
           }
           if (h->opt_lr_pack == 1) {
             Timed t(h, KK_SPLIT, c.s);
@@ -1166,7 +1357,38 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
         launch_input_bwd(a, c.s);
       }
     }
-    for (size_t bi = 0; bi < h->blocks.size(); ++bi) {
+    if (p.vsum) {
+      // F+ = theta * (Y1 X^T) and W = Y2 C^T over every (copy, sample, rank)
+      // of each LowRank block, one product each
+      GemmArgs pv = gemm_common(c);
+      pv.B_padK = p.QK;
+      pv.rowsA = h->vy_rows;
+      pv.rowsB = h->vx_rows;
+      pv.blocks = h->d_vblocks;
+      pv.ngroups = (int)h->vblocks.size();
+      pv.opA = (const uint16_t*)((char*)c.ws + p.vY1);
+      pv.planeA = h->vy_rows * p.QK;
+      pv.opB = (const uint16_t*)((char*)c.ws + p.vX);
+      pv.planeB = h->vx_rows * p.QK;
+      pv.params = params;
+      pv.pflows = param_flows;
+      pv.splitk = 1;
+      const GemmShape vshp = param_gemm_shape_tiles(h, p.pl[GK_PARAM][0], p.pl[GK_PARAM][1], h->v_param_tiles256,
+                                                    h->v_param_tiles128);
+      {
+        Timed t(h, KK_PARAM, c.s);
+        launch_gemm(EPI_PARAM, p.pl[GK_PARAM][0], p.pl[GK_PARAM][1], vshp, pv, c.s);
+      }
+      if (zstat) {
+        pv.opA = (const uint16_t*)((char*)c.ws + p.vY2);
+        pv.opB = (const uint16_t*)((char*)c.ws + p.vC);
+        pv.params = nullptr;                 // no weights: W
+        pv.pflows = lowrank->z_flows;
+        Timed t(h, KK_PARAM, c.s);
+        launch_gemm(EPI_PARAM, p.pl[GK_PARAM][0], p.pl[GK_PARAM][1], vshp, pv, c.s);
+      }
+    }
+    for (size_t bi = 0; bi < h->blocks.size() && !p.vsum; ++bi) {
       if (h->lr_p_off[bi] < 0) continue;
       const BlockRec& bl = h->blocks[bi];
       Timed t(h, KK_LRBWD, c.s);

@@ -457,6 +457,92 @@ Handle* compile_layout(const pc_circuit_desc* d) {
     }
   }
 
+  // LowRank "sum_exp" on a virtual batch (pyjuice.parameterizations.LowRank,
+  // definition: sum_exp "is k matmuls with the shared parameters"): a block
+  // record per distinct LowRank weight block, placed after the plain blocks
+  // in the weight-plane arenas, with its copies' node-major operand rows and
+  // its own parameter-flow tile prefixes; a group record per LowRank group.
+  if (h->lowrank_form == PC_LOWRANK_SUM_EXP && h->lr_groups > 0) {
+    std::map<int32_t, int> vid;                       // block -> virtual block
+    std::vector<std::vector<std::pair<int, int>>> per;  // virtual block -> (sum layer, group)
+    h->vgroups.assign(h->lr_groups, GroupRec{});
+    for (int si = 0; si < (int)h->sums.size(); ++si) {
+      SumPlan& sp = h->sums[si];
+      if (!sp.lowrank) continue;
+      for (int g = 0; g < (int)sp.groups.size(); ++g) {
+        const GroupRec& r = sp.groups[g];
+        auto it = vid.find(r.block);
+        if (it == vid.end()) {
+          it = vid.emplace(r.block, (int)h->vblocks.size()).first;
+          BlockRec b{};
+          b.param_offset = h->blocks[r.block].param_offset;
+          b.M = r.M;
+          b.N = r.N;
+          h->vblocks.push_back(b);
+          per.emplace_back();
+        }
+        per[it->second].push_back({si, g});
+      }
+    }
+    int64_t th = h->theta_elems, tht = h->thetaT_elems, xr = 0, yr = 0;
+    int32_t pk = 0, p256 = 0, p128 = 0;
+    h->vcopy_layer.assign(h->vblocks.size(), {});
+    for (size_t v = 0; v < h->vblocks.size(); ++v) {
+      BlockRec& B = h->vblocks[v];
+      const int64_t Mp = round_up(B.M, ROW_PAD), Np = round_up(B.N, ROW_PAD);
+      const int64_t MpK = round_up(B.M, K_PAD), NpK = round_up(B.N, K_PAD);
+      B.ncopies = (int32_t)per[v].size();
+      B.g_base = yr;
+      B.e_base = xr;
+      B.th_off = th;
+      th += Mp * NpK;
+      B.tht_off = tht;
+      tht += Np * MpK;
+      B.pk_start = pk;
+      pk += (int32_t)((Mp / 64) * (Np / 64));
+      B.pt256 = p256;
+      p256 += (int32_t)((Mp / 256) * (Np / 256));
+      B.pt128 = p128;
+      p128 += (int32_t)((Mp / 128) * (Np / 128));
+      for (int c = 0; c < B.ncopies; ++c) {
+        const SumPlan& sp = h->sums[per[v][c].first];
+        const GroupRec& r = sp.groups[per[v][c].second];
+        GroupRec q{};
+        q.out_start = r.out_start;
+        q.M = r.M;
+        q.N = r.N;
+        q.cbs = r.cbs;
+        q.blk_off = r.blk_off;
+        q.nblk = r.nblk;
+        q.param_offset = r.param_offset;
+        q.block = (int32_t)v;
+        q.m_row = r.m_row;
+        q.mt_start = q.ct_start = q.pk_start = q.pg_start = 0;
+        q.e_koff = q.g_koff = 0;
+        q.e_row = xr + c * Np;
+        q.g_row = yr + c * Mp;
+        q.scratch_row = r.scratch_row;
+        q.lowrank = r.lowrank;
+        q.share_src = 0;
+        q.share_next = -1;
+        q.ch_start = r.ch_start;
+        q.s_row = -1;
+        h->vgroups[sp.lr_gidx[per[v][c].second]] = q;
+        h->vcopy_layer[v].push_back(sp.layer);
+        h->v_max_k = std::max<int32_t>(h->v_max_k, (int32_t)std::max(MpK, NpK));
+      }
+      xr += B.ncopies * Np;
+      yr += B.ncopies * Mp;
+    }
+    h->theta_elems = th;
+    h->thetaT_elems = tht;
+    h->v_pk_tiles = pk;
+    h->v_param_tiles256 = p256;
+    h->v_param_tiles128 = p128;
+    h->vx_rows = xr;
+    h->vy_rows = yr;
+  }
+
   // EM row segments: every distinct block and input table
   {
     std::map<int64_t, RowSeg> segs;

@@ -167,6 +167,43 @@ void launch_lr_bwd(const LRArgs& a, int fp32, hipStream_t s);
 void launch_lr_zstat(const LRArgs& a, int fp32, hipStream_t s);
 void launch_lr_fplus(const float* P, int nsg, int64_t elems, float* pflows, hipStream_t s);
 
+// One LowRank "sum_exp" group on the virtual batch (k_vbatch.hip): Q = B k
+// virtual columns q = b k + r; the batch-major operand vbt has Qpad rows
+// (rows [0, Q) and [Q, 2Q) the two halves) and the node-major arenas
+// nlo / nhi (X / C forward, Y1 / Y2 backward) rows n_row0 + node of n_rows,
+// K = q padded to QK; np_bt / np_n bfloat16 planes (np_n = 0: not kept).
+struct VBArgs {
+  int32_t B, M, N, krank, Q, Qpad, QK;
+  int32_t out_start, m_row, cbs, blk_off, scratch_row, store;
+  const int32_t* chblocks;
+  const float* A;          // [B, M, k]
+  const float* Bf;         // [B, k, N]
+  const uint32_t* mkeys;
+  float* vals;
+  float* out_flows;
+  float* scratch;
+  uint16_t* vbt;
+  int64_t vbt_plane;
+  int32_t np_bt;
+  uint16_t* nlo;
+  uint16_t* nhi;
+  int64_t n_plane, n_rows, n_row0;
+  int32_t np_n;
+  const float* C1;         // [B, M rounded up to 32] f / S, f / Z
+  const float* C2;
+  float* S;                // [B, M]
+  float* Z;
+  const float* U;          // [B, M, k] theta X^T, theta C^T (kept: the coefficient kernel's U, W)
+  const float* W;
+  const float* R1;         // [B, N, k] theta^T Y1^T, theta^T Y2^T
+  const float* R2;
+  float* dB;               // [B, k, N]
+};
+void launch_vb_fwd_pack(const VBArgs& a, hipStream_t s);
+void launch_vb_fwd_reduce(const VBArgs& a, hipStream_t s);
+void launch_vb_bwd_pack(const VBArgs& a, hipStream_t s);
+void launch_vb_bwd_reduce(const VBArgs& a, hipStream_t s);
+
 void launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
 void launch_fill_ranges(float* flows, const FillRange* d_ranges, int nranges, int64_t max_count, int B,
                         hipStream_t s);

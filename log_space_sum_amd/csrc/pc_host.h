@@ -170,6 +170,22 @@ struct Handle {
   int32_t lr_groups = 0;               // LowRank: number of LowRank groups
   int64_t lr_p_elems = 0;              // LowRank: elements of the distinct LowRank weight blocks
   std::vector<int64_t> lr_p_off;       // per weight block: offset of its LowRank partials, -1 if none
+  // LowRank "sum_exp" on a virtual batch (used unless opt_sumexp_fused):
+  // one block record per distinct LowRank weight block, with its weight
+  // planes after the plain blocks' (th_off, tht_off), the node-major rows of
+  // its copies' virtual operands (X = exp(B) e and C = exp(B) at e_base +
+  // copy * N_pad; Y1 = exp(A) c1 and Y2 = exp(A) c2 at g_base + copy * M_pad)
+  // and its parameter-flow tile prefixes; and one group record per LowRank
+  // group (index lr_gidx): that copy's block and operand rows.
+  std::vector<BlockRec> vblocks;
+  std::vector<GroupRec> vgroups;
+  std::vector<std::vector<int32_t>> vcopy_layer;   // per virtual block: the layer of each copy
+  int32_t v_pk_tiles = 0, v_param_tiles256 = 0, v_param_tiles128 = 0;
+  int64_t vx_rows = 0, vy_rows = 0;                // node-major rows of the X / C and Y1 / Y2 arenas
+  int32_t v_max_k = 0;                             // widest contraction of the two per-layer products
+  int opt_sumexp_fused = 0;                        // 1: "sum_exp" through the fused LowRank kernels
+  BlockRec* d_vblocks = nullptr;
+  GroupRec* d_vgroups = nullptr;
   std::vector<RowSeg> rowsegs;
   int32_t total_rows = 0;
   std::vector<int32_t> outputs;
@@ -218,6 +234,13 @@ struct WsPlan {
   size_t lrE, lrZ, lrS, lrU, lrW, lrC1, lrC2, lrP;   // LowRank regions (float32)
   size_t lrPz;                                       // partials of the denominator statistic W
   size_t lrPK;                                       // LowRank fragment records of every LowRank group
+  // LowRank "sum_exp" virtual batch: the batch-major operand of the layer's two
+  // products ([Qpad rows = 2 B k padded, K] per plane), the node-major X, C, Y1,
+  // Y2 arenas ([rows, QK = B k padded to 64] per plane), the backward's
+  // products R1, R2 ([B, N, k] float32 each)
+  bool vsum;
+  int32_t Qv, Qpad, QK;
+  size_t vbt, vX, vC, vY1, vY2, vR;
   std::vector<int64_t> lr_pk_off;                    // per LowRank group: byte offset of its records
   int lr_nsg;                                        // LowRank parameter-flow partials: ceil(B/8)
   size_t partials, counters;

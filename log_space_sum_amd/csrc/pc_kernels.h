@@ -6,7 +6,7 @@
 
 namespace pc {
 
-enum Epi { EPI_FWD = 0, EPI_ELEM = 1, EPI_PARAM = 2 };
+enum Epi { EPI_FWD = 0, EPI_ELEM = 1, EPI_PARAM = 2, EPI_VSTORE = 3 };
 
 // Arguments of the MFMA product kernel (see k_gemm.hip).
 struct GemmArgs {
@@ -54,6 +54,15 @@ struct GemmArgs {
   int64_t gp_s_row, gp_g_row, gp_direct_rows, gp_direct_plane, gp_trans_plane;
   uint16_t* gp_direct;
   uint16_t* gp_trans;
+  // plain-store products of the LowRank "sum_exp" virtual batch (EPI_VSTORE):
+  // the one group's weights (vs_elem 0: theta, rows M, K = N; 1: theta^T,
+  // rows N, K = M) times the batch-major operand whose B (= 2 Q) rows are the
+  // virtual columns q' = b * k + r (q' < Q) and Q + b * k + r; output (row,
+  // q') goes to vs_lo (q' < Q) or vs_hi at [b][row][r] (rows of the product,
+  // rank vs_rank)
+  int32_t vs_elem, vs_rank, vs_half;
+  float* vs_lo;
+  float* vs_hi;
 };
 
 // Output tile shapes of the product kernel (M x N per workgroup).

@@ -21,13 +21,13 @@ def _gpu():
     L.lib()
 
 
-def _lowrank_full(cfg, mode, what):
+def _lowrank_full(cfg, mode, what, options=None):
     """Values and log-likelihood end to end; values, element flows, parameter
     flows, dLL/dA and dLL/dB per layer (recomputed by the oracle from each
     layer's GPU inputs); flows end to end at gpu_util.e2e_flow_tol (the stated
     tolerance in auto mode; plus the float32-storage term at fp32 level)."""
     G.say(f"case {what} mode={mode} B={cfg['B']}")
-    gpu = G.run_gpu(cfg, mode)
+    gpu = G.run_gpu(cfg, mode, options=options)
     orc = G.run_oracle(cfg)
     G.check_values(gpu["vals"], orc["vals"], mode, f"{what} node values")
     G.check_values(gpu["ll"], orc["ll"], mode, f"{what} log-likelihood")
@@ -98,21 +98,35 @@ def test_lowrank_z_correction(mode, H, T, V, rank, B, spread):
     (96, 3, 9, 32, 24, 4.0),      # rank 32 (two K steps), 4-nat spread
     (80, 3, 7, 64, 19, 1.0),      # rank 64
 ])
-def test_lowrank_sum_exp(mode, H, T, V, rank, B, spread):
+@pytest.mark.parametrize("path", ["virtual", "fused"])
+def test_lowrank_sum_exp(mode, H, T, V, rank, B, spread, path):
     """The "sum_exp" form (g_b[i, j] = sum_r exp(A_b[i, r]) exp(B_b[r, j])):
-    the same checks as the exp_sum form."""
+    the same checks as the exp_sum form, through the products with the
+    shared weights on the virtual batch (default) and the fused kernels."""
     cfg = make_config("lowrank", H=H, T=T, V=V, rank=rank, B=B, spread=spread, form="sum_exp")
-    _lowrank_full(cfg, mode, f"lowrank sum_exp H{H} T{T} r{rank} s{spread}")
+    _lowrank_full(cfg, mode, f"lowrank sum_exp ({path}) H{H} T{T} r{rank} s{spread}",
+                  options=[("sumexp_fused", 1 if path == "fused" else 0)])
 
 
-def test_lowrank_sum_exp_z_correction():
-    """W and the conditional M-step under the "sum_exp" form (auto)."""
+@pytest.mark.parametrize("mode", ["auto", "fp32"])
+def test_lowrank_sum_exp_virtual_mid_size(mode):
+    """The virtual batch at 256 states and 64 samples of rank 16 (1024 virtual
+    columns, several column tiles of both products)."""
+    cfg = make_config("lowrank", H=256, T=6, V=32, rank=16, B=64, spread=1.0, form="sum_exp")
+    _lowrank_full(cfg, mode, "lowrank sum_exp (virtual) H256 T6 r16")
+
+
+@pytest.mark.parametrize("path", ["virtual", "fused"])
+def test_lowrank_sum_exp_z_correction(path):
+    """W and the conditional M-step under the "sum_exp" form (auto), W added
+    to what the buffer held."""
     import oracle
     cfg = make_config("lowrank", H=64, T=4, V=9, rank=16, B=29, spread=1.0, form="sum_exp")
     circ = cfg["circuit"]
-    what = "lowrank sum_exp z-correction"
+    what = f"lowrank sum_exp ({path}) z-correction"
     G.say(f"case {what} mode=auto B={cfg['B']}")
-    gpu = G.run_gpu(cfg, "auto", z_init=np.zeros(circ.num_params, np.float32), em_corrected=(1.0, 0.0))
+    gpu = G.run_gpu(cfg, "auto", z_init=np.zeros(circ.num_params, np.float32), em_corrected=(1.0, 0.0),
+                    options=[("sumexp_fused", 1 if path == "fused" else 0)])
     orc = G.run_oracle(cfg)
     inside = np.zeros(circ.num_params, bool)
     for off, n in oracle.lowrank_param_ranges(circ):
