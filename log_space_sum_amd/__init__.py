@@ -97,19 +97,44 @@ class PCError(RuntimeError):
         self.code = code
 
 
+def load_library(path: str):
+    """A build of the library at `path`, its calls typed (does not make it
+    the one the binding uses; see using_library)."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m log_space_sum_amd.build`")
+    L = C.CDLL(path)
+    for name, (res, args) in EXPORTS.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    return L
+
+
 def lib():
     """The loaded libpc.so (raises if it has not been built)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m log_space_sum_amd.build`")
-        L = C.CDLL(LIB_PATH)
-        for name, (res, args) in EXPORTS.items():
-            f = getattr(L, name)
-            f.restype = res
-            f.argtypes = args
-        _lib = L
+        _lib = load_library(LIB_PATH)
     return _lib
+
+
+class using_library:
+    """Context in which the binding's calls go to another build of the
+    library (loaded with load_library; handles compiled meanwhile keep it)."""
+
+    def __init__(self, path: str):
+        self.other = load_library(path)
+
+    def __enter__(self):
+        global _lib
+        self.saved = lib()
+        _lib = self.other
+        return self.other
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.saved
+        return False
 
 
 def _check(code):
@@ -135,14 +160,15 @@ class Handle:
 
     def __init__(self, ptr, circuit):
         self.ptr = ptr
+        self.lib = lib()             # the build that made it frees it
         self.num_nodes = circuit.num_nodes
         self.num_params = circuit.num_params
         self.num_vars = circuit.num_vars
         self.root = circuit.root
 
     def __del__(self):
-        if getattr(self, "ptr", None) and _lib is not None:
-            _lib.pc_destroy(self.ptr)
+        if getattr(self, "ptr", None) and getattr(self, "lib", None) is not None:
+            self.lib.pc_destroy(self.ptr)
             self.ptr = None
 
 

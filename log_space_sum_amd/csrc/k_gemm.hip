@@ -250,13 +250,12 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
 
   // ---- locate the problem, the tile and the K range ------------------------
-  int S = 1, split = 0, tile = logical;
-  if (EPI == EPI_PARAM) tile += a.tile0;
-  if (EPI != EPI_PARAM) {
-    S = a.splitk;
-    tile = logical / S;
-    split = logical - tile * S;
-  }
+  // splitk workgroups share one tile's K range (the parameter-flow product's
+  // K is every tied copy's samples; its tiles count from tile0)
+  const int S = a.splitk;
+  const int ltile = logical / S;               // the launch's tile (split-K partials, arrival counters)
+  const int split = logical - ltile * S;
+  const int tile = EPI == EPI_PARAM ? ltile + a.tile0 : ltile;
   // the forward's operand layout: weights [M rows, K = N] (forward products,
   // and virtual-batch stores with vs_elem == 0); else the transposed weights
   const bool fwdA = EPI == EPI_FWD || (EPI == EPI_VSTORE && !a.vs_elem);
@@ -328,8 +327,9 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
     {
       const int c0 = a.copy_lo < bl.ncopies ? a.copy_lo : bl.ncopies;
       const int c1 = a.copy_hi < bl.ncopies ? a.copy_hi : bl.ncopies;
-      kbeg = c0 * kst;
-      kend = (c1 > c0 ? c1 : c0) * kst;
+      const int tot = (c1 > c0 ? c1 - c0 : 0) * kst;      // K slices of the copies
+      kbeg = c0 * kst + (int)((int64_t)split * tot / S);
+      kend = c0 * kst + (int)((int64_t)(split + 1) * tot / S);
     }
     Ab = a.opA;
     Bb = a.opB;
@@ -510,8 +510,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
   // to the device coherence point, so no cache-wide write-back is needed),
   // completed (vmcnt 0) before the arrival counter moves; the last arrival
   // reads every partial back with device-scope atomic loads, in split order.
-  if (EPI != EPI_PARAM && S > 1) {
-    float* mine = a.partials + ((int64_t)tile * S + split) * (NREG * 256);
+  if (S > 1) {
+    float* mine = a.partials + ((int64_t)ltile * S + split) * (NREG * 256);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -523,11 +523,11 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0)
-      last_flag = (__hip_atomic_fetch_add(a.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+      last_flag = (__hip_atomic_fetch_add(a.counters + ltile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                    (unsigned)(S - 1));
     __syncthreads();
     if (!last_flag) return;
-    const float* base = a.partials + (int64_t)tile * S * (NREG * 256);
+    const float* base = a.partials + (int64_t)ltile * S * (NREG * 256);
     // in chunks of CH registers over all SM >= S splits (about 128 values
     // per lane): every load of a chunk in flight at once, then the splits
     // added in order
@@ -559,7 +559,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
     if (S <= 2) reduce(std::integral_constant<int, 64>(), std::integral_constant<int, 2>());
     else if (S <= 4) reduce(std::integral_constant<int, 32>(), std::integral_constant<int, 4>());
     else reduce(std::integral_constant<int, 16>(), std::integral_constant<int, 8>());
-    if (tid == 0) __hip_atomic_store(a.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_store(a.counters + ltile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   if constexpr (EPI == EPI_VSTORE) {
@@ -887,7 +887,7 @@ static void launch_planes(int pa, int pb, int tile, int grid, const GemmArgs& a,
 
 void launch_gemm(int epi, int pa, int pb, const GemmShape& sh, const GemmArgs& a, hipStream_t s) {
   if (sh.tiles <= 0) return;
-  const int grid = sh.tiles * (epi == EPI_PARAM ? 1 : sh.splitk);
+  const int grid = sh.tiles * sh.splitk;
   if (epi == EPI_FWD) launch_planes<EPI_FWD>(pa, pb, sh.tile, grid, a, s);
   else if (epi == EPI_ELEM) launch_planes<EPI_ELEM>(pa, pb, sh.tile, grid, a, s);
   else if (epi == EPI_VSTORE) launch_planes<EPI_VSTORE>(pa, pb, sh.tile, grid, a, s);

@@ -128,23 +128,42 @@ __global__ __launch_bounds__(512) void k_vb_fwd_pack(VBArgs a) {
   }
 }
 
-// Forward reduction over the rank, one (sample, node) per thread:
-// Sraw = sum_r a Tx, Z = sum_r a Tc (Tx, Tc stored as U, W [B, M, k]),
-// v = m + log(Sraw / Z) (-inf unless both are positive).
+// Forward reduction over the rank, four lanes per (sample, node), lane l of
+// the four taking ranks 4l .. 4l + 3 (+ 16 t): Sraw = sum_r a Tx, Z = sum_r a
+// Tc (Tx, Tc stored as U, W [B, M, k]), v = m + log(Sraw / Z) (-inf unless
+// both are positive).  The four lanes' sums are added in a fixed order.
 __global__ __launch_bounds__(256) void k_vb_fwd_reduce(VBArgs a) {
-  const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (x >= (int64_t)a.B * a.M) return;
-  const int b = (int)(x / a.M), i = (int)(x - (int64_t)b * a.M);
+  const int64_t x = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 2;
+  const int l = threadIdx.x & 3;
+  const bool live = x < (int64_t)a.B * a.M;
   const int kr = a.krank;
-  const float* Ar = a.A + x * kr;
-  const float* Ur = a.U + x * kr;
-  const float* Wr = a.W + x * kr;
   float S = 0.0f, Z = 0.0f;
-  for (int r = 0; r < kr; ++r) {
-    const float av = expf(Ar[r]);
-    S += av * Ur[r];
-    Z += av * Wr[r];
+  if (live) {
+    const float* Ar = a.A + x * kr;
+    const float* Ur = a.U + x * kr;
+    const float* Wr = a.W + x * kr;
+    for (int r0 = 4 * l; r0 < kr; r0 += 16) {
+      if ((kr & 3) == 0) {
+        const float4 av = *(const float4*)(Ar + r0), uv = *(const float4*)(Ur + r0), wv = *(const float4*)(Wr + r0);
+        const float e0 = expf(av.x), e1 = expf(av.y), e2 = expf(av.z), e3 = expf(av.w);
+        S += e0 * uv.x + e1 * uv.y + e2 * uv.z + e3 * uv.w;
+        Z += e0 * wv.x + e1 * wv.y + e2 * wv.z + e3 * wv.w;
+      } else {
+        for (int r = r0; r < r0 + 4 && r < kr; ++r) {
+          const float e = expf(Ar[r]);
+          S += e * Ur[r];
+          Z += e * Wr[r];
+        }
+      }
+    }
   }
+  // lanes 0..3 of the row: (0 + 1) + (2 + 3)
+  S += __shfl_xor(S, 1);
+  Z += __shfl_xor(Z, 1);
+  S += __shfl_xor(S, 2);
+  Z += __shfl_xor(Z, 2);
+  if (!live || l != 0) return;
+  const int b = (int)(x / a.M), i = (int)(x - (int64_t)b * a.M);
   a.S[x] = S;
   a.Z[x] = Z;
   const float sh = key_shift_vb(a.mkeys[(int64_t)a.m_row * a.B + b]);
@@ -203,27 +222,52 @@ __global__ __launch_bounds__(512) void k_vb_bwd_pack(VBArgs a) {
   }
 }
 
-// Backward reduction over the rank, one (sample, child) per thread: the child
-// flow e sum_r c R1 (stored, added, or into the layer's scratch rows when
-// several groups share children) and dLL/dB_b[r, j] = c (e R1 - R2).
+// Backward reduction over the rank, four lanes per (sample, child), lane l
+// taking ranks 4l .. 4l + 3 (+ 16 t): dLL/dB_b[r, j] = c (e R1 - R2) and the
+// child flow e sum_r c R1 (the four lanes' sums added in a fixed order;
+// stored, added, or into the layer's scratch rows when several groups share
+// children).
 __global__ __launch_bounds__(256) void k_vb_bwd_reduce(VBArgs a) {
-  const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (x >= (int64_t)a.B * a.N) return;
-  const int b = (int)(x / a.N), j = (int)(x - (int64_t)b * a.N);
+  const int64_t x = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 2;
+  const int l = threadIdx.x & 3;
+  const bool live = x < (int64_t)a.B * a.N;
   const int kr = a.krank;
-  const int child = child_vb(a, j);
-  const float sh = key_shift_vb(a.mkeys[(int64_t)a.m_row * a.B + b]);
-  const float ev = expf(a.vals[(int64_t)child * a.B + b] - sh);
-  const float* R1 = a.R1 + x * kr;
-  const float* R2 = a.R2 + x * kr;
-  float t = 0.0f;
-  for (int r = 0; r < kr; ++r) {
-    const int64_t o = ((int64_t)b * kr + r) * a.N + j;
-    const float cv = expf(a.Bf[o]);
-    const float r1 = R1[r];
-    t += cv * r1;
-    a.dB[o] = cv * (ev * r1 - R2[r]);
+  int b = 0, j = 0, child = 0;
+  float ev = 0.0f, t = 0.0f;
+  if (live) {
+    b = (int)(x / a.N);
+    j = (int)(x - (int64_t)b * a.N);
+    child = child_vb(a, j);
+    const float sh = key_shift_vb(a.mkeys[(int64_t)a.m_row * a.B + b]);
+    ev = expf(a.vals[(int64_t)child * a.B + b] - sh);
+    const float* R1 = a.R1 + x * kr;
+    const float* R2 = a.R2 + x * kr;
+    for (int r0 = 4 * l; r0 < kr; r0 += 16) {
+      float r1[4] = {0.0f, 0.0f, 0.0f, 0.0f}, r2[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if ((kr & 3) == 0) {
+        const float4 u = *(const float4*)(R1 + r0), w = *(const float4*)(R2 + r0);
+        r1[0] = u.x; r1[1] = u.y; r1[2] = u.z; r1[3] = u.w;
+        r2[0] = w.x; r2[1] = w.y; r2[2] = w.z; r2[3] = w.w;
+      } else {
+        for (int e = 0; e < 4 && r0 + e < kr; ++e) {
+          r1[e] = R1[r0 + e];
+          r2[e] = R2[r0 + e];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = r0 + e;
+        if (r >= kr) break;
+        const int64_t o = ((int64_t)b * kr + r) * a.N + j;
+        const float cv = expf(a.Bf[o]);
+        t += cv * r1[e];
+        a.dB[o] = cv * (ev * r1[e] - r2[e]);
+      }
+    }
   }
+  t += __shfl_xor(t, 1);
+  t += __shfl_xor(t, 2);
+  if (!live || l != 0) return;
   const float fl = ev * t;
   if (a.scratch_row >= 0) {
     a.scratch[(int64_t)(a.scratch_row + j) * a.B + b] = fl;
@@ -239,7 +283,7 @@ void launch_vb_fwd_pack(const VBArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_vb_fwd_pack, dim3(tiles), dim3(512), 0, s, a);
 }
 void launch_vb_fwd_reduce(const VBArgs& a, hipStream_t s) {
-  const int64_t n = (int64_t)a.B * a.M;
+  const int64_t n = (int64_t)a.B * a.M * 4;
   hipLaunchKernelGGL(k_vb_fwd_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
 }
 void launch_vb_bwd_pack(const VBArgs& a, hipStream_t s) {
@@ -247,7 +291,7 @@ void launch_vb_bwd_pack(const VBArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_vb_bwd_pack, dim3(tiles), dim3(512), 0, s, a);
 }
 void launch_vb_bwd_reduce(const VBArgs& a, hipStream_t s) {
-  const int64_t n = (int64_t)a.B * a.N;
+  const int64_t n = (int64_t)a.B * a.N * 4;
   hipLaunchKernelGGL(k_vb_bwd_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
 }
 

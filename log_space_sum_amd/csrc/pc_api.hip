@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
+#include <cstdint>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -206,6 +208,15 @@ GemmShape vb_gemm_shape(const Handle* h, const GroupRec& r, bool elem, int Qpad,
 
 GemmShape param_gemm_shape_tiles(const Handle* h, int pa, int pb, int tiles256, int tiles128);
 
+// K split of a parameter-flow launch with `tiles` output tiles over
+// `kslices` 32-wide K slices (its copies' samples): a power of two up to 8
+// until the launch has 256 workgroups, keeping >= 8 slices per split.
+int param_splitk(int tiles, int64_t kslices) {
+  int S = 1;
+  while (tiles * S < 256 && S * 2 <= 8 && kslices / (S * 2) >= 8) S *= 2;
+  return S;
+}
+
 GemmShape param_gemm_shape(const Handle* h, int pa, int pb) {
   return param_gemm_shape_tiles(h, pa, pb, h->param_tiles256, h->param_tiles128);
 }
@@ -295,6 +306,39 @@ WsPlan plan_workspace(const Handle* h, int B, bool fwd_only) {
     p.ncounters = nct;
     p.partials = take((size_t)pel * 4);
     p.counters = take((size_t)nct * 4);
+    // the parameter-flow launches: every plain block at once, one block
+    // (chunks on the second stream), the LowRank "sum_exp" blocks
+    int64_t ppel = 0;
+    int32_t pct = 0;
+    auto consider = [&](const GemmShape& g, int64_t kslices) {
+      const int S = param_splitk(g.tiles, kslices);
+      if (S > 1) ppel = std::max<int64_t>(ppel, (int64_t)g.tiles * S * g.mt * g.nt);
+      pct = std::max(pct, g.tiles);
+    };
+    if (!bw) {
+    } else if (h->has_plain_sums) {
+      const GemmShape g = param_gemm_shape(h, p.pl[GK_PARAM][0], p.pl[GK_PARAM][1]);
+      int64_t kmin = INT64_MAX;
+      for (const BlockRec& bl : h->blocks)
+        if (bl.ncopies > 0) {
+          kmin = std::min<int64_t>(kmin, (int64_t)bl.ncopies * (p.B_padK / 32));
+          GemmShape gb = g;
+          gb.tiles = (int)((round_up(bl.M, ROW_PAD) / g.mt) * (round_up(bl.N, ROW_PAD) / g.nt));
+          consider(gb, (int64_t)bl.ncopies * (p.B_padK / 32));   // a chunk of all its copies at most
+        }
+      if (kmin != INT64_MAX) consider(g, kmin);
+    }
+    if (bw && vsum_active(h)) {
+      const int QK = (int)round_up((int64_t)B * h->lowrank_rank, K_PAD);
+      const GemmShape g = param_gemm_shape_tiles(h, p.pl[GK_PARAM][0], p.pl[GK_PARAM][1], h->v_param_tiles256,
+                                                 h->v_param_tiles128);
+      int64_t kmin = INT64_MAX;
+      for (const BlockRec& bl : h->vblocks) kmin = std::min<int64_t>(kmin, (int64_t)bl.ncopies * (QK / 32));
+      if (kmin != INT64_MAX) consider(g, kmin);
+    }
+    p.npcounters = pct;
+    p.ppartials = take((size_t)ppel * 4);
+    p.pcounters = take((size_t)pct * 4);
   }
   // LowRank: exp of the children (per layer), kept Z/S/U/W, per-layer
   // coefficients, parameter-flow partials (ceil(B/8) copies of each block)
@@ -1111,6 +1155,10 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
       Timed t(h, KK_OTHER, c.s);
       launch_fill_u32(v.counters, p.ncounters, 0u, c.s);
     }
+    if (p.npcounters > 0) {
+      Timed t(h, KK_OTHER, c.s);
+      launch_fill_u32((uint32_t*)((char*)c.ws + p.pcounters), p.npcounters, 0u, c.s);
+    }
     if (!h->inputs.empty()) {
       Timed t(h, KK_OTHER, c.s);
       launch_bucket(v.tokT, h->num_vars, B, h->max_cats, v.bucket_ptr, v.bucket_idx, c.s);
@@ -1135,8 +1183,16 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
     pg.planeB = v.earena_plane;
     pg.params = params;
     pg.pflows = param_flows;
-    pg.splitk = 1;
-    const GemmShape pshp = param_gemm_shape(h, p.pl[GK_PARAM][0], p.pl[GK_PARAM][1]);
+    pg.partials = (float*)((char*)c.ws + p.ppartials);
+    pg.counters = (uint32_t*)((char*)c.ws + p.pcounters);
+    GemmShape pshp = param_gemm_shape(h, p.pl[GK_PARAM][0], p.pl[GK_PARAM][1]);
+    {
+      int64_t kmin = INT64_MAX;
+      for (const BlockRec& bl : h->blocks)
+        if (bl.ncopies > 0) kmin = std::min<int64_t>(kmin, (int64_t)bl.ncopies * (p.B_padK / 32));
+      pshp.splitk = kmin == INT64_MAX ? 1 : param_splitk(pshp.tiles, kmin);
+      pg.splitk = pshp.splitk;
+    }
     struct Chunk {
       int ready, block, lo, hi;
     };
@@ -1193,6 +1249,8 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
         const int64_t Mp = round_up(bl.M, ROW_PAD), Np = round_up(bl.N, ROW_PAD);
         g.tile0 = shp.mt == 256 ? bl.pt256 : shp.nt == 256 ? 2 * bl.pt256 : bl.pt128;
         shp.tiles = (int)((Mp / shp.mt) * (Np / shp.nt));
+        shp.splitk = param_splitk(shp.tiles, (int64_t)(ch.hi - ch.lo) * (p.B_padK / 32));
+        g.splitk = shp.splitk;
         Timed t(h, KK_PARAM, side);
         launch_gemm(EPI_PARAM, p.pl[GK_PARAM][0], p.pl[GK_PARAM][1], shp, g, side);
         ++next_chunk;
@@ -1372,9 +1430,16 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
       pv.planeB = h->vx_rows * p.QK;
       pv.params = params;
       pv.pflows = param_flows;
-      pv.splitk = 1;
-      const GemmShape vshp = param_gemm_shape_tiles(h, p.pl[GK_PARAM][0], p.pl[GK_PARAM][1], h->v_param_tiles256,
-                                                    h->v_param_tiles128);
+      pv.partials = (float*)((char*)c.ws + p.ppartials);
+      pv.counters = (uint32_t*)((char*)c.ws + p.pcounters);
+      GemmShape vshp = param_gemm_shape_tiles(h, p.pl[GK_PARAM][0], p.pl[GK_PARAM][1], h->v_param_tiles256,
+                                              h->v_param_tiles128);
+      {
+        int64_t kmin = INT64_MAX;
+        for (const BlockRec& bl : h->vblocks) kmin = std::min<int64_t>(kmin, (int64_t)bl.ncopies * (p.QK / 32));
+        vshp.splitk = param_splitk(vshp.tiles, kmin);
+        pv.splitk = vshp.splitk;
+      }
       {
         Timed t(h, KK_PARAM, c.s);
         launch_gemm(EPI_PARAM, p.pl[GK_PARAM][0], p.pl[GK_PARAM][1], vshp, pv, c.s);

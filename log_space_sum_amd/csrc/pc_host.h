@@ -246,6 +246,10 @@ struct WsPlan {
   size_t partials, counters;
   int64_t partial_elems;
   int32_t ncounters;
+  // split-K state of the parameter-flow products (their own: those can run on
+  // the second stream beside split-K per-layer products)
+  size_t ppartials, pcounters;
+  int32_t npcounters;
   size_t lowrank_bytes;
   size_t total;
 };
