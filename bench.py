@@ -10,8 +10,10 @@ Prints one JSON line.  `value` is the sum layers' algorithmic throughput:
 3 products (forward, element flows, parameter flows) x 2*M*N*B flops per sum
 group, divided by the whole step's wall time.  The roofline object describes
 the dominant kernel: algorithmic flops per launch over its mean launch time
-(HIP events on the library's stream, recorded in a second timed pass over the
-same number of steps), against the bf16 dense MFMA peak of MI355X.
+(in a second timed pass over the same number of steps, every kernel is
+launched with a HIP event pair that its own dispatch packet stamps at the
+kernel's start and end, on the stream it runs on), against the bf16 dense MFMA
+peak of MI355X.
 The CPU baseline times the float64 oracle on a bounded sample of the same
 workload (a subset of the batch) on the host's cores.
 """
@@ -89,7 +91,12 @@ def cpu_baseline(cfg, sample_B, min_s=10.0, max_passes=100000):
             "seconds": total}
 
 
-PEAK_EXP_G = 19660.0   # MI355X VALU transcendental rate: 157.3 TFLOP/s fp32 vector = 78.6 T FMA/s, exp at 1/4
+# MI355X exp rate: 256 CUs x 4 SIMDs x 16 lanes = 16384 fp32 lane operations
+# per clock; CDNA4 issues transcendentals (v_exp_f32) at half that rate, so
+# 8192 exps per clock x 2.4 GHz = 19.66 T exp/s.  (A probe of independent exp
+# chains measured 13.0 T exp/s next to 52 T packed FMA/s = 26 T FMA issue/s:
+# the same 1:2 ratio at a 1.6 GHz clock under load.)
+PEAK_EXP_G = 19660.0
 
 
 def bench_lowrank(args):
@@ -158,13 +165,32 @@ def bench_lowrank(args):
     pairs = B * pairs_per_sample                       # (sample, node, child) triples per pass
     exps = 2 * pairs                                   # forward + backward recomputation
     value = exps / (ms * 1e-3) / 1e9
-    dom = max(("lowrank_fwd", "lowrank_bwd"), key=lambda k: kt[k][1])
-    n_launch, tot_ms = kt[dom]
-    per_launch_exps = pairs * args.steps / max(n_launch, 1)
-    avg_ms = tot_ms / max(n_launch, 1)
-    achieved = per_launch_exps / (avg_ms * 1e-3) / 1e9
+    if args.lowrank_form == "sum_exp":
+        # the virtual-batch products with the shared weights dominate: per
+        # LowRank group one forward product theta [X | C]^T and one backward
+        # product theta^T [Y1 | Y2]^T, 2 * M * N * (2 B k) flops each
+        rank = int(cfg["cfg"]["rank"])
+        kind_flops = {"sum_fwd_gemm": 4 * pairs * rank, "elem_flow_gemm": 4 * pairs * rank}
+        dom = max(kind_flops, key=lambda k: kt[k][1])
+        n_launch, tot_ms = kt[dom]
+        avg_ms = tot_ms / max(n_launch, 1)
+        per_launch = kind_flops[dom] * args.steps / max(n_launch, 1)
+        roofline = {"kernel": dom, "bound": "mfma", "achieved": round(per_launch / (avg_ms * 1e-3) / 1e12, 3),
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(per_launch / (avg_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                    "traffic": kernel_traffic("lowrank_" + dom), "per_launch_gflop": round(per_launch / 1e9, 4),
+                    "avg_launch_ms": round(avg_ms, 5)}
+    else:
+        dom = max(("lowrank_fwd", "lowrank_bwd", "lowrank_coef"), key=lambda k: kt[k][1])
+        n_launch, tot_ms = kt[dom]
+        per_launch_exps = pairs * args.steps / max(n_launch, 1)
+        avg_ms = tot_ms / max(n_launch, 1)
+        achieved = per_launch_exps / (avg_ms * 1e-3) / 1e9
+        roofline = {"kernel": dom, "bound": "alu", "achieved": round(achieved, 2), "peak": PEAK_EXP_G,
+                    "unit": "Gexp/s", "frac": round(achieved / PEAK_EXP_G, 4), "traffic": kernel_traffic(dom),
+                    "avg_launch_ms": round(avg_ms, 5)}
     out = {
-        "metric": "LowRank exp_sum fwd+bwd exp throughput (frac of VALU exp peak), HMM 1024 lat x 64 pos, rank 16, batch 64",
+        "metric": f"LowRank {args.lowrank_form} fwd+bwd exp throughput, HMM 1024 lat x 64 pos, rank 16, batch 64",
         "value": round(value, 2), "unit": "Gexp/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16-split" if args.mode == "auto" else "bf16x6-split", "data": "synthetic",
@@ -173,9 +199,7 @@ def bench_lowrank(args):
                    "hip_graph": bool(args.graph and zf is None),
                    "global_batch": B},
         "kernel_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in kt.items() if v[0]},
-        "roofline": {"kernel": dom, "bound": "alu", "achieved": round(achieved, 2), "peak": PEAK_EXP_G,
-                     "unit": "Gexp/s", "frac": round(achieved / PEAK_EXP_G, 4), "traffic": kernel_traffic(dom),
-                     "avg_launch_ms": round(avg_ms, 5)},
+        "roofline": roofline,
     }
     if not args.no_cpu:
         import numpy as np

@@ -353,15 +353,20 @@ const char* pc_last_error(void);
 int pc_layout_info(pc_handle h, pc_layout_summary* info);
 int pc_layer_class(pc_handle h, int layer, int* cls);
 
-/* Kernel timing: when enabled, pc_forward / pc_backward record a HIP event
- * pair on `stream` around every kernel launch; pc_kernel_times() then returns,
- * per kernel kind, the number of launches and the summed milliseconds of all
- * launches recorded since the last reset (it synchronises on those events).
+/* Kernel timing: when enabled, every kernel that pc_forward / pc_backward
+ * launch on `stream` is launched with a HIP event pair that its own dispatch
+ * packet stamps at the kernel's start and end (hipExtLaunchKernelGGL), so a
+ * pair measures one kernel's execution, the duration a kernel trace reports;
+ * pc_kernel_times() then returns, per kernel kind, the number of launches and
+ * the summed milliseconds of all launches recorded since the last reset (it
+ * synchronises on those events).  Copies and fills through the HIP runtime
+ * are not counted.
  * kinds: 0 sum forward GEMM, 1 element-flow GEMM, 2 parameter-flow GEMM,
  * 3 weight split, 4 column max, 5 exponentiate children, 6 scaled flows,
  * 7 input forward, 8 input backward, 9 product forward, 10 product backward,
- * 11 EM, 12 LowRank forward, 13 LowRank backward, 14 other. */
-#define PC_NUM_KERNEL_KINDS 15
+ * 11 EM, 12 LowRank forward, 13 LowRank backward, 14 other,
+ * 15 LowRank flow coefficients. */
+#define PC_NUM_KERNEL_KINDS 16
 int pc_set_timing(pc_handle h, int enable);
 int pc_kernel_times(pc_handle h, int64_t* launches, double* ms);
 

@@ -23,10 +23,10 @@ PC_CLASS_SHARED, PC_CLASS_STRIDED, PC_CLASS_GENERAL, PC_CLASS_LOWRANK = 0, 1, 2,
 PC_BWD_SEEDED = 1
 PC_LOWRANK_EXP_SUM, PC_LOWRANK_SUM_EXP = 0, 1
 LOWRANK_FORMS = {"exp_sum": PC_LOWRANK_EXP_SUM, "sum_exp": PC_LOWRANK_SUM_EXP}
-PC_NUM_KERNEL_KINDS = 15
+PC_NUM_KERNEL_KINDS = 16
 KERNEL_KINDS = ["sum_fwd_gemm", "elem_flow_gemm", "param_flow_gemm", "weight_split", "column_max",
                 "exp_children", "scaled_flows", "input_fwd", "input_bwd", "product_fwd",
-                "product_bwd", "em", "lowrank_fwd", "lowrank_bwd", "other"]
+                "product_bwd", "em", "lowrank_fwd", "lowrank_bwd", "other", "lowrank_coef"]
 MODES = {"auto": PC_PREC_AUTO, "fp32": PC_PREC_FP32, "tf32": PC_PREC_TF32}
 GEMM_KINDS = {"fwd": 0, "elem": 1, "param": 2}
 

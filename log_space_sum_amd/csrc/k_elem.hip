@@ -1118,39 +1118,39 @@ static int grid_for(int64_t n, int per = 256, int cap = 65536) {
 }
 
 void launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s) {
-  if (n > 0) hipLaunchKernelGGL(k_fill_u32, dim3(grid_for(n)), dim3(256), 0, s, p, n, v);
+  if (n > 0) launch_kernel(k_fill_u32, dim3(grid_for(n)), dim3(256), 0, s, p, n, v);
 }
 void launch_fill_ranges(float* flows, const FillRange* d_ranges, int nranges, int64_t max_count, int B, hipStream_t s) {
   if (nranges <= 0) return;
   const int gx = grid_for(max_count * B, 256, 4096);
-  hipLaunchKernelGGL(k_fill_ranges, dim3(gx, nranges), dim3(256), 0, s, flows, d_ranges, B);
+  launch_kernel(k_fill_ranges, dim3(gx, nranges), dim3(256), 0, s, flows, d_ranges, B);
 }
 void launch_copy_row(const float* src, float* dst, int B, hipStream_t s) {
-  hipLaunchKernelGGL(k_copy_row, dim3((B + 255) / 256), dim3(256), 0, s, src, dst, B);
+  launch_kernel(k_copy_row, dim3((B + 255) / 256), dim3(256), 0, s, src, dst, B);
 }
 void launch_tokens_t(const int32_t* tok, int32_t* tokT, int B, int V, hipStream_t s) {
-  hipLaunchKernelGGL(k_tokens_t, dim3((V + 31) / 32, (B + 31) / 32), dim3(256), 0, s, tok, tokT, B, V);
+  launch_kernel(k_tokens_t, dim3((V + 31) / 32, (B + 31) / 32), dim3(256), 0, s, tok, tokT, B, V);
 }
 // V = 4 needs B % 4 == 0 (rows 16-byte aligned); the base pointers come
 // from the caller's allocations, aligned far beyond 16 bytes.
 #define PC_LAUNCH_V(kern, n_items, args, s)                                                       \
   do {                                                                                          \
     if ((args).B % 4 == 0)                                                                      \
-      hipLaunchKernelGGL(kern<4>, dim3(grid_for((int64_t)(n_items) * ((args).B / 4))), dim3(256), 0, s, args); \
+      launch_kernel(kern<4>, dim3(grid_for((int64_t)(n_items) * ((args).B / 4))), dim3(256), 0, s, args); \
     else                                                                                        \
-      hipLaunchKernelGGL(kern<1>, dim3(grid_for((int64_t)(n_items) * (args).B)), dim3(256), 0, s, args);       \
+      launch_kernel(kern<1>, dim3(grid_for((int64_t)(n_items) * (args).B)), dim3(256), 0, s, args);       \
   } while (0)
 
 void launch_input_fwd(const InputArgs& a, hipStream_t s) {
   // a lane takes the kernel's 4 items per pass (their loads in flight together)
   if ((a.B & 3) == 0)
-    hipLaunchKernelGGL(k_input_fwd<4>, dim3(grid_for((int64_t)a.num_nodes * (a.B / 4), 256 * 4)), dim3(256), 0, s, a);
+    launch_kernel(k_input_fwd<4>, dim3(grid_for((int64_t)a.num_nodes * (a.B / 4), 256 * 4)), dim3(256), 0, s, a);
   else
     PC_LAUNCH_V(k_input_fwd, a.num_nodes, a, s);
 }
 void launch_bucket(const int32_t* tokT, int V, int B, int Kmax, int32_t* bptr, int32_t* bidx, hipStream_t s) {
   const size_t sh = (size_t)(Kmax + 1 + B) * sizeof(int32_t);
-  hipLaunchKernelGGL(k_bucket, dim3(V), dim3(256), sh, s, tokT, B, Kmax, bptr, bidx);
+  launch_kernel(k_bucket, dim3(V), dim3(256), sh, s, tokT, B, Kmax, bptr, bidx);
 }
 void launch_input_bwd(const InputArgs& a, hipStream_t s) {
   if (a.num_rows <= 0) return;
@@ -1159,19 +1159,19 @@ void launch_input_bwd(const InputArgs& a, hipStream_t s) {
     // rows of several nodes: the row's nodes over 4 waves; else one row per wave
     if (a.max_row_nodes >= 2) {
       if (a.B <= 64 * kPfB && a.K <= 512)
-        hipLaunchKernelGGL(k_input_bwd_pf<4>, dim3(a.num_rows), dim3(256), per * 4, s, a);
+        launch_kernel(k_input_bwd_pf<4>, dim3(a.num_rows), dim3(256), per * 4, s, a);
       else
-        hipLaunchKernelGGL(k_input_bwd<4>, dim3(a.num_rows), dim3(256), per * 4, s, a);
+        launch_kernel(k_input_bwd<4>, dim3(a.num_rows), dim3(256), per * 4, s, a);
     } else {
       const size_t sh = (size_t)(5 * a.B + a.K + 1) * sizeof(float);
       const int nchunk = (a.max_var_nodes + kVarChunk - 1) / kVarChunk;
       if (a.B <= 64 * kPfB)
-        hipLaunchKernelGGL(k_input_bwd_var_pf, dim3(a.num_vars * nchunk), dim3(256), sh, s, a);
+        launch_kernel(k_input_bwd_var_pf, dim3(a.num_vars * nchunk), dim3(256), sh, s, a);
       else
-        hipLaunchKernelGGL(k_input_bwd_var, dim3(a.num_vars * nchunk), dim3(256), sh, s, a);
+        launch_kernel(k_input_bwd_var, dim3(a.num_vars * nchunk), dim3(256), sh, s, a);
     }
   } else {
-    hipLaunchKernelGGL(k_input_bwd_wide, dim3(a.num_rows), dim3(256), (size_t)a.B * sizeof(float), s, a);
+    launch_kernel(k_input_bwd_wide, dim3(a.num_rows), dim3(256), (size_t)a.B * sizeof(float), s, a);
   }
 }
 void launch_prod_fwd(const ProdArgs& a, hipStream_t s) { PC_LAUNCH_V(k_prod_fwd, a.num_nodes, a, s); }
@@ -1187,15 +1187,15 @@ static void launch_colmax_v(const SumArgs& a, int row_tiles, hipStream_t s) {
   const int g4 = row_tiles * ((a.B + 255) / 256), g2 = row_tiles * ((a.B + 127) / 128);
   const int g1 = row_tiles * ((a.B + 63) / 64);
   if (a.B % 4 == 0 && g4 >= 512)
-    hipLaunchKernelGGL((k_colmax<4, PROD, 16>), dim3(g4), dim3(256), 0, s, a);
+    launch_kernel((k_colmax<4, PROD, 16>), dim3(g4), dim3(256), 0, s, a);
   else if (a.B % 2 == 0 && g2 >= 512)
-    hipLaunchKernelGGL((k_colmax<2, PROD, 16>), dim3(g2), dim3(256), 0, s, a);
+    launch_kernel((k_colmax<2, PROD, 16>), dim3(g2), dim3(256), 0, s, a);
   else if (g1 >= 512)
-    hipLaunchKernelGGL((k_colmax<1, PROD, 16>), dim3(g1), dim3(256), 0, s, a);
+    launch_kernel((k_colmax<1, PROD, 16>), dim3(g1), dim3(256), 0, s, a);
   else if (g1 * 4 >= 512)
-    hipLaunchKernelGGL((k_colmax<1, PROD, 4>), dim3(g1 * 4), dim3(256), 0, s, a);
+    launch_kernel((k_colmax<1, PROD, 4>), dim3(g1 * 4), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((k_colmax<1, PROD, 1>), dim3(g1 * 16), dim3(256), 0, s, a);
+    launch_kernel((k_colmax<1, PROD, 1>), dim3(g1 * 16), dim3(256), 0, s, a);
 }
 void launch_colmax(const SumArgs& a, int row_tiles, hipStream_t s) {
   if (row_tiles <= 0) return;
@@ -1203,28 +1203,28 @@ void launch_colmax(const SumArgs& a, int row_tiles, hipStream_t s) {
   else launch_colmax_v<false>(a, row_tiles, s);
 }
 void launch_exp_pack(const SumArgs& a, int row_tiles, hipStream_t s) {
-  if (row_tiles > 0) hipLaunchKernelGGL((k_pack<0, false>), dim3(row_tiles * a.btiles), dim3(512), 0, s, a);
+  if (row_tiles > 0) launch_kernel((k_pack<0, false>), dim3(row_tiles * a.btiles), dim3(512), 0, s, a);
 }
 // Scaled flows; with a.fp_on also the following product layer's backward, its
 // other children on up to 1024 extra workgroups.
 void launch_g_pack(const SumArgs& a, int row_tiles, hipStream_t s) {
   if (row_tiles <= 0) return;
   if (!a.fp_on) {
-    hipLaunchKernelGGL((k_pack<1, false>), dim3(row_tiles * a.btiles), dim3(512), 0, s, a);
+    launch_kernel((k_pack<1, false>), dim3(row_tiles * a.btiles), dim3(512), 0, s, a);
     return;
   }
   SumArgs b = a;
   b.fp_tiles = row_tiles * a.btiles;
   // up to 16 workgroups per CU for the other children (2 items per lane per pass)
   const int rest = b.fp_nrest > 0 ? grid_for((int64_t)b.fp_nrest * ((a.B + 3) / 4), 256, 4096) : 0;
-  hipLaunchKernelGGL((k_pack<1, true>), dim3(b.fp_tiles + rest), dim3(512), 0, s, b);
+  launch_kernel((k_pack<1, true>), dim3(b.fp_tiles + rest), dim3(512), 0, s, b);
 }
 void launch_theta_pack(const ThetaArgs& a, int tiles, hipStream_t s) {
-  if (tiles > 0) hipLaunchKernelGGL(k_theta_pack, dim3(tiles), dim3(256), 0, s, a);
+  if (tiles > 0) launch_kernel(k_theta_pack, dim3(tiles), dim3(256), 0, s, a);
 }
 void launch_elem_reduce(const SumArgs& a, hipStream_t s) { PC_LAUNCH_V(k_elem_reduce, a.nuniq, a, s); }
 void launch_em(const EmArgs& a, int rows, hipStream_t s) {
-  if (rows > 0) hipLaunchKernelGGL(k_em, dim3((rows + 3) / 4), dim3(256), 0, s, a, rows);
+  if (rows > 0) launch_kernel(k_em, dim3((rows + 3) / 4), dim3(256), 0, s, a, rows);
 }
 
 }  // namespace pc

@@ -506,10 +506,13 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
   __builtin_amdgcn_s_waitcnt(0);       // no load may still target LDS past this point
 
   // ---- split-K: the last workgroup of a tile adds the partials in order -----
-  // Partials are published with device-scope atomic stores (written through
-  // to the device coherence point, so no cache-wide write-back is needed),
-  // completed (vmcnt 0) before the arrival counter moves; the last arrival
-  // reads every partial back with device-scope atomic loads, in split order.
+  // Partials are written and read with device-scope atomics (no data race).
+  // Ordering: the workgroup barrier orders every lane's partial stores before
+  // the arrival increment of lane 0, a device-scope release; the last arriving
+  // workgroup's increment is an acquire that reads it, and its barrier orders
+  // that acquire before its lanes' partial loads.  Happens-before is
+  // transitive across the two scopes, so the last arrival reads every split's
+  // finished partials; it adds them in split order (deterministic).
   if (S > 1) {
     float* mine = a.partials + ((int64_t)ltile * S + split) * (NREG * 256);
 #pragma unroll
@@ -523,7 +526,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0)
-      last_flag = (__hip_atomic_fetch_add(a.counters + ltile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+      last_flag = (__hip_atomic_fetch_add(a.counters + ltile, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
                    (unsigned)(S - 1));
     __syncthreads();
     if (!last_flag) return;
@@ -835,7 +838,7 @@ static void launch_shape(int grid, const GemmArgs& a, hipStream_t s) {
   constexpr int KT = gemm_kt(PA, PB, MT, NT);
   constexpr int NS = gemm_stages(PA, PB, MT, NT);
   static_assert(NS >= 2, "LDS ring needs two stages");
-  hipLaunchKernelGGL((k_gemm<EPI, PA, PB, MT, NT, WM, KT, NS>), dim3(grid), dim3(256), 0, s, a);
+  launch_kernel((k_gemm<EPI, PA, PB, MT, NT, WM, KT, NS>), dim3(grid), dim3(256), 0, s, a);
 }
 
 template <int EPI, int PA, int PB>

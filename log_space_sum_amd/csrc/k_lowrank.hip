@@ -755,8 +755,8 @@ static int lr_kb(int krank) { return krank <= 32 ? 1 : 2; }
 
 template <int PH, int PG, int KC, int KB>
 static void lr_fwd_kk(const LRArgs& a, const dim3& grid, hipStream_t s) {
-  if (a.sumexp) hipLaunchKernelGGL((k_lr_fwd<PH, PG, KC, KB, true>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((k_lr_fwd<PH, PG, KC, KB>), grid, dim3(256), 0, s, a);
+  if (a.sumexp) launch_kernel((k_lr_fwd<PH, PG, KC, KB, true>), grid, dim3(256), 0, s, a);
+  else launch_kernel((k_lr_fwd<PH, PG, KC, KB>), grid, dim3(256), 0, s, a);
 }
 template <int PH, int PG>
 static void lr_fwd_k(const LRArgs& a, hipStream_t s) {
@@ -768,8 +768,8 @@ static void lr_fwd_k(const LRArgs& a, hipStream_t s) {
 }
 template <int PH, int PG, int KC, int KB, bool WS>
 static void lr_bwd_kk(const LRArgs& a, const dim3& grid, hipStream_t s) {
-  if (a.sumexp) hipLaunchKernelGGL((k_lr_bwd<PH, PG, KC, KB, WS, true>), grid, dim3(512), 0, s, a);
-  else hipLaunchKernelGGL((k_lr_bwd<PH, PG, KC, KB, WS>), grid, dim3(512), 0, s, a);
+  if (a.sumexp) launch_kernel((k_lr_bwd<PH, PG, KC, KB, WS, true>), grid, dim3(512), 0, s, a);
+  else launch_kernel((k_lr_bwd<PH, PG, KC, KB, WS>), grid, dim3(512), 0, s, a);
 }
 template <int PH, int PG, bool WS = false>
 static void lr_bwd_k(const LRArgs& a, hipStream_t s) {
@@ -792,9 +792,9 @@ int lr_pack_workgroups(int B, int M, int N, int krank) {
 template <int PH, int PG>
 static void lr_pack_k(const LRPackArgs& pa, const dim3& grid, hipStream_t s) {
   const int kc = lr_kc(pa.krank);
-  if (kc == 1) hipLaunchKernelGGL((k_lr_pack<PH, PG, 1, 1>), grid, dim3(256), 0, s, pa);
-  else if (kc == 2) hipLaunchKernelGGL((k_lr_pack<PH, PG, 2, 1>), grid, dim3(256), 0, s, pa);
-  else hipLaunchKernelGGL((k_lr_pack<PH, PG, 4, 2>), grid, dim3(256), 0, s, pa);
+  if (kc == 1) launch_kernel((k_lr_pack<PH, PG, 1, 1>), grid, dim3(256), 0, s, pa);
+  else if (kc == 2) launch_kernel((k_lr_pack<PH, PG, 2, 1>), grid, dim3(256), 0, s, pa);
+  else launch_kernel((k_lr_pack<PH, PG, 4, 2>), grid, dim3(256), 0, s, pa);
 }
 void launch_lr_pack(const LRPackArgs& pa, int fp32, hipStream_t s) {
   if (pa.ngroups <= 0) return;
@@ -804,7 +804,7 @@ void launch_lr_pack(const LRPackArgs& pa, int fp32, hipStream_t s) {
 }
 void launch_lr_coef(const LRArgs& a, hipStream_t s) {
   const int64_t n = (int64_t)a.B * ((a.M + 31) / 32 * 32);
-  hipLaunchKernelGGL(k_lr_coef, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+  launch_kernel(k_lr_coef, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
 }
 void launch_lr_fwd(const LRArgs& a, int fp32, hipStream_t s) {
   if (fp32) lr_fwd_k<3, 3>(a, s);
@@ -819,7 +819,7 @@ void launch_lr_zstat(const LRArgs& a, int fp32, hipStream_t s) {
   else lr_bwd_k<2, 1, true>(a, s);
 }
 void launch_lr_fplus(const float* P, int nsg, int64_t elems, float* pflows, hipStream_t s) {
-  hipLaunchKernelGGL(k_lr_fplus, dim3(grid_lr(elems)), dim3(256), 0, s, P, nsg, elems, pflows);
+  launch_kernel(k_lr_fplus, dim3(grid_lr(elems)), dim3(256), 0, s, P, nsg, elems, pflows);
 }
 
 }  // namespace pc

@@ -280,19 +280,19 @@ __global__ __launch_bounds__(256) void k_vb_bwd_reduce(VBArgs a) {
 // ---- launchers ------------------------------------------------------------
 void launch_vb_fwd_pack(const VBArgs& a, hipStream_t s) {
   const int tiles = ((a.QK + 63) / 64) * ((a.N + 63) / 64);
-  hipLaunchKernelGGL(k_vb_fwd_pack, dim3(tiles), dim3(512), 0, s, a);
+  launch_kernel(k_vb_fwd_pack, dim3(tiles), dim3(512), 0, s, a);
 }
 void launch_vb_fwd_reduce(const VBArgs& a, hipStream_t s) {
   const int64_t n = (int64_t)a.B * a.M * 4;
-  hipLaunchKernelGGL(k_vb_fwd_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+  launch_kernel(k_vb_fwd_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
 }
 void launch_vb_bwd_pack(const VBArgs& a, hipStream_t s) {
   const int tiles = ((a.QK + 63) / 64) * ((a.M + 63) / 64);
-  hipLaunchKernelGGL(k_vb_bwd_pack, dim3(tiles), dim3(512), 0, s, a);
+  launch_kernel(k_vb_bwd_pack, dim3(tiles), dim3(512), 0, s, a);
 }
 void launch_vb_bwd_reduce(const VBArgs& a, hipStream_t s) {
   const int64_t n = (int64_t)a.B * a.N * 4;
-  hipLaunchKernelGGL(k_vb_bwd_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+  launch_kernel(k_vb_bwd_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
 }
 
 }  // namespace pc

@@ -64,28 +64,45 @@ struct DeviceGuard {
 
 enum KernelKind {
   KK_FWD = 0, KK_ELEM, KK_PARAM, KK_SPLIT, KK_COLMAX, KK_EXP, KK_GPACK, KK_INFWD, KK_INBWD,
-  KK_PRODFWD, KK_PRODBWD, KK_EM, KK_LRFWD, KK_LRBWD, KK_OTHER
+  KK_PRODFWD, KK_PRODBWD, KK_EM, KK_LRFWD, KK_LRBWD, KK_OTHER, KK_LRCOEF
 };
 
-// Records a HIP event pair around one launch when the handle times kernels.
-struct Timed {
+}  // namespace
+
+EventSink*& pc::event_sink() {
+  static thread_local EventSink* sink = nullptr;
+  return sink;
+}
+
+namespace {
+
+// Times the launches made in its scope under one kernel kind when the handle
+// times kernels: each launch stamps an event pair of its own (pc_launch.h).
+struct Timed : EventSink {
   Handle* h;
-  hipStream_t s;
-  size_t slot = 0;
-  Timed(Handle* h_, int kind, hipStream_t s_) : h(h_), s(s_) {
-    if (!h->timing || h->no_events) return;
+  int kind;
+  EventSink* prev = nullptr;
+  bool on;
+  Timed(Handle* h_, int kind_, hipStream_t) : h(h_), kind(kind_), on(h_->timing && !h_->no_events) {
+    if (on) {
+      prev = event_sink();
+      event_sink() = this;
+    }
+  }
+  ~Timed() override {
+    if (on) event_sink() = prev;
+  }
+  void acquire(hipEvent_t* start, hipEvent_t* stop) override {
     if (h->events_used == h->events.size()) {
       Handle::Ev ev{kind, nullptr, nullptr};
       HIPCHECK(hipEventCreate((hipEvent_t*)&ev.start));
       HIPCHECK(hipEventCreate((hipEvent_t*)&ev.stop));
       h->events.push_back(ev);
     }
-    slot = h->events_used++;
-    h->events[slot].kind = kind;
-    HIPCHECK(hipEventRecord((hipEvent_t)h->events[slot].start, s));
-  }
-  ~Timed() {
-    if (h->timing && !h->no_events) (void)hipEventRecord((hipEvent_t)h->events[slot].stop, s);
+    Handle::Ev& ev = h->events[h->events_used++];
+    ev.kind = kind;
+    *start = (hipEvent_t)ev.start;
+    *stop = (hipEvent_t)ev.stop;
   }
 };
 
@@ -1273,7 +1290,7 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
             // "sum_exp" on the virtual batch: c1, c2 and dA; Y1, Y2 operands;
             // theta^T [Y1 | Y2]^T; child flows and dB
             {
-              Timed t(h, KK_LRBWD, c.s);
+              Timed t(h, KK_LRCOEF, c.s);
               launch_lr_coef(la, c.s);
             }
             VBArgs vb = vb_args(c, sp, gi, lowrank, vals, node_flows, true);
@@ -1293,8 +1310,11 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
             Timed t(h, KK_SPLIT, c.s);
             lr_pack_group(c, sp, gi, lowrank);
           }
+          {
+            Timed t(h, KK_LRCOEF, c.s);
+            launch_lr_coef(la, c.s);
+          }
           Timed t(h, KK_LRBWD, c.s);
-          launch_lr_coef(la, c.s);
           launch_lr_bwd(la, p.mode == PC_PREC_FP32, c.s);
           if (zstat) {   // W's partials, from this layer's c2 = f / Z before the next layer rewrites it
             LRArgs lz = la;

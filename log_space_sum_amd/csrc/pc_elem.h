@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include "pc_device.h"
+#include "pc_launch.h"
 
 namespace pc {
 
