@@ -137,6 +137,17 @@ def test_hclt_small(mode):
 
 
 @pytest.mark.parametrize("mode", MODES)
+def test_hclt_wide_level_tiles(mode):
+    """A strided level wide enough for the automatic 128 x 128 product tiles
+    (at least 4 x 256 of them: 69 groups x 2 row tiles x 8 column tiles at
+    batch 1024) next to levels that keep 128 x 64 tiles, in one pass."""
+    cfg = make_config("hclt", num_vars=180, H=256, K=16, B=1024)
+    widths = [len(ly.groups) * 2 * (cfg["B"] // 128) for ly in cfg["circuit"].layers if type(ly).__name__ == "Sum"]
+    assert max(widths) >= 1024 and min(widths) < 1024
+    _full(cfg, mode, "hclt 180x256 wide level")
+
+
+@pytest.mark.parametrize("mode", MODES)
 def test_hclt_multi_unit_groups(mode):
     """Evenly strided (batched) layers whose groups span two 256-row units
     (320 latents per variable) in layers of several groups, with a ragged
