@@ -114,6 +114,7 @@ def bench_lowrank(args):
     h = L.pc_compile_layout(circ, device=0)
     L.pc_set_precision(h, args.mode)
     L.pc_set_option(h, "lr_pack", args.lr_pack)
+    L.pc_set_option(h, "flow_fp8", args.flow_fp8)
     params = torch.tensor(cfg["params"], device=dev)
     tokens = torch.tensor(cfg["tokens"], device=dev)
     vals = torch.empty((circ.num_nodes, B), device=dev)
@@ -195,7 +196,9 @@ def bench_lowrank(args):
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16-split" if args.mode == "auto" else "bf16x6-split", "data": "synthetic",
         "config": {"workload": f"lowrank {args.lowrank_form} hmm1024x64 symbols 512 rank 16 batch 64 fwd+bwd+em"
-                               + (" (z-corrected)" if args.z_correction else ""), "precision_mode": args.mode,
+                               + (" (z-corrected)" if args.z_correction else "")
+                               + (" (fp8 end products)" if args.flow_fp8 and args.lowrank_form == "sum_exp" else ""),
+                   "precision_mode": args.mode,
                    "hip_graph": bool(args.graph and zf is None),
                    "global_batch": B},
         "kernel_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in kt.items() if v[0]},
@@ -250,6 +253,8 @@ def main():
                     help="LowRank workload: how the factors make the scale")
     ap.add_argument("--z-correction", type=int, default=0, choices=[0, 1],
                     help="LowRank workload: also accumulate the denominator statistic W and take the conditional M-step")
+    ap.add_argument("--flow-fp8", type=int, default=0, choices=[0, 1],
+                    help="LowRank sum_exp: parameter flows and W from e4m3 operands (auto mode)")
     ap.add_argument("--graph", type=int, default=0, choices=[0, 1],
                     help="time replays of the step recorded as a HIP graph (1) or eager launches (0; measured the same: the queue already runs ahead of the host)")
     ap.add_argument("--layer-tile", type=int, default=0, help="product-kernel option: 0 auto, 1 128x128, 2 256x128, 3 128x256, 4 128x64, 5 64x128")

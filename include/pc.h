@@ -248,6 +248,15 @@ int pc_set_split(pc_handle h, int mode, int gemm_kind, int planes_a, int planes_
  * (pyjuice.parameterizations.LowRank, definition and Note: "sum_exp" is k
  * matmuls with the shared parameters), 1 through the fused LowRank kernels
  * (one visit per sample, node and child; results differ by rounding).
+ * PC_OPT_FLOW_FP8 (pyjuice.parameterizations.LowRank, Parameters:
+ * flow_precision "fp8"): 0 (default) bf16 operands, 1 the two products at the
+ * end of a "sum_exp" backward on the virtual batch -- the parameter flows
+ * theta * (Y1 X^T) and the denominator statistic W = Y2 C^T over every
+ * (copy, sample, rank) -- from e4m3 operands with one power-of-two scale per
+ * row and 32 consecutive (sample, rank) columns, fp32 accumulation.  Applies
+ * in PC_PREC_AUTO only (the fp32-level mode, and batches below 16, keep their
+ * split products) and to nothing else: values, element flows and dLL/dA,
+ * dLL/dB are unchanged; the statistics are about 16x less accurate.
  * Changing an option can change pc_workspace_bytes.
  * Errors: PC_ERR_INVALID_ARG (unknown option or value). */
 #define PC_OPT_LAYER_TILE 0
@@ -257,6 +266,7 @@ int pc_set_split(pc_handle h, int mode, int gemm_kind, int planes_a, int planes_
 #define PC_OPT_PARAM_CHUNK 4
 #define PC_OPT_LR_PACK    5
 #define PC_OPT_SUMEXP_FUSED 6
+#define PC_OPT_FLOW_FP8   7
 int pc_set_option(pc_handle h, int option, int value);
 
 /* Bytes of workspace pc_forward / pc_backward need for `batch` samples in the

@@ -246,7 +246,7 @@ def pc_set_split(h: Handle, mode, gemm_kind, planes_a: int, planes_b: int):
 
 
 OPTIONS = {"layer_tile": 0, "param_tile": 1, "split_max": 2, "fuse": 3, "param_chunk": 4, "lr_pack": 5,
-           "sumexp_fused": 6}
+           "sumexp_fused": 6, "flow_fp8": 7}
 
 
 def pc_set_option(h: Handle, option, value: int):
@@ -255,7 +255,9 @@ def pc_set_option(h: Handle, option, value: int):
     layers inside the adjacent sum layer's kernels, 0: separate launches),
     param_chunk (-1 automatic; 0: parameter flows in one product at the end;
     n: in chunks of n tied copies on a second stream, overlapping the element
-    flows)."""
+    flows), sumexp_fused (1: LowRank "sum_exp" through the fused kernels),
+    flow_fp8 (1: the "sum_exp" parameter flows and denominator statistic from
+    e4m3 operands in auto mode)."""
     option = OPTIONS.get(option, option) if isinstance(option, str) else option
     _check(lib().pc_set_option(h.ptr, int(option), int(value)))
 

@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpc.so")
-SOURCES = ["pc_compile.cpp", "pc_api.hip", "k_gemm.hip", "k_elem.hip", "k_lowrank.hip", "k_vbatch.hip"]
+SOURCES = ["pc_compile.cpp", "pc_api.hip", "k_gemm.hip", "k_elem.hip", "k_lowrank.hip", "k_vbatch.hip", "k_f8gemm.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

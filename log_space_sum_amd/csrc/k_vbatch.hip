@@ -66,6 +66,54 @@ __device__ __forceinline__ void store8_planes(const float (&x)[8], int np, uint1
   }
 }
 
+// float -> e4m3 (OCP FP8 E4M3: bias 7, 3 mantissa bits, largest finite 448,
+// no infinities), round to nearest even; |x| < 464 (the caller scales to
+// below 256).  Normal range by rounding the float's mantissa to 3 bits,
+// subnormals (below 2^-6) as the nearest multiple of 2^-9.
+__device__ __forceinline__ uint32_t f2e4m3(float x) {
+  if (!(x == x)) return 0x7fu;
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float ax = fabsf(x);
+  uint32_t code;
+  if (ax >= 0.015625f) {
+    uint32_t u = __float_as_uint(ax);
+    u += 0x7ffffu + ((u >> 20) & 1u);
+    code = ((((u >> 23) & 0xffu) - 120u) << 3) | ((u >> 20) & 7u);
+    code = code > 0x7eu ? 0x7eu : code;
+  } else {
+    code = (uint32_t)rintf(ax * 512.0f);
+  }
+  return sign | code;
+}
+
+// 8 consecutive K values of one row, a quarter of a 32-wide K block whose
+// other quarters are held by the neighbouring lanes (lane & 3 = the quarter,
+// all four lanes call this): the block's scale 2^e with e = floor(log2 max|x|)
+// - 7 (the block's largest magnitude lands in [128, 256)), the values x 2^-e
+// as e4m3 in one 8-byte store, and the scale byte 127 + e from quarter 0.
+// `st` false: the lane takes part in the maximum but stores nothing.
+__device__ __forceinline__ void store8_e4m3(const float (&x)[8], bool st, uint8_t* dst, uint8_t* sdst) {
+  float m = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[e]));
+  m = fmaxf(m, __shfl_xor(m, 1));
+  m = fmaxf(m, __shfl_xor(m, 2));
+  int e = 0;
+  if (m >= 1.17549435e-38f && m <= 3.4e38f) {
+    e = (int)((__float_as_uint(m) >> 23) & 0xffu) - 127 - 7;
+    e = e < -127 ? -127 : e > 127 ? 127 : e;
+  }
+  if (!st) return;
+  uint32_t w[2] = {0u, 0u};
+#pragma unroll
+  for (int k = 0; k < 8; ++k) w[k >> 2] |= f2e4m3(ldexpf(x[k], -e)) << (8 * (k & 3));
+  *(uint2*)dst = make_uint2(w[0], w[1]);
+  if ((threadIdx.x & 3) == 0) *sdst = (uint8_t)(127 + e);
+}
+
+__device__ __forceinline__ int64_t panel8(int64_t r, int64_t k, int64_t R) { return ((k >> 6) * R + r) * 64 + (k & 63); }
+__device__ __forceinline__ int64_t scale8(int64_t r, int64_t k, int64_t R) { return (k >> 5) * R + r; }
+
 __device__ __forceinline__ int child_vb(const VBArgs& a, int j) {
   return a.chblocks[a.blk_off + j / a.cbs] + j % a.cbs;
 }
@@ -111,20 +159,27 @@ __global__ __launch_bounds__(512) void k_vb_fwd_pack(VBArgs a) {
       store8_planes(cc, a.np_bt, a.vbt + panel(a.Q + q, jb, a.Qpad), a.vbt_plane);
     }
   }
-  if (a.np_n == 0) return;        // forward only: no node-major operands
+  if (a.np_n == 0 && !a.f8) return;   // forward only: no node-major operands
   __syncthreads();
   {
     const int jl = tid >> 3, c8 = tid & 7;
     const int j = j0 + jl;
-    if (j >= a.N) return;
+    if (j >= a.N) return;            // the four lanes of a K block share j
     float x[8], cc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       x[e] = tx[c8 * 8 + e][jl];
       cc[e] = tc[c8 * 8 + e][jl];
     }
-    store8_planes(x, a.np_n, a.nlo + panel(a.n_row0 + j, q0 + c8 * 8, a.n_rows), a.n_plane);
-    store8_planes(cc, a.np_n, a.nhi + panel(a.n_row0 + j, q0 + c8 * 8, a.n_rows), a.n_plane);
+    const int64_t row = a.n_row0 + j;
+    const int k = q0 + c8 * 8;
+    if (a.f8) {
+      store8_e4m3(x, true, a.n8lo + panel8(row, k, a.n_rows), a.s8lo + scale8(row, k, a.n_rows));
+      store8_e4m3(cc, true, a.n8hi + panel8(row, k, a.n_rows), a.s8hi + scale8(row, k, a.n_rows));
+    } else {
+      store8_planes(x, a.np_n, a.nlo + panel(row, k, a.n_rows), a.n_plane);
+      store8_planes(cc, a.np_n, a.nhi + panel(row, k, a.n_rows), a.n_plane);
+    }
   }
 }
 
@@ -201,7 +256,12 @@ __global__ __launch_bounds__(512) void k_vb_bwd_pack(VBArgs a) {
       t1[il][c8 * 8 + e] = v1;
       t2[il][c8 * 8 + e] = v2;
     }
-    if (i < a.M && a.np_n > 0) {
+    if (a.f8) {
+      // rows past M (the four lanes of a K block share i) store nothing
+      const int64_t row = a.n_row0 + i;
+      store8_e4m3(y1, i < a.M, a.n8lo + panel8(row, qb, a.n_rows), a.s8lo + scale8(row, qb, a.n_rows));
+      store8_e4m3(y2, i < a.M, a.n8hi + panel8(row, qb, a.n_rows), a.s8hi + scale8(row, qb, a.n_rows));
+    } else if (i < a.M && a.np_n > 0) {
       store8_planes(y1, a.np_n, a.nlo + panel(a.n_row0 + i, qb, a.n_rows), a.n_plane);
       store8_planes(y2, a.np_n, a.nhi + panel(a.n_row0 + i, qb, a.n_rows), a.n_plane);
     }

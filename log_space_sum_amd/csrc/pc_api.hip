@@ -243,6 +243,16 @@ int param_splitk(int tiles, int64_t kslices) {
   return S;
 }
 
+// K split of an e4m3 parameter-flow launch with `tiles` 128 x 128 tiles over
+// `ksteps` 64-wide K steps: a power of two up to 16 until the launch has 256
+// workgroups (one per CU; measured: 1024^2 outputs over 64512 K take 185 us
+// with 4 splits, 215 us with 8, 346 us with 16), keeping >= 8 steps per split.
+int f8_splitk(int tiles, int64_t ksteps) {
+  int S = 1;
+  while (tiles * S < 256 && S * 2 <= 16 && ksteps / (S * 2) >= 8) S *= 2;
+  return S;
+}
+
 GemmShape param_gemm_shape(const Handle* h, int pa, int pb) {
   return param_gemm_shape_tiles(h, pa, pb, h->param_tiles256, h->param_tiles128);
 }
@@ -360,7 +370,14 @@ WsPlan plan_workspace(const Handle* h, int B, bool fwd_only) {
                                                  h->v_param_tiles128);
       int64_t kmin = INT64_MAX;
       for (const BlockRec& bl : h->vblocks) kmin = std::min<int64_t>(kmin, (int64_t)bl.ncopies * (QK / 32));
-      if (kmin != INT64_MAX) consider(g, kmin);
+      if (kmin == INT64_MAX) {
+      } else if (h->opt_flow_fp8 && p.mode == PC_PREC_AUTO) {
+        const int S = f8_splitk(h->v_param_tiles128, kmin / 2);
+        if (S > 1) ppel = std::max<int64_t>(ppel, (int64_t)h->v_param_tiles128 * S * 128 * 128);
+        pct = std::max(pct, h->v_param_tiles128);
+      } else {
+        consider(g, kmin);
+      }
     }
     p.npcounters = pct;
     p.ppartials = take((size_t)ppel * 4);
@@ -403,10 +420,22 @@ WsPlan plan_workspace(const Handle* h, int B, bool fwd_only) {
     p.Qpad = (int)round_up(2 * (int64_t)p.Qv, std::max(nt, 64));
     const size_t npb = (size_t)std::max(p.pl[GK_FWD][1], p.pl[GK_ELEM][1]);
     p.vbt = take(npb * p.Qpad * h->v_max_k * 2);
-    p.vX = take(bw * p.pl[GK_PARAM][1] * h->vx_rows * p.QK * 2);
-    p.vC = take(bw * p.pl[GK_PARAM][1] * h->vx_rows * p.QK * 2);
-    p.vY1 = take(bw * p.pl[GK_PARAM][0] * h->vy_rows * p.QK * 2);
-    p.vY2 = take(bw * p.pl[GK_PARAM][0] * h->vy_rows * p.QK * 2);
+    // the end products' node-major operands: bf16 planes, or e4m3 bytes and
+    // scales (PC_OPT_FLOW_FP8 in auto mode)
+    p.vf8 = bw && h->opt_flow_fp8 && p.mode == PC_PREC_AUTO;
+    const size_t b16 = bw && !p.vf8 ? 1 : 0, b8 = p.vf8 ? 1 : 0;
+    p.vX = take(b16 * p.pl[GK_PARAM][1] * h->vx_rows * p.QK * 2);
+    p.vC = take(b16 * p.pl[GK_PARAM][1] * h->vx_rows * p.QK * 2);
+    p.vY1 = take(b16 * p.pl[GK_PARAM][0] * h->vy_rows * p.QK * 2);
+    p.vY2 = take(b16 * p.pl[GK_PARAM][0] * h->vy_rows * p.QK * 2);
+    p.vX8 = take(b8 * h->vx_rows * p.QK);
+    p.vC8 = take(b8 * h->vx_rows * p.QK);
+    p.vY18 = take(b8 * h->vy_rows * p.QK);
+    p.vY28 = take(b8 * h->vy_rows * p.QK);
+    p.vXs = take(b8 * h->vx_rows * (p.QK / 32));
+    p.vCs = take(b8 * h->vx_rows * (p.QK / 32));
+    p.vY1s = take(b8 * h->vy_rows * (p.QK / 32));
+    p.vY2s = take(b8 * h->vy_rows * (p.QK / 32));
     p.vR = take(bw * 2 * (size_t)B * h->lr_max_n * kr * 4);
   }
   p.lowrank = lr0;
@@ -651,6 +680,14 @@ VBArgs vb_args(const Call& c, const SumPlan& sp, int g, const pc_lowrank_io* io,
   a.n_rows = bwd ? h->vy_rows : h->vx_rows;
   a.n_plane = a.n_rows * c.p.QK;
   a.n_row0 = bwd ? vr.g_row : vr.e_row;
+  if (c.p.vf8) {
+    a.f8 = 1;
+    a.np_n = 0;
+    a.n8lo = (uint8_t*)(base + (bwd ? c.p.vY18 : c.p.vX8));
+    a.n8hi = (uint8_t*)(base + (bwd ? c.p.vY28 : c.p.vC8));
+    a.s8lo = (uint8_t*)(base + (bwd ? c.p.vY1s : c.p.vXs));
+    a.s8hi = (uint8_t*)(base + (bwd ? c.p.vY2s : c.p.vCs));
+  }
   a.C1 = (const float*)(base + c.p.lrC1);
   a.C2 = (const float*)(base + c.p.lrC2);
   a.Z = (float*)(base + c.p.lrZ) + sp.lr_row[g] * B;
@@ -1068,6 +1105,9 @@ int pc_set_option(pc_handle hh, int option, int value) {
     } else if (option == PC_OPT_SUMEXP_FUSED) {
       if (value != 0 && value != 1) fail(PC_ERR_INVALID_ARG, "sumexp_fused must be 0 or 1");
       h->opt_sumexp_fused = value;
+    } else if (option == PC_OPT_FLOW_FP8) {
+      if (value != 0 && value != 1) fail(PC_ERR_INVALID_ARG, "flow_fp8 must be 0 or 1");
+      h->opt_flow_fp8 = value;
     } else {
       fail(PC_ERR_INVALID_ARG, "unknown option");
     }
@@ -1444,9 +1484,30 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
         launch_input_bwd(a, c.s);
       }
     }
+    for (size_t bi = 0; bi < h->blocks.size() && !p.vsum; ++bi) {
+      if (h->lr_p_off[bi] < 0) continue;
+      const BlockRec& bl = h->blocks[bi];
+      Timed t(h, KK_LRBWD, c.s);
+      launch_lr_fplus((float*)((char*)c.ws + p.lrP) + h->lr_p_off[bi] * p.lr_nsg, p.lr_nsg, (int64_t)bl.M * bl.N,
+                      param_flows + bl.param_offset, c.s);
+      if (zstat)
+        launch_lr_fplus((float*)((char*)c.ws + p.lrPz) + h->lr_p_off[bi] * p.lr_nsg, p.lr_nsg, (int64_t)bl.M * bl.N,
+                        lowrank->z_flows + bl.param_offset, c.s);
+    }
+    if (!chunks.empty()) {
+      launch_ready_chunks(-(1 << 29));
+      hipEvent_t e = (hipEvent_t)h->chunk_events[chunks.size()];
+      HIPCHECK(hipEventRecord(e, side));
+      HIPCHECK(hipStreamWaitEvent(c.s, e, 0));
+    } else if (h->has_plain_sums) {
+      Timed t(h, KK_PARAM, c.s);
+      launch_gemm(EPI_PARAM, p.pl[GK_PARAM][0], p.pl[GK_PARAM][1], pshp, pg, c.s);
+    }
     if (p.vsum) {
       // F+ = theta * (Y1 X^T) and W = Y2 C^T over every (copy, sample, rank)
-      // of each LowRank block, one product each
+      // of each LowRank block, one product each; after the plain blocks'
+      // parameter flows (joined from the second stream above), whose split-K
+      // partials and arrival counters they share
       GemmArgs pv = gemm_common(c);
       pv.B_padK = p.QK;
       pv.rowsA = h->vy_rows;
@@ -1469,37 +1530,54 @@ int pc_backward(pc_handle hh, int batch, const int32_t* tokens, const float* par
         vshp.splitk = param_splitk(vshp.tiles, kmin);
         pv.splitk = vshp.splitk;
       }
-      {
-        Timed t(h, KK_PARAM, c.s);
-        launch_gemm(EPI_PARAM, p.pl[GK_PARAM][0], p.pl[GK_PARAM][1], vshp, pv, c.s);
+      if (p.vf8) {
+        // e4m3 operands (PC_OPT_FLOW_FP8): F+ from Y1, X; W from Y2, C
+        char* base = (char*)c.ws;
+        int64_t kmin = INT64_MAX;
+        for (const BlockRec& bl : h->vblocks) kmin = std::min<int64_t>(kmin, (int64_t)bl.ncopies * (p.QK / 64));
+        F8Args f{};
+        f.A = (const uint8_t*)(base + p.vY18);
+        f.sA = (const uint8_t*)(base + p.vY1s);
+        f.rowsA = h->vy_rows;
+        f.B = (const uint8_t*)(base + p.vX8);
+        f.sB = (const uint8_t*)(base + p.vXs);
+        f.rowsB = h->vx_rows;
+        f.QK = p.QK;
+        f.nblocks = (int)h->vblocks.size();
+        f.blocks = h->d_vblocks;
+        f.params = params;
+        f.out = param_flows;
+        f.splitk = f8_splitk(h->v_param_tiles128, kmin);
+        f.partials = (float*)(base + p.ppartials);
+        f.counters = (uint32_t*)(base + p.pcounters);
+        {
+          Timed t(h, KK_PARAM, c.s);
+          launch_f8param(f, h->v_param_tiles128, c.s);
+        }
+        if (zstat) {
+          f.A = (const uint8_t*)(base + p.vY28);
+          f.sA = (const uint8_t*)(base + p.vY2s);
+          f.B = (const uint8_t*)(base + p.vC8);
+          f.sB = (const uint8_t*)(base + p.vCs);
+          f.params = nullptr;                // no weights: W
+          f.out = lowrank->z_flows;
+          Timed t(h, KK_PARAM, c.s);
+          launch_f8param(f, h->v_param_tiles128, c.s);
+        }
+      } else {
+        {
+          Timed t(h, KK_PARAM, c.s);
+          launch_gemm(EPI_PARAM, p.pl[GK_PARAM][0], p.pl[GK_PARAM][1], vshp, pv, c.s);
+        }
+        if (zstat) {
+          pv.opA = (const uint16_t*)((char*)c.ws + p.vY2);
+          pv.opB = (const uint16_t*)((char*)c.ws + p.vC);
+          pv.params = nullptr;                 // no weights: W
+          pv.pflows = lowrank->z_flows;
+          Timed t(h, KK_PARAM, c.s);
+          launch_gemm(EPI_PARAM, p.pl[GK_PARAM][0], p.pl[GK_PARAM][1], vshp, pv, c.s);
+        }
       }
-      if (zstat) {
-        pv.opA = (const uint16_t*)((char*)c.ws + p.vY2);
-        pv.opB = (const uint16_t*)((char*)c.ws + p.vC);
-        pv.params = nullptr;                 // no weights: W
-        pv.pflows = lowrank->z_flows;
-        Timed t(h, KK_PARAM, c.s);
-        launch_gemm(EPI_PARAM, p.pl[GK_PARAM][0], p.pl[GK_PARAM][1], vshp, pv, c.s);
-      }
-    }
-    for (size_t bi = 0; bi < h->blocks.size() && !p.vsum; ++bi) {
-      if (h->lr_p_off[bi] < 0) continue;
-      const BlockRec& bl = h->blocks[bi];
-      Timed t(h, KK_LRBWD, c.s);
-      launch_lr_fplus((float*)((char*)c.ws + p.lrP) + h->lr_p_off[bi] * p.lr_nsg, p.lr_nsg, (int64_t)bl.M * bl.N,
-                      param_flows + bl.param_offset, c.s);
-      if (zstat)
-        launch_lr_fplus((float*)((char*)c.ws + p.lrPz) + h->lr_p_off[bi] * p.lr_nsg, p.lr_nsg, (int64_t)bl.M * bl.N,
-                        lowrank->z_flows + bl.param_offset, c.s);
-    }
-    if (!chunks.empty()) {
-      launch_ready_chunks(-(1 << 29));
-      hipEvent_t e = (hipEvent_t)h->chunk_events[chunks.size()];
-      HIPCHECK(hipEventRecord(e, side));
-      HIPCHECK(hipStreamWaitEvent(c.s, e, 0));
-    } else if (h->has_plain_sums) {
-      Timed t(h, KK_PARAM, c.s);
-      launch_gemm(EPI_PARAM, p.pl[GK_PARAM][0], p.pl[GK_PARAM][1], pshp, pg, c.s);
     }
     check_launch();
     return PC_OK;

@@ -190,6 +190,14 @@ struct VBArgs {
   uint16_t* nhi;
   int64_t n_plane, n_rows, n_row0;
   int32_t np_n;
+  // e4m3 node-major operands instead of the bf16 planes (f8 = 1): bytes in
+  // 64-wide K-blocked panels of n_rows rows, one power-of-two scale byte per
+  // row and 32 consecutive K at (k / 32) * n_rows + row
+  int32_t f8;
+  uint8_t* n8lo;
+  uint8_t* n8hi;
+  uint8_t* s8lo;
+  uint8_t* s8hi;
   const float* C1;         // [B, M rounded up to 32] f / S, f / Z
   const float* C2;
   float* S;                // [B, M]

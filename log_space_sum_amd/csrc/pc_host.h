@@ -184,6 +184,7 @@ struct Handle {
   int64_t vx_rows = 0, vy_rows = 0;                // node-major rows of the X / C and Y1 / Y2 arenas
   int32_t v_max_k = 0;                             // widest contraction of the two per-layer products
   int opt_sumexp_fused = 0;                        // 1: "sum_exp" through the fused LowRank kernels
+  int opt_flow_fp8 = 0;                            // 1: "sum_exp" end products from e4m3 operands (auto)
   BlockRec* d_vblocks = nullptr;
   GroupRec* d_vgroups = nullptr;
   std::vector<RowSeg> rowsegs;
@@ -241,6 +242,8 @@ struct WsPlan {
   bool vsum;
   int32_t Qv, Qpad, QK;
   size_t vbt, vX, vC, vY1, vY2, vR;
+  bool vf8;                                        // e4m3 end products: the node-major operands below
+  size_t vX8, vC8, vY18, vY28, vXs, vCs, vY1s, vY2s;
   std::vector<int64_t> lr_pk_off;                    // per LowRank group: byte offset of its records
   int lr_nsg;                                        // LowRank parameter-flow partials: ceil(B/8)
   size_t partials, counters;

@@ -66,6 +66,29 @@ struct GemmArgs {
   float* vs_hi;
 };
 
+// The LowRank "sum_exp" parameter-flow products from e4m3 operands
+// (k_f8gemm.hip): node-major operand panels of 64-byte K blocks, one E8M0
+// scale per row and 32 consecutive K, 128 x 128 output tiles counted by the
+// blocks' pt128 prefix, the contraction over every tied copy (copy s of a
+// block at rows g_base + s * M_pad of A and e_base + s * N_pad of B).
+struct F8Args {
+  const uint8_t* A;
+  const uint8_t* sA;
+  int64_t rowsA;
+  const uint8_t* B;
+  const uint8_t* sB;
+  int64_t rowsB;
+  int32_t QK;                   // K of one copy (a multiple of 64)
+  int32_t nblocks;
+  const BlockRec* blocks;
+  const float* params;          // F+ = theta * product; null: W = product
+  float* out;                   // accumulated at each block's param_offset, rows of N
+  int32_t splitk;
+  float* partials;              // [tiles][splitk][128 x 128]
+  uint32_t* counters;           // one per tile, zero between launches
+};
+void launch_f8param(const F8Args& a, int tiles, hipStream_t s);
+
 // Output tile shapes of the product kernel (M x N per workgroup).
 enum GemmTile { TILE_AUTO = 0, TILE_128x128 = 1, TILE_256x128 = 2, TILE_256x256 = 3, TILE_128x256 = 4, TILE_128x64 = 5, TILE_64x128 = 6 };
 

@@ -157,12 +157,27 @@ def test_options():
     h = L.pc_compile_layout(W.hmm(64, 6, 9), device=-1)
     for name, good, bad in (("layer_tile", (0, 1, 2, 3, 4, 5), (6, -1)), ("param_tile", (0, 1, 2, 3), (4,)),
                             ("split_max", (1, 2, 4, 8), (0, 3, 16)), ("fuse", (0, 1), (2, -1)),
-                            ("param_chunk", (-1, 0, 1, 8, 100), (-2,)), ("lr_pack", (0, 1), (2, -1))):
+                            ("param_chunk", (-1, 0, 1, 8, 100), (-2,)), ("lr_pack", (0, 1), (2, -1)),
+                            ("sumexp_fused", (0, 1), (2, -1)), ("flow_fp8", (0, 1), (2, -1))):
         for v in good:
             L.pc_set_option(h, name, v)
         for v in bad:
             _expect(L.PC_ERR_INVALID_ARG, L.pc_set_option, h, name, v)
     _expect(L.PC_ERR_INVALID_ARG, L.pc_set_option, h, 9, 0)
+
+
+def test_flow_fp8_workspace():
+    """The e4m3 end products keep one byte (and a scale byte per 32) per
+    operand element instead of bf16 planes: a smaller workspace in auto mode,
+    the same one at fp32 level, where the option does not apply."""
+    h = L.pc_compile_layout(W.hmm(64, 6, 9, lowrank_rank=16, lowrank_form="sum_exp"), device=-1)
+    base = L.pc_workspace_bytes(h, 32)
+    L.pc_set_option(h, "flow_fp8", 1)
+    assert L.pc_workspace_bytes(h, 32) < base
+    L.pc_set_precision(h, "fp32")
+    f8 = L.pc_workspace_bytes(h, 32)
+    L.pc_set_option(h, "flow_fp8", 0)
+    assert L.pc_workspace_bytes(h, 32) == f8
 
 
 def test_host_only_handle_refuses_device_calls():

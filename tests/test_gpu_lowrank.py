@@ -251,3 +251,68 @@ def test_lowrank_full_size_sampled(mode):
     off = circ.meta["off_trans"]
     got = gpu["pflows"][off:off + H * H].reshape(H, H)[rows]
     G.check_flows(got, ref, mode, "full-size F+ rows (all copies and samples, per layer)")
+
+
+# The pages' measured error of the M-step ratio F+ / F- with fp8 end products
+# (LowRank page, Parameters: flow_precision), median and largest relative
+# error at the two ends of the factors' spread they report (0.3 and 4 nats).
+FP8_PAGE_ERR = {0.3: (3e-4, 2e-3), 4.0: (1.4e-2, 0.18)}
+
+
+def _ratio_err(gpu, orc, circ, params):
+    import oracle
+    inside = np.zeros(circ.num_params, bool)
+    for off, n in oracle.lowrank_param_ranges(circ):
+        inside[off:off + n] = True
+    keep = inside & (orc["z_flows"] > 0) & (params > 0)
+    r_o = orc["pflows"][keep] / orc["z_flows"][keep]
+    r_g = gpu["pflows"][keep].astype(np.float64) / gpu["z_flows"][keep].astype(np.float64)
+    err = np.abs(r_g - r_o) / np.abs(r_o)
+    return float(np.median(err)), float(err.max()), int((gpu["pflows"][keep] == 0).sum()), keep
+
+
+@pytest.mark.parametrize("spread", [0.3, 1.0, 4.0])
+def test_lowrank_sum_exp_flow_fp8(spread):
+    """PC_OPT_FLOW_FP8 (auto): the "sum_exp" parameter flows and denominator
+    statistic from e4m3 operands.  With as many terms per statistic entry as
+    the pages' measurement (63 tied copies x 64 samples x rank 16, here on 256
+    states), the M-step ratio F+ / F- against the float64 oracle end to end
+    is of the order of the pages' fp8 figures -- within twice their median
+    and largest error (at 1 nat: the 4-nat figures), a margin for another
+    instance of another size -- and no entry is made 0; the bf16 default's
+    error is printed beside.  Values,
+    element flows, dLL/dA, dLL/dB and the parameter flows outside the LowRank
+    blocks are bit-identical to the default."""
+    cfg = make_config("lowrank", H=256, T=64, V=32, rank=16, B=64, spread=spread, form="sum_exp")
+    circ = cfg["circuit"]
+    params = np.asarray(cfg["params"], np.float64)
+    G.say(f"case lowrank sum_exp flow_fp8 spread={spread}")
+    z0 = np.zeros(circ.num_params, np.float32)
+    g8 = G.run_gpu(cfg, "auto", z_init=z0, options=[("flow_fp8", 1)])
+    g16 = G.run_gpu(cfg, "auto", z_init=z0)
+    orc = G.run_oracle(cfg)
+    med8, max8, zeros8, keep = _ratio_err(g8, orc, circ, params)
+    med16, max16, _, _ = _ratio_err(g16, orc, circ, params)
+    G.say(f"  F+/F- relative error: fp8 median {med8:.3g} max {max8:.3g}; bf16 median {med16:.3g} max {max16:.3g}")
+    page_med, page_max = FP8_PAGE_ERR.get(spread, FP8_PAGE_ERR[4.0])
+    assert med8 <= 2 * page_med and max8 <= 2 * page_max, (med8, max8, page_med, page_max)
+    assert zeros8 == 0, f"{zeros8} parameter flows made 0"
+    for k in ("vals", "flows", "ll"):
+        assert np.array_equal(g8[k], g16[k], equal_nan=True), k
+    for s in range(len(g8["dA"])):
+        assert np.array_equal(g8["dA"][s], g16["dA"][s]) and np.array_equal(g8["dB"][s], g16["dB"][s])
+    import oracle
+    inside = np.zeros(circ.num_params, bool)
+    for off, n in oracle.lowrank_param_ranges(circ):
+        inside[off:off + n] = True
+    assert np.array_equal(g8["pflows"][~inside], g16["pflows"][~inside])
+
+
+def test_lowrank_sum_exp_flow_fp8_off_in_fp32():
+    """Under the fp32-level mode the option changes nothing (bit-identical)."""
+    cfg = make_config("lowrank", H=64, T=4, V=9, rank=16, B=29, spread=1.0, form="sum_exp")
+    z0 = np.zeros(cfg["circuit"].num_params, np.float32)
+    a = G.run_gpu(cfg, "fp32", z_init=z0, options=[("flow_fp8", 1)])
+    b = G.run_gpu(cfg, "fp32", z_init=z0)
+    for k in ("vals", "flows", "pflows", "z_flows"):
+        assert np.array_equal(a[k], b[k], equal_nan=True), k
