@@ -42,6 +42,12 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kChunkF = 512, kChunkB = 512;
 constexpr int kSlabF = 32 * (kChunkF + 4), kSlabB = 32 * (kChunkB + 4);
 
+// Order-preserving 32-bit key of a float (integer atomic max = float max).
+__device__ __forceinline__ uint32_t float_to_key_lr(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 __device__ __forceinline__ float key_to_shift_lr(uint32_t k) {
   const uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
   const float m = __uint_as_float(u);
@@ -224,13 +230,19 @@ __global__ __launch_bounds__(256) void k_lr_pack(LRPackArgs pa) {
 // ("exp_sum"), exp(A_b[i, k]) (c1 U[i, k] - c2 W[i, k]) ("sum_exp", whose U and
 // W sum theta e exp(B) and theta exp(B) over the children).
 __global__ __launch_bounds__(256) void k_lr_coef(LRArgs a) {
+  // four lanes per (sample, row): lane l takes ranks 4l .. 4l + 3 (+ 16 t), so
+  // the four lanes of a row read and write 64 contiguous bytes at a time
   const int ldC = (a.M + 31) / 32 * 32;
-  const int64_t xc = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t xt = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t xc = xt >> 2;
+  const int l = (int)(xt & 3);
   if (xc >= (int64_t)a.B * ldC) return;
   const int b = (int)(xc / ldC), i = (int)(xc - (int64_t)b * ldC);
   if (i >= a.M) {
-    a.C1[xc] = 0.0f;
-    a.C2[xc] = 0.0f;
+    if (l == 0) {
+      a.C1[xc] = 0.0f;
+      a.C2[xc] = 0.0f;
+    }
     return;
   }
   const int64_t x = (int64_t)b * a.M + i;
@@ -239,28 +251,37 @@ __global__ __launch_bounds__(256) void k_lr_coef(LRArgs a) {
     // the product node's flow, added to zero as the product backward does,
     // stored for both its children
     f = 0.0f + a.flows[(int64_t)(a.fp_pstart + i) * a.B + b];
-    a.out_flows[(int64_t)(a.out_start + i) * a.B + b] = f;
-    a.out_flows[(int64_t)(a.fp_other + i) * a.B + b] = f;
+    if (l == 0) {
+      a.out_flows[(int64_t)(a.out_start + i) * a.B + b] = f;
+      a.out_flows[(int64_t)(a.fp_other + i) * a.B + b] = f;
+    }
   } else {
     f = a.flows[(int64_t)(a.out_start + i) * a.B + b];
   }
   const float Z = a.Z[x], S = a.S[x];
   const bool ok = f != 0.0f && Z > 0.0f && S > 0.0f;
   const float c1 = ok ? f / S : 0.0f, c2 = ok ? f / Z : 0.0f;
-  a.C1[xc] = c1;
-  a.C2[xc] = c2;
+  if (l == 0) {
+    a.C1[xc] = c1;
+    a.C2[xc] = c2;
+  }
   const int kr = a.krank;
-  if (a.sumexp) {
-    for (int k = 0; k < kr; ++k)
-      a.dA[x * kr + k] = expf(a.A[x * kr + k]) * (c1 * a.U[x * kr + k] - c2 * a.W[x * kr + k]);
-  } else if ((kr & 3) == 0) {        // rows of U, W, dA 16-byte aligned
-    for (int k = 0; k < kr; k += 4) {
-      const float4 u = ld4(a.U + x * kr + k), w = ld4(a.W + x * kr + k);
-      *(float4*)(a.dA + x * kr + k) =
-          make_float4(c1 * u.x - c2 * w.x, c1 * u.y - c2 * w.y, c1 * u.z - c2 * w.z, c1 * u.w - c2 * w.w);
+  const int64_t o = x * kr;
+  if ((kr & 3) == 0) {        // rows of A, U, W, dA 16-byte aligned
+    for (int k = 4 * l; k < kr; k += 16) {
+      const float4 u = ld4(a.U + o + k), w = ld4(a.W + o + k);
+      float4 d = make_float4(c1 * u.x - c2 * w.x, c1 * u.y - c2 * w.y, c1 * u.z - c2 * w.z, c1 * u.w - c2 * w.w);
+      if (a.sumexp) {
+        const float4 av = ld4(a.A + o + k);
+        d = make_float4(expf(av.x) * d.x, expf(av.y) * d.y, expf(av.z) * d.z, expf(av.w) * d.w);
+      }
+      *(float4*)(a.dA + o + k) = d;
     }
   } else {
-    for (int k = 0; k < kr; ++k) a.dA[x * kr + k] = c1 * a.U[x * kr + k] - c2 * a.W[x * kr + k];
+    for (int k = l; k < kr; k += 4) {
+      const float d = c1 * a.U[o + k] - c2 * a.W[o + k];
+      a.dA[o + k] = a.sumexp ? expf(a.A[o + k]) * d : d;
+    }
   }
 }
 
@@ -455,12 +476,33 @@ __global__ __launch_bounds__(256) void k_lr_fwd(LRArgs a) {
   }
   const float Z = Zp + __shfl_xor(Zp, 32), S = Sp + __shfl_xor(Sp, 32);
   const int i = i0 + l32;
-  if (!act || i >= M) return;
+  const bool live = act && i < M;
+  const float v = live ? ((Z > 0.0f && S > 0.0f) ? key_to_shift_lr(a.mkeys[(int64_t)a.m_row * a.B + bq]) + logf(S / Z)
+                                                  : -INFINITY)
+                       : -INFINITY;
+  if (a.ep_on) {
+    // the product layer above (its node = children added in child order, as
+    // the product kernel does) and the maximum of the wave's 32 rows of
+    // sample b for the next sum layer's shift
+    float pm = -INFINITY;
+    if (live && h == 0) {
+      const int q = a.out_start + i - a.ep_base_s;
+      if (q >= 0 && q < a.ep_pcount) {
+        const float o = a.vals[(int64_t)(a.ep_base_o + q) * a.B + b];
+        const float pv = a.ep_qs == 0 ? (0.0f + v) + o : (0.0f + o) + v;
+        a.vals[(int64_t)(a.ep_pstart + q) * a.B + b] = pv;
+        pm = pv;
+      }
+    }
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) pm = fmaxf(pm, __shfl_xor(pm, d));
+    if (lane == 0 && act) atomicMax(a.mkeys_out + (int64_t)a.ep_mrow * a.B + b, float_to_key_lr(pm));
+  }
+  if (!live) return;
   if (h == 0) {
-    const float sh = key_to_shift_lr(a.mkeys[(int64_t)a.m_row * a.B + b]);
     a.Z[(int64_t)b * M + i] = Z;
     a.S[(int64_t)b * M + i] = S;
-    a.vals[(int64_t)(a.out_start + i) * a.B + b] = (Z > 0.0f && S > 0.0f) ? sh + logf(S / Z) : -INFINITY;
+    a.vals[(int64_t)(a.out_start + i) * a.B + b] = v;
   }
   // accumulator register r of rank block kb: row k = kb*32 + (r/4)*8 + h*4 + r%4, column i
 #pragma unroll
@@ -803,7 +845,7 @@ void launch_lr_pack(const LRPackArgs& pa, int fp32, hipStream_t s) {
   else lr_pack_k<2, 1>(pa, grid, s);
 }
 void launch_lr_coef(const LRArgs& a, hipStream_t s) {
-  const int64_t n = (int64_t)a.B * ((a.M + 31) / 32 * 32);
+  const int64_t n = (int64_t)a.B * ((a.M + 31) / 32 * 32) * 4;
   launch_kernel(k_lr_coef, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
 }
 void launch_lr_fwd(const LRArgs& a, int fp32, hipStream_t s) {

@@ -913,7 +913,11 @@ void run_forward(const Call& c, const int32_t* tokens, const float* params, floa
         for (int q = 0; q < 8; ++q) a.fp_abase[q] = pp.abase[q];
         a.wvals = node_vals;
       }
-      if (!(h->opt_fuse && sp.epi_max)) {   // else published by the previous layer's product epilogue
+      // the column maxima are published by the previous layer when it has a
+      // product epilogue: plain layers' forward products and the fused
+      // LowRank forward kernels (not the "sum_exp" virtual batch)
+      const bool published = h->opt_fuse && sp.epi_max && !(p.vsum && h->sums[sp.epi_src].lowrank);
+      if (!published) {
         Timed t(h, KK_COLMAX, c.s);
         launch_colmax(a, sp.pktiles, c.s);
       }
@@ -937,6 +941,17 @@ void run_forward(const Call& c, const int32_t* tokens, const float* params, floa
             continue;
           }
           LRArgs la = lr_args(c, sp, gi, lowrank, params, node_vals, nullptr);
+          if (h->opt_fuse && sp.epi_prod >= 0) {     // the product layer above and the next shift
+            const ProductPlan& pp = h->prods[sp.epi_prod];
+            la.ep_on = 1;
+            la.ep_qs = sp.epi_qs;
+            la.ep_base_s = pp.abase[sp.epi_qs];
+            la.ep_base_o = pp.abase[1 - sp.epi_qs];
+            la.ep_pstart = pp.node_start;
+            la.ep_pcount = pp.num_nodes;
+            la.ep_mrow = sp.epi_mrow;
+            la.mkeys_out = v.mkeys;
+          }
           if (h->opt_lr_pack == 1) {
             Timed t(h, KK_SPLIT, c.s);
             lr_pack_group(c, sp, gi, lowrank);

@@ -667,20 +667,20 @@ Handle* compile_layout(const pc_circuit_desc* d) {
       sp.bwd_prod = b.idx;
     }
   }
-  // Forward product epilogues (see SumPlan::epi_prod): plain sum layer L1,
-  // affine product layer P of two children per node evaluated by the next sum
-  // layer's column maxima (fwd_fused), plain sum layer L3 with a single group
-  // whose children are
-  // exactly P's nodes.  P's child range q_s must be L1's outputs node for
-  // node, its other child ranges must avoid L1's outputs.
+  // Forward product epilogues (see SumPlan::epi_prod): sum layer L1 (its
+  // product kernel's epilogue, or for a LowRank layer the kernel that writes
+  // its node values), affine product layer P of two children per node
+  // evaluated by the next sum layer's column maxima (fwd_fused), sum layer L3
+  // with a single group whose children are exactly P's nodes.  P's child
+  // range q_s must be L1's outputs node for node, its other child ranges must
+  // avoid L1's outputs.
   for (size_t li = 0; li + 2 < h->layers.size(); ++li) {
     const LayerRef a = h->layers[li], b = h->layers[li + 1], c = h->layers[li + 2];
     if (a.kind != PC_LAYER_SUM || b.kind != PC_LAYER_PRODUCT || c.kind != PC_LAYER_SUM) continue;
     SumPlan& s1 = h->sums[a.idx];
     ProductPlan& pp = h->prods[b.idx];
     SumPlan& s3 = h->sums[c.idx];
-    if (s1.lowrank || s3.lowrank || !pp.affine || pp.max_deg != 2 || !pp.fwd_fused || s3.fwd_prod != b.idx)
-      continue;
+    if (!pp.affine || pp.max_deg != 2 || !pp.fwd_fused || s3.fwd_prod != b.idx) continue;
     if (s3.groups.size() != 1 || s3.groups[0].N != pp.num_nodes) continue;
     {   // L3's children: P's nodes, each once
       const GroupRec& r = s3.groups[0];
@@ -717,6 +717,7 @@ Handle* compile_layout(const pc_circuit_desc* d) {
     s1.epi_qs = qs;
     s1.epi_mrow = s3.groups[0].m_row;
     s3.epi_max = true;
+    s3.epi_src = a.idx;
   }
   // Element-flow product epilogues (see SumPlan::gp_sum): plain single-group
   // sum layer A (M a multiple of 64), affine two-child product layer P fused

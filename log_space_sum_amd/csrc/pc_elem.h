@@ -120,6 +120,13 @@ struct LRArgs {
   // coefficients: the following product layer's backward first (fp_on): the
   // flow of product node fp_pstart + i goes to output i and to node fp_other + i
   int32_t fp_on, fp_pstart, fp_other;
+  // forward: the following affine two-child product layer evaluated with the
+  // node values (ep_on): output node n is child ep_qs of product node
+  // q = n - ep_base_s when 0 <= q < ep_pcount, whose other child is
+  // ep_base_o + q; the product value goes to node ep_pstart + q and its
+  // per-sample maximum to keys row ep_mrow (the next sum layer's shift)
+  int32_t ep_on, ep_qs, ep_base_s, ep_base_o, ep_pstart, ep_pcount, ep_mrow;
+  uint32_t* mkeys_out;
   int32_t sumexp;        // the "sum_exp" form (records of exp(A), exp(B))
   const int32_t* chblocks;
   const float* theta;

@@ -81,7 +81,8 @@ struct SumPlan {
   // the one before it in the column-max kernel (forward), the one after it in
   // the scaled-flow packing (backward).
   int fwd_prod = -1, bwd_prod = -1;
-  // Forward product epilogue: this layer's forward product also evaluates the
+  // Forward product epilogue: this layer's forward product (LowRank layers:
+  // the kernel that writes their node values) also evaluates the
   // affine product layer epi_prod that follows it (its nodes i take child
   // epi_qs, abase[epi_qs] + i, from this layer's outputs; their other
   // children come from earlier layers) and publishes the column maxima of the
@@ -90,6 +91,7 @@ struct SumPlan {
   // (epi_max).
   int epi_prod = -1, epi_qs = -1, epi_mrow = -1;
   bool epi_max = false;
+  int epi_src = -1;                                // the sum layer publishing this layer's maxima
   // Element-flow product epilogue: this layer's element-flow product also does
   // the scaled-flow packing of sum layer gp_sum (the backward of the affine
   // two-child product layer gp_prod between them: the product node's flow
