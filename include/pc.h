@@ -151,7 +151,13 @@ typedef struct pc_handle_s* pc_handle;
  * f_b[i] * exp(A_b B_b)[i,j] / Z_b[i] for every LowRank weight block, in the
  * parameter flows' layout; pc_backward ADDS it (like param_flows; only the
  * LowRank blocks' entries are touched; 0 where f = 0 or Z = 0).  NULL skips
- * it (the statistic costs one more pass over every (sample, node, child)). */
+ * it (the statistic costs one more pass over every (sample, node, child)).
+ * Supported factor range: the kernels form theta * g in float32 with no
+ * per-row shift, so every exp(h) (h = (A_b B_b)[i,j], or each exp(A) and
+ * exp(B) of the "sum_exp" form) must be finite and each row's largest
+ * theta * g a normal float32: h <= about 88 + |log theta| nats and the row's
+ * largest h above about -87 + |log theta|.  Outside it a row's value is
+ * non-finite or -inf where the exact one is finite. */
 typedef struct pc_lowrank_io {
   int32_t num_slots;
   const float* const* A;
