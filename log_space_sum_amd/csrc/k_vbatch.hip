@@ -130,24 +130,37 @@ __device__ __forceinline__ int child_vb(const VBArgs& a, int j) {
 // products' columns there are never stored).
 __global__ __launch_bounds__(512) void k_vb_fwd_pack(VBArgs a) {
   __shared__ float tx[64][65], tc[64][65];
+  __shared__ float te[64][65];     // e of the tile's children for its samples (q0 / k ..)
   const int nqt = (a.QK + 63) / 64;
   const int qt = blockIdx.x % nqt, jt = blockIdx.x / nqt;
   const int q0 = qt * 64, j0 = jt * 64;
   const int tid = threadIdx.x;
+  // phase 0: e[j, b] = exp(child j - m[b]) once per (child, sample) of the
+  // tile (its 64 virtual columns cover at most 64 samples), not once per rank
+  {
+    const int bfirst = q0 / a.krank;
+    const int nb = min((q0 + 63) / a.krank, a.B - 1) - bfirst + 1;
+    for (int it = tid; it < 64 * nb; it += 512) {
+      const int jl = it & 63, bl = it >> 6, j = j0 + jl, b = bfirst + bl;
+      float ev = 0.0f;
+      if (j < a.N) ev = expf(a.vals[(int64_t)child_vb(a, j) * a.B + b] - key_shift_vb(a.mkeys[(int64_t)a.m_row * a.B + b]));
+      te[bl][jl] = ev;
+    }
+  }
+  __syncthreads();
   {
     const int r8 = tid >> 3, c8 = tid & 7;
     const int q = q0 + r8, jb = j0 + c8 * 8;
     float x[8], cc[8];
     const bool qv = q < a.Q;
-    const int b = qv ? q / a.krank : 0;
-    const float sh = qv ? key_shift_vb(a.mkeys[(int64_t)a.m_row * a.B + b]) : 0.0f;
+    const int bl = qv ? q / a.krank - q0 / a.krank : 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int j = jb + e;
       float cv = 0.0f, ev = 0.0f;
       if (qv && j < a.N) {
         cv = expf(a.Bf[(int64_t)q * a.N + j]);
-        ev = expf(a.vals[(int64_t)child_vb(a, j) * a.B + b] - sh);
+        ev = te[bl][c8 * 8 + e];
       }
       cc[e] = cv;
       x[e] = cv * ev;
