@@ -1192,7 +1192,10 @@ static void launch_colmax_v(const SumArgs& a, int row_tiles, hipStream_t s) {
     launch_kernel((k_colmax<2, PROD, 16>), dim3(g2), dim3(256), 0, s, a);
   else if (g1 >= 512)
     launch_kernel((k_colmax<1, PROD, 16>), dim3(g1), dim3(256), 0, s, a);
-  else if (g1 * 4 >= 512)
+  // small layers: fewer workgroups with 16 children each rather than 256
+  // with 4 (each workgroup publishes one atomic maximum per sample; on 1024
+  // children x 64 samples: 4.6 us instead of 7.7)
+  else if (g1 * 4 >= 64)
     launch_kernel((k_colmax<1, PROD, 4>), dim3(g1 * 4), dim3(256), 0, s, a);
   else
     launch_kernel((k_colmax<1, PROD, 1>), dim3(g1 * 16), dim3(256), 0, s, a);
