@@ -316,3 +316,25 @@ def test_lowrank_sum_exp_flow_fp8_off_in_fp32():
     b = G.run_gpu(cfg, "fp32", z_init=z0)
     for k in ("vals", "flows", "pflows", "z_flows"):
         assert np.array_equal(a[k], b[k], equal_nan=True), k
+
+
+def test_lowrank_sum_exp_flow_fp8_ragged():
+    """The e4m3 end products on ragged sizes: 200 states (tiles past the
+    rows), rank 5 and batch 37 (185 virtual columns, K steps ending mid-way
+    through a 64-wide block, an odd number of K steps per copy).  Few terms
+    per statistic entry here, so the bar is the pages' 4-nat fp8 figures
+    (twice the median and the largest error); padding read as data would
+    fail it by orders of magnitude, or give non-finite entries."""
+    cfg = make_config("lowrank", H=200, T=6, V=16, rank=5, B=37, spread=1.0, form="sum_exp")
+    circ = cfg["circuit"]
+    params = np.asarray(cfg["params"], np.float64)
+    G.say("case lowrank sum_exp flow_fp8 ragged H200 r5 B37")
+    z0 = np.zeros(circ.num_params, np.float32)
+    g8 = G.run_gpu(cfg, "auto", z_init=z0, options=[("flow_fp8", 1)])
+    orc = G.run_oracle(cfg)
+    med8, max8, zeros8, keep = _ratio_err(g8, orc, circ, params)
+    G.say(f"  F+/F- relative error: fp8 median {med8:.3g} max {max8:.3g}")
+    assert np.isfinite(g8["pflows"]).all() and np.isfinite(g8["z_flows"]).all()
+    page_med, page_max = FP8_PAGE_ERR[4.0]
+    assert med8 <= 2 * page_med and max8 <= 2 * page_max, (med8, max8)
+    assert zeros8 == 0
