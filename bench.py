@@ -274,7 +274,7 @@ def main():
                          "dispatch for scaling FETCH_SIZE / WRITE_SIZE counters to bytes")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for {args.gpus}).",
+        print(f"bench.py runs on one GPU: the library has no multi-GPU path (asked for {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
 
