@@ -944,8 +944,9 @@ __device__ __forceinline__ void split_store4(const float (&x)[4], int np, uint16
   }
 }
 
-// Weights of every block split into planes, row-major [M_pad, N_padK] (forward
-// operand) and transposed [N_pad, M_padK] (element-flow operand).  A 64 x 64
+// Weights of every block split into planes, [M_pad, N_padK] (forward operand)
+// and transposed [N_pad, M_padK] (element-flow operand), both in fragment
+// order (frag_major).  A 64 x 64
 // tile per workgroup; each thread takes 4 consecutive columns of 4 rows (all
 // four loads issued first, 16-byte loads when the block's rows are 16-byte
 // aligned), and after the LDS transpose 4 consecutive rows of 4 columns, so
@@ -959,7 +960,6 @@ __global__ __launch_bounds__(256) void k_theta_pack(ThetaArgs a) {
   const int lt = t - bl.pk_start;
   const int i0 = (lt / ntj) * 64, j0 = (lt % ntj) * 64;
   const int NpK = (bl.N + K_PAD - 1) / K_PAD * K_PAD, MpK = (bl.M + K_PAD - 1) / K_PAD * K_PAD;
-  const int64_t Mp = (bl.M + ROW_PAD - 1) / ROW_PAD * ROW_PAD, Np = (bl.N + ROW_PAD - 1) / ROW_PAD * ROW_PAD;
   const bool vec = ((bl.param_offset | (int64_t)bl.N) & 3) == 0;
   const int tid = threadIdx.x, rr = tid >> 4, c4 = (tid & 15) * 4;
   const int j = j0 + c4;
@@ -981,7 +981,7 @@ __global__ __launch_bounds__(256) void k_theta_pack(ThetaArgs a) {
     const int r = rr + 16 * q;
 #pragma unroll
     for (int e = 0; e < 4; ++e) tile[r][c4 + e] = x[q][e];
-    if (j < NpK) split_store4(x[q], a.np_fwd, a.theta + bl.th_off + panel(i0 + r, j, Mp), a.theta_plane);
+    if (j < NpK) split_store4(x[q], a.np_fwd, a.theta + bl.th_off + frag_major(i0 + r, j, NpK >> 5), a.theta_plane);
   }
   __syncthreads();
   const int i = i0 + c4;                       // 4 consecutive rows of the block
@@ -990,7 +990,7 @@ __global__ __launch_bounds__(256) void k_theta_pack(ThetaArgs a) {
   for (int q = 0; q < 4; ++q) {
     const int jl = rr + 16 * q;
     const float y[4] = {tile[c4][jl], tile[c4 + 1][jl], tile[c4 + 2][jl], tile[c4 + 3][jl]};
-    split_store4(y, a.np_elem, a.thetaT + bl.tht_off + panel(j0 + jl, i, Np), a.thetaT_plane);
+    split_store4(y, a.np_elem, a.thetaT + bl.tht_off + frag_major(j0 + jl, i, MpK >> 5), a.thetaT_plane);
   }
 }
 

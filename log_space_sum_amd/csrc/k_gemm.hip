@@ -164,22 +164,45 @@ struct ReadOrder {
   }
 };
 
+// The same for B alone (the weights in registers): read u < PB*FN is plane
+// u/FN, column block u%FN.
+template <int PA, int PB, int FM, int FN>
+struct ReadOrderB {
+  using PP = Pairs<PA, PB>;
+  static constexpr int NRD = PB * FN;
+  static constexpr int at(int o) {
+    bool seen[NRD] = {};
+    int n = 0;
+    for (int t = 0; t < PP::N * FM * FN; ++t) {
+      const int pr = t / (FM * FN), j = t % FN;
+      const int ub = PP::at(pr, 1) * FN + j;
+      if (!seen[ub]) {
+        seen[ub] = true;
+        if (n++ == o) return ub;
+      }
+    }
+    return 0;
+  }
+};
+
 // LDS ring geometry.  A stage holds one K slice (KT wide) of every plane of
-// both operands, rows unpadded (KT * 2 bytes), 16-byte chunks XOR-swizzled by
+// the operands it carries (both, or only B when the weights go straight to
+// registers: AD), rows unpadded (KT * 2 bytes), 16-byte chunks XOR-swizzled by
 // row so that the 128-bit fragment reads of 16 consecutive rows touch 16
 // distinct chunk slots of 64 banks (and those of 8 consecutive rows 8 distinct
 // slots of 32 banks).  One wave load instruction fills 1 KB (64 lanes x 16 B)
 // of a stage: RPI rows.
-template <int PA, int PB, int MT, int NT, int KT>
+template <int PA, int PB, int MT, int NT, int KT, bool AD>
 struct Ring {
   static constexpr int RB = KT * 2;                 // bytes per row of a slice
   static constexpr int CPR = RB / 16;               // 16-byte chunks per row (8 or 4)
   static constexpr int RPI = 1024 / RB;             // rows per load instruction (8 or 16)
+  static constexpr int AIN = AD ? 0 : PA;           // A planes in the ring
   static constexpr int AEL = MT * KT, BEL = NT * KT;                 // elements per plane
-  static constexpr int STAGE = PA * AEL + PB * BEL;                   // elements per stage
+  static constexpr int STAGE = AIN * AEL + PB * BEL;                  // elements per stage
   static constexpr int IA = MT / RPI, IB = NT / RPI;                 // instructions per plane
-  static constexpr int PER_WAVE = (PA * IA + PB * IB) / 4;           // instructions per wave per slice
-  static constexpr int QA = PA * IA / 4;                              // of which A
+  static constexpr int PER_WAVE = (AIN * IA + PB * IB) / 4;          // instructions per wave per slice
+  static constexpr int QA = AIN * IA / 4;                             // of which A
   static_assert(IA % 4 == 0 && IB % 4 == 0, "each wave loads whole instructions of one plane");
 
   static __device__ __forceinline__ int swz(int row) {
@@ -193,7 +216,11 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
   constexpr int WTM = MT / WM, WTN = NT / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   constexpr int SUB = ROW_PAD / MT;            // tiles per 256-row block
-  using R = Ring<PA, PB, MT, NT, KT>;
+  // forward, element-flow and virtual-batch products: the weights (A) go
+  // from global memory straight into registers in fragment order, the ring
+  // carries B only
+  constexpr bool AD = EPI != EPI_PARAM;
+  using R = Ring<PA, PB, MT, NT, KT, AD>;
   using PP = Pairs<PA, PB>;
   constexpr int KS = KT / 16;                  // matrix K steps per slice
   constexpr int NMF = PP::N * FM * FN;         // matrix instructions per K step
@@ -205,7 +232,10 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
   // the ring: NS stages (the loads filling it are issued from inline
   // assembly, so the compiler tracks no dependence between a stage being
   // filled and the reads of another)
-  __shared__ __attribute__((aligned(1024))) uint16_t ring[NS * R::STAGE];
+  // (the epilogue reuses it for its pass tile, column shifts, child rows and maxima)
+  constexpr int EPI_FLOATS = WM * 32 * (NT + 8) + NT + MT + (256 / (NT / 4)) * NT;
+  constexpr int RING_EL = NS * R::STAGE > 2 * EPI_FLOATS ? NS * R::STAGE : 2 * EPI_FLOATS;
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[RING_EL];
   __shared__ int last_flag;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -229,6 +259,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
   int kst, kbeg, kend, m0, n0;
   int64_t acopy = 0, bcopy = 0;                // row step per tied copy (parameter flows)
   int ka0 = 0, kb0 = 0;
+  int ksl_a = 0;                               // AD: K slices of the weight block (its fragment-order row pitch)
   GroupRec gr{};
   BlockRec bl{};
   if (EPI == EPI_FWD || EPI == EPI_ELEM || EPI == EPI_VSTORE) {
@@ -258,6 +289,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
       kb0 = gr.g_koff;
     }
     ra0 = m0;
+    ksl_a = ((fwdA ? bl.N : bl.M) + K_PAD - 1) / K_PAD * K_PAD / 32;
     Bb = a.opB;
     kbeg = split * kst / S;
     kend = (split + 1) * kst / S;
@@ -311,7 +343,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
     constexpr int q0 = decltype(Q)::value;
     const int qq = q0 * 4 + wave;
     constexpr bool isA = q0 < R::QA;
-    const int qi = isA ? qq % R::IA : (qq - PA * R::IA) % R::IB;
+    const int qi = isA ? qq % R::IA : (qq - R::AIN * R::IA) % R::IB;
     const int row = qi * R::RPI + lane / R::CPR;
     const int chunk = (lane % R::CPR) ^ R::swz(row);     // the swizzle is an involution
     const int64_t rows = isA ? RA : RB;
@@ -350,6 +382,12 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
   // uniform byte bases of the next slice to load
   const char* sa = nullptr;
   const char* sb = nullptr;
+  // AD: this lane's 16 bytes of K step 0 of slice kbeg, row block
+  // (m0 + wm0) / 32, plane 0 (fragment order: a slice is 2048 bytes, a K step
+  // 1024, the next row block ksl_a slices on, the next plane pAb bytes on)
+  const char* a_lane = nullptr;
+  if constexpr (AD) a_lane = (const char*)Ab + (((int64_t)((m0 + wm0) >> 5) * ksl_a + kbeg) * 2048 + lane * 16);
+  const char* sA = nullptr;
   // (past the last slice the ring keeps re-loading it: the stages it lands in
   // are never read, and every wait stays a constant)
   auto slice_bases = [&]() {
@@ -368,6 +406,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
       ea = ((int64_t)((ka0 + k) >> 5) * RA + ra0) * 32;
       eb = ((int64_t)((kb0 + k) >> 5) * RB + rb0) * 32;
     }
+    if constexpr (AD) sA = a_lane + (int64_t)next_load * 2048;
     ++next_load;
     sa = (const char*)Ab + ea * 2;
     sb = (const char*)Bb + eb * 2;
@@ -376,11 +415,12 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
   auto dma = [&](int j, auto Q) {
     constexpr int q0 = decltype(Q)::value;
     constexpr bool isA = q0 < R::QA;
-    constexpr int p = isA ? (q0 * 4) / R::IA : (q0 * 4 - PA * R::IA) / R::IB;
+    constexpr int p = isA ? (q0 * 4) / R::IA : (q0 * 4 - R::AIN * R::IA) / R::IB;
     const char* base = isA ? sa + p * pAb : sb + p * pBb;
     lds_load16(base, voff[q0], ring_lds + j * (R::STAGE * 2) + (q0 * 4 + wave) * 1024);
   };
 
+  if constexpr (!AD) {
   bf16x8_t fa[2][PA][FM], fb[2][PB][FN];
   // fragment read u of K step KSI of a stage into buffer BF
   auto frag = [&](auto BF, int sbyte, auto KSI, auto U) {
@@ -394,7 +434,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
     } else {
       constexpr int p = (u - PA * FM) / FN, jj = (u - PA * FM) % FN;
       fb[bf][p][jj] =
-          *(const bf16x8_t*)(st + (sbyte + b_off[ks]) + (PA * R::AEL * 2 + p * R::BEL * 2 + jj * 32 * R::RB));
+          *(const bf16x8_t*)(st + (sbyte + b_off[ks]) + (R::AIN * R::AEL * 2 + p * R::BEL * 2 + jj * 32 * R::RB));
     }
   };
   auto mfma = [&](auto BF, auto T) {
@@ -467,6 +507,111 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
     }
     step(std::true_type(), j);
   }
+  } else {
+  // ---- weights in registers: slice s of A in buffer s % NS -------------------
+  // Each wave loads its own FM row blocks of every plane, QD loads of 1 KB per
+  // slice (ordinary loads: the compiler waits for them before their first
+  // use); B streams through the ring as above.  The main loop is unrolled NS
+  // times so that the register buffer and the stage of every step are
+  // constants.  Every step issues its loads (past the last slice it re-loads
+  // that slice, into a buffer and stage nobody reads), and every step waits
+  // for the next slice and reads its first fragments (after the last one the
+  // stage read holds an old slice and the values go unused): the waits stay
+  // constants.
+  constexpr int QD = PA * FM * KS;             // direct weight loads per wave per slice
+  constexpr int PWA = PW + QD;                 // vector-memory instructions per wave per slice
+  constexpr int NRB = PB * FN;                 // fragment reads (B) per K step
+  using RB_ = ReadOrderB<PA, PB, FM, FN>;
+  bf16x8_t areg[NS][PA][FM][KS];
+  bf16x8_t fb[2][PB][FN];
+  // direct load q of the slice at sA into buffer BUF
+  auto aload = [&](auto BUF, auto Q) {
+    constexpr int buf = decltype(BUF)::value, q = decltype(Q)::value;
+    constexpr int p = q / (FM * KS), i = (q / KS) % FM, ks = q % KS;
+    areg[buf][p][i][ks] = *(const bf16x8_t*)(sA + p * pAb + (int64_t)i * ksl_a * 2048 + ks * 1024);
+  };
+  // B fragment read u of K step KSI of the stage at byte sbyte into buffer BF
+  auto fragb = [&](auto BF, int sbyte, auto KSI, auto U) {
+    constexpr int bf = decltype(BF)::value;
+    constexpr int ks = decltype(KSI)::value;
+    constexpr int u = decltype(U)::value;
+    constexpr int p = u / FN, jj = u % FN;
+    const char* st = (const char*)ring;
+    fb[bf][p][jj] = *(const bf16x8_t*)(st + (sbyte + b_off[ks]) + (p * R::BEL * 2 + jj * 32 * R::RB));
+  };
+  auto mfmad = [&](auto BUF, auto KSI, auto BF, auto T) {
+    constexpr int buf = decltype(BUF)::value, ks = decltype(KSI)::value, bf = decltype(BF)::value;
+    constexpr int t = decltype(T)::value;
+    constexpr int pr = t / (FM * FN), i = (t / FN) % FM, j = t % FN;
+    constexpr int pa = PP::at(pr, 0), pb = PP::at(pr, 1);
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(areg[buf][pa][i][ks], fb[bf][pb][j], acc[i][j], 0, 0, 0);
+  };
+  constexpr int H = NMF / 2;
+  auto stepd = [&](auto JC) {
+    constexpr int J = decltype(JC)::value;
+    constexpr int JN = (J + 1) % NS, JL = (J + NS - 1) % NS;
+    constexpr int sbyte = J * (R::STAGE * 2), snext = JN * (R::STAGE * 2);
+    slice_bases();
+    sfor<KS>([&](auto KSI) {
+      constexpr int ks = decltype(KSI)::value;
+      constexpr int bf = ks & 1;
+      using BF = std::integral_constant<int, bf>;
+      using BN = std::integral_constant<int, bf ^ 1>;
+      constexpr bool lastks = ks + 1 == KS;
+      if constexpr (lastks) {
+        // the next slice has landed once at most the NS-2 slices issued after it are in flight
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(WaitVmLgkm<(NS - 2) * PWA>::imm);
+        ring_barrier();
+      }
+      sfor<NMF>([&](auto T) {
+        constexpr int t = decltype(T)::value;
+        mfmad(std::integral_constant<int, J>(), KSI, BF(), T);
+        if constexpr (t < H) {
+          constexpr int o0 = t * NRB / H, o1 = (t + 1) * NRB / H;
+          sfor<o1 - o0>([&](auto O) {
+            constexpr int u = RB_::at(o0 + decltype(O)::value);
+            if constexpr (!lastks) fragb(BN(), sbyte, std::integral_constant<int, ks + 1>(), std::integral_constant<int, u>());
+            else fragb(std::integral_constant<int, 0>(), snext, std::integral_constant<int, 0>(), std::integral_constant<int, u>());
+          });
+        } else if constexpr (ks == 0) {
+          constexpr int o0 = (t - H) * PWA / (NMF - H), o1 = (t - H + 1) * PWA / (NMF - H);
+          sfor<o1 - o0>([&](auto O) {
+            constexpr int q = o0 + decltype(O)::value;
+            if constexpr (q < QD) aload(std::integral_constant<int, JL>(), std::integral_constant<int, q>());
+            else dma(JL, std::integral_constant<int, q - QD>());
+          });
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    });
+  };
+  if (n > 0) {
+    // prologue: slices 0 .. NS-2 in flight, slice 0 readable, its first fragments read
+    sfor<NS - 1>([&](auto S0) {
+      slice_bases();
+      sfor<QD>([&](auto Q) { aload(S0, Q); });
+      sfor<PW>([&](auto Q) { dma(decltype(S0)::value, Q); });
+    });
+    __builtin_amdgcn_s_waitcnt(WaitVmLgkm<(NS - 2) * PWA>::imm);
+    ring_barrier();
+    sfor<NRB>([&](auto U) { fragb(std::integral_constant<int, 0>(), 0, std::integral_constant<int, 0>(), U); });
+    // whole rounds of NS steps with no branch between the steps (so the
+    // compiler's waits for the weight registers count every load issued
+    // since), then the last n % NS steps
+    int it0 = 0;
+    for (; it0 + NS <= n; it0 += NS) sfor<NS>([&](auto JC) { stepd(JC); });
+    if (it0 < n)
+      sfor<NS - 1>([&](auto JC) {
+        if (it0 + decltype(JC)::value < n) stepd(JC);
+      });
+  }
+  }
+  // 32 wait states between the last matrix instructions and the branches to
+  // the code that reads the accumulators (split-K partials, epilogue).
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(0);       // no load may still target LDS past this point
 
   // ---- split-K: the last workgroup of a tile adds the partials in order -----
@@ -564,7 +709,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
   constexpr int NCH = PR * NT / 4 / 256;       // 4-column chunks per thread per pass
   constexpr int TPC = 256 / (NT / 4);          // threads sharing a 4-column chunk (product-epilogue maxima)
   static_assert(PR * NT % 1024 == 0, "whole chunks per thread");
-  static_assert((PR * LDT + NT + MT + TPC * NT) * 4 <= NS * R::STAGE * 2, "epilogue tile fits the ring");
+  static_assert((PR * LDT + NT + MT + TPC * NT) * 4 <= RING_EL * 2, "epilogue tile fits the ring");
   const int B = a.B;
   float* tl = (float*)ring;                    // [PR][LDT]
   float* sh_col = tl + PR * LDT;               // [NT]
@@ -800,8 +945,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
 template <int EPI, int PA, int PB, int MT, int NT, int WM>
 static void launch_shape(int grid, const GemmArgs& a, hipStream_t s) {
   constexpr int KT = gemm_kt(PA, PB, MT, NT);
-  constexpr int NS = gemm_stages(PA, PB, MT, NT);
-  static_assert(NS >= 2, "LDS ring needs two stages");
+  constexpr int NS = EPI == EPI_PARAM ? gemm_stages(PA, PB, MT, NT) : gemm_stages_direct(PA, PB, MT, NT, MT / WM / 32);
+  static_assert(NS >= (EPI == EPI_PARAM ? 2 : 3), "LDS ring stages");
   launch_kernel((k_gemm<EPI, PA, PB, MT, NT, WM, KT, NS>), dim3(grid), dim3(256), 0, s, a);
 }
 
@@ -817,12 +962,14 @@ static void launch_tile(int tile, int grid, const GemmArgs& a, hipStream_t s) {
     if (tile == TILE_128x256) launch_shape<EPI, PA, PB, 128, 256, 2>(grid, a, s);
     else launch_shape<EPI, PA, PB, 128, 128, 2>(grid, a, s);
   } else {
-    if (tile == TILE_256x128) launch_shape<EPI, PA, PB, 256, 128, 2>(grid, a, s);
+    // the weights go to registers: 128 x 64 and 256 x 128 with the waves
+    // stacked along M, each loading only its own rows; 64 x 128, 128 x 128
+    // and 128 x 256 with 2 x 2 waves, two waves loading each row block (four
+    // 32 x 128 waves on 128 x 128 tiles gave wrong sums in three accumulator
+    // registers with fewer than three planes per operand, cause not found)
+    if (tile == TILE_256x128) launch_shape<EPI, PA, PB, 256, 128, 4>(grid, a, s);
     else if (tile == TILE_128x256) launch_shape<EPI, PA, PB, 128, 256, 2>(grid, a, s);
-    // 128 x 64: waves side by side along M (32 x 64 each) when the first
-    // operand has more planes, else 2 x 2 (64 x 32 each): the fewer fragment
-    // reads per K step (LDS reads, not the matrix instructions, set the pace)
-    else if (tile == TILE_128x64) launch_shape<EPI, PA, PB, 128, 64, (PA > PB ? 4 : 2)>(grid, a, s);
+    else if (tile == TILE_128x64) launch_shape<EPI, PA, PB, 128, 64, 4>(grid, a, s);
     else if (tile == TILE_64x128) launch_shape<EPI, PA, PB, 64, 128, 2>(grid, a, s);
     else launch_shape<EPI, PA, PB, 128, 128, 2>(grid, a, s);
   }
@@ -832,7 +979,7 @@ static void launch_tile(int tile, int grid, const GemmArgs& a, hipStream_t s) {
 template <int PA, int PB>
 static void launch_vstore(int tile, int grid, const GemmArgs& a, hipStream_t s) {
   if (tile == TILE_64x128) launch_shape<EPI_VSTORE, PA, PB, 64, 128, 2>(grid, a, s);
-  else launch_shape<EPI_VSTORE, PA, PB, 128, 64, (PA > PB ? 4 : 2)>(grid, a, s);
+  else launch_shape<EPI_VSTORE, PA, PB, 128, 64, 4>(grid, a, s);
 }
 
 template <int EPI>

@@ -28,6 +28,16 @@ constexpr int KB = 32;
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 __host__ __device__ inline int64_t panel(int64_t r, int64_t k, int64_t R) { return ((k >> 5) * R + r) * KB + (k & 31); }
+// The weight operands of the forward and element-flow products are stored in
+// matrix-instruction fragment order instead: 32-row x 32-K blocks of 1024
+// elements, row-block major (ks K blocks per row block), and inside a block
+// the two 16-wide K steps one after the other, each as 64 lanes x 8 values:
+// lane (r % 32) + 32 h of K step s holds K s*16 + h*8 .. + 7 of row r, the A
+// operand of v_mfma_f32_32x32x16_bf16.  A wave loads its 32 rows of one K
+// step with one contiguous 1 KB instruction, straight into registers.
+__host__ __device__ inline int64_t frag_major(int64_t r, int64_t k, int64_t ks) {
+  return ((r >> 5) * ks + (k >> 5)) * 1024 + ((k >> 4) & 1) * 512 + ((r & 31) + ((k >> 3) & 1) * 32) * 8 + (k & 7);
+}
 
 // One sum group (node block) of a sum layer.
 struct GroupRec {

@@ -110,6 +110,16 @@ constexpr int gemm_stages(int pa, int pb, int mt, int nt) {
              : ((160 - 2) * 1024) / ((pa * mt + pb * nt) * gemm_kt(pa, pb, mt, nt) * 2);
 }
 
+// Ring stages when the weights go straight to registers (forward, element-flow
+// and virtual-batch products): the ring holds B only, and the registers hold
+// one slice of weights per stage (pa * fm * 8 per lane: at most about 128 in
+// all); 3 to 8 stages, within 160 KB of LDS.
+constexpr int gemm_stages_direct(int pa, int pb, int mt, int nt, int fm) {
+  const int by_regs = 16 / (pa * fm) < 3 ? 3 : 16 / (pa * fm) > 8 ? 8 : 16 / (pa * fm);
+  const int by_lds = ((160 - 2) * 1024) / (pb * nt * gemm_kt(pa, pb, mt, nt) * 2);
+  return by_regs < by_lds ? by_regs : by_lds;
+}
+
 // Shape of a forward / element-flow launch over a layer whose outputs span
 // `rows256` 256-row blocks, batch padded to B_pad, largest padded K `kpad`.
 // Automatic: 8192-output tiles, 64 x 128 when the first operand has more
