@@ -559,9 +559,14 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
       using BN = std::integral_constant<int, bf ^ 1>;
       constexpr bool lastks = ks + 1 == KS;
       if constexpr (lastks) {
-        // the next slice has landed once at most the NS-2 slices issued after it are in flight
+        // the next slice's B has landed in LDS once at most (NS-2)*PW loads
+        // are in flight: loads into registers and loads into LDS each
+        // complete in issue order, but not in order with each other, and were
+        // one of that slice's LDS loads still in flight, so would be the
+        // (NS-2)*PW LDS loads issued after it.  (The compiler's own waits for
+        // the weight registers count only register loads, so they hold too.)
         __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(WaitVmLgkm<(NS - 2) * PWA>::imm);
+        __builtin_amdgcn_s_waitcnt(WaitVmLgkm<(NS - 2) * PW>::imm);
         ring_barrier();
       }
       sfor<NMF>([&](auto T) {
@@ -593,7 +598,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
       sfor<QD>([&](auto Q) { aload(S0, Q); });
       sfor<PW>([&](auto Q) { dma(decltype(S0)::value, Q); });
     });
-    __builtin_amdgcn_s_waitcnt(WaitVmLgkm<(NS - 2) * PWA>::imm);
+    __builtin_amdgcn_s_waitcnt(WaitVmLgkm<(NS - 2) * PW>::imm);
     ring_barrier();
     sfor<NRB>([&](auto U) { fragb(std::integral_constant<int, 0>(), 0, std::integral_constant<int, 0>(), U); });
     // whole rounds of NS steps with no branch between the steps (so the

@@ -206,16 +206,9 @@ void free_tables(Handle* h) {
 
 GemmShape layer_gemm_shape(const Handle* h, const SumPlan& sp, int kind, int B_pad, int pa, int pb) {
   const int rows256 = kind == GK_FWD ? sp.mtiles : sp.ctiles, kpad = kind == GK_FWD ? sp.max_npk : sp.max_mpk;
-  GemmShape g = layer_shape(rows256, B_pad, kpad, pa, pb, h->opt_layer_tile, h->opt_split_max);
-  // Automatic tiles of a launch with many tiles per CU (a wide level of
-  // strided groups): 128 x 128 instead of 128 x 64, half the tiles with twice
-  // the work each, so the per-tile ring fill and epilogue are paid half as
-  // often and every operand byte staged in LDS feeds twice the matrix work.
-  // Only where the padded batch is whole 128-column tiles.
-  if (h->opt_layer_tile == TILE_AUTO && g.tile == TILE_128x64 && B_pad % 128 == 0 &&
-      rows256 * 2 * (B_pad / 128) >= 4 * 256)
-    g = layer_shape(rows256, B_pad, kpad, pa, pb, TILE_128x128, h->opt_split_max);
-  return g;
+  // (wide levels of strided groups keep the automatic 128 x 64 tiles too: with
+  // the weights in registers, 128 x 128 tiles ran the HCLT step no faster)
+  return layer_shape(rows256, B_pad, kpad, pa, pb, h->opt_layer_tile, h->opt_split_max);
 }
 
 // The LowRank "sum_exp" virtual batch runs (no fused kernels asked for).

@@ -123,13 +123,14 @@ constexpr int gemm_stages_direct(int pa, int pb, int mt, int nt, int fm) {
 // Shape of a forward / element-flow launch over a layer whose outputs span
 // `rows256` 256-row blocks, batch padded to B_pad, largest padded K `kpad`.
 // Automatic: 8192-output tiles, 64 x 128 when the first operand has more
-// planes than the second, else 128 x 64.  A tile loads pa * MT + pb * NT
-// elements per K step, least at MT / NT = pb / pa, and the per-CU request
-// rate, not the matrix instructions, sets the pace (on the 4096-node HMM
-// layers at batch 512, 256 tiles with the full K: forward products 64 x 128
-// 8.6% faster than 128 x 64, element flows 128 x 64 2% faster than 64 x 128;
-// 128 x 64 was 3% faster per step than 128 x 128 split in two and, at batch
-// 128 split in four, 8% faster than 128 x 128 split in eight).  The K split
+// planes than the second, else 128 x 64 (the shape of every automatic
+// split).  A tile loads pa * MT + pb * NT elements per K step, least at
+// MT / NT = pb / pa, and the per-CU request rate, not the matrix
+// instructions, sets the pace (measured with both operands staged in LDS,
+// 4096-node HMM layers at batch 512: 128 x 64 3% faster per step than
+// 128 x 128 split in two, and at batch 128 split in four 8% faster than
+// 128 x 128 split in eight; with the weights in registers the HCLT step ran
+// as fast on 128 x 64 tiles as on 128 x 128 tiles for its wide levels).  The K split
 // (a power of two up to split_max) grows until the launch has 256 workgroups,
 // keeping >= 4 slices per split.
 // Columns (samples) of the tile a forward / element-flow launch uses.

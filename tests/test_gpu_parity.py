@@ -136,15 +136,17 @@ def test_hclt_small(mode):
     _full(cfg, mode, "hclt 30x48")
 
 
+@pytest.mark.parametrize("tile", [0, 1])
 @pytest.mark.parametrize("mode", MODES)
-def test_hclt_wide_level_tiles(mode):
-    """A strided level wide enough for the automatic 128 x 128 product tiles
-    (at least 4 x 256 of them: 69 groups x 2 row tiles x 8 column tiles at
-    batch 1024) next to levels that keep 128 x 64 tiles, in one pass."""
+def test_hclt_wide_level_tiles(mode, tile):
+    """A strided level with many product tiles per CU (at least 4 x 256
+    128 x 128 tiles: 69 groups x 2 row tiles x 8 column tiles at batch 1024)
+    next to narrow levels, in one pass, on the automatic tiles and on
+    128 x 128 tiles (layer_tile 1)."""
     cfg = make_config("hclt", num_vars=180, H=256, K=16, B=1024)
     widths = [len(ly.groups) * 2 * (cfg["B"] // 128) for ly in cfg["circuit"].layers if type(ly).__name__ == "Sum"]
     assert max(widths) >= 1024 and min(widths) < 1024
-    _full(cfg, mode, "hclt 180x256 wide level")
+    _full(cfg, mode, f"hclt 180x256 wide level, layer tile {tile}", options=[("layer_tile", tile)])
 
 
 @pytest.mark.parametrize("mode", MODES)
