@@ -24,7 +24,10 @@
 // fragments of the next 16-wide K step are read from LDS while the matrix
 // instructions of the current one run, and the loads of the slice NS-1 ahead
 // are issued between them; the ring barrier sits in the middle of a slice's
-// last matrix instructions, so its wait overlaps them.
+// last matrix instructions, so its wait overlaps them.  In the forward,
+// element-flow and virtual-batch products the weights (A) skip the ring: they
+// are stored in fragment order (frag_major) and each wave loads its own rows
+// straight into a register ring of NS slices; the LDS ring carries B only.
 //
 // Forward and element-flow products of one layer have few output tiles; they
 // split K over `splitk` workgroups.  Every split writes its partial tile, and
