@@ -202,13 +202,25 @@ def test_block_sparse_circuit(mode):
     _full(cfg, mode, "block-sparse circuit")
 
 
-def test_deterministic():
-    """Two runs give bitwise identical values, flows and parameter flows."""
-    cfg = make_config(kind="block_layer", seed=4, M_blocks=6, node_block=40, ch_blocks=5,
-                      ch_block=32, B=33)
-    r = G.run_gpu(cfg, "auto", repeat=2)
+@pytest.mark.parametrize("what,cfg_args,mode", [
+    ("block layer", dict(kind="block_layer", seed=4, M_blocks=6, node_block=40, ch_blocks=5, ch_block=32, B=33),
+     "auto"),
+    # wide strided level with the weights in registers (a wait that counted
+    # loads of both kinds made these flows differ from run to run)
+    ("hclt 180x256 wide level", dict(name="hclt", num_vars=180, H=256, K=16, B=1024), "fp32"),
+    ("hclt 180x256 wide level", dict(name="hclt", num_vars=180, H=256, K=16, B=1024), "auto"),
+    # K split over four workgroups (batch 128)
+    ("hmm 1024x6", dict(name="hmm4096", H=1024, T=6, B=128), "auto"),
+])
+def test_deterministic(what, cfg_args, mode):
+    """Three runs give bitwise identical values, flows and parameter flows."""
+    args = dict(cfg_args)
+    cfg = make_config(args.pop("name", None), **args)
+    G.say(f"case determinism {what} mode={mode} B={cfg['B']}")
+    r = G.run_gpu(cfg, mode, repeat=3)
     for k in ("vals", "flows", "pflows"):
-        np.testing.assert_array_equal(r[0][k], r[1][k])
+        for i in (1, 2):
+            np.testing.assert_array_equal(r[0][k], r[i][k], err_msg=f"{what}: {k}, run {i} vs run 0")
 
 
 @pytest.mark.parametrize("kind", ["fwd", "elem", "param"])
