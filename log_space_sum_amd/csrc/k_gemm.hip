@@ -522,7 +522,6 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
   // stage read holds an old slice and the values go unused): the waits stay
   // constants.
   constexpr int QD = PA * FM * KS;             // direct weight loads per wave per slice
-  constexpr int PWA = PW + QD;                 // vector-memory instructions per wave per slice
   constexpr int NRB = PB * FN;                 // fragment reads (B) per K step
   using RB_ = ReadOrderB<PA, PB, FM, FN>;
   bf16x8_t areg[NS][PA][FM][KS];
@@ -583,11 +582,16 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
             else fragb(std::integral_constant<int, 0>(), snext, std::integral_constant<int, 0>(), std::integral_constant<int, u>());
           });
         } else if constexpr (ks == 0) {
-          constexpr int o0 = (t - H) * PWA / (NMF - H), o1 = (t - H + 1) * PWA / (NMF - H);
+          // the ring's loads in the first K step (all before the step's ring
+          // wait, which counts them), the weights' in the second: the
+          // requests spread over the slice (3-4 % faster per product than
+          // all in the first K step)
+          constexpr int o0 = (t - H) * PW / (NMF - H), o1 = (t - H + 1) * PW / (NMF - H);
+          sfor<o1 - o0>([&](auto O) { dma(JL, std::integral_constant<int, o0 + decltype(O)::value>()); });
+        } else if constexpr (ks == 1) {
+          constexpr int o0 = (t - H) * QD / (NMF - H), o1 = (t - H + 1) * QD / (NMF - H);
           sfor<o1 - o0>([&](auto O) {
-            constexpr int q = o0 + decltype(O)::value;
-            if constexpr (q < QD) aload(std::integral_constant<int, JL>(), std::integral_constant<int, q>());
-            else dma(JL, std::integral_constant<int, q - QD>());
+            aload(std::integral_constant<int, JL>(), std::integral_constant<int, o0 + decltype(O)::value>());
           });
         }
         __builtin_amdgcn_sched_barrier(0);
